@@ -1,0 +1,385 @@
+"""Pins of the CPU oracle against things other than itself: the pages' worked numbers
+(tests/golden), closed forms, brute force on tiny inputs and invariants.  CPU only."""
+import itertools
+import json
+import math
+import os
+
+import numpy as np
+import pytest
+
+import oracle as O
+
+GOLDEN = json.load(open(os.path.join(os.path.dirname(__file__), "golden", "page_examples.json")))
+
+
+def _rng(seed):
+    return np.random.default_rng(seed)
+
+
+def _tiny_experts(rng, E, d, d_ff, act, bias=False):
+    ws = []
+    for _ in range(E):
+        w = O.ExpertWeights(
+            w1=rng.standard_normal((d_ff, d)) / math.sqrt(d),
+            w2=rng.standard_normal((d, d_ff)) / math.sqrt(d_ff),
+            w3=rng.standard_normal((d_ff, d)) / math.sqrt(d) if act == "swiglu" else None,
+            b1=rng.standard_normal(d_ff) * 0.1 if bias else None,
+            b2=rng.standard_normal(d) * 0.1 if bias else None,
+        )
+        ws.append(w)
+    return ws
+
+
+# ------------------------------------------------------------------ capacity
+@pytest.mark.parametrize("key", ["capacity_example", "switch_capacity", "decode_capacity"])
+def test_capacity_worked_values(key):
+    g = GOLDEN[key]
+    assert O.capacity(g["n_tokens"], g["n_experts"], g["k"], g["alpha"]) == g["capacity"]
+
+
+def test_capacity_unlimited():
+    assert O.capacity(100, 8, 2, None) is None
+    assert O.capacity(100, 8, 2, 0.0) is None
+
+
+def _sequential_keep(idx, E, cap):
+    """Independent coding of the capacity rule: walk tokens in order with one counter
+    per expert."""
+    n, k = idx.shape
+    cnt = [0] * E
+    keep = np.zeros((n, k), bool)
+    for t in range(n):
+        for j in range(k):
+            e = int(idx[t, j])
+            if cap is None or cnt[e] < cap:
+                keep[t, j] = True
+            cnt[e] += 1
+    return keep
+
+
+@pytest.mark.parametrize("cap", [None, 0, 1, 3, 7])
+def test_capacity_and_permutation_bruteforce(cap):
+    rng = _rng(1)
+    N, E, k = 57, 6, 3
+    # skewed selection: random distinct experts, biased towards low ids
+    z = rng.standard_normal((N, E)).astype(np.float32) + np.linspace(1.5, 0, E, dtype=np.float32)
+    idx = O.select_topk(z, k)
+    plan = O.plan_dispatch(idx, E, cap)
+    keep = _sequential_keep(idx, E, cap)
+    assert np.array_equal(plan.keep, keep)
+    if cap is not None:
+        assert (plan.kept_count <= cap).all()
+        assert np.array_equal(plan.keep, plan.rank < cap)
+    assert plan.kept_count.sum() + plan.n_dropped == N * k
+    # permutation by sorting (expert, token) of kept pairs
+    pairs = sorted((int(idx[t, j]), t, j) for t in range(N) for j in range(k) if keep[t, j])
+    assert np.array_equal(plan.row_token, [t for _, t, _ in pairs])
+    assert np.array_equal(plan.row_slot, [j for _, _, j in pairs])
+    counts = np.bincount([e for e, _, _ in pairs], minlength=E)
+    assert np.array_equal(plan.expert_offsets, np.concatenate([[0], np.cumsum(counts)]))
+    for r, (e, t, j) in enumerate(pairs):
+        assert plan.slot_row[t, j] == r
+    assert (plan.slot_row[~keep] == -1).all()
+    # rows strictly increasing in token inside each segment
+    for e in range(E):
+        seg = plan.row_token[plan.expert_offsets[e]:plan.expert_offsets[e + 1]]
+        assert (np.diff(seg) > 0).all()
+
+
+# ------------------------------------------------------------------ selection
+def _lexsort_topk(z, k):
+    n, E = z.shape
+    out = np.empty((n, k), np.int32)
+    for t in range(n):
+        order = np.lexsort((np.arange(E), -z[t].astype(np.float64)))
+        out[t] = order[:k]
+    return out
+
+
+def _subset_topk(z_row, k):
+    """Brute force: the k-subset of largest sum; among equal sums the lexicographically
+    smallest (itertools yields subsets in lexicographic order, strict > keeps the first);
+    slots then sorted by descending score, ascending index."""
+    best, best_s = None, -math.inf
+    for s in itertools.combinations(range(len(z_row)), k):
+        tot = sum(float(z_row[i]) for i in s)
+        if tot > best_s:
+            best, best_s = s, tot
+    return sorted(best, key=lambda i: (-float(z_row[i]), i))
+
+
+def test_topk_two_codings_with_ties():
+    rng = _rng(2)
+    z = rng.integers(-3, 4, size=(300, 16)).astype(np.float32) * np.float32(0.5)
+    for k in (1, 2, 5, 16):
+        assert np.array_equal(O.select_topk(z, k), _lexsort_topk(z, k))
+
+
+def test_topk_bruteforce_subsets():
+    rng = _rng(3)
+    z = rng.integers(-2, 3, size=(120, 6)).astype(np.float32)
+    for k in (1, 2, 3, 6):
+        got = O.select_topk(z, k)
+        for t in range(z.shape[0]):
+            assert list(got[t]) == _subset_topk(z[t], k)
+
+
+def test_topk_all_equal_and_signed_zero():
+    z = np.zeros((5, 9), np.float32)
+    assert (O.select_topk(z, 3) == np.arange(3)).all()
+    z2 = np.array([[-0.0, 0.0, -1.0]], np.float32)
+    assert list(O.select_topk(z2, 2)[0]) == [0, 1]  # -0.0 == +0.0 is a tie -> lower index
+
+
+def test_logit_bias_acts_before_selection_and_softmax():
+    logits = np.array([[0.0, 0.5]], np.float32)
+    b = np.array([1.0, 0.0], np.float32)
+    z = O.biased_scores(logits, b)
+    assert list(O.select_topk(z, 1)[0]) == [0]
+    p = O.softmax64(z)
+    assert abs(p[0, 0] - 1.0 / (1.0 + math.exp(-0.5))) < 1e-15
+
+
+# ------------------------------------------------------------------ gate weights
+def test_softmax_closed_form():
+    z = np.array([[0.0, 1.0, 2.0]], np.float32)
+    p = O.softmax64(z)
+    s = 1 + math.e + math.e ** 2
+    assert np.allclose(p[0], [1 / s, math.e / s, math.e ** 2 / s], rtol=1e-15, atol=0)
+
+
+def test_renormalised_weights_sum_to_one_and_kE_gives_softmax():
+    rng = _rng(4)
+    z = rng.standard_normal((200, 10)).astype(np.float32)
+    p = O.softmax64(z)
+    for k in (1, 2, 6):
+        idx = O.select_topk(z, k)
+        w = O.gate_weights(p, idx, True)
+        assert np.abs(w.sum(1) - 1).max() <= 4 * k * np.finfo(np.float64).eps
+        if k == 1:
+            assert (w == 1.0).all()
+    idx = O.select_topk(z, 10)
+    w = O.gate_weights(p, idx, True)
+    assert np.allclose(w, np.take_along_axis(p, idx, 1), rtol=1e-14, atol=0)
+    # without renormalisation the weights are the raw probabilities, descending
+    w_raw = O.gate_weights(p, O.select_topk(z, 2), False)
+    assert (w_raw[:, 0] >= w_raw[:, 1]).all()
+
+
+# ------------------------------------------------------------------ statistics
+@pytest.mark.parametrize("E,k", [(8, 2), (64, 1), (160, 6), (3, 2)])
+def test_aux_is_one_under_uniform_probabilities(E, k):
+    N = 50
+    z = np.zeros((N, E), np.float32)  # W_router = 0 gives these logits
+    p = O.softmax64(z)
+    st = O.balance_stats(p, O.select_topk(z, k), E)
+    assert abs(st.aux - GOLDEN["uniform_balance_loss"]["aux"]) < 1e-12
+    assert np.allclose(st.prob_mean, 1.0 / E, rtol=1e-14)
+
+
+def test_page_exercise_balanced_selection():
+    g = GOLDEN["balanced_exercise"]
+    N, k, E = g["n_tokens"], g["k"], g["n_experts"]
+    z = np.zeros((N, E), np.float32)
+    t = np.arange(N)
+    z[t, t % E] = 2.0
+    z[t, (t + E // 2) % E] = 1.0
+    idx = O.select_topk(z, k)
+    p = O.softmax64(z)
+    st = O.balance_stats(p, idx, E)
+    assert (st.sel_count == g["per_expert"]).all()
+    plan = O.plan_dispatch(idx, E, None)
+    assert (plan.kept_count == g["per_expert"]).all()
+    # exactly balanced selection: freq = 1/E, so aux = sum(prob_mean) = 1
+    assert abs(st.aux - 1.0) < 1e-12
+
+
+def test_aux_closed_form_two_experts():
+    a = 0.75
+    z = np.array([[a, 0.0]], np.float32)
+    p = O.softmax64(z)
+    st = O.balance_stats(p, O.select_topk(z, 1), 2)
+    assert list(st.sel_count) == [1, 0]
+    assert abs(st.aux - 2.0 / (1.0 + math.exp(-a))) < 1e-15
+
+
+def test_stats_count_before_capacity():
+    z = np.zeros((10, 4), np.float32)
+    z[:, 2] = 1.0
+    idx = O.select_topk(z, 1)
+    st = O.balance_stats(O.softmax64(z), idx, 4)
+    assert list(st.sel_count) == [0, 0, 10, 0]
+    plan = O.plan_dispatch(idx, 4, O.capacity(10, 4, 1, 1.0))  # C = 2
+    assert list(plan.kept_count) == [0, 0, 2, 0] and plan.n_dropped == 8
+
+
+# ------------------------------------------------------------------ experts
+# Standard normal CDF values from printed tables: Phi(1), Phi(2), Phi(-1).
+PHI1, PHI2, PHI_M1 = 0.8413447460685429, 0.9772498680518208, 0.15865525393145707
+
+
+def test_activation_values():
+    u = np.array([0.0, 1.0, 2.0, -1.0, 30.0])
+    g = O.gelu(u)
+    assert g[0] == 0.0
+    assert abs(g[1] - PHI1) < 1e-15 and abs(g[2] - 2 * PHI2) < 1e-15
+    assert abs(g[3] + PHI_M1) < 1e-15 and g[4] == 30.0
+    s = O.silu(np.array([0.0, 1.0, -1.0, -800.0]))
+    assert s[0] == 0.0 and abs(s[1] - 0.7310585786300049) < 1e-15
+    assert abs(s[2] + 0.2689414213699951) < 1e-15 and s[3] == 0.0
+
+
+def _loop_ffn(xrow, w, act):
+    """Pure-Python dense FFN of one token (independent coding)."""
+    d_ff, d = w.w1.shape
+    h = []
+    for f in range(d_ff):
+        u = sum(w.w1[f, c] * xrow[c] for c in range(d)) + (w.b1[f] if w.b1 is not None else 0.0)
+        if act == "gelu":
+            h.append(0.5 * u * (1 + math.erf(u / math.sqrt(2))))
+        else:
+            v = sum(w.w3[f, c] * xrow[c] for c in range(d))
+            h.append(u / (1 + math.exp(-u)) * v)
+    return [sum(w.w2[o, f] * h[f] for f in range(d_ff)) + (w.b2[o] if w.b2 is not None else 0.0)
+            for o in range(d)]
+
+
+@pytest.mark.parametrize("act,bias", [("gelu", True), ("swiglu", False)])
+def test_single_expert_is_the_dense_ffn(act, bias):
+    rng = _rng(5)
+    N, d, d_ff = 5, 4, 6
+    x = rng.standard_normal((N, d)).astype(np.float32)
+    ws = _tiny_experts(rng, 1, d, d_ff, act, bias)
+    r = O.forward(x, "f32", np.zeros((d, 1), np.float32), 1, lambda e: ws[e], 1, act)
+    for t in range(N):
+        ref = _loop_ffn(x[t].astype(np.float64), ws[0], act)
+        assert np.allclose(r.y[t], ref, rtol=1e-13, atol=1e-15)
+
+
+def test_identical_experts_reduce_to_dense_ffn():
+    rng = _rng(6)
+    N, d, d_ff, E = 7, 4, 5, 5
+    x = rng.standard_normal((N, d)).astype(np.float32)
+    w0 = _tiny_experts(rng, 1, d, d_ff, "swiglu")[0]
+    wr = rng.standard_normal((d, E)).astype(np.float32)
+    r = O.forward(x, "f32", wr, 3, lambda e: w0, E, "swiglu")
+    for t in range(N):
+        assert np.allclose(r.y[t], _loop_ffn(x[t].astype(np.float64), w0, "swiglu"),
+                           rtol=1e-13, atol=1e-15)
+
+
+def test_router_logits_against_loops():
+    rng = _rng(7)
+    x = rng.standard_normal((6, 9)).astype(np.float32)
+    wr = rng.standard_normal((9, 4)).astype(np.float32)
+    L = O.router_logits(x.astype(np.float64), wr.astype(np.float64))
+    for t in range(6):
+        for e in range(4):
+            ref = sum(float(x[t, c]) * float(wr[c, e]) for c in range(9))
+            assert abs(float(L[t, e]) - ref) <= 1e-7 * max(1.0, abs(ref))
+
+
+def test_bf16_decode_exact():
+    bits = np.array([0x3F80, 0xBF80, 0x4049, 0x0000, 0x8000, 0x7F7F], np.uint16)
+    v = O.decode_bf16(bits)
+    assert v[0] == 1.0 and v[1] == -1.0 and v[2] == np.float32(3.140625)
+    assert v[3] == 0.0 and np.signbit(v[4]) and v[5] == np.float32(3.3895314e38)
+
+
+# ------------------------------------------------------------------ whole layer
+def _bruteforce_layer(x, logits, bias, k, ws, shared, act, cap, renorm=True):
+    """Every expert on every token, a dense gate matrix that is zero outside kept slots,
+    routing by subset search, capacity by sequential counters.  Pure Python loops."""
+    N, d = x.shape
+    E = logits.shape[1]
+    z = [[float(np.float32(logits[t, e]) + np.float32(0 if bias is None else bias[e]))
+          for e in range(E)] for t in range(N)]
+    idx = np.array([_subset_topk(np.array(z[t]), k) for t in range(N)], np.int32)
+    keep = _sequential_keep(idx, E, cap)
+    y = np.zeros((N, d))
+    for t in range(N):
+        m = max(z[t])
+        ex = [math.exp(v - m) for v in z[t]]
+        p = [v / sum(ex) for v in ex]
+        sel_sum = sum(p[i] for i in idx[t])
+        gate = [0.0] * E
+        for j in range(k):
+            if keep[t, j]:
+                gate[idx[t, j]] = p[idx[t, j]] / (sel_sum if renorm else 1.0)
+        xt = x[t].astype(np.float64)
+        for e in range(E):
+            ye = _loop_ffn(xt, ws[e], act)
+            y[t] += gate[e] * np.array(ye)
+        for s in shared:
+            y[t] += np.array(_loop_ffn(xt, s, act))
+    return y, idx, keep
+
+
+@pytest.mark.parametrize("act,cap,n_shared,renorm", [
+    ("gelu", None, 0, True), ("swiglu", 2, 0, True), ("swiglu", None, 2, True),
+    ("gelu", 1, 1, False)])
+def test_layer_matches_dense_bruteforce(act, cap, n_shared, renorm):
+    rng = _rng(8)
+    N, d, d_ff, E, k = 11, 4, 6, 4, 2
+    x = rng.standard_normal((N, d)).astype(np.float32)
+    logits = rng.standard_normal((N, E)).astype(np.float32)
+    bias = (rng.uniform(-0.3, 0.3, E)).astype(np.float32)
+    ws = _tiny_experts(rng, E, d, d_ff, act, bias=(act == "gelu"))
+    sh = _tiny_experts(rng, n_shared, d, d_ff, act)
+    alpha = None if cap is None else cap / ((k * N) // E)
+    r = O.forward(x, "f32", None, k, lambda e: ws[e], E, act, logit_bias=bias, alpha=alpha,
+                  renormalize=renorm, shared=lambda s: sh[s], n_shared=n_shared, logits=logits)
+    assert r.cap == cap
+    y, idx, keep = _bruteforce_layer(x, logits, bias, k, ws, sh, act, cap, renorm)
+    assert np.array_equal(r.topk_idx, idx) and np.array_equal(r.plan.keep, keep)
+    assert np.allclose(r.y, y, rtol=1e-12, atol=1e-14)
+
+
+def test_fully_dropped_token_is_zero():
+    rng = _rng(9)
+    N, d, d_ff, E = 8, 3, 4, 2
+    x = rng.standard_normal((N, d)).astype(np.float32)
+    logits = np.zeros((N, E), np.float32)
+    logits[:, 0] = 1.0  # everyone wants expert 0
+    ws = _tiny_experts(rng, E, d, d_ff, "gelu")
+    r = O.forward(x, "f32", None, 1, lambda e: ws[e], E, "gelu", alpha=0.5, logits=logits)
+    assert r.cap == 2
+    assert (r.y[2:] == 0).all() and (np.abs(r.y[:2]) > 0).any()
+
+
+def test_token_permutation_equivariance_and_subset():
+    rng = _rng(10)
+    N, d, d_ff, E, k = 20, 5, 6, 5, 2
+    x = rng.standard_normal((N, d)).astype(np.float32)
+    wr = rng.standard_normal((d, E)).astype(np.float32)
+    ws = _tiny_experts(rng, E, d, d_ff, "swiglu")
+    f = lambda xx, **kw: O.forward(xx, "f32", wr, k, lambda e: ws[e], E, "swiglu", **kw)
+    r = f(x)
+    perm = rng.permutation(N)
+    rp = f(x[perm])
+    assert np.allclose(rp.y, r.y[perm], rtol=1e-13, atol=1e-15)
+    sub = np.array([3, 17, 0])
+    rs = f(x, tokens=sub)
+    assert np.allclose(rs.y, r.y[sub], rtol=1e-14, atol=1e-15)
+
+
+def test_expert_relabelling_invariance():
+    rng = _rng(11)
+    N, d, d_ff, E, k = 15, 4, 5, 6, 3
+    x = rng.standard_normal((N, d)).astype(np.float32)
+    wr = rng.standard_normal((d, E)).astype(np.float32)
+    ws = _tiny_experts(rng, E, d, d_ff, "gelu", bias=True)
+    r = O.forward(x, "f32", wr, k, lambda e: ws[e], E, "gelu")
+    perm = rng.permutation(E)  # new expert i is old expert perm[i]
+    r2 = O.forward(x, "f32", wr[:, perm], k, lambda e: ws[perm[e]], E, "gelu")
+    assert np.allclose(r2.y, r.y, rtol=1e-13, atol=1e-15)
+    assert np.array_equal(perm[r2.topk_idx], r.topk_idx)
+
+
+def test_empty_batch():
+    ws = _tiny_experts(_rng(12), 3, 4, 5, "gelu")
+    r = O.forward(np.zeros((0, 4), np.float32), "f32", np.ones((4, 3), np.float32), 2,
+                  lambda e: ws[e], 3, "gelu", alpha=1.0)
+    assert r.y.shape == (0, 4) and r.plan.n_dropped == 0 and r.stats.aux == 0.0
+    assert list(r.plan.expert_offsets) == [0, 0, 0, 0]
