@@ -1,0 +1,234 @@
+#!/usr/bin/env python3
+"""Throughput of the routed MoE FFN forward pass on one MI355X.
+
+One step = one moe_forward over a batch of synthetic tokens: router product, gate,
+statistics, capacity, dispatch, routed expert FFNs, shared experts, combine.  The
+default workload is the Mixtral-shaped layer (4096 tokens, d 4096, 8 SwiGLU experts of
+width 14336, top-2, bf16), the one the layer's throughput targets are stated on; other
+workloads can be chosen with --config.
+
+Prints one JSON line: tokens/s over the timed steps, per-stage times from HIP events
+recorded by the library on the launch stream, the roofline position of the dominant
+kernel, and the CPU oracle timed on a bounded sample of the same workload.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+PEAK_BF16_TFLOPS = 2500.0  # dense MFMA, MI355X
+PEAK_F32_TFLOPS = 157.3
+PEAK_HBM_GBPS = 8000.0
+METRIC = "MoE-layer tokens/s; grouped-GEMM TFLOP/s & % of MFMA peak; dispatch GB/s"
+STAGES = ["route", "dispatch", "gemm1", "gemm2", "shared", "combine"]
+
+
+def describe(cfg) -> str:
+    s = (f"{cfg.name}: N={cfg.n_tokens} d={cfg.d_model} E={cfg.n_experts} k={cfg.top_k} "
+         f"{cfg.act} d_ff={cfg.d_ff} {cfg.dtype}")
+    if cfg.n_shared:
+        s += f" +{cfg.n_shared} shared"
+    if cfg.alpha:
+        s += f" capacity_factor={cfg.alpha}"
+    if cfg.logit_bias != "none":
+        s += f" logit_bias={cfg.logit_bias}"
+    return s
+
+
+def kernel_work(cfg, kept: int, touched: int):
+    """Algorithmic flops and HBM bytes of each stage (padding and dropped rows excluded)."""
+    es = 2 if cfg.dtype == "bf16" else 4
+    n, d, f, k = cfg.n_tokens, cfg.d_model, cfg.d_ff, cfg.top_k
+    m1 = 2 if cfg.act == "swiglu" else 1
+    sh = cfg.n_shared
+    w = {}
+    w["gemm1"] = dict(flops=2.0 * kept * d * f * m1,
+                      bytes=touched * m1 * f * d * es + kept * d * es + kept * f * es)
+    w["gemm2"] = dict(flops=2.0 * kept * f * d,
+                      bytes=touched * d * f * es + kept * f * es + kept * d * es)
+    w["shared"] = dict(flops=2.0 * n * d * f * sh * (m1 + 1),
+                       bytes=sh * (m1 + 1) * f * d * es + n * d * es * 2 + n * sh * f * es * 2)
+    w["dispatch"] = dict(flops=0.0, bytes=n * d * es + kept * d * es + n * k * 4 * 2 + kept * 4)
+    w["combine"] = dict(flops=0.0, bytes=kept * d * es + n * k * 8 + n * d * es * (2 if sh else 1))
+    w["route"] = dict(flops=2.0 * n * d * cfg.n_experts,
+                      bytes=n * d * es + d * cfg.n_experts * 4 + n * (cfg.n_experts * 4 + k * 8))
+    return w
+
+
+def roofline(name, work, ms, dtype):
+    peak_f = PEAK_BF16_TFLOPS if dtype == "bf16" else PEAK_F32_TFLOPS
+    ridge = peak_f * 1e12 / (PEAK_HBM_GBPS * 1e9)
+    fl, by = work["flops"], work["bytes"]
+    if fl > 0 and fl / by >= ridge:
+        ach = fl / (ms * 1e-3) / 1e12
+        return dict(kernel=name, bound="mfma", achieved=round(ach, 2), peak=peak_f, unit="TFLOP/s",
+                    frac=round(ach / peak_f, 4), traffic=None, avg_ms=round(ms, 5),
+                    algorithmic_flops=fl, algorithmic_bytes=by)
+    ach = by / (ms * 1e-3) / 1e9
+    return dict(kernel=name, bound="hbm", achieved=round(ach, 1), peak=PEAK_HBM_GBPS, unit="GB/s",
+                frac=round(ach / PEAK_HBM_GBPS, 4), traffic=None, avg_ms=round(ms, 5),
+                algorithmic_flops=fl, algorithmic_bytes=by)
+
+
+def cpu_baseline(cfg, inp, logits, budget_s: float):
+    """The CPU oracle, as it stands, on the first n_s tokens of the same inputs (routing
+    and capacity over every token), n_s sized to about budget_s seconds."""
+    import numpy as np
+
+    import oracle as O
+
+    def host(t):
+        t = t.detach().contiguous()
+        if str(t.dtype) == "torch.bfloat16":
+            import torch
+
+            return t.view(torch.int16).cpu().numpy().view(np.uint16)
+        return t.cpu().numpy()
+
+    x = host(inp.x)
+    lb = None if inp.logit_bias is None else host(inp.logit_bias)
+    wr = host(inp.w_router)
+    raw = {}
+    for e in range(cfg.n_experts):  # staging copies to host memory: not timed
+        raw[e] = {k: host(getattr(inp, k)[e]) for k in ("w1", "w2", "w3", "b1", "b2")
+                  if getattr(inp, k) is not None}
+    sraw = {}
+    for s in range(cfg.n_shared):
+        sraw[s] = {k: host(getattr(inp, "s" + k)[s]) for k in ("w1", "w2", "w3")
+                   if getattr(inp, "s" + k) is not None}
+
+    def widen_expert(w):
+        return O.ExpertWeights(**{k: O.widen(v, cfg.dtype) for k, v in w.items()})
+
+    def run(n_s):
+        t0 = time.perf_counter()
+        O.forward(x, cfg.dtype, wr, cfg.top_k, lambda e: widen_expert(raw[e]), cfg.n_experts,
+                  cfg.act, logit_bias=lb, alpha=cfg.alpha, renormalize=cfg.renormalize,
+                  shared=(lambda s: widen_expert(sraw[s])) if cfg.n_shared else None,
+                  n_shared=cfg.n_shared, tokens=np.arange(n_s))
+        return time.perf_counter() - t0
+
+    n = cfg.n_tokens
+    n_s = min(n, 16)
+    t = run(n_s)
+    if t < 0.5 * budget_s and n_s < n:
+        n_s = int(min(n, max(n_s, n_s * 0.8 * budget_s / t)))
+        t = run(n_s)
+    try:
+        from threadpoolctl import threadpool_info
+
+        cores = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    except Exception:  # pragma: no cover
+        cores = len(os.sched_getaffinity(0))
+    return dict(value=round(n_s / t, 2), unit="tokens/s", cores=int(cores), kind="oracle",
+                sample=f"first {n_s} of {n} tokens (router product, gate and capacity over all "
+                       f"{n}); float64 numpy; {t:.1f} s",
+                seconds=round(t, 2))
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--config", default="mixtral")
+    ap.add_argument("--cpu-seconds", type=float, default=15.0)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print("bench.py runs on one GPU only: this build has no multi-GPU path "
+              "(the layer is measured on a single MI355X); use --gpus 1", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    from sparse_mixture_experts_forward_amd import CONFIGS, MoELayer, synth
+    from sparse_mixture_experts_forward_amd import _binding as B
+
+    B.lib()  # fails loudly if the HIP library is not built
+    cfg = CONFIGS[args.config]
+    dev = torch.device("cuda:0")
+    inp = synth.DeviceInputs(cfg, dev)
+    layer = MoELayer.from_inputs(inp)
+    n = cfg.n_tokens
+    stats = layer.new_stats(n)
+    y = torch.empty_like(inp.x)
+
+    for _ in range(args.warmup):
+        layer.forward(inp.x, y, stats)
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(B.MOE_N_STAGE_EVENTS)]
+          for _ in range(args.steps)]
+    for row in ev:  # create the events
+        for e in row:
+            e.record()
+    torch.cuda.synchronize()
+    handles = [[e.cuda_event for e in row] for row in ev]
+
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        layer.forward(inp.x, y, stats, stage_events=handles[i])
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t0
+
+    stage_ms = {s: 0.0 for s in STAGES}
+    for row in ev:
+        for j, s in enumerate(STAGES):
+            stage_ms[s] += row[j].elapsed_time(row[j + 1]) / args.steps
+    step_gpu_ms = sum(ev[i][0].elapsed_time(ev[i][-1]) for i in range(args.steps)) / args.steps
+
+    kept = int(stats["kept_count"].sum().item())
+    touched = int((stats["kept_count"] > 0).sum().item())
+    work = kernel_work(cfg, kept, touched)
+    kernels = {s: roofline(s, work[s], stage_ms[s], cfg.dtype) for s in STAGES if stage_ms[s] > 0}
+    dominant = max(("gemm1", "gemm2", "shared", "dispatch", "combine", "route"),
+                   key=lambda s: stage_ms[s])
+    gemm_ms = stage_ms["gemm1"] + stage_ms["gemm2"] + stage_ms["shared"]
+    gemm_flops = work["gemm1"]["flops"] + work["gemm2"]["flops"] + work["shared"]["flops"]
+    gemm_tflops = gemm_flops / (gemm_ms * 1e-3) / 1e12 if gemm_ms > 0 else 0.0
+    peak = PEAK_BF16_TFLOPS if cfg.dtype == "bf16" else PEAK_F32_TFLOPS
+    disp_gbps = work["dispatch"]["bytes"] / (stage_ms["dispatch"] * 1e-3) / 1e9
+    comb_gbps = work["combine"]["bytes"] / (stage_ms["combine"] * 1e-3) / 1e9
+
+    out = {
+        "metric": METRIC,
+        "value": round(n * args.steps / elapsed, 1),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(elapsed / args.steps * 1e3, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": cfg.dtype,
+        "data": "synthetic (seeded counter-based generator; x ~ N(0,1), weights ~ N(0,1/fan_in))",
+        "config": {"workload": describe(cfg), "n_tokens": n, "d_model": cfg.d_model,
+                   "d_ff": cfg.d_ff, "n_experts": cfg.n_experts, "top_k": cfg.top_k,
+                   "n_shared": cfg.n_shared, "capacity_factor": cfg.alpha,
+                   "kept_rows": kept, "experts_touched": touched},
+        "roofline": kernels[dominant],
+        "grouped_gemm_tflops": round(gemm_tflops, 2),
+        "grouped_gemm_frac_of_peak": round(gemm_tflops / peak, 4),
+        "dispatch_gbps": round(disp_gbps, 1),
+        "dispatch_frac_of_hbm": round(disp_gbps / PEAK_HBM_GBPS, 4),
+        "combine_gbps": round(comb_gbps, 1),
+        "stages_ms": {s: round(v, 5) for s, v in stage_ms.items()},
+        "step_gpu_ms_events": round(step_gpu_ms, 4),
+        "kernels": kernels,
+    }
+    if not args.no_cpu_baseline:
+        out["cpu_baseline"] = cpu_baseline(cfg, inp, stats["logits"], args.cpu_seconds)
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,243 @@
+/*
+ * moe.h -- C ABI of a forward pass of a top-k routed Mixture-of-Experts FFN layer on
+ * AMD Instinct MI355X (gfx950).
+ *
+ * Pages the operations are defined on (short names used below):
+ *   [Why-MoE]      ai.learningdata.cn/blog/why-moe-works-sparse-activation-mpcjx0i3,
+ *                  "为什么MoE有效？稀疏激活的数学直觉与工程实践"
+ *   [DeepSeek-V2]  www.wzjinhao.cn/news/59210, summary of the DeepSeek-V2 report
+ *   [MoE-2pct]     www.mhpn.cn/news/707057, "拆解大模型里被悄悄激活的那2%"
+ *   [MoE-overview] www.mooersco.com/news/2648626, MoE overview
+ *
+ * Conventions shared by every entry point
+ *   - Pointers are DEVICE pointers unless a comment says otherwise.  The caller owns
+ *     every buffer; the library never allocates, frees or retains caller memory.
+ *   - Every call is asynchronous on `stream` (a hipStream_t; NULL = the null stream)
+ *     and does no host synchronisation.  Results are valid once the stream reaches the
+ *     point after the call.
+ *   - Arguments are checked on the host before any device work is queued; a bad
+ *     argument returns MOE_ERR_INVALID_ARG (or MOE_ERR_UNSUPPORTED for a shape or type
+ *     outside the supported set, MOE_ERR_WORKSPACE for a too-small workspace) and
+ *     queues nothing.  A failed kernel launch returns MOE_ERR_HIP.  Faults inside a
+ *     kernel surface at the caller's next synchronisation with the stream.
+ *     moe_last_error() gives a human-readable detail of the last failure on the
+ *     calling thread.
+ *   - Buffer sizes cannot be checked (only pointers are passed); each argument states
+ *     the size it must have.
+ *   - Inputs must be finite.  Results for NaN or Inf inputs are unspecified.
+ *   - Matrices are row-major.  Expert weights follow torch.nn.Linear, [out][in]:
+ *     W1, W3 are [E][d_ff][d], W2 is [E][d][d_ff], b1 is [E][d_ff], b2 is [E][d].
+ *   - bf16 data is stored as IEEE bfloat16 (upper 16 bits of a float32).  All products
+ *     accumulate in float32.  Rounding to bf16 is round-to-nearest-even.
+ *   - Results are deterministic: the same inputs give the same bits on every run.
+ *   - Calls on different streams may run concurrently if their buffers do not overlap.
+ */
+#ifndef MOE_MI355X_H
+#define MOE_MI355X_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  MOE_OK = 0,
+  MOE_ERR_INVALID_ARG = 1,
+  MOE_ERR_UNSUPPORTED = 2,
+  MOE_ERR_WORKSPACE = 3,
+  MOE_ERR_HIP = 4
+} moe_status;
+
+typedef enum { MOE_F32 = 0, MOE_BF16 = 1 } moe_dtype;
+
+typedef enum { MOE_ACT_GELU = 0, MOE_ACT_SWIGLU = 1 } moe_act;
+
+/* Largest number of experts (routed or segments) a call accepts. */
+#define MOE_MAX_EXPERTS 512
+
+/*
+ * moe_capacity -- host function, no device work.
+ * Expert capacity C = floor(floor(k*N/E) * alpha) ([MoE-2pct] §3.1 gives
+ * floor(kN/E) x alpha; its §5.3 works N=32, E=64, k=2, alpha=1.2 to C=1).
+ * Returns -1 (no limit) when alpha <= 0, and -1 with moe_last_error() set when
+ * n_tokens < 0, n_experts < 1 or k < 1.
+ */
+int64_t moe_capacity(int64_t n_tokens, int32_t n_experts, int32_t k, double alpha);
+
+/*
+ * moe_route -- router product, gate and balance statistics.
+ *   logits[t][e] = sum_c x[t][c] * w_router[c][e]       ([Why-MoE] §2.2, no bias)
+ *   z[t][e]      = logits[t][e] + logit_bias[e]          (one float32 add;
+ *                                                         [DeepSeek-V2] §2.2)
+ *   p[t][:]      = softmax(z[t][:])
+ *   topk_idx[t][j], j = 0..k-1: the k largest z[t][:], largest first, ties to the
+ *                  lower expert index ([Why-MoE] §2.2 top-k; selecting on z equals
+ *                  selecting on p because softmax is increasing)
+ *   topk_w[t][j] = p[t][topk_idx[t][j]] / sum_j' p[t][topk_idx[t][j']] if renormalize,
+ *                  else p[t][topk_idx[t][j]]          ([Why-MoE] §2.2 renormalisation)
+ *   sel_count[e] = number of (t, j) with topk_idx[t][j] == e (before any capacity)
+ *   prob_mean[e] = (1/N) sum_t p[t][e]
+ *   aux[0]       = E * sum_e (sel_count[e] / (N*k)) * prob_mean[e]
+ *                  ([DeepSeek-V2] §2.2 load_balance_loss; equals 1 when routing is
+ *                  uniform).  For N == 0 the statistics are written as zeros.
+ * Arguments
+ *   x          [N][d], x_dtype (MOE_F32 or MOE_BF16); d % 4 == 0.  May be NULL when
+ *              logits_in is given.
+ *   w_router   [d][E] float32.  May be NULL when logits_in is given.
+ *   logit_bias [E] float32 or NULL (no bias).
+ *   E          1..MOE_MAX_EXPERTS; 1 <= k <= E, k <= 16.
+ *   logits_in  [N][E] float32 or NULL.  If given, the product is skipped and these
+ *              logits are used (lets a caller condition the gate on known logits).
+ *   logits_out [N][E] float32 or NULL: the float32 logits (before the bias).
+ *   topk_idx   [N][k] int32, topk_w [N][k] float32 (required).
+ *   sel_count  [E] int32, prob_mean [E] float32, aux [1] float32 (each may be NULL).
+ *   ws         device workspace of at least moe_route_workspace_size(N, E) bytes,
+ *              256-byte aligned (may be NULL if that size is 0).
+ */
+size_t moe_route_workspace_size(int64_t n_tokens, int32_t n_experts);
+moe_status moe_route(void* stream, const void* x, moe_dtype x_dtype, int64_t n_tokens,
+                     int64_t d_model, const float* w_router, const float* logit_bias,
+                     int32_t n_experts, int32_t k, int32_t renormalize,
+                     const float* logits_in, float* logits_out, int32_t* topk_idx,
+                     float* topk_w, int32_t* sel_count, float* prob_mean, float* aux,
+                     void* ws, size_t ws_bytes);
+
+/*
+ * moe_dispatch -- capacity clipping and permutation of tokens by expert.
+ * For each expert e the assignments (t, j) with topk_idx[t][j] == e are taken in
+ * increasing token order; the first `capacity` are kept and the rest dropped
+ * ([MoE-2pct] §4.2 keeps the first capacity tokens of an expert; [MoE-overview]
+ * §2.3.2 drops the overflow).  Kept assignments are laid out expert-major, token-
+ * ascending inside an expert:
+ *   expert_offsets [E+1] int32: exclusive prefix sum of the kept counts
+ *   row_token      [N*k] int32: token of permuted row r (rows >= expert_offsets[E]
+ *                  are left untouched)
+ *   slot_row       [N][k] int32: permuted row of (t, j), or -1 if it was dropped
+ *   kept_count     [E] int32 or NULL, n_dropped [1] int32 or NULL
+ *   x_perm         [N*k][d] (x_dtype) or NULL: x_perm[r] = x[row_token[r]]
+ * capacity < 0 means no limit; capacity == 0 drops every assignment (use
+ * moe_capacity to derive it from a capacity factor).
+ * x may be NULL when x_perm is NULL.  d % 8 == 0 for bf16, d % 4 == 0 for float32.
+ * ws: at least moe_dispatch_workspace_size(N, k, E) bytes.
+ */
+size_t moe_dispatch_workspace_size(int64_t n_tokens, int32_t k, int32_t n_experts);
+moe_status moe_dispatch(void* stream, const int32_t* topk_idx, int64_t n_tokens, int32_t k,
+                        int32_t n_experts, int64_t capacity, const void* x, moe_dtype x_dtype,
+                        int64_t d_model, int32_t* expert_offsets, int32_t* row_token,
+                        int32_t* slot_row, int32_t* kept_count, int32_t* n_dropped,
+                        void* x_perm, void* ws, size_t ws_bytes);
+
+/*
+ * moe_expert_ffn -- the expert networks over variable-length row segments (one grouped
+ * launch per layer of the experts).  Segment s covers rows seg_offsets[s] ..
+ * seg_offsets[s+1]-1 of a, h and y and uses expert s's weights:
+ *   GELU   ([Why-MoE] §2.1 and its MoELayer listing):
+ *          h = GELU(a W1^T + b1), y = h W2^T + b2, GELU(u) = u * Phi(u) (exact erf form)
+ *   SwiGLU ([MoE-2pct] §3.2):  h = SiLU(a W1^T) * (a W3^T), y = h W2^T (+ b2)
+ * Arguments
+ *   dtype        MOE_BF16 (bf16 data, float32 accumulation, bf16 h and y) or MOE_F32.
+ *   a            [rows][d]; rows = seg_offsets[S] (read on the device).
+ *   seg_offsets  [S+1] int32 DEVICE array, non-decreasing, seg_offsets[0] == 0,
+ *                seg_offsets[S] <= max_rows.  1 <= S <= MOE_MAX_EXPERTS.
+ *   max_rows     upper bound on seg_offsets[S] (sizes the launch; no row beyond it is
+ *                touched).
+ *   d, d_ff      bf16: both multiples of 64.  float32: both multiples of 4.
+ *   w1 [S][d_ff][d]; w3 [S][d_ff][d] (SwiGLU only, else NULL); b1 [S][d_ff] or NULL;
+ *   w2 [S][d][d_ff]; b2 [S][d] or NULL.  All in `dtype`.
+ *   h  [max_rows][d_ff] and y [max_rows][d] in `dtype` (outputs).
+ */
+moe_status moe_expert_ffn(void* stream, moe_dtype dtype, moe_act act, const void* a,
+                          const int32_t* seg_offsets, int32_t n_segments, int64_t max_rows,
+                          int64_t d_model, int64_t d_ff, const void* w1, const void* w3,
+                          const void* b1, const void* w2, const void* b2, void* h, void* y);
+
+/*
+ * moe_combine -- routing-weighted sum of the expert rows back into token order
+ * ([Why-MoE] §2.1: y = sum_i g_i(x) Expert_i(x); [DeepSeek-V2] §2.3: shared experts
+ * add their unweighted output).
+ *   out[t] = shared_y[t] + sum_{j=0..k-1, slot_row[t][j] >= 0} topk_w[t][j] * y_rows[slot_row[t][j]]
+ * accumulated in float32 in exactly that order (shared first, then j ascending); a
+ * token with every slot dropped and no shared output gets 0.
+ *   y_rows [*][d], shared_y [N][d] or NULL, out [N][d], all in `dtype`.
+ *   slot_row [N][k] int32, topk_w [N][k] float32.
+ */
+moe_status moe_combine(void* stream, moe_dtype dtype, const void* y_rows,
+                       const int32_t* slot_row, const float* topk_w, int64_t n_tokens,
+                       int32_t k, int64_t d_model, const void* shared_y, void* out);
+
+/* Whole-layer configuration and weights for moe_forward. */
+typedef struct {
+  int64_t n_tokens;       /* N >= 0 */
+  int64_t d_model;        /* d */
+  int64_t d_ff;           /* hidden width of every expert, routed and shared */
+  int32_t n_experts;      /* routed experts E */
+  int32_t top_k;          /* k */
+  int32_t n_shared;       /* always-on shared experts (0..8) */
+  int32_t renormalize;    /* 1: divide the k weights by their sum */
+  moe_act act;
+  moe_dtype dtype;        /* x, expert weights, intermediates and output */
+  double capacity_factor; /* alpha; <= 0 means no capacity limit */
+} moe_config;
+
+typedef struct {
+  const float* w_router;   /* [d][E] float32 */
+  const float* logit_bias; /* [E] float32 or NULL */
+  const void* w1;          /* [E][d_ff][d] */
+  const void* w3;          /* [E][d_ff][d], SwiGLU only */
+  const void* b1;          /* [E][d_ff] or NULL */
+  const void* w2;          /* [E][d][d_ff] */
+  const void* b2;          /* [E][d] or NULL */
+  const void* shared_w1;   /* [n_shared][d_ff][d] */
+  const void* shared_w3;   /* [n_shared][d_ff][d], SwiGLU only */
+  const void* shared_w2;   /* [n_shared][d][d_ff] */
+} moe_weights;
+
+/* Number of optional stage markers of moe_forward (see moe_stats.stage_events). */
+#define MOE_N_STAGE_EVENTS 7
+
+/* Optional device outputs of moe_forward; every field may be NULL. */
+typedef struct {
+  float* logits;           /* [N][E] */
+  int32_t* topk_idx;       /* [N][k] */
+  float* topk_w;           /* [N][k] */
+  int32_t* sel_count;      /* [E] */
+  float* prob_mean;        /* [E] */
+  float* aux;              /* [1] */
+  int32_t* kept_count;     /* [E] */
+  int32_t* n_dropped;      /* [1] */
+  int32_t* expert_offsets; /* [E+1] */
+  int32_t* slot_row;       /* [N][k] */
+  /* Timing markers (hipEvent_t handles owned by the caller, or NULL): stage_events[i]
+   * is recorded on the stream at boundary i -- 0 before routing, 1 after routing and
+   * its statistics, 2 after dispatch, 3 after the routed first expert layer, 4 after
+   * the routed second expert layer, 5 after the shared experts, 6 after the combine. */
+  void* stage_events[MOE_N_STAGE_EVENTS];
+} moe_stats;
+
+/*
+ * moe_forward -- the whole layer: route, statistics, capacity, dispatch, routed expert
+ * FFNs, shared expert FFNs (every token, weight 1), weighted combine.  Equivalent to
+ * moe_route, moe_capacity, moe_dispatch, moe_expert_ffn and moe_combine in sequence
+ * ([Why-MoE] §3 MoELayer.forward, [DeepSeek-V2] §2.2-§2.3), with every intermediate in
+ * `ws`.  x [N][d] and y [N][d] are in cfg->dtype; y may not alias x.
+ * Supported: bf16 with d % 64 == 0 and d_ff % 64 == 0, or float32 with d % 4 == 0 and
+ * d_ff % 4 == 0; 1 <= k <= min(E, 16); E <= MOE_MAX_EXPERTS.
+ * ws: at least moe_forward_workspace_size(cfg) bytes, 256-byte aligned.
+ */
+size_t moe_forward_workspace_size(const moe_config* cfg);
+moe_status moe_forward(void* stream, const moe_config* cfg, const moe_weights* w,
+                       const void* x, void* y, const moe_stats* out, void* ws,
+                       size_t ws_bytes);
+
+/* Static description of a status code. */
+const char* moe_status_string(moe_status s);
+/* Detail of the last failure on the calling thread ("" if none). */
+const char* moe_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MOE_MI355X_H */

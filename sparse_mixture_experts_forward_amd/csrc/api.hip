@@ -1,0 +1,454 @@
+// C ABI of the MoE forward library: argument checks, workspace layout, and the order
+// of the kernels (include/moe.h documents every entry point).
+
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <functional>
+
+#include "../../include/moe.h"
+#include "kernels.h"
+
+namespace {
+
+thread_local char g_err[512] = "";
+
+moe_status fail(moe_status s, const char* fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(g_err, sizeof(g_err), fmt, ap);
+  va_end(ap);
+  return s;
+}
+
+moe_status hip_check(hipError_t e, const char* what) {
+  if (e == hipSuccess) return MOE_OK;
+  return fail(MOE_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
+}
+
+#define MOE_TRY(expr)                  \
+  do {                                 \
+    const moe_status _s = (expr);      \
+    if (_s != MOE_OK) return _s;       \
+  } while (0)
+
+constexpr size_t kAlign = 256;
+
+size_t align_up(size_t v) { return (v + kAlign - 1) / kAlign * kAlign; }
+
+// Bump allocator over the caller's workspace; with base == nullptr it only measures.
+struct Carve {
+  char* base;
+  size_t used = 0;
+  explicit Carve(void* b) : base(static_cast<char*>(b)) {}
+  template <typename T>
+  T* take(size_t count) {
+    T* p = base ? reinterpret_cast<T*>(base + used) : nullptr;
+    used += align_up(count * sizeof(T));
+    return p;
+  }
+};
+
+size_t elem_size(moe_dtype t) { return t == MOE_BF16 ? 2 : 4; }
+
+bool dtype_ok(moe_dtype t) { return t == MOE_F32 || t == MOE_BF16; }
+
+moe_status check_aligned(const void* p, size_t a, const char* name) {
+  if (reinterpret_cast<uintptr_t>(p) % a != 0)
+    return fail(MOE_ERR_INVALID_ARG, "%s must be %zu-byte aligned", name, a);
+  return MOE_OK;
+}
+
+moe_status check_route_args(const void* x, moe_dtype xt, int64_t n, int64_t d,
+                            const float* wr, int32_t e, int32_t k, const float* logits_in,
+                            const int32_t* idx, const float* w) {
+  if (n < 0) return fail(MOE_ERR_INVALID_ARG, "n_tokens < 0");
+  if (e < 1) return fail(MOE_ERR_INVALID_ARG, "n_experts < 1");
+  if (e > MOE_MAX_EXPERTS) return fail(MOE_ERR_UNSUPPORTED, "n_experts > %d", MOE_MAX_EXPERTS);
+  if (k < 1 || k > e) return fail(MOE_ERR_INVALID_ARG, "need 1 <= k <= n_experts");
+  if (k > 16) return fail(MOE_ERR_UNSUPPORTED, "k > 16");
+  if (!dtype_ok(xt)) return fail(MOE_ERR_INVALID_ARG, "unknown x dtype");
+  if (n > 0) {
+    if (!idx || !w) return fail(MOE_ERR_INVALID_ARG, "topk_idx and topk_w are required");
+    if (!logits_in) {
+      if (!x || !wr) return fail(MOE_ERR_INVALID_ARG, "x and w_router are required");
+      if (d < 4 || d % 4 != 0) return fail(MOE_ERR_UNSUPPORTED, "d_model must be a positive multiple of 4");
+      MOE_TRY(check_aligned(x, 8, "x"));
+    }
+  }
+  if (n * static_cast<int64_t>(k) > INT32_MAX || n * static_cast<int64_t>(e) > INT32_MAX)
+    return fail(MOE_ERR_UNSUPPORTED, "n_tokens too large");
+  return MOE_OK;
+}
+
+size_t route_ws(int64_t n, int32_t e) {
+  Carve c(nullptr);
+  const int64_t b = moe::route_blocks(n);
+  c.take<float>(b * e);
+  c.take<int32_t>(b * e);
+  return c.used;
+}
+
+size_t dispatch_ws(int64_t n, int32_t k, int32_t e) {
+  Carve c(nullptr);
+  const moe::DispatchGrid g = moe::dispatch_grid(n, k);
+  c.take<int32_t>(g.n_blocks * e);
+  c.take<int32_t>(g.n_blocks * e);
+  return c.used;
+}
+
+moe_status run_route(hipStream_t st, const void* x, moe_dtype xt, int64_t n, int64_t d,
+                     const float* wr, const float* bias, int32_t e, int32_t k, int32_t renorm,
+                     const float* logits_in, float* logits_out, int32_t* idx, float* w,
+                     int32_t* sel, float* pm, float* aux, void* ws) {
+  Carve c(ws);
+  const int64_t b = moe::route_blocks(n);
+  float* pp = c.take<float>(b * e);
+  int32_t* pc = c.take<int32_t>(b * e);
+  MOE_TRY(hip_check(moe::launch_route(st, x, xt == MOE_BF16, n, d, wr, bias, e, k, renorm,
+                                      logits_in, logits_out, idx, w, pp, pc),
+                    "router kernel launch"));
+  return hip_check(moe::launch_route_finalize(st, pp, pc, b, n, e, k, sel, pm, aux),
+                   "router statistics launch");
+}
+
+moe_status run_dispatch(hipStream_t st, const int32_t* idx, int64_t n, int32_t k, int32_t e,
+                        int64_t cap, const void* x, int64_t row_bytes, int32_t* offsets,
+                        int32_t* row_token, int32_t* slot_row, int32_t* kept, int32_t* dropped,
+                        void* x_perm, void* ws) {
+  Carve c(ws);
+  const moe::DispatchGrid g = moe::dispatch_grid(n, k);
+  int32_t* hist = c.take<int32_t>(g.n_blocks * e);
+  int32_t* base = c.take<int32_t>(g.n_blocks * e);
+  return hip_check(moe::launch_dispatch(st, idx, n, k, e, cap, x, row_bytes, offsets, row_token,
+                                        slot_row, kept, dropped, x_perm, hist, base),
+                   "dispatch kernels launch");
+}
+
+moe_status check_ffn_shape(moe_dtype dt, moe_act act, int64_t d, int64_t d_ff) {
+  if (!dtype_ok(dt)) return fail(MOE_ERR_INVALID_ARG, "unknown dtype");
+  if (act != MOE_ACT_GELU && act != MOE_ACT_SWIGLU) return fail(MOE_ERR_INVALID_ARG, "unknown activation");
+  if (d <= 0 || d_ff <= 0) return fail(MOE_ERR_INVALID_ARG, "d_model and d_ff must be positive");
+  const int64_t q = dt == MOE_BF16 ? 64 : 4;
+  if (d % q != 0 || d_ff % q != 0)
+    return fail(MOE_ERR_UNSUPPORTED, "d_model and d_ff must be multiples of %lld for this dtype",
+                static_cast<long long>(q));
+  if (d > (1 << 20) || d_ff > (1 << 20)) return fail(MOE_ERR_UNSUPPORTED, "d_model or d_ff too large");
+  return MOE_OK;
+}
+
+// The two grouped products of one FFN layer of experts.
+moe_status run_ffn(hipStream_t st, moe_dtype dt, moe_act act, const void* a, int64_t lda,
+                   const int32_t* seg_off, int32_t n_seg, int32_t single_rows, int64_t max_rows,
+                   int64_t d, int64_t d_ff, const void* w1, const void* w3, const void* b1,
+                   int64_t w_seg_stride, const void* w2, const void* b2, int64_t w2_kchunk,
+                   int64_t w2_kbatch_stride, void* h, void* y,
+                   const std::function<moe_status()>& between = nullptr) {
+  const bool bf = dt == MOE_BF16;
+  moe::GemmArgs g1{};
+  g1.a = a; g1.lda = lda;
+  g1.b0 = w1; g1.b1 = (act == MOE_ACT_SWIGLU) ? w3 : nullptr;
+  g1.ldb = d; g1.b_seg_stride = w_seg_stride;
+  g1.kchunk = d; g1.kbatch_stride = 0;
+  g1.bias = (act == MOE_ACT_GELU) ? b1 : nullptr; g1.bias_seg_stride = d_ff;
+  g1.c = h; g1.ldc = d_ff;
+  g1.seg_off = seg_off; g1.n_seg = n_seg; g1.single_rows = single_rows;
+  g1.n_out = static_cast<int32_t>(d_ff); g1.k = static_cast<int32_t>(d);
+  MOE_TRY(hip_check(moe::launch_gemm(st, bf, act == MOE_ACT_SWIGLU ? moe::EPI_SWIGLU : moe::EPI_GELU,
+                                     g1, max_rows),
+                    "expert GEMM1 launch"));
+  if (between) MOE_TRY(between());
+  moe::GemmArgs g2{};
+  g2.a = h; g2.lda = d_ff;
+  g2.b0 = w2; g2.b1 = nullptr;
+  g2.ldb = w2_kchunk; g2.b_seg_stride = w_seg_stride;
+  g2.kchunk = w2_kchunk; g2.kbatch_stride = w2_kbatch_stride;
+  g2.bias = b2; g2.bias_seg_stride = d;
+  g2.c = y; g2.ldc = d;
+  g2.seg_off = seg_off; g2.n_seg = n_seg; g2.single_rows = single_rows;
+  g2.n_out = static_cast<int32_t>(d); g2.k = static_cast<int32_t>(d_ff);
+  return hip_check(moe::launch_gemm(st, bf, moe::EPI_NONE, g2, max_rows), "expert GEMM2 launch");
+}
+
+int64_t capacity_of(int64_t n, int32_t e, int32_t k, double alpha) {
+  if (!(alpha > 0.0)) return -1;
+  const int64_t base = (static_cast<int64_t>(k) * n) / e;
+  return static_cast<int64_t>(std::floor(static_cast<double>(base) * alpha));
+}
+
+int64_t max_rows_of(int64_t n, int32_t e, int32_t k, int64_t cap) {
+  const int64_t all = n * k;
+  if (cap < 0) return all;
+  const int64_t lim = cap * e;
+  return lim < all ? lim : all;
+}
+
+struct ForwardLayout {
+  int32_t *idx, *sel, *offsets, *row_token, *slot_row, *kept, *dropped;
+  float *w, *pm, *aux;
+  void *route_ws, *dispatch_ws, *x_perm, *h, *y_rows, *h_sh, *y_sh;
+  size_t used;
+};
+
+ForwardLayout forward_layout(const moe_config& c, void* ws) {
+  Carve cv(ws);
+  ForwardLayout L{};
+  const int64_t n = c.n_tokens, nk = c.n_tokens * c.top_k;
+  const int32_t e = c.n_experts;
+  const size_t es = elem_size(c.dtype);
+  const int64_t cap = capacity_of(n, e, c.top_k, c.capacity_factor);
+  const int64_t R = max_rows_of(n, e, c.top_k, cap);
+  L.idx = cv.take<int32_t>(nk);
+  L.w = cv.take<float>(nk);
+  L.sel = cv.take<int32_t>(e);
+  L.pm = cv.take<float>(e);
+  L.aux = cv.take<float>(1);
+  L.offsets = cv.take<int32_t>(e + 1);
+  L.row_token = cv.take<int32_t>(nk);
+  L.slot_row = cv.take<int32_t>(nk);
+  L.kept = cv.take<int32_t>(e);
+  L.dropped = cv.take<int32_t>(1);
+  L.route_ws = cv.take<char>(route_ws(n, e));
+  L.dispatch_ws = cv.take<char>(dispatch_ws(n, c.top_k, e));
+  L.x_perm = cv.take<char>(R * c.d_model * es);
+  L.h = cv.take<char>(R * c.d_ff * es);
+  L.y_rows = cv.take<char>(R * c.d_model * es);
+  if (c.n_shared > 0) {
+    L.h_sh = cv.take<char>(n * c.n_shared * c.d_ff * es);
+    L.y_sh = cv.take<char>(n * c.d_model * es);
+  }
+  L.used = cv.used;
+  return L;
+}
+
+moe_status check_config(const moe_config* c) {
+  if (!c) return fail(MOE_ERR_INVALID_ARG, "cfg is NULL");
+  if (c->n_tokens < 0) return fail(MOE_ERR_INVALID_ARG, "n_tokens < 0");
+  if (c->n_experts < 1) return fail(MOE_ERR_INVALID_ARG, "n_experts < 1");
+  if (c->n_experts > MOE_MAX_EXPERTS) return fail(MOE_ERR_UNSUPPORTED, "n_experts > %d", MOE_MAX_EXPERTS);
+  if (c->top_k < 1 || c->top_k > c->n_experts) return fail(MOE_ERR_INVALID_ARG, "need 1 <= top_k <= n_experts");
+  if (c->top_k > 16) return fail(MOE_ERR_UNSUPPORTED, "top_k > 16");
+  if (c->n_shared < 0 || c->n_shared > 8) return fail(MOE_ERR_UNSUPPORTED, "n_shared must be 0..8");
+  MOE_TRY(check_ffn_shape(c->dtype, c->act, c->d_model, c->d_ff));
+  if (c->n_tokens * static_cast<int64_t>(c->top_k) > INT32_MAX / 2)
+    return fail(MOE_ERR_UNSUPPORTED, "n_tokens * top_k too large");
+  if (c->n_tokens * static_cast<int64_t>(c->n_shared) * c->d_ff > INT32_MAX)
+    return fail(MOE_ERR_UNSUPPORTED, "shared hidden activations too large");
+  return MOE_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* moe_last_error(void) { return g_err; }
+
+const char* moe_status_string(moe_status s) {
+  switch (s) {
+    case MOE_OK: return "ok";
+    case MOE_ERR_INVALID_ARG: return "invalid argument";
+    case MOE_ERR_UNSUPPORTED: return "unsupported shape or type";
+    case MOE_ERR_WORKSPACE: return "workspace too small";
+    case MOE_ERR_HIP: return "HIP runtime error";
+  }
+  return "unknown status";
+}
+
+int64_t moe_capacity(int64_t n_tokens, int32_t n_experts, int32_t k, double alpha) {
+  if (n_tokens < 0 || n_experts < 1 || k < 1) {
+    fail(MOE_ERR_INVALID_ARG, "moe_capacity: need n_tokens >= 0, n_experts >= 1, k >= 1");
+    return -1;
+  }
+  return capacity_of(n_tokens, n_experts, k, alpha);
+}
+
+size_t moe_route_workspace_size(int64_t n_tokens, int32_t n_experts) {
+  if (n_tokens < 0 || n_experts < 1) return 0;
+  return route_ws(n_tokens, n_experts);
+}
+
+moe_status moe_route(void* stream, const void* x, moe_dtype x_dtype, int64_t n_tokens,
+                     int64_t d_model, const float* w_router, const float* logit_bias,
+                     int32_t n_experts, int32_t k, int32_t renormalize,
+                     const float* logits_in, float* logits_out, int32_t* topk_idx,
+                     float* topk_w, int32_t* sel_count, float* prob_mean, float* aux,
+                     void* ws, size_t ws_bytes) {
+  MOE_TRY(check_route_args(x, x_dtype, n_tokens, d_model, w_router, n_experts, k, logits_in,
+                           topk_idx, topk_w));
+  const size_t need = route_ws(n_tokens, n_experts);
+  if (ws_bytes < need) return fail(MOE_ERR_WORKSPACE, "moe_route needs %zu workspace bytes", need);
+  if (need > 0) {
+    if (!ws) return fail(MOE_ERR_INVALID_ARG, "ws is NULL");
+    MOE_TRY(check_aligned(ws, kAlign, "ws"));
+  }
+  return run_route(static_cast<hipStream_t>(stream), x, x_dtype, n_tokens, d_model, w_router,
+                   logit_bias, n_experts, k, renormalize ? 1 : 0, logits_in, logits_out,
+                   topk_idx, topk_w, sel_count, prob_mean, aux, ws);
+}
+
+size_t moe_dispatch_workspace_size(int64_t n_tokens, int32_t k, int32_t n_experts) {
+  if (n_tokens < 0 || k < 1 || n_experts < 1) return 0;
+  return dispatch_ws(n_tokens, k, n_experts);
+}
+
+moe_status moe_dispatch(void* stream, const int32_t* topk_idx, int64_t n_tokens, int32_t k,
+                        int32_t n_experts, int64_t capacity, const void* x, moe_dtype x_dtype,
+                        int64_t d_model, int32_t* expert_offsets, int32_t* row_token,
+                        int32_t* slot_row, int32_t* kept_count, int32_t* n_dropped,
+                        void* x_perm, void* ws, size_t ws_bytes) {
+  if (n_tokens < 0) return fail(MOE_ERR_INVALID_ARG, "n_tokens < 0");
+  if (n_experts < 1) return fail(MOE_ERR_INVALID_ARG, "n_experts < 1");
+  if (n_experts > MOE_MAX_EXPERTS) return fail(MOE_ERR_UNSUPPORTED, "n_experts > %d", MOE_MAX_EXPERTS);
+  if (k < 1 || k > n_experts) return fail(MOE_ERR_INVALID_ARG, "need 1 <= k <= n_experts");
+  if (k > 16) return fail(MOE_ERR_UNSUPPORTED, "k > 16");
+  if (!expert_offsets) return fail(MOE_ERR_INVALID_ARG, "expert_offsets is required");
+  if (n_tokens * static_cast<int64_t>(k) > INT32_MAX / 2) return fail(MOE_ERR_UNSUPPORTED, "n_tokens too large");
+  if (n_tokens > 0 && (!topk_idx || !row_token || !slot_row))
+    return fail(MOE_ERR_INVALID_ARG, "topk_idx, row_token and slot_row are required");
+  int64_t row_bytes = 0;
+  if (x_perm) {
+    if (!dtype_ok(x_dtype)) return fail(MOE_ERR_INVALID_ARG, "unknown x dtype");
+    if (!x) return fail(MOE_ERR_INVALID_ARG, "x is required when x_perm is given");
+    row_bytes = d_model * static_cast<int64_t>(elem_size(x_dtype));
+    if (d_model <= 0 || row_bytes % 16 != 0)
+      return fail(MOE_ERR_UNSUPPORTED, "x rows must be a positive multiple of 16 bytes");
+    MOE_TRY(check_aligned(x, 16, "x"));
+    MOE_TRY(check_aligned(x_perm, 16, "x_perm"));
+  }
+  const size_t need = dispatch_ws(n_tokens, k, n_experts);
+  if (ws_bytes < need) return fail(MOE_ERR_WORKSPACE, "moe_dispatch needs %zu workspace bytes", need);
+  if (need > 0) {
+    if (!ws) return fail(MOE_ERR_INVALID_ARG, "ws is NULL");
+    MOE_TRY(check_aligned(ws, kAlign, "ws"));
+  }
+  return run_dispatch(static_cast<hipStream_t>(stream), topk_idx, n_tokens, k, n_experts,
+                      capacity, x, row_bytes, expert_offsets, row_token, slot_row, kept_count,
+                      n_dropped, x_perm, ws);
+}
+
+moe_status moe_expert_ffn(void* stream, moe_dtype dtype, moe_act act, const void* a,
+                          const int32_t* seg_offsets, int32_t n_segments, int64_t max_rows,
+                          int64_t d_model, int64_t d_ff, const void* w1, const void* w3,
+                          const void* b1, const void* w2, const void* b2, void* h, void* y) {
+  MOE_TRY(check_ffn_shape(dtype, act, d_model, d_ff));
+  if (n_segments < 1) return fail(MOE_ERR_INVALID_ARG, "n_segments < 1");
+  if (n_segments > MOE_MAX_EXPERTS) return fail(MOE_ERR_UNSUPPORTED, "n_segments > %d", MOE_MAX_EXPERTS);
+  if (max_rows < 0) return fail(MOE_ERR_INVALID_ARG, "max_rows < 0");
+  if (max_rows > INT32_MAX / 2) return fail(MOE_ERR_UNSUPPORTED, "max_rows too large");
+  if (max_rows == 0) return MOE_OK;
+  if (!a || !seg_offsets || !w1 || !w2 || !h || !y)
+    return fail(MOE_ERR_INVALID_ARG, "a, seg_offsets, w1, w2, h and y are required");
+  if (act == MOE_ACT_SWIGLU && !w3) return fail(MOE_ERR_INVALID_ARG, "SwiGLU needs w3");
+  MOE_TRY(check_aligned(a, 16, "a"));
+  MOE_TRY(check_aligned(w1, 16, "w1"));
+  MOE_TRY(check_aligned(w2, 16, "w2"));
+  if (w3) MOE_TRY(check_aligned(w3, 16, "w3"));
+  MOE_TRY(check_aligned(h, 16, "h"));
+  MOE_TRY(check_aligned(y, 16, "y"));
+  return run_ffn(static_cast<hipStream_t>(stream), dtype, act, a, d_model, seg_offsets,
+                 n_segments, 0, max_rows, d_model, d_ff, w1, w3, b1, d_ff * d_model, w2, b2,
+                 d_ff, 0, h, y, nullptr);
+}
+
+moe_status moe_combine(void* stream, moe_dtype dtype, const void* y_rows,
+                       const int32_t* slot_row, const float* topk_w, int64_t n_tokens,
+                       int32_t k, int64_t d_model, const void* shared_y, void* out) {
+  if (!dtype_ok(dtype)) return fail(MOE_ERR_INVALID_ARG, "unknown dtype");
+  if (n_tokens < 0) return fail(MOE_ERR_INVALID_ARG, "n_tokens < 0");
+  if (k < 1 || k > 16) return fail(MOE_ERR_INVALID_ARG, "need 1 <= k <= 16");
+  const int64_t vec = dtype == MOE_BF16 ? 8 : 4;
+  if (d_model <= 0 || d_model % vec != 0)
+    return fail(MOE_ERR_UNSUPPORTED, "d_model must be a positive multiple of %lld", static_cast<long long>(vec));
+  if (n_tokens == 0) return MOE_OK;
+  if (!y_rows || !slot_row || !topk_w || !out)
+    return fail(MOE_ERR_INVALID_ARG, "y_rows, slot_row, topk_w and out are required");
+  MOE_TRY(check_aligned(y_rows, 16, "y_rows"));
+  MOE_TRY(check_aligned(out, 16, "out"));
+  if (shared_y) MOE_TRY(check_aligned(shared_y, 16, "shared_y"));
+  return hip_check(moe::launch_combine(static_cast<hipStream_t>(stream), dtype == MOE_BF16, y_rows,
+                                       slot_row, topk_w, n_tokens, k, d_model, shared_y, out),
+                   "combine launch");
+}
+
+size_t moe_forward_workspace_size(const moe_config* cfg) {
+  if (check_config(cfg) != MOE_OK) return 0;
+  return forward_layout(*cfg, nullptr).used;
+}
+
+moe_status moe_forward(void* stream, const moe_config* cfg, const moe_weights* w,
+                       const void* x, void* y, const moe_stats* out, void* ws,
+                       size_t ws_bytes) {
+  MOE_TRY(check_config(cfg));
+  if (!w) return fail(MOE_ERR_INVALID_ARG, "weights are NULL");
+  const moe_config& c = *cfg;
+  const bool swiglu = c.act == MOE_ACT_SWIGLU;
+  if (!w->w_router || !w->w1 || !w->w2 || (swiglu && !w->w3))
+    return fail(MOE_ERR_INVALID_ARG, "w_router, w1, w2 (and w3 for SwiGLU) are required");
+  if (c.n_shared > 0 && (!w->shared_w1 || !w->shared_w2 || (swiglu && !w->shared_w3)))
+    return fail(MOE_ERR_INVALID_ARG, "shared expert weights are required when n_shared > 0");
+  if (c.n_tokens > 0 && (!x || !y)) return fail(MOE_ERR_INVALID_ARG, "x and y are required");
+  if (c.n_tokens > 0 && x == y) return fail(MOE_ERR_INVALID_ARG, "y may not alias x");
+  const ForwardLayout need = forward_layout(c, nullptr);
+  if (ws_bytes < need.used) return fail(MOE_ERR_WORKSPACE, "moe_forward needs %zu workspace bytes", need.used);
+  if (!ws) return fail(MOE_ERR_INVALID_ARG, "ws is NULL");
+  MOE_TRY(check_aligned(ws, kAlign, "ws"));
+  if (c.n_tokens > 0) {
+    MOE_TRY(check_aligned(x, 16, "x"));
+    MOE_TRY(check_aligned(y, 16, "y"));
+  }
+  const void* wptrs[] = {w->w1, w->w2, w->w3, w->shared_w1, w->shared_w2, w->shared_w3};
+  for (const void* p : wptrs)
+    if (p) MOE_TRY(check_aligned(p, 16, "expert weights"));
+
+  static const moe_stats kNoStats{};
+  const moe_stats& o = out ? *out : kNoStats;
+  const ForwardLayout L = forward_layout(c, ws);
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  const int64_t n = c.n_tokens;
+  const int32_t e = c.n_experts, k = c.top_k;
+  const size_t es = elem_size(c.dtype);
+  int32_t* idx = o.topk_idx ? o.topk_idx : L.idx;
+  float* tw = o.topk_w ? o.topk_w : L.w;
+  int32_t* offsets = o.expert_offsets ? o.expert_offsets : L.offsets;
+  int32_t* slot_row = o.slot_row ? o.slot_row : L.slot_row;
+
+  auto mark = [&](int i) -> moe_status {
+    if (!o.stage_events[i]) return MOE_OK;
+    return hip_check(hipEventRecord(static_cast<hipEvent_t>(o.stage_events[i]), st),
+                     "stage event record");
+  };
+  MOE_TRY(mark(0));
+  // a1-a3: router product, gate, statistics
+  MOE_TRY(run_route(st, x, c.dtype, n, c.d_model, w->w_router, w->logit_bias, e, k,
+                    c.renormalize ? 1 : 0, nullptr, o.logits, idx, tw, o.sel_count,
+                    o.prob_mean, o.aux, L.route_ws));
+  MOE_TRY(mark(1));
+  // a4-a5: capacity and permutation
+  const int64_t cap = capacity_of(n, e, k, c.capacity_factor);
+  MOE_TRY(run_dispatch(st, idx, n, k, e, cap, x, c.d_model * static_cast<int64_t>(es), offsets,
+                       L.row_token, slot_row, o.kept_count, o.n_dropped, L.x_perm,
+                       L.dispatch_ws));
+  MOE_TRY(mark(2));
+  const int64_t R = max_rows_of(n, e, k, cap);
+  // a6-a7: routed experts over the expert-major segments
+  MOE_TRY(run_ffn(st, c.dtype, c.act, L.x_perm, c.d_model, offsets, e, 0, R, c.d_model, c.d_ff,
+                  w->w1, w->w3, w->b1, c.d_ff * c.d_model, w->w2, w->b2, c.d_ff, 0, L.h,
+                  L.y_rows, [&]() { return mark(3); }));
+  MOE_TRY(mark(4));
+  // a8: shared experts, all tokens; the S experts act as one FFN of width S*d_ff (W1/W3
+  // rows concatenate, W2 splits its reduction into S chunks of d_ff)
+  if (c.n_shared > 0) {
+    const int64_t dffs = c.d_ff * c.n_shared;
+    MOE_TRY(run_ffn(st, c.dtype, c.act, x, c.d_model, nullptr, 1, static_cast<int32_t>(n), n,
+                    c.d_model, dffs, w->shared_w1, w->shared_w3, nullptr, 0, w->shared_w2,
+                    nullptr, c.d_ff, c.d_model * c.d_ff, L.h_sh, L.y_sh, nullptr));
+  }
+  MOE_TRY(mark(5));
+  // a9: weighted combine (shared first, then slots in order)
+  MOE_TRY(hip_check(moe::launch_combine(st, c.dtype == MOE_BF16, L.y_rows, slot_row, tw, n, k,
+                                        c.d_model, c.n_shared > 0 ? L.y_sh : nullptr, y),
+                    "combine launch"));
+  return mark(6);
+}
+
+}  // extern "C"

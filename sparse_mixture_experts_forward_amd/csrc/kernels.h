@@ -1,0 +1,75 @@
+// Host-side launchers of the MoE kernels (internal to the library; the public C ABI
+// is include/moe.h).  Each returns hipSuccess or the launch error.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace moe {
+
+// ---------------------------------------------------------------- router
+constexpr int kRouteTokens = 16;  // tokens per router workgroup
+
+inline int64_t route_blocks(int64_t n_tokens) {
+  return (n_tokens + kRouteTokens - 1) / kRouteTokens;
+}
+
+hipError_t launch_route(hipStream_t st, const void* x, bool x_bf16, int64_t n, int64_t d,
+                        const float* w_router, const float* logit_bias, int e, int k,
+                        int renorm, const float* logits_in, float* logits_out,
+                        int32_t* topk_idx, float* topk_w, float* part_prob,
+                        int32_t* part_cnt);
+
+hipError_t launch_route_finalize(hipStream_t st, const float* part_prob,
+                                 const int32_t* part_cnt, int64_t n_blocks, int64_t n,
+                                 int e, int k, int32_t* sel_count, float* prob_mean,
+                                 float* aux);
+
+// ---------------------------------------------------------------- dispatch
+struct DispatchGrid {
+  int64_t tokens_per_block;
+  int64_t n_blocks;
+};
+DispatchGrid dispatch_grid(int64_t n_tokens, int32_t k);
+
+hipError_t launch_dispatch(hipStream_t st, const int32_t* topk_idx, int64_t n, int k, int e,
+                           int64_t capacity, const void* x, int64_t row_bytes,
+                           int32_t* expert_offsets, int32_t* row_token, int32_t* slot_row,
+                           int32_t* kept_count, int32_t* n_dropped, void* x_perm,
+                           int32_t* blk_hist, int32_t* blk_base);
+
+// ---------------------------------------------------------------- grouped GEMM
+enum Epilogue { EPI_NONE = 0, EPI_GELU = 1, EPI_SWIGLU = 2 };
+
+// One grouped product C[rows][n_out] = epi(A[rows][K] * B_s^T) over the segments of
+// seg_off (or one segment of single_rows rows when seg_off is null).
+struct GemmArgs {
+  const void* a;
+  int64_t lda;
+  const void* b0;        // [S][n_out][ldb] (W1 or W2)
+  const void* b1;        // W3 for SwiGLU, else null
+  int64_t ldb;           // row stride of B (elements)
+  int64_t b_seg_stride;  // elements between segments' weights
+  int64_t kchunk;        // K elements per B batch (== K unless K is split over batches)
+  int64_t kbatch_stride; // elements between K batches
+  const void* bias;      // [S][n_out] or null
+  int64_t bias_seg_stride;
+  void* c;
+  int64_t ldc;
+  const int32_t* seg_off;
+  int32_t n_seg;
+  int32_t single_rows;
+  int32_t max_rows;  // rows of A and C; segment bounds are clamped to [0, max_rows]
+  int32_t n_out;  // output columns (h columns for SwiGLU)
+  int32_t k;      // reduction length
+};
+
+hipError_t launch_gemm(hipStream_t st, bool bf16, Epilogue epi, const GemmArgs& g,
+                       int64_t max_rows);
+
+// ---------------------------------------------------------------- combine
+hipError_t launch_combine(hipStream_t st, bool bf16, const void* y_rows,
+                          const int32_t* slot_row, const float* topk_w, int64_t n, int k,
+                          int64_t d, const void* shared_y, void* out);
+
+}  // namespace moe

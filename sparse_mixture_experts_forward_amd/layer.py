@@ -1,0 +1,142 @@
+"""Torch-facing wrappers: allocate outputs and workspaces with torch, then call the
+C entry points through the binding.  Torch supplies device memory and the stream
+only; every step of the layer runs in the HIP library."""
+from __future__ import annotations
+
+from typing import Optional
+
+import torch
+
+from . import _binding as B
+from .configs import MoEConfig
+
+
+def workspace(nbytes: int, device) -> Optional[torch.Tensor]:
+    """Device workspace (torch's caching allocator returns 512-byte aligned blocks)."""
+    if nbytes <= 0:
+        return None
+    return torch.empty(nbytes, dtype=torch.uint8, device=device)
+
+
+def _act(name: str) -> int:
+    return B.MOE_ACT_SWIGLU if name == "swiglu" else B.MOE_ACT_GELU
+
+
+class MoELayer:
+    """A routed MoE FFN layer whose weights live on the GPU.
+
+    weights: dict with w_router [d][E] float32, optional logit_bias [E] float32,
+    w1/w3 [E][d_ff][d], w2 [E][d][d_ff], optional b1 [E][d_ff] / b2 [E][d], and for
+    shared experts shared_w1/shared_w3 [S][d_ff][d], shared_w2 [S][d][d_ff].
+    """
+
+    def __init__(self, cfg: MoEConfig, weights: dict):
+        self.cfg = cfg
+        self.w = {k: v for k, v in weights.items() if v is not None}
+        self.device = self.w["w1"].device
+        self._ws = None
+        self._ws_key = None
+
+    @classmethod
+    def from_inputs(cls, inp) -> "MoELayer":
+        """Build from a synth.DeviceInputs."""
+        w = dict(w_router=inp.w_router, logit_bias=inp.logit_bias, w1=inp.w1, w3=inp.w3,
+                 b1=inp.b1, w2=inp.w2, b2=inp.b2, shared_w1=inp.sw1, shared_w3=inp.sw3,
+                 shared_w2=inp.sw2)
+        return cls(inp.cfg, w)
+
+    def config_c(self, n_tokens: int) -> B.MoEConfigC:
+        c = self.cfg
+        return B.make_config(n_tokens, c.d_model, c.d_ff, c.n_experts, c.top_k, _act(c.act),
+                             B.MOE_BF16 if c.dtype == "bf16" else B.MOE_F32,
+                             c.alpha or 0.0, c.n_shared, c.renormalize)
+
+    def capacity(self, n_tokens: int) -> int:
+        c = self.cfg
+        return B.moe_capacity(n_tokens, c.n_experts, c.top_k, c.alpha or 0.0)
+
+    def _workspace(self, n_tokens: int) -> Optional[torch.Tensor]:
+        if self._ws_key != n_tokens:
+            self._ws = workspace(B.moe_forward_workspace_size(self.config_c(n_tokens)),
+                                 self.device)
+            self._ws_key = n_tokens
+        return self._ws
+
+    def new_stats(self, n_tokens: int) -> dict:
+        c, dev = self.cfg, self.device
+        i32, f32 = torch.int32, torch.float32
+        return dict(
+            logits=torch.empty((n_tokens, c.n_experts), dtype=f32, device=dev),
+            topk_idx=torch.empty((n_tokens, c.top_k), dtype=i32, device=dev),
+            topk_w=torch.empty((n_tokens, c.top_k), dtype=f32, device=dev),
+            sel_count=torch.empty(c.n_experts, dtype=i32, device=dev),
+            prob_mean=torch.empty(c.n_experts, dtype=f32, device=dev),
+            aux=torch.empty(1, dtype=f32, device=dev),
+            kept_count=torch.empty(c.n_experts, dtype=i32, device=dev),
+            n_dropped=torch.empty(1, dtype=i32, device=dev),
+            expert_offsets=torch.empty(c.n_experts + 1, dtype=i32, device=dev),
+            slot_row=torch.empty((n_tokens, c.top_k), dtype=i32, device=dev))
+
+    def forward(self, x: torch.Tensor, y: Optional[torch.Tensor] = None,
+                stats: Optional[dict] = None, stream=None, stage_events=None) -> torch.Tensor:
+        n = x.shape[0]
+        if y is None:
+            y = torch.empty_like(x)
+        B.moe_forward(self.config_c(n), self.w, x, y, self._workspace(n), stats, stream,
+                      stage_events)
+        return y
+
+    __call__ = forward
+
+    # ---------------------------------------------------------------- staged calls
+    def route(self, x: Optional[torch.Tensor], logits_in: Optional[torch.Tensor] = None,
+              n_tokens: Optional[int] = None, stream=None) -> dict:
+        c = self.cfg
+        n = n_tokens if n_tokens is not None else (x if x is not None else logits_in).shape[0]
+        s = self.new_stats(n)
+        ws = workspace(B.moe_route_workspace_size(n, c.n_experts), self.device)
+        B.moe_route(x, self.w["w_router"] if x is not None else None, self.w.get("logit_bias"),
+                    c.n_experts, c.top_k, c.renormalize, logits_in,
+                    s["logits"] if logits_in is None else None, s["topk_idx"], s["topk_w"],
+                    s["sel_count"], s["prob_mean"], s["aux"], ws, n_tokens=n, stream=stream)
+        return s
+
+    def dispatch(self, x: torch.Tensor, topk_idx: torch.Tensor, capacity: Optional[int] = None,
+                 with_copy: bool = True, stream=None) -> dict:
+        c = self.cfg
+        n, k = topk_idx.shape
+        cap = self.capacity(n) if capacity is None else capacity
+        dev = self.device
+        out = dict(expert_offsets=torch.empty(c.n_experts + 1, dtype=torch.int32, device=dev),
+                   row_token=torch.full((max(n * k, 1),), -7, dtype=torch.int32, device=dev),
+                   slot_row=torch.empty((n, k), dtype=torch.int32, device=dev),
+                   kept_count=torch.empty(c.n_experts, dtype=torch.int32, device=dev),
+                   n_dropped=torch.empty(1, dtype=torch.int32, device=dev),
+                   x_perm=(torch.zeros((max(n * k, 1), x.shape[1]), dtype=x.dtype, device=dev)
+                           if with_copy else None))
+        ws = workspace(B.moe_dispatch_workspace_size(n, k, c.n_experts), dev)
+        B.moe_dispatch(topk_idx, c.n_experts, cap, x if with_copy else None,
+                       out["expert_offsets"], out["row_token"], out["slot_row"],
+                       out["kept_count"], out["n_dropped"], out["x_perm"], ws, stream=stream)
+        return out
+
+    def expert_ffn(self, a: torch.Tensor, seg_offsets: torch.Tensor, max_rows: int,
+                   shared: bool = False, stream=None):
+        c = self.cfg
+        p = "shared_" if shared else ""
+        w1, w2 = self.w[p + "w1"], self.w[p + "w2"]
+        w3 = self.w.get(p + "w3")
+        b1 = None if shared else self.w.get("b1")
+        b2 = None if shared else self.w.get("b2")
+        rows = max(max_rows, 1)
+        h = torch.empty((rows, c.d_ff), dtype=a.dtype, device=a.device)
+        y = torch.empty((rows, c.d_model), dtype=a.dtype, device=a.device)
+        B.moe_expert_ffn(_act(c.act), a, seg_offsets, w1.shape[0], max_rows, w1, w3, b1, w2,
+                         b2, h, y, stream=stream)
+        return h, y
+
+    def combine(self, y_rows, slot_row, topk_w, shared_y=None, stream=None):
+        n = slot_row.shape[0]
+        out = torch.empty((n, self.cfg.d_model), dtype=y_rows.dtype, device=y_rows.device)
+        B.moe_combine(y_rows, slot_row, topk_w, shared_y, out, stream=stream)
+        return out

@@ -1,0 +1,110 @@
+"""The C-ABI library: it loads, exports every entry point include/moe.h declares, and its
+host-side logic (argument checks, capacity, workspace sizes) behaves as documented.
+No call here reaches the GPU: every call either is host-only or fails validation."""
+import ctypes as C
+import os
+import re
+
+import pytest
+
+from sparse_mixture_experts_forward_amd import _binding as B
+
+import oracle as O
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "moe.h")
+
+pytestmark = pytest.mark.skipif(not os.path.exists(B.LIB_PATH),
+                                reason="library not built (run the package build)")
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    names = re.findall(r"^\s*(?:const\s+)?[a-z_0-9]+\s*\*?\s*(moe_[a-z_]+)\s*\(", text, flags=re.M)
+    return sorted(set(names))
+
+
+def test_every_declared_symbol_is_exported():
+    names = declared_functions()
+    assert {"moe_route", "moe_dispatch", "moe_expert_ffn", "moe_combine", "moe_forward"} <= set(names)
+    lib = C.CDLL(B.LIB_PATH)
+    for n in names:
+        assert hasattr(lib, n), n
+    assert set(names) == set(B._SIGS), "binding signatures must cover the header exactly"
+
+
+@pytest.mark.parametrize("n,e,k,alpha", [(32, 64, 2, 1.2), (8192, 64, 1, 1.25), (64, 64, 2, 1.2),
+                                         (1000, 8, 2, 1.0), (7, 3, 2, 2.5), (31, 64, 1, 1.5),
+                                         (100, 8, 2, 0.0), (100, 8, 2, -1.0), (0, 4, 1, 1.0)])
+def test_capacity_matches_oracle(n, e, k, alpha):
+    want = O.capacity(n, e, k, alpha)
+    assert B.moe_capacity(n, e, k, alpha) == (-1 if want is None else want)
+
+
+def test_capacity_rejects_bad_arguments():
+    assert B.moe_capacity(-1, 4, 1, 1.0) == -1
+    assert "n_experts" in B.lib().moe_last_error().decode()
+
+
+def _route_status(**kw):
+    a = dict(stream=None, x=None, xt=B.MOE_BF16, n=4, d=64, wr=None, bias=None, e=8, k=2,
+             renorm=1, li=None, lo=None, idx=None, w=None, sel=None, pm=None, aux=None,
+             ws=None, wsb=0)
+    a.update(kw)
+    return B.lib().moe_route(*a.values())
+
+
+def test_route_validation():
+    L = B.lib()
+    fake = 4096  # never dereferenced: validation fails first
+    assert _route_status(e=0) == B.MOE_ERR_INVALID_ARG
+    assert _route_status(k=9) == B.MOE_ERR_INVALID_ARG
+    assert _route_status(e=600, k=2) == B.MOE_ERR_UNSUPPORTED
+    assert _route_status(e=40, k=17) == B.MOE_ERR_UNSUPPORTED
+    assert _route_status() == B.MOE_ERR_INVALID_ARG  # missing outputs
+    assert _route_status(idx=fake, w=fake) == B.MOE_ERR_INVALID_ARG  # missing x / w_router
+    assert _route_status(idx=fake, w=fake, x=fake, wr=fake, d=6) == B.MOE_ERR_UNSUPPORTED
+    need = L.moe_route_workspace_size(4, 8)
+    assert need > 0
+    st = _route_status(idx=fake, w=fake, x=fake, wr=fake, ws=fake, wsb=need - 1)
+    assert st == B.MOE_ERR_WORKSPACE and "workspace" in L.moe_last_error().decode()
+    assert L.moe_status_string(B.MOE_ERR_WORKSPACE).decode() == "workspace too small"
+
+
+def test_dispatch_and_combine_validation():
+    L = B.lib()
+    fake = 4096
+    assert L.moe_dispatch(None, fake, 4, 3, 2, -1, None, 0, 0, fake, fake, fake, None, None,
+                          None, None, 0) == B.MOE_ERR_INVALID_ARG  # k > E
+    assert L.moe_dispatch(None, fake, 4, 2, 8, -1, fake, B.MOE_BF16, 12, fake, fake, fake,
+                          None, None, fake, fake, 1 << 20) == B.MOE_ERR_UNSUPPORTED  # 24-byte rows
+    assert L.moe_dispatch(None, fake, 4, 2, 8, -1, None, 0, 0, None, fake, fake, None, None,
+                          None, fake, 1 << 20) == B.MOE_ERR_INVALID_ARG  # no offsets
+    assert L.moe_combine(None, B.MOE_BF16, fake, fake, fake, 4, 2, 12, None, fake) == B.MOE_ERR_UNSUPPORTED
+    assert L.moe_combine(None, 7, fake, fake, fake, 4, 2, 16, None, fake) == B.MOE_ERR_INVALID_ARG
+    assert L.moe_expert_ffn(None, B.MOE_BF16, B.MOE_ACT_GELU, fake, fake, 2, 10, 100, 256,
+                            fake, None, None, fake, None, fake, fake) == B.MOE_ERR_UNSUPPORTED
+    assert L.moe_expert_ffn(None, B.MOE_BF16, B.MOE_ACT_SWIGLU, fake, fake, 2, 10, 128, 256,
+                            fake, None, None, fake, None, fake, fake) == B.MOE_ERR_INVALID_ARG
+    assert L.moe_expert_ffn(None, B.MOE_F32, B.MOE_ACT_GELU, fake, fake, 0, 10, 128, 256,
+                            fake, None, None, fake, None, fake, fake) == B.MOE_ERR_INVALID_ARG
+
+
+def test_forward_validation_and_workspace():
+    L = B.lib()
+    cfg = B.make_config(4096, 4096, 14336, 8, 2, B.MOE_ACT_SWIGLU, B.MOE_BF16)
+    ws = B.moe_forward_workspace_size(cfg)
+    # x_perm + y_rows + h for 8192 rows dominate
+    assert ws >= 8192 * (4096 * 2 + 14336) * 2
+    capped = B.make_config(64, 4096, 11008, 64, 2, B.MOE_ACT_SWIGLU, B.MOE_BF16, capacity_factor=1.2)
+    assert B.moe_forward_workspace_size(capped) > 0
+    bad = B.make_config(16, 100, 256, 8, 2, B.MOE_ACT_SWIGLU, B.MOE_BF16)  # d % 64 != 0
+    assert B.moe_forward_workspace_size(bad) == 0
+    w = B.MoEWeightsC()
+    s = B.MoEStatsC()
+    st = L.moe_forward(None, C.byref(cfg), C.byref(w), 4096, 8192, C.byref(s), None, 0)
+    assert st == B.MOE_ERR_INVALID_ARG
+    with pytest.raises(B.MoEError):
+        B._check("moe_forward", st)
+    assert L.moe_forward(None, C.byref(bad), C.byref(w), None, None, None, None, 0) == B.MOE_ERR_UNSUPPORTED

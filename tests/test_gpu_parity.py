@@ -1,0 +1,380 @@
+"""Parity of the HIP path (through the C ABI) with the CPU oracle, stage by stage and for
+the whole layer, on the five workloads and on edge cases.  Integer results (routing,
+counts, permutation) must be bit-exact given the GPU's float32 logits; floating-point
+results must meet the stated tolerances."""
+import numpy as np
+import pytest
+import torch
+
+import oracle as O
+from gpu_helpers import (DEV, TOL, DeviceExperts, logits_tolerance, normwise_err, print_case,
+                         to_host_bits, widen_t)
+from sparse_mixture_experts_forward_amd import CONFIGS, MoELayer, synth
+from sparse_mixture_experts_forward_amd import _binding as B
+from sparse_mixture_experts_forward_amd.layer import workspace
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU visible")
+    B.lib()  # raises if the HIP library is missing: there is no fallback
+
+
+def _up(a: np.ndarray, dtype: str):
+    if dtype == "bf16":
+        return synth.torch_bf16_from_bits(a, DEV)
+    return torch.from_numpy(np.ascontiguousarray(a)).to(DEV)
+
+
+def _route(x, wr, lb, E, k, renorm=True, logits_in=None, n=None):
+    n = n if n is not None else (x if x is not None else logits_in).shape[0]
+    i32, f32 = torch.int32, torch.float32
+    out = dict(logits=torch.empty((n, E), dtype=f32, device=DEV) if logits_in is None else None,
+               idx=torch.empty((n, k), dtype=i32, device=DEV),
+               w=torch.empty((n, k), dtype=f32, device=DEV),
+               sel=torch.empty(E, dtype=i32, device=DEV),
+               pm=torch.empty(E, dtype=f32, device=DEV),
+               aux=torch.empty(1, dtype=f32, device=DEV))
+    ws = workspace(B.moe_route_workspace_size(n, E), DEV)
+    B.moe_route(x, wr, lb, E, k, renorm, logits_in, out["logits"], out["idx"], out["w"],
+                out["sel"], out["pm"], out["aux"], ws, n_tokens=n)
+    torch.cuda.synchronize()
+    return {kk: (None if v is None else v.cpu().numpy()) for kk, v in out.items()}
+
+
+def _check_gate(logits32, bias, k, E, got, renorm=True):
+    z = O.biased_scores(logits32, bias)
+    idx = O.select_topk(z, k)
+    assert np.array_equal(got["idx"], idx), "top-k indices differ"
+    p = O.softmax64(z)
+    w = O.gate_weights(p, idx, renorm)
+    np.testing.assert_allclose(got["w"], w, rtol=2e-6, atol=1e-7)
+    st = O.balance_stats(p, idx, E)
+    assert np.array_equal(got["sel"], st.sel_count)
+    np.testing.assert_allclose(got["pm"], st.prob_mean, rtol=2e-5, atol=1e-8)
+    assert abs(float(got["aux"][0]) - st.aux) <= 1e-5 * max(st.aux, 1e-30)
+    return idx
+
+
+# ------------------------------------------------------------------ generator
+def test_generator_gpu_matches_host():
+    cfg = CONFIGS["switch"].with_tokens(64)
+    print_case("generator", cfg.name)
+    h = synth.HostInputs(cfg)
+    d = synth.DeviceInputs(cfg, DEV)
+    assert np.array_equal(to_host_bits(d.x), h.x)
+    assert np.array_equal(d.w_router.cpu().numpy().view(np.uint32), h.w_router.view(np.uint32))
+    w = h.expert(5)
+    assert np.array_equal(to_host_bits(d.w1[5]), w["w1"])
+    assert np.array_equal(to_host_bits(d.w2[5]), w["w2"])
+    key = synth.stream_key(0, 77, 3, 1)
+    a = synth.normal_np(key, 1 << 18, 0.02, start=123)
+    b = synth.normal_torch(key, 1 << 18, 0.02, DEV, start=123).cpu().numpy()
+    assert np.array_equal(a.view(np.uint32), b.view(np.uint32))
+
+
+# ------------------------------------------------------------------ router + gate
+@pytest.mark.parametrize("name", list(CONFIGS))
+def test_router_parity_full_size(name):
+    cfg = CONFIGS[name]
+    print_case("router", name, cfg.n_tokens)
+    h = synth.HostInputs(cfg)
+    x = _up(h.x, cfg.dtype)
+    wr = torch.from_numpy(h.w_router).to(DEV)
+    lb = None if h.logit_bias is None else torch.from_numpy(h.logit_bias).to(DEV)
+    got = _route(x, wr, lb, cfg.n_experts, cfg.top_k, cfg.renormalize)
+    x64 = O.widen(h.x, cfg.dtype)
+    wr64 = h.w_router.astype(np.float64)
+    ref = x64 @ wr64
+    tol = logits_tolerance(x64, wr64)
+    bad = np.abs(got["logits"].astype(np.float64) - ref) > tol
+    assert not bad.any(), f"{bad.sum()} logits outside tolerance"
+    _check_gate(got["logits"], h.logit_bias, cfg.top_k, cfg.n_experts, got, cfg.renormalize)
+
+
+@pytest.mark.parametrize("E,k,bias", [(160, 6, False), (160, 6, True), (8, 2, False),
+                                      (64, 1, True), (3, 3, False), (1, 1, False),
+                                      (512, 16, True), (100, 7, False)])
+def test_gate_ties_on_given_logits(E, k, bias):
+    print_case("gate-ties", E, k, bias)
+    rng = np.random.default_rng(E * 31 + k)
+    n = 301
+    L = (rng.integers(-2, 3, size=(n, E)) * 0.5).astype(np.float32)  # many exact ties
+    L[0] = 0.0
+    L[1] = -0.0
+    L[2, : min(E, 2)] = [-0.0, 0.0][: min(E, 2)]
+    b = (rng.integers(-1, 2, size=E) * 0.5).astype(np.float32) if bias else None
+    got = _route(None, None, None if b is None else torch.from_numpy(b).to(DEV), E, k,
+                 logits_in=torch.from_numpy(L).to(DEV))
+    _check_gate(L, b, k, E, got)
+
+
+@pytest.mark.parametrize("E,k", [(8, 2), (64, 1), (64, 2), (160, 6)])
+def test_aux_is_one_under_uniform_routing(E, k):
+    print_case("aux-uniform", E, k)
+    n, d = 333, 64
+    x = torch.randn((n, d), device=DEV).to(torch.bfloat16)
+    wr = torch.zeros((d, E), dtype=torch.float32, device=DEV)
+    got = _route(x, wr, None, E, k)
+    assert (got["idx"] == np.arange(k)).all()
+    tol = 0.0 if E in (8, 64) else 1e-6
+    assert abs(float(got["aux"][0]) - 1.0) <= tol
+    assert np.abs(got["w"].sum(1) - 1).max() <= k * 2.0 ** -23
+
+
+# ------------------------------------------------------------------ dispatch
+def _distinct_idx(rng, n, E, k, skew=0.0):
+    score = rng.random((n, E)) + skew * np.linspace(1, 0, E)[None, :]
+    return np.argsort(-score, axis=1)[:, :k].astype(np.int32)
+
+
+def _dispatch(idx_np, E, cap, x):
+    n, k = idx_np.shape
+    layer_like = MoELayer.__new__(MoELayer)
+    layer_like.cfg = CONFIGS["tiny"].scaled(n_experts=E, top_k=k)
+    layer_like.device = torch.device(DEV)
+    out = MoELayer.dispatch(layer_like, x, torch.from_numpy(idx_np).to(DEV), capacity=cap,
+                            with_copy=x is not None)
+    torch.cuda.synchronize()
+    return out
+
+
+def _check_dispatch(idx, E, cap, out, x_bits=None):
+    plan = O.plan_dispatch(idx, E, None if cap < 0 else cap)
+    total = int(plan.expert_offsets[-1])
+    assert np.array_equal(out["expert_offsets"].cpu().numpy(), plan.expert_offsets)
+    assert np.array_equal(out["row_token"].cpu().numpy()[:total], plan.row_token)
+    assert np.array_equal(out["slot_row"].cpu().numpy(), plan.slot_row)
+    assert np.array_equal(out["kept_count"].cpu().numpy(), plan.kept_count)
+    assert int(out["n_dropped"].cpu()[0]) == plan.n_dropped
+    if x_bits is not None:
+        xp = to_host_bits(out["x_perm"])[:total]
+        assert np.array_equal(xp, x_bits[plan.row_token])
+    return plan
+
+
+@pytest.mark.parametrize("n,E,k,cap,skew,dtype", [
+    (1, 8, 2, -1, 0.0, "bf16"), (5, 3, 3, 1, 0.0, "f32"), (1000, 8, 2, -1, 0.0, "bf16"),
+    (1000, 8, 2, 0, 0.0, "bf16"), (4097, 64, 1, 37, 2.0, "bf16"), (4096, 160, 6, -1, 0.5, "bf16"),
+    (3000, 512, 16, 3, 1.0, "f32"), (8192, 64, 1, 160, 3.0, "bf16"), (64, 64, 2, 2, 0.0, "bf16"),
+    (777, 1, 1, 100, 0.0, "f32")])
+def test_dispatch_parity(n, E, k, cap, skew, dtype):
+    print_case("dispatch", n, E, k, cap, dtype)
+    rng = np.random.default_rng(n + E + k)
+    idx = _distinct_idx(rng, n, E, k, skew)
+    d = 64 if dtype == "bf16" else 12
+    xf = rng.standard_normal((n, d)).astype(np.float32)
+    xb = synth.f32_to_bf16_bits(xf) if dtype == "bf16" else xf
+    out = _dispatch(idx, E, cap, _up(xb, dtype))
+    _check_dispatch(idx, E, cap, out, xb)
+
+
+def test_dispatch_without_copy_and_empty():
+    print_case("dispatch-empty")
+    idx = np.zeros((0, 2), np.int32)
+    out = _dispatch(idx, 8, -1, None)
+    assert (out["expert_offsets"].cpu().numpy() == 0).all()
+    assert int(out["n_dropped"].cpu()[0]) == 0
+    rng = np.random.default_rng(3)
+    idx = _distinct_idx(rng, 100, 8, 2)
+    out = _dispatch(idx, 8, 5, None)
+    _check_dispatch(idx, 8, 5, out)
+
+
+# ------------------------------------------------------------------ expert FFN
+def _ffn_case(dtype, act, bias, d, d_ff, sizes, seed=0):
+    rng = np.random.default_rng(seed)
+    S = len(sizes)
+    rows = int(sum(sizes))
+    off = np.concatenate([[0], np.cumsum(sizes)]).astype(np.int32)
+    cvt = (lambda a: synth.f32_to_bf16_bits(a)) if dtype == "bf16" else (lambda a: a)
+    a = cvt(rng.standard_normal((max(rows, 1), d)).astype(np.float32))
+    w1 = cvt((rng.standard_normal((S, d_ff, d)) / np.sqrt(d)).astype(np.float32))
+    w3 = cvt((rng.standard_normal((S, d_ff, d)) / np.sqrt(d)).astype(np.float32)) if act == "swiglu" else None
+    w2 = cvt((rng.standard_normal((S, d, d_ff)) / np.sqrt(d_ff)).astype(np.float32))
+    b1 = cvt((0.1 * rng.standard_normal((S, d_ff))).astype(np.float32)) if bias else None
+    b2 = cvt((0.1 * rng.standard_normal((S, d))).astype(np.float32)) if bias else None
+    up = lambda v: None if v is None else _up(v, dtype)
+    t = dict(a=up(a), w1=up(w1), w3=up(w3), w2=up(w2), b1=up(b1), b2=up(b2))
+    h = torch.zeros((max(rows, 1), d_ff), dtype=t["a"].dtype, device=DEV)
+    y = torch.zeros((max(rows, 1), d), dtype=t["a"].dtype, device=DEV)
+    B.moe_expert_ffn(B.MOE_ACT_SWIGLU if act == "swiglu" else B.MOE_ACT_GELU, t["a"],
+                     torch.from_numpy(off).to(DEV), S, rows, t["w1"], t["w3"], t["b1"], t["w2"],
+                     t["b2"], h, y)
+    torch.cuda.synchronize()
+    a64 = O.widen(a, dtype)
+    hg, yg = widen_t(h), widen_t(y)
+    err_h = err_y = err_e2e = 0.0
+    for s in range(S):
+        r0, r1 = off[s], off[s + 1]
+        if r1 == r0:
+            continue
+        w = O.ExpertWeights(w1=O.widen(w1[s], dtype), w2=O.widen(w2[s], dtype),
+                            w3=None if w3 is None else O.widen(w3[s], dtype),
+                            b1=None if b1 is None else O.widen(b1[s], dtype),
+                            b2=None if b2 is None else O.widen(b2[s], dtype))
+        ho = O.expert_hidden(a64[r0:r1], w, act)
+        err_h = max(err_h, normwise_err(hg[r0:r1], ho))
+        err_y = max(err_y, normwise_err(yg[r0:r1], O.expert_output(hg[r0:r1], w)))
+        err_e2e = max(err_e2e, normwise_err(yg[r0:r1], O.expert_output(ho, w)))
+    return err_h, err_y, err_e2e
+
+
+FFN_CASES = [
+    # dtype, act, bias, d, d_ff, segment sizes (covers BM 32/64/128/256, empty and
+    # one-row segments, ragged row tails and a partial column tile)
+    ("bf16", "swiglu", False, 192, 320, [0, 1, 37, 300, 513, 0, 64]),
+    ("bf16", "gelu", True, 192, 320, [0, 1, 37, 300, 513, 0, 64]),
+    ("bf16", "swiglu", False, 256, 512, [3, 1, 2, 7, 30, 5, 0, 9]),
+    ("bf16", "gelu", False, 128, 256, [40, 70, 90, 33]),
+    ("bf16", "swiglu", False, 320, 384, [600, 700, 10]),
+    ("bf16", "gelu", True, 64, 128, [1]),
+    ("f32", "gelu", True, 128, 512, [30, 0, 100, 126]),
+    ("f32", "swiglu", False, 132, 260, [65, 1, 0, 200]),
+]
+
+
+@pytest.mark.parametrize("case", FFN_CASES, ids=[f"{c[0]}-{c[1]}-{c[3]}x{c[4]}-{len(c[5])}seg" for c in FFN_CASES])
+def test_expert_ffn_parity(case):
+    print_case("expert_ffn", case)
+    dtype = case[0]
+    err_h, err_y, err_e2e = _ffn_case(*case)
+    tol = TOL[dtype]
+    assert err_h <= tol, f"h error {err_h}"
+    assert err_y <= tol, f"y error given h {err_y}"
+    assert err_e2e <= tol, f"y error end to end {err_e2e}"
+
+
+# ------------------------------------------------------------------ combine
+@pytest.mark.parametrize("dtype,shared,k", [("bf16", False, 2), ("bf16", True, 6), ("f32", False, 1),
+                                            ("f32", True, 3)])
+def test_combine_parity(dtype, shared, k):
+    print_case("combine", dtype, shared, k)
+    rng = np.random.default_rng(k)
+    n, d, rows = 333, 256, 500
+    cvt = (lambda a: synth.f32_to_bf16_bits(a)) if dtype == "bf16" else (lambda a: a)
+    yr = cvt(rng.standard_normal((rows, d)).astype(np.float32))
+    sy = cvt(rng.standard_normal((n, d)).astype(np.float32)) if shared else None
+    slot = rng.integers(-1, rows, size=(n, k)).astype(np.int32)
+    slot[:5] = -1  # fully dropped tokens
+    w = rng.random((n, k)).astype(np.float32)
+    out = torch.empty((n, d), dtype=torch.bfloat16 if dtype == "bf16" else torch.float32, device=DEV)
+    B.moe_combine(_up(yr, dtype), torch.from_numpy(slot).to(DEV), torch.from_numpy(w).to(DEV),
+                  None if sy is None else _up(sy, dtype), out)
+    torch.cuda.synchronize()
+    yr64 = O.widen(yr, dtype)
+    ref = np.zeros((n, d)) if sy is None else O.widen(sy, dtype).copy()
+    for j in range(k):
+        m = slot[:, j] >= 0
+        ref[m] += w[m, j, None].astype(np.float64) * yr64[slot[m, j]]
+    got = widen_t(out)
+    if not shared:
+        assert (got[:5] == 0).all()
+    rel = 2.0 ** -8 if dtype == "bf16" else 1e-6
+    assert np.all(np.abs(got - ref) <= rel * np.abs(ref) + 1e-6 * np.abs(ref).max())
+
+
+# ------------------------------------------------------------------ whole layer
+def _forward_and_oracle(cfg, tokens=None, check_all_logits=True):
+    inp = synth.DeviceInputs(cfg, DEV)
+    layer = MoELayer.from_inputs(inp)
+    n = cfg.n_tokens
+    st = layer.new_stats(n)
+    y = layer.forward(inp.x, stats=st)
+    torch.cuda.synchronize()
+    Lg = st["logits"].cpu().numpy()
+    xb = to_host_bits(inp.x)
+    x64 = O.widen(xb, cfg.dtype)
+    wr64 = inp.w_router.cpu().numpy().astype(np.float64)
+    rows = slice(None) if check_all_logits else (tokens if tokens is not None else slice(None))
+    ref = x64[rows] @ wr64
+    assert not (np.abs(Lg[rows] - ref) > logits_tolerance(x64[rows], wr64)).any()
+    lb = None if inp.logit_bias is None else inp.logit_bias.cpu().numpy()
+    r = O.forward(xb, cfg.dtype, None, cfg.top_k, DeviceExperts(layer.w), cfg.n_experts, cfg.act,
+                  logit_bias=lb, alpha=cfg.alpha, renormalize=cfg.renormalize,
+                  shared=DeviceExperts(layer.w, shared=True) if cfg.n_shared else None,
+                  n_shared=cfg.n_shared, logits=Lg, tokens=tokens)
+    # integer results: bit-exact
+    assert np.array_equal(st["topk_idx"].cpu().numpy(), r.topk_idx)
+    assert np.array_equal(st["sel_count"].cpu().numpy(), r.stats.sel_count)
+    assert np.array_equal(st["kept_count"].cpu().numpy(), r.plan.kept_count)
+    assert int(st["n_dropped"].cpu()[0]) == r.plan.n_dropped
+    assert np.array_equal(st["expert_offsets"].cpu().numpy(), r.plan.expert_offsets)
+    assert np.array_equal(st["slot_row"].cpu().numpy(), r.plan.slot_row)
+    np.testing.assert_allclose(st["topk_w"].cpu().numpy(), r.topk_w, rtol=2e-6, atol=1e-7)
+    np.testing.assert_allclose(st["prob_mean"].cpu().numpy(), r.stats.prob_mean, rtol=2e-5, atol=1e-8)
+    assert abs(float(st["aux"].cpu()[0]) - r.stats.aux) <= 1e-5 * r.stats.aux
+    yg = widen_t(y)[r.tokens]
+    err = normwise_err(yg, r.y)
+    return err, r, y
+
+
+REDUCED = {"tiny": 256, "switch": 1024, "mixtral": 256, "deepseek": 128, "decode": 64}
+
+
+@pytest.mark.parametrize("name", list(CONFIGS))
+def test_forward_parity_reduced(name):
+    cfg = CONFIGS[name].with_tokens(REDUCED[name])
+    print_case("forward", name, cfg.n_tokens)
+    err, r, _ = _forward_and_oracle(cfg)
+    print(f"  {name}: normwise error {err:.3e}, dropped {r.plan.n_dropped}", flush=True)
+    assert err <= TOL[cfg.dtype]
+
+
+@pytest.mark.parametrize("name", ["switch", "mixtral", "deepseek", "decode"])
+def test_forward_parity_full_size_sampled(name):
+    cfg = CONFIGS[name]
+    print_case("forward-full", name, cfg.n_tokens)
+    n = cfg.n_tokens
+    rng = np.random.default_rng(1)
+    tokens = np.unique(np.concatenate([np.arange(6), np.arange(n - 6, n),
+                                       rng.choice(n, size=min(n, 12), replace=False)]))
+    err, r, _ = _forward_and_oracle(cfg, tokens=tokens, check_all_logits=True)
+    print(f"  {name}: normwise error {err:.3e} on {len(tokens)} tokens, dropped {r.plan.n_dropped}",
+          flush=True)
+    assert err <= TOL[cfg.dtype]
+    torch.cuda.empty_cache()
+
+
+def test_forward_is_deterministic():
+    cfg = CONFIGS["mixtral"].with_tokens(300).scaled(d_ff=1024)
+    print_case("determinism", cfg.name, cfg.n_tokens)
+    inp = synth.DeviceInputs(cfg, DEV)
+    layer = MoELayer.from_inputs(inp)
+    s1, s2 = layer.new_stats(300), layer.new_stats(300)
+    y1 = layer.forward(inp.x, stats=s1).clone()
+    y2 = layer.forward(inp.x, stats=s2)
+    torch.cuda.synchronize()
+    assert torch.equal(y1.view(torch.int16), y2.view(torch.int16))
+    for key in s1:
+        assert torch.equal(s1[key], s2[key]), key
+
+
+def test_forward_edge_cases():
+    print_case("edge", "empty / single / all dropped")
+    # all dropped: C = floor(32/64) * 1.25 = 0 -> y is exactly 0
+    cfg = CONFIGS["switch"].with_tokens(32).scaled(d_ff=256)
+    err, r, y = _forward_and_oracle(cfg)
+    assert r.cap == 0 and r.plan.n_dropped == 32
+    assert (to_host_bits(y) == 0).all()
+    # all dropped but with shared experts -> y = shared output only
+    cfg = CONFIGS["deepseek"].with_tokens(16).scaled(alpha=0.01, d_ff=128)
+    err, r, _ = _forward_and_oracle(cfg)
+    assert r.cap == 0 and err <= TOL["bf16"]
+    # a single token
+    cfg = CONFIGS["mixtral"].with_tokens(1).scaled(d_ff=512)
+    err, r, _ = _forward_and_oracle(cfg)
+    assert err <= TOL["bf16"]
+    # no tokens
+    cfg = CONFIGS["tiny"].with_tokens(0)
+    inp = synth.DeviceInputs(cfg.with_tokens(4), DEV)
+    layer = MoELayer.from_inputs(inp)
+    st = layer.new_stats(0)
+    y = layer.forward(inp.x[:0], stats=st)
+    torch.cuda.synchronize()
+    assert y.shape == (0, cfg.d_model)
+    assert (st["sel_count"].cpu() == 0).all() and float(st["aux"].cpu()[0]) == 0.0
+    assert (st["expert_offsets"].cpu() == 0).all()
