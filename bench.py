@@ -54,7 +54,8 @@ def kernel_work(cfg, kept: int, touched: int):
     w["gemm2"] = dict(flops=2.0 * kept * f * d,
                       bytes=touched * d * f * es + kept * f * es + kept * d * es)
     w["shared"] = dict(flops=2.0 * n * d * f * sh * (m1 + 1),
-                       bytes=sh * (m1 + 1) * f * d * es + n * d * es * 2 + n * sh * f * es * 2)
+                       bytes=(sh * (m1 + 1) * f * d * es + n * d * es * 2 + n * sh * f * es * 2)
+                       if sh else 0)
     w["dispatch"] = dict(flops=0.0, bytes=n * d * es + kept * d * es + n * k * 4 * 2 + kept * 4)
     w["combine"] = dict(flops=0.0, bytes=kept * d * es + n * k * 8 + n * d * es * (2 if sh else 1))
     w["route"] = dict(flops=2.0 * n * d * cfg.n_experts,
@@ -118,7 +119,10 @@ def cpu_baseline(cfg, inp, logits, budget_s: float):
     n = cfg.n_tokens
     n_s = min(n, 16)
     t = run(n_s)
-    if t < 0.5 * budget_s and n_s < n:
+    while t < budget_s / 4 and n_s < n:  # the first runs are dominated by fixed costs
+        n_s = min(n, n_s * 4)
+        t = run(n_s)
+    if t < 0.6 * budget_s and n_s < n:
         n_s = int(min(n, max(n_s, n_s * 0.8 * budget_s / t)))
         t = run(n_s)
     try:
@@ -141,6 +145,9 @@ def main():
     ap.add_argument("--config", default="mixtral")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--calibrate-copy-mib", type=int, default=0,
+                    help="after the timed steps, run one plain device copy of this many MiB "
+                         "(the reference kernel that scales hardware byte counters)")
     args = ap.parse_args()
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
@@ -179,6 +186,15 @@ def main():
     torch.cuda.synchronize()
     elapsed = time.perf_counter() - t0
 
+    if args.calibrate_copy_mib > 0:  # outside the timed region
+        src = torch.empty(args.calibrate_copy_mib << 20, dtype=torch.uint8, device=dev)
+        dst = torch.empty_like(src)
+        src.fill_(1)
+        torch.cuda.synchronize()
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
+
     stage_ms = {s: 0.0 for s in STAGES}
     for row in ev:
         for j, s in enumerate(STAGES):
@@ -188,9 +204,9 @@ def main():
     kept = int(stats["kept_count"].sum().item())
     touched = int((stats["kept_count"] > 0).sum().item())
     work = kernel_work(cfg, kept, touched)
-    kernels = {s: roofline(s, work[s], stage_ms[s], cfg.dtype) for s in STAGES if stage_ms[s] > 0}
-    dominant = max(("gemm1", "gemm2", "shared", "dispatch", "combine", "route"),
-                   key=lambda s: stage_ms[s])
+    kernels = {s: roofline(s, work[s], stage_ms[s], cfg.dtype) for s in STAGES
+               if stage_ms[s] > 0 and (work[s]["flops"] > 0 or work[s]["bytes"] > 0)}
+    dominant = max(kernels, key=lambda s: stage_ms[s])
     gemm_ms = stage_ms["gemm1"] + stage_ms["gemm2"] + stage_ms["shared"]
     gemm_flops = work["gemm1"]["flops"] + work["gemm2"]["flops"] + work["shared"]["flops"]
     gemm_tflops = gemm_flops / (gemm_ms * 1e-3) / 1e12 if gemm_ms > 0 else 0.0

@@ -11,7 +11,9 @@ import ctypes as C
 import os
 from typing import Optional
 
-LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libmoe_mi355x.so")
+# the in-tree build; MOE_MI355X_LIB selects another build of the same library
+LIB_PATH = os.environ.get("MOE_MI355X_LIB") or os.path.join(
+    os.path.dirname(os.path.abspath(__file__)), "libmoe_mi355x.so")
 
 MOE_OK, MOE_ERR_INVALID_ARG, MOE_ERR_UNSUPPORTED, MOE_ERR_WORKSPACE, MOE_ERR_HIP = range(5)
 MOE_F32, MOE_BF16 = 0, 1

@@ -7,23 +7,25 @@
 //   EPI_SWIGLU  C = SiLU(A W1^T) * (A W3^T)            (both products in one tile)
 //   EPI_NONE    C = A W2^T (+ b2)
 //
-// bf16 kernel (gfx950 matrix cores, v_mfma_f32_16x16x32_bf16, float32 accumulation):
+// bf16 kernel (gfx950 matrix cores, float32 accumulation):
 //   * one workgroup = 4 waves computes BM activation rows x 256 weight rows; waves are
-//     2 x 2, each owning BM/2 rows x 128 weight rows as (BM/32) x 8 MFMA tiles of 16x16;
+//     2 x 2, each owning BM/2 rows x 128 weight rows as tiles of v_mfma_f32_32x32x16_bf16
+//     (v_mfma_f32_16x16x32_bf16 when BM = 32, i.e. 16 rows per wave);
 //   * weights are the MFMA A operand, activations the B operand, so a lane ends with 4
 //     consecutive output columns of one row (8-byte stores of bf16);
-//   * K advances 64 at a time through two LDS stages (double buffer, one barrier per
-//     stage); global loads for stage k+1 are in flight while stage k is multiplied;
-//   * LDS rows are 128 bytes; the 16-byte chunk c of row r is stored at chunk c ^ (r & 7),
-//     which makes both the row-wise stores and the fragment reads conflict free;
+//   * K advances 32 at a time through a ring of 4 LDS stages filled by direct-to-LDS
+//     loads (global_load_lds_dwordx4) issued 3 stages ahead; each stage ends with a
+//     barrier that waits only for the loads of the next stage, so the other two stay
+//     in flight across it;
+//   * LDS rows are 64 bytes; the 16-byte chunk c of row r is stored at chunk
+//     c ^ ((r >> 1) & 3), which keeps the fragment reads free of bank conflicts;
 //   * SwiGLU: each wave's 128 weight rows are 64 rows of W1 followed by the same 64 rows
 //     of W3, so g and u of an output element sit in the same lane;
 //   * scheduling happens on the device: every workgroup scans the segment offsets
 //     written by the dispatch step, so no host round trip is needed.  Tiles are ordered
-//     segment by segment, 8 column tiles x all row tiles of a segment at a time, and the
-//     workgroup -> tile map gives each XCD (workgroup id mod 8) a contiguous range of
-//     that order, so tiles that share weight and activation panels run together on one
-//     XCD and share its L2.
+//     segment by segment, 8 column tiles x all row tiles of a segment at a time.  With
+//     MOE_GEMM_XCD_REMAP the workgroup -> tile map gives each XCD (workgroup id mod 8) a
+//     contiguous range of that order instead of every eighth tile.
 // float32 kernel: a plain LDS-tiled SIMT product (64 x 64 tiles) with the same
 // scheduling and epilogues; it serves the small float32 workload.
 
@@ -34,9 +36,16 @@ namespace moe {
 namespace {
 
 constexpr int kThreads = 256;
-constexpr int kBK = 64;       // bf16: reduction depth per LDS stage
+constexpr int kBK = 32;       // bf16: reduction depth per LDS stage
+constexpr int kStages = 4;    // LDS ring depth (loads run kStages-1 stages ahead)
 constexpr int kBRows = 256;   // bf16: weight rows per workgroup
-constexpr int kGroupN = 8;    // column tiles per scheduling group
+#ifndef MOE_GEMM_GROUP_N
+#define MOE_GEMM_GROUP_N 8
+#endif
+#ifndef MOE_GEMM_XCD_REMAP
+#define MOE_GEMM_XCD_REMAP 1
+#endif
+constexpr int kGroupN = MOE_GEMM_GROUP_N;  // column tiles per scheduling group
 constexpr int kXcds = 8;
 
 struct Tile {
@@ -103,11 +112,16 @@ __device__ bool schedule_tile(const int32_t* __restrict__ seg_off, int n_seg,
   if (tid == 0) s_start[n_seg] = total;
   __syncthreads();
 
+#if MOE_GEMM_XCD_REMAP
   const int xcd = blockIdx.x % kXcds;
   const int i = blockIdx.x / kXcds;
   const int per = (total + kXcds - 1) / kXcds;
   const int L = xcd * per + i;
   if (i >= per || L >= total) return false;
+#else
+  const int L = blockIdx.x;
+  if (L >= total) return false;
+#endif
 #pragma unroll
   for (int u = 0; u < 2; ++u) {
     const int s = 2 * tid + u;
@@ -139,54 +153,182 @@ __device__ __forceinline__ uint2 pack_bf16x4(float a, float b, float c, float d)
   return r;
 }
 
-// global -> registers for the stage starting at k0 (16-byte chunks; for SwiGLU the
-// thread rows j = 2, 3, 6, 7 read W3, the others W1)
-template <int A_LOADS, int B_LOADS, bool DUAL, bool KSPLIT>
-__device__ __forceinline__ void gload_stage(const GemmArgs& g, int k0,
-                                            const uint16_t* __restrict__ a_base,
-                                            const int32_t (&a_off)[A_LOADS],
-                                            const uint16_t* __restrict__ b_base0,
-                                            const uint16_t* __restrict__ b_base1,
-                                            const int32_t (&b_off)[B_LOADS],
-                                            u32x4_t (&ra)[A_LOADS], u32x4_t (&rb)[B_LOADS]) {
-  int64_t bk = k0;
-  if (KSPLIT) {
-    const int64_t kb = k0 / g.kchunk;
-    bk = kb * g.kbatch_stride + (k0 - kb * g.kchunk);
+typedef __attribute__((address_space(3))) void lds_void_t;
+typedef __attribute__((address_space(1))) void global_void_t;
+
+// The two bf16 matrix-core shapes.  Weights are the A operand (rows i of D), activations
+// the B operand (columns j of D); both supply 8 consecutive k (16 bytes) per lane.
+template <int MF>
+struct Mfma;
+
+template <>
+struct Mfma<16> {  // v_mfma_f32_16x16x32_bf16: 16 x 16 tile, k 32, 4 results per lane
+  static constexpr int M = 16, KSTEPS = kBK / 32, ACC = 4;  // one k-step per stage
+  typedef f32x4_t acc_t;
+  __device__ static int row(int lane) { return lane & 15; }
+  __device__ static int chunk(int lane, int ks) { return ks * 4 + (lane >> 4); }
+  __device__ static acc_t mma(bf16x8_t a, bf16x8_t b, acc_t c) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
   }
+  // result register 4*q + r holds D[i = ni(q, lane) + r][j = row(lane)]
+  __device__ static int ni(int q, int lane) { return 4 * (lane >> 4) + 0 * q; }
+};
+
+template <>
+struct Mfma<32> {  // v_mfma_f32_32x32x16_bf16: 32 x 32 tile, k 16, 16 results per lane
+  static constexpr int M = 32, KSTEPS = kBK / 16, ACC = 16;
+  typedef f32x16_t acc_t;
+  __device__ static int row(int lane) { return lane & 31; }
+  __device__ static int chunk(int lane, int ks) { return ks * 2 + (lane >> 5); }
+  __device__ static acc_t mma(bf16x8_t a, bf16x8_t b, acc_t c) {
+    return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+  }
+  __device__ static int ni(int q, int lane) { return 8 * q + 4 * (lane >> 5); }
+};
+
+// 32x32 tiles once a wave holds at least 32 activation rows: issued from one wave per
+// SIMD they keep the matrix cores near peak, where 16x16 tiles reach about 60 %.
+template <int BM>
+struct MfmaFor {
+  static constexpr int value = (BM / 2 >= 32) ? 32 : 16;
+};
+
+// Per-thread view of the operand tiles: direct-to-LDS load sources and fragment reads.
+template <int BM, bool DUAL, bool KSPLIT>
+struct TileIO {
+  static constexpr int MF = MfmaFor<BM>::value;
+  using S = Mfma<MF>;
+  static constexpr int WM = BM / 2;            // activation rows per wave
+  static constexpr int TM = WM / S::M;         // MFMA tiles per wave along activation rows
+  static constexpr int TN = 128 / S::M;        // MFMA tiles per wave along weight rows
+  static constexpr int A_GRPS = BM / 16;                   // 16-row groups of A per stage
+  static constexpr int A_GRP = A_GRPS >= 4 ? A_GRPS / 4 : 1;  // per wave (every wave issues the
+                                                           // same count; with fewer groups than
+                                                           // waves, waves repeat a group)
+  static constexpr int B_GRP = kBRows / 64;    // 16-row groups per wave per stage (B)
+  const uint16_t* a_base;
+  const uint16_t* b_base0;
+  const uint16_t* b_base1;
+  uint32_t a_off[A_GRP];  // byte offsets
+  uint32_t b_off[B_GRP];
+  int wave, lane, wm, wn, b_row, a_row;
+  int co[S::KSTEPS];      // swizzled element offset of this lane's chunk per k-step
+  int64_t kchunk, kbatch_stride;
+
+  // One stage of loads: wave w fills the 8-row groups w, w+4, ... of A and B.  Lane l
+  // writes LDS row 8*group + l/8, physical chunk l%8, i.e. logical chunk (l%8)^(l/8).
+  // Addresses are a wave-uniform base that carries k plus a loop-invariant unsigned
+  // 32-bit lane offset (the scalar-base form of the load).
+  __device__ __forceinline__ void dma(uint16_t* as, uint16_t* bs, int k0) const {
+    int64_t bk = k0;
+    if (KSPLIT) {
+      const int64_t kb = k0 / kchunk;
+      bk = kb * kbatch_stride + (k0 - kb * kchunk);
+    }
+    const char* ak = reinterpret_cast<const char*>(a_base + k0);
+    const char* bk0 = reinterpret_cast<const char*>(b_base0 + bk);
+    const char* bk1 = reinterpret_cast<const char*>(b_base1 + bk);
 #pragma unroll
-  for (int j = 0; j < A_LOADS; ++j) ra[j] = *reinterpret_cast<const u32x4_t*>(a_base + a_off[j] + k0);
+    for (int j = 0; j < A_GRP; ++j)
+      __builtin_amdgcn_global_load_lds((global_void_t*)(ak + a_off[j]),
+                                       (lds_void_t*)(as + ((wave + 4 * j) % A_GRPS) * 16 * kBK),
+                                       16, 0, 0);
 #pragma unroll
-  for (int j = 0; j < B_LOADS; ++j) {
-    const uint16_t* bb = (DUAL && ((j >> 1) & 1)) ? b_base1 : b_base0;
-    rb[j] = *reinterpret_cast<const u32x4_t*>(bb + b_off[j] + bk);
+    for (int j = 0; j < B_GRP; ++j) {
+      const char* bb = (DUAL && (j & 1)) ? bk1 : bk0;
+      __builtin_amdgcn_global_load_lds((global_void_t*)(bb + b_off[j]),
+                                       (lds_void_t*)(bs + (wave + 4 * j) * 16 * kBK), 16, 0, 0);
+    }
+  }
+};
+
+// Scheduling hints for the k-steps of one stage: the fragment reads of k-step ks+1
+// are spread between the MFMAs of k-step ks.
+template <int KS, int KSTEPS, int R, int P, int SLOT>
+__device__ __forceinline__ void sched_kstep() {
+  if constexpr (KS + 1 < KSTEPS) {
+    if constexpr (SLOT < R) {
+      constexpr int lo = SLOT * P / R, hi = (SLOT + 1) * P / R;
+      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+      if constexpr (hi > lo) __builtin_amdgcn_sched_group_barrier(0x008, hi - lo, 0);
+      sched_kstep<KS, KSTEPS, R, P, SLOT + 1>();
+    } else {
+      sched_kstep<KS + 1, KSTEPS, R, P, 0>();
+    }
+  } else if constexpr (KS + 1 == KSTEPS) {
+    __builtin_amdgcn_sched_group_barrier(0x008, P, 0);
   }
 }
 
-// registers -> one LDS stage, chunk c of row r stored at chunk c ^ (r & 7)
-template <int A_LOADS, int B_LOADS>
-__device__ __forceinline__ void lstore_stage(uint16_t* __restrict__ as, uint16_t* __restrict__ bs,
-                                             int lrow, int sw, const u32x4_t (&ra)[A_LOADS],
-                                             const u32x4_t (&rb)[B_LOADS]) {
+// One K stage (32 deep) of MFMAs over the fragments in (ac, bc); fragments of the next
+// k-step are requested from LDS before the current k-step's MFMAs are issued.
+template <int BM, bool DUAL, bool KSPLIT>
+__device__ __forceinline__ void gemm_stage(
+    const TileIO<BM, DUAL, KSPLIT>& io, const uint16_t* __restrict__ ac,
+    const uint16_t* __restrict__ bc,
+    typename Mfma<TileIO<BM, DUAL, KSPLIT>::MF>::acc_t (&acc)[TileIO<BM, DUAL, KSPLIT>::TN]
+                                                             [TileIO<BM, DUAL, KSPLIT>::TM]) {
+  using IO = TileIO<BM, DUAL, KSPLIT>;
+  using S = typename IO::S;
+  constexpr int TM = IO::TM, TN = IO::TN, KS = S::KSTEPS;
+  bf16x8_t wf[2][TN], af[2][TM];
 #pragma unroll
-  for (int j = 0; j < A_LOADS; ++j)
-    *reinterpret_cast<u32x4_t*>(&as[(lrow + 32 * j) * kBK + sw]) = ra[j];
+  for (int tn = 0; tn < TN; ++tn)
+    wf[0][tn] = *reinterpret_cast<const bf16x8_t*>(&bc[io.b_row + tn * S::M * kBK + io.co[0]]);
 #pragma unroll
-  for (int j = 0; j < B_LOADS; ++j)
-    *reinterpret_cast<u32x4_t*>(&bs[(lrow + 32 * j) * kBK + sw]) = rb[j];
+  for (int tm = 0; tm < TM; ++tm)
+    af[0][tm] = *reinterpret_cast<const bf16x8_t*>(&ac[io.a_row + tm * S::M * kBK + io.co[0]]);
+#pragma unroll
+  for (int ks = 0; ks < KS; ++ks) {
+    const int c = ks & 1;
+    if (ks + 1 < KS) {
+#pragma unroll
+      for (int tn = 0; tn < TN; ++tn)
+        wf[c ^ 1][tn] =
+            *reinterpret_cast<const bf16x8_t*>(&bc[io.b_row + tn * S::M * kBK + io.co[ks + 1]]);
+#pragma unroll
+      for (int tm = 0; tm < TM; ++tm)
+        af[c ^ 1][tm] =
+            *reinterpret_cast<const bf16x8_t*>(&ac[io.a_row + tm * S::M * kBK + io.co[ks + 1]]);
+    }
+#pragma unroll
+    for (int tn = 0; tn < TN; ++tn)
+#pragma unroll
+      for (int tm = 0; tm < TM; ++tm) acc[tn][tm] = S::mma(wf[c][tn], af[c][tm], acc[tn][tm]);
+  }
+  __builtin_amdgcn_sched_group_barrier(0x100, TN + TM, 0);
+  sched_kstep<0, KS, TN + TM, TN * TM, 0>();
+}
+
+// Stage boundary of the LDS ring: wait until this wave's own LDS reads are done and at
+// most N of its direct-to-LDS loads are still in flight (the stages after the next one),
+// then a workgroup barrier.  A full __syncthreads would also drain the loads that are
+// meant to stay in flight.  The empty asm statements keep the compiler from moving
+// memory accesses across the barrier; they emit no instruction.
+template <int N>
+__device__ __forceinline__ void barrier_keep_loads() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  // s_waitcnt fields (gfx9): vmcnt [3:0] and [15:14], expcnt [6:4] (7 = no wait),
+  // lgkmcnt [11:8] (0 = all LDS operations done)
+  __builtin_amdgcn_s_waitcnt((N & 0xF) | ((N >> 4) << 14) | (0x7 << 4));
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
 }
 
 // ------------------------------------------------------------------ bf16 MFMA kernel
 template <int BM, int EPI, bool KSPLIT>
 __global__ __launch_bounds__(kThreads, 1) void gemm_bf16_kernel(GemmArgs g) {
-  constexpr int WM = BM / 2;       // activation rows per wave
-  constexpr int TM = WM / 16;      // MFMA tiles per wave along the rows
-  constexpr int TN = 8;            // MFMA tiles per wave along the weight rows (128)
-  constexpr int A_LOADS = BM / 32; // 16-byte chunks per thread per stage
-  constexpr int B_LOADS = kBRows / 32;
+  using IO = TileIO<BM, EPI == EPI_SWIGLU, KSPLIT>;
+  using S = typename IO::S;
+  constexpr int WM = IO::WM;
+  constexpr int TM = IO::TM;
+  constexpr int TN = IO::TN;
   static_assert(TM >= 1, "BM must be >= 32");
-  __shared__ __attribute__((aligned(16))) uint16_t As[2][BM * kBK];
-  __shared__ __attribute__((aligned(16))) uint16_t Bs[2][kBRows * kBK];
+  // the LDS ring as distinct objects, so that the compiler can tell the stage being read
+  // from the stages being filled
+  __shared__ __attribute__((aligned(16))) uint16_t As0[BM * kBK], As1[BM * kBK], As2[BM * kBK], As3[BM * kBK];
+  __shared__ __attribute__((aligned(16))) uint16_t Bs0[kBRows * kBK], Bs1[kBRows * kBK], Bs2[kBRows * kBK], Bs3[kBRows * kBK];
   __shared__ SchedSmem sched;
 
   const int n_ntiles = (EPI == EPI_SWIGLU) ? (g.n_out + 127) / 128 : (g.n_out + 255) / 256;
@@ -196,90 +338,98 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_bf16_kernel(GemmArgs g) {
 
   const int tid = threadIdx.x;
   const int lane = tid & (kWave - 1);
-  const int wave = tid / kWave;
-  const int wm = wave >> 1, wn = wave & 1;
-  const int lrow = tid >> 3, lchunk = tid & 7;
-  const int sw = (lchunk ^ (lrow & 7)) * 8;  // swizzled element offset of this thread's chunk
-
-  const uint16_t* __restrict__ a_base =
-      static_cast<const uint16_t*>(g.a) + tile.row0 * g.lda + lchunk * 8;
-  int32_t a_off[A_LOADS];
+  const int wave = __builtin_amdgcn_readfirstlane(tid / kWave);  // uniform per wave
+  IO io;
+  io.wave = wave;
+  io.lane = lane;
+  io.wm = wave >> 1;
+  io.wn = wave & 1;
+  io.kchunk = g.kchunk;
+  io.kbatch_stride = g.kbatch_stride;
+  const int dl_row = lane >> 2;                                 // row inside a 16-row group
+  const int dl_chunk = ((lane & 3) ^ ((lane >> 3) & 3)) * 8;     // logical chunk this lane loads
+  io.a_base = static_cast<const uint16_t*>(g.a) + tile.row0 * g.lda;
 #pragma unroll
-  for (int j = 0; j < A_LOADS; ++j) {
-    const int r = min(lrow + 32 * j, tile.m_valid - 1);
-    a_off[j] = r * static_cast<int32_t>(g.lda);
+  for (int j = 0; j < IO::A_GRP; ++j) {
+    const int r = min(16 * ((wave + 4 * j) % IO::A_GRPS) + dl_row, tile.m_valid - 1);
+    io.a_off[j] = static_cast<uint32_t>((r * static_cast<int32_t>(g.lda) + dl_chunk) * 2);
   }
-  // weight rows: thread row lrow + 32 j; for SwiGLU rows 64..127 and 192..255 of the tile
-  // (j = 2, 3, 6, 7) come from W3, the others from W1
-  const uint16_t* __restrict__ b_base0 =
-      static_cast<const uint16_t*>(g.b0) + tile.seg * g.b_seg_stride + lchunk * 8;
-  const uint16_t* __restrict__ b_base1 =
-      (EPI == EPI_SWIGLU)
-          ? static_cast<const uint16_t*>(g.b1) + tile.seg * g.b_seg_stride + lchunk * 8
-          : b_base0;
-  int32_t b_off[B_LOADS];
+  io.b_base0 = static_cast<const uint16_t*>(g.b0) + tile.seg * g.b_seg_stride;
+  io.b_base1 = (EPI == EPI_SWIGLU) ? static_cast<const uint16_t*>(g.b1) + tile.seg * g.b_seg_stride
+                                   : io.b_base0;
 #pragma unroll
-  for (int j = 0; j < B_LOADS; ++j) {
-    const int i = lrow + 32 * j;
+  for (int j = 0; j < IO::B_GRP; ++j) {
+    const int i = 16 * (wave + 4 * j) + dl_row;  // LDS row of the tile
     int n = (EPI == EPI_SWIGLU) ? tile.nt * 128 + (i >> 7) * 64 + (i & 63) : tile.nt * 256 + i;
     n = min(n, g.n_out - 1);
-    b_off[j] = n * static_cast<int32_t>(g.ldb);
+    io.b_off[j] = static_cast<uint32_t>(n) * static_cast<uint32_t>(g.ldb) * 2u +
+                  static_cast<uint32_t>(dl_chunk * 2);
   }
+  const int frow = S::row(lane);
+#pragma unroll
+  for (int ks = 0; ks < S::KSTEPS; ++ks) io.co[ks] = (S::chunk(lane, ks) ^ ((frow >> 1) & 3)) * 8;
+  io.b_row = (io.wn * 128 + frow) * kBK;
+  io.a_row = (io.wm * WM + frow) * kBK;
+  const int wm = io.wm, wn = io.wn;
 
-  u32x4_t ra[A_LOADS], rb[B_LOADS];
-  f32x4_t acc[TN][TM];
+  typename S::acc_t acc[TN][TM];
 #pragma unroll
   for (int a = 0; a < TN; ++a)
 #pragma unroll
-    for (int b = 0; b < TM; ++b) acc[a][b] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+    for (int b = 0; b < TM; ++b)
+#pragma unroll
+      for (int r = 0; r < S::ACC; ++r) acc[a][b][r] = 0.f;
 
   const int KT = g.k / kBK;
-  const int frow = lane & 15;
-  gload_stage<A_LOADS, B_LOADS, EPI == EPI_SWIGLU, KSPLIT>(g, 0, a_base, a_off, b_base0, b_base1, b_off, ra, rb);
-  lstore_stage<A_LOADS, B_LOADS>(As[0], Bs[0], lrow, sw, ra, rb);
-  __syncthreads();
-  for (int kt = 0; kt < KT; ++kt) {
-    const int cur = kt & 1;
-    if (kt + 1 < KT)
-      gload_stage<A_LOADS, B_LOADS, EPI == EPI_SWIGLU, KSPLIT>(g, (kt + 1) * kBK, a_base, a_off, b_base0, b_base1, b_off, ra, rb);
-#pragma unroll
-    for (int ks = 0; ks < 2; ++ks) {
-      const int chunk = ks * 4 + (lane >> 4);
-      const int coff = (chunk ^ (lane & 7)) * 8;  // row & 7 == lane & 7 for every fragment row
-      bf16x8_t bf[TN], af[TM];
-#pragma unroll
-      for (int tn = 0; tn < TN; ++tn)
-        bf[tn] = *reinterpret_cast<const bf16x8_t*>(
-            &Bs[cur][(wn * 128 + tn * 16 + frow) * kBK + coff]);
-#pragma unroll
-      for (int tm = 0; tm < TM; ++tm)
-        af[tm] = *reinterpret_cast<const bf16x8_t*>(
-            &As[cur][(wm * WM + tm * 16 + frow) * kBK + coff]);
-#pragma unroll
-      for (int tn = 0; tn < TN; ++tn)
-#pragma unroll
-        for (int tm = 0; tm < TM; ++tm)
-          acc[tn][tm] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(bf[tn], af[tm], acc[tn][tm], 0, 0, 0);
-    }
-    if (kt + 1 < KT) lstore_stage<A_LOADS, B_LOADS>(As[cur ^ 1], Bs[cur ^ 1], lrow, sw, ra, rb);
-    __syncthreads();
+  constexpr int LPW = IO::A_GRP + IO::B_GRP;   // direct-to-LDS loads per wave per stage
+  // prologue: stages 0, 1, 2 in flight (loads past the last stage repeat the last stage,
+  // which keeps the count of loads in flight the same at every barrier)
+  io.dma(As0, Bs0, 0);
+  io.dma(As1, Bs1, min(1, KT - 1) * kBK);
+  io.dma(As2, Bs2, min(2, KT - 1) * kBK);
+  barrier_keep_loads<2 * LPW>();
+#define MOE_STAGE(RA, RB, DA, DB, AHEAD)                                                   \
+  do {                                                                                     \
+    io.dma(DA, DB, min(kt + (AHEAD), KT - 1) * kBK);                                       \
+    gemm_stage<BM, EPI == EPI_SWIGLU, KSPLIT>(io, RA, RB, acc);                            \
+    barrier_keep_loads<2 * LPW>();                                                         \
+  } while (0)
+  int kt = 0;
+  for (; kt + 4 <= KT; kt += 4) {
+    MOE_STAGE(As0, Bs0, As3, Bs3, 3);
+    MOE_STAGE(As1, Bs1, As0, Bs0, 4);
+    MOE_STAGE(As2, Bs2, As1, Bs1, 5);
+    MOE_STAGE(As3, Bs3, As2, Bs2, 6);
   }
+  if (kt < KT) MOE_STAGE(As0, Bs0, As3, Bs3, 3);
+  if (kt + 1 < KT) MOE_STAGE(As1, Bs1, As0, Bs0, 4);
+  if (kt + 2 < KT) MOE_STAGE(As2, Bs2, As1, Bs1, 5);
+#undef MOE_STAGE
+  // no load may still be writing this workgroup's LDS when it exits
+  __builtin_amdgcn_s_waitcnt(0);
 
-  // ---------------- epilogue: lane holds rows (lane & 15), columns 4*(lane >> 4) + r
+  // ---------------- epilogue: register 4q + r of tile (tn, tm) is the output element
+  // (activation row tm*M + row(lane), weight row tn*M + ni(q, lane) + r); the four r are
+  // consecutive output columns (one 8-byte store of bf16)
   uint16_t* __restrict__ C = static_cast<uint16_t*>(g.c);
-  const int nq = 4 * (lane >> 4);
+  constexpr int NQ = S::ACC / 4;
   if (EPI == EPI_SWIGLU) {
 #pragma unroll
     for (int tn = 0; tn < TN / 2; ++tn) {
-      const int col = tile.nt * 128 + wn * 64 + tn * 16 + nq;
 #pragma unroll
-      for (int tm = 0; tm < TM; ++tm) {
-        const int m = wm * WM + tm * 16 + frow;
-        if (m < tile.m_valid && col < g.n_out) {
-          const f32x4_t gv = acc[tn][tm], uv = acc[tn + TN / 2][tm];
-          *reinterpret_cast<uint2*>(C + (tile.row0 + m) * g.ldc + col) =
-              pack_bf16x4(silu(gv[0]) * uv[0], silu(gv[1]) * uv[1], silu(gv[2]) * uv[2],
-                          silu(gv[3]) * uv[3]);
+      for (int q = 0; q < NQ; ++q) {
+        const int col = tile.nt * 128 + wn * 64 + tn * S::M + S::ni(q, lane);
+#pragma unroll
+        for (int tm = 0; tm < TM; ++tm) {
+          const int m = wm * WM + tm * S::M + frow;
+          if (m < tile.m_valid && col < g.n_out) {
+            float v[4];
+#pragma unroll
+            for (int r = 0; r < 4; ++r)
+              v[r] = silu(acc[tn][tm][4 * q + r]) * acc[tn + TN / 2][tm][4 * q + r];
+            *reinterpret_cast<uint2*>(C + (tile.row0 + m) * g.ldc + col) =
+                pack_bf16x4(v[0], v[1], v[2], v[3]);
+          }
         }
       }
     }
@@ -287,24 +437,27 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_bf16_kernel(GemmArgs g) {
     const uint16_t* bias = static_cast<const uint16_t*>(g.bias);
 #pragma unroll
     for (int tn = 0; tn < TN; ++tn) {
-      const int col = tile.nt * 256 + wn * 128 + tn * 16 + nq;
-      float bv[4] = {0.f, 0.f, 0.f, 0.f};
-      if (bias != nullptr && col < g.n_out) {
 #pragma unroll
-        for (int r = 0; r < 4; ++r) bv[r] = bf16_to_f32(bias[tile.seg * g.bias_seg_stride + col + r]);
-      }
+      for (int q = 0; q < NQ; ++q) {
+        const int col = tile.nt * 256 + wn * 128 + tn * S::M + S::ni(q, lane);
+        float bv[4] = {0.f, 0.f, 0.f, 0.f};
+        if (bias != nullptr && col < g.n_out) {
 #pragma unroll
-      for (int tm = 0; tm < TM; ++tm) {
-        const int m = wm * WM + tm * 16 + frow;
-        if (m < tile.m_valid && col < g.n_out) {
-          float v[4];
+          for (int r = 0; r < 4; ++r) bv[r] = bf16_to_f32(bias[tile.seg * g.bias_seg_stride + col + r]);
+        }
 #pragma unroll
-          for (int r = 0; r < 4; ++r) {
-            v[r] = acc[tn][tm][r] + bv[r];
-            if (EPI == EPI_GELU) v[r] = gelu_erf(v[r]);
+        for (int tm = 0; tm < TM; ++tm) {
+          const int m = wm * WM + tm * S::M + frow;
+          if (m < tile.m_valid && col < g.n_out) {
+            float v[4];
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+              v[r] = acc[tn][tm][4 * q + r] + bv[r];
+              if (EPI == EPI_GELU) v[r] = gelu_erf(v[r]);
+            }
+            *reinterpret_cast<uint2*>(C + (tile.row0 + m) * g.ldc + col) =
+                pack_bf16x4(v[0], v[1], v[2], v[3]);
           }
-          *reinterpret_cast<uint2*>(C + (tile.row0 + m) * g.ldc + col) =
-              pack_bf16x4(v[0], v[1], v[2], v[3]);
         }
       }
     }
