@@ -43,7 +43,7 @@ constexpr int kBRows = 256;   // bf16: weight rows per workgroup
 #define MOE_GEMM_GROUP_N 8
 #endif
 #ifndef MOE_GEMM_XCD_REMAP
-#define MOE_GEMM_XCD_REMAP 1
+#define MOE_GEMM_XCD_REMAP 0
 #endif
 constexpr int kGroupN = MOE_GEMM_GROUP_N;  // column tiles per scheduling group
 constexpr int kXcds = 8;
@@ -242,78 +242,105 @@ struct TileIO {
   }
 };
 
-// Scheduling hints for the k-steps of one stage: the fragment reads of k-step ks+1
-// are spread between the MFMAs of k-step ks.
-template <int KS, int KSTEPS, int R, int P, int SLOT>
-__device__ __forceinline__ void sched_kstep() {
-  if constexpr (KS + 1 < KSTEPS) {
-    if constexpr (SLOT < R) {
-      constexpr int lo = SLOT * P / R, hi = (SLOT + 1) * P / R;
-      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
-      if constexpr (hi > lo) __builtin_amdgcn_sched_group_barrier(0x008, hi - lo, 0);
-      sched_kstep<KS, KSTEPS, R, P, SLOT + 1>();
-    } else {
-      sched_kstep<KS + 1, KSTEPS, R, P, 0>();
-    }
-  } else if constexpr (KS + 1 == KSTEPS) {
-    __builtin_amdgcn_sched_group_barrier(0x008, P, 0);
-  }
+// Fragments of one k-step: TN weight fragments and TM activation fragments (16 bytes
+// each, one ds_read_b128 apiece).
+template <class IO>
+struct Frags {
+  bf16x8_t w[IO::TN];
+  bf16x8_t a[IO::TM];
+};
+
+template <class IO>
+__device__ __forceinline__ void read_frags(const IO& io, const uint16_t* __restrict__ ac,
+                                           const uint16_t* __restrict__ bc, int ks,
+                                           Frags<IO>& f) {
+  using S = typename IO::S;
+#pragma unroll
+  for (int tn = 0; tn < IO::TN; ++tn)
+    f.w[tn] = *reinterpret_cast<const bf16x8_t*>(&bc[io.b_row + tn * S::M * kBK + io.co[ks]]);
+#pragma unroll
+  for (int tm = 0; tm < IO::TM; ++tm)
+    f.a[tm] = *reinterpret_cast<const bf16x8_t*>(&ac[io.a_row + tm * S::M * kBK + io.co[ks]]);
 }
 
-// One K stage (32 deep) of MFMAs over the fragments in (ac, bc); fragments of the next
-// k-step are requested from LDS before the current k-step's MFMAs are issued.
-template <int BM, bool DUAL, bool KSPLIT>
-__device__ __forceinline__ void gemm_stage(
-    const TileIO<BM, DUAL, KSPLIT>& io, const uint16_t* __restrict__ ac,
-    const uint16_t* __restrict__ bc,
-    typename Mfma<TileIO<BM, DUAL, KSPLIT>::MF>::acc_t (&acc)[TileIO<BM, DUAL, KSPLIT>::TN]
-                                                             [TileIO<BM, DUAL, KSPLIT>::TM]) {
-  using IO = TileIO<BM, DUAL, KSPLIT>;
-  using S = typename IO::S;
-  constexpr int TM = IO::TM, TN = IO::TN, KS = S::KSTEPS;
-  bf16x8_t wf[2][TN], af[2][TM];
+template <class IO>
+__device__ __forceinline__ void mma_frags(
+    const Frags<IO>& f, typename IO::S::acc_t (&acc)[IO::TN][IO::TM]) {
 #pragma unroll
-  for (int tn = 0; tn < TN; ++tn)
-    wf[0][tn] = *reinterpret_cast<const bf16x8_t*>(&bc[io.b_row + tn * S::M * kBK + io.co[0]]);
+  for (int tn = 0; tn < IO::TN; ++tn)
 #pragma unroll
-  for (int tm = 0; tm < TM; ++tm)
-    af[0][tm] = *reinterpret_cast<const bf16x8_t*>(&ac[io.a_row + tm * S::M * kBK + io.co[0]]);
-#pragma unroll
-  for (int ks = 0; ks < KS; ++ks) {
-    const int c = ks & 1;
-    if (ks + 1 < KS) {
-#pragma unroll
-      for (int tn = 0; tn < TN; ++tn)
-        wf[c ^ 1][tn] =
-            *reinterpret_cast<const bf16x8_t*>(&bc[io.b_row + tn * S::M * kBK + io.co[ks + 1]]);
-#pragma unroll
-      for (int tm = 0; tm < TM; ++tm)
-        af[c ^ 1][tm] =
-            *reinterpret_cast<const bf16x8_t*>(&ac[io.a_row + tm * S::M * kBK + io.co[ks + 1]]);
-    }
-#pragma unroll
-    for (int tn = 0; tn < TN; ++tn)
-#pragma unroll
-      for (int tm = 0; tm < TM; ++tm) acc[tn][tm] = S::mma(wf[c][tn], af[c][tm], acc[tn][tm]);
+    for (int tm = 0; tm < IO::TM; ++tm) acc[tn][tm] = IO::S::mma(f.w[tn], f.a[tm], acc[tn][tm]);
+}
+
+// Scheduling hints for the P MFMAs of one k-step together with V direct-to-LDS loads
+// and R fragment reads: slot i (i < NSLOT) issues one MFMA, then its share of the loads
+// and reads; the remaining MFMAs follow.  The memory operations are front-loaded so the
+// last fragment read completes well before the k-step that consumes it (or the
+// lgkmcnt wait of the stage boundary), while the matrix core always has an MFMA queued.
+template <int V, int R, int P, int SLOT, int NSLOT>
+__device__ __forceinline__ void sched_mix() {
+  if constexpr (SLOT < NSLOT) {
+    constexpr int v_lo = SLOT * V / NSLOT, v_hi = (SLOT + 1) * V / NSLOT;
+    constexpr int r_lo = SLOT * R / NSLOT, r_hi = (SLOT + 1) * R / NSLOT;
+    if constexpr (SLOT < P) __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+    if constexpr (v_hi > v_lo) __builtin_amdgcn_sched_group_barrier(0x010, v_hi - v_lo, 0);
+    if constexpr (r_hi > r_lo) __builtin_amdgcn_sched_group_barrier(0x100, r_hi - r_lo, 0);
+    sched_mix<V, R, P, SLOT + 1, NSLOT>();
+  } else if constexpr (P > NSLOT) {
+    __builtin_amdgcn_sched_group_barrier(0x008, P - NSLOT, 0);
   }
-  __builtin_amdgcn_sched_group_barrier(0x100, TN + TM, 0);
-  sched_kstep<0, KS, TN + TM, TN * TM, 0>();
 }
 
 // Stage boundary of the LDS ring: wait until this wave's own LDS reads are done and at
 // most N of its direct-to-LDS loads are still in flight (the stages after the next one),
 // then a workgroup barrier.  A full __syncthreads would also drain the loads that are
 // meant to stay in flight.  The empty asm statements keep the compiler from moving
-// memory accesses across the barrier; they emit no instruction.
+// memory accesses across the barrier and the scheduling barriers keep every other
+// instruction on its side; none of them emits an instruction.
 template <int N>
 __device__ __forceinline__ void barrier_keep_loads() {
   static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_sched_barrier(0);  // no instruction (MFMAs included) crosses the boundary
   // s_waitcnt fields (gfx9): vmcnt [3:0] and [15:14], expcnt [6:4] (7 = no wait),
   // lgkmcnt [11:8] (0 = all LDS operations done)
   __builtin_amdgcn_s_waitcnt((N & 0xF) | ((N >> 4) << 14) | (0x7 << 4));
   asm volatile("" ::: "memory");
   __builtin_amdgcn_s_barrier();
   asm volatile("" ::: "memory");
+  __builtin_amdgcn_sched_barrier(0);
+}
+
+// One stage of the ring.  On entry `fa` holds k-step 0 of this stage (buffer ac/bc).
+// The stage boundary sits before the MFMAs of the last k-step: the barrier there
+// releases this stage's buffer (every wave has finished reading it) and makes the next
+// stage's buffer (an/bn) visible, so the refill of ac/bc with stage `k_next` and the
+// reads of the next stage's first fragments are issued between the last k-step's
+// MFMAs and the matrix cores do not wait for the barrier.  With one k-step per stage
+// the two fragment sets swap roles from stage to stage.
+template <class IO, int LPW>
+__device__ __forceinline__ void pipe_stage(const IO& io, uint16_t* ac, uint16_t* bc,
+                                           const uint16_t* an, const uint16_t* bn,
+                                           int k_next, Frags<IO>& fa, Frags<IO>& fb,
+                                           typename IO::S::acc_t (&acc)[IO::TN][IO::TM]) {
+  constexpr int KS = IO::S::KSTEPS;
+  constexpr int R = IO::TN + IO::TM, P = IO::TN * IO::TM;
+  static_assert(KS == 1 || KS == 2, "one or two k-steps per stage");
+  if constexpr (KS == 2) {
+    read_frags(io, ac, bc, 1, fb);
+    mma_frags(fa, acc);
+    sched_mix<0, R, P, 0, R>();
+    barrier_keep_loads<2 * LPW>();
+    io.dma(ac, bc, k_next);
+    read_frags(io, an, bn, 0, fa);
+    mma_frags(fb, acc);
+    sched_mix<LPW, R, P, 0, (R > LPW ? R : LPW)>();
+  } else {
+    barrier_keep_loads<2 * LPW>();
+    io.dma(ac, bc, k_next);
+    read_frags(io, an, bn, 0, fb);
+    mma_frags(fa, acc);
+    sched_mix<LPW, R, P, 0, (R > LPW ? R : LPW)>();
+  }
 }
 
 // ------------------------------------------------------------------ bf16 MFMA kernel
@@ -382,28 +409,29 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_bf16_kernel(GemmArgs g) {
 
   const int KT = g.k / kBK;
   constexpr int LPW = IO::A_GRP + IO::B_GRP;   // direct-to-LDS loads per wave per stage
-  // prologue: stages 0, 1, 2 in flight (loads past the last stage repeat the last stage,
-  // which keeps the count of loads in flight the same at every barrier)
+  // prologue: stages 0..3 in flight (loads past the last stage repeat the last stage,
+  // which keeps the count of loads in flight the same at every barrier), then the
+  // first fragments of stage 0
   io.dma(As0, Bs0, 0);
   io.dma(As1, Bs1, min(1, KT - 1) * kBK);
   io.dma(As2, Bs2, min(2, KT - 1) * kBK);
-  barrier_keep_loads<2 * LPW>();
-#define MOE_STAGE(RA, RB, DA, DB, AHEAD)                                                   \
-  do {                                                                                     \
-    io.dma(DA, DB, min(kt + (AHEAD), KT - 1) * kBK);                                       \
-    gemm_stage<BM, EPI == EPI_SWIGLU, KSPLIT>(io, RA, RB, acc);                            \
-    barrier_keep_loads<2 * LPW>();                                                         \
-  } while (0)
+  io.dma(As3, Bs3, min(3, KT - 1) * kBK);
+  barrier_keep_loads<3 * LPW>();
+  Frags<IO> f0, f1;
+  read_frags(io, As0, Bs0, 0, f0);
+  constexpr bool kSwap = S::KSTEPS == 1;  // fragment sets alternate between stages
+#define MOE_STAGE(RA, RB, NA, NB, AHEAD, FA, FB)                                           \
+  pipe_stage<IO, LPW>(io, RA, RB, NA, NB, min(kt + (AHEAD), KT - 1) * kBK, FA, FB, acc)
   int kt = 0;
   for (; kt + 4 <= KT; kt += 4) {
-    MOE_STAGE(As0, Bs0, As3, Bs3, 3);
-    MOE_STAGE(As1, Bs1, As0, Bs0, 4);
-    MOE_STAGE(As2, Bs2, As1, Bs1, 5);
-    MOE_STAGE(As3, Bs3, As2, Bs2, 6);
+    MOE_STAGE(As0, Bs0, As1, Bs1, 4, f0, f1);
+    MOE_STAGE(As1, Bs1, As2, Bs2, 5, kSwap ? f1 : f0, kSwap ? f0 : f1);
+    MOE_STAGE(As2, Bs2, As3, Bs3, 6, f0, f1);
+    MOE_STAGE(As3, Bs3, As0, Bs0, 7, kSwap ? f1 : f0, kSwap ? f0 : f1);
   }
-  if (kt < KT) MOE_STAGE(As0, Bs0, As3, Bs3, 3);
-  if (kt + 1 < KT) MOE_STAGE(As1, Bs1, As0, Bs0, 4);
-  if (kt + 2 < KT) MOE_STAGE(As2, Bs2, As1, Bs1, 5);
+  if (kt < KT) MOE_STAGE(As0, Bs0, As1, Bs1, 4, f0, f1);
+  if (kt + 1 < KT) MOE_STAGE(As1, Bs1, As2, Bs2, 5, kSwap ? f1 : f0, kSwap ? f0 : f1);
+  if (kt + 2 < KT) MOE_STAGE(As2, Bs2, As3, Bs3, 6, f0, f1);
 #undef MOE_STAGE
   // no load may still be writing this workgroup's LDS when it exits
   __builtin_amdgcn_s_waitcnt(0);
