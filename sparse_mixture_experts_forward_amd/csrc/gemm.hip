@@ -18,7 +18,7 @@
 //     barrier that waits only for the loads of the next stage, so the other two stay
 //     in flight across it;
 //   * LDS rows are 64 bytes; the 16-byte chunk c of row r is stored at chunk
-//     c ^ ((r >> 1) & 3), which keeps the fragment reads free of bank conflicts;
+//     c ^ lds_swizzle(r), which keeps the fragment reads free of bank conflicts;
 //   * SwiGLU: each wave's 128 weight rows are 64 rows of W1 followed by the same 64 rows
 //     of W3, so g and u of an output element sit in the same lane;
 //   * scheduling happens on the device: every workgroup scans the segment offsets
@@ -36,8 +36,7 @@ namespace moe {
 namespace {
 
 constexpr int kThreads = 256;
-constexpr int kBK = 32;       // bf16: reduction depth per LDS stage
-constexpr int kStages = 4;    // LDS ring depth (loads run kStages-1 stages ahead)
+constexpr int kBK = 64;       // bf16: reduction depth per LDS stage (128-byte rows)
 constexpr int kBRows = 256;   // bf16: weight rows per workgroup
 #ifndef MOE_GEMM_GROUP_N
 #define MOE_GEMM_GROUP_N 8
@@ -146,6 +145,13 @@ __device__ bool schedule_tile(const int32_t* __restrict__ seg_off, int n_seg,
   return true;
 }
 
+// Physical 16-byte chunk of a 128-byte LDS row r: logical chunk c is stored at c ^ f(r)
+// with f(r) = ((r >> 1) ^ ((r & 1) << 2)) & 7.  A ds_read_b128 of a fragment has lanes
+// on consecutive rows and one logical chunk; f makes every 8 consecutive rows (served
+// together when the LDS delivers 128 bytes a cycle) and every 16 consecutive rows
+// (256 bytes a cycle) land on distinct banks.  f depends on bits 0..3 of r only.
+__device__ __forceinline__ int lds_swizzle(int r) { return ((r >> 1) ^ ((r & 1) << 2)) & 7; }
+
 __device__ __forceinline__ uint2 pack_bf16x4(float a, float b, float c, float d) {
   uint2 r;
   r.x = static_cast<uint32_t>(f32_to_bf16(a)) | (static_cast<uint32_t>(f32_to_bf16(b)) << 16);
@@ -201,11 +207,10 @@ struct TileIO {
   static constexpr int WM = BM / 2;            // activation rows per wave
   static constexpr int TM = WM / S::M;         // MFMA tiles per wave along activation rows
   static constexpr int TN = 128 / S::M;        // MFMA tiles per wave along weight rows
-  static constexpr int A_GRPS = BM / 16;                   // 16-row groups of A per stage
-  static constexpr int A_GRP = A_GRPS >= 4 ? A_GRPS / 4 : 1;  // per wave (every wave issues the
-                                                           // same count; with fewer groups than
-                                                           // waves, waves repeat a group)
-  static constexpr int B_GRP = kBRows / 64;    // 16-row groups per wave per stage (B)
+  static constexpr int A_GRPS = BM / 8;        // 8-row load groups of A per stage
+  static constexpr int A_GRP = A_GRPS / 4;     // per wave
+  static constexpr int B_GRP = kBRows / 32;    // 8-row load groups of B per wave per stage
+  static_assert(A_GRPS % 4 == 0, "BM must be a multiple of 32");
   const uint16_t* a_base;
   const uint16_t* b_base0;
   const uint16_t* b_base1;
@@ -215,8 +220,9 @@ struct TileIO {
   int co[S::KSTEPS];      // swizzled element offset of this lane's chunk per k-step
   int64_t kchunk, kbatch_stride;
 
-  // One stage of loads: wave w fills the 8-row groups w, w+4, ... of A and B.  Lane l
-  // writes LDS row 8*group + l/8, physical chunk l%8, i.e. logical chunk (l%8)^(l/8).
+  // One stage of loads: wave w fills the 8-row groups w, w+4, ... of A and B; one
+  // instruction moves 8 rows x 128 bytes (whole cache lines).  Lane l writes LDS row
+  // 8*group + l/8, physical chunk l%8, and so loads logical chunk (l%8) ^ f(row).
   // Addresses are a wave-uniform base that carries k plus a loop-invariant unsigned
   // 32-bit lane offset (the scalar-base form of the load).
   __device__ __forceinline__ void dma(uint16_t* as, uint16_t* bs, int k0) const {
@@ -231,45 +237,50 @@ struct TileIO {
 #pragma unroll
     for (int j = 0; j < A_GRP; ++j)
       __builtin_amdgcn_global_load_lds((global_void_t*)(ak + a_off[j]),
-                                       (lds_void_t*)(as + ((wave + 4 * j) % A_GRPS) * 16 * kBK),
-                                       16, 0, 0);
+                                       (lds_void_t*)(as + (wave + 4 * j) * 8 * kBK), 16, 0, 0);
 #pragma unroll
     for (int j = 0; j < B_GRP; ++j) {
-      const char* bb = (DUAL && (j & 1)) ? bk1 : bk0;
+      // SwiGLU: LDS rows with bit 6 set (groups j = 2, 3 mod 4) hold W3 rows
+      const char* bb = (DUAL && ((j >> 1) & 1)) ? bk1 : bk0;
       __builtin_amdgcn_global_load_lds((global_void_t*)(bb + b_off[j]),
-                                       (lds_void_t*)(bs + (wave + 4 * j) * 16 * kBK), 16, 0, 0);
+                                       (lds_void_t*)(bs + (wave + 4 * j) * 8 * kBK), 16, 0, 0);
     }
   }
 };
 
-// Fragments of one k-step: TN weight fragments and TM activation fragments (16 bytes
-// each, one ds_read_b128 apiece).
+// Fragments of one k-step: TN weight fragments and up to TM activation fragments (16
+// bytes each, one ds_read_b128 apiece).  A wave owns the activation row blocks wm,
+// wm + 2, wm + 4, ... (blocks of S::M rows); TA of them hold rows of the tile, and only
+// those are read and multiplied (TA = 0: the wave only helps with the loads).
 template <class IO>
 struct Frags {
   bf16x8_t w[IO::TN];
   bf16x8_t a[IO::TM];
 };
 
-template <class IO>
+template <class IO, int TA>
 __device__ __forceinline__ void read_frags(const IO& io, const uint16_t* __restrict__ ac,
                                            const uint16_t* __restrict__ bc, int ks,
                                            Frags<IO>& f) {
   using S = typename IO::S;
+  if constexpr (TA > 0) {
 #pragma unroll
-  for (int tn = 0; tn < IO::TN; ++tn)
-    f.w[tn] = *reinterpret_cast<const bf16x8_t*>(&bc[io.b_row + tn * S::M * kBK + io.co[ks]]);
+    for (int tn = 0; tn < IO::TN; ++tn)
+      f.w[tn] = *reinterpret_cast<const bf16x8_t*>(&bc[io.b_row + tn * S::M * kBK + io.co[ks]]);
 #pragma unroll
-  for (int tm = 0; tm < IO::TM; ++tm)
-    f.a[tm] = *reinterpret_cast<const bf16x8_t*>(&ac[io.a_row + tm * S::M * kBK + io.co[ks]]);
+    for (int tm = 0; tm < TA; ++tm)
+      f.a[tm] =
+          *reinterpret_cast<const bf16x8_t*>(&ac[io.a_row + tm * 2 * S::M * kBK + io.co[ks]]);
+  }
 }
 
-template <class IO>
+template <class IO, int TA>
 __device__ __forceinline__ void mma_frags(
     const Frags<IO>& f, typename IO::S::acc_t (&acc)[IO::TN][IO::TM]) {
 #pragma unroll
   for (int tn = 0; tn < IO::TN; ++tn)
 #pragma unroll
-    for (int tm = 0; tm < IO::TM; ++tm) acc[tn][tm] = IO::S::mma(f.w[tn], f.a[tm], acc[tn][tm]);
+    for (int tm = 0; tm < TA; ++tm) acc[tn][tm] = IO::S::mma(f.w[tn], f.a[tm], acc[tn][tm]);
 }
 
 // Scheduling hints for the P MFMAs of one k-step together with V direct-to-LDS loads
@@ -310,146 +321,98 @@ __device__ __forceinline__ void barrier_keep_loads() {
   __builtin_amdgcn_sched_barrier(0);
 }
 
-// One stage of the ring.  On entry `fa` holds k-step 0 of this stage (buffer ac/bc).
-// The stage boundary sits before the MFMAs of the last k-step: the barrier there
-// releases this stage's buffer (every wave has finished reading it) and makes the next
-// stage's buffer (an/bn) visible, so the refill of ac/bc with stage `k_next` and the
-// reads of the next stage's first fragments are issued between the last k-step's
-// MFMAs and the matrix cores do not wait for the barrier.  With one k-step per stage
-// the two fragment sets swap roles from stage to stage.
-template <class IO, int LPW>
-__device__ __forceinline__ void pipe_stage(const IO& io, uint16_t* ac, uint16_t* bc,
-                                           const uint16_t* an, const uint16_t* bn,
-                                           int k_next, Frags<IO>& fa, Frags<IO>& fb,
-                                           typename IO::S::acc_t (&acc)[IO::TN][IO::TM]) {
-  constexpr int KS = IO::S::KSTEPS;
-  constexpr int R = IO::TN + IO::TM, P = IO::TN * IO::TM;
-  static_assert(KS == 1 || KS == 2, "one or two k-steps per stage");
-  if constexpr (KS == 2) {
-    read_frags(io, ac, bc, 1, fb);
-    mma_frags(fa, acc);
-    sched_mix<0, R, P, 0, R>();
-    barrier_keep_loads<2 * LPW>();
-    io.dma(ac, bc, k_next);
-    read_frags(io, an, bn, 0, fa);
-    mma_frags(fb, acc);
-    sched_mix<LPW, R, P, 0, (R > LPW ? R : LPW)>();
-  } else {
-    barrier_keep_loads<2 * LPW>();
-    io.dma(ac, bc, k_next);
-    read_frags(io, an, bn, 0, fb);
-    mma_frags(fa, acc);
-    sched_mix<LPW, R, P, 0, (R > LPW ? R : LPW)>();
+// Multiply-and-read steps ks = KS .. K1-1 of a stage: the fragments of k-step ks are in
+// f[ks & 1] while those of k-step ks + 1 are read into the other set.
+template <class IO, int TA, int KS, int K1>
+__device__ __forceinline__ void inner_steps(const IO& io, const uint16_t* ac, const uint16_t* bc,
+                                            Frags<IO> (&f)[2],
+                                            typename IO::S::acc_t (&acc)[IO::TN][IO::TM]) {
+  if constexpr (KS < K1) {
+    constexpr int R = TA > 0 ? IO::TN + TA : 0, P = IO::TN * TA;
+    read_frags<IO, TA>(io, ac, bc, KS + 1, f[(KS + 1) & 1]);
+    mma_frags<IO, TA>(f[KS & 1], acc);
+    sched_mix<0, R, P, 0, (R > 0 ? R : 1)>();
+    inner_steps<IO, TA, KS + 1, K1>(io, ac, bc, f, acc);
   }
 }
 
-// ------------------------------------------------------------------ bf16 MFMA kernel
-template <int BM, int EPI, bool KSPLIT>
-__global__ __launch_bounds__(kThreads, 1) void gemm_bf16_kernel(GemmArgs g) {
-  using IO = TileIO<BM, EPI == EPI_SWIGLU, KSPLIT>;
+// One stage of the two-buffer LDS ring.  On entry f[0] holds k-step 0 of this stage
+// (buffer ac/bc) and the loads of the next stage (buffer an/bn) are in flight.  The
+// stage boundary sits before the MFMAs of the last k-step: the barrier there releases
+// this stage's buffer (every wave has read all its fragments) and makes the next
+// stage's buffer visible, so the refill of ac/bc with the stage after next and the
+// reads of the next stage's first fragments are issued between the last k-step's MFMAs
+// and the matrix cores do not wait for the barrier.  Past the last stage the refill
+// repeats the last stage (kept unconditional so that the loads stay interleaved with
+// the MFMAs; the data is never read).
+template <class IO, int LPW, int TA>
+__device__ __forceinline__ void pipe_stage(const IO& io, uint16_t* ac, uint16_t* bc,
+                                           const uint16_t* an, const uint16_t* bn,
+                                           int k_refill, Frags<IO> (&f)[2],
+                                           typename IO::S::acc_t (&acc)[IO::TN][IO::TM]) {
+  constexpr int KS = IO::S::KSTEPS;
+  constexpr int R = TA > 0 ? IO::TN + TA : 0, P = IO::TN * TA;
+  constexpr int NSLOT = R > LPW ? R : LPW;
+  static_assert(KS % 2 == 0, "an even number of k-steps per stage");
+  inner_steps<IO, TA, 0, KS - 1>(io, ac, bc, f, acc);
+  barrier_keep_loads<0>();
+  io.dma(ac, bc, k_refill);
+  read_frags<IO, TA>(io, an, bn, 0, f[0]);
+  mma_frags<IO, TA>(f[1], acc);
+  sched_mix<LPW, R, P, 0, NSLOT>();
+}
+
+// The K loop of one tile for a wave with TA active row blocks.  On entry the loads of
+// stages 0 and 1 are in flight and stage 0 is visible to the workgroup.
+template <class IO, int LPW, int TA>
+__device__ __forceinline__ void k_loop(const IO& io, uint16_t* As0, uint16_t* Bs0, uint16_t* As1,
+                                       uint16_t* Bs1, int KT,
+                                       typename IO::S::acc_t (&acc)[IO::TN][IO::TM]) {
+  Frags<IO> f[2];
+  read_frags<IO, TA>(io, As0, Bs0, 0, f[0]);
+  int kt = 0;
+  for (; kt + 2 <= KT; kt += 2) {
+    pipe_stage<IO, LPW, TA>(io, As0, Bs0, As1, Bs1, min(kt + 2, KT - 1) * kBK, f, acc);
+    pipe_stage<IO, LPW, TA>(io, As1, Bs1, As0, Bs0, min(kt + 3, KT - 1) * kBK, f, acc);
+  }
+  if (kt < KT) pipe_stage<IO, LPW, TA>(io, As0, Bs0, As1, Bs1, (KT - 1) * kBK, f, acc);
+}
+
+// The rest of a tile for a wave with TA active row blocks: the K loop, then the epilogue.
+// Each TA has its own accumulators, so no accumulator state is shared between the
+// variants.  Register 4q + r of tile (tn, tm) is the output element (activation row
+// (2 tm + wm)*M + row(lane), weight row tn*M + ni(q, lane) + r); the four r are
+// consecutive output columns (one 8-byte store of bf16).
+template <class IO, int LPW, int EPI, int TA>
+__device__ __forceinline__ void tile_body(const GemmArgs& g, const Tile& tile, const IO& io,
+                                          uint16_t* As0, uint16_t* Bs0, uint16_t* As1,
+                                          uint16_t* Bs1, int KT) {
   using S = typename IO::S;
-  constexpr int WM = IO::WM;
-  constexpr int TM = IO::TM;
   constexpr int TN = IO::TN;
-  static_assert(TM >= 1, "BM must be >= 32");
-  // the LDS ring as distinct objects, so that the compiler can tell the stage being read
-  // from the stages being filled
-  __shared__ __attribute__((aligned(16))) uint16_t As0[BM * kBK], As1[BM * kBK], As2[BM * kBK], As3[BM * kBK];
-  __shared__ __attribute__((aligned(16))) uint16_t Bs0[kBRows * kBK], Bs1[kBRows * kBK], Bs2[kBRows * kBK], Bs3[kBRows * kBK];
-  __shared__ SchedSmem sched;
-
-  const int n_ntiles = (EPI == EPI_SWIGLU) ? (g.n_out + 127) / 128 : (g.n_out + 255) / 256;
-  Tile tile;
-  if (!schedule_tile<BM>(g.seg_off, g.n_seg, g.single_rows, g.max_rows, n_ntiles, sched, tile))
-    return;
-
-  const int tid = threadIdx.x;
-  const int lane = tid & (kWave - 1);
-  const int wave = __builtin_amdgcn_readfirstlane(tid / kWave);  // uniform per wave
-  IO io;
-  io.wave = wave;
-  io.lane = lane;
-  io.wm = wave >> 1;
-  io.wn = wave & 1;
-  io.kchunk = g.kchunk;
-  io.kbatch_stride = g.kbatch_stride;
-  const int dl_row = lane >> 2;                                 // row inside a 16-row group
-  const int dl_chunk = ((lane & 3) ^ ((lane >> 3) & 3)) * 8;     // logical chunk this lane loads
-  io.a_base = static_cast<const uint16_t*>(g.a) + tile.row0 * g.lda;
-#pragma unroll
-  for (int j = 0; j < IO::A_GRP; ++j) {
-    const int r = min(16 * ((wave + 4 * j) % IO::A_GRPS) + dl_row, tile.m_valid - 1);
-    io.a_off[j] = static_cast<uint32_t>((r * static_cast<int32_t>(g.lda) + dl_chunk) * 2);
-  }
-  io.b_base0 = static_cast<const uint16_t*>(g.b0) + tile.seg * g.b_seg_stride;
-  io.b_base1 = (EPI == EPI_SWIGLU) ? static_cast<const uint16_t*>(g.b1) + tile.seg * g.b_seg_stride
-                                   : io.b_base0;
-#pragma unroll
-  for (int j = 0; j < IO::B_GRP; ++j) {
-    const int i = 16 * (wave + 4 * j) + dl_row;  // LDS row of the tile
-    int n = (EPI == EPI_SWIGLU) ? tile.nt * 128 + (i >> 7) * 64 + (i & 63) : tile.nt * 256 + i;
-    n = min(n, g.n_out - 1);
-    io.b_off[j] = static_cast<uint32_t>(n) * static_cast<uint32_t>(g.ldb) * 2u +
-                  static_cast<uint32_t>(dl_chunk * 2);
-  }
-  const int frow = S::row(lane);
-#pragma unroll
-  for (int ks = 0; ks < S::KSTEPS; ++ks) io.co[ks] = (S::chunk(lane, ks) ^ ((frow >> 1) & 3)) * 8;
-  io.b_row = (io.wn * 128 + frow) * kBK;
-  io.a_row = (io.wm * WM + frow) * kBK;
-  const int wm = io.wm, wn = io.wn;
-
-  typename S::acc_t acc[TN][TM];
+  typename S::acc_t acc[TN][IO::TM];
 #pragma unroll
   for (int a = 0; a < TN; ++a)
 #pragma unroll
-    for (int b = 0; b < TM; ++b)
+    for (int b = 0; b < TA; ++b)
 #pragma unroll
       for (int r = 0; r < S::ACC; ++r) acc[a][b][r] = 0.f;
-
-  const int KT = g.k / kBK;
-  constexpr int LPW = IO::A_GRP + IO::B_GRP;   // direct-to-LDS loads per wave per stage
-  // prologue: stages 0..3 in flight (loads past the last stage repeat the last stage,
-  // which keeps the count of loads in flight the same at every barrier), then the
-  // first fragments of stage 0
-  io.dma(As0, Bs0, 0);
-  io.dma(As1, Bs1, min(1, KT - 1) * kBK);
-  io.dma(As2, Bs2, min(2, KT - 1) * kBK);
-  io.dma(As3, Bs3, min(3, KT - 1) * kBK);
-  barrier_keep_loads<3 * LPW>();
-  Frags<IO> f0, f1;
-  read_frags(io, As0, Bs0, 0, f0);
-  constexpr bool kSwap = S::KSTEPS == 1;  // fragment sets alternate between stages
-#define MOE_STAGE(RA, RB, NA, NB, AHEAD, FA, FB)                                           \
-  pipe_stage<IO, LPW>(io, RA, RB, NA, NB, min(kt + (AHEAD), KT - 1) * kBK, FA, FB, acc)
-  int kt = 0;
-  for (; kt + 4 <= KT; kt += 4) {
-    MOE_STAGE(As0, Bs0, As1, Bs1, 4, f0, f1);
-    MOE_STAGE(As1, Bs1, As2, Bs2, 5, kSwap ? f1 : f0, kSwap ? f0 : f1);
-    MOE_STAGE(As2, Bs2, As3, Bs3, 6, f0, f1);
-    MOE_STAGE(As3, Bs3, As0, Bs0, 7, kSwap ? f1 : f0, kSwap ? f0 : f1);
-  }
-  if (kt < KT) MOE_STAGE(As0, Bs0, As1, Bs1, 4, f0, f1);
-  if (kt + 1 < KT) MOE_STAGE(As1, Bs1, As2, Bs2, 5, kSwap ? f1 : f0, kSwap ? f0 : f1);
-  if (kt + 2 < KT) MOE_STAGE(As2, Bs2, As3, Bs3, 6, f0, f1);
-#undef MOE_STAGE
+  k_loop<IO, LPW, TA>(io, As0, Bs0, As1, Bs1, KT, acc);
   // no load may still be writing this workgroup's LDS when it exits
   __builtin_amdgcn_s_waitcnt(0);
+  if constexpr (TA == 0) return;
 
-  // ---------------- epilogue: register 4q + r of tile (tn, tm) is the output element
-  // (activation row tm*M + row(lane), weight row tn*M + ni(q, lane) + r); the four r are
-  // consecutive output columns (one 8-byte store of bf16)
+  const int lane = io.lane, wm = io.wm, wn = io.wn, frow = S::row(lane);
   uint16_t* __restrict__ C = static_cast<uint16_t*>(g.c);
   constexpr int NQ = S::ACC / 4;
-  if (EPI == EPI_SWIGLU) {
+  if constexpr (EPI == EPI_SWIGLU) {
 #pragma unroll
     for (int tn = 0; tn < TN / 2; ++tn) {
 #pragma unroll
       for (int q = 0; q < NQ; ++q) {
         const int col = tile.nt * 128 + wn * 64 + tn * S::M + S::ni(q, lane);
 #pragma unroll
-        for (int tm = 0; tm < TM; ++tm) {
-          const int m = wm * WM + tm * S::M + frow;
+        for (int tm = 0; tm < TA; ++tm) {
+          const int m = (2 * tm + wm) * S::M + frow;
           if (m < tile.m_valid && col < g.n_out) {
             float v[4];
 #pragma unroll
@@ -471,11 +434,12 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_bf16_kernel(GemmArgs g) {
         float bv[4] = {0.f, 0.f, 0.f, 0.f};
         if (bias != nullptr && col < g.n_out) {
 #pragma unroll
-          for (int r = 0; r < 4; ++r) bv[r] = bf16_to_f32(bias[tile.seg * g.bias_seg_stride + col + r]);
+          for (int r = 0; r < 4; ++r)
+            bv[r] = bf16_to_f32(bias[tile.seg * g.bias_seg_stride + col + r]);
         }
 #pragma unroll
-        for (int tm = 0; tm < TM; ++tm) {
-          const int m = wm * WM + tm * S::M + frow;
+        for (int tm = 0; tm < TA; ++tm) {
+          const int m = (2 * tm + wm) * S::M + frow;
           if (m < tile.m_valid && col < g.n_out) {
             float v[4];
 #pragma unroll
@@ -489,6 +453,96 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_bf16_kernel(GemmArgs g) {
         }
       }
     }
+  }
+}
+
+// ------------------------------------------------------------------ bf16 MFMA kernel
+template <int BM, int EPI, bool KSPLIT>
+__global__ __launch_bounds__(kThreads, 1) void gemm_bf16_kernel(GemmArgs g) {
+  using IO = TileIO<BM, EPI == EPI_SWIGLU, KSPLIT>;
+  using S = typename IO::S;
+  constexpr int WM = IO::WM;
+  constexpr int TM = IO::TM;
+  constexpr int TN = IO::TN;
+  static_assert(TM >= 1, "BM must be >= 32");
+  // the LDS ring as distinct objects, so that the compiler can tell the stage being read
+  // from the stage being filled
+  __shared__ __attribute__((aligned(16))) uint16_t As0[BM * kBK], As1[BM * kBK];
+  __shared__ __attribute__((aligned(16))) uint16_t Bs0[kBRows * kBK], Bs1[kBRows * kBK];
+  __shared__ SchedSmem sched;
+
+  const int n_ntiles = (EPI == EPI_SWIGLU) ? (g.n_out + 127) / 128 : (g.n_out + 255) / 256;
+  Tile tile;
+  if (!schedule_tile<BM>(g.seg_off, g.n_seg, g.single_rows, g.max_rows, n_ntiles, sched, tile))
+    return;
+
+  const int tid = threadIdx.x;
+  const int lane = tid & (kWave - 1);
+  const int wave = __builtin_amdgcn_readfirstlane(tid / kWave);  // uniform per wave
+  IO io;
+  io.wave = wave;
+  io.lane = lane;
+  io.wm = wave >> 1;
+  io.wn = wave & 1;
+  io.kchunk = g.kchunk;
+  io.kbatch_stride = g.kbatch_stride;
+  const int dl_row = lane >> 3;  // row inside an 8-row load group
+  io.a_base = static_cast<const uint16_t*>(g.a) + tile.row0 * g.lda;
+#pragma unroll
+  for (int j = 0; j < IO::A_GRP; ++j) {
+    const int i = 8 * (wave + 4 * j) + dl_row;  // LDS row of the tile
+    const int r = min(i, tile.m_valid - 1);     // rows past the segment repeat its last row
+    const int chunk = ((lane & 7) ^ lds_swizzle(i)) * 8;
+    io.a_off[j] = static_cast<uint32_t>((r * static_cast<int32_t>(g.lda) + chunk) * 2);
+  }
+  io.b_base0 = static_cast<const uint16_t*>(g.b0) + tile.seg * g.b_seg_stride;
+  io.b_base1 = (EPI == EPI_SWIGLU) ? static_cast<const uint16_t*>(g.b1) + tile.seg * g.b_seg_stride
+                                   : io.b_base0;
+#pragma unroll
+  for (int j = 0; j < IO::B_GRP; ++j) {
+    const int i = 8 * (wave + 4 * j) + dl_row;  // LDS row of the tile
+    int n = (EPI == EPI_SWIGLU) ? tile.nt * 128 + (i >> 7) * 64 + (i & 63) : tile.nt * 256 + i;
+    n = min(n, g.n_out - 1);
+    const int chunk = ((lane & 7) ^ lds_swizzle(i)) * 8;
+    io.b_off[j] = static_cast<uint32_t>(n) * static_cast<uint32_t>(g.ldb) * 2u +
+                  static_cast<uint32_t>(chunk * 2);
+  }
+  const int frow = S::row(lane);
+#pragma unroll
+  for (int ks = 0; ks < S::KSTEPS; ++ks) io.co[ks] = (S::chunk(lane, ks) ^ lds_swizzle(frow)) * 8;
+  io.b_row = (io.wn * 128 + frow) * kBK;
+  io.a_row = (io.wm * S::M + frow) * kBK;  // row block wm; the wave's next blocks are 2 apart
+  const int wm = io.wm;
+
+  const int KT = g.k / kBK;
+  constexpr int LPW = IO::A_GRP + IO::B_GRP;   // direct-to-LDS loads per wave per stage
+  // prologue: stages 0 and 1 in flight
+  io.dma(As0, Bs0, 0);
+  if (KT > 1) io.dma(As1, Bs1, kBK);
+  if (KT > 1)
+    barrier_keep_loads<LPW>();
+  else
+    barrier_keep_loads<0>();
+  // row blocks of this wave that hold rows of the tile (every wave runs the same stages
+  // and barriers; only the MFMA work differs)
+  const int nb = (tile.m_valid + S::M - 1) / S::M;
+  const int ta = __builtin_amdgcn_readfirstlane(min(max((nb - wm + 1) / 2, 0), TM));
+  if (ta >= TM) {
+    tile_body<IO, LPW, EPI, TM>(g, tile, io, As0, Bs0, As1, Bs1, KT);
+  } else if constexpr (TM > 1) {
+    if (ta == 0)
+      tile_body<IO, LPW, EPI, 0>(g, tile, io, As0, Bs0, As1, Bs1, KT);
+    else if (ta == 1)
+      tile_body<IO, LPW, EPI, 1>(g, tile, io, As0, Bs0, As1, Bs1, KT);
+    else if constexpr (TM > 2) {
+      if (ta == 2)
+        tile_body<IO, LPW, EPI, 2>(g, tile, io, As0, Bs0, As1, Bs1, KT);
+      else if constexpr (TM > 3) {
+        if (ta == 3) tile_body<IO, LPW, EPI, 3>(g, tile, io, As0, Bs0, As1, Bs1, KT);
+      }
+    }
+  } else {
+    tile_body<IO, LPW, EPI, 0>(g, tile, io, As0, Bs0, As1, Bs1, KT);
   }
 }
 
@@ -606,9 +660,10 @@ hipError_t launch_bf16_epi(hipStream_t st, const GemmArgs& g, int64_t max_rows) 
   const bool ksplit = g.kchunk != g.k;
   const int n_seg_eff = g.seg_off ? g.n_seg : 1;
   const int64_t avg = max_rows / (n_seg_eff > 0 ? n_seg_eff : 1);
-  if (avg >= 192) return launch_bf16_bm<256, EPI>(st, g, max_rows, ksplit);
-  if (avg >= 96) return launch_bf16_bm<128, EPI>(st, g, max_rows, ksplit);
-  if (avg >= 48) return launch_bf16_bm<64, EPI>(st, g, max_rows, ksplit);
+  // 256-row tiles skip the MFMAs of row blocks past a segment's end, so they serve any
+  // segment of a few dozen rows or more; below that the weights dominate and 32-row
+  // tiles (two workgroups per CU) keep more weight loads in flight
+  if (avg >= 48) return launch_bf16_bm<256, EPI>(st, g, max_rows, ksplit);
   return launch_bf16_bm<32, EPI>(st, g, max_rows, ksplit);
 }
 

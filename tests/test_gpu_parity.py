@@ -224,7 +224,7 @@ def _ffn_case(dtype, act, bias, d, d_ff, sizes, seed=0):
 
 
 FFN_CASES = [
-    # dtype, act, bias, d, d_ff, segment sizes (covers BM 32/64/128/256, empty and
+    # dtype, act, bias, d, d_ff, segment sizes (covers both tile heights, empty and
     # one-row segments, ragged row tails and a partial column tile)
     ("bf16", "swiglu", False, 192, 320, [0, 1, 37, 300, 513, 0, 64]),
     ("bf16", "gelu", True, 192, 320, [0, 1, 37, 300, 513, 0, 64]),
@@ -232,6 +232,9 @@ FFN_CASES = [
     ("bf16", "gelu", False, 128, 256, [40, 70, 90, 33]),
     ("bf16", "swiglu", False, 320, 384, [600, 700, 10]),
     ("bf16", "gelu", True, 64, 128, [1]),
+    # tails of every 32-row block count, so each wave row runs 0..4 active blocks
+    ("bf16", "swiglu", False, 192, 320, [100, 150, 200, 250, 129, 65, 193, 255]),
+    ("bf16", "gelu", True, 128, 256, [161, 97, 33, 225, 289]),
     ("f32", "gelu", True, 128, 512, [30, 0, 100, 126]),
     ("f32", "swiglu", False, 132, 260, [65, 1, 0, 200]),
 ]
