@@ -204,13 +204,15 @@ template <int BM, bool DUAL, bool KSPLIT>
 struct TileIO {
   static constexpr int MF = MfmaFor<BM>::value;
   using S = Mfma<MF>;
-  static constexpr int WM = BM / 2;            // activation rows per wave
-  static constexpr int TM = WM / S::M;         // MFMA tiles per wave along activation rows
+  static constexpr int TM = BM / 2 / S::M;     // row blocks per wave (activation rows)
   static constexpr int TN = 128 / S::M;        // MFMA tiles per wave along weight rows
   static constexpr int A_GRPS = BM / 8;        // 8-row load groups of A per stage
   static constexpr int A_GRP = A_GRPS / 4;     // per wave
   static constexpr int B_GRP = kBRows / 32;    // 8-row load groups of B per wave per stage
   static_assert(A_GRPS % 4 == 0, "BM must be a multiple of 32");
+  // LDS ring depth of the weight operand: the 256-row tiles spend the whole 160 KB of
+  // LDS on 2 activation and 3 weight stages, so weights are loaded three stages ahead
+  static constexpr int NBB = BM >= 256 ? 3 : 2;
   const uint16_t* a_base;
   const uint16_t* b_base0;
   const uint16_t* b_base1;
@@ -220,24 +222,26 @@ struct TileIO {
   int co[S::KSTEPS];      // swizzled element offset of this lane's chunk per k-step
   int64_t kchunk, kbatch_stride;
 
-  // One stage of loads: wave w fills the 8-row groups w, w+4, ... of A and B; one
+  // Loads of one stage: wave w fills the 8-row groups w, w+4, ... of the tile; one
   // instruction moves 8 rows x 128 bytes (whole cache lines).  Lane l writes LDS row
   // 8*group + l/8, physical chunk l%8, and so loads logical chunk (l%8) ^ f(row).
   // Addresses are a wave-uniform base that carries k plus a loop-invariant unsigned
   // 32-bit lane offset (the scalar-base form of the load).
-  __device__ __forceinline__ void dma(uint16_t* as, uint16_t* bs, int k0) const {
+  __device__ __forceinline__ void dma_a(uint16_t* as, int k0) const {
+    const char* ak = reinterpret_cast<const char*>(a_base + k0);
+#pragma unroll
+    for (int j = 0; j < A_GRP; ++j)
+      __builtin_amdgcn_global_load_lds((global_void_t*)(ak + a_off[j]),
+                                       (lds_void_t*)(as + (wave + 4 * j) * 8 * kBK), 16, 0, 0);
+  }
+  __device__ __forceinline__ void dma_b(uint16_t* bs, int k0) const {
     int64_t bk = k0;
     if (KSPLIT) {
       const int64_t kb = k0 / kchunk;
       bk = kb * kbatch_stride + (k0 - kb * kchunk);
     }
-    const char* ak = reinterpret_cast<const char*>(a_base + k0);
     const char* bk0 = reinterpret_cast<const char*>(b_base0 + bk);
     const char* bk1 = reinterpret_cast<const char*>(b_base1 + bk);
-#pragma unroll
-    for (int j = 0; j < A_GRP; ++j)
-      __builtin_amdgcn_global_load_lds((global_void_t*)(ak + a_off[j]),
-                                       (lds_void_t*)(as + (wave + 4 * j) * 8 * kBK), 16, 0, 0);
 #pragma unroll
     for (int j = 0; j < B_GRP; ++j) {
       // SwiGLU: LDS rows with bit 6 set (groups j = 2, 3 mod 4) hold W3 rows
@@ -279,6 +283,17 @@ __device__ __forceinline__ void mma_frags(
     const Frags<IO>& f, typename IO::S::acc_t (&acc)[IO::TN][IO::TM]) {
 #pragma unroll
   for (int tn = 0; tn < IO::TN; ++tn)
+#pragma unroll
+    for (int tm = 0; tm < TA; ++tm) acc[tn][tm] = IO::S::mma(f.w[tn], f.a[tm], acc[tn][tm]);
+}
+
+// Half H (0 or 1) of one k-step's MFMAs, split along the weight tiles.
+template <class IO, int TA, int H>
+__device__ __forceinline__ void mma_frags_half(
+    const Frags<IO>& f, typename IO::S::acc_t (&acc)[IO::TN][IO::TM]) {
+  constexpr int N0 = H == 0 ? 0 : IO::TN / 2, N1 = H == 0 ? IO::TN / 2 : IO::TN;
+#pragma unroll
+  for (int tn = N0; tn < N1; ++tn)
 #pragma unroll
     for (int tm = 0; tm < TA; ++tm) acc[tn][tm] = IO::S::mma(f.w[tn], f.a[tm], acc[tn][tm]);
 }
@@ -336,46 +351,80 @@ __device__ __forceinline__ void inner_steps(const IO& io, const uint16_t* ac, co
   }
 }
 
-// One stage of the two-buffer LDS ring.  On entry f[0] holds k-step 0 of this stage
-// (buffer ac/bc) and the loads of the next stage (buffer an/bn) are in flight.  The
-// stage boundary sits before the MFMAs of the last k-step: the barrier there releases
-// this stage's buffer (every wave has read all its fragments) and makes the next
-// stage's buffer visible, so the refill of ac/bc with the stage after next and the
-// reads of the next stage's first fragments are issued between the last k-step's MFMAs
-// and the matrix cores do not wait for the barrier.  Past the last stage the refill
-// repeats the last stage (kept unconditional so that the loads stay interleaved with
-// the MFMAs; the data is never read).
-template <class IO, int LPW, int TA>
+// Stage s of the LDS rings (activations ac, weights bc).  On entry f[0] holds k-step 0
+// of the stage.  The stage boundary sits before the MFMAs of the last k-step: the
+// barrier there releases this stage's buffers (every wave has read all its fragments)
+// and makes the next stage (an, bn) visible.  The released buffers are refilled with
+// stage s + 2 (activations) and stage s + NBB (weights) and the next stage's first
+// fragments are read, all between the last k-step's MFMAs, so the matrix cores do not
+// wait for the barrier.  Loads are issued activations first, then weights, so that at
+// the next boundary everything except this boundary's weight loads must have landed
+// (loads complete in order): with a 3-deep weight ring those stay in flight.  Past the
+// last stage the refills repeat the last stage (kept unconditional so that the loads
+// stay interleaved with the MFMAs; the data is never read).
+template <class IO, int TA>
 __device__ __forceinline__ void pipe_stage(const IO& io, uint16_t* ac, uint16_t* bc,
-                                           const uint16_t* an, const uint16_t* bn,
-                                           int k_refill, Frags<IO> (&f)[2],
+                                           const uint16_t* an, const uint16_t* bn, int ka,
+                                           int kb, Frags<IO> (&f)[2],
                                            typename IO::S::acc_t (&acc)[IO::TN][IO::TM]) {
   constexpr int KS = IO::S::KSTEPS;
   constexpr int R = TA > 0 ? IO::TN + TA : 0, P = IO::TN * TA;
-  constexpr int NSLOT = R > LPW ? R : LPW;
+  constexpr int LA = IO::A_GRP, LB = IO::B_GRP;
   static_assert(KS % 2 == 0, "an even number of k-steps per stage");
   inner_steps<IO, TA, 0, KS - 1>(io, ac, bc, f, acc);
-  barrier_keep_loads<0>();
-  io.dma(ac, bc, k_refill);
+  barrier_keep_loads<IO::NBB == 3 ? LB : 0>();
+  // the last k-step's MFMAs, split in two halves around the activation / weight loads
+  io.dma_a(ac, ka);
   read_frags<IO, TA>(io, an, bn, 0, f[0]);
-  mma_frags<IO, TA>(f[1], acc);
-  sched_mix<LPW, R, P, 0, NSLOT>();
+  mma_frags_half<IO, TA, 0>(f[1], acc);
+  sched_mix<LA, R, P / 2, 0, (R > LA ? R : LA)>();
+  __builtin_amdgcn_sched_barrier(0);  // every activation load precedes every weight load
+  io.dma_b(bc, kb);
+  mma_frags_half<IO, TA, 1>(f[1], acc);
+  sched_mix<LB, 0, P - P / 2, 0, LB>();
 }
 
-// The K loop of one tile for a wave with TA active row blocks.  On entry the loads of
-// stages 0 and 1 are in flight and stage 0 is visible to the workgroup.
-template <class IO, int LPW, int TA>
-__device__ __forceinline__ void k_loop(const IO& io, uint16_t* As0, uint16_t* Bs0, uint16_t* As1,
-                                       uint16_t* Bs1, int KT,
+// The K loop of one tile for a wave with TA active row blocks (KT >= 1).  On entry the
+// prologue's loads are in flight and stage 0 is visible to the workgroup.  Stage s reads
+// activation buffer s % 2 and weight buffer s % NBB; one loop iteration covers the
+// period of both rings.
+template <class IO, int TA>
+__device__ __forceinline__ void k_loop(const IO& io, uint16_t* As0, uint16_t* As1, uint16_t* Bs0,
+                                       uint16_t* Bs1, uint16_t* Bs2, int KT,
                                        typename IO::S::acc_t (&acc)[IO::TN][IO::TM]) {
+  constexpr int NBB = IO::NBB;
   Frags<IO> f[2];
   read_frags<IO, TA>(io, As0, Bs0, 0, f[0]);
+  // whole periods of the two rings in the loop, the remaining stages after it as
+  // straight-line code, so that every stage is entered through the previous stage's
+  // boundary on every path (the compiler then sees each buffer's loads waited for)
+#define MOE_STAGE(I, AC, BC, AN, BN)                                                        \
+  pipe_stage<IO, TA>(io, AC, BC, AN, BN, min(kt + (I) + 2, KT - 1) * kBK,                  \
+                     min(kt + (I) + NBB, KT - 1) * kBK, f, acc)
   int kt = 0;
-  for (; kt + 2 <= KT; kt += 2) {
-    pipe_stage<IO, LPW, TA>(io, As0, Bs0, As1, Bs1, min(kt + 2, KT - 1) * kBK, f, acc);
-    pipe_stage<IO, LPW, TA>(io, As1, Bs1, As0, Bs0, min(kt + 3, KT - 1) * kBK, f, acc);
+  if constexpr (NBB == 3) {
+    for (; kt + 6 <= KT; kt += 6) {
+      MOE_STAGE(0, As0, Bs0, As1, Bs1);
+      MOE_STAGE(1, As1, Bs1, As0, Bs2);
+      MOE_STAGE(2, As0, Bs2, As1, Bs0);
+      MOE_STAGE(3, As1, Bs0, As0, Bs1);
+      MOE_STAGE(4, As0, Bs1, As1, Bs2);
+      MOE_STAGE(5, As1, Bs2, As0, Bs0);
+    }
+    const int rem = KT - kt;
+    if (rem >= 1) MOE_STAGE(0, As0, Bs0, As1, Bs1);
+    if (rem >= 2) MOE_STAGE(1, As1, Bs1, As0, Bs2);
+    if (rem >= 3) MOE_STAGE(2, As0, Bs2, As1, Bs0);
+    if (rem >= 4) MOE_STAGE(3, As1, Bs0, As0, Bs1);
+    if (rem >= 5) MOE_STAGE(4, As0, Bs1, As1, Bs2);
+  } else {
+    for (; kt + 2 <= KT; kt += 2) {
+      MOE_STAGE(0, As0, Bs0, As1, Bs1);
+      MOE_STAGE(1, As1, Bs1, As0, Bs0);
+    }
+    if (kt < KT) MOE_STAGE(0, As0, Bs0, As1, Bs1);
   }
-  if (kt < KT) pipe_stage<IO, LPW, TA>(io, As0, Bs0, As1, Bs1, (KT - 1) * kBK, f, acc);
+#undef MOE_STAGE
 }
 
 // The rest of a tile for a wave with TA active row blocks: the K loop, then the epilogue.
@@ -383,10 +432,10 @@ __device__ __forceinline__ void k_loop(const IO& io, uint16_t* As0, uint16_t* Bs
 // variants.  Register 4q + r of tile (tn, tm) is the output element (activation row
 // (2 tm + wm)*M + row(lane), weight row tn*M + ni(q, lane) + r); the four r are
 // consecutive output columns (one 8-byte store of bf16).
-template <class IO, int LPW, int EPI, int TA>
+template <class IO, int EPI, int TA>
 __device__ __forceinline__ void tile_body(const GemmArgs& g, const Tile& tile, const IO& io,
-                                          uint16_t* As0, uint16_t* Bs0, uint16_t* As1,
-                                          uint16_t* Bs1, int KT) {
+                                          uint16_t* As0, uint16_t* As1, uint16_t* Bs0,
+                                          uint16_t* Bs1, uint16_t* Bs2, int KT) {
   using S = typename IO::S;
   constexpr int TN = IO::TN;
   typename S::acc_t acc[TN][IO::TM];
@@ -396,7 +445,7 @@ __device__ __forceinline__ void tile_body(const GemmArgs& g, const Tile& tile, c
     for (int b = 0; b < TA; ++b)
 #pragma unroll
       for (int r = 0; r < S::ACC; ++r) acc[a][b][r] = 0.f;
-  k_loop<IO, LPW, TA>(io, As0, Bs0, As1, Bs1, KT, acc);
+  k_loop<IO, TA>(io, As0, As1, Bs0, Bs1, Bs2, KT, acc);
   // no load may still be writing this workgroup's LDS when it exits
   __builtin_amdgcn_s_waitcnt(0);
   if constexpr (TA == 0) return;
@@ -461,20 +510,25 @@ template <int BM, int EPI, bool KSPLIT>
 __global__ __launch_bounds__(kThreads, 1) void gemm_bf16_kernel(GemmArgs g) {
   using IO = TileIO<BM, EPI == EPI_SWIGLU, KSPLIT>;
   using S = typename IO::S;
-  constexpr int WM = IO::WM;
   constexpr int TM = IO::TM;
   constexpr int TN = IO::TN;
   static_assert(TM >= 1, "BM must be >= 32");
-  // the LDS ring as distinct objects, so that the compiler can tell the stage being read
-  // from the stage being filled
+  // the LDS rings as distinct objects, so that the compiler can tell the stages being
+  // read from the stages being filled.  The tile scheduler's scratch lives in the third
+  // weight buffer (for the 256-row tiles the rings take all 160 KB of LDS): the barrier
+  // after scheduling orders its last reads before the first load into that buffer.
+  constexpr int kB2 = IO::NBB == 3 ? kBRows * kBK : (sizeof(SchedSmem) + 15) / 16 * 8;
   __shared__ __attribute__((aligned(16))) uint16_t As0[BM * kBK], As1[BM * kBK];
   __shared__ __attribute__((aligned(16))) uint16_t Bs0[kBRows * kBK], Bs1[kBRows * kBK];
-  __shared__ SchedSmem sched;
+  __shared__ __attribute__((aligned(16))) uint16_t Bs2[kB2];
+  static_assert(sizeof(SchedSmem) <= sizeof(Bs2), "scheduler scratch must fit");
+  SchedSmem& sched = *reinterpret_cast<SchedSmem*>(Bs2);
 
   const int n_ntiles = (EPI == EPI_SWIGLU) ? (g.n_out + 127) / 128 : (g.n_out + 255) / 256;
   Tile tile;
   if (!schedule_tile<BM>(g.seg_off, g.n_seg, g.single_rows, g.max_rows, n_ntiles, sched, tile))
     return;
+  __syncthreads();  // the scheduler scratch is dead from here on
 
   const int tid = threadIdx.x;
   const int lane = tid & (kWave - 1);
@@ -515,34 +569,42 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_bf16_kernel(GemmArgs g) {
   const int wm = io.wm;
 
   const int KT = g.k / kBK;
-  constexpr int LPW = IO::A_GRP + IO::B_GRP;   // direct-to-LDS loads per wave per stage
-  // prologue: stages 0 and 1 in flight
-  io.dma(As0, Bs0, 0);
-  if (KT > 1) io.dma(As1, Bs1, kBK);
-  if (KT > 1)
-    barrier_keep_loads<LPW>();
-  else
-    barrier_keep_loads<0>();
+  constexpr int LA = IO::A_GRP, LB = IO::B_GRP;  // direct-to-LDS loads per wave per stage
+  // prologue: with a 3-deep weight ring, issue A0 B0 B1 A1 B2 (at every later boundary
+  // exactly the weight loads of the boundary before may still be in flight); else
+  // A0 B0 A1 B1.  Stages past the last one repeat it.
+  io.dma_a(As0, 0);
+  io.dma_b(Bs0, 0);
+  if constexpr (IO::NBB == 3) {
+    io.dma_b(Bs1, min(1, KT - 1) * kBK);
+    io.dma_a(As1, min(1, KT - 1) * kBK);
+    io.dma_b(Bs2, min(2, KT - 1) * kBK);
+    barrier_keep_loads<LB + LA + LB>();
+  } else {
+    io.dma_a(As1, min(1, KT - 1) * kBK);
+    io.dma_b(Bs1, min(1, KT - 1) * kBK);
+    barrier_keep_loads<LA + LB>();
+  }
   // row blocks of this wave that hold rows of the tile (every wave runs the same stages
   // and barriers; only the MFMA work differs)
   const int nb = (tile.m_valid + S::M - 1) / S::M;
   const int ta = __builtin_amdgcn_readfirstlane(min(max((nb - wm + 1) / 2, 0), TM));
   if (ta >= TM) {
-    tile_body<IO, LPW, EPI, TM>(g, tile, io, As0, Bs0, As1, Bs1, KT);
+    tile_body<IO, EPI, TM>(g, tile, io, As0, As1, Bs0, Bs1, Bs2, KT);
   } else if constexpr (TM > 1) {
     if (ta == 0)
-      tile_body<IO, LPW, EPI, 0>(g, tile, io, As0, Bs0, As1, Bs1, KT);
+      tile_body<IO, EPI, 0>(g, tile, io, As0, As1, Bs0, Bs1, Bs2, KT);
     else if (ta == 1)
-      tile_body<IO, LPW, EPI, 1>(g, tile, io, As0, Bs0, As1, Bs1, KT);
+      tile_body<IO, EPI, 1>(g, tile, io, As0, As1, Bs0, Bs1, Bs2, KT);
     else if constexpr (TM > 2) {
       if (ta == 2)
-        tile_body<IO, LPW, EPI, 2>(g, tile, io, As0, Bs0, As1, Bs1, KT);
+        tile_body<IO, EPI, 2>(g, tile, io, As0, As1, Bs0, Bs1, Bs2, KT);
       else if constexpr (TM > 3) {
-        if (ta == 3) tile_body<IO, LPW, EPI, 3>(g, tile, io, As0, Bs0, As1, Bs1, KT);
+        if (ta == 3) tile_body<IO, EPI, 3>(g, tile, io, As0, As1, Bs0, Bs1, Bs2, KT);
       }
     }
   } else {
-    tile_body<IO, LPW, EPI, 0>(g, tile, io, As0, Bs0, As1, Bs1, KT);
+    tile_body<IO, EPI, 0>(g, tile, io, As0, As1, Bs0, Bs1, Bs2, KT);
   }
 }
 
