@@ -83,8 +83,9 @@ int64_t moe_capacity(int64_t n_tokens, int32_t n_experts, int32_t k, double alph
  *                  ([DeepSeek-V2] §2.2 load_balance_loss; equals 1 when routing is
  *                  uniform).  For N == 0 the statistics are written as zeros.
  * Arguments
- *   x          [N][d], x_dtype (MOE_F32 or MOE_BF16); d % 4 == 0.  May be NULL when
- *              logits_in is given.
+ *   x          [N][d], x_dtype (MOE_F32 or MOE_BF16); d % 4 == 0 for MOE_F32 (x 8-byte
+ *              aligned), d % 8 == 0 for MOE_BF16 (x 16-byte aligned).  May be NULL
+ *              when logits_in is given.
  *   w_router   [d][E] float32.  May be NULL when logits_in is given.
  *   logit_bias [E] float32 or NULL (no bias).
  *   E          1..MOE_MAX_EXPERTS; 1 <= k <= E, k <= 16.
@@ -93,10 +94,15 @@ int64_t moe_capacity(int64_t n_tokens, int32_t n_experts, int32_t k, double alph
  *   logits_out [N][E] float32 or NULL: the float32 logits (before the bias).
  *   topk_idx   [N][k] int32, topk_w [N][k] float32 (required).
  *   sel_count  [E] int32, prob_mean [E] float32, aux [1] float32 (each may be NULL).
- *   ws         device workspace of at least moe_route_workspace_size(N, E) bytes,
+ *   ws         device workspace of at least moe_route_workspace_size(N, d, E) bytes,
  *              256-byte aligned (may be NULL if that size is 0).
+ * Precision: logits are float32 dot products.  For MOE_BF16 x the float32 w_router is
+ * split exactly into three bf16 parts whose products with the (exact) bf16 x are
+ * accumulated in float32 by the matrix cores; the d_model reduction may be split into
+ * slices whose partial sums are added in slice order.  Results are identical from run
+ * to run.
  */
-size_t moe_route_workspace_size(int64_t n_tokens, int32_t n_experts);
+size_t moe_route_workspace_size(int64_t n_tokens, int64_t d_model, int32_t n_experts);
 moe_status moe_route(void* stream, const void* x, moe_dtype x_dtype, int64_t n_tokens,
                      int64_t d_model, const float* w_router, const float* logit_bias,
                      int32_t n_experts, int32_t k, int32_t renormalize,

@@ -55,7 +55,7 @@ _lib = None
 _VP, _I64, _I32, _SZ, _DBL = C.c_void_p, C.c_int64, C.c_int32, C.c_size_t, C.c_double
 _SIGS = {
     "moe_capacity": (_I64, [_I64, _I32, _I32, _DBL]),
-    "moe_route_workspace_size": (_SZ, [_I64, _I32]),
+    "moe_route_workspace_size": (_SZ, [_I64, _I64, _I32]),
     "moe_route": (C.c_int, [_VP, _VP, C.c_int, _I64, _I64, _VP, _VP, _I32, _I32, _I32, _VP, _VP,
                             _VP, _VP, _VP, _VP, _VP, _VP, _SZ]),
     "moe_dispatch_workspace_size": (_SZ, [_I64, _I32, _I32]),
@@ -134,8 +134,8 @@ def moe_capacity(n_tokens: int, n_experts: int, k: int, alpha: float) -> int:
     return int(lib().moe_capacity(n_tokens, n_experts, k, float(alpha)))
 
 
-def moe_route_workspace_size(n_tokens: int, n_experts: int) -> int:
-    return int(lib().moe_route_workspace_size(n_tokens, n_experts))
+def moe_route_workspace_size(n_tokens: int, d_model: int, n_experts: int) -> int:
+    return int(lib().moe_route_workspace_size(n_tokens, d_model, n_experts))
 
 
 def moe_route(x, w_router, logit_bias, n_experts: int, k: int, renormalize: bool,

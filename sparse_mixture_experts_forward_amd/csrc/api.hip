@@ -1,6 +1,7 @@
 // C ABI of the MoE forward library: argument checks, workspace layout, and the order
 // of the kernels (include/moe.h documents every entry point).
 
+#include <algorithm>
 #include <cmath>
 #include <cstdarg>
 #include <cstdio>
@@ -72,8 +73,11 @@ moe_status check_route_args(const void* x, moe_dtype xt, int64_t n, int64_t d,
     if (!idx || !w) return fail(MOE_ERR_INVALID_ARG, "topk_idx and topk_w are required");
     if (!logits_in) {
       if (!x || !wr) return fail(MOE_ERR_INVALID_ARG, "x and w_router are required");
-      if (d < 4 || d % 4 != 0) return fail(MOE_ERR_UNSUPPORTED, "d_model must be a positive multiple of 4");
-      MOE_TRY(check_aligned(x, 8, "x"));
+      const int64_t q = xt == MOE_BF16 ? 8 : 4;
+      if (d < q || d % q != 0)
+        return fail(MOE_ERR_UNSUPPORTED, "d_model must be a positive multiple of %lld for this dtype",
+                    static_cast<long long>(q));
+      MOE_TRY(check_aligned(x, xt == MOE_BF16 ? 16 : 8, "x"));
     }
   }
   if (n * static_cast<int64_t>(k) > INT32_MAX || n * static_cast<int64_t>(e) > INT32_MAX)
@@ -81,11 +85,34 @@ moe_status check_route_args(const void* x, moe_dtype xt, int64_t n, int64_t d,
   return MOE_OK;
 }
 
-size_t route_ws(int64_t n, int32_t e) {
+// Router workspace: statistics partials (one row per router or gate workgroup), and
+// for bf16 activations the three-part bf16 split of W_router and the sliced partial
+// logits.  Sized for either activation type.
+struct RouteWs {
+  float* pp;
+  int32_t* pc;
+  double* term;
+  uint16_t* wp;
+  float* part;
+};
+
+RouteWs route_layout(Carve& c, int64_t n, int64_t d, int32_t e) {
+  RouteWs r{};
+  const int64_t b = std::max(moe::route_blocks(n), moe::gate_blocks(n));
+  r.pp = c.take<float>(b * e);
+  r.pc = c.take<int32_t>(b * e);
+  r.term = c.take<double>(e);
+  if (d >= 8 && d % 8 == 0) {
+    const moe::RoutePlan pl = moe::route_plan(n, d, e);
+    r.wp = c.take<uint16_t>(3 * static_cast<int64_t>(pl.e_pad) * d);
+    r.part = c.take<float>(static_cast<int64_t>(pl.ks) * n * e);
+  }
+  return r;
+}
+
+size_t route_ws(int64_t n, int64_t d, int32_t e) {
   Carve c(nullptr);
-  const int64_t b = moe::route_blocks(n);
-  c.take<float>(b * e);
-  c.take<int32_t>(b * e);
+  route_layout(c, n, d, e);
   return c.used;
 }
 
@@ -94,6 +121,7 @@ size_t dispatch_ws(int64_t n, int32_t k, int32_t e) {
   const moe::DispatchGrid g = moe::dispatch_grid(n, k);
   c.take<int32_t>(g.n_blocks * e);
   c.take<int32_t>(g.n_blocks * e);
+  c.take<int32_t>(e);
   return c.used;
 }
 
@@ -102,13 +130,32 @@ moe_status run_route(hipStream_t st, const void* x, moe_dtype xt, int64_t n, int
                      const float* logits_in, float* logits_out, int32_t* idx, float* w,
                      int32_t* sel, float* pm, float* aux, void* ws) {
   Carve c(ws);
-  const int64_t b = moe::route_blocks(n);
-  float* pp = c.take<float>(b * e);
-  int32_t* pc = c.take<int32_t>(b * e);
-  MOE_TRY(hip_check(moe::launch_route(st, x, xt == MOE_BF16, n, d, wr, bias, e, k, renorm,
-                                      logits_in, logits_out, idx, w, pp, pc),
-                    "router kernel launch"));
-  return hip_check(moe::launch_route_finalize(st, pp, pc, b, n, e, k, sel, pm, aux),
+  const RouteWs r = route_layout(c, n, d, e);
+  int64_t rows;
+  if (logits_in) {
+    // the gate alone, over the caller's logits
+    rows = moe::gate_blocks(n);
+    MOE_TRY(hip_check(moe::launch_route_gate(st, logits_in, 1, n, e, bias, k, renorm, logits_out,
+                                             idx, w, r.pp, r.pc),
+                      "router gate launch"));
+  } else if (xt == MOE_BF16) {
+    const moe::RoutePlan pl = moe::route_plan(n, d, e);
+    rows = moe::gate_blocks(n);
+    if (n == 0) return hip_check(moe::launch_route_finalize(st, r.pp, r.pc, 0, 0, e, k, sel, pm, aux, r.term),
+                                 "router statistics launch");
+    MOE_TRY(hip_check(moe::launch_route_split(st, wr, pl, r.wp), "router weight split launch"));
+    MOE_TRY(hip_check(moe::launch_route_logits(st, static_cast<const uint16_t*>(x), pl, r.wp, r.part),
+                      "router logits launch"));
+    MOE_TRY(hip_check(moe::launch_route_gate(st, r.part, pl.ks, n, e, bias, k, renorm, logits_out,
+                                             idx, w, r.pp, r.pc),
+                      "router gate launch"));
+  } else {
+    rows = moe::route_blocks(n);
+    MOE_TRY(hip_check(moe::launch_route(st, static_cast<const float*>(x), n, d, wr, bias, e, k,
+                                        renorm, logits_out, idx, w, r.pp, r.pc),
+                      "router kernel launch"));
+  }
+  return hip_check(moe::launch_route_finalize(st, r.pp, r.pc, rows, n, e, k, sel, pm, aux, r.term),
                    "router statistics launch");
 }
 
@@ -120,8 +167,9 @@ moe_status run_dispatch(hipStream_t st, const int32_t* idx, int64_t n, int32_t k
   const moe::DispatchGrid g = moe::dispatch_grid(n, k);
   int32_t* hist = c.take<int32_t>(g.n_blocks * e);
   int32_t* base = c.take<int32_t>(g.n_blocks * e);
+  int32_t* kept_tmp = c.take<int32_t>(e);
   return hip_check(moe::launch_dispatch(st, idx, n, k, e, cap, x, row_bytes, offsets, row_token,
-                                        slot_row, kept, dropped, x_perm, hist, base),
+                                        slot_row, kept, dropped, x_perm, hist, base, kept_tmp),
                    "dispatch kernels launch");
 }
 
@@ -208,7 +256,7 @@ ForwardLayout forward_layout(const moe_config& c, void* ws) {
   L.slot_row = cv.take<int32_t>(nk);
   L.kept = cv.take<int32_t>(e);
   L.dropped = cv.take<int32_t>(1);
-  L.route_ws = cv.take<char>(route_ws(n, e));
+  L.route_ws = cv.take<char>(route_ws(n, c.d_model, e));
   L.dispatch_ws = cv.take<char>(dispatch_ws(n, c.top_k, e));
   L.x_perm = cv.take<char>(R * c.d_model * es);
   L.h = cv.take<char>(R * c.d_ff * es);
@@ -262,9 +310,9 @@ int64_t moe_capacity(int64_t n_tokens, int32_t n_experts, int32_t k, double alph
   return capacity_of(n_tokens, n_experts, k, alpha);
 }
 
-size_t moe_route_workspace_size(int64_t n_tokens, int32_t n_experts) {
-  if (n_tokens < 0 || n_experts < 1) return 0;
-  return route_ws(n_tokens, n_experts);
+size_t moe_route_workspace_size(int64_t n_tokens, int64_t d_model, int32_t n_experts) {
+  if (n_tokens < 0 || d_model < 0 || n_experts < 1) return 0;
+  return route_ws(n_tokens, d_model, n_experts);
 }
 
 moe_status moe_route(void* stream, const void* x, moe_dtype x_dtype, int64_t n_tokens,
@@ -275,7 +323,7 @@ moe_status moe_route(void* stream, const void* x, moe_dtype x_dtype, int64_t n_t
                      void* ws, size_t ws_bytes) {
   MOE_TRY(check_route_args(x, x_dtype, n_tokens, d_model, w_router, n_experts, k, logits_in,
                            topk_idx, topk_w));
-  const size_t need = route_ws(n_tokens, n_experts);
+  const size_t need = route_ws(n_tokens, d_model, n_experts);
   if (ws_bytes < need) return fail(MOE_ERR_WORKSPACE, "moe_route needs %zu workspace bytes", need);
   if (need > 0) {
     if (!ws) return fail(MOE_ERR_INVALID_ARG, "ws is NULL");

@@ -4,11 +4,11 @@
 // expert are ranked in increasing token order; ranks below the capacity are kept, the
 // rest dropped; kept rows are laid out expert-major, token-ascending.
 //
-// Three kernels over contiguous token chunks (one workgroup per chunk):
+// Kernels over contiguous token chunks (one workgroup per chunk) and experts:
 //   1. hist:    LDS histogram of the chunk's expert ids -> blk_hist[e][b]
-//   2. scan:    one workgroup; per expert, exclusive scan over chunks (the rank of the
-//               chunk's first assignment), kept = min(total, C), exclusive scan over
-//               experts -> expert_offsets
+//   2. scan:    one workgroup per expert; exclusive scan over chunks (the rank of the
+//               chunk's first assignment), kept = min(total, C); then one workgroup,
+//               exclusive scan over experts -> expert_offsets
 //   3. scatter: per chunk, the stable in-chunk rank of each assignment (ballot-based
 //               match inside a wave, running per-expert counters in LDS), the row
 //               maps, then the copy of every token row to its kept rows with 16-byte
@@ -40,47 +40,67 @@ __global__ __launch_bounds__(kThreads) void dispatch_hist_kernel(
   for (int e = threadIdx.x; e < E; e += kThreads) blk_hist[e * n_blocks + blockIdx.x] = h[e];
 }
 
-constexpr int kScanThreads = 1024;
-
-__global__ __launch_bounds__(kScanThreads) void dispatch_scan_kernel(
-    const int32_t* __restrict__ blk_hist, int64_t n_blocks, int E, int64_t capacity,
-    int64_t n_assign, int32_t* __restrict__ blk_base, int32_t* __restrict__ expert_offsets,
-    int32_t* __restrict__ kept_count, int32_t* __restrict__ n_dropped) {
-  __shared__ int32_t kept[kMaxExperts];
-  const int lane = lane_id();
-  const int wave = threadIdx.x / kWave;
-  constexpr int n_waves = kScanThreads / kWave;
-  for (int e = wave; e < E; e += n_waves) {
-    int running = 0;
-    for (int64_t b0 = 0; b0 < n_blocks; b0 += kWave) {
-      const int64_t b = b0 + lane;
-      const int v = (b < n_blocks) ? blk_hist[e * n_blocks + b] : 0;
-      const int incl = wave_incl_scan(v);
-      if (b < n_blocks) blk_base[e * n_blocks + b] = running + incl - v;
-      running += __shfl(incl, kWave - 1, kWave);
-    }
-    if (lane == 0) {
-      const int64_t kc = (capacity >= 0 && running > capacity) ? capacity : running;
-      kept[e] = static_cast<int32_t>(kc);
-    }
-  }
+// Workgroup-wide inclusive scan of one value per thread (4 waves, wave sums through
+// LDS); `total` receives the sum over the workgroup.
+__device__ __forceinline__ int block_incl_scan(int v, int* wsum, int& total) {
+  const int lane = lane_id(), wave = threadIdx.x / kWave;
+  const int incl = wave_incl_scan(v);
+  if (lane == kWave - 1) wsum[wave] = incl;
   __syncthreads();
-  if (wave == 0) {
-    int running = 0;
-    for (int e0 = 0; e0 < E; e0 += kWave) {
-      const int e = e0 + lane;
-      const int v = (e < E) ? kept[e] : 0;
-      const int incl = wave_incl_scan(v);
-      if (e < E) {
-        expert_offsets[e] = running + incl - v;
-        if (kept_count) kept_count[e] = v;
-      }
-      running += __shfl(incl, kWave - 1, kWave);
+  int off = 0, tot = 0;
+#pragma unroll
+  for (int w = 0; w < kThreads / kWave; ++w) {
+    off += (w < wave) ? wsum[w] : 0;
+    tot += wsum[w];
+  }
+  __syncthreads();  // wsum may be rewritten by the next call
+  total = tot;
+  return off + incl;
+}
+
+// One workgroup per expert: exclusive scan of its chunk counts -> blk_base, and the
+// kept count min(total, capacity).
+__global__ __launch_bounds__(kThreads) void dispatch_scan_kernel(
+    const int32_t* __restrict__ blk_hist, int64_t n_blocks, int64_t capacity,
+    int32_t* __restrict__ blk_base, int32_t* __restrict__ kept) {
+  __shared__ int wsum[kThreads / kWave];
+  const int e = blockIdx.x;
+  int running = 0;
+  for (int64_t b0 = 0; b0 < n_blocks; b0 += kThreads) {
+    const int64_t b = b0 + threadIdx.x;
+    const int v = (b < n_blocks) ? blk_hist[e * n_blocks + b] : 0;
+    int chunk_total;
+    const int incl = block_incl_scan(v, wsum, chunk_total);
+    if (b < n_blocks) blk_base[e * n_blocks + b] = running + incl - v;
+    running += chunk_total;
+  }
+  if (threadIdx.x == kThreads - 1) {
+    const int64_t kc = (capacity >= 0 && running > capacity) ? capacity : running;
+    kept[e] = static_cast<int32_t>(kc);
+  }
+}
+
+// One workgroup: exclusive scan of the kept counts over experts -> expert_offsets.
+__global__ __launch_bounds__(kThreads) void dispatch_offsets_kernel(
+    const int32_t* __restrict__ kept, int E, int64_t n_assign,
+    int32_t* __restrict__ expert_offsets, int32_t* __restrict__ kept_count,
+    int32_t* __restrict__ n_dropped) {
+  __shared__ int wsum[kThreads / kWave];
+  int running = 0;
+  for (int e0 = 0; e0 < E; e0 += kThreads) {
+    const int e = e0 + threadIdx.x;
+    const int v = (e < E) ? kept[e] : 0;
+    int chunk_total;
+    const int incl = block_incl_scan(v, wsum, chunk_total);
+    if (e < E) {
+      expert_offsets[e] = running + incl - v;
+      if (kept_count) kept_count[e] = v;
     }
-    if (lane == 0) {
-      expert_offsets[E] = running;
-      if (n_dropped) n_dropped[0] = static_cast<int32_t>(n_assign - running);
-    }
+    running += chunk_total;
+  }
+  if (threadIdx.x == 0) {
+    expert_offsets[E] = running;
+    if (n_dropped) n_dropped[0] = static_cast<int32_t>(n_assign - running);
   }
 }
 
@@ -174,7 +194,7 @@ hipError_t launch_dispatch(hipStream_t st, const int32_t* topk_idx, int64_t n, i
                            int64_t capacity, const void* x, int64_t row_bytes,
                            int32_t* expert_offsets, int32_t* row_token, int32_t* slot_row,
                            int32_t* kept_count, int32_t* n_dropped, void* x_perm,
-                           int32_t* blk_hist, int32_t* blk_base) {
+                           int32_t* blk_hist, int32_t* blk_base, int32_t* kept_tmp) {
   const DispatchGrid g = dispatch_grid(n, k);
   if (g.n_blocks > 0) {
     hipLaunchKernelGGL(dispatch_hist_kernel, dim3(static_cast<unsigned>(g.n_blocks)),
@@ -183,10 +203,13 @@ hipError_t launch_dispatch(hipStream_t st, const int32_t* topk_idx, int64_t n, i
     hipError_t err = hipGetLastError();
     if (err != hipSuccess) return err;
   }
-  hipLaunchKernelGGL(dispatch_scan_kernel, dim3(1), dim3(kScanThreads), 0, st, blk_hist,
-                     g.n_blocks, e, capacity, n * k, blk_base, expert_offsets, kept_count,
-                     n_dropped);
+  hipLaunchKernelGGL(dispatch_scan_kernel, dim3(static_cast<unsigned>(e)), dim3(kThreads), 0, st,
+                     blk_hist, g.n_blocks, capacity, blk_base, kept_tmp);
   hipError_t err = hipGetLastError();
+  if (err != hipSuccess) return err;
+  hipLaunchKernelGGL(dispatch_offsets_kernel, dim3(1), dim3(kThreads), 0, st, kept_tmp, e, n * k,
+                     expert_offsets, kept_count, n_dropped);
+  err = hipGetLastError();
   if (err != hipSuccess || g.n_blocks == 0) return err;
   hipLaunchKernelGGL(dispatch_scatter_kernel, dim3(static_cast<unsigned>(g.n_blocks)),
                      dim3(kThreads), 0, st, topk_idx, n, k, e, g.tokens_per_block,

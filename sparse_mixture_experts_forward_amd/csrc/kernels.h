@@ -14,16 +14,48 @@ inline int64_t route_blocks(int64_t n_tokens) {
   return (n_tokens + kRouteTokens - 1) / kRouteTokens;
 }
 
-hipError_t launch_route(hipStream_t st, const void* x, bool x_bf16, int64_t n, int64_t d,
+// float32 router: fused product and gate, 16 tokens per workgroup
+hipError_t launch_route(hipStream_t st, const float* x, int64_t n, int64_t d,
                         const float* w_router, const float* logit_bias, int e, int k,
-                        int renorm, const float* logits_in, float* logits_out,
-                        int32_t* topk_idx, float* topk_w, float* part_prob,
-                        int32_t* part_cnt);
+                        int renorm, float* logits_out, int32_t* topk_idx, float* topk_w,
+                        float* part_prob, int32_t* part_cnt);
 
+// bf16 router: exact three-part bf16 split of W_router, the sliced logits product and
+// the gate over the slices' partial logits.
+// Gate: tokens per wave grow with N so that about a thousand waves run (1..16).
+inline int gate_tokens_per_wave(int64_t n_tokens) {
+  const int64_t t = (n_tokens + 1023) / 1024;
+  return static_cast<int>(t < 1 ? 1 : (t > 16 ? 16 : t));
+}
+inline int64_t gate_blocks(int64_t n_tokens) {
+  const int64_t per = 4 * static_cast<int64_t>(gate_tokens_per_wave(n_tokens));
+  return (n_tokens + per - 1) / per;
+}
+
+struct RoutePlan {
+  int64_t n, d;
+  int e, e_pad;          // experts, padded to whole expert groups
+  int ept, egroups;      // 16-expert tiles per workgroup, expert groups
+  int64_t token_tiles;   // 64-token tiles
+  int64_t kper;          // d_model slice per workgroup (multiple of 32)
+  int ks;                // number of slices
+};
+RoutePlan route_plan(int64_t n, int64_t d, int e);
+
+hipError_t launch_route_split(hipStream_t st, const float* w_router, const RoutePlan& pl,
+                              uint16_t* wp);
+hipError_t launch_route_logits(hipStream_t st, const uint16_t* x, const RoutePlan& pl,
+                               const uint16_t* wp, float* part);
+hipError_t launch_route_gate(hipStream_t st, const float* part, int ks, int64_t n, int e,
+                             const float* bias, int k, int renorm, float* logits_out,
+                             int32_t* topk_idx, float* topk_w, float* part_prob,
+                             int32_t* part_cnt);
+
+// Statistics over `rows` partial rows: per-expert workgroups (sel_count, prob_mean and
+// the aux terms, `term` is E doubles of scratch), then the aux sum.
 hipError_t launch_route_finalize(hipStream_t st, const float* part_prob,
-                                 const int32_t* part_cnt, int64_t n_blocks, int64_t n,
-                                 int e, int k, int32_t* sel_count, float* prob_mean,
-                                 float* aux);
+                                 const int32_t* part_cnt, int64_t rows, int64_t n, int e, int k,
+                                 int32_t* sel_count, float* prob_mean, float* aux, double* term);
 
 // ---------------------------------------------------------------- dispatch
 struct DispatchGrid {
@@ -36,7 +68,7 @@ hipError_t launch_dispatch(hipStream_t st, const int32_t* topk_idx, int64_t n, i
                            int64_t capacity, const void* x, int64_t row_bytes,
                            int32_t* expert_offsets, int32_t* row_token, int32_t* slot_row,
                            int32_t* kept_count, int32_t* n_dropped, void* x_perm,
-                           int32_t* blk_hist, int32_t* blk_base);
+                           int32_t* blk_hist, int32_t* blk_base, int32_t* kept_tmp);
 
 // ---------------------------------------------------------------- grouped GEMM
 enum Epilogue { EPI_NONE = 0, EPI_GELU = 1, EPI_SWIGLU = 2 };

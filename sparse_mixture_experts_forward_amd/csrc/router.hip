@@ -1,16 +1,21 @@
-// Router: fused float32 logits product + per-token gate (bias, softmax, top-k,
-// renormalisation) + per-workgroup balance-statistics partials, and a fixed-order
-// finalize of the statistics.
+// Router: logits product, per-token gate (bias, softmax, top-k, renormalisation) with
+// per-workgroup balance-statistics partials, and a fixed-order finalize of the
+// statistics.
 //
 // Method ([Why-MoE] §2.2; [DeepSeek-V2] §2.2): logits = x W_router (no bias),
 // z = logits + b, p = softmax(z), the k largest z with ties to the lower expert,
 // weights renormalised over the k, selection counts and mean probabilities per expert.
 //
-// Layout of the work: one workgroup (4 waves) owns 16 tokens and every expert.  The
-// product uses the float32 matrix cores (v_mfma_f32_16x16x4f32); the reduction over
-// d_model is split across the 4 waves, whose partial sums are added in wave order
-// through LDS, so the logits are reproducible run to run.  Each wave then gates 4
-// tokens with the experts spread over its 64 lanes.
+// bf16 activations: W_router (float32) is split exactly into three bf16 parts,
+// W = W_hi + W_mid + W_lo (8 + 8 + 8 significant bits cover float32's 24), and since a
+// bf16 x is exact, x W = x W_hi + x W_mid + x W_lo is computed with bf16 matrix cores
+// (v_mfma_f32_16x16x32_bf16) accumulating in float32: float32 accuracy at bf16 matrix
+// throughput.  Workgroups own 64 tokens x up to 256 experts x a slice of d_model; the
+// slices' partial logits are summed in slice order by the gate kernel, so the logits
+// are reproducible run to run.  float32 activations use a fused kernel on the float32
+// matrix cores (v_mfma_f32_16x16x4f32) that owns 16 tokens and every expert.
+//
+// Gate: one wave per token at a time, experts spread over its 64 lanes.
 
 #include <cfloat>
 
@@ -33,6 +38,78 @@ __device__ __forceinline__ void load_x4(const uint16_t* p, float v[4]) {
   v[1] = bf16_to_f32(static_cast<uint16_t>(q.x >> 16));
   v[2] = bf16_to_f32(static_cast<uint16_t>(q.y & 0xffffu));
   v[3] = bf16_to_f32(static_cast<uint16_t>(q.y >> 16));
+}
+
+// Gate of one token by one wave: lane j holds the logits l[i] of experts j + 64 i.
+// Writes topk_idx / topk_w of token t and adds p and the selection counts to the lane's
+// statistics accumulators.
+template <int VPL>
+__device__ __forceinline__ void gate_token(const float (&l)[VPL], int lane, int E,
+                                           const float* __restrict__ bias, int k, int renorm,
+                                           int64_t t, int32_t* __restrict__ topk_idx,
+                                           float* __restrict__ topk_w, float (&pacc)[VPL],
+                                           int32_t (&cacc)[VPL]) {
+  float z[VPL], ex[VPL];
+  float lmax = -INFINITY;
+#pragma unroll
+  for (int i = 0; i < VPL; ++i) {
+    const int e = lane + kWave * i;
+    if (e < E) {
+      z[i] = bias ? __fadd_rn(l[i], bias[e]) : l[i];
+      lmax = fmaxf(lmax, z[i]);
+    } else {
+      z[i] = -INFINITY;
+    }
+  }
+  const float m = wave_max(lmax);
+  float lsum = 0.f;
+#pragma unroll
+  for (int i = 0; i < VPL; ++i) {
+    const int e = lane + kWave * i;
+    ex[i] = (e < E) ? expf(z[i] - m) : 0.f;
+    lsum += ex[i];
+  }
+  const float s = wave_sum(lsum);
+#pragma unroll
+  for (int i = 0; i < VPL; ++i) pacc[i] += ex[i] / s;
+
+  // k rounds of a wave-wide argmax (largest z, then lowest index)
+  float sel_ex_sum = 0.f;
+  float my_ex = 0.f;  // lane j keeps slot j's exp
+  int my_idx = 0;
+  for (int j = 0; j < k; ++j) {
+    float bv = -INFINITY;
+    int be = 0x7fffffff;
+#pragma unroll
+    for (int i = 0; i < VPL; ++i) {
+      const int e = lane + kWave * i;
+      if (z[i] > bv || (z[i] == bv && e < be)) { bv = z[i]; be = e; }
+    }
+#pragma unroll
+    for (int msk = 32; msk >= 1; msk >>= 1) {
+      const float ov = __shfl_xor(bv, msk, kWave);
+      const int oe = __shfl_xor(be, msk, kWave);
+      if (ov > bv || (ov == bv && oe < be)) { bv = ov; be = oe; }
+    }
+    const int owner = be & (kWave - 1);
+    const int slot = be / kWave;
+    float oex = 0.f;
+#pragma unroll
+    for (int i = 0; i < VPL; ++i) {
+      if (lane == owner && i == slot) {
+        oex = ex[i];
+        z[i] = -INFINITY;
+        cacc[i] += 1;
+      }
+    }
+    const float wex = __shfl(oex, owner, kWave);
+    sel_ex_sum += wex;
+    if (lane == j) { my_ex = wex; my_idx = be; }
+  }
+  if (lane < k) {
+    topk_idx[t * k + lane] = my_idx;
+    topk_w[t * k + lane] = renorm ? my_ex / sel_ex_sum : my_ex / s;
+  }
 }
 
 // ET: upper bound on the number of 16-expert column tiles (E_pad = 16 * n_et <= 16 * ET).
@@ -118,71 +195,14 @@ __global__ __launch_bounds__(kThreads) void route_kernel(
   int32_t cacc[VPL];
 #pragma unroll
   for (int i = 0; i < VPL; ++i) { pacc[i] = 0.f; cacc[i] = 0; }
-
   for (int tt = wave; tt < ntok; tt += 4) {
-    const int64_t t = t0 + tt;
-    float z[VPL], ex[VPL];
-    float lmax = -INFINITY;
+    float l[VPL];
 #pragma unroll
     for (int i = 0; i < VPL; ++i) {
       const int e = lane + kWave * i;
-      if (e < E) {
-        const float l = red[tt * EP + e];
-        z[i] = bias ? __fadd_rn(l, bias[e]) : l;
-        lmax = fmaxf(lmax, z[i]);
-      } else {
-        z[i] = -INFINITY;
-      }
+      l[i] = e < E ? red[tt * EP + e] : 0.f;
     }
-    const float m = wave_max(lmax);
-    float lsum = 0.f;
-#pragma unroll
-    for (int i = 0; i < VPL; ++i) {
-      const int e = lane + kWave * i;
-      ex[i] = (e < E) ? expf(z[i] - m) : 0.f;
-      lsum += ex[i];
-    }
-    const float s = wave_sum(lsum);
-#pragma unroll
-    for (int i = 0; i < VPL; ++i) pacc[i] += ex[i] / s;
-
-    // k rounds of a wave-wide argmax (largest z, then lowest index)
-    float sel_ex_sum = 0.f;
-    float my_ex = 0.f;  // lane j keeps slot j's exp
-    int my_idx = 0;
-    for (int j = 0; j < k; ++j) {
-      float bv = -INFINITY;
-      int be = 0x7fffffff;
-#pragma unroll
-      for (int i = 0; i < VPL; ++i) {
-        const int e = lane + kWave * i;
-        if (z[i] > bv || (z[i] == bv && e < be)) { bv = z[i]; be = e; }
-      }
-#pragma unroll
-      for (int msk = 32; msk >= 1; msk >>= 1) {
-        const float ov = __shfl_xor(bv, msk, kWave);
-        const int oe = __shfl_xor(be, msk, kWave);
-        if (ov > bv || (ov == bv && oe < be)) { bv = ov; be = oe; }
-      }
-      const int owner = be & (kWave - 1);
-      const int slot = be / kWave;
-      float oex = 0.f;
-#pragma unroll
-      for (int i = 0; i < VPL; ++i) {
-        if (lane == owner && i == slot) {
-          oex = ex[i];
-          z[i] = -INFINITY;
-          cacc[i] += 1;
-        }
-      }
-      const float wex = __shfl(oex, owner, kWave);
-      sel_ex_sum += wex;
-      if (lane == j) { my_ex = wex; my_idx = be; }
-    }
-    if (lane < k) {
-      topk_idx[t * k + lane] = my_idx;
-      topk_w[t * k + lane] = renorm ? my_ex / sel_ex_sum : my_ex / s;
-    }
+    gate_token<VPL>(l, lane, E, bias, k, renorm, t0 + tt, topk_idx, topk_w, pacc, cacc);
   }
 
   // ---------------- per-workgroup statistics partials, waves added in order
@@ -203,34 +223,235 @@ __global__ __launch_bounds__(kThreads) void route_kernel(
   }
 }
 
-// One workgroup: per expert, sum the partials over router workgroups in order (float64),
-// then aux = E * sum_e (count_e / (N k)) * prob_mean_e.
-__global__ __launch_bounds__(kThreads) void route_finalize_kernel(
-    const float* __restrict__ part_prob, const int32_t* __restrict__ part_cnt,
-    int64_t n_blocks, int64_t n, int E, int k, int32_t* __restrict__ sel_count,
-    float* __restrict__ prob_mean, float* __restrict__ aux) {
+// ------------------------------------------------------------ bf16 logits product
+constexpr int kLT = 64;    // tokens per logits workgroup
+constexpr int kLKC = 32;   // k per LDS chunk
+constexpr int kLRow = 40;  // LDS row stride in bf16: 80-byte rows make the 16-byte
+                           // fragment reads of 16 consecutive rows conflict free
+
+// W_router [d][E] float32 -> wp[3][E_pad][d] bf16 (k contiguous), the exact three-part
+// split w = hi + mid + lo (each part the bf16 rounding of what the previous parts left);
+// rows e >= E are zero.  Thread (e, 8 consecutive k).
+__global__ __launch_bounds__(kThreads) void route_split_kernel(const float* __restrict__ wr,
+                                                               int64_t d, int E, int E_pad,
+                                                               uint16_t* __restrict__ wp) {
+  const int64_t i = static_cast<int64_t>(blockIdx.x) * kThreads + threadIdx.x;
+  const int64_t nk8 = d / 8;
+  if (i >= static_cast<int64_t>(E_pad) * nk8) return;
+  const int e = static_cast<int>(i % E_pad);  // consecutive lanes: consecutive experts
+  const int64_t k0 = (i / E_pad) * 8;
+  uint32_t hi[4], mid[4], lo[4];
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    uint16_t h2[2], m2[2], l2[2];
+#pragma unroll
+    for (int r = 0; r < 2; ++r) {
+      const float w = e < E ? wr[(k0 + 2 * q + r) * E + e] : 0.f;
+      h2[r] = f32_to_bf16(w);
+      const float r1 = w - bf16_to_f32(h2[r]);  // exact
+      m2[r] = f32_to_bf16(r1);
+      const float r2 = r1 - bf16_to_f32(m2[r]);  // exact
+      l2[r] = f32_to_bf16(r2);
+    }
+    hi[q] = h2[0] | (static_cast<uint32_t>(h2[1]) << 16);
+    mid[q] = m2[0] | (static_cast<uint32_t>(m2[1]) << 16);
+    lo[q] = l2[0] | (static_cast<uint32_t>(l2[1]) << 16);
+  }
+  const int64_t plane = static_cast<int64_t>(E_pad) * d;
+  uint16_t* dst = wp + static_cast<int64_t>(e) * d + k0;
+  *reinterpret_cast<u32x4_t*>(dst) = u32x4_t{hi[0], hi[1], hi[2], hi[3]};
+  *reinterpret_cast<u32x4_t*>(dst + plane) = u32x4_t{mid[0], mid[1], mid[2], mid[3]};
+  *reinterpret_cast<u32x4_t*>(dst + 2 * plane) = u32x4_t{lo[0], lo[1], lo[2], lo[3]};
+}
+
+// Partial logits part[z][t][e] = sum over k in slice z of x[t][k] * w[k][e], for the
+// 64 tokens of workgroup x, the EPT*16 experts of group y and the k slice z (kper wide).
+// Wave w owns tokens 16w..16w+15 and all the group's experts: per 32-deep chunk one
+// activation fragment and 3*EPT weight fragments, 3*EPT MFMAs.  Chunks are staged
+// through LDS, double buffered, with the next chunk's global loads in flight during
+// the current chunk's MFMAs.
+template <int EPT>
+__global__ __launch_bounds__(kThreads) void route_logits_kernel(
+    const uint16_t* __restrict__ x, int64_t n, int64_t d, const uint16_t* __restrict__ wp,
+    int E_pad, int64_t kper, float* __restrict__ part, int E) {
+  constexpr int WROWS = 3 * EPT * 16;            // weight rows per chunk (3 parts)
+  constexpr int WPIECES = WROWS * 4;             // 16-byte pieces per chunk
+  constexpr int WPT = (WPIECES + kThreads - 1) / kThreads;
+  __shared__ __attribute__((aligned(16))) uint16_t xs[2][kLT * kLRow];
+  __shared__ __attribute__((aligned(16))) uint16_t ws[2][WROWS * kLRow];
+  const int tid = threadIdx.x, lane = tid & (kWave - 1), wave = tid / kWave;
+  const int64_t t0 = static_cast<int64_t>(blockIdx.x) * kLT;
+  const int e0 = blockIdx.y * EPT * 16;
+  const int64_t kb = static_cast<int64_t>(blockIdx.z) * kper;
+  const int64_t ke = min(d, kb + kper);
+  const int nch = static_cast<int>((ke - kb + kLKC - 1) / kLKC);
+  const int64_t plane = static_cast<int64_t>(E_pad) * d;
+
+  // this thread's load pieces: x row tid/4, chunk piece tid%4; weights piece tid + 256 j
+  const int xr = tid >> 2, xp = tid & 3;
+  const bool x_ok = t0 + xr < n;
+  const uint16_t* xsrc = x + (x_ok ? t0 + xr : 0) * d + xp * 8;
+  u32x4_t xv, wv[WPT];
+  auto load = [&](int c) {
+    const int64_t k = kb + static_cast<int64_t>(c) * kLKC;
+    const u32x4_t zero = {0u, 0u, 0u, 0u};
+    xv = (x_ok && k + xp * 8 < ke) ? *reinterpret_cast<const u32x4_t*>(xsrc + k) : zero;
+#pragma unroll
+    for (int j = 0; j < WPT; ++j) {
+      const int i = tid + kThreads * j;
+      const int row = i >> 2, pc = i & 3;
+      const int p = row / (EPT * 16), er = row - p * (EPT * 16);
+      wv[j] = (i < WPIECES && k + pc * 8 < ke)
+                  ? *reinterpret_cast<const u32x4_t*>(wp + p * plane +
+                                                      static_cast<int64_t>(e0 + er) * d + k + pc * 8)
+                  : zero;
+    }
+  };
+  auto store = [&](int buf) {
+    *reinterpret_cast<u32x4_t*>(&xs[buf][xr * kLRow + xp * 8]) = xv;
+#pragma unroll
+    for (int j = 0; j < WPT; ++j) {
+      const int i = tid + kThreads * j;
+      if (i < WPIECES) *reinterpret_cast<u32x4_t*>(&ws[buf][(i >> 2) * kLRow + (i & 3) * 8]) = wv[j];
+    }
+  };
+
+  f32x4_t acc[EPT];
+#pragma unroll
+  for (int et = 0; et < EPT; ++et) acc[et] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+  const int fr = lane & 15, fk = (lane >> 4) * 8;  // fragment row and k offset of a lane
+  if (nch > 0) {
+    load(0);
+    store(0);
+  }
+  __syncthreads();
+  for (int c = 0; c < nch; ++c) {
+    const int buf = c & 1;
+    if (c + 1 < nch) load(c + 1);
+    const bf16x8_t a = *reinterpret_cast<const bf16x8_t*>(&xs[buf][(16 * wave + fr) * kLRow + fk]);
+#pragma unroll
+    for (int et = 0; et < EPT; ++et) {
+#pragma unroll
+      for (int p = 0; p < 3; ++p) {
+        const bf16x8_t b = *reinterpret_cast<const bf16x8_t*>(
+            &ws[buf][(p * EPT * 16 + et * 16 + fr) * kLRow + fk]);
+        acc[et] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, acc[et], 0, 0, 0);
+      }
+    }
+    if (c + 1 < nch) store(buf ^ 1);
+    __syncthreads();
+  }
+  // lane holds tokens 16 w + 4 (lane/16) + r, expert e0 + 16 et + lane%16
+#pragma unroll
+  for (int et = 0; et < EPT; ++et) {
+    const int e = e0 + et * 16 + fr;
+    if (e >= E) continue;
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const int64_t t = t0 + 16 * wave + 4 * (lane >> 4) + r;
+      if (t < n) part[(static_cast<int64_t>(blockIdx.z) * n + t) * E + e] = acc[et][r];
+    }
+  }
+}
+
+// ------------------------------------------------------------ gate
+// Gate of 4 * tpw tokens per workgroup (tpw per wave, one token at a time): logits are
+// the sum of the ks partial slices in slice order (or logits_in when ks == 1 and part
+// == logits_in).  Per-workgroup statistics partials are added in wave order.
+template <int VPL>
+__global__ __launch_bounds__(kThreads) void route_gate_kernel(
+    const float* __restrict__ part, int ks, int64_t n, int E, const float* __restrict__ bias,
+    int k, int renorm, int tpw, float* __restrict__ logits_out, int32_t* __restrict__ topk_idx,
+    float* __restrict__ topk_w, float* __restrict__ part_prob, int32_t* __restrict__ part_cnt) {
+  constexpr int EP = VPL * kWave;
+  __shared__ float sprob[4 * EP];
+  __shared__ int32_t scnt[4 * EP];
+  const int lane = lane_id();
+  const int wave = threadIdx.x / kWave;
+  const int64_t tw = (static_cast<int64_t>(blockIdx.x) * 4 + wave) * tpw;  // wave's first token
+  float pacc[VPL];
+  int32_t cacc[VPL];
+#pragma unroll
+  for (int i = 0; i < VPL; ++i) { pacc[i] = 0.f; cacc[i] = 0; }
+  for (int tt = 0; tt < tpw; ++tt) {
+    const int64_t t = tw + tt;
+    if (t >= n) break;
+    float l[VPL];
+#pragma unroll
+    for (int i = 0; i < VPL; ++i) {
+      const int e = lane + kWave * i;
+      float v = 0.f;
+      if (e < E) {
+        for (int z = 0; z < ks; ++z) v += part[(static_cast<int64_t>(z) * n + t) * E + e];
+        if (logits_out) logits_out[t * E + e] = v;
+      }
+      l[i] = v;
+    }
+    gate_token<VPL>(l, lane, E, bias, k, renorm, t, topk_idx, topk_w, pacc, cacc);
+  }
+#pragma unroll
+  for (int i = 0; i < VPL; ++i) {
+    sprob[wave * EP + lane + kWave * i] = pacc[i];
+    scnt[wave * EP + lane + kWave * i] = cacc[i];
+  }
+  __syncthreads();
+  for (int e = threadIdx.x; e < E; e += kThreads) {
+    part_prob[static_cast<int64_t>(blockIdx.x) * E + e] =
+        ((sprob[e] + sprob[EP + e]) + sprob[2 * EP + e]) + sprob[3 * EP + e];
+    part_cnt[static_cast<int64_t>(blockIdx.x) * E + e] =
+        scnt[e] + scnt[EP + e] + scnt[2 * EP + e] + scnt[3 * EP + e];
+  }
+}
+
+// ------------------------------------------------------------ statistics finalize
+// One workgroup per expert: thread j adds rows j, j + 256, ... of the partials in order
+// (float64), then a fixed-shape tree over the 256 threads; writes sel_count, prob_mean
+// and the expert's aux term (count / (N k)) * prob_mean.
+__global__ __launch_bounds__(kThreads) void route_stats_kernel(
+    const float* __restrict__ part_prob, const int32_t* __restrict__ part_cnt, int64_t rows,
+    int64_t n, int E, int k, int32_t* __restrict__ sel_count, float* __restrict__ prob_mean,
+    double* __restrict__ term) {
+  __shared__ double sp[kThreads];
+  __shared__ int64_t sc[kThreads];
+  const int e = blockIdx.x;
+  double ps = 0.0;
+  int64_t cs = 0;
+  for (int64_t b = threadIdx.x; b < rows; b += kThreads) {
+    ps += static_cast<double>(part_prob[b * E + e]);
+    cs += part_cnt[b * E + e];
+  }
+  sp[threadIdx.x] = ps;
+  sc[threadIdx.x] = cs;
+  __syncthreads();
+  for (int s = kThreads / 2; s >= 1; s >>= 1) {
+    if (threadIdx.x < s) {
+      sp[threadIdx.x] += sp[threadIdx.x + s];
+      sc[threadIdx.x] += sc[threadIdx.x + s];
+    }
+    __syncthreads();
+  }
+  if (threadIdx.x == 0) {
+    const double pm = n > 0 ? sp[0] / static_cast<double>(n) : 0.0;
+    const double fr = n > 0 ? static_cast<double>(sc[0]) / static_cast<double>(n * k) : 0.0;
+    if (sel_count) sel_count[e] = static_cast<int32_t>(sc[0]);
+    if (prob_mean) prob_mean[e] = static_cast<float>(pm);
+    term[e] = fr * pm;
+  }
+}
+
+// aux = E * sum_e term[e], the sum over a fixed-shape tree.
+__global__ __launch_bounds__(kThreads) void route_aux_kernel(const double* __restrict__ term,
+                                                             int E, float* __restrict__ aux) {
   __shared__ double red[kThreads];
   double local = 0.0;
-  for (int e = threadIdx.x; e < E; e += kThreads) {
-    double ps = 0.0;
-    int64_t cs = 0;
-    for (int64_t b = 0; b < n_blocks; ++b) {
-      ps += static_cast<double>(part_prob[b * E + e]);
-      cs += part_cnt[b * E + e];
-    }
-    const double pm = n > 0 ? ps / static_cast<double>(n) : 0.0;
-    const double fr = n > 0 ? static_cast<double>(cs) / static_cast<double>(n * k) : 0.0;
-    if (sel_count) sel_count[e] = static_cast<int32_t>(cs);
-    if (prob_mean) prob_mean[e] = static_cast<float>(pm);
-    local += fr * pm;
-  }
+  for (int e = threadIdx.x; e < E; e += kThreads) local += term[e];
   red[threadIdx.x] = local;
   __syncthreads();
   for (int s = kThreads / 2; s >= 1; s >>= 1) {
     if (threadIdx.x < s) red[threadIdx.x] += red[threadIdx.x + s];
     __syncthreads();
   }
-  if (threadIdx.x == 0 && aux) aux[0] = static_cast<float>(static_cast<double>(E) * red[0]);
+  if (threadIdx.x == 0) aux[0] = static_cast<float>(static_cast<double>(E) * red[0]);
 }
 
 template <typename XT, int ET>
@@ -260,29 +481,109 @@ hipError_t launch_route_dt(hipStream_t st, const void* x, int64_t n, int64_t d,
   return launch_route_t<XT, 32>(st, x, n, d, wr, bias, e, k, renorm, li, lo, idx, w, pp, pc);
 }
 
+template <int EPT>
+hipError_t launch_logits_t(hipStream_t st, const uint16_t* x, const RoutePlan& pl,
+                           const uint16_t* wp, float* part) {
+  const dim3 grid(static_cast<unsigned>(pl.token_tiles), static_cast<unsigned>(pl.egroups),
+                  static_cast<unsigned>(pl.ks));
+  hipLaunchKernelGGL((route_logits_kernel<EPT>), grid, dim3(kThreads), 0, st, x, pl.n, pl.d,
+                     wp, pl.e_pad, pl.kper, part, pl.e);
+  return hipGetLastError();
+}
+
+template <int VPL>
+hipError_t launch_gate_t(hipStream_t st, const float* part, int ks, int64_t n, int e,
+                         const float* bias, int k, int renorm, float* lo, int32_t* idx,
+                         float* w, float* pp, int32_t* pc) {
+  const int tpw = gate_tokens_per_wave(n);
+  hipLaunchKernelGGL((route_gate_kernel<VPL>), dim3(static_cast<unsigned>(gate_blocks(n))),
+                     dim3(kThreads), 0, st, part, ks, n, e, bias, k, renorm, tpw, lo, idx, w,
+                     pp, pc);
+  return hipGetLastError();
+}
+
 }  // namespace
 
-hipError_t launch_route(hipStream_t st, const void* x, bool x_bf16, int64_t n, int64_t d,
+hipError_t launch_route(hipStream_t st, const float* x, int64_t n, int64_t d,
                         const float* w_router, const float* logit_bias, int e, int k,
-                        int renorm, const float* logits_in, float* logits_out,
-                        int32_t* topk_idx, float* topk_w, float* part_prob,
-                        int32_t* part_cnt) {
+                        int renorm, float* logits_out, int32_t* topk_idx, float* topk_w,
+                        float* part_prob, int32_t* part_cnt) {
   if (n <= 0) return hipSuccess;
-  if (x_bf16)
-    return launch_route_dt<uint16_t>(st, x, n, d, w_router, logit_bias, e, k, renorm,
-                                     logits_in, logits_out, topk_idx, topk_w, part_prob,
-                                     part_cnt);
-  return launch_route_dt<float>(st, x, n, d, w_router, logit_bias, e, k, renorm, logits_in,
+  return launch_route_dt<float>(st, x, n, d, w_router, logit_bias, e, k, renorm, nullptr,
                                 logits_out, topk_idx, topk_w, part_prob, part_cnt);
 }
 
+RoutePlan route_plan(int64_t n, int64_t d, int e) {
+  RoutePlan pl{};
+  pl.n = n;
+  pl.d = d;
+  pl.e = e;
+  const int tiles = (e + 15) / 16;
+  static const int kEpt[] = {1, 2, 4, 6, 8, 10, 12, 16};
+  pl.ept = 16;
+  for (int v : kEpt)
+    if (v >= tiles) { pl.ept = v; break; }
+  pl.egroups = (tiles + pl.ept - 1) / pl.ept;
+  pl.e_pad = pl.egroups * pl.ept * 16;
+  pl.token_tiles = (n + kLT - 1) / kLT;
+  // split d so that about 256 workgroups run (at most 16 slices: the gate adds them)
+  const int64_t chunks = (d + kLKC - 1) / kLKC;
+  const int64_t base = pl.token_tiles * pl.egroups;
+  int64_t ks = base > 0 ? (256 + base - 1) / base : 1;
+  ks = ks < 1 ? 1 : (ks > 16 ? 16 : ks);
+  ks = ks > chunks ? chunks : ks;
+  pl.kper = ((chunks + ks - 1) / ks) * kLKC;
+  pl.ks = static_cast<int>((d + pl.kper - 1) / pl.kper);
+  return pl;
+}
+
+hipError_t launch_route_split(hipStream_t st, const float* w_router, const RoutePlan& pl,
+                              uint16_t* wp) {
+  const int64_t threads = static_cast<int64_t>(pl.e_pad) * (pl.d / 8);
+  if (threads <= 0) return hipSuccess;
+  hipLaunchKernelGGL(route_split_kernel, dim3(static_cast<unsigned>((threads + kThreads - 1) / kThreads)),
+                     dim3(kThreads), 0, st, w_router, pl.d, pl.e, pl.e_pad, wp);
+  return hipGetLastError();
+}
+
+hipError_t launch_route_logits(hipStream_t st, const uint16_t* x, const RoutePlan& pl,
+                               const uint16_t* wp, float* part) {
+  if (pl.n <= 0) return hipSuccess;
+  switch (pl.ept) {
+    case 1: return launch_logits_t<1>(st, x, pl, wp, part);
+    case 2: return launch_logits_t<2>(st, x, pl, wp, part);
+    case 4: return launch_logits_t<4>(st, x, pl, wp, part);
+    case 6: return launch_logits_t<6>(st, x, pl, wp, part);
+    case 8: return launch_logits_t<8>(st, x, pl, wp, part);
+    case 10: return launch_logits_t<10>(st, x, pl, wp, part);
+    case 12: return launch_logits_t<12>(st, x, pl, wp, part);
+    default: return launch_logits_t<16>(st, x, pl, wp, part);
+  }
+}
+
+hipError_t launch_route_gate(hipStream_t st, const float* part, int ks, int64_t n, int e,
+                             const float* bias, int k, int renorm, float* logits_out,
+                             int32_t* topk_idx, float* topk_w, float* part_prob,
+                             int32_t* part_cnt) {
+  if (n <= 0) return hipSuccess;
+  const int vpl = (e + kWave - 1) / kWave;
+  if (vpl <= 1) return launch_gate_t<1>(st, part, ks, n, e, bias, k, renorm, logits_out, topk_idx, topk_w, part_prob, part_cnt);
+  if (vpl <= 2) return launch_gate_t<2>(st, part, ks, n, e, bias, k, renorm, logits_out, topk_idx, topk_w, part_prob, part_cnt);
+  if (vpl <= 3) return launch_gate_t<3>(st, part, ks, n, e, bias, k, renorm, logits_out, topk_idx, topk_w, part_prob, part_cnt);
+  if (vpl <= 4) return launch_gate_t<4>(st, part, ks, n, e, bias, k, renorm, logits_out, topk_idx, topk_w, part_prob, part_cnt);
+  return launch_gate_t<8>(st, part, ks, n, e, bias, k, renorm, logits_out, topk_idx, topk_w, part_prob, part_cnt);
+}
+
 hipError_t launch_route_finalize(hipStream_t st, const float* part_prob,
-                                 const int32_t* part_cnt, int64_t n_blocks, int64_t n,
-                                 int e, int k, int32_t* sel_count, float* prob_mean,
-                                 float* aux) {
-  if (!sel_count && !prob_mean && !aux) return hipSuccess;
-  hipLaunchKernelGGL(route_finalize_kernel, dim3(1), dim3(kThreads), 0, st, part_prob,
-                     part_cnt, n_blocks, n, e, k, sel_count, prob_mean, aux);
+                                 const int32_t* part_cnt, int64_t rows, int64_t n, int e, int k,
+                                 int32_t* sel_count, float* prob_mean, float* aux, double* term) {
+  hipLaunchKernelGGL(route_stats_kernel, dim3(static_cast<unsigned>(e)), dim3(kThreads), 0, st,
+                     part_prob, part_cnt, rows, n, e, k, sel_count, prob_mean, term);
+  {
+    const hipError_t err = hipGetLastError();
+    if (err != hipSuccess) return err;
+  }
+  if (aux) hipLaunchKernelGGL(route_aux_kernel, dim3(1), dim3(kThreads), 0, st, term, e, aux);
   return hipGetLastError();
 }
 

@@ -94,7 +94,7 @@ class MoELayer:
         c = self.cfg
         n = n_tokens if n_tokens is not None else (x if x is not None else logits_in).shape[0]
         s = self.new_stats(n)
-        ws = workspace(B.moe_route_workspace_size(n, c.n_experts), self.device)
+        ws = workspace(B.moe_route_workspace_size(n, c.d_model, c.n_experts), self.device)
         B.moe_route(x, self.w["w_router"] if x is not None else None, self.w.get("logit_bias"),
                     c.n_experts, c.top_k, c.renormalize, logits_in,
                     s["logits"] if logits_in is None else None, s["topk_idx"], s["topk_w"],

@@ -65,7 +65,10 @@ def test_route_validation():
     assert _route_status() == B.MOE_ERR_INVALID_ARG  # missing outputs
     assert _route_status(idx=fake, w=fake) == B.MOE_ERR_INVALID_ARG  # missing x / w_router
     assert _route_status(idx=fake, w=fake, x=fake, wr=fake, d=6) == B.MOE_ERR_UNSUPPORTED
-    need = L.moe_route_workspace_size(4, 8)
+    # bf16 activations need d_model % 8 == 0, float32 ones d_model % 4 == 0
+    assert _route_status(idx=fake, w=fake, x=fake, wr=fake, d=12) == B.MOE_ERR_UNSUPPORTED
+    assert L.moe_route_workspace_size(4, 64, 8) >= L.moe_route_workspace_size(4, 0, 8) > 0
+    need = L.moe_route_workspace_size(4, 64, 8)
     assert need > 0
     st = _route_status(idx=fake, w=fake, x=fake, wr=fake, ws=fake, wsb=need - 1)
     assert st == B.MOE_ERR_WORKSPACE and "workspace" in L.moe_last_error().decode()

@@ -38,7 +38,7 @@ def _route(x, wr, lb, E, k, renorm=True, logits_in=None, n=None):
                sel=torch.empty(E, dtype=i32, device=DEV),
                pm=torch.empty(E, dtype=f32, device=DEV),
                aux=torch.empty(1, dtype=f32, device=DEV))
-    ws = workspace(B.moe_route_workspace_size(n, E), DEV)
+    ws = workspace(B.moe_route_workspace_size(n, x.shape[1] if x is not None else 0, E), DEV)
     B.moe_route(x, wr, lb, E, k, renorm, logits_in, out["logits"], out["idx"], out["w"],
                 out["sel"], out["pm"], out["aux"], ws, n_tokens=n)
     torch.cuda.synchronize()
@@ -93,6 +93,27 @@ def test_router_parity_full_size(name):
     bad = np.abs(got["logits"].astype(np.float64) - ref) > tol
     assert not bad.any(), f"{bad.sum()} logits outside tolerance"
     _check_gate(got["logits"], h.logit_bias, cfg.top_k, cfg.n_experts, got, cfg.renormalize)
+
+
+# bf16 router shapes: ragged token tiles, expert counts off the 16-expert tiles, two
+# expert groups (E > 256), a d_model tail chunk, one and many d_model slices
+@pytest.mark.parametrize("n,d,E,k", [(1, 64, 8, 2), (65, 200, 40, 3), (130, 1000, 300, 8),
+                                     (64, 4096, 64, 2), (777, 520, 160, 6), (2049, 96, 17, 1),
+                                     (5, 8, 512, 16)])
+def test_router_bf16_shapes(n, d, E, k):
+    print_case("router-bf16", n, d, E, k)
+    rng = np.random.default_rng(n + d + E)
+    xh = synth.f32_to_bf16_bits(rng.standard_normal((n, d)).astype(np.float32))
+    wh = (rng.standard_normal((d, E)) / np.sqrt(d)).astype(np.float32)
+    bh = (rng.standard_normal(E) * 0.1).astype(np.float32)
+    got = _route(_up(xh, "bf16"), torch.from_numpy(wh).to(DEV), torch.from_numpy(bh).to(DEV),
+                 E, k)
+    x64 = O.widen(xh, "bf16")
+    ref = x64 @ wh.astype(np.float64)
+    tol = logits_tolerance(x64, wh.astype(np.float64))
+    bad = np.abs(got["logits"].astype(np.float64) - ref) > tol
+    assert not bad.any(), f"{bad.sum()} logits outside tolerance"
+    _check_gate(got["logits"], bh, k, E, got)
 
 
 @pytest.mark.parametrize("E,k,bias", [(160, 6, False), (160, 6, True), (8, 2, False),
