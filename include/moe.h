@@ -218,7 +218,8 @@ typedef struct {
   /* Timing markers (hipEvent_t handles owned by the caller, or NULL): stage_events[i]
    * is recorded on the stream at boundary i -- 0 before routing, 1 after routing and
    * its statistics, 2 after dispatch, 3 after the routed first expert layer, 4 after
-   * the routed second expert layer, 5 after the shared experts, 6 after the combine. */
+   * the routed second expert layer, 5 once the shared experts are also done (they run
+   * concurrently, see moe_forward), 6 after the combine. */
   void* stage_events[MOE_N_STAGE_EVENTS];
 } moe_stats;
 
@@ -231,6 +232,12 @@ typedef struct {
  * Supported: bf16 with d % 64 == 0 and d_ff % 64 == 0, or float32 with d % 4 == 0 and
  * d_ff % 4 == 0; 1 <= k <= min(E, 16); E <= MOE_MAX_EXPERTS.
  * ws: at least moe_forward_workspace_size(cfg) bytes, 256-byte aligned.
+ * Streams: all work is ordered after earlier work on `stream`, and work enqueued on
+ * `stream` afterwards sees every output.  With shared experts the library forks them
+ * onto an internal stream of the current device (default priority, created on the
+ * first such call and kept until the process ends) and joins it back before the
+ * combine, using events; calls from several host threads are serialised while they
+ * enqueue.
  */
 size_t moe_forward_workspace_size(const moe_config* cfg);
 moe_status moe_forward(void* stream, const moe_config* cfg, const moe_weights* w,

@@ -6,6 +6,8 @@
 #include <cstdarg>
 #include <cstdio>
 #include <functional>
+#include <mutex>
+#include <unordered_map>
 
 #include "../../include/moe.h"
 #include "kernels.h"
@@ -216,6 +218,31 @@ moe_status run_ffn(hipStream_t st, moe_dtype dt, moe_act act, const void* a, int
   g2.seg_off = seg_off; g2.n_seg = n_seg; g2.single_rows = single_rows;
   g2.n_out = static_cast<int32_t>(d); g2.k = static_cast<int32_t>(d_ff);
   return hip_check(moe::launch_gemm(st, bf, moe::EPI_NONE, g2, max_rows), "expert GEMM2 launch");
+}
+
+// A second stream per device (default priority, created on first use) on which the
+// shared experts run concurrently with the router, dispatch and routed experts: they
+// depend on x only.  The fork and join events are reused, so their use is serialised
+// by `mu` for as long as a call enqueues work.
+struct SideStream {
+  hipStream_t s = nullptr;
+  hipEvent_t fork = nullptr, join = nullptr;
+};
+
+std::mutex g_side_mu;
+
+moe_status side_stream(SideStream** out) {
+  static std::unordered_map<int, SideStream> by_dev;
+  int dev = 0;
+  MOE_TRY(hip_check(hipGetDevice(&dev), "hipGetDevice"));
+  SideStream& ss = by_dev[dev];
+  if (!ss.s) {
+    MOE_TRY(hip_check(hipStreamCreateWithFlags(&ss.s, hipStreamNonBlocking), "side stream create"));
+    MOE_TRY(hip_check(hipEventCreateWithFlags(&ss.fork, hipEventDisableTiming), "event create"));
+    MOE_TRY(hip_check(hipEventCreateWithFlags(&ss.join, hipEventDisableTiming), "event create"));
+  }
+  *out = &ss;
+  return MOE_OK;
 }
 
 int64_t capacity_of(int64_t n, int32_t e, int32_t k, double alpha) {
@@ -477,20 +504,31 @@ moe_status moe_forward(void* stream, const moe_config* cfg, const moe_weights* w
                        L.row_token, slot_row, o.kept_count, o.n_dropped, L.x_perm,
                        L.dispatch_ws));
   MOE_TRY(mark(2));
+  // a8 (forked): shared experts, all tokens, on the side stream, concurrent with the
+  // routed experts (forked after the latency-bound router and dispatch, whose few
+  // workgroups would otherwise wait behind its tiles); the S experts act as one FFN of
+  // width S*d_ff (W1/W3 rows concatenate, W2 splits its reduction into S chunks of d_ff)
+  SideStream* side = nullptr;
+  std::unique_lock<std::mutex> side_lock(g_side_mu, std::defer_lock);
+  if (c.n_shared > 0 && n > 0) {
+    side_lock.lock();
+    MOE_TRY(side_stream(&side));
+    MOE_TRY(hip_check(hipEventRecord(side->fork, st), "fork event record"));
+    MOE_TRY(hip_check(hipStreamWaitEvent(side->s, side->fork, 0), "fork wait"));
+    const int64_t dffs = c.d_ff * c.n_shared;
+    MOE_TRY(run_ffn(side->s, c.dtype, c.act, x, c.d_model, nullptr, 1, static_cast<int32_t>(n), n,
+                    c.d_model, dffs, w->shared_w1, w->shared_w3, nullptr, 0, w->shared_w2,
+                    nullptr, c.d_ff, c.d_model * c.d_ff, L.h_sh, L.y_sh, nullptr));
+    MOE_TRY(hip_check(hipEventRecord(side->join, side->s), "join event record"));
+  }
   const int64_t R = max_rows_of(n, e, k, cap);
   // a6-a7: routed experts over the expert-major segments
   MOE_TRY(run_ffn(st, c.dtype, c.act, L.x_perm, c.d_model, offsets, e, 0, R, c.d_model, c.d_ff,
                   w->w1, w->w3, w->b1, c.d_ff * c.d_model, w->w2, w->b2, c.d_ff, 0, L.h,
                   L.y_rows, [&]() { return mark(3); }));
   MOE_TRY(mark(4));
-  // a8: shared experts, all tokens; the S experts act as one FFN of width S*d_ff (W1/W3
-  // rows concatenate, W2 splits its reduction into S chunks of d_ff)
-  if (c.n_shared > 0) {
-    const int64_t dffs = c.d_ff * c.n_shared;
-    MOE_TRY(run_ffn(st, c.dtype, c.act, x, c.d_model, nullptr, 1, static_cast<int32_t>(n), n,
-                    c.d_model, dffs, w->shared_w1, w->shared_w3, nullptr, 0, w->shared_w2,
-                    nullptr, c.d_ff, c.d_model * c.d_ff, L.h_sh, L.y_sh, nullptr));
-  }
+  // join: the combine needs the shared experts' output
+  if (side) MOE_TRY(hip_check(hipStreamWaitEvent(st, side->join, 0), "join wait"));
   MOE_TRY(mark(5));
   // a9: weighted combine (shared first, then slots in order)
   MOE_TRY(hip_check(moe::launch_combine(st, c.dtype == MOE_BF16, L.y_rows, slot_row, tw, n, k,
