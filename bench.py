@@ -14,6 +14,9 @@ kernel, and the CPU oracle timed on a bounded sample of the same workload.
 from __future__ import annotations
 
 import argparse
+import csv
+import glob
+import hashlib
 import json
 import os
 import sys
@@ -28,6 +31,103 @@ PEAK_F32_TFLOPS = 157.3
 PEAK_HBM_GBPS = 8000.0
 METRIC = "MoE-layer tokens/s; grouped-GEMM TFLOP/s & % of MFMA peak; dispatch GB/s"
 STAGES = ["route", "dispatch", "gemm1", "gemm2", "shared", "combine"]
+PROFILES = os.path.join(ROOT, "profiles")
+CSRC = os.path.join(ROOT, "sparse_mixture_experts_forward_amd", "csrc")
+# kernel symbol of each stage's launch, as rocprofv3 names it (bf16 workloads)
+STAGE_KERNEL = {"gemm1_swiglu": "gemm_bf16_kernel<256, 2, false>",
+                "gemm1_gelu": "gemm_bf16_kernel<256, 1, false>",
+                "gemm2": "gemm_bf16_kernel<256, 0, false>"}
+CALIB_KERNEL = "MulFunctor"  # the plain float32 copy (x * 1) that scales byte counters
+
+
+def sources_hash() -> str:
+    """Hash of the HIP sources: stored with counter-derived traffic, which is reported
+    only while the kernels are unchanged."""
+    h = hashlib.sha256()
+    for f in sorted(glob.glob(os.path.join(CSRC, "*"))):
+        with open(f, "rb") as fh:
+            h.update(os.path.basename(f).encode() + fh.read())
+    return h.hexdigest()[:16]
+
+
+def stage_symbol(cfg, stage: str):
+    if stage == "gemm1":
+        return STAGE_KERNEL["gemm1_swiglu" if cfg.act == "swiglu" else "gemm1_gelu"]
+    return STAGE_KERNEL.get(stage)
+
+
+def _pmc_rows(path: str):
+    files = glob.glob(os.path.join(path, "**", "*counter_collection.csv"), recursive=True)
+    rows = []
+    for f in files:
+        with open(f) as fh:
+            rows += list(csv.DictReader(fh))
+    return rows
+
+
+def _counter_values(path: str, counter: str) -> dict:
+    vals = {}
+    for r in _pmc_rows(path):
+        if r["Counter_Name"] == counter:
+            vals.setdefault(r["Kernel_Name"], []).append(float(r["Counter_Value"]))
+    return vals
+
+
+def digest_pmc(cfg_name: str, dirs, calib_mib: int) -> dict:
+    """Per-dispatch HBM bytes of each stage kernel from rocprofv3 --pmc runs of this
+    bench (FETCH_SIZE, WRITE_SIZE; KiB per dispatch), each scaled by what the same
+    counter reads for the plain copy kernel (--calibrate-copy-mib, its own run) that
+    reads and writes calib_mib MiB once.  dirs = (fetch, write, calib_fetch,
+    calib_write)."""
+    from sparse_mixture_experts_forward_amd import CONFIGS
+
+    cfg = CONFIGS[cfg_name]
+    fetch_dir, write_dir, cfetch_dir, cwrite_dir = dirs
+    out = {"config": cfg_name, "sources": sources_hash(), "calib_bytes": calib_mib << 20,
+           "kernels": {}}
+    per = {}
+    for counter, path, cpath in (("FETCH_SIZE", fetch_dir, cfetch_dir),
+                                 ("WRITE_SIZE", write_dir, cwrite_dir)):
+        vals = _counter_values(path, counter)
+        calib = [v for name, vs in _counter_values(cpath, counter).items()
+                 if CALIB_KERNEL in name for v in vs]
+        if len(calib) != 1:
+            raise SystemExit(f"expected one {CALIB_KERNEL} dispatch with {counter} in {cpath}")
+        scale = (calib_mib << 20) / (calib[0] * 1024.0)  # bytes per counted byte
+        per[counter] = (vals, scale)
+        out[counter.lower() + "_calib_kib"] = calib[0]
+        out[counter.lower() + "_scale"] = round(scale, 4)
+    for stage in STAGES:
+        sym = stage_symbol(cfg, stage)
+        if sym is None:
+            continue
+        rec = {}
+        for counter in ("FETCH_SIZE", "WRITE_SIZE"):
+            vals, scale = per[counter]
+            got = [v for name, vs in vals.items() if sym in name for v in vs]
+            if got:
+                rec[counter.lower() + "_bytes"] = round(sum(got) / len(got) * 1024.0 * scale)
+                rec["dispatches"] = len(got)
+        if rec:
+            rec["symbol"] = sym
+            out["kernels"][stage] = rec
+    return out
+
+
+def stored_traffic(cfg_name: str, stage: str):
+    """HBM bytes per launch of a stage kernel from the committed counter digest, or None
+    if there is none or the kernels changed since it was taken."""
+    path = os.path.join(PROFILES, f"traffic_{cfg_name}.json")
+    if not os.path.exists(path):
+        return None
+    with open(path) as fh:
+        d = json.load(fh)
+    if d.get("sources") != sources_hash():
+        return None
+    k = d.get("kernels", {}).get(stage)
+    if not k or "fetch_size_bytes" not in k or "write_size_bytes" not in k:
+        return None
+    return k["fetch_size_bytes"] + k["write_size_bytes"]
 
 
 def describe(cfg) -> str:
@@ -146,9 +246,22 @@ def main():
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--calibrate-copy-mib", type=int, default=0,
-                    help="after the timed steps, run one plain device copy of this many MiB "
-                         "(the reference kernel that scales hardware byte counters)")
+                    help="run only one plain device copy (float32 x * 1) of this many MiB: "
+                         "the reference kernel that scales hardware byte counters")
+    ap.add_argument("--digest-pmc", nargs=4,
+                    metavar=("FETCH_DIR", "WRITE_DIR", "CALIB_FETCH_DIR", "CALIB_WRITE_DIR"),
+                    help="no GPU work: turn rocprofv3 --pmc runs (FETCH_SIZE, WRITE_SIZE) of "
+                         "this bench and of --calibrate-copy-mib into "
+                         "profiles/traffic_<config>.json")
     args = ap.parse_args()
+    if args.digest_pmc:
+        d = digest_pmc(args.config, args.digest_pmc, args.calibrate_copy_mib or 1024)
+        os.makedirs(PROFILES, exist_ok=True)
+        with open(os.path.join(PROFILES, f"traffic_{args.config}.json"), "w") as fh:
+            json.dump(d, fh, indent=1)
+            fh.write("\n")
+        print(json.dumps(d))
+        return
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
         print("bench.py runs on one GPU only: this build has no multi-GPU path "
@@ -156,6 +269,17 @@ def main():
         sys.exit(2)
 
     import torch
+
+    if args.calibrate_copy_mib > 0:
+        # one elementwise kernel that reads and writes calibrate_copy_mib MiB once
+        dev = torch.device("cuda:0")
+        src = torch.ones((args.calibrate_copy_mib << 20) // 4, dtype=torch.float32, device=dev)
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        torch.mul(src, 1.0, out=dst)
+        torch.cuda.synchronize()
+        print(json.dumps({"calibration_copy_bytes": args.calibrate_copy_mib << 20}))
+        return
 
     from sparse_mixture_experts_forward_amd import CONFIGS, MoELayer, synth
     from sparse_mixture_experts_forward_amd import _binding as B
@@ -186,15 +310,6 @@ def main():
     torch.cuda.synchronize()
     elapsed = time.perf_counter() - t0
 
-    if args.calibrate_copy_mib > 0:  # outside the timed region
-        src = torch.empty(args.calibrate_copy_mib << 20, dtype=torch.uint8, device=dev)
-        dst = torch.empty_like(src)
-        src.fill_(1)
-        torch.cuda.synchronize()
-        dst.copy_(src)
-        torch.cuda.synchronize()
-        del src, dst
-
     stage_ms = {s: 0.0 for s in STAGES}
     for row in ev:
         for j, s in enumerate(STAGES):
@@ -206,6 +321,9 @@ def main():
     work = kernel_work(cfg, kept, touched)
     kernels = {s: roofline(s, work[s], stage_ms[s], cfg.dtype) for s in STAGES
                if stage_ms[s] > 0 and (work[s]["flops"] > 0 or work[s]["bytes"] > 0)}
+    for s, r in kernels.items():
+        r["symbol"] = stage_symbol(cfg, s)
+        r["traffic"] = stored_traffic(cfg.name, s)
     dominant = max(kernels, key=lambda s: stage_ms[s])
     gemm_ms = stage_ms["gemm1"] + stage_ms["gemm2"] + stage_ms["shared"]
     gemm_flops = work["gemm1"]["flops"] + work["gemm2"]["flops"] + work["shared"]["flops"]
