@@ -245,6 +245,9 @@ def main():
     ap.add_argument("--config", default="mixtral")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-cold", action="store_true",
+                    help="skip the cold-cache pass (a 1 GiB scratch write before each step "
+                         "evicts L2 and the 256 MB Infinity Cache; stage times only)")
     ap.add_argument("--calibrate-copy-mib", type=int, default=0,
                     help="run only one plain device copy (float32 x * 1) of this many MiB: "
                          "the reference kernel that scales hardware byte counters")
@@ -311,10 +314,35 @@ def main():
     elapsed = time.perf_counter() - t0
 
     stage_ms = {s: 0.0 for s in STAGES}
+    stage_all = {s: [] for s in STAGES}
     for row in ev:
         for j, s in enumerate(STAGES):
-            stage_ms[s] += row[j].elapsed_time(row[j + 1]) / args.steps
+            t = row[j].elapsed_time(row[j + 1])
+            stage_ms[s] += t / args.steps
+            stage_all[s].append(t)
     step_gpu_ms = sum(ev[i][0].elapsed_time(ev[i][-1]) for i in range(args.steps)) / args.steps
+
+    def median(v):
+        v = sorted(v)
+        return v[len(v) // 2] if len(v) % 2 else 0.5 * (v[len(v) // 2 - 1] + v[len(v) // 2])
+
+    cold = None
+    if not args.no_cold:
+        # each step preceded by a 1 GiB scratch write (outside the stage events)
+        scratch = torch.empty(1 << 28, dtype=torch.float32, device=dev)
+        cold_all = {s: [] for s in STAGES}
+        cold_step = []
+        for row in ev:
+            scratch.fill_(1.0)
+            layer.forward(inp.x, y, stats, stage_events=[e.cuda_event for e in row])
+        torch.cuda.synchronize()
+        for row in ev:
+            for j, s in enumerate(STAGES):
+                cold_all[s].append(row[j].elapsed_time(row[j + 1]))
+            cold_step.append(row[0].elapsed_time(row[-1]))
+        del scratch
+        cold = {"step_ms_median": round(median(cold_step), 4),
+                "stages_ms_median": {s: round(median(v), 5) for s, v in cold_all.items()}}
 
     kept = int(stats["kept_count"].sum().item())
     touched = int((stats["kept_count"] > 0).sum().item())
@@ -356,9 +384,15 @@ def main():
         "dispatch_frac_of_hbm": round(disp_gbps / PEAK_HBM_GBPS, 4),
         "combine_gbps": round(comb_gbps, 1),
         "stages_ms": {s: round(v, 5) for s, v in stage_ms.items()},
+        "stages_ms_median": {s: round(median(v), 5) for s, v in stage_all.items()},
         "step_gpu_ms_events": round(step_gpu_ms, 4),
         "kernels": kernels,
     }
+    if cold is not None:
+        cm = cold["stages_ms_median"]
+        cold["dispatch_gbps"] = round(work["dispatch"]["bytes"] / (cm["dispatch"] * 1e-3) / 1e9, 1)
+        cold["combine_gbps"] = round(work["combine"]["bytes"] / (cm["combine"] * 1e-3) / 1e9, 1)
+        out["cold"] = cold
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(cfg, inp, stats["logits"], args.cpu_seconds)
     print(json.dumps(out), flush=True)

@@ -32,6 +32,11 @@ design notes of the repository):
     of the same token are not re-normalised);
   * selection frequency is counted before capacity and divided by N*k;
   * mean router probability is the mean over tokens of the full softmax of z;
+  * with the bias acting on selection only ([Why-MoE] §2.4, the DeepSeek-V3 scheme),
+    selection is still on z, while the gate weights and the mean probabilities come
+    from the softmax of the unbiased logits; the batch-level update lowers the bias of
+    an expert chosen more often than the mean load N*k/E by gamma, raises it by gamma
+    when chosen less often, and leaves it when equal (the step size is the caller's);
   * GELU is the exact erf form; SwiGLU is W2 (SiLU(W1 x) * (W3 x)).
 
 Every function here is pinned by tests that do not call it to check itself (closed
@@ -130,6 +135,26 @@ def gate_weights(p64: np.ndarray, idx: np.ndarray, renormalize: bool = True) -> 
     if renormalize:
         g = g / g.sum(axis=1, keepdims=True)
     return g
+
+
+def update_bias(logit_bias32: np.ndarray, sel_count: np.ndarray, n_tokens: int, k: int,
+                gamma: float) -> np.ndarray:
+    """Batch-level bias update of the bias-for-selection scheme ([Why-MoE] §2.4: an
+    expert whose load is too high gets a lower bias, one whose load is too low a higher
+    one; the logits themselves are untouched).  Load is the number of selections;
+    compared with the mean N*k/E as sel_count*E against N*k (integers, exact).  One
+    float32 addition or subtraction of gamma per expert."""
+    b = np.asarray(logit_bias32, dtype=F32).copy()
+    e = b.shape[0]
+    g = F32(gamma)
+    for i in range(e):
+        load = int(sel_count[i]) * e
+        mean = int(n_tokens) * int(k)
+        if load > mean:
+            b[i] = F32(b[i] - g)
+        elif load < mean:
+            b[i] = F32(b[i] + g)
+    return b
 
 
 @dataclass
@@ -300,6 +325,7 @@ def forward(
     n_shared: int = 0,
     logits: Optional[np.ndarray] = None,
     tokens: Optional[np.ndarray] = None,
+    bias_selection_only: bool = False,
 ) -> ForwardResult:
     """Forward pass of the layer on x [N, d].
 
@@ -308,7 +334,9 @@ def forward(
     [N, E]) is given the router product is skipped and everything downstream is
     conditioned on it (this is how integer results are compared bit for bit).  If
     ``tokens`` is given, only those tokens' outputs are computed (routing, statistics
-    and capacity still see every token, because capacity couples them).
+    and capacity still see every token, because capacity couples them).  With
+    ``bias_selection_only`` the bias steers selection only ([Why-MoE] §2.4): weights
+    and mean probabilities use the softmax of the unbiased logits.
     """
     x64 = widen(x, x_dtype)
     n = x64.shape[0]
@@ -317,7 +345,7 @@ def forward(
     logits = np.asarray(logits, dtype=F32)
     z = biased_scores(logits, logit_bias)
     idx = select_topk(z, k)
-    p = softmax64(z)
+    p = softmax64(logits if bias_selection_only else z)
     w = gate_weights(p, idx, renormalize)
     st = balance_stats(p, idx, n_experts)
     cap = capacity(n, n_experts, k, alpha)

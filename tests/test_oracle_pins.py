@@ -383,3 +383,94 @@ def test_empty_batch():
                   lambda e: ws[e], 3, "gelu", alpha=1.0)
     assert r.y.shape == (0, 4) and r.plan.n_dropped == 0 and r.stats.aux == 0.0
     assert list(r.plan.expert_offsets) == [0, 0, 0, 0]
+
+
+# ------------------------------------------------------------------ bias for selection only
+# [Why-MoE] §2.4 (the DeepSeek-V3 scheme): the bias steers which experts are chosen,
+# the router's own logits give the weights.
+def _route_parts(L, b, k, sel_only):
+    r = O.forward(np.zeros((L.shape[0], 4), np.float32), "f32", np.zeros((4, L.shape[1]), np.float32),
+                  k, lambda e: None, L.shape[1], "gelu", logit_bias=b, logits=L, tokens=np.array([], np.int64),
+                  bias_selection_only=sel_only)
+    return r.topk_idx, r.topk_w, r.stats
+
+
+def test_selection_only_bias_closed_form():
+    # logits [3, 2, 0, -1], a bias of +5 on expert 2 makes it the first choice; the
+    # weights are the unbiased probabilities of {2, 0} renormalised: 1/(e^3+1), e^3/(e^3+1)
+    L = np.array([[3.0, 2.0, 0.0, -1.0]], np.float32)
+    b = np.array([0.0, 0.0, 5.0, 0.0], np.float32)
+    idx, w, _ = _route_parts(L, b, 2, True)
+    assert idx.tolist() == [[2, 0]]
+    e3 = math.exp(3.0)
+    np.testing.assert_allclose(w[0], [1.0 / (e3 + 1.0), e3 / (e3 + 1.0)], rtol=1e-15)
+    # the same bias feeding the weights (DeepSeek-V2) gives e^5 / (e^5 + e^3) for slot 0
+    _, w2, _ = _route_parts(L, b, 2, False)
+    np.testing.assert_allclose(w2[0, 0], math.exp(5.0) / (math.exp(5.0) + e3), rtol=1e-15)
+
+
+def test_selection_only_weights_ignore_a_bias_that_keeps_the_choice():
+    rng = _rng(11)
+    L = (rng.standard_normal((50, 6)) * 3).astype(np.float32)
+    idx0, w0, _ = _route_parts(L, None, 2, True)
+    # a bias small enough to leave every top-2 set and slot order unchanged
+    z = np.sort(L, axis=1)[:, ::-1]
+    gap = float(np.min(z[:, 0:2] - z[:, 1:3]))
+    b = (rng.random(6).astype(np.float32) - 0.5) * np.float32(gap * 0.4)
+    idx1, w1, _ = _route_parts(L, b, 2, True)
+    assert np.array_equal(idx0, idx1)
+    assert np.array_equal(w0, w1)
+    _, wv2, _ = _route_parts(L, b, 2, False)  # with the bias in the weights they move
+    assert not np.array_equal(w0, wv2)
+
+
+def test_selection_only_zero_bias_is_the_plain_router():
+    rng = _rng(12)
+    L = rng.standard_normal((40, 8)).astype(np.float32)
+    for sel_only in (False, True):
+        idx, w, st = _route_parts(L, np.zeros(8, np.float32), 3, sel_only)
+        idxn, wn, stn = _route_parts(L, None, 3, False)
+        assert np.array_equal(idx, idxn) and np.array_equal(w, wn)
+        assert np.array_equal(st.prob_mean, stn.prob_mean)
+
+
+def test_selection_only_aux_is_one_on_equal_logits():
+    # equal logits: unbiased probabilities are exactly 1/E, so prob_mean = 1/E and
+    # aux = E * sum(freq / E) = 1 whatever the bias makes the selection
+    E, k, n = 8, 2, 64
+    L = np.zeros((n, E), np.float32)
+    b = np.array([3, 2, 1, 0, 0, 0, 0, 0], np.float32)
+    idx, _, st = _route_parts(L, b, k, True)
+    assert (idx == np.array([0, 1])).all()
+    np.testing.assert_array_equal(st.prob_mean, np.full(E, 1.0 / E))
+    assert st.aux == 1.0
+    _, _, st2 = _route_parts(L, b, k, False)  # the V2 reading counts the bias
+    assert st2.aux > 1.0
+
+
+def test_bias_update_worked_example():
+    # N*k = 8 selections over 4 experts: mean load 2; loads [3, 1, 2, 2]
+    sel = np.array([3, 1, 2, 2])
+    b = np.array([0.5, -0.25, 0.0, 1.0], np.float32)
+    got = O.update_bias(b, sel, n_tokens=4, k=2, gamma=0.25)
+    assert got.dtype == np.float32
+    assert got.tolist() == [0.25, 0.0, 0.0, 1.0]
+    # a mean load that is not an integer: N*k = 7 over 2 experts -> 3.5
+    got = O.update_bias(np.zeros(2, np.float32), np.array([4, 3]), n_tokens=7, k=1, gamma=0.125)
+    assert got.tolist() == [-0.125, 0.125]
+
+
+def test_bias_update_balances_a_skewed_router():
+    # repeated route + update on fixed skewed logits: the load of the busiest expert
+    # ends far lower than it started, near the mean load
+    rng = _rng(13)
+    E, k, n = 8, 2, 512
+    L = (rng.standard_normal((n, E)) + np.linspace(2.0, 0.0, E)).astype(np.float32)
+    b = np.zeros(E, np.float32)
+    loads = []
+    for _ in range(60):
+        idx, _, st = _route_parts(L, b, k, True)
+        loads.append(int(st.sel_count.max()))
+        b = O.update_bias(b, st.sel_count, n, k, gamma=0.05)
+    assert loads[-1] < 0.6 * loads[0]
+    assert loads[-1] <= 1.5 * n * k / E
