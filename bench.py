@@ -139,6 +139,8 @@ def describe(cfg) -> str:
         s += f" capacity_factor={cfg.alpha}"
     if cfg.logit_bias != "none":
         s += f" logit_bias={cfg.logit_bias}"
+    if cfg.bias_selection_only:
+        s += " (bias for selection only)"
     return s
 
 
@@ -212,6 +214,7 @@ def cpu_baseline(cfg, inp, logits, budget_s: float):
         t0 = time.perf_counter()
         O.forward(x, cfg.dtype, wr, cfg.top_k, lambda e: widen_expert(raw[e]), cfg.n_experts,
                   cfg.act, logit_bias=lb, alpha=cfg.alpha, renormalize=cfg.renormalize,
+                  bias_selection_only=cfg.bias_selection_only,
                   shared=(lambda s: widen_expert(sraw[s])) if cfg.n_shared else None,
                   n_shared=cfg.n_shared, tokens=np.arange(n_s))
         return time.perf_counter() - t0
@@ -245,6 +248,9 @@ def main():
     ap.add_argument("--config", default="mixtral")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--bias-selection-only", action="store_true",
+                    help="the logit bias steers selection only (weights from the unbiased "
+                         "softmax)")
     ap.add_argument("--no-cold", action="store_true",
                     help="skip the cold-cache pass (a 1 GiB scratch write before each step "
                          "evicts L2 and the 256 MB Infinity Cache; stage times only)")
@@ -289,6 +295,8 @@ def main():
 
     B.lib()  # fails loudly if the HIP library is not built
     cfg = CONFIGS[args.config]
+    if args.bias_selection_only:
+        cfg = cfg.scaled(bias_selection_only=True)
     dev = torch.device("cuda:0")
     inp = synth.DeviceInputs(cfg, dev)
     layer = MoELayer.from_inputs(inp)

@@ -77,6 +77,10 @@ int64_t moe_capacity(int64_t n_tokens, int32_t n_experts, int32_t k, double alph
  *                  selecting on p because softmax is increasing)
  *   topk_w[t][j] = p[t][topk_idx[t][j]] / sum_j' p[t][topk_idx[t][j']] if renormalize,
  *                  else p[t][topk_idx[t][j]]          ([Why-MoE] §2.2 renormalisation)
+ *   bias_selection_only = 1 ([Why-MoE] §2.4, the DeepSeek-V3 scheme): selection is
+ *                  still on z, but p[t][:] = softmax(logits[t][:]) (unbiased) for the
+ *                  weights and prob_mean: the bias steers which experts are chosen and
+ *                  leaves the router's own probabilities alone.
  *   sel_count[e] = number of (t, j) with topk_idx[t][j] == e (before any capacity)
  *   prob_mean[e] = (1/N) sum_t p[t][e]
  *   aux[0]       = E * sum_e (sel_count[e] / (N*k)) * prob_mean[e]
@@ -106,9 +110,26 @@ size_t moe_route_workspace_size(int64_t n_tokens, int64_t d_model, int32_t n_exp
 moe_status moe_route(void* stream, const void* x, moe_dtype x_dtype, int64_t n_tokens,
                      int64_t d_model, const float* w_router, const float* logit_bias,
                      int32_t n_experts, int32_t k, int32_t renormalize,
+                     int32_t bias_selection_only,
                      const float* logits_in, float* logits_out, int32_t* topk_idx,
                      float* topk_w, int32_t* sel_count, float* prob_mean, float* aux,
                      void* ws, size_t ws_bytes);
+
+/*
+ * moe_update_bias -- batch-level update of the selection bias ([Why-MoE] §2.4: an
+ * expert whose load is too high gets its bias lowered, one whose load is too low gets
+ * it raised; the router's weights are not touched).  With the load of expert e taken
+ * as sel_count[e] (its selections in a batch of n_tokens tokens, as moe_route writes
+ * it) and the mean load n_tokens*k/E:
+ *   logit_bias[e] -= gamma  if sel_count[e]*E > n_tokens*k
+ *   logit_bias[e] += gamma  if sel_count[e]*E < n_tokens*k     (float32 add/subtract)
+ * and unchanged when equal (integer comparison, exact).  The step size gamma is the
+ * caller's (the pages leave it open).  sel_count [E] int32 and logit_bias [E] float32
+ * are device arrays; logit_bias is updated in place.  Needs n_tokens >= 0, 1 <= k,
+ * 1 <= E <= MOE_MAX_EXPERTS, finite gamma.
+ */
+moe_status moe_update_bias(void* stream, const int32_t* sel_count, int32_t n_experts,
+                           int64_t n_tokens, int32_t k, float gamma, float* logit_bias);
 
 /*
  * moe_dispatch -- capacity clipping and permutation of tokens by expert.
@@ -182,6 +203,7 @@ typedef struct {
   int32_t top_k;          /* k */
   int32_t n_shared;       /* always-on shared experts (0..8) */
   int32_t renormalize;    /* 1: divide the k weights by their sum */
+  int32_t bias_selection_only; /* 1: logit_bias steers selection only (see moe_route) */
   moe_act act;
   moe_dtype dtype;        /* x, expert weights, intermediates and output */
   double capacity_factor; /* alpha; <= 0 means no capacity limit */

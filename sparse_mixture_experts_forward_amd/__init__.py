@@ -8,6 +8,6 @@ generator.
 from ._binding import (  # noqa: F401
     MOE_ACT_GELU, MOE_ACT_SWIGLU, MOE_BF16, MOE_F32, MoEError, lib, make_config, moe_capacity,
     moe_combine, moe_dispatch, moe_dispatch_workspace_size, moe_expert_ffn, moe_forward,
-    moe_forward_workspace_size, moe_route, moe_route_workspace_size)
+    moe_forward_workspace_size, moe_route, moe_route_workspace_size, moe_update_bias)
 from .configs import CONFIGS, MoEConfig  # noqa: F401
 from .layer import MoELayer, workspace  # noqa: F401

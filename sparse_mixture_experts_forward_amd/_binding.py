@@ -31,7 +31,8 @@ class MoEError(RuntimeError):
 class MoEConfigC(C.Structure):
     _fields_ = [("n_tokens", C.c_int64), ("d_model", C.c_int64), ("d_ff", C.c_int64),
                 ("n_experts", C.c_int32), ("top_k", C.c_int32), ("n_shared", C.c_int32),
-                ("renormalize", C.c_int32), ("act", C.c_int), ("dtype", C.c_int),
+                ("renormalize", C.c_int32), ("bias_selection_only", C.c_int32),
+                ("act", C.c_int), ("dtype", C.c_int),
                 ("capacity_factor", C.c_double)]
 
 
@@ -56,8 +57,9 @@ _VP, _I64, _I32, _SZ, _DBL = C.c_void_p, C.c_int64, C.c_int32, C.c_size_t, C.c_d
 _SIGS = {
     "moe_capacity": (_I64, [_I64, _I32, _I32, _DBL]),
     "moe_route_workspace_size": (_SZ, [_I64, _I64, _I32]),
-    "moe_route": (C.c_int, [_VP, _VP, C.c_int, _I64, _I64, _VP, _VP, _I32, _I32, _I32, _VP, _VP,
-                            _VP, _VP, _VP, _VP, _VP, _VP, _SZ]),
+    "moe_route": (C.c_int, [_VP, _VP, C.c_int, _I64, _I64, _VP, _VP, _I32, _I32, _I32, _I32, _VP,
+                            _VP, _VP, _VP, _VP, _VP, _VP, _VP, _SZ]),
+    "moe_update_bias": (C.c_int, [_VP, _VP, _I32, _I64, _I32, C.c_float, _VP]),
     "moe_dispatch_workspace_size": (_SZ, [_I64, _I32, _I32]),
     "moe_dispatch": (C.c_int, [_VP, _VP, _I64, _I32, _I32, _I64, _VP, C.c_int, _I64, _VP, _VP,
                                _VP, _VP, _VP, _VP, _VP, _SZ]),
@@ -140,16 +142,24 @@ def moe_route_workspace_size(n_tokens: int, d_model: int, n_experts: int) -> int
 
 def moe_route(x, w_router, logit_bias, n_experts: int, k: int, renormalize: bool,
               logits_in, logits_out, topk_idx, topk_w, sel_count, prob_mean, aux, ws,
-              n_tokens: Optional[int] = None, stream=None):
+              n_tokens: Optional[int] = None, stream=None, bias_selection_only: bool = False):
     if n_tokens is None:
         n_tokens = (x if x is not None else logits_in).shape[0]
     d = x.shape[1] if x is not None else 0
     xdt = _dtype(x) if x is not None else MOE_F32
     st = lib().moe_route(_stream(stream), _ptr(x), xdt, n_tokens, d, _ptr(w_router),
                          _ptr(logit_bias), n_experts, k, 1 if renormalize else 0,
-                         _ptr(logits_in), _ptr(logits_out), _ptr(topk_idx), _ptr(topk_w),
+                         1 if bias_selection_only else 0, _ptr(logits_in), _ptr(logits_out),
+                         _ptr(topk_idx), _ptr(topk_w),
                          _ptr(sel_count), _ptr(prob_mean), _ptr(aux), _ptr(ws), _ws_bytes(ws))
     _check("moe_route", st)
+
+
+def moe_update_bias(sel_count, n_experts: int, n_tokens: int, k: int, gamma: float, logit_bias,
+                    stream=None):
+    st = lib().moe_update_bias(_stream(stream), _ptr(sel_count), n_experts, n_tokens, k,
+                               float(gamma), _ptr(logit_bias))
+    _check("moe_update_bias", st)
 
 
 def moe_dispatch_workspace_size(n_tokens: int, k: int, n_experts: int) -> int:
@@ -187,9 +197,9 @@ def moe_combine(y_rows, slot_row, topk_w, shared_y, out, stream=None):
 
 
 def make_config(n_tokens, d_model, d_ff, n_experts, top_k, act, dtype, capacity_factor=0.0,
-                n_shared=0, renormalize=True) -> MoEConfigC:
+                n_shared=0, renormalize=True, bias_selection_only=False) -> MoEConfigC:
     return MoEConfigC(n_tokens, d_model, d_ff, n_experts, top_k, n_shared,
-                      1 if renormalize else 0, act, dtype,
+                      1 if renormalize else 0, 1 if bias_selection_only else 0, act, dtype,
                       float(capacity_factor) if capacity_factor else 0.0)
 
 

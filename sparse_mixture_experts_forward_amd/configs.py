@@ -32,6 +32,7 @@ class MoEConfig:
     n_shared: int = 0
     logit_bias: str = "none"  # "none" | "skew4" (+2.0 on experts 0..3) | "uniform0.1"
     renormalize: bool = True
+    bias_selection_only: bool = False  # the logit bias steers selection only (V3 scheme)
 
     def with_tokens(self, n: int) -> "MoEConfig":
         return replace(self, n_tokens=n)

@@ -112,6 +112,10 @@ RouteWs route_layout(Carve& c, int64_t n, int64_t d, int32_t e) {
   return r;
 }
 
+int32_t gate_flags(int32_t renormalize, int32_t bias_selection_only) {
+  return (renormalize ? moe::kGateRenorm : 0) | (bias_selection_only ? moe::kGateSelectionOnly : 0);
+}
+
 size_t route_ws(int64_t n, int64_t d, int32_t e) {
   Carve c(nullptr);
   route_layout(c, n, d, e);
@@ -128,7 +132,7 @@ size_t dispatch_ws(int64_t n, int32_t k, int32_t e) {
 }
 
 moe_status run_route(hipStream_t st, const void* x, moe_dtype xt, int64_t n, int64_t d,
-                     const float* wr, const float* bias, int32_t e, int32_t k, int32_t renorm,
+                     const float* wr, const float* bias, int32_t e, int32_t k, int32_t flags,
                      const float* logits_in, float* logits_out, int32_t* idx, float* w,
                      int32_t* sel, float* pm, float* aux, void* ws) {
   Carve c(ws);
@@ -137,7 +141,7 @@ moe_status run_route(hipStream_t st, const void* x, moe_dtype xt, int64_t n, int
   if (logits_in) {
     // the gate alone, over the caller's logits
     rows = moe::gate_blocks(n);
-    MOE_TRY(hip_check(moe::launch_route_gate(st, logits_in, 1, n, e, bias, k, renorm, logits_out,
+    MOE_TRY(hip_check(moe::launch_route_gate(st, logits_in, 1, n, e, bias, k, flags, logits_out,
                                              idx, w, r.pp, r.pc),
                       "router gate launch"));
   } else if (xt == MOE_BF16) {
@@ -148,13 +152,13 @@ moe_status run_route(hipStream_t st, const void* x, moe_dtype xt, int64_t n, int
     MOE_TRY(hip_check(moe::launch_route_split(st, wr, pl, r.wp), "router weight split launch"));
     MOE_TRY(hip_check(moe::launch_route_logits(st, static_cast<const uint16_t*>(x), pl, r.wp, r.part),
                       "router logits launch"));
-    MOE_TRY(hip_check(moe::launch_route_gate(st, r.part, pl.ks, n, e, bias, k, renorm, logits_out,
+    MOE_TRY(hip_check(moe::launch_route_gate(st, r.part, pl.ks, n, e, bias, k, flags, logits_out,
                                              idx, w, r.pp, r.pc),
                       "router gate launch"));
   } else {
     rows = moe::route_blocks(n);
     MOE_TRY(hip_check(moe::launch_route(st, static_cast<const float*>(x), n, d, wr, bias, e, k,
-                                        renorm, logits_out, idx, w, r.pp, r.pc),
+                                        flags, logits_out, idx, w, r.pp, r.pc),
                       "router kernel launch"));
   }
   return hip_check(moe::launch_route_finalize(st, r.pp, r.pc, rows, n, e, k, sel, pm, aux, r.term),
@@ -345,7 +349,7 @@ size_t moe_route_workspace_size(int64_t n_tokens, int64_t d_model, int32_t n_exp
 moe_status moe_route(void* stream, const void* x, moe_dtype x_dtype, int64_t n_tokens,
                      int64_t d_model, const float* w_router, const float* logit_bias,
                      int32_t n_experts, int32_t k, int32_t renormalize,
-                     const float* logits_in, float* logits_out, int32_t* topk_idx,
+                     int32_t bias_selection_only, const float* logits_in, float* logits_out, int32_t* topk_idx,
                      float* topk_w, int32_t* sel_count, float* prob_mean, float* aux,
                      void* ws, size_t ws_bytes) {
   MOE_TRY(check_route_args(x, x_dtype, n_tokens, d_model, w_router, n_experts, k, logits_in,
@@ -357,8 +361,21 @@ moe_status moe_route(void* stream, const void* x, moe_dtype x_dtype, int64_t n_t
     MOE_TRY(check_aligned(ws, kAlign, "ws"));
   }
   return run_route(static_cast<hipStream_t>(stream), x, x_dtype, n_tokens, d_model, w_router,
-                   logit_bias, n_experts, k, renormalize ? 1 : 0, logits_in, logits_out,
+                   logit_bias, n_experts, k, gate_flags(renormalize, bias_selection_only),
+                   logits_in, logits_out,
                    topk_idx, topk_w, sel_count, prob_mean, aux, ws);
+}
+
+moe_status moe_update_bias(void* stream, const int32_t* sel_count, int32_t n_experts,
+                           int64_t n_tokens, int32_t k, float gamma, float* logit_bias) {
+  if (n_experts < 1) return fail(MOE_ERR_INVALID_ARG, "n_experts < 1");
+  if (n_experts > MOE_MAX_EXPERTS) return fail(MOE_ERR_UNSUPPORTED, "n_experts > %d", MOE_MAX_EXPERTS);
+  if (n_tokens < 0 || k < 1) return fail(MOE_ERR_INVALID_ARG, "need n_tokens >= 0 and k >= 1");
+  if (!std::isfinite(gamma)) return fail(MOE_ERR_INVALID_ARG, "gamma must be finite");
+  if (!sel_count || !logit_bias) return fail(MOE_ERR_INVALID_ARG, "sel_count and logit_bias are required");
+  return hip_check(moe::launch_update_bias(static_cast<hipStream_t>(stream), sel_count, n_experts,
+                                           n_tokens, k, gamma, logit_bias),
+                   "bias update launch");
 }
 
 size_t moe_dispatch_workspace_size(int64_t n_tokens, int32_t k, int32_t n_experts) {
@@ -495,7 +512,8 @@ moe_status moe_forward(void* stream, const moe_config* cfg, const moe_weights* w
   MOE_TRY(mark(0));
   // a1-a3: router product, gate, statistics
   MOE_TRY(run_route(st, x, c.dtype, n, c.d_model, w->w_router, w->logit_bias, e, k,
-                    c.renormalize ? 1 : 0, nullptr, o.logits, idx, tw, o.sel_count,
+                    gate_flags(c.renormalize, c.bias_selection_only), nullptr, o.logits, idx,
+                    tw, o.sel_count,
                     o.prob_mean, o.aux, L.route_ws));
   MOE_TRY(mark(1));
   // a4-a5: capacity and permutation

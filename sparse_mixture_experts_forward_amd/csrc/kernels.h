@@ -8,6 +8,11 @@
 namespace moe {
 
 // ---------------------------------------------------------------- router
+// Gate flags (the `renorm` argument of the router launchers): renormalise the k
+// weights; the bias steers selection only (weights and statistics from the softmax of
+// the unbiased logits).
+constexpr int kGateRenorm = 1;
+constexpr int kGateSelectionOnly = 2;
 constexpr int kRouteTokens = 16;  // tokens per router workgroup
 
 inline int64_t route_blocks(int64_t n_tokens) {
@@ -50,6 +55,10 @@ hipError_t launch_route_gate(hipStream_t st, const float* part, int ks, int64_t 
                              const float* bias, int k, int renorm, float* logits_out,
                              int32_t* topk_idx, float* topk_w, float* part_prob,
                              int32_t* part_cnt);
+
+// Batch-level bias update: b[e] -= gamma if sel_count[e]*E > N*k, += gamma if below.
+hipError_t launch_update_bias(hipStream_t st, const int32_t* sel_count, int e, int64_t n, int k,
+                              float gamma, float* logit_bias);
 
 // Statistics over `rows` partial rows: per-expert workgroups (sel_count, prob_mean and
 // the aux terms, `term` is E doubles of scratch), then the aux sum.

@@ -41,32 +41,35 @@ __device__ __forceinline__ void load_x4(const uint16_t* p, float v[4]) {
 }
 
 // Gate of one token by one wave: lane j holds the logits l[i] of experts j + 64 i.
+// Selection is on z = l + bias; the probabilities are the softmax of z, or with
+// sel_only (the bias steers selection only, [Why-MoE] §2.4) the softmax of l.
 // Writes topk_idx / topk_w of token t and adds p and the selection counts to the lane's
 // statistics accumulators.
 template <int VPL>
 __device__ __forceinline__ void gate_token(const float (&l)[VPL], int lane, int E,
                                            const float* __restrict__ bias, int k, int renorm,
-                                           int64_t t, int32_t* __restrict__ topk_idx,
+                                           int sel_only, int64_t t,
+                                           int32_t* __restrict__ topk_idx,
                                            float* __restrict__ topk_w, float (&pacc)[VPL],
                                            int32_t (&cacc)[VPL]) {
   float z[VPL], ex[VPL];
-  float lmax = -INFINITY;
+  float qmax = -INFINITY;
 #pragma unroll
   for (int i = 0; i < VPL; ++i) {
     const int e = lane + kWave * i;
     if (e < E) {
       z[i] = bias ? __fadd_rn(l[i], bias[e]) : l[i];
-      lmax = fmaxf(lmax, z[i]);
+      qmax = fmaxf(qmax, sel_only ? l[i] : z[i]);
     } else {
       z[i] = -INFINITY;
     }
   }
-  const float m = wave_max(lmax);
+  const float m = wave_max(qmax);
   float lsum = 0.f;
 #pragma unroll
   for (int i = 0; i < VPL; ++i) {
     const int e = lane + kWave * i;
-    ex[i] = (e < E) ? expf(z[i] - m) : 0.f;
+    ex[i] = (e < E) ? expf((sel_only ? l[i] : z[i]) - m) : 0.f;
     lsum += ex[i];
   }
   const float s = wave_sum(lsum);
@@ -116,11 +119,12 @@ __device__ __forceinline__ void gate_token(const float (&l)[VPL], int lane, int 
 template <typename XT, int ET>
 __global__ __launch_bounds__(kThreads) void route_kernel(
     const XT* __restrict__ x, int64_t n, int64_t d, const float* __restrict__ wr,
-    const float* __restrict__ bias, int E, int k, int renorm,
+    const float* __restrict__ bias, int E, int k, int flags,
     const float* __restrict__ logits_in, float* __restrict__ logits_out,
     int32_t* __restrict__ topk_idx, float* __restrict__ topk_w,
     float* __restrict__ part_prob, int32_t* __restrict__ part_cnt) {
   constexpr int EP = ET * 16;             // padded expert count (LDS row stride)
+  const int renorm = flags & kGateRenorm, sel_only = (flags & kGateSelectionOnly) ? 1 : 0;
   constexpr int VPL = (EP + kWave - 1) / kWave;  // experts per lane in the gate
   __shared__ float red[kRouteTokens * EP];
   __shared__ float sprob[4 * EP];
@@ -202,7 +206,7 @@ __global__ __launch_bounds__(kThreads) void route_kernel(
       const int e = lane + kWave * i;
       l[i] = e < E ? red[tt * EP + e] : 0.f;
     }
-    gate_token<VPL>(l, lane, E, bias, k, renorm, t0 + tt, topk_idx, topk_w, pacc, cacc);
+    gate_token<VPL>(l, lane, E, bias, k, renorm, sel_only, t0 + tt, topk_idx, topk_w, pacc, cacc);
   }
 
   // ---------------- per-workgroup statistics partials, waves added in order
@@ -361,9 +365,10 @@ __global__ __launch_bounds__(kThreads) void route_logits_kernel(
 template <int VPL>
 __global__ __launch_bounds__(kThreads) void route_gate_kernel(
     const float* __restrict__ part, int ks, int64_t n, int E, const float* __restrict__ bias,
-    int k, int renorm, int tpw, float* __restrict__ logits_out, int32_t* __restrict__ topk_idx,
+    int k, int flags, int tpw, float* __restrict__ logits_out, int32_t* __restrict__ topk_idx,
     float* __restrict__ topk_w, float* __restrict__ part_prob, int32_t* __restrict__ part_cnt) {
   constexpr int EP = VPL * kWave;
+  const int renorm = flags & kGateRenorm, sel_only = (flags & kGateSelectionOnly) ? 1 : 0;
   __shared__ float sprob[4 * EP];
   __shared__ int32_t scnt[4 * EP];
   const int lane = lane_id();
@@ -387,7 +392,7 @@ __global__ __launch_bounds__(kThreads) void route_gate_kernel(
       }
       l[i] = v;
     }
-    gate_token<VPL>(l, lane, E, bias, k, renorm, t, topk_idx, topk_w, pacc, cacc);
+    gate_token<VPL>(l, lane, E, bias, k, renorm, sel_only, t, topk_idx, topk_w, pacc, cacc);
   }
 #pragma unroll
   for (int i = 0; i < VPL; ++i) {
@@ -437,6 +442,19 @@ __global__ __launch_bounds__(kThreads) void route_stats_kernel(
     if (prob_mean) prob_mean[e] = static_cast<float>(pm);
     term[e] = fr * pm;
   }
+}
+
+// Batch-level bias update of the bias-for-selection scheme ([Why-MoE] §2.4): an expert
+// chosen more often than the mean load N*k/E (compared as sel_count*E against N*k, in
+// integers) has gamma subtracted from its bias, one chosen less often gamma added.
+__global__ __launch_bounds__(kThreads) void route_update_bias_kernel(
+    const int32_t* __restrict__ sel_count, int E, int64_t nk, float gamma,
+    float* __restrict__ logit_bias) {
+  const int e = blockIdx.x * kThreads + threadIdx.x;
+  if (e >= E) return;
+  const int64_t load = static_cast<int64_t>(sel_count[e]) * E;
+  const float b = logit_bias[e];
+  logit_bias[e] = load > nk ? __fsub_rn(b, gamma) : (load < nk ? __fadd_rn(b, gamma) : b);
 }
 
 // aux = E * sum_e term[e], the sum over a fixed-shape tree.
@@ -572,6 +590,13 @@ hipError_t launch_route_gate(hipStream_t st, const float* part, int ks, int64_t 
   if (vpl <= 3) return launch_gate_t<3>(st, part, ks, n, e, bias, k, renorm, logits_out, topk_idx, topk_w, part_prob, part_cnt);
   if (vpl <= 4) return launch_gate_t<4>(st, part, ks, n, e, bias, k, renorm, logits_out, topk_idx, topk_w, part_prob, part_cnt);
   return launch_gate_t<8>(st, part, ks, n, e, bias, k, renorm, logits_out, topk_idx, topk_w, part_prob, part_cnt);
+}
+
+hipError_t launch_update_bias(hipStream_t st, const int32_t* sel_count, int e, int64_t n, int k,
+                              float gamma, float* logit_bias) {
+  hipLaunchKernelGGL(route_update_bias_kernel, dim3(static_cast<unsigned>((e + kThreads - 1) / kThreads)),
+                     dim3(kThreads), 0, st, sel_count, e, n * k, gamma, logit_bias);
+  return hipGetLastError();
 }
 
 hipError_t launch_route_finalize(hipStream_t st, const float* part_prob,

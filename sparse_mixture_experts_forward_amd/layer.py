@@ -49,7 +49,7 @@ class MoELayer:
         c = self.cfg
         return B.make_config(n_tokens, c.d_model, c.d_ff, c.n_experts, c.top_k, _act(c.act),
                              B.MOE_BF16 if c.dtype == "bf16" else B.MOE_F32,
-                             c.alpha or 0.0, c.n_shared, c.renormalize)
+                             c.alpha or 0.0, c.n_shared, c.renormalize, c.bias_selection_only)
 
     def capacity(self, n_tokens: int) -> int:
         c = self.cfg
@@ -98,8 +98,15 @@ class MoELayer:
         B.moe_route(x, self.w["w_router"] if x is not None else None, self.w.get("logit_bias"),
                     c.n_experts, c.top_k, c.renormalize, logits_in,
                     s["logits"] if logits_in is None else None, s["topk_idx"], s["topk_w"],
-                    s["sel_count"], s["prob_mean"], s["aux"], ws, n_tokens=n, stream=stream)
+                    s["sel_count"], s["prob_mean"], s["aux"], ws, n_tokens=n, stream=stream,
+                    bias_selection_only=c.bias_selection_only)
         return s
+
+    def update_bias(self, sel_count: torch.Tensor, n_tokens: int, gamma: float, stream=None):
+        """Batch-level update of the selection bias in place (logit_bias must exist)."""
+        c = self.cfg
+        B.moe_update_bias(sel_count, c.n_experts, n_tokens, c.top_k, gamma,
+                          self.w["logit_bias"], stream=stream)
 
     def dispatch(self, x: torch.Tensor, topk_idx: torch.Tensor, capacity: Optional[int] = None,
                  with_copy: bool = True, stream=None) -> dict:

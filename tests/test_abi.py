@@ -49,8 +49,8 @@ def test_capacity_rejects_bad_arguments():
 
 def _route_status(**kw):
     a = dict(stream=None, x=None, xt=B.MOE_BF16, n=4, d=64, wr=None, bias=None, e=8, k=2,
-             renorm=1, li=None, lo=None, idx=None, w=None, sel=None, pm=None, aux=None,
-             ws=None, wsb=0)
+             renorm=1, sel_only=0, li=None, lo=None, idx=None, w=None, sel=None, pm=None,
+             aux=None, ws=None, wsb=0)
     a.update(kw)
     return B.lib().moe_route(*a.values())
 
@@ -111,3 +111,14 @@ def test_forward_validation_and_workspace():
     with pytest.raises(B.MoEError):
         B._check("moe_forward", st)
     assert L.moe_forward(None, C.byref(bad), C.byref(w), None, None, None, None, 0) == B.MOE_ERR_UNSUPPORTED
+
+
+def test_update_bias_validation():
+    L = B.lib()
+    fake = 4096  # never dereferenced: validation fails first
+    assert L.moe_update_bias(None, fake, 0, 10, 2, 0.1, fake) == B.MOE_ERR_INVALID_ARG
+    assert L.moe_update_bias(None, fake, 600, 10, 2, 0.1, fake) == B.MOE_ERR_UNSUPPORTED
+    assert L.moe_update_bias(None, fake, 8, -1, 2, 0.1, fake) == B.MOE_ERR_INVALID_ARG
+    assert L.moe_update_bias(None, fake, 8, 10, 0, 0.1, fake) == B.MOE_ERR_INVALID_ARG
+    assert L.moe_update_bias(None, fake, 8, 10, 2, float("nan"), fake) == B.MOE_ERR_INVALID_ARG
+    assert L.moe_update_bias(None, None, 8, 10, 2, 0.1, fake) == B.MOE_ERR_INVALID_ARG

@@ -29,7 +29,7 @@ def _up(a: np.ndarray, dtype: str):
     return torch.from_numpy(np.ascontiguousarray(a)).to(DEV)
 
 
-def _route(x, wr, lb, E, k, renorm=True, logits_in=None, n=None):
+def _route(x, wr, lb, E, k, renorm=True, logits_in=None, n=None, sel_only=False):
     n = n if n is not None else (x if x is not None else logits_in).shape[0]
     i32, f32 = torch.int32, torch.float32
     out = dict(logits=torch.empty((n, E), dtype=f32, device=DEV) if logits_in is None else None,
@@ -40,16 +40,16 @@ def _route(x, wr, lb, E, k, renorm=True, logits_in=None, n=None):
                aux=torch.empty(1, dtype=f32, device=DEV))
     ws = workspace(B.moe_route_workspace_size(n, x.shape[1] if x is not None else 0, E), DEV)
     B.moe_route(x, wr, lb, E, k, renorm, logits_in, out["logits"], out["idx"], out["w"],
-                out["sel"], out["pm"], out["aux"], ws, n_tokens=n)
+                out["sel"], out["pm"], out["aux"], ws, n_tokens=n, bias_selection_only=sel_only)
     torch.cuda.synchronize()
     return {kk: (None if v is None else v.cpu().numpy()) for kk, v in out.items()}
 
 
-def _check_gate(logits32, bias, k, E, got, renorm=True):
+def _check_gate(logits32, bias, k, E, got, renorm=True, sel_only=False):
     z = O.biased_scores(logits32, bias)
     idx = O.select_topk(z, k)
     assert np.array_equal(got["idx"], idx), "top-k indices differ"
-    p = O.softmax64(z)
+    p = O.softmax64(np.asarray(logits32, np.float32) if sel_only else z)
     w = O.gate_weights(p, idx, renorm)
     np.testing.assert_allclose(got["w"], w, rtol=2e-6, atol=1e-7)
     st = O.balance_stats(p, idx, E)
@@ -144,6 +144,52 @@ def test_aux_is_one_under_uniform_routing(E, k):
     tol = 0.0 if E in (8, 64) else 1e-6
     assert abs(float(got["aux"][0]) - 1.0) <= tol
     assert np.abs(got["w"].sum(1) - 1).max() <= k * 2.0 ** -23
+
+
+# ------------------------------------------------------------------ bias for selection only
+@pytest.mark.parametrize("name", ["deepseek", "switch"])
+def test_router_selection_only_bias_full_size(name):
+    cfg = CONFIGS[name]
+    print_case("router-selection-only", name, cfg.n_tokens)
+    h = synth.HostInputs(cfg)
+    lb = torch.from_numpy(h.logit_bias).to(DEV)
+    got = _route(_up(h.x, cfg.dtype), torch.from_numpy(h.w_router).to(DEV), lb, cfg.n_experts,
+                 cfg.top_k, cfg.renormalize, sel_only=True)
+    _check_gate(got["logits"], h.logit_bias, cfg.top_k, cfg.n_experts, got, cfg.renormalize,
+                sel_only=True)
+
+
+@pytest.mark.parametrize("E,k", [(160, 6), (8, 2), (64, 1), (33, 5)])
+def test_gate_selection_only_on_given_logits(E, k):
+    print_case("gate-selection-only", E, k)
+    rng = np.random.default_rng(E + 7 * k)
+    n = 257
+    L = (rng.integers(-3, 4, size=(n, E)) * 0.5).astype(np.float32)  # ties
+    b = (rng.integers(-4, 5, size=E) * 0.25).astype(np.float32)
+    got = _route(None, None, torch.from_numpy(b).to(DEV), E, k,
+                 logits_in=torch.from_numpy(L).to(DEV), sel_only=True)
+    _check_gate(L, b, k, E, got, sel_only=True)
+
+
+@pytest.mark.parametrize("E,n,k", [(160, 4096, 6), (8, 4096, 2), (7, 13, 3), (512, 100, 16)])
+def test_update_bias_matches_oracle(E, n, k):
+    print_case("update-bias", E, n, k)
+    rng = np.random.default_rng(E + n)
+    sel = rng.integers(0, 2 * n * k // E + 2, size=E).astype(np.int32)
+    sel[: min(3, E)] = (n * k) // E if (n * k) % E == 0 else sel[: min(3, E)]  # some exact means
+    b = (rng.standard_normal(E) * 0.1).astype(np.float32)
+    bd = torch.from_numpy(b).to(DEV)
+    B.moe_update_bias(torch.from_numpy(sel).to(DEV), E, n, k, 0.001, bd)
+    torch.cuda.synchronize()
+    want = O.update_bias(b, sel, n, k, 0.001)
+    assert np.array_equal(bd.cpu().numpy().view(np.uint32), want.view(np.uint32))
+
+
+def test_forward_parity_selection_only_bias():
+    cfg = CONFIGS["deepseek"].with_tokens(128).scaled(bias_selection_only=True)
+    print_case("forward-selection-only", cfg.name, cfg.n_tokens)
+    err, r, _ = _forward_and_oracle(cfg)
+    assert err <= TOL[cfg.dtype]
 
 
 # ------------------------------------------------------------------ dispatch
@@ -303,6 +349,8 @@ def test_combine_parity(dtype, shared, k):
 
 # ------------------------------------------------------------------ whole layer
 def _forward_and_oracle(cfg, tokens=None, check_all_logits=True):
+    """Forward on the GPU; the oracle conditioned on its logits; integer results
+    compared bit for bit, weights and statistics within float32 tolerance."""
     inp = synth.DeviceInputs(cfg, DEV)
     layer = MoELayer.from_inputs(inp)
     n = cfg.n_tokens
@@ -320,7 +368,8 @@ def _forward_and_oracle(cfg, tokens=None, check_all_logits=True):
     r = O.forward(xb, cfg.dtype, None, cfg.top_k, DeviceExperts(layer.w), cfg.n_experts, cfg.act,
                   logit_bias=lb, alpha=cfg.alpha, renormalize=cfg.renormalize,
                   shared=DeviceExperts(layer.w, shared=True) if cfg.n_shared else None,
-                  n_shared=cfg.n_shared, logits=Lg, tokens=tokens)
+                  n_shared=cfg.n_shared, logits=Lg, tokens=tokens,
+                  bias_selection_only=cfg.bias_selection_only)
     # integer results: bit-exact
     assert np.array_equal(st["topk_idx"].cpu().numpy(), r.topk_idx)
     assert np.array_equal(st["sel_count"].cpu().numpy(), r.stats.sel_count)
