@@ -181,6 +181,48 @@ def balance_stats(p64: np.ndarray, idx: np.ndarray, n_experts: int) -> BalanceSt
     return BalanceStats(sel, freq, prob_mean, aux)
 
 
+@dataclass
+class RouterMonitor:
+    z_loss: float  # 0.001 * mean_t logsumexp(logits[t, :])^2
+    entropy: float  # mean_t of -sum_j w_j ln w_j over the token's renormalised top-k
+    load_sumsq: float  # sum_e (sel_count[e] / N)^2
+    load_cv: float  # std_e(sel_count) / mean_e(sel_count), population std
+    drop_rate: float  # dropped assignments / (N*k)
+
+
+def router_monitor(logits32: np.ndarray, p64: np.ndarray, idx: np.ndarray, sel_count: np.ndarray,
+                   n_dropped: int) -> RouterMonitor:
+    """Monitoring signals of the router named on the pages, each taken as defined there:
+      z_loss      [MoE-overview] §3.3: 0.001 * mean(logsumexp(router_logits)^2), on the
+                  router's own (unbiased) logits;
+      entropy     [GPT4-2pct] §2.3: per token -sum p~ log p~ over the softmax of its
+                  top-k logits, i.e. the k selected probabilities renormalised, averaged
+                  over tokens (natural log);
+      load_sumsq  [MoE-2pct] §2.2: sum over experts of (selections of e / N)^2, the
+                  page's balance term without its coefficient;
+      load_cv     [GPT4-2pct] §4.1 (step 3): standard deviation over mean of the
+                  per-expert selection counts;
+      drop_rate   [MoE-overview] §4.3 (pitfall 2): share of the N*k assignments cut by
+                  the capacity.
+    For N = 0 every signal is 0."""
+    n, k = idx.shape
+    e = sel_count.shape[0]
+    if n == 0:
+        return RouterMonitor(0.0, 0.0, 0.0, 0.0, 0.0)
+    l64 = np.asarray(logits32, dtype=F32).astype(F64)
+    m = l64.max(axis=1, keepdims=True)
+    lse = (m + np.log(np.exp(l64 - m).sum(axis=1, keepdims=True)))[:, 0]
+    q = p64[np.arange(n)[:, None], idx]
+    q = q / q.sum(axis=1, keepdims=True)
+    ent = -(q * np.log(q)).sum(axis=1)
+    cnt = np.asarray(sel_count, dtype=F64)
+    mean = cnt.sum() / e
+    cv = float(np.sqrt(((cnt - mean) ** 2).sum() / e) / mean) if mean > 0 else 0.0
+    return RouterMonitor(z_loss=float(0.001 * np.mean(lse * lse)), entropy=float(ent.mean()),
+                         load_sumsq=float(((cnt / n) ** 2).sum()), load_cv=cv,
+                         drop_rate=float(n_dropped) / float(n * k))
+
+
 # ----------------------------------------------------------------------------------
 # Capacity and dispatch.  [MoE-2pct] §3.1 (capacity formula), §4.2 (MoEFeedForward
 # keeps the first expert_capacity tokens an expert receives), §5.3 (worked example);
@@ -307,6 +349,7 @@ class ForwardResult:
     plan: DispatchPlan
     tokens: np.ndarray  # int64, tokens whose outputs are in y
     y: np.ndarray  # float64 [len(tokens), d]
+    monitor: Optional[RouterMonitor] = None
     extra: dict = field(default_factory=dict)
 
 
@@ -366,4 +409,5 @@ def forward(
         slots = np.array([j for _, j in sel], dtype=np.int64)
         ye = expert_ffn(x64[toks[rows]], expert(e), act)
         y[rows] += w[toks[rows], slots][:, None] * ye
-    return ForwardResult(logits, z, p, idx, w, st, cap, plan, toks, y)
+    mon = router_monitor(logits, p, idx, st.sel_count, plan.n_dropped)
+    return ForwardResult(logits, z, p, idx, w, st, cap, plan, toks, y, mon)

@@ -474,3 +474,76 @@ def test_bias_update_balances_a_skewed_router():
         b = O.update_bias(b, st.sel_count, n, k, gamma=0.05)
     assert loads[-1] < 0.6 * loads[0]
     assert loads[-1] <= 1.5 * n * k / E
+
+
+# ------------------------------------------------------------------ router monitoring signals
+def test_monitor_equal_logits_closed_forms():
+    # equal logits: logsumexp = ln E, the k selections (experts 0..k-1, lowest index on
+    # ties) carry equal renormalised weights, so the entropy is ln k; the counts are
+    # N on k experts and 0 elsewhere
+    n, E, k = 40, 8, 2
+    L = np.zeros((n, E), np.float32)
+    z = O.biased_scores(L, None)
+    idx = O.select_topk(z, k)
+    p = O.softmax64(z)
+    st = O.balance_stats(p, idx, E)
+    m = O.router_monitor(L, p, idx, st.sel_count, 0)
+    assert m.z_loss == pytest.approx(0.001 * math.log(E) ** 2, rel=1e-14)
+    assert m.entropy == pytest.approx(math.log(k), rel=1e-14)
+    assert m.load_sumsq == pytest.approx(k * 1.0, rel=1e-14)  # k experts at (N/N)^2
+    # counts [N, N, 0 x 6]: mean N/4, std = N/4 * sqrt(3) -> CV = sqrt(3)
+    assert m.load_cv == pytest.approx(math.sqrt(3.0), rel=1e-14)
+    assert m.drop_rate == 0.0
+
+
+def test_monitor_balanced_page_exercise():
+    # [Why-MoE] §6: 1000 tokens, top-2, 8 experts, 250 selections each -> CV = 0 and
+    # sum_e (250/1000)^2 = 8/16 = k^2/E
+    g = GOLDEN["balanced_exercise"]
+    n, E, k = g["n_tokens"], g["n_experts"], g["k"]
+    t = np.arange(n)
+    idx = np.stack([t % E, (t + E // 2) % E], axis=1).astype(np.int64)
+    sel = np.bincount(idx.ravel(), minlength=E)
+    assert (sel == g["per_expert"]).all()
+    p = np.full((n, E), 1.0 / E)
+    m = O.router_monitor(np.zeros((n, E), np.float32), p, idx, sel, 0)
+    assert m.load_cv == 0.0
+    assert m.load_sumsq == pytest.approx(k * k / E, rel=1e-15)
+    assert m.entropy == pytest.approx(math.log(2.0), rel=1e-14)
+
+
+def test_monitor_concentration_and_drops():
+    # every selection on one expert: CV = sqrt(E - 1); k = 1 -> entropy 0; a capacity of
+    # 0 drops every assignment
+    n, E = 16, 5
+    L = np.tile(np.array([[4.0, 0.0, 0.0, 0.0, 0.0]], np.float32), (n, 1))
+    z = O.biased_scores(L, None)
+    idx = O.select_topk(z, 1)
+    p = O.softmax64(z)
+    st = O.balance_stats(p, idx, E)
+    plan = O.plan_dispatch(idx, E, 0)
+    m = O.router_monitor(L, p, idx, st.sel_count, plan.n_dropped)
+    assert m.load_cv == pytest.approx(math.sqrt(E - 1), rel=1e-14)
+    assert m.entropy == 0.0
+    assert m.drop_rate == 1.0
+    assert m.load_sumsq == 1.0
+    lse = 4.0 + math.log(1.0 + 4.0 * math.exp(-4.0))
+    assert m.z_loss == pytest.approx(0.001 * lse * lse, rel=1e-14)
+
+
+def test_monitor_two_slot_entropy_closed_form():
+    # top-2 of logits [a, b, very low]: renormalised weights are sigmoid(a - b) and its
+    # complement, entropy = -q ln q - (1 - q) ln (1 - q)
+    L = np.array([[1.5, 0.25, -30.0]], np.float32)
+    z = O.biased_scores(L, None)
+    idx = O.select_topk(z, 2)
+    p = O.softmax64(z)
+    m = O.router_monitor(L, p, idx, np.bincount(idx.ravel(), minlength=3), 0)
+    q = 1.0 / (1.0 + math.exp(-(1.5 - 0.25)))
+    assert m.entropy == pytest.approx(-q * math.log(q) - (1 - q) * math.log(1 - q), rel=1e-12)
+
+
+def test_monitor_empty_batch():
+    m = O.router_monitor(np.zeros((0, 4), np.float32), np.zeros((0, 4)), np.zeros((0, 2), np.int64),
+                         np.zeros(4, np.int64), 0)
+    assert (m.z_loss, m.entropy, m.load_sumsq, m.load_cv, m.drop_rate) == (0, 0, 0, 0, 0)
