@@ -86,6 +86,15 @@ int64_t moe_capacity(int64_t n_tokens, int32_t n_experts, int32_t k, double alph
  *   aux[0]       = E * sum_e (sel_count[e] / (N*k)) * prob_mean[e]
  *                  ([DeepSeek-V2] §2.2 load_balance_loss; equals 1 when routing is
  *                  uniform).  For N == 0 the statistics are written as zeros.
+ *   monitor[0..3] (float32, optional): router health signals, accumulated in double
+ *     [0] z-loss  = 0.001 * (1/N) sum_t (log sum_e exp logits[t][e])^2 on the unbiased
+ *                   logits ([MoE-overview] §3.3)
+ *     [1] entropy = (1/N) sum_t -sum_j q[t][j] ln q[t][j], q[t][:] = the token's k
+ *                   selected probabilities renormalised to sum 1 ([GPT4-2pct] §2.3)
+ *     [2] sum_e (sel_count[e] / N)^2  ([MoE-2pct] §2.2 balance term, no coefficient)
+ *     [3] coefficient of variation of sel_count: population standard deviation over
+ *         mean ([GPT4-2pct] §4.1)
+ *     All four are 0 for N == 0.
  * Arguments
  *   x          [N][d], x_dtype (MOE_F32 or MOE_BF16); d % 4 == 0 for MOE_F32 (x 8-byte
  *              aligned), d % 8 == 0 for MOE_BF16 (x 16-byte aligned).  May be NULL
@@ -97,7 +106,8 @@ int64_t moe_capacity(int64_t n_tokens, int32_t n_experts, int32_t k, double alph
  *              logits are used (lets a caller condition the gate on known logits).
  *   logits_out [N][E] float32 or NULL: the float32 logits (before the bias).
  *   topk_idx   [N][k] int32, topk_w [N][k] float32 (required).
- *   sel_count  [E] int32, prob_mean [E] float32, aux [1] float32 (each may be NULL).
+ *   sel_count  [E] int32, prob_mean [E] float32, aux [1] float32, monitor [4] float32
+ *              (each may be NULL).
  *   ws         device workspace of at least moe_route_workspace_size(N, d, E) bytes,
  *              256-byte aligned (may be NULL if that size is 0).
  * Precision: logits are float32 dot products.  For MOE_BF16 x the float32 w_router is
@@ -113,7 +123,7 @@ moe_status moe_route(void* stream, const void* x, moe_dtype x_dtype, int64_t n_t
                      int32_t bias_selection_only,
                      const float* logits_in, float* logits_out, int32_t* topk_idx,
                      float* topk_w, int32_t* sel_count, float* prob_mean, float* aux,
-                     void* ws, size_t ws_bytes);
+                     float* monitor, void* ws, size_t ws_bytes);
 
 /*
  * moe_update_bias -- batch-level update of the selection bias ([Why-MoE] §2.4: an
@@ -237,6 +247,9 @@ typedef struct {
   int32_t* n_dropped;      /* [1] */
   int32_t* expert_offsets; /* [E+1] */
   int32_t* slot_row;       /* [N][k] */
+  /* [5]: moe_route's monitor[0..3], then [4] = n_dropped / (N k), the share of
+   * assignments cut by the capacity ([MoE-overview] §4.3); 0 for N == 0 */
+  float* monitor;
   /* Timing markers (hipEvent_t handles owned by the caller, or NULL): stage_events[i]
    * is recorded on the stream at boundary i -- 0 before routing, 1 after routing and
    * its statistics, 2 after dispatch, 3 after the routed first expert layer, 4 after

@@ -43,7 +43,7 @@ class MoEWeightsC(C.Structure):
 
 MOE_N_STAGE_EVENTS = 7
 STAT_FIELDS = ("logits", "topk_idx", "topk_w", "sel_count", "prob_mean", "aux", "kept_count",
-               "n_dropped", "expert_offsets", "slot_row")
+               "n_dropped", "expert_offsets", "slot_row", "monitor")
 
 
 class MoEStatsC(C.Structure):
@@ -58,7 +58,7 @@ _SIGS = {
     "moe_capacity": (_I64, [_I64, _I32, _I32, _DBL]),
     "moe_route_workspace_size": (_SZ, [_I64, _I64, _I32]),
     "moe_route": (C.c_int, [_VP, _VP, C.c_int, _I64, _I64, _VP, _VP, _I32, _I32, _I32, _I32, _VP,
-                            _VP, _VP, _VP, _VP, _VP, _VP, _VP, _SZ]),
+                            _VP, _VP, _VP, _VP, _VP, _VP, _VP, _VP, _SZ]),
     "moe_update_bias": (C.c_int, [_VP, _VP, _I32, _I64, _I32, C.c_float, _VP]),
     "moe_dispatch_workspace_size": (_SZ, [_I64, _I32, _I32]),
     "moe_dispatch": (C.c_int, [_VP, _VP, _I64, _I32, _I32, _I64, _VP, C.c_int, _I64, _VP, _VP,
@@ -142,7 +142,8 @@ def moe_route_workspace_size(n_tokens: int, d_model: int, n_experts: int) -> int
 
 def moe_route(x, w_router, logit_bias, n_experts: int, k: int, renormalize: bool,
               logits_in, logits_out, topk_idx, topk_w, sel_count, prob_mean, aux, ws,
-              n_tokens: Optional[int] = None, stream=None, bias_selection_only: bool = False):
+              n_tokens: Optional[int] = None, stream=None, bias_selection_only: bool = False,
+              monitor=None):
     if n_tokens is None:
         n_tokens = (x if x is not None else logits_in).shape[0]
     d = x.shape[1] if x is not None else 0
@@ -151,7 +152,8 @@ def moe_route(x, w_router, logit_bias, n_experts: int, k: int, renormalize: bool
                          _ptr(logit_bias), n_experts, k, 1 if renormalize else 0,
                          1 if bias_selection_only else 0, _ptr(logits_in), _ptr(logits_out),
                          _ptr(topk_idx), _ptr(topk_w),
-                         _ptr(sel_count), _ptr(prob_mean), _ptr(aux), _ptr(ws), _ws_bytes(ws))
+                         _ptr(sel_count), _ptr(prob_mean), _ptr(aux), _ptr(monitor), _ptr(ws),
+                         _ws_bytes(ws))
     _check("moe_route", st)
 
 

@@ -93,7 +93,9 @@ moe_status check_route_args(const void* x, moe_dtype xt, int64_t n, int64_t d,
 struct RouteWs {
   float* pp;
   int32_t* pc;
+  float* pmon;
   double* term;
+  int64_t* cnt;
   uint16_t* wp;
   float* part;
 };
@@ -103,7 +105,9 @@ RouteWs route_layout(Carve& c, int64_t n, int64_t d, int32_t e) {
   const int64_t b = std::max(moe::route_blocks(n), moe::gate_blocks(n));
   r.pp = c.take<float>(b * e);
   r.pc = c.take<int32_t>(b * e);
+  r.pmon = c.take<float>(2 * b);
   r.term = c.take<double>(e);
+  r.cnt = c.take<int64_t>(e);
   if (d >= 8 && d % 8 == 0) {
     const moe::RoutePlan pl = moe::route_plan(n, d, e);
     r.wp = c.take<uint16_t>(3 * static_cast<int64_t>(pl.e_pad) * d);
@@ -134,35 +138,39 @@ size_t dispatch_ws(int64_t n, int32_t k, int32_t e) {
 moe_status run_route(hipStream_t st, const void* x, moe_dtype xt, int64_t n, int64_t d,
                      const float* wr, const float* bias, int32_t e, int32_t k, int32_t flags,
                      const float* logits_in, float* logits_out, int32_t* idx, float* w,
-                     int32_t* sel, float* pm, float* aux, void* ws) {
+                     int32_t* sel, float* pm, float* aux, float* monitor, void* ws) {
   Carve c(ws);
   const RouteWs r = route_layout(c, n, d, e);
+  if (monitor) flags |= moe::kGateMonitor;
+  auto finalize = [&](int64_t rows) {
+    return hip_check(moe::launch_route_finalize(st, r.pp, r.pc, r.pmon, rows, n, e, k, sel, pm,
+                                                aux, monitor, r.term, r.cnt),
+                     "router statistics launch");
+  };
   int64_t rows;
   if (logits_in) {
     // the gate alone, over the caller's logits
     rows = moe::gate_blocks(n);
     MOE_TRY(hip_check(moe::launch_route_gate(st, logits_in, 1, n, e, bias, k, flags, logits_out,
-                                             idx, w, r.pp, r.pc),
+                                             idx, w, r.pp, r.pc, r.pmon),
                       "router gate launch"));
   } else if (xt == MOE_BF16) {
     const moe::RoutePlan pl = moe::route_plan(n, d, e);
     rows = moe::gate_blocks(n);
-    if (n == 0) return hip_check(moe::launch_route_finalize(st, r.pp, r.pc, 0, 0, e, k, sel, pm, aux, r.term),
-                                 "router statistics launch");
+    if (n == 0) return finalize(0);
     MOE_TRY(hip_check(moe::launch_route_split(st, wr, pl, r.wp), "router weight split launch"));
     MOE_TRY(hip_check(moe::launch_route_logits(st, static_cast<const uint16_t*>(x), pl, r.wp, r.part),
                       "router logits launch"));
     MOE_TRY(hip_check(moe::launch_route_gate(st, r.part, pl.ks, n, e, bias, k, flags, logits_out,
-                                             idx, w, r.pp, r.pc),
+                                             idx, w, r.pp, r.pc, r.pmon),
                       "router gate launch"));
   } else {
     rows = moe::route_blocks(n);
     MOE_TRY(hip_check(moe::launch_route(st, static_cast<const float*>(x), n, d, wr, bias, e, k,
-                                        flags, logits_out, idx, w, r.pp, r.pc),
+                                        flags, logits_out, idx, w, r.pp, r.pc, r.pmon),
                       "router kernel launch"));
   }
-  return hip_check(moe::launch_route_finalize(st, r.pp, r.pc, rows, n, e, k, sel, pm, aux, r.term),
-                   "router statistics launch");
+  return finalize(rows);
 }
 
 moe_status run_dispatch(hipStream_t st, const int32_t* idx, int64_t n, int32_t k, int32_t e,
@@ -351,7 +359,7 @@ moe_status moe_route(void* stream, const void* x, moe_dtype x_dtype, int64_t n_t
                      int32_t n_experts, int32_t k, int32_t renormalize,
                      int32_t bias_selection_only, const float* logits_in, float* logits_out, int32_t* topk_idx,
                      float* topk_w, int32_t* sel_count, float* prob_mean, float* aux,
-                     void* ws, size_t ws_bytes) {
+                     float* monitor, void* ws, size_t ws_bytes) {
   MOE_TRY(check_route_args(x, x_dtype, n_tokens, d_model, w_router, n_experts, k, logits_in,
                            topk_idx, topk_w));
   const size_t need = route_ws(n_tokens, d_model, n_experts);
@@ -363,7 +371,7 @@ moe_status moe_route(void* stream, const void* x, moe_dtype x_dtype, int64_t n_t
   return run_route(static_cast<hipStream_t>(stream), x, x_dtype, n_tokens, d_model, w_router,
                    logit_bias, n_experts, k, gate_flags(renormalize, bias_selection_only),
                    logits_in, logits_out,
-                   topk_idx, topk_w, sel_count, prob_mean, aux, ws);
+                   topk_idx, topk_w, sel_count, prob_mean, aux, monitor, ws);
 }
 
 moe_status moe_update_bias(void* stream, const int32_t* sel_count, int32_t n_experts,
@@ -503,6 +511,7 @@ moe_status moe_forward(void* stream, const moe_config* cfg, const moe_weights* w
   float* tw = o.topk_w ? o.topk_w : L.w;
   int32_t* offsets = o.expert_offsets ? o.expert_offsets : L.offsets;
   int32_t* slot_row = o.slot_row ? o.slot_row : L.slot_row;
+  int32_t* dropped = o.n_dropped ? o.n_dropped : L.dropped;
 
   auto mark = [&](int i) -> moe_status {
     if (!o.stage_events[i]) return MOE_OK;
@@ -514,13 +523,15 @@ moe_status moe_forward(void* stream, const moe_config* cfg, const moe_weights* w
   MOE_TRY(run_route(st, x, c.dtype, n, c.d_model, w->w_router, w->logit_bias, e, k,
                     gate_flags(c.renormalize, c.bias_selection_only), nullptr, o.logits, idx,
                     tw, o.sel_count,
-                    o.prob_mean, o.aux, L.route_ws));
+                    o.prob_mean, o.aux, o.monitor, L.route_ws));
   MOE_TRY(mark(1));
   // a4-a5: capacity and permutation
   const int64_t cap = capacity_of(n, e, k, c.capacity_factor);
   MOE_TRY(run_dispatch(st, idx, n, k, e, cap, x, c.d_model * static_cast<int64_t>(es), offsets,
-                       L.row_token, slot_row, o.kept_count, o.n_dropped, L.x_perm,
+                       L.row_token, slot_row, o.kept_count, dropped, L.x_perm,
                        L.dispatch_ws));
+  if (o.monitor)
+    MOE_TRY(hip_check(moe::launch_drop_rate(st, dropped, n * k, o.monitor + 4), "drop rate launch"));
   MOE_TRY(mark(2));
   // a8 (forked): shared experts, all tokens, on the side stream, concurrent with the
   // routed experts (forked after the latency-bound router and dispatch, whose few

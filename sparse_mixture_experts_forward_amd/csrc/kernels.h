@@ -13,6 +13,7 @@ namespace moe {
 // the unbiased logits).
 constexpr int kGateRenorm = 1;
 constexpr int kGateSelectionOnly = 2;
+constexpr int kGateMonitor = 4;  // also the per-workgroup monitoring partials (part_mon)
 constexpr int kRouteTokens = 16;  // tokens per router workgroup
 
 inline int64_t route_blocks(int64_t n_tokens) {
@@ -23,7 +24,7 @@ inline int64_t route_blocks(int64_t n_tokens) {
 hipError_t launch_route(hipStream_t st, const float* x, int64_t n, int64_t d,
                         const float* w_router, const float* logit_bias, int e, int k,
                         int renorm, float* logits_out, int32_t* topk_idx, float* topk_w,
-                        float* part_prob, int32_t* part_cnt);
+                        float* part_prob, int32_t* part_cnt, float* part_mon);
 
 // bf16 router: exact three-part bf16 split of W_router, the sliced logits product and
 // the gate over the slices' partial logits.
@@ -54,17 +55,22 @@ hipError_t launch_route_logits(hipStream_t st, const uint16_t* x, const RoutePla
 hipError_t launch_route_gate(hipStream_t st, const float* part, int ks, int64_t n, int e,
                              const float* bias, int k, int renorm, float* logits_out,
                              int32_t* topk_idx, float* topk_w, float* part_prob,
-                             int32_t* part_cnt);
+                             int32_t* part_cnt, float* part_mon);
 
 // Batch-level bias update: b[e] -= gamma if sel_count[e]*E > N*k, += gamma if below.
 hipError_t launch_update_bias(hipStream_t st, const int32_t* sel_count, int e, int64_t n, int k,
                               float gamma, float* logit_bias);
 
 // Statistics over `rows` partial rows: per-expert workgroups (sel_count, prob_mean and
-// the aux terms, `term` is E doubles of scratch), then the aux sum.
+// the aux terms; `term` E doubles and `cnt` E counts of scratch), then aux and, if
+// `monitor` is given, z-loss, mean top-k entropy, sum of squared load shares and load
+// CV (monitor[0..3]; part_mon holds two floats per row).
 hipError_t launch_route_finalize(hipStream_t st, const float* part_prob,
-                                 const int32_t* part_cnt, int64_t rows, int64_t n, int e, int k,
-                                 int32_t* sel_count, float* prob_mean, float* aux, double* term);
+                                 const int32_t* part_cnt, const float* part_mon, int64_t rows,
+                                 int64_t n, int e, int k, int32_t* sel_count, float* prob_mean,
+                                 float* aux, float* monitor, double* term, int64_t* cnt);
+// out[0] = n_dropped / (N k)
+hipError_t launch_drop_rate(hipStream_t st, const int32_t* n_dropped, int64_t nk, float* out);
 
 // ---------------------------------------------------------------- dispatch
 struct DispatchGrid {

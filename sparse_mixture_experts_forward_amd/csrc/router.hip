@@ -45,13 +45,15 @@ __device__ __forceinline__ void load_x4(const uint16_t* p, float v[4]) {
 // sel_only (the bias steers selection only, [Why-MoE] §2.4) the softmax of l.
 // Writes topk_idx / topk_w of token t and adds p and the selection counts to the lane's
 // statistics accumulators.
+// With monitor, also adds the token's logsumexp(l)^2 to lse2 and the entropy of its
+// renormalised top-k weights to ent (wave-uniform values).
 template <int VPL>
 __device__ __forceinline__ void gate_token(const float (&l)[VPL], int lane, int E,
                                            const float* __restrict__ bias, int k, int renorm,
-                                           int sel_only, int64_t t,
+                                           int sel_only, int monitor, int64_t t,
                                            int32_t* __restrict__ topk_idx,
                                            float* __restrict__ topk_w, float (&pacc)[VPL],
-                                           int32_t (&cacc)[VPL]) {
+                                           int32_t (&cacc)[VPL], float& lse2, float& ent) {
   float z[VPL], ex[VPL];
   float qmax = -INFINITY;
 #pragma unroll
@@ -113,6 +115,26 @@ __device__ __forceinline__ void gate_token(const float (&l)[VPL], int lane, int 
     topk_idx[t * k + lane] = my_idx;
     topk_w[t * k + lane] = renorm ? my_ex / sel_ex_sum : my_ex / s;
   }
+  if (monitor) {
+    float lse;
+    if (sel_only || bias == nullptr) {
+      lse = m + logf(s);  // the softmax above was already over l
+    } else {
+      float lm = -INFINITY;
+#pragma unroll
+      for (int i = 0; i < VPL; ++i)
+        if (lane + kWave * i < E) lm = fmaxf(lm, l[i]);
+      lm = wave_max(lm);
+      float ls = 0.f;
+#pragma unroll
+      for (int i = 0; i < VPL; ++i)
+        if (lane + kWave * i < E) ls += expf(l[i] - lm);
+      lse = lm + logf(wave_sum(ls));
+    }
+    lse2 += lse * lse;
+    const float q = (lane < k) ? my_ex / sel_ex_sum : 0.f;
+    ent += wave_sum(q > 0.f ? -q * logf(q) : 0.f);
+  }
 }
 
 // ET: upper bound on the number of 16-expert column tiles (E_pad = 16 * n_et <= 16 * ET).
@@ -122,13 +144,16 @@ __global__ __launch_bounds__(kThreads) void route_kernel(
     const float* __restrict__ bias, int E, int k, int flags,
     const float* __restrict__ logits_in, float* __restrict__ logits_out,
     int32_t* __restrict__ topk_idx, float* __restrict__ topk_w,
-    float* __restrict__ part_prob, int32_t* __restrict__ part_cnt) {
+    float* __restrict__ part_prob, int32_t* __restrict__ part_cnt, float* __restrict__ part_mon) {
   constexpr int EP = ET * 16;             // padded expert count (LDS row stride)
   const int renorm = flags & kGateRenorm, sel_only = (flags & kGateSelectionOnly) ? 1 : 0;
+  const int monitor = (flags & kGateMonitor) ? 1 : 0;
+  float lse2 = 0.f, ent = 0.f;
   constexpr int VPL = (EP + kWave - 1) / kWave;  // experts per lane in the gate
   __shared__ float red[kRouteTokens * EP];
   __shared__ float sprob[4 * EP];
   __shared__ int32_t scnt[4 * EP];
+  __shared__ float smon[8];
 
   const int lane = lane_id();
   const int wave = threadIdx.x / kWave;
@@ -206,7 +231,8 @@ __global__ __launch_bounds__(kThreads) void route_kernel(
       const int e = lane + kWave * i;
       l[i] = e < E ? red[tt * EP + e] : 0.f;
     }
-    gate_token<VPL>(l, lane, E, bias, k, renorm, sel_only, t0 + tt, topk_idx, topk_w, pacc, cacc);
+    gate_token<VPL>(l, lane, E, bias, k, renorm, sel_only, monitor, t0 + tt, topk_idx, topk_w, pacc,
+                    cacc, lse2, ent);
   }
 
   // ---------------- per-workgroup statistics partials, waves added in order
@@ -218,12 +244,20 @@ __global__ __launch_bounds__(kThreads) void route_kernel(
       scnt[wave * EP + e] = cacc[i];
     }
   }
+  if (monitor && lane == 0) {
+    smon[wave] = lse2;
+    smon[4 + wave] = ent;
+  }
   __syncthreads();
   for (int e = threadIdx.x; e < E; e += kThreads) {
     part_prob[static_cast<int64_t>(blockIdx.x) * E + e] =
         ((sprob[e] + sprob[EP + e]) + sprob[2 * EP + e]) + sprob[3 * EP + e];
     part_cnt[static_cast<int64_t>(blockIdx.x) * E + e] =
         scnt[e] + scnt[EP + e] + scnt[2 * EP + e] + scnt[3 * EP + e];
+  }
+  if (monitor && threadIdx.x == 0) {
+    part_mon[2 * blockIdx.x] = ((smon[0] + smon[1]) + smon[2]) + smon[3];
+    part_mon[2 * blockIdx.x + 1] = ((smon[4] + smon[5]) + smon[6]) + smon[7];
   }
 }
 
@@ -366,11 +400,15 @@ template <int VPL>
 __global__ __launch_bounds__(kThreads) void route_gate_kernel(
     const float* __restrict__ part, int ks, int64_t n, int E, const float* __restrict__ bias,
     int k, int flags, int tpw, float* __restrict__ logits_out, int32_t* __restrict__ topk_idx,
-    float* __restrict__ topk_w, float* __restrict__ part_prob, int32_t* __restrict__ part_cnt) {
+    float* __restrict__ topk_w, float* __restrict__ part_prob, int32_t* __restrict__ part_cnt,
+    float* __restrict__ part_mon) {
   constexpr int EP = VPL * kWave;
   const int renorm = flags & kGateRenorm, sel_only = (flags & kGateSelectionOnly) ? 1 : 0;
+  const int monitor = (flags & kGateMonitor) ? 1 : 0;
+  float lse2 = 0.f, ent = 0.f;
   __shared__ float sprob[4 * EP];
   __shared__ int32_t scnt[4 * EP];
+  __shared__ float smon[8];
   const int lane = lane_id();
   const int wave = threadIdx.x / kWave;
   const int64_t tw = (static_cast<int64_t>(blockIdx.x) * 4 + wave) * tpw;  // wave's first token
@@ -392,12 +430,17 @@ __global__ __launch_bounds__(kThreads) void route_gate_kernel(
       }
       l[i] = v;
     }
-    gate_token<VPL>(l, lane, E, bias, k, renorm, sel_only, t, topk_idx, topk_w, pacc, cacc);
+    gate_token<VPL>(l, lane, E, bias, k, renorm, sel_only, monitor, t, topk_idx, topk_w, pacc, cacc,
+                    lse2, ent);
   }
 #pragma unroll
   for (int i = 0; i < VPL; ++i) {
     sprob[wave * EP + lane + kWave * i] = pacc[i];
     scnt[wave * EP + lane + kWave * i] = cacc[i];
+  }
+  if (monitor && lane == 0) {
+    smon[wave] = lse2;
+    smon[4 + wave] = ent;
   }
   __syncthreads();
   for (int e = threadIdx.x; e < E; e += kThreads) {
@@ -405,6 +448,10 @@ __global__ __launch_bounds__(kThreads) void route_gate_kernel(
         ((sprob[e] + sprob[EP + e]) + sprob[2 * EP + e]) + sprob[3 * EP + e];
     part_cnt[static_cast<int64_t>(blockIdx.x) * E + e] =
         scnt[e] + scnt[EP + e] + scnt[2 * EP + e] + scnt[3 * EP + e];
+  }
+  if (monitor && threadIdx.x == 0) {
+    part_mon[2 * blockIdx.x] = ((smon[0] + smon[1]) + smon[2]) + smon[3];
+    part_mon[2 * blockIdx.x + 1] = ((smon[4] + smon[5]) + smon[6]) + smon[7];
   }
 }
 
@@ -415,7 +462,7 @@ __global__ __launch_bounds__(kThreads) void route_gate_kernel(
 __global__ __launch_bounds__(kThreads) void route_stats_kernel(
     const float* __restrict__ part_prob, const int32_t* __restrict__ part_cnt, int64_t rows,
     int64_t n, int E, int k, int32_t* __restrict__ sel_count, float* __restrict__ prob_mean,
-    double* __restrict__ term) {
+    double* __restrict__ term, int64_t* __restrict__ cnt) {
   __shared__ double sp[kThreads];
   __shared__ int64_t sc[kThreads];
   const int e = blockIdx.x;
@@ -441,6 +488,7 @@ __global__ __launch_bounds__(kThreads) void route_stats_kernel(
     if (sel_count) sel_count[e] = static_cast<int32_t>(sc[0]);
     if (prob_mean) prob_mean[e] = static_cast<float>(pm);
     term[e] = fr * pm;
+    cnt[e] = sc[0];
   }
 }
 
@@ -457,30 +505,65 @@ __global__ __launch_bounds__(kThreads) void route_update_bias_kernel(
   logit_bias[e] = load > nk ? __fsub_rn(b, gamma) : (load < nk ? __fadd_rn(b, gamma) : b);
 }
 
-// aux = E * sum_e term[e], the sum over a fixed-shape tree.
-__global__ __launch_bounds__(kThreads) void route_aux_kernel(const double* __restrict__ term,
-                                                             int E, float* __restrict__ aux) {
-  __shared__ double red[kThreads];
-  double local = 0.0;
-  for (int e = threadIdx.x; e < E; e += kThreads) local += term[e];
-  red[threadIdx.x] = local;
+// aux = E * sum_e term[e], the sum over a fixed-shape tree.  With monitor (4 floats):
+// z-loss 0.001 * (sum of the rows' logsumexp^2) / N, the mean top-k entropy, the sum
+// over experts of (count / N)^2 and the count's standard deviation over its mean.
+__global__ __launch_bounds__(kThreads) void route_aux_kernel(
+    const double* __restrict__ term, const int64_t* __restrict__ cnt,
+    const float* __restrict__ part_mon, int64_t rows, int64_t n, int E,
+    float* __restrict__ aux, float* __restrict__ monitor) {
+  __shared__ double red[5][kThreads];
+  double v[5] = {0.0, 0.0, 0.0, 0.0, 0.0};
+  for (int e = threadIdx.x; e < E; e += kThreads) v[0] += term[e];
+  if (monitor) {
+    for (int64_t b = threadIdx.x; b < rows; b += kThreads) {
+      v[1] += static_cast<double>(part_mon[2 * b]);
+      v[2] += static_cast<double>(part_mon[2 * b + 1]);
+    }
+    for (int e = threadIdx.x; e < E; e += kThreads) {
+      const double c = static_cast<double>(cnt[e]);
+      v[3] += c;
+      v[4] += c * c;
+    }
+  }
+#pragma unroll
+  for (int q = 0; q < 5; ++q) red[q][threadIdx.x] = v[q];
   __syncthreads();
   for (int s = kThreads / 2; s >= 1; s >>= 1) {
-    if (threadIdx.x < s) red[threadIdx.x] += red[threadIdx.x + s];
+    if (threadIdx.x < s) {
+#pragma unroll
+      for (int q = 0; q < 5; ++q) red[q][threadIdx.x] += red[q][threadIdx.x + s];
+    }
     __syncthreads();
   }
-  if (threadIdx.x == 0) aux[0] = static_cast<float>(static_cast<double>(E) * red[0]);
+  if (threadIdx.x != 0) return;
+  if (aux) aux[0] = static_cast<float>(static_cast<double>(E) * red[0][0]);
+  if (monitor) {
+    const double nn = static_cast<double>(n);
+    const double mean = red[3][0] / E;
+    const double var = red[4][0] / E - mean * mean;
+    monitor[0] = n > 0 ? static_cast<float>(0.001 * red[1][0] / nn) : 0.f;
+    monitor[1] = n > 0 ? static_cast<float>(red[2][0] / nn) : 0.f;
+    monitor[2] = n > 0 ? static_cast<float>(red[4][0] / (nn * nn)) : 0.f;
+    monitor[3] = mean > 0.0 ? static_cast<float>(sqrt(var > 0.0 ? var : 0.0) / mean) : 0.f;
+  }
+}
+
+// drop rate = n_dropped / (N k), written after the dispatch.
+__global__ void route_drop_rate_kernel(const int32_t* __restrict__ n_dropped, int64_t nk,
+                                       float* __restrict__ out) {
+  if (threadIdx.x == 0) out[0] = nk > 0 ? static_cast<float>(static_cast<double>(n_dropped[0]) / nk) : 0.f;
 }
 
 template <typename XT, int ET>
 hipError_t launch_route_t(hipStream_t st, const void* x, int64_t n, int64_t d,
                           const float* wr, const float* bias, int e, int k, int renorm,
                           const float* logits_in, float* logits_out, int32_t* idx,
-                          float* w, float* pp, int32_t* pc) {
+                          float* w, float* pp, int32_t* pc, float* pm) {
   const int64_t blocks = route_blocks(n);
   hipLaunchKernelGGL((route_kernel<XT, ET>), dim3(static_cast<unsigned>(blocks)),
                      dim3(kThreads), 0, st, static_cast<const XT*>(x), n, d, wr, bias, e, k,
-                     renorm, logits_in, logits_out, idx, w, pp, pc);
+                     renorm, logits_in, logits_out, idx, w, pp, pc, pm);
   return hipGetLastError();
 }
 
@@ -488,15 +571,15 @@ template <typename XT>
 hipError_t launch_route_dt(hipStream_t st, const void* x, int64_t n, int64_t d,
                            const float* wr, const float* bias, int e, int k, int renorm,
                            const float* li, float* lo, int32_t* idx, float* w, float* pp,
-                           int32_t* pc) {
+                           int32_t* pc, float* pm) {
   const int n_et = (e + 15) / 16;
-  if (n_et <= 1) return launch_route_t<XT, 1>(st, x, n, d, wr, bias, e, k, renorm, li, lo, idx, w, pp, pc);
-  if (n_et <= 2) return launch_route_t<XT, 2>(st, x, n, d, wr, bias, e, k, renorm, li, lo, idx, w, pp, pc);
-  if (n_et <= 4) return launch_route_t<XT, 4>(st, x, n, d, wr, bias, e, k, renorm, li, lo, idx, w, pp, pc);
-  if (n_et <= 8) return launch_route_t<XT, 8>(st, x, n, d, wr, bias, e, k, renorm, li, lo, idx, w, pp, pc);
-  if (n_et <= 10) return launch_route_t<XT, 10>(st, x, n, d, wr, bias, e, k, renorm, li, lo, idx, w, pp, pc);
-  if (n_et <= 16) return launch_route_t<XT, 16>(st, x, n, d, wr, bias, e, k, renorm, li, lo, idx, w, pp, pc);
-  return launch_route_t<XT, 32>(st, x, n, d, wr, bias, e, k, renorm, li, lo, idx, w, pp, pc);
+  if (n_et <= 1) return launch_route_t<XT, 1>(st, x, n, d, wr, bias, e, k, renorm, li, lo, idx, w, pp, pc, pm);
+  if (n_et <= 2) return launch_route_t<XT, 2>(st, x, n, d, wr, bias, e, k, renorm, li, lo, idx, w, pp, pc, pm);
+  if (n_et <= 4) return launch_route_t<XT, 4>(st, x, n, d, wr, bias, e, k, renorm, li, lo, idx, w, pp, pc, pm);
+  if (n_et <= 8) return launch_route_t<XT, 8>(st, x, n, d, wr, bias, e, k, renorm, li, lo, idx, w, pp, pc, pm);
+  if (n_et <= 10) return launch_route_t<XT, 10>(st, x, n, d, wr, bias, e, k, renorm, li, lo, idx, w, pp, pc, pm);
+  if (n_et <= 16) return launch_route_t<XT, 16>(st, x, n, d, wr, bias, e, k, renorm, li, lo, idx, w, pp, pc, pm);
+  return launch_route_t<XT, 32>(st, x, n, d, wr, bias, e, k, renorm, li, lo, idx, w, pp, pc, pm);
 }
 
 template <int EPT>
@@ -512,11 +595,11 @@ hipError_t launch_logits_t(hipStream_t st, const uint16_t* x, const RoutePlan& p
 template <int VPL>
 hipError_t launch_gate_t(hipStream_t st, const float* part, int ks, int64_t n, int e,
                          const float* bias, int k, int renorm, float* lo, int32_t* idx,
-                         float* w, float* pp, int32_t* pc) {
+                         float* w, float* pp, int32_t* pc, float* pm) {
   const int tpw = gate_tokens_per_wave(n);
   hipLaunchKernelGGL((route_gate_kernel<VPL>), dim3(static_cast<unsigned>(gate_blocks(n))),
                      dim3(kThreads), 0, st, part, ks, n, e, bias, k, renorm, tpw, lo, idx, w,
-                     pp, pc);
+                     pp, pc, pm);
   return hipGetLastError();
 }
 
@@ -525,10 +608,10 @@ hipError_t launch_gate_t(hipStream_t st, const float* part, int ks, int64_t n, i
 hipError_t launch_route(hipStream_t st, const float* x, int64_t n, int64_t d,
                         const float* w_router, const float* logit_bias, int e, int k,
                         int renorm, float* logits_out, int32_t* topk_idx, float* topk_w,
-                        float* part_prob, int32_t* part_cnt) {
+                        float* part_prob, int32_t* part_cnt, float* part_mon) {
   if (n <= 0) return hipSuccess;
   return launch_route_dt<float>(st, x, n, d, w_router, logit_bias, e, k, renorm, nullptr,
-                                logits_out, topk_idx, topk_w, part_prob, part_cnt);
+                                logits_out, topk_idx, topk_w, part_prob, part_cnt, part_mon);
 }
 
 RoutePlan route_plan(int64_t n, int64_t d, int e) {
@@ -582,14 +665,14 @@ hipError_t launch_route_logits(hipStream_t st, const uint16_t* x, const RoutePla
 hipError_t launch_route_gate(hipStream_t st, const float* part, int ks, int64_t n, int e,
                              const float* bias, int k, int renorm, float* logits_out,
                              int32_t* topk_idx, float* topk_w, float* part_prob,
-                             int32_t* part_cnt) {
+                             int32_t* part_cnt, float* part_mon) {
   if (n <= 0) return hipSuccess;
   const int vpl = (e + kWave - 1) / kWave;
-  if (vpl <= 1) return launch_gate_t<1>(st, part, ks, n, e, bias, k, renorm, logits_out, topk_idx, topk_w, part_prob, part_cnt);
-  if (vpl <= 2) return launch_gate_t<2>(st, part, ks, n, e, bias, k, renorm, logits_out, topk_idx, topk_w, part_prob, part_cnt);
-  if (vpl <= 3) return launch_gate_t<3>(st, part, ks, n, e, bias, k, renorm, logits_out, topk_idx, topk_w, part_prob, part_cnt);
-  if (vpl <= 4) return launch_gate_t<4>(st, part, ks, n, e, bias, k, renorm, logits_out, topk_idx, topk_w, part_prob, part_cnt);
-  return launch_gate_t<8>(st, part, ks, n, e, bias, k, renorm, logits_out, topk_idx, topk_w, part_prob, part_cnt);
+  if (vpl <= 1) return launch_gate_t<1>(st, part, ks, n, e, bias, k, renorm, logits_out, topk_idx, topk_w, part_prob, part_cnt, part_mon);
+  if (vpl <= 2) return launch_gate_t<2>(st, part, ks, n, e, bias, k, renorm, logits_out, topk_idx, topk_w, part_prob, part_cnt, part_mon);
+  if (vpl <= 3) return launch_gate_t<3>(st, part, ks, n, e, bias, k, renorm, logits_out, topk_idx, topk_w, part_prob, part_cnt, part_mon);
+  if (vpl <= 4) return launch_gate_t<4>(st, part, ks, n, e, bias, k, renorm, logits_out, topk_idx, topk_w, part_prob, part_cnt, part_mon);
+  return launch_gate_t<8>(st, part, ks, n, e, bias, k, renorm, logits_out, topk_idx, topk_w, part_prob, part_cnt, part_mon);
 }
 
 hipError_t launch_update_bias(hipStream_t st, const int32_t* sel_count, int e, int64_t n, int k,
@@ -600,15 +683,23 @@ hipError_t launch_update_bias(hipStream_t st, const int32_t* sel_count, int e, i
 }
 
 hipError_t launch_route_finalize(hipStream_t st, const float* part_prob,
-                                 const int32_t* part_cnt, int64_t rows, int64_t n, int e, int k,
-                                 int32_t* sel_count, float* prob_mean, float* aux, double* term) {
+                                 const int32_t* part_cnt, const float* part_mon, int64_t rows,
+                                 int64_t n, int e, int k, int32_t* sel_count, float* prob_mean,
+                                 float* aux, float* monitor, double* term, int64_t* cnt) {
   hipLaunchKernelGGL(route_stats_kernel, dim3(static_cast<unsigned>(e)), dim3(kThreads), 0, st,
-                     part_prob, part_cnt, rows, n, e, k, sel_count, prob_mean, term);
+                     part_prob, part_cnt, rows, n, e, k, sel_count, prob_mean, term, cnt);
   {
     const hipError_t err = hipGetLastError();
     if (err != hipSuccess) return err;
   }
-  if (aux) hipLaunchKernelGGL(route_aux_kernel, dim3(1), dim3(kThreads), 0, st, term, e, aux);
+  if (aux || monitor)
+    hipLaunchKernelGGL(route_aux_kernel, dim3(1), dim3(kThreads), 0, st, term, cnt, part_mon, rows,
+                       n, e, aux, monitor);
+  return hipGetLastError();
+}
+
+hipError_t launch_drop_rate(hipStream_t st, const int32_t* n_dropped, int64_t nk, float* out) {
+  hipLaunchKernelGGL(route_drop_rate_kernel, dim3(1), dim3(kWave), 0, st, n_dropped, nk, out);
   return hipGetLastError();
 }
 

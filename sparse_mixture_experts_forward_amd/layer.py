@@ -75,7 +75,8 @@ class MoELayer:
             kept_count=torch.empty(c.n_experts, dtype=i32, device=dev),
             n_dropped=torch.empty(1, dtype=i32, device=dev),
             expert_offsets=torch.empty(c.n_experts + 1, dtype=i32, device=dev),
-            slot_row=torch.empty((n_tokens, c.top_k), dtype=i32, device=dev))
+            slot_row=torch.empty((n_tokens, c.top_k), dtype=i32, device=dev),
+            monitor=torch.empty(5, dtype=f32, device=dev))
 
     def forward(self, x: torch.Tensor, y: Optional[torch.Tensor] = None,
                 stats: Optional[dict] = None, stream=None, stage_events=None) -> torch.Tensor:
@@ -99,7 +100,7 @@ class MoELayer:
                     c.n_experts, c.top_k, c.renormalize, logits_in,
                     s["logits"] if logits_in is None else None, s["topk_idx"], s["topk_w"],
                     s["sel_count"], s["prob_mean"], s["aux"], ws, n_tokens=n, stream=stream,
-                    bias_selection_only=c.bias_selection_only)
+                    bias_selection_only=c.bias_selection_only, monitor=s["monitor"])
         return s
 
     def update_bias(self, sel_count: torch.Tensor, n_tokens: int, gamma: float, stream=None):

@@ -50,7 +50,7 @@ def test_capacity_rejects_bad_arguments():
 def _route_status(**kw):
     a = dict(stream=None, x=None, xt=B.MOE_BF16, n=4, d=64, wr=None, bias=None, e=8, k=2,
              renorm=1, sel_only=0, li=None, lo=None, idx=None, w=None, sel=None, pm=None,
-             aux=None, ws=None, wsb=0)
+             aux=None, mon=None, ws=None, wsb=0)
     a.update(kw)
     return B.lib().moe_route(*a.values())
 

@@ -37,10 +37,12 @@ def _route(x, wr, lb, E, k, renorm=True, logits_in=None, n=None, sel_only=False)
                w=torch.empty((n, k), dtype=f32, device=DEV),
                sel=torch.empty(E, dtype=i32, device=DEV),
                pm=torch.empty(E, dtype=f32, device=DEV),
-               aux=torch.empty(1, dtype=f32, device=DEV))
+               aux=torch.empty(1, dtype=f32, device=DEV),
+               mon=torch.full((4,), -1.0, dtype=f32, device=DEV))
     ws = workspace(B.moe_route_workspace_size(n, x.shape[1] if x is not None else 0, E), DEV)
     B.moe_route(x, wr, lb, E, k, renorm, logits_in, out["logits"], out["idx"], out["w"],
-                out["sel"], out["pm"], out["aux"], ws, n_tokens=n, bias_selection_only=sel_only)
+                out["sel"], out["pm"], out["aux"], ws, n_tokens=n, bias_selection_only=sel_only,
+                monitor=out["mon"])
     torch.cuda.synchronize()
     return {kk: (None if v is None else v.cpu().numpy()) for kk, v in out.items()}
 
@@ -56,7 +58,21 @@ def _check_gate(logits32, bias, k, E, got, renorm=True, sel_only=False):
     assert np.array_equal(got["sel"], st.sel_count)
     np.testing.assert_allclose(got["pm"], st.prob_mean, rtol=2e-5, atol=1e-8)
     assert abs(float(got["aux"][0]) - st.aux) <= 1e-5 * max(st.aux, 1e-30)
+    _check_monitor(got["mon"], O.router_monitor(logits32, p, idx, st.sel_count, 0))
     return idx
+
+
+def _check_monitor(got, mon):
+    """Router health signals: z-loss and entropy are float32 per token (logsumexp, the
+    selected probabilities' -q ln q) summed in double; the load signals come from the
+    exact counts in double."""
+    z, h, sq, cv = (float(v) for v in got[:4])
+    assert abs(z - mon.z_loss) <= 2e-5 * mon.z_loss + 1e-9, (z, mon.z_loss)
+    assert abs(h - mon.entropy) <= 2e-5 * mon.entropy + 2e-6, (h, mon.entropy)
+    assert abs(sq - mon.load_sumsq) <= 1e-6 * mon.load_sumsq, (sq, mon.load_sumsq)
+    assert abs(cv - mon.load_cv) <= 1e-6 * mon.load_cv + 1e-7, (cv, mon.load_cv)
+    if len(got) > 4:
+        assert abs(float(got[4]) - mon.drop_rate) <= 1e-7 * mon.drop_rate, (got[4], mon.drop_rate)
 
 
 # ------------------------------------------------------------------ generator
@@ -380,6 +396,7 @@ def _forward_and_oracle(cfg, tokens=None, check_all_logits=True):
     np.testing.assert_allclose(st["topk_w"].cpu().numpy(), r.topk_w, rtol=2e-6, atol=1e-7)
     np.testing.assert_allclose(st["prob_mean"].cpu().numpy(), r.stats.prob_mean, rtol=2e-5, atol=1e-8)
     assert abs(float(st["aux"].cpu()[0]) - r.stats.aux) <= 1e-5 * r.stats.aux
+    _check_monitor(st["monitor"].cpu().numpy(), r.monitor)
     yg = widen_t(y)[r.tokens]
     err = normwise_err(yg, r.y)
     return err, r, y
@@ -450,4 +467,5 @@ def test_forward_edge_cases():
     torch.cuda.synchronize()
     assert y.shape == (0, cfg.d_model)
     assert (st["sel_count"].cpu() == 0).all() and float(st["aux"].cpu()[0]) == 0.0
+    assert (st["monitor"].cpu() == 0).all()
     assert (st["expert_offsets"].cpu() == 0).all()
