@@ -89,8 +89,9 @@ int64_t moe_capacity(int64_t n_tokens, int32_t n_experts, int32_t k, double alph
  *   monitor[0..3] (float32, optional): router health signals, accumulated in double
  *     [0] z-loss  = 0.001 * (1/N) sum_t (log sum_e exp logits[t][e])^2 on the unbiased
  *                   logits ([MoE-overview] §3.3)
- *     [1] entropy = (1/N) sum_t -sum_j q[t][j] ln q[t][j], q[t][:] = the token's k
- *                   selected probabilities renormalised to sum 1 ([GPT4-2pct] §2.3)
+ *     [1] entropy = (1/N) sum_t -sum_j q[t][j] log2 q[t][j] (bits), q[t][:] = the
+ *                   token's k selected probabilities renormalised to sum 1
+ *                   ([GPT4-2pct] §2.3, base 2 as in its §3.1)
  *     [2] sum_e (sel_count[e] / N)^2  ([MoE-2pct] §2.2 balance term, no coefficient)
  *     [3] coefficient of variation of sel_count: population standard deviation over
  *         mean ([GPT4-2pct] §4.1)

@@ -184,7 +184,7 @@ def balance_stats(p64: np.ndarray, idx: np.ndarray, n_experts: int) -> BalanceSt
 @dataclass
 class RouterMonitor:
     z_loss: float  # 0.001 * mean_t logsumexp(logits[t, :])^2
-    entropy: float  # mean_t of -sum_j w_j ln w_j over the token's renormalised top-k
+    entropy: float  # mean_t of -sum_j w_j log2 w_j over the token's renormalised top-k
     load_sumsq: float  # sum_e (sel_count[e] / N)^2
     load_cv: float  # std_e(sel_count) / mean_e(sel_count), population std
     drop_rate: float  # dropped assignments / (N*k)
@@ -195,9 +195,10 @@ def router_monitor(logits32: np.ndarray, p64: np.ndarray, idx: np.ndarray, sel_c
     """Monitoring signals of the router named on the pages, each taken as defined there:
       z_loss      [MoE-overview] §3.3: 0.001 * mean(logsumexp(router_logits)^2), on the
                   router's own (unbiased) logits;
-      entropy     [GPT4-2pct] §2.3: per token -sum p~ log p~ over the softmax of its
+      entropy     [GPT4-2pct] §2.3: per token -sum p~ log2 p~ over the softmax of its
                   top-k logits, i.e. the k selected probabilities renormalised, averaged
-                  over tokens (natural log);
+                  over tokens; in bits, the base of the page's §3.1 measuring code (its
+                  §2.3 figures, up to 0.85 for two slots, exceed ln 2 and so need base 2);
       load_sumsq  [MoE-2pct] §2.2: sum over experts of (selections of e / N)^2, the
                   page's balance term without its coefficient;
       load_cv     [GPT4-2pct] §4.1 (step 3): standard deviation over mean of the
@@ -214,7 +215,7 @@ def router_monitor(logits32: np.ndarray, p64: np.ndarray, idx: np.ndarray, sel_c
     lse = (m + np.log(np.exp(l64 - m).sum(axis=1, keepdims=True)))[:, 0]
     q = p64[np.arange(n)[:, None], idx]
     q = q / q.sum(axis=1, keepdims=True)
-    ent = -(q * np.log(q)).sum(axis=1)
+    ent = -(q * np.log2(q)).sum(axis=1)
     cnt = np.asarray(sel_count, dtype=F64)
     mean = cnt.sum() / e
     cv = float(np.sqrt(((cnt - mean) ** 2).sum() / e) / mean) if mean > 0 else 0.0

@@ -46,7 +46,7 @@ __device__ __forceinline__ void load_x4(const uint16_t* p, float v[4]) {
 // Writes topk_idx / topk_w of token t and adds p and the selection counts to the lane's
 // statistics accumulators.
 // With monitor, also adds the token's logsumexp(l)^2 to lse2 and the entropy of its
-// renormalised top-k weights to ent (wave-uniform values).
+// renormalised top-k weights (in bits) to ent (wave-uniform values).
 template <int VPL>
 __device__ __forceinline__ void gate_token(const float (&l)[VPL], int lane, int E,
                                            const float* __restrict__ bias, int k, int renorm,
@@ -133,7 +133,7 @@ __device__ __forceinline__ void gate_token(const float (&l)[VPL], int lane, int 
     }
     lse2 += lse * lse;
     const float q = (lane < k) ? my_ex / sel_ex_sum : 0.f;
-    ent += wave_sum(q > 0.f ? -q * logf(q) : 0.f);
+    ent += wave_sum(q > 0.f ? -q * log2f(q) : 0.f);
   }
 }
 

@@ -64,7 +64,7 @@ def _check_gate(logits32, bias, k, E, got, renorm=True, sel_only=False):
 
 def _check_monitor(got, mon):
     """Router health signals: z-loss and entropy are float32 per token (logsumexp, the
-    selected probabilities' -q ln q) summed in double; the load signals come from the
+    selected probabilities' -q log2 q) summed in double; the load signals come from the
     exact counts in double."""
     z, h, sq, cv = (float(v) for v in got[:4])
     assert abs(z - mon.z_loss) <= 2e-5 * mon.z_loss + 1e-9, (z, mon.z_loss)

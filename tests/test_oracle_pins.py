@@ -479,7 +479,7 @@ def test_bias_update_balances_a_skewed_router():
 # ------------------------------------------------------------------ router monitoring signals
 def test_monitor_equal_logits_closed_forms():
     # equal logits: logsumexp = ln E, the k selections (experts 0..k-1, lowest index on
-    # ties) carry equal renormalised weights, so the entropy is ln k; the counts are
+    # ties) carry equal renormalised weights, so the entropy is log2 k bits; the counts are
     # N on k experts and 0 elsewhere
     n, E, k = 40, 8, 2
     L = np.zeros((n, E), np.float32)
@@ -489,7 +489,7 @@ def test_monitor_equal_logits_closed_forms():
     st = O.balance_stats(p, idx, E)
     m = O.router_monitor(L, p, idx, st.sel_count, 0)
     assert m.z_loss == pytest.approx(0.001 * math.log(E) ** 2, rel=1e-14)
-    assert m.entropy == pytest.approx(math.log(k), rel=1e-14)
+    assert m.entropy == pytest.approx(math.log2(k), rel=1e-14)
     assert m.load_sumsq == pytest.approx(k * 1.0, rel=1e-14)  # k experts at (N/N)^2
     # counts [N, N, 0 x 6]: mean N/4, std = N/4 * sqrt(3) -> CV = sqrt(3)
     assert m.load_cv == pytest.approx(math.sqrt(3.0), rel=1e-14)
@@ -509,7 +509,7 @@ def test_monitor_balanced_page_exercise():
     m = O.router_monitor(np.zeros((n, E), np.float32), p, idx, sel, 0)
     assert m.load_cv == 0.0
     assert m.load_sumsq == pytest.approx(k * k / E, rel=1e-15)
-    assert m.entropy == pytest.approx(math.log(2.0), rel=1e-14)
+    assert m.entropy == pytest.approx(1.0, rel=1e-14)  # one bit
 
 
 def test_monitor_concentration_and_drops():
@@ -533,14 +533,14 @@ def test_monitor_concentration_and_drops():
 
 def test_monitor_two_slot_entropy_closed_form():
     # top-2 of logits [a, b, very low]: renormalised weights are sigmoid(a - b) and its
-    # complement, entropy = -q ln q - (1 - q) ln (1 - q)
+    # complement, entropy = -q log2 q - (1 - q) log2 (1 - q)
     L = np.array([[1.5, 0.25, -30.0]], np.float32)
     z = O.biased_scores(L, None)
     idx = O.select_topk(z, 2)
     p = O.softmax64(z)
     m = O.router_monitor(L, p, idx, np.bincount(idx.ravel(), minlength=3), 0)
     q = 1.0 / (1.0 + math.exp(-(1.5 - 0.25)))
-    assert m.entropy == pytest.approx(-q * math.log(q) - (1 - q) * math.log(1 - q), rel=1e-12)
+    assert m.entropy == pytest.approx(-q * math.log2(q) - (1 - q) * math.log2(1 - q), rel=1e-12)
 
 
 def test_monitor_empty_batch():
