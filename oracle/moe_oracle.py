@@ -37,6 +37,10 @@ design notes of the repository):
     from the softmax of the unbiased logits; the batch-level update lowers the bias of
     an expert chosen more often than the mean load N*k/E by gamma, raises it by gamma
     when chosen less often, and leaves it when equal (the step size is the caller's);
+  * overflow re-routing runs in rounds after the plain capacity rule; in each round an
+    unplaced slot proposes to its token's next preferred expert that still has room,
+    experts accept in token order; the slot's weight becomes that of its new expert;
+  * the log-form adaptive alpha is held at 1 for batches below 256 tokens;
   * GELU is the exact erf form; SwiGLU is W2 (SiLU(W1 x) * (W3 x)).
 
 Every function here is pinned by tests that do not call it to check itself (closed
@@ -281,6 +285,109 @@ def plan_dispatch(idx: np.ndarray, n_experts: int, cap: Optional[int]) -> Dispat
 
 
 # ----------------------------------------------------------------------------------
+# Adaptive capacity and overflow re-routing.  [MoE-2pct] §3.1: an expert whose
+# assignments exceed its capacity sends the excess on to the next-best expert, and
+# alpha should grow with the batch (its tip: 1 + 0.5 log2(N/256)); §5.3: the capacity
+# factor 1 + 0.5 min(1, N/256) in a capacity computed without the inner floor.
+# ----------------------------------------------------------------------------------
+def alpha_log(n_tokens: int) -> float:
+    """[MoE-2pct] §3.1 tip: alpha = 1 + 0.5 log2(N/256).  The page uses it for batches
+    growing from 256; below 256 alpha is held at 1 (reading: the formula would fall
+    to 0 at N = 64 and below zero under it)."""
+    if n_tokens <= 256:
+        return 1.0
+    return 1.0 + 0.5 * math.log2(n_tokens / 256.0)
+
+
+def capacity_log(n_tokens: int, n_experts: int, k: int) -> int:
+    """C = floor(floor(k*N/E) * alpha_log(N)), the §3.1 capacity with the tip's alpha."""
+    base = (k * n_tokens) // n_experts
+    return int(math.floor(float(base) * alpha_log(n_tokens)))
+
+
+def capacity_linear(n_tokens: int, n_experts: int, k: int) -> int:
+    """[MoE-2pct] §5.3: cf = 1 + 0.5 min(1, N/256), C = floor(k*N/E * cf), evaluated
+    exactly in rationals (the page's float expression, without its rounding)."""
+    from fractions import Fraction
+
+    cf = 1 + Fraction(1, 2) * min(Fraction(1), Fraction(n_tokens, 256))
+    return int(math.floor(Fraction(k * n_tokens, n_experts) * cf))
+
+
+@dataclass
+class Reroute:
+    topk_idx: np.ndarray  # int64 [N, k], the expert each slot ends on
+    placed: np.ndarray  # bool [N, k], slot holds a place within its expert's capacity
+    n_rerouted: int  # slots placed on an expert other than their first choice
+    rounds: int  # rounds that made at least one proposal
+
+
+def preference_order(z32: np.ndarray) -> np.ndarray:
+    """Each token's experts from most to least preferred: descending z, the lower index
+    first on ties (the same order the top-k selection uses)."""
+    n, e = z32.shape
+    order = np.empty((n, e), dtype=np.int64)
+    ids = np.arange(e)
+    for t in range(n):
+        order[t] = np.lexsort((ids, -z32[t].astype(F64)))
+    return order
+
+
+def reroute(z32: np.ndarray, idx: np.ndarray, n_experts: int, cap: Optional[int],
+            max_rounds: int) -> Reroute:
+    """Overflow re-routing ([MoE-2pct] §3.1), taken in rounds (reading):
+      round 0 is the plain capacity rule (plan_dispatch): every expert keeps its first
+      C assignments in token order; the slots it cannot keep are unplaced and every
+      expert's spare room is C minus what it kept.
+      round r = 1..max_rounds: the experts with spare room at the start of the round
+      are open.  Every unplaced slot, token by token and slot by slot, proposes to its
+      token's most preferred expert that the token has not yet held, proposed to or
+      passed over, skipping experts that are not open (they never reopen).  An expert
+      accepts its proposals in token order while it has room; a rejected slot stays
+      unplaced and tries again in the next round.  Rounds stop early once no slot has
+      an expert left to propose to.
+    A placed slot moves to the expert that accepted it; a slot never placed keeps its
+    first-choice expert and is dropped there, as without re-routing."""
+    n, k = idx.shape
+    new = np.asarray(idx, dtype=np.int64).copy()
+    if cap is None or n == 0 or max_rounds <= 0:
+        return Reroute(new, np.ones((n, k), dtype=bool) if cap is None else
+                       plan_dispatch(new, n_experts, cap).keep, 0, 0)
+    order = preference_order(z32)
+    assert np.array_equal(order[:, :k], new), "topk_idx must be the top-k of z"
+    plan0 = plan_dispatch(new, n_experts, cap)
+    placed = plan0.keep.copy()
+    room = cap - plan0.kept_count
+    nxt = np.full(n, k, dtype=np.int64)  # next position of the token's order to consider
+    rounds = 0
+    for _ in range(max_rounds):
+        open_ = room > 0
+        proposals = []
+        for t in range(n):
+            for j in range(k):
+                if placed[t, j]:
+                    continue
+                while nxt[t] < n_experts and not open_[order[t, nxt[t]]]:
+                    nxt[t] += 1
+                if nxt[t] == n_experts:
+                    continue
+                proposals.append((t, j, int(order[t, nxt[t]])))
+                nxt[t] += 1
+        if not proposals:
+            break
+        rounds += 1
+        taken = np.zeros(n_experts, dtype=np.int64)
+        for t, j, e in proposals:  # token order, then slot order
+            if taken[e] < room[e]:
+                taken[e] += 1
+                new[t, j] = e
+                placed[t, j] = True
+        room = room - taken
+    n_rerouted = int(placed.sum() - plan0.keep.sum())
+    return Reroute(new, placed, n_rerouted, rounds)
+
+
+# ----------------------------------------------------------------------------------
 # Expert networks.  [Why-MoE] §2.1 (dense FFN W2 GELU(W1 x)) and its MoELayer listing
 # (Linear(d, d_ff) -> GELU -> Linear(d_ff, d)); [MoE-2pct] §3.2 (SwiGLU expert).
 # Weights follow torch.nn.Linear: W1, W3 are [d_ff, d], W2 is [d, d_ff].
@@ -370,6 +477,8 @@ def forward(
     logits: Optional[np.ndarray] = None,
     tokens: Optional[np.ndarray] = None,
     bias_selection_only: bool = False,
+    capacity_rule: str = "fixed",
+    reroute_rounds: int = 0,
 ) -> ForwardResult:
     """Forward pass of the layer on x [N, d].
 
@@ -380,7 +489,12 @@ def forward(
     ``tokens`` is given, only those tokens' outputs are computed (routing, statistics
     and capacity still see every token, because capacity couples them).  With
     ``bias_selection_only`` the bias steers selection only ([Why-MoE] §2.4): weights
-    and mean probabilities use the softmax of the unbiased logits.
+    and mean probabilities use the softmax of the unbiased logits.  ``capacity_rule``
+    "fixed" uses alpha, "linear" and "log" the batch-dependent capacities of
+    [MoE-2pct] §5.3 and §3.1.  With ``reroute_rounds`` > 0 the slots over capacity are
+    re-routed (``reroute``) before the dispatch; the gate weights are then those of the
+    experts the slots end on (renormalised over them if ``renormalize``), while the
+    statistics and the monitor's routing signals describe the router's own choice.
     """
     x64 = widen(x, x_dtype)
     n = x64.shape[0]
@@ -392,8 +506,23 @@ def forward(
     p = softmax64(logits if bias_selection_only else z)
     w = gate_weights(p, idx, renormalize)
     st = balance_stats(p, idx, n_experts)
-    cap = capacity(n, n_experts, k, alpha)
+    if capacity_rule == "fixed":
+        cap = capacity(n, n_experts, k, alpha)
+    elif capacity_rule == "linear":
+        cap = capacity_linear(n, n_experts, k)
+    elif capacity_rule == "log":
+        cap = capacity_log(n, n_experts, k)
+    else:
+        raise ValueError(capacity_rule)
+    route_idx = idx
+    rr = None
+    if reroute_rounds > 0 and cap is not None:
+        rr = reroute(z, idx, n_experts, cap, reroute_rounds)
+        idx = rr.topk_idx
+        w = gate_weights(p, idx, renormalize)
     plan = plan_dispatch(idx, n_experts, cap)
+    if rr is not None:
+        assert np.array_equal(plan.keep, rr.placed)
 
     toks = np.arange(n, dtype=np.int64) if tokens is None else np.asarray(tokens, np.int64)
     pos = {int(t): i for i, t in enumerate(toks)}
@@ -410,5 +539,9 @@ def forward(
         slots = np.array([j for _, j in sel], dtype=np.int64)
         ye = expert_ffn(x64[toks[rows]], expert(e), act)
         y[rows] += w[toks[rows], slots][:, None] * ye
-    mon = router_monitor(logits, p, idx, st.sel_count, plan.n_dropped)
-    return ForwardResult(logits, z, p, idx, w, st, cap, plan, toks, y, mon)
+    mon = router_monitor(logits, p, route_idx, st.sel_count, plan.n_dropped)
+    res = ForwardResult(logits, z, p, idx, w, st, cap, plan, toks, y, mon)
+    if rr is not None:
+        res.extra["reroute"] = rr
+        res.extra["route_idx"] = route_idx
+    return res

@@ -547,3 +547,228 @@ def test_monitor_empty_batch():
     m = O.router_monitor(np.zeros((0, 4), np.float32), np.zeros((0, 4)), np.zeros((0, 2), np.int64),
                          np.zeros(4, np.int64), 0)
     assert (m.z_loss, m.entropy, m.load_sumsq, m.load_cv, m.drop_rate) == (0, 0, 0, 0, 0)
+
+
+# ------------------------------------------------------------------ adaptive capacity
+def test_capacity_linear_worked_values():
+    for n, E, k, c in GOLDEN["adaptive_linear"]["cases"]:
+        assert O.capacity_linear(n, E, k) == c, (n, E, k)
+
+
+def test_capacity_log_worked_values():
+    g = GOLDEN["adaptive_log"]
+    for n, a in g["alpha"]:
+        assert O.alpha_log(n) == a
+    for n, E, k, c in g["cases"]:
+        assert O.capacity_log(n, E, k) == c, (n, E, k)
+    # below 256 tokens alpha is held at 1, so the capacity is floor(kN/E)
+    assert O.capacity_log(64, 64, 2) == 2 and O.capacity_log(1, 8, 2) == 0
+
+
+def test_capacity_linear_is_monotone_and_bounded():
+    # between the fixed factors 1.0 and 1.5 at every N, and non-decreasing in N
+    prev = -1
+    for n in range(0, 2000, 7):
+        c = O.capacity_linear(n, 16, 2)
+        assert math.floor(2 * n / 16) <= c <= math.floor(2 * n / 16 * 1.5)
+        assert c >= prev
+        prev = c
+
+
+# ------------------------------------------------------------------ overflow re-routing
+def _rr_case(L, k, cap, rounds):
+    L = np.asarray(L, np.float32)
+    z = O.biased_scores(L, None)
+    idx = O.select_topk(z, k)
+    return idx, O.reroute(z, idx, L.shape[1], cap, rounds)
+
+
+def test_reroute_hand_example_token_order():
+    # every token prefers expert 0 (capacity 1): token 0 keeps it; tokens 1 and 3 both
+    # move on to expert 1, which takes the earlier token (1); token 2 moves to expert 2;
+    # in the second round token 3's next choice, expert 2, is full, and expert 0 was
+    # never open, so nothing is proposed and the rounds end after the first
+    L = [[3, 2, 1], [3, 2, 1], [3, 1, 2], [3, 2, 1]]
+    idx, rr = _rr_case(L, 1, 1, 10)
+    assert rr.topk_idx[:, 0].tolist() == [0, 1, 2, 0]
+    assert rr.placed[:, 0].tolist() == [True, True, True, False]
+    assert rr.n_rerouted == 2 and rr.rounds == 1
+
+
+def test_reroute_skips_experts_full_at_round_start():
+    # experts 0 and 1 are full after the plain rule; in the first round tokens 1 and 2
+    # pass over expert 1 and land on their next open experts 2 and 3
+    L = [[4, 3, 2, 1], [4, 3, 2, 1], [4, 3, 1, 2], [3, 4, 2, 1]]
+    idx, rr = _rr_case(L, 1, 1, 1)
+    assert idx[:, 0].tolist() == [0, 0, 0, 1]
+    assert rr.topk_idx[:, 0].tolist() == [0, 2, 3, 1]
+    assert rr.placed.all() and rr.n_rerouted == 2
+
+
+def test_reroute_round_limit():
+    # three tokens in the same order of preference, capacity 1: one round places token 1
+    # on expert 1 and leaves token 2 unplaced; a second round gives it expert 2
+    L = [[3, 2, 1]] * 3
+    _, r1 = _rr_case(L, 1, 1, 1)
+    assert r1.topk_idx[:, 0].tolist() == [0, 1, 0] and r1.placed[:, 0].tolist() == [True, True, False]
+    _, r2 = _rr_case(L, 1, 1, 2)
+    assert r2.topk_idx[:, 0].tolist() == [0, 1, 2] and r2.placed.all()
+
+
+def test_reroute_weights_follow_the_new_expert():
+    # k=2, capacity 1: token 0 keeps experts 0 and 1; token 1's slot 0 moves to expert 2
+    # (the only one with room), its slot 1 stays dropped on expert 1.  The renormalised
+    # weights are the softmax of the token's logits restricted to experts {2, 1}.
+    L = np.array([[2.0, 1.0, 0.0], [2.0, 1.0, 0.5]], np.float32)
+    idx, rr = _rr_case(L, 2, 1, 5)
+    assert rr.topk_idx.tolist() == [[0, 1], [2, 1]]
+    assert rr.placed.tolist() == [[True, True], [True, False]]
+    p = O.softmax64(O.biased_scores(L, None))
+    w = O.gate_weights(p, rr.topk_idx, True)
+    assert w[1, 0] == pytest.approx(1.0 / (1.0 + math.exp(0.5)), rel=1e-14)
+    assert w[1, 1] == pytest.approx(1.0 / (1.0 + math.exp(-0.5)), rel=1e-14)
+    wn = O.gate_weights(p, rr.topk_idx, False)
+    s = math.exp(2.0) + math.exp(1.0) + math.exp(0.5)
+    assert wn[1, 0] == pytest.approx(math.exp(0.5) / s, rel=1e-14)
+
+
+def test_reroute_without_overflow_changes_nothing():
+    rng = _rng(5)
+    L = rng.standard_normal((64, 8)).astype(np.float32)
+    z = O.biased_scores(L, None)
+    idx = O.select_topk(z, 2)
+    for cap in (None, 64 * 2):
+        rr = O.reroute(z, idx, 8, cap, 4)
+        assert np.array_equal(rr.topk_idx, idx) and rr.placed.all() and rr.n_rerouted == 0
+    # k = E: a token already holds every expert, there is nowhere to move
+    idx4 = O.select_topk(O.biased_scores(L[:, :4], None), 4)
+    rr = O.reroute(O.biased_scores(L[:, :4], None), idx4, 4, 3, 8)
+    assert np.array_equal(rr.topk_idx, idx4) and rr.n_rerouted == 0
+
+
+@pytest.mark.parametrize("seed,n,E,k,cap,rounds", [(1, 200, 16, 2, 20, 1), (2, 200, 16, 2, 20, 16),
+                                                   (3, 300, 8, 1, 30, 3), (4, 97, 12, 4, 25, 12),
+                                                   (5, 256, 64, 6, 18, 64)])
+def test_reroute_invariants(seed, n, E, k, cap, rounds):
+    rng = _rng(seed)
+    # skewed preferences so that several experts overflow
+    L = (rng.standard_normal((n, E)) + np.linspace(1.5, 0, E)).astype(np.float32)
+    z = O.biased_scores(L, None)
+    idx = O.select_topk(z, k)
+    plan0 = O.plan_dispatch(idx, E, cap)
+    assert plan0.n_dropped > 0
+    rr = O.reroute(z, idx, E, cap, rounds)
+    new = rr.topk_idx
+    # placed slots never exceed an expert's capacity; a token never holds an expert twice
+    load = np.bincount(new[rr.placed], minlength=E)
+    assert (load <= cap).all()
+    assert all(len(set(row)) == k for row in new.tolist())
+    # first-round keeps stay where they were; moved slots go to experts the token ranks
+    # below all of its own choices
+    assert (rr.placed >= plan0.keep).all()
+    assert np.array_equal(new[plan0.keep], idx[plan0.keep])
+    moved = new != idx
+    assert (moved <= rr.placed).all() and int(moved.sum()) == rr.n_rerouted
+    for t, j in zip(*np.nonzero(moved)):
+        e = new[t, j]
+        assert e not in idx[t]
+        assert all((z[t, e] < z[t, o]) or (z[t, e] == z[t, o] and e > o) for o in idx[t])
+    # the plain capacity rule applied to the new experts keeps exactly the placed slots
+    assert np.array_equal(O.plan_dispatch(new, E, cap).keep, rr.placed)
+    if rounds >= E:
+        # no spare room is left that an unplaced slot could have taken
+        room = cap - load
+        for t, j in zip(*np.nonzero(~rr.placed)):
+            assert all(room[e] == 0 or e in new[t] for e in range(E))
+
+
+def test_reroute_brute_force_tiny():
+    # tiny problems against a direct simulation written differently: each token keeps
+    # the set of experts it has held or proposed to, and proposes to its best expert
+    # outside that set that has room (an expert full once stays full, so passing over
+    # it needs no record); experts take proposals in token order while room remains
+    for seed in range(40):
+        rng = _rng(100 + seed)
+        n, E = int(rng.integers(1, 7)), int(rng.integers(2, 5))
+        k = int(rng.integers(1, E + 1))
+        cap = int(rng.integers(0, 3))
+        rounds = int(rng.integers(1, 5))
+        L = rng.integers(-2, 3, size=(n, E)).astype(np.float32)
+        z = O.biased_scores(L, None)
+        idx = O.select_topk(z, k)
+        rr = O.reroute(z, idx, E, cap, rounds)
+        prefs = [sorted(range(E), key=lambda e, t=t: (-float(z[t, e]), e)) for t in range(n)]
+        held = [list(prefs[t][:k]) for t in range(n)]
+        load = [0] * E
+        ok = [[False] * k for _ in range(n)]
+        for t in range(n):
+            for j in range(k):
+                if load[held[t][j]] < cap:
+                    load[held[t][j]] += 1
+                    ok[t][j] = True
+        tried = [set(prefs[t][:k]) for t in range(n)]
+        for _ in range(rounds):
+            has_room = [load[e] < cap for e in range(E)]
+            props = []
+            for t in range(n):
+                for j in range(k):
+                    if ok[t][j]:
+                        continue
+                    cand = [e for e in prefs[t] if e not in tried[t] and has_room[e]]
+                    if cand:
+                        tried[t].add(cand[0])
+                        props.append((t, j, cand[0]))
+            if not props:
+                break
+            for t, j, e in props:
+                if load[e] < cap:
+                    load[e] += 1
+                    held[t][j] = e
+                    ok[t][j] = True
+        assert rr.topk_idx.tolist() == held, seed
+        assert rr.placed.tolist() == ok, seed
+
+
+@pytest.mark.parametrize("renorm,rounds", [(True, 1), (False, 3), (True, 8)])
+def test_layer_with_reroute_matches_dense_loops(renorm, rounds):
+    # the rerouted layer as a dense gate over every expert: a slot's gate is the
+    # softmax probability of the expert it ends on (over the final experts of the token
+    # when renormalised), zero when the slot stays unplaced
+    rng = _rng(21)
+    N, d, d_ff, E, k = 13, 4, 5, 5, 2
+    x = rng.standard_normal((N, d)).astype(np.float32)
+    logits = (rng.standard_normal((N, E)) + np.array([1.0, 0.8, 0, 0, -0.5])).astype(np.float32)
+    ws = _tiny_experts(rng, E, d, d_ff, "gelu", bias=True)
+    alpha = 0.6  # C = floor(floor(26/5) * 0.6) = 3
+    r = O.forward(x, "f32", None, k, lambda e: ws[e], E, "gelu", alpha=alpha,
+                  renormalize=renorm, logits=logits, reroute_rounds=rounds)
+    assert r.cap == 3
+    rr = r.extra["reroute"]
+    assert rr.n_rerouted > 0
+    base = O.forward(x, "f32", None, k, lambda e: ws[e], E, "gelu", alpha=alpha,
+                     renormalize=renorm, logits=logits)
+    assert r.plan.n_dropped == base.plan.n_dropped - rr.n_rerouted
+    assert np.array_equal(r.stats.sel_count, base.stats.sel_count)  # the router's choice
+    for t in range(N):
+        zt = [float(v) for v in logits[t]]
+        m = max(zt)
+        ex = [math.exp(v - m) for v in zt]
+        p = [v / sum(ex) for v in ex]
+        fin = [int(e) for e in rr.topk_idx[t]]
+        den = sum(p[e] for e in fin) if renorm else 1.0
+        yt = np.zeros(d)
+        for j in range(k):
+            if rr.placed[t, j]:
+                yt += p[fin[j]] / den * np.array(_loop_ffn(x[t].astype(np.float64), ws[fin[j]], "gelu"))
+        assert np.allclose(r.y[t], yt, rtol=1e-12, atol=1e-14), t
+
+
+def test_layer_reroute_without_capacity_is_plain():
+    rng = _rng(22)
+    N, d, d_ff, E, k = 9, 4, 4, 4, 2
+    x = rng.standard_normal((N, d)).astype(np.float32)
+    logits = rng.standard_normal((N, E)).astype(np.float32)
+    ws = _tiny_experts(rng, E, d, d_ff, "swiglu")
+    a = O.forward(x, "f32", None, k, lambda e: ws[e], E, "swiglu", logits=logits, reroute_rounds=4)
+    b = O.forward(x, "f32", None, k, lambda e: ws[e], E, "swiglu", logits=logits)
+    assert np.array_equal(a.topk_idx, b.topk_idx) and np.array_equal(a.y, b.y)
