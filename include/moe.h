@@ -57,6 +57,13 @@ typedef enum { MOE_ACT_GELU = 0, MOE_ACT_SWIGLU = 1 } moe_act;
 /* Largest number of experts (routed or segments) a call accepts. */
 #define MOE_MAX_EXPERTS 512
 
+/* How the expert capacity is derived from the batch (moe_capacity_rule). */
+typedef enum {
+  MOE_CAPACITY_FIXED = 0,  /* floor(floor(k*N/E) * alpha), alpha <= 0: no limit */
+  MOE_CAPACITY_LINEAR = 1, /* [MoE-2pct] §5.3 factor growing linearly up to N = 256 */
+  MOE_CAPACITY_LOG = 2     /* [MoE-2pct] §3.1 tip: alpha growing with log2(N/256) */
+} moe_capacity_rule_t;
+
 /*
  * moe_capacity -- host function, no device work.
  * Expert capacity C = floor(floor(k*N/E) * alpha) ([MoE-2pct] §3.1 gives
@@ -65,6 +72,20 @@ typedef enum { MOE_ACT_GELU = 0, MOE_ACT_SWIGLU = 1 } moe_act;
  * n_tokens < 0, n_experts < 1 or k < 1.
  */
 int64_t moe_capacity(int64_t n_tokens, int32_t n_experts, int32_t k, double alpha);
+
+/*
+ * moe_capacity_rule -- host function, no device work.  Capacity under a rule:
+ *   MOE_CAPACITY_FIXED   moe_capacity(N, E, k, alpha)
+ *   MOE_CAPACITY_LINEAR  factor f = 1 + 0.5 * min(1, N/256), C = floor(k*N/E * f)
+ *                        ([MoE-2pct] §5.3's fix for small decode batches; evaluated
+ *                        exactly in integers), alpha ignored
+ *   MOE_CAPACITY_LOG     alpha(N) = 1 + 0.5 * log2(N/256) for N > 256, 1 otherwise
+ *                        (the §3.1 tip, which the page applies to batches growing
+ *                        from 256), C = floor(floor(k*N/E) * alpha(N)) in double
+ * Returns -1 with moe_last_error() set for bad arguments or an unknown rule.
+ */
+int64_t moe_capacity_rule(int64_t n_tokens, int32_t n_experts, int32_t k, int32_t rule,
+                          double alpha);
 
 /*
  * moe_route -- router product, gate and balance statistics.
@@ -143,6 +164,45 @@ moe_status moe_update_bias(void* stream, const int32_t* sel_count, int32_t n_exp
                            int64_t n_tokens, int32_t k, float gamma, float* logit_bias);
 
 /*
+ * moe_reroute -- overflow re-routing ([MoE-2pct] §3.1: assignments beyond an expert's
+ * capacity are sent on to the next-best expert).  Runs before moe_dispatch with the
+ * same capacity and rewrites topk_idx / topk_w so that moe_dispatch then keeps every
+ * re-routed slot:
+ *   round 0: the plain capacity rule of moe_dispatch (each expert keeps its first
+ *     `capacity` assignments in token order); the rest are unplaced and every expert
+ *     has room capacity - kept.
+ *   rounds 1..max_rounds: experts with room at the round's start are open.  Each
+ *     unplaced slot, token by token and slot by slot (j ascending), proposes to its
+ *     token's most preferred expert (descending z = logits + logit_bias, the lower
+ *     index first on ties) that the token has neither held nor proposed to and that is
+ *     open; each expert accepts proposals in token order while its room lasts.  An
+ *     accepted slot moves: topk_idx[t][j] = the new expert.  A slot never accepted
+ *     keeps its expert and is dropped by moe_dispatch.
+ *   The weights of every token that moved a slot are recomputed from the experts its
+ *   slots now hold: p = softmax(z) (softmax of the unbiased logits if
+ *   bias_selection_only), topk_w[t][j] = p[topk_idx[t][j]], divided by their sum over
+ *   j if renormalize.  Other tokens' weights are not touched.
+ * Arguments
+ *   logits     [N][E] float32: moe_route's logits_out (before the bias).
+ *   logit_bias [E] float32 or NULL, as given to moe_route.
+ *   topk_idx   [N][k] int32 (in/out): moe_route's selection for these logits and bias
+ *              (its top-k of z; anything else gives unspecified results).
+ *   topk_w     [N][k] float32 (in/out).
+ *   capacity   < 0: no limit, nothing moves.  max_rounds >= 0 (0: nothing moves;
+ *              more than E - k rounds change nothing).
+ *   n_rerouted [1] int32 or NULL: number of slots moved.
+ *   ws         at least moe_reroute_workspace_size(N, k, E) bytes, 256-byte aligned
+ *              (may be NULL when nothing can move).
+ * 1 <= k <= min(E, 16), E <= MOE_MAX_EXPERTS.  Results are deterministic.
+ */
+size_t moe_reroute_workspace_size(int64_t n_tokens, int32_t k, int32_t n_experts);
+moe_status moe_reroute(void* stream, const float* logits, const float* logit_bias,
+                       int64_t n_tokens, int32_t n_experts, int32_t k, int32_t renormalize,
+                       int32_t bias_selection_only, int64_t capacity, int32_t max_rounds,
+                       int32_t* topk_idx, float* topk_w, int32_t* n_rerouted, void* ws,
+                       size_t ws_bytes);
+
+/*
  * moe_dispatch -- capacity clipping and permutation of tokens by expert.
  * For each expert e the assignments (t, j) with topk_idx[t][j] == e are taken in
  * increasing token order; the first `capacity` are kept and the rest dropped
@@ -217,7 +277,10 @@ typedef struct {
   int32_t bias_selection_only; /* 1: logit_bias steers selection only (see moe_route) */
   moe_act act;
   moe_dtype dtype;        /* x, expert weights, intermediates and output */
-  double capacity_factor; /* alpha; <= 0 means no capacity limit */
+  double capacity_factor; /* alpha; <= 0 means no capacity limit (MOE_CAPACITY_FIXED) */
+  int32_t capacity_rule;  /* moe_capacity_rule_t */
+  int32_t reroute_rounds; /* > 0: re-route overflow (moe_reroute) in up to this many
+                             rounds before the dispatch; 0: drop it */
 } moe_config;
 
 typedef struct {
@@ -251,6 +314,7 @@ typedef struct {
   /* [5]: moe_route's monitor[0..3], then [4] = n_dropped / (N k), the share of
    * assignments cut by the capacity ([MoE-overview] §4.3); 0 for N == 0 */
   float* monitor;
+  int32_t* n_rerouted;     /* [1]: slots moved by re-routing (0 without it) */
   /* Timing markers (hipEvent_t handles owned by the caller, or NULL): stage_events[i]
    * is recorded on the stream at boundary i -- 0 before routing, 1 after routing and
    * its statistics, 2 after dispatch, 3 after the routed first expert layer, 4 after
@@ -262,7 +326,8 @@ typedef struct {
 /*
  * moe_forward -- the whole layer: route, statistics, capacity, dispatch, routed expert
  * FFNs, shared expert FFNs (every token, weight 1), weighted combine.  Equivalent to
- * moe_route, moe_capacity, moe_dispatch, moe_expert_ffn and moe_combine in sequence
+ * moe_route, moe_capacity_rule, moe_reroute (when cfg->reroute_rounds > 0 and the
+ * capacity is finite), moe_dispatch, moe_expert_ffn and moe_combine in sequence
  * ([Why-MoE] §3 MoELayer.forward, [DeepSeek-V2] §2.2-§2.3), with every intermediate in
  * `ws`.  x [N][d] and y [N][d] are in cfg->dtype; y may not alias x.
  * Supported: bf16 with d % 64 == 0 and d_ff % 64 == 0, or float32 with d % 4 == 0 and

@@ -19,6 +19,9 @@ MOE_OK, MOE_ERR_INVALID_ARG, MOE_ERR_UNSUPPORTED, MOE_ERR_WORKSPACE, MOE_ERR_HIP
 MOE_F32, MOE_BF16 = 0, 1
 MOE_ACT_GELU, MOE_ACT_SWIGLU = 0, 1
 MOE_MAX_EXPERTS = 512
+MOE_CAPACITY_FIXED, MOE_CAPACITY_LINEAR, MOE_CAPACITY_LOG = range(3)
+CAPACITY_RULES = {"fixed": MOE_CAPACITY_FIXED, "linear": MOE_CAPACITY_LINEAR,
+                  "log": MOE_CAPACITY_LOG}
 
 
 class MoEError(RuntimeError):
@@ -33,7 +36,8 @@ class MoEConfigC(C.Structure):
                 ("n_experts", C.c_int32), ("top_k", C.c_int32), ("n_shared", C.c_int32),
                 ("renormalize", C.c_int32), ("bias_selection_only", C.c_int32),
                 ("act", C.c_int), ("dtype", C.c_int),
-                ("capacity_factor", C.c_double)]
+                ("capacity_factor", C.c_double), ("capacity_rule", C.c_int32),
+                ("reroute_rounds", C.c_int32)]
 
 
 class MoEWeightsC(C.Structure):
@@ -43,7 +47,7 @@ class MoEWeightsC(C.Structure):
 
 MOE_N_STAGE_EVENTS = 7
 STAT_FIELDS = ("logits", "topk_idx", "topk_w", "sel_count", "prob_mean", "aux", "kept_count",
-               "n_dropped", "expert_offsets", "slot_row", "monitor")
+               "n_dropped", "expert_offsets", "slot_row", "monitor", "n_rerouted")
 
 
 class MoEStatsC(C.Structure):
@@ -56,10 +60,14 @@ _lib = None
 _VP, _I64, _I32, _SZ, _DBL = C.c_void_p, C.c_int64, C.c_int32, C.c_size_t, C.c_double
 _SIGS = {
     "moe_capacity": (_I64, [_I64, _I32, _I32, _DBL]),
+    "moe_capacity_rule": (_I64, [_I64, _I32, _I32, _I32, _DBL]),
     "moe_route_workspace_size": (_SZ, [_I64, _I64, _I32]),
     "moe_route": (C.c_int, [_VP, _VP, C.c_int, _I64, _I64, _VP, _VP, _I32, _I32, _I32, _I32, _VP,
                             _VP, _VP, _VP, _VP, _VP, _VP, _VP, _VP, _SZ]),
     "moe_update_bias": (C.c_int, [_VP, _VP, _I32, _I64, _I32, C.c_float, _VP]),
+    "moe_reroute_workspace_size": (_SZ, [_I64, _I32, _I32]),
+    "moe_reroute": (C.c_int, [_VP, _VP, _VP, _I64, _I32, _I32, _I32, _I32, _I64, _I32, _VP, _VP,
+                              _VP, _VP, _SZ]),
     "moe_dispatch_workspace_size": (_SZ, [_I64, _I32, _I32]),
     "moe_dispatch": (C.c_int, [_VP, _VP, _I64, _I32, _I32, _I64, _VP, C.c_int, _I64, _VP, _VP,
                                _VP, _VP, _VP, _VP, _VP, _SZ]),
@@ -136,6 +144,25 @@ def moe_capacity(n_tokens: int, n_experts: int, k: int, alpha: float) -> int:
     return int(lib().moe_capacity(n_tokens, n_experts, k, float(alpha)))
 
 
+def moe_capacity_rule(n_tokens: int, n_experts: int, k: int, rule: int, alpha: float = 0.0) -> int:
+    return int(lib().moe_capacity_rule(n_tokens, n_experts, k, rule, float(alpha)))
+
+
+def moe_reroute_workspace_size(n_tokens: int, k: int, n_experts: int) -> int:
+    return int(lib().moe_reroute_workspace_size(n_tokens, k, n_experts))
+
+
+def moe_reroute(logits, logit_bias, n_experts: int, k: int, renormalize: bool,
+                bias_selection_only: bool, capacity: int, max_rounds: int, topk_idx, topk_w,
+                n_rerouted, ws, stream=None):
+    n = topk_idx.shape[0]
+    st = lib().moe_reroute(_stream(stream), _ptr(logits), _ptr(logit_bias), n, n_experts, k,
+                           1 if renormalize else 0, 1 if bias_selection_only else 0, capacity,
+                           max_rounds, _ptr(topk_idx), _ptr(topk_w), _ptr(n_rerouted), _ptr(ws),
+                           _ws_bytes(ws))
+    _check("moe_reroute", st)
+
+
 def moe_route_workspace_size(n_tokens: int, d_model: int, n_experts: int) -> int:
     return int(lib().moe_route_workspace_size(n_tokens, d_model, n_experts))
 
@@ -199,10 +226,12 @@ def moe_combine(y_rows, slot_row, topk_w, shared_y, out, stream=None):
 
 
 def make_config(n_tokens, d_model, d_ff, n_experts, top_k, act, dtype, capacity_factor=0.0,
-                n_shared=0, renormalize=True, bias_selection_only=False) -> MoEConfigC:
+                n_shared=0, renormalize=True, bias_selection_only=False,
+                capacity_rule=MOE_CAPACITY_FIXED, reroute_rounds=0) -> MoEConfigC:
     return MoEConfigC(n_tokens, d_model, d_ff, n_experts, top_k, n_shared,
                       1 if renormalize else 0, 1 if bias_selection_only else 0, act, dtype,
-                      float(capacity_factor) if capacity_factor else 0.0)
+                      float(capacity_factor) if capacity_factor else 0.0, capacity_rule,
+                      reroute_rounds)
 
 
 def moe_forward_workspace_size(cfg: MoEConfigC) -> int:

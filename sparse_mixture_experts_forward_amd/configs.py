@@ -33,6 +33,8 @@ class MoEConfig:
     logit_bias: str = "none"  # "none" | "skew4" (+2.0 on experts 0..3) | "uniform0.1"
     renormalize: bool = True
     bias_selection_only: bool = False  # the logit bias steers selection only (V3 scheme)
+    capacity_rule: str = "fixed"  # "fixed" (alpha) | "linear" | "log" (batch-dependent)
+    reroute_rounds: int = 0  # > 0: overflow goes on to the next-best experts with room
 
     def with_tokens(self, n: int) -> "MoEConfig":
         return replace(self, n_tokens=n)

@@ -126,6 +126,31 @@ size_t route_ws(int64_t n, int64_t d, int32_t e) {
   return c.used;
 }
 
+// Overflow re-routing workspace; with base == nullptr only measures.
+moe::RerouteWs reroute_layout(Carve& c, int64_t n, int32_t k, int32_t e) {
+  const moe::DispatchGrid g = moe::dispatch_grid(n, k);
+  moe::RerouteWs w{};
+  w.blk_hist = c.take<int32_t>(g.n_blocks * e);
+  w.blk_base = c.take<int32_t>(g.n_blocks * e);
+  w.kept = c.take<int32_t>(e);
+  w.room = c.take<int32_t>(e);
+  w.state = c.take<uint8_t>(n * k);
+  w.thr_z = c.take<float>(n);
+  w.thr_e = c.take<int32_t>(n);
+  w.props = c.take<int32_t>(n * k);
+  return w;
+}
+
+size_t reroute_ws(int64_t n, int32_t k, int32_t e) {
+  Carve c(nullptr);
+  reroute_layout(c, n, k, e);
+  return c.used;
+}
+
+// Rounds beyond E - k cannot move anything more: each round a token proposes to at
+// least one expert it has not held, or has none left.
+int32_t clamp_rounds(int32_t rounds, int32_t e, int32_t k) { return std::min(rounds, e - k); }
+
 size_t dispatch_ws(int64_t n, int32_t k, int32_t e) {
   Carve c(nullptr);
   const moe::DispatchGrid g = moe::dispatch_grid(n, k);
@@ -257,6 +282,29 @@ moe_status side_stream(SideStream** out) {
   return MOE_OK;
 }
 
+// Batch-dependent capacities: [MoE-2pct] §5.3 (factor 1 + 0.5 min(1, N/256) inside
+// floor(kN/E * factor), evaluated exactly in integers) and §3.1's tip (alpha =
+// 1 + 0.5 log2(N/256), held at 1 for N <= 256, in floor(floor(kN/E) * alpha)).
+int64_t capacity_linear(int64_t n, int32_t e, int32_t k) {
+  const int64_t kn = static_cast<int64_t>(k) * n;
+  if (n >= 256) return (3 * kn) / (2 * static_cast<int64_t>(e));
+  return (kn * (512 + n)) / (512 * static_cast<int64_t>(e));
+}
+
+int64_t capacity_log(int64_t n, int32_t e, int32_t k) {
+  const int64_t base = (static_cast<int64_t>(k) * n) / e;
+  const double alpha = n <= 256 ? 1.0 : 1.0 + 0.5 * std::log2(static_cast<double>(n) / 256.0);
+  return static_cast<int64_t>(std::floor(static_cast<double>(base) * alpha));
+}
+
+int64_t capacity_of(int64_t n, int32_t e, int32_t k, double alpha);
+
+int64_t capacity_by_rule(int64_t n, int32_t e, int32_t k, int32_t rule, double alpha) {
+  if (rule == MOE_CAPACITY_LINEAR) return capacity_linear(n, e, k);
+  if (rule == MOE_CAPACITY_LOG) return capacity_log(n, e, k);
+  return capacity_of(n, e, k, alpha);
+}
+
 int64_t capacity_of(int64_t n, int32_t e, int32_t k, double alpha) {
   if (!(alpha > 0.0)) return -1;
   const int64_t base = (static_cast<int64_t>(k) * n) / e;
@@ -272,8 +320,9 @@ int64_t max_rows_of(int64_t n, int32_t e, int32_t k, int64_t cap) {
 
 struct ForwardLayout {
   int32_t *idx, *sel, *offsets, *row_token, *slot_row, *kept, *dropped;
-  float *w, *pm, *aux;
+  float *w, *pm, *aux, *logits;
   void *route_ws, *dispatch_ws, *x_perm, *h, *y_rows, *h_sh, *y_sh;
+  moe::RerouteWs rr;
   size_t used;
 };
 
@@ -283,7 +332,7 @@ ForwardLayout forward_layout(const moe_config& c, void* ws) {
   const int64_t n = c.n_tokens, nk = c.n_tokens * c.top_k;
   const int32_t e = c.n_experts;
   const size_t es = elem_size(c.dtype);
-  const int64_t cap = capacity_of(n, e, c.top_k, c.capacity_factor);
+  const int64_t cap = capacity_by_rule(n, e, c.top_k, c.capacity_rule, c.capacity_factor);
   const int64_t R = max_rows_of(n, e, c.top_k, cap);
   L.idx = cv.take<int32_t>(nk);
   L.w = cv.take<float>(nk);
@@ -297,6 +346,10 @@ ForwardLayout forward_layout(const moe_config& c, void* ws) {
   L.dropped = cv.take<int32_t>(1);
   L.route_ws = cv.take<char>(route_ws(n, c.d_model, e));
   L.dispatch_ws = cv.take<char>(dispatch_ws(n, c.top_k, e));
+  if (c.reroute_rounds > 0 && cap >= 0) {
+    L.logits = cv.take<float>(n * e);
+    L.rr = reroute_layout(cv, n, c.top_k, e);
+  }
   L.x_perm = cv.take<char>(R * c.d_model * es);
   L.h = cv.take<char>(R * c.d_ff * es);
   L.y_rows = cv.take<char>(R * c.d_model * es);
@@ -316,6 +369,9 @@ moe_status check_config(const moe_config* c) {
   if (c->top_k < 1 || c->top_k > c->n_experts) return fail(MOE_ERR_INVALID_ARG, "need 1 <= top_k <= n_experts");
   if (c->top_k > 16) return fail(MOE_ERR_UNSUPPORTED, "top_k > 16");
   if (c->n_shared < 0 || c->n_shared > 8) return fail(MOE_ERR_UNSUPPORTED, "n_shared must be 0..8");
+  if (c->capacity_rule < MOE_CAPACITY_FIXED || c->capacity_rule > MOE_CAPACITY_LOG)
+    return fail(MOE_ERR_INVALID_ARG, "unknown capacity rule");
+  if (c->reroute_rounds < 0) return fail(MOE_ERR_INVALID_ARG, "reroute_rounds < 0");
   MOE_TRY(check_ffn_shape(c->dtype, c->act, c->d_model, c->d_ff));
   if (c->n_tokens * static_cast<int64_t>(c->top_k) > INT32_MAX / 2)
     return fail(MOE_ERR_UNSUPPORTED, "n_tokens * top_k too large");
@@ -347,6 +403,52 @@ int64_t moe_capacity(int64_t n_tokens, int32_t n_experts, int32_t k, double alph
     return -1;
   }
   return capacity_of(n_tokens, n_experts, k, alpha);
+}
+
+int64_t moe_capacity_rule(int64_t n_tokens, int32_t n_experts, int32_t k, int32_t rule,
+                          double alpha) {
+  if (n_tokens < 0 || n_experts < 1 || k < 1 || rule < MOE_CAPACITY_FIXED || rule > MOE_CAPACITY_LOG) {
+    fail(MOE_ERR_INVALID_ARG, "moe_capacity_rule: need n_tokens >= 0, n_experts >= 1, k >= 1 and a known rule");
+    return -1;
+  }
+  return capacity_by_rule(n_tokens, n_experts, k, rule, alpha);
+}
+
+size_t moe_reroute_workspace_size(int64_t n_tokens, int32_t k, int32_t n_experts) {
+  if (n_tokens < 0 || k < 1 || n_experts < 1) return 0;
+  return reroute_ws(n_tokens, k, n_experts);
+}
+
+moe_status moe_reroute(void* stream, const float* logits, const float* logit_bias,
+                       int64_t n_tokens, int32_t n_experts, int32_t k, int32_t renormalize,
+                       int32_t bias_selection_only, int64_t capacity, int32_t max_rounds,
+                       int32_t* topk_idx, float* topk_w, int32_t* n_rerouted, void* ws,
+                       size_t ws_bytes) {
+  if (n_tokens < 0) return fail(MOE_ERR_INVALID_ARG, "n_tokens < 0");
+  if (n_experts < 1) return fail(MOE_ERR_INVALID_ARG, "n_experts < 1");
+  if (n_experts > MOE_MAX_EXPERTS) return fail(MOE_ERR_UNSUPPORTED, "n_experts > %d", MOE_MAX_EXPERTS);
+  if (k < 1 || k > n_experts) return fail(MOE_ERR_INVALID_ARG, "need 1 <= k <= n_experts");
+  if (k > 16) return fail(MOE_ERR_UNSUPPORTED, "k > 16");
+  if (max_rounds < 0) return fail(MOE_ERR_INVALID_ARG, "max_rounds < 0");
+  if (n_tokens * static_cast<int64_t>(k) > INT32_MAX / 2) return fail(MOE_ERR_UNSUPPORTED, "n_tokens too large");
+  if (n_tokens * static_cast<int64_t>(n_experts) > INT32_MAX) return fail(MOE_ERR_UNSUPPORTED, "n_tokens too large");
+  const bool active = n_tokens > 0 && capacity >= 0 && max_rounds > 0;
+  if (active && (!logits || !topk_idx || !topk_w))
+    return fail(MOE_ERR_INVALID_ARG, "logits, topk_idx and topk_w are required");
+  const size_t need = reroute_ws(n_tokens, k, n_experts);
+  if (active) {
+    if (ws_bytes < need) return fail(MOE_ERR_WORKSPACE, "moe_reroute needs %zu workspace bytes", need);
+    if (!ws) return fail(MOE_ERR_INVALID_ARG, "ws is NULL");
+    MOE_TRY(check_aligned(ws, kAlign, "ws"));
+  }
+  Carve c(active ? ws : nullptr);
+  const moe::RerouteWs w = reroute_layout(c, n_tokens, k, n_experts);
+  return hip_check(moe::launch_reroute(static_cast<hipStream_t>(stream), logits, logit_bias,
+                                       n_tokens, k, n_experts, renormalize ? 1 : 0,
+                                       bias_selection_only ? 1 : 0, active ? capacity : -1,
+                                       active ? clamp_rounds(max_rounds, n_experts, k) : 0,
+                                       topk_idx, topk_w, n_rerouted, w),
+                   "re-routing launch");
 }
 
 size_t moe_route_workspace_size(int64_t n_tokens, int64_t d_model, int32_t n_experts) {
@@ -512,6 +614,9 @@ moe_status moe_forward(void* stream, const moe_config* cfg, const moe_weights* w
   int32_t* offsets = o.expert_offsets ? o.expert_offsets : L.offsets;
   int32_t* slot_row = o.slot_row ? o.slot_row : L.slot_row;
   int32_t* dropped = o.n_dropped ? o.n_dropped : L.dropped;
+  const int64_t cap = capacity_by_rule(n, e, k, c.capacity_rule, c.capacity_factor);
+  const bool reroute = c.reroute_rounds > 0 && cap >= 0 && n > 0;
+  float* logits = (reroute && !o.logits) ? L.logits : o.logits;
 
   auto mark = [&](int i) -> moe_status {
     if (!o.stage_events[i]) return MOE_OK;
@@ -521,12 +626,17 @@ moe_status moe_forward(void* stream, const moe_config* cfg, const moe_weights* w
   MOE_TRY(mark(0));
   // a1-a3: router product, gate, statistics
   MOE_TRY(run_route(st, x, c.dtype, n, c.d_model, w->w_router, w->logit_bias, e, k,
-                    gate_flags(c.renormalize, c.bias_selection_only), nullptr, o.logits, idx,
+                    gate_flags(c.renormalize, c.bias_selection_only), nullptr, logits, idx,
                     tw, o.sel_count,
                     o.prob_mean, o.aux, o.monitor, L.route_ws));
   MOE_TRY(mark(1));
-  // a4-a5: capacity and permutation
-  const int64_t cap = capacity_of(n, e, k, c.capacity_factor);
+  // a4-a5: capacity (slots over it re-routed first if asked) and permutation
+  if (reroute || o.n_rerouted)
+    MOE_TRY(hip_check(moe::launch_reroute(st, logits, w->logit_bias, n, k, e, c.renormalize ? 1 : 0,
+                                          c.bias_selection_only ? 1 : 0, reroute ? cap : -1,
+                                          reroute ? clamp_rounds(c.reroute_rounds, e, k) : 0,
+                                          idx, tw, o.n_rerouted, L.rr),
+                      "re-routing launch"));
   MOE_TRY(run_dispatch(st, idx, n, k, e, cap, x, c.d_model * static_cast<int64_t>(es), offsets,
                        L.row_token, slot_row, o.kept_count, dropped, L.x_perm,
                        L.dispatch_ws));

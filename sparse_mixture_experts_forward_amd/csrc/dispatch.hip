@@ -40,6 +40,43 @@ __global__ __launch_bounds__(kThreads) void dispatch_hist_kernel(
   for (int e = threadIdx.x; e < E; e += kThreads) blk_hist[e * n_blocks + blockIdx.x] = h[e];
 }
 
+// Ranks every assignment of the chunk [q_begin, q_end) among the chunk's assignments
+// to the same expert, in index order, continuing the per-expert counters `cnt` (LDS,
+// E entries, advanced by the chunk's counts).  Run by one whole wave: lanes that share
+// an expert id are grouped by ballot (the lowest lane leads), so no atomics decide an
+// order.  Calls f(q, e, r) for every q of the chunk, with e = ids[q] and r its rank,
+// or e = -1 and r = 0 when ids[q] is not an expert.  f runs per lane and must not
+// contain wave-level operations.
+template <typename F>
+__device__ __forceinline__ void chunk_ranks(const int32_t* __restrict__ ids, int64_t q_begin,
+                                            int64_t q_end, int E, int32_t* cnt, F&& f) {
+  const int lane = lane_id();
+  for (int64_t q0 = q_begin; q0 < q_end; q0 += kWave) {
+    const int64_t q = q0 + lane;
+    const bool valid = q < q_end;
+    const int e = valid ? ids[q] : -1;
+    const bool ve = valid && e >= 0 && e < E;
+    uint64_t rem = __ballot(ve);
+    int my_rank = 0, my_leader = 0, lead_base = 0;
+    while (rem) {
+      const int leader = __ffsll(static_cast<unsigned long long>(rem)) - 1;
+      const int el = __shfl(e, leader, kWave);
+      const uint64_t grp = __ballot(ve && e == el);
+      if (ve && e == el) {
+        my_rank = __popcll(grp & lanemask_lt());
+        my_leader = leader;
+      }
+      if (lane == leader) {
+        lead_base = cnt[el];
+        cnt[el] = lead_base + __popcll(grp);
+      }
+      rem &= ~grp;
+    }
+    const int base = __shfl(lead_base, my_leader, kWave);
+    if (valid) f(q, ve ? e : -1, ve ? base + my_rank : 0);
+  }
+}
+
 // Workgroup-wide inclusive scan of one value per thread (4 waves, wave sums through
 // LDS); `total` receives the sum over the workgroup.
 __device__ __forceinline__ int block_incl_scan(int v, int* wsum, int& total) {
@@ -59,10 +96,12 @@ __device__ __forceinline__ int block_incl_scan(int v, int* wsum, int& total) {
 }
 
 // One workgroup per expert: exclusive scan of its chunk counts -> blk_base, and the
-// kept count min(total, capacity).
+// kept count min(total, limit).  Without `room` the limit is `capacity` (< 0: none).
+// With `room` (re-routing) the limit is `capacity` if >= 0, else room[e], and room[e]
+// becomes limit - kept.
 __global__ __launch_bounds__(kThreads) void dispatch_scan_kernel(
     const int32_t* __restrict__ blk_hist, int64_t n_blocks, int64_t capacity,
-    int32_t* __restrict__ blk_base, int32_t* __restrict__ kept) {
+    int32_t* __restrict__ blk_base, int32_t* __restrict__ kept, int32_t* __restrict__ room) {
   __shared__ int wsum[kThreads / kWave];
   const int e = blockIdx.x;
   int running = 0;
@@ -75,8 +114,10 @@ __global__ __launch_bounds__(kThreads) void dispatch_scan_kernel(
     running += chunk_total;
   }
   if (threadIdx.x == kThreads - 1) {
-    const int64_t kc = (capacity >= 0 && running > capacity) ? capacity : running;
+    const int64_t lim = (room && capacity < 0) ? room[e] : capacity;
+    const int64_t kc = (lim >= 0 && running > lim) ? lim : running;
     kept[e] = static_cast<int32_t>(kc);
+    if (room) room[e] = static_cast<int32_t>(lim - kc);
   }
 }
 
@@ -119,44 +160,19 @@ __global__ __launch_bounds__(kThreads) void dispatch_scatter_kernel(
   const int64_t q_begin = t0 * k, q_end = t1 * k;
 
   if (threadIdx.x < kWave) {
-    const int lane = lane_id();
-    for (int64_t q0 = q_begin; q0 < q_end; q0 += kWave) {
-      const int64_t q = q0 + lane;
-      const bool valid = q < q_end;
-      const int e = valid ? topk_idx[q] : -1;
-      const bool ve = valid && e >= 0 && e < E;
-      // group the lanes by expert id; the lowest lane of a group is its leader
-      uint64_t rem = __ballot(ve);
-      int my_rank = 0, my_leader = 0, lead_base = 0;
-      while (rem) {
-        const int leader = __ffsll(static_cast<unsigned long long>(rem)) - 1;
-        const int el = __shfl(e, leader, kWave);
-        const uint64_t grp = __ballot(ve && e == el);
-        if (ve && e == el) {
-          my_rank = __popcll(grp & lanemask_lt());
-          my_leader = leader;
+    const int32_t* base_e = blk_base + blockIdx.x;
+    chunk_ranks(topk_idx, q_begin, q_end, E, cnt, [&](int64_t q, int e, int r_in) {
+      int32_t r = -1;
+      if (e >= 0) {
+        const int64_t rank = static_cast<int64_t>(base_e[e * n_blocks]) + r_in;
+        if (capacity < 0 || rank < capacity) {
+          r = expert_offsets[e] + static_cast<int32_t>(rank);
+          row_token[r] = static_cast<int32_t>(q / k);
         }
-        if (lane == leader) {
-          lead_base = cnt[el];
-          cnt[el] = lead_base + __popcll(grp);
-        }
-        rem &= ~grp;
       }
-      const int base = __shfl(lead_base, my_leader, kWave);
-      if (valid) {
-        int32_t r = -1;
-        if (ve) {
-          const int64_t rank =
-              static_cast<int64_t>(blk_base[e * n_blocks + blockIdx.x]) + base + my_rank;
-          if (capacity < 0 || rank < capacity) {
-            r = expert_offsets[e] + static_cast<int32_t>(rank);
-            row_token[r] = static_cast<int32_t>(q / k);
-          }
-        }
-        slot_row[q] = r;
-        srow[q - q_begin] = r;
-      }
-    }
+      slot_row[q] = r;
+      srow[q - q_begin] = r;
+    });
   }
   if (x_perm == nullptr) return;
   __syncthreads();
@@ -172,6 +188,195 @@ __global__ __launch_bounds__(kThreads) void dispatch_scatter_kernel(
       const int32_t r = srow[tt * k + j];
       if (r >= 0) *reinterpret_cast<uint4*>(x_perm + static_cast<int64_t>(r) * row_bytes + c * 16) = v;
     }
+  }
+}
+
+// ---------------------------------------------------------------- overflow re-routing
+// ([MoE-2pct] §3.1: an expert's assignments beyond its capacity go on to the next-best
+// expert.)  Rounds over the dispatch's token chunks.  Slot states: 0 placed on its
+// first choice, 1 unplaced, 2 placed after moving, 3 unplaced with no expert left.
+// Every token keeps a threshold (z, e): the last expert it proposed to, or its last
+// selection; its candidates are the experts after the threshold in its order of
+// preference (descending z = logits + bias, lower index first on ties).  Experts held
+// by the token are never after the threshold.
+constexpr uint8_t kPlaced = 0, kUnplaced = 1, kMoved = 2, kExhausted = 3;
+
+// Round 0 (first != 0, props = topk_idx): a slot ranked below kept[e] stays placed,
+// the others are unplaced; every token's threshold becomes its last selection.
+// Later rounds (props = this round's proposals, -1 for none): a proposal ranked below
+// kept[e] (the number of proposals expert e accepts) moves its slot to e.
+__global__ __launch_bounds__(kThreads) void reroute_accept_kernel(
+    const int32_t* props, int64_t n, int k, int E, int64_t tpb, int64_t n_blocks,
+    const int32_t* __restrict__ blk_base, const int32_t* __restrict__ kept, int first,
+    const float* __restrict__ logits, const float* __restrict__ bias,
+    int32_t* topk_idx /* = props in round 0 */, uint8_t* __restrict__ state,
+    float* __restrict__ thr_z, int32_t* __restrict__ thr_e, int32_t* __restrict__ n_moved) {
+  __shared__ int32_t cnt[kMaxExperts];
+  for (int e = threadIdx.x; e < E; e += kThreads) cnt[e] = 0;
+  __syncthreads();
+  if (threadIdx.x >= kWave) return;
+  const int64_t t0 = static_cast<int64_t>(blockIdx.x) * tpb;
+  const int64_t t1 = min(n, t0 + tpb);
+  const int32_t* base_e = blk_base + blockIdx.x;
+  int moved = 0;
+  chunk_ranks(props, t0 * k, t1 * k, E, cnt, [&](int64_t q, int e, int r) {
+    const bool take = e >= 0 && base_e[e * n_blocks] + r < kept[e];
+    if (first) {
+      state[q] = take ? kPlaced : kUnplaced;
+      const int64_t t = q / k;
+      if (q - t * k == k - 1 && e >= 0) {
+        thr_e[t] = e;
+        thr_z[t] = logits[t * E + e] + (bias ? bias[e] : 0.f);
+      }
+    } else if (take) {
+      topk_idx[q] = e;
+      state[q] = kMoved;
+      ++moved;
+    }
+  });
+  if (first) {
+    if (blockIdx.x == 0 && threadIdx.x == 0 && n_moved) n_moved[0] = 0;
+    return;
+  }
+  const float tot = wave_sum(static_cast<float>(moved));  // < 2^24 per chunk: exact
+  if (threadIdx.x == 0 && tot > 0.f && n_moved) atomicAdd(n_moved, static_cast<int32_t>(tot));
+}
+
+// One round's proposals.  Experts with room at the round's start are open.  Each
+// token with unplaced slots takes, slot by slot, its best open candidate after its
+// threshold (a wave per token, VPL experts per lane), and the threshold moves to the
+// last one taken; slots left without a candidate are exhausted for good (the open set
+// only shrinks).  The chunk's per-expert proposal counts go to blk_hist[e][chunk].
+template <int VPL>
+__global__ __launch_bounds__(kThreads) void reroute_propose_kernel(
+    const float* __restrict__ logits, const float* __restrict__ bias, int64_t n, int k, int E,
+    int64_t tpb, int64_t n_blocks, const int32_t* __restrict__ room,
+    uint8_t* __restrict__ state, float* __restrict__ thr_z, int32_t* __restrict__ thr_e,
+    int32_t* __restrict__ props, int32_t* __restrict__ blk_hist) {
+  __shared__ int32_t open_e[kMaxExperts];
+  __shared__ int32_t h[kMaxExperts];
+  for (int e = threadIdx.x; e < E; e += kThreads) {
+    open_e[e] = room[e] > 0;
+    h[e] = 0;
+  }
+  __syncthreads();
+  const int lane = lane_id(), wave = threadIdx.x / kWave;
+  const int64_t t0 = static_cast<int64_t>(blockIdx.x) * tpb;
+  const int64_t t1 = min(n, t0 + tpb);
+  for (int64_t t = t0 + wave; t < t1; t += kThreads / kWave) {
+    const int64_t q0 = t * k;
+    const int my_state = lane < k ? state[q0 + lane] : kPlaced;
+    uint64_t rem = __ballot(my_state == kUnplaced);
+    int my_prop = -1;
+    if (rem) {
+      float tz = thr_z[t];
+      int te = thr_e[t];
+      float z[VPL];
+      bool ok[VPL];
+#pragma unroll
+      for (int i = 0; i < VPL; ++i) {
+        const int e = lane + kWave * i;
+        ok[i] = false;
+        z[i] = 0.f;
+        if (e < E) {
+          z[i] = logits[t * E + e] + (bias ? bias[e] : 0.f);
+          ok[i] = open_e[e] && (z[i] < tz || (z[i] == tz && e > te));
+        }
+      }
+      while (rem) {
+        bool have = false;
+        float bz = 0.f;
+        int be = 0;
+#pragma unroll
+        for (int i = 0; i < VPL; ++i) {
+          const int e = lane + kWave * i;
+          if (ok[i] && (!have || z[i] > bz)) {  // e ascends with i: ties keep the first
+            have = true;
+            bz = z[i];
+            be = e;
+          }
+        }
+#pragma unroll
+        for (int m = 1; m < kWave; m <<= 1) {
+          const float oz = __shfl_xor(bz, m, kWave);
+          const int oe = __shfl_xor(be, m, kWave);
+          const bool oh = __shfl_xor(static_cast<int>(have), m, kWave) != 0;
+          if (oh && (!have || oz > bz || (oz == bz && oe < be))) {
+            have = true;
+            bz = oz;
+            be = oe;
+          }
+        }
+        if (!have) break;  // wave-uniform
+        const int j = __ffsll(static_cast<unsigned long long>(rem)) - 1;
+        rem &= rem - 1;
+        if (lane == j) my_prop = be;
+#pragma unroll
+        for (int i = 0; i < VPL; ++i)
+          if (lane + kWave * i == be) ok[i] = false;
+        tz = bz;
+        te = be;
+      }
+      if (lane == 0) {
+        thr_z[t] = tz;
+        thr_e[t] = te;
+      }
+      if (lane < k && ((rem >> lane) & 1ull)) state[q0 + lane] = kExhausted;
+      if (my_prop >= 0) atomicAdd(&h[my_prop], 1);  // LDS counts; order is not used
+    }
+    if (lane < k) props[q0 + lane] = my_prop;
+  }
+  __syncthreads();
+  for (int e = threadIdx.x; e < E; e += kThreads) blk_hist[e * n_blocks + blockIdx.x] = h[e];
+}
+
+__global__ void reroute_zero_kernel(int32_t* __restrict__ n_moved) {
+  if (threadIdx.x == 0) n_moved[0] = 0;
+}
+
+// Gate weights of the tokens that moved a slot: the probabilities of the experts the
+// slots now hold (softmax of z, or of the unbiased logits with sel_only), renormalised
+// over those k experts if renorm.  One wave per token.
+template <int VPL>
+__global__ __launch_bounds__(kThreads) void reroute_weights_kernel(
+    const float* __restrict__ logits, const float* __restrict__ bias, int64_t n, int k, int E,
+    int renorm, int sel_only, const uint8_t* __restrict__ state,
+    const int32_t* __restrict__ topk_idx, float* __restrict__ topk_w) {
+  const int lane = lane_id();
+  const int64_t waves = static_cast<int64_t>(gridDim.x) * (kThreads / kWave);
+  const float* b = sel_only ? nullptr : bias;
+  for (int64_t t = static_cast<int64_t>(blockIdx.x) * (kThreads / kWave) + threadIdx.x / kWave;
+       t < n; t += waves) {
+    const int64_t q0 = t * k;
+    const int my_state = lane < k ? state[q0 + lane] : kPlaced;
+    if (__ballot(my_state == kMoved) == 0) continue;
+    const float* l = logits + t * E;
+    float sj = -INFINITY;
+    if (lane < k) {
+      const int e = topk_idx[q0 + lane];
+      sj = l[e] + (b ? b[e] : 0.f);
+    }
+    float m, denom;
+    if (renorm) {
+      m = wave_max(sj);
+      denom = wave_sum(lane < k ? expf(sj - m) : 0.f);
+    } else {
+      float s[VPL];
+      float mx = -INFINITY;
+#pragma unroll
+      for (int i = 0; i < VPL; ++i) {
+        const int e = lane + kWave * i;
+        s[i] = e < E ? l[e] + (b ? b[e] : 0.f) : -INFINITY;
+        mx = fmaxf(mx, s[i]);
+      }
+      m = wave_max(mx);
+      float acc = 0.f;
+#pragma unroll
+      for (int i = 0; i < VPL; ++i)
+        if (lane + kWave * i < E) acc += expf(s[i] - m);
+      denom = wave_sum(acc);
+    }
+    if (lane < k) topk_w[q0 + lane] = expf(sj - m) / denom;
   }
 }
 
@@ -204,7 +409,7 @@ hipError_t launch_dispatch(hipStream_t st, const int32_t* topk_idx, int64_t n, i
     if (err != hipSuccess) return err;
   }
   hipLaunchKernelGGL(dispatch_scan_kernel, dim3(static_cast<unsigned>(e)), dim3(kThreads), 0, st,
-                     blk_hist, g.n_blocks, capacity, blk_base, kept_tmp);
+                     blk_hist, g.n_blocks, capacity, blk_base, kept_tmp, nullptr);
   hipError_t err = hipGetLastError();
   if (err != hipSuccess) return err;
   hipLaunchKernelGGL(dispatch_offsets_kernel, dim3(1), dim3(kThreads), 0, st, kept_tmp, e, n * k,
@@ -215,6 +420,67 @@ hipError_t launch_dispatch(hipStream_t st, const int32_t* topk_idx, int64_t n, i
                      dim3(kThreads), 0, st, topk_idx, n, k, e, g.tokens_per_block,
                      g.n_blocks, capacity, blk_base, expert_offsets, row_token, slot_row,
                      static_cast<const uint8_t*>(x), row_bytes, static_cast<uint8_t*>(x_perm));
+  return hipGetLastError();
+}
+
+hipError_t launch_reroute(hipStream_t st, const float* logits, const float* bias, int64_t n,
+                          int k, int e, int renorm, int sel_only, int64_t capacity, int rounds,
+                          int32_t* topk_idx, float* topk_w, int32_t* n_moved,
+                          const RerouteWs& w) {
+  const DispatchGrid g = dispatch_grid(n, k);
+  if (g.n_blocks == 0 || capacity < 0 || rounds <= 0) {  // nothing can move
+    if (n_moved) hipLaunchKernelGGL(reroute_zero_kernel, dim3(1), dim3(kWave), 0, st, n_moved);
+    return hipGetLastError();
+  }
+  const dim3 grid(static_cast<unsigned>(g.n_blocks)), blk(kThreads);
+  const int64_t tpb = g.tokens_per_block;
+  // round 0: the plain capacity rule
+  hipLaunchKernelGGL(dispatch_hist_kernel, grid, blk, 0, st, topk_idx, n, k, e, tpb, g.n_blocks,
+                     w.blk_hist);
+  hipError_t err = hipGetLastError();
+  if (err != hipSuccess) return err;
+  hipLaunchKernelGGL(dispatch_scan_kernel, dim3(static_cast<unsigned>(e)), blk, 0, st, w.blk_hist,
+                     g.n_blocks, capacity, w.blk_base, w.kept, w.room);
+  if ((err = hipGetLastError()) != hipSuccess) return err;
+  hipLaunchKernelGGL(reroute_accept_kernel, grid, blk, 0, st, topk_idx, n, k, e, tpb, g.n_blocks,
+                     w.blk_base, w.kept, 1, logits, bias, topk_idx, w.state, w.thr_z, w.thr_e,
+                     n_moved);
+  if ((err = hipGetLastError()) != hipSuccess) return err;
+  const int vpl = (e + kWave - 1) / kWave;
+  for (int r = 0; r < rounds; ++r) {
+    switch (vpl) {
+#define MOE_PROPOSE(V)                                                                        \
+  case V:                                                                                     \
+    hipLaunchKernelGGL(reroute_propose_kernel<V>, grid, blk, 0, st, logits, bias, n, k, e, tpb, \
+                       g.n_blocks, w.room, w.state, w.thr_z, w.thr_e, w.props, w.blk_hist);   \
+    break;
+      MOE_PROPOSE(1) MOE_PROPOSE(2) MOE_PROPOSE(3) MOE_PROPOSE(4)
+      MOE_PROPOSE(5) MOE_PROPOSE(6) MOE_PROPOSE(7) MOE_PROPOSE(8)
+#undef MOE_PROPOSE
+      default: return hipErrorInvalidValue;
+    }
+    if ((err = hipGetLastError()) != hipSuccess) return err;
+    hipLaunchKernelGGL(dispatch_scan_kernel, dim3(static_cast<unsigned>(e)), blk, 0, st,
+                       w.blk_hist, g.n_blocks, int64_t{-1}, w.blk_base, w.kept, w.room);
+    if ((err = hipGetLastError()) != hipSuccess) return err;
+    hipLaunchKernelGGL(reroute_accept_kernel, grid, blk, 0, st, w.props, n, k, e, tpb,
+                       g.n_blocks, w.blk_base, w.kept, 0, logits, bias, topk_idx, w.state,
+                       w.thr_z, w.thr_e, n_moved);
+    if ((err = hipGetLastError()) != hipSuccess) return err;
+  }
+  const int64_t wblocks = std::min<int64_t>((n + 3) / 4, 2048);
+  switch (vpl) {
+#define MOE_WEIGHTS(V)                                                                       \
+  case V:                                                                                    \
+    hipLaunchKernelGGL(reroute_weights_kernel<V>, dim3(static_cast<unsigned>(wblocks)), blk, \
+                       0, st, logits, bias, n, k, e, renorm, sel_only, w.state, topk_idx,    \
+                       topk_w);                                                              \
+    break;
+    MOE_WEIGHTS(1) MOE_WEIGHTS(2) MOE_WEIGHTS(3) MOE_WEIGHTS(4)
+    MOE_WEIGHTS(5) MOE_WEIGHTS(6) MOE_WEIGHTS(7) MOE_WEIGHTS(8)
+#undef MOE_WEIGHTS
+    default: return hipErrorInvalidValue;
+  }
   return hipGetLastError();
 }
 

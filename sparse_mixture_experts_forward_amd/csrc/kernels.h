@@ -85,6 +85,23 @@ hipError_t launch_dispatch(hipStream_t st, const int32_t* topk_idx, int64_t n, i
                            int32_t* kept_count, int32_t* n_dropped, void* x_perm,
                            int32_t* blk_hist, int32_t* blk_base, int32_t* kept_tmp);
 
+// Workspace of the overflow re-routing (all device arrays): blk_hist / blk_base
+// [E][n_blocks] (dispatch_grid), kept / room [E], state [N*k], thr_z / thr_e [N],
+// props [N*k].
+struct RerouteWs {
+  int32_t *blk_hist, *blk_base, *kept, *room;
+  uint8_t* state;
+  float* thr_z;
+  int32_t *thr_e, *props;
+};
+// Re-routes the slots over `capacity` (>= 0) in up to `rounds` rounds: rewrites
+// topk_idx of the moved slots and topk_w of their tokens; n_moved[0] (optional)
+// receives the number of moved slots.  logits [N][E] float32 are the router's.
+hipError_t launch_reroute(hipStream_t st, const float* logits, const float* bias, int64_t n,
+                          int k, int e, int renorm, int sel_only, int64_t capacity, int rounds,
+                          int32_t* topk_idx, float* topk_w, int32_t* n_moved,
+                          const RerouteWs& w);
+
 // ---------------------------------------------------------------- grouped GEMM
 enum Epilogue { EPI_NONE = 0, EPI_GELU = 1, EPI_SWIGLU = 2 };
 

@@ -49,11 +49,13 @@ class MoELayer:
         c = self.cfg
         return B.make_config(n_tokens, c.d_model, c.d_ff, c.n_experts, c.top_k, _act(c.act),
                              B.MOE_BF16 if c.dtype == "bf16" else B.MOE_F32,
-                             c.alpha or 0.0, c.n_shared, c.renormalize, c.bias_selection_only)
+                             c.alpha or 0.0, c.n_shared, c.renormalize, c.bias_selection_only,
+                             B.CAPACITY_RULES[c.capacity_rule], c.reroute_rounds)
 
     def capacity(self, n_tokens: int) -> int:
         c = self.cfg
-        return B.moe_capacity(n_tokens, c.n_experts, c.top_k, c.alpha or 0.0)
+        return B.moe_capacity_rule(n_tokens, c.n_experts, c.top_k,
+                                   B.CAPACITY_RULES[c.capacity_rule], c.alpha or 0.0)
 
     def _workspace(self, n_tokens: int) -> Optional[torch.Tensor]:
         if self._ws_key != n_tokens:
@@ -76,7 +78,8 @@ class MoELayer:
             n_dropped=torch.empty(1, dtype=i32, device=dev),
             expert_offsets=torch.empty(c.n_experts + 1, dtype=i32, device=dev),
             slot_row=torch.empty((n_tokens, c.top_k), dtype=i32, device=dev),
-            monitor=torch.empty(5, dtype=f32, device=dev))
+            monitor=torch.empty(5, dtype=f32, device=dev),
+            n_rerouted=torch.empty(1, dtype=i32, device=dev))
 
     def forward(self, x: torch.Tensor, y: Optional[torch.Tensor] = None,
                 stats: Optional[dict] = None, stream=None, stage_events=None) -> torch.Tensor:
@@ -102,6 +105,20 @@ class MoELayer:
                     s["sel_count"], s["prob_mean"], s["aux"], ws, n_tokens=n, stream=stream,
                     bias_selection_only=c.bias_selection_only, monitor=s["monitor"])
         return s
+
+    def reroute(self, logits: torch.Tensor, topk_idx: torch.Tensor, topk_w: torch.Tensor,
+                capacity: Optional[int] = None, rounds: Optional[int] = None,
+                stream=None) -> torch.Tensor:
+        """Overflow re-routing in place on topk_idx / topk_w; returns n_rerouted [1]."""
+        c = self.cfg
+        n, k = topk_idx.shape
+        cap = self.capacity(n) if capacity is None else capacity
+        r = c.reroute_rounds if rounds is None else rounds
+        out = torch.empty(1, dtype=torch.int32, device=self.device)
+        ws = workspace(B.moe_reroute_workspace_size(n, k, c.n_experts), self.device)
+        B.moe_reroute(logits, self.w.get("logit_bias"), c.n_experts, k, c.renormalize,
+                      c.bias_selection_only, cap, r, topk_idx, topk_w, out, ws, stream=stream)
+        return out
 
     def update_bias(self, sel_count: torch.Tensor, n_tokens: int, gamma: float, stream=None):
         """Batch-level update of the selection bias in place (logit_bias must exist)."""

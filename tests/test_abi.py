@@ -122,3 +122,43 @@ def test_update_bias_validation():
     assert L.moe_update_bias(None, fake, 8, 10, 0, 0.1, fake) == B.MOE_ERR_INVALID_ARG
     assert L.moe_update_bias(None, fake, 8, 10, 2, float("nan"), fake) == B.MOE_ERR_INVALID_ARG
     assert L.moe_update_bias(None, None, 8, 10, 2, 0.1, fake) == B.MOE_ERR_INVALID_ARG
+
+
+@pytest.mark.parametrize("n,e,k", [(32, 64, 2), (256, 64, 2), (1000, 64, 2), (0, 8, 2), (255, 8, 1),
+                                   (257, 8, 2), (4096, 160, 6), (8192, 64, 1), (64, 64, 2),
+                                   (1 << 20, 512, 16), (3000, 7, 3), (777, 13, 5)])
+def test_capacity_rules_match_oracle(n, e, k):
+    assert B.moe_capacity_rule(n, e, k, B.MOE_CAPACITY_LINEAR) == O.capacity_linear(n, e, k)
+    assert B.moe_capacity_rule(n, e, k, B.MOE_CAPACITY_LOG) == O.capacity_log(n, e, k)
+    want = O.capacity(n, e, k, 1.25)
+    assert B.moe_capacity_rule(n, e, k, B.MOE_CAPACITY_FIXED, 1.25) == want
+    assert B.moe_capacity_rule(n, e, k, 7) == -1
+    assert B.moe_capacity_rule(-1, e, k, B.MOE_CAPACITY_LOG) == -1
+
+
+def test_reroute_validation():
+    L = B.lib()
+    fake = 4096  # never dereferenced: validation fails first
+
+    def call(n=8, e=4, k=2, cap=1, rounds=2, lg=fake, idx=fake, w=fake, ws=None, wsb=0):
+        return L.moe_reroute(None, lg, None, n, e, k, 1, 0, cap, rounds, idx, w, None, ws, wsb)
+
+    assert call(e=0) == B.MOE_ERR_INVALID_ARG
+    assert call(k=5) == B.MOE_ERR_INVALID_ARG
+    assert call(e=600) == B.MOE_ERR_UNSUPPORTED
+    assert call(e=40, k=17) == B.MOE_ERR_UNSUPPORTED
+    assert call(rounds=-1) == B.MOE_ERR_INVALID_ARG
+    assert call(n=-1) == B.MOE_ERR_INVALID_ARG
+    assert call(lg=None) == B.MOE_ERR_INVALID_ARG
+    need = L.moe_reroute_workspace_size(8, 2, 4)
+    assert need > 0
+    assert call(ws=fake, wsb=need - 1) == B.MOE_ERR_WORKSPACE
+    assert call(ws=fake + 8, wsb=need) == B.MOE_ERR_INVALID_ARG  # misaligned
+    assert L.moe_reroute_workspace_size(1000, 2, 64) > L.moe_reroute_workspace_size(10, 2, 64)
+    # a forward configuration with re-routing needs room for the logits as well
+    base = B.make_config(64, 4096, 11008, 64, 2, B.MOE_ACT_SWIGLU, B.MOE_BF16, capacity_factor=1.2)
+    rr = B.make_config(64, 4096, 11008, 64, 2, B.MOE_ACT_SWIGLU, B.MOE_BF16, capacity_factor=1.2,
+                       reroute_rounds=4)
+    assert B.moe_forward_workspace_size(rr) >= B.moe_forward_workspace_size(base) + 64 * 64 * 4
+    bad = B.make_config(64, 4096, 11008, 64, 2, B.MOE_ACT_SWIGLU, B.MOE_BF16, capacity_rule=9)
+    assert B.moe_forward_workspace_size(bad) == 0

@@ -208,6 +208,98 @@ def test_forward_parity_selection_only_bias():
     assert err <= TOL[cfg.dtype]
 
 
+# ------------------------------------------------------------------ overflow re-routing
+def _reroute_case(L, b, E, k, cap, rounds, renorm=True, sel_only=False):
+    """GPU route (on given logits) then GPU re-route; the oracle re-routes the same
+    selection.  Indices and placement bit-exact, weights within float32 tolerance."""
+    Ld = torch.from_numpy(L).to(DEV)
+    bd = None if b is None else torch.from_numpy(b).to(DEV)
+    got = _route(None, None, bd, E, k, renorm, logits_in=Ld, sel_only=sel_only)
+    idx0 = _check_gate(L, b, k, E, got, renorm, sel_only)
+    idx_d = torch.from_numpy(got["idx"]).to(DEV)
+    w_d = torch.from_numpy(got["w"]).to(DEV)
+    n = L.shape[0]
+    moved = torch.full((1,), -5, dtype=torch.int32, device=DEV)
+    ws = workspace(B.moe_reroute_workspace_size(n, k, E), DEV)
+    B.moe_reroute(Ld, bd, E, k, renorm, sel_only, cap, rounds, idx_d, w_d, moved, ws)
+    torch.cuda.synchronize()
+    z = O.biased_scores(L, b)
+    rr = O.reroute(z, idx0, E, None if cap < 0 else cap, min(rounds, E - k))
+    gi = idx_d.cpu().numpy()
+    assert np.array_equal(gi, rr.topk_idx), f"{int((gi != rr.topk_idx).sum())} slots differ"
+    assert int(moved.cpu()[0]) == rr.n_rerouted
+    p = O.softmax64(L if sel_only else z)
+    np.testing.assert_allclose(w_d.cpu().numpy(), O.gate_weights(p, rr.topk_idx, renorm),
+                               rtol=2e-6, atol=1e-7)
+    if cap >= 0:
+        # the plain dispatch of the new selection keeps exactly the placed slots
+        out = _dispatch(gi, E, cap, None)
+        assert np.array_equal(out["slot_row"].cpu().numpy() >= 0, rr.placed)
+    return rr
+
+
+@pytest.mark.parametrize("n,E,k,cap,rounds,bias,sel_only,renorm", [
+    (301, 16, 2, 20, 1, False, False, True), (301, 16, 2, 20, 16, True, False, True),
+    (1000, 64, 1, 12, 4, True, False, True), (257, 160, 6, 8, 3, True, True, True),
+    (64, 64, 2, 2, 62, False, False, False), (5000, 8, 2, 1300, 6, True, False, False),
+    (300, 512, 16, 10, 5, True, False, True), (77, 130, 3, 1, 127, False, False, True),
+    (200, 8, 2, 0, 3, False, False, True)])
+def test_reroute_parity(n, E, k, cap, rounds, bias, sel_only, renorm):
+    print_case("reroute", n, E, k, cap, rounds, bias, sel_only, renorm)
+    rng = np.random.default_rng(n * 7 + E + k)
+    # preferences skewed towards the low experts so that several overflow
+    L = (rng.standard_normal((n, E)) + np.linspace(1.0, 0.0, E)).astype(np.float32)
+    b = (rng.uniform(-0.2, 0.2, E)).astype(np.float32) if bias else None
+    rr = _reroute_case(L, b, E, k, cap, rounds, renorm, sel_only)
+    if cap > 0:
+        assert rr.n_rerouted > 0
+
+
+def test_reroute_with_ties_and_no_op_cases():
+    print_case("reroute-ties")
+    rng = np.random.default_rng(3)
+    n, E, k = 400, 24, 3
+    L = (rng.integers(-2, 3, size=(n, E)) * 0.5).astype(np.float32)  # many exact ties
+    b = (rng.integers(-1, 2, size=E) * 0.5).astype(np.float32)
+    for rounds in (1, 2, 50):
+        _reroute_case(L, b, E, k, 30, rounds)
+    # no limit, or no rounds: nothing moves and the weights are untouched
+    rr = _reroute_case(L, b, E, k, -1, 4)
+    assert rr.n_rerouted == 0
+    rr = _reroute_case(L, b, E, k, 30, 0)
+    assert rr.n_rerouted == 0
+
+
+def test_forward_parity_reroute_switch():
+    cfg = CONFIGS["switch"].with_tokens(1024).scaled(reroute_rounds=4, d_ff=1024)
+    print_case("forward-reroute", cfg.name, cfg.n_tokens)
+    err, r, _ = _forward_and_oracle(cfg)
+    assert r.extra["reroute"].n_rerouted > 0
+    assert err <= TOL[cfg.dtype]
+
+
+@pytest.mark.parametrize("rule", ["linear", "log"])
+def test_forward_parity_adaptive_capacity_reroute(rule):
+    cfg = CONFIGS["decode"].scaled(capacity_rule=rule, reroute_rounds=62, d_ff=2048)
+    print_case("forward-adaptive", cfg.name, rule)
+    err, r, _ = _forward_and_oracle(cfg)
+    assert r.cap == (O.capacity_linear if rule == "linear" else O.capacity_log)(64, 64, 2)
+    assert err <= TOL[cfg.dtype]
+
+
+def test_forward_parity_reroute_full_size_switch_sampled():
+    cfg = CONFIGS["switch"].scaled(reroute_rounds=8)
+    print_case("forward-reroute-full", cfg.name, cfg.n_tokens)
+    rng = np.random.default_rng(2)
+    n = cfg.n_tokens
+    tokens = np.unique(np.concatenate([np.arange(4), np.arange(n - 4, n),
+                                       rng.choice(n, size=12, replace=False)]))
+    err, r, _ = _forward_and_oracle(cfg, tokens=tokens)
+    print(f"  rerouted {r.extra['reroute'].n_rerouted}, dropped {r.plan.n_dropped}", flush=True)
+    assert err <= TOL[cfg.dtype]
+    torch.cuda.empty_cache()
+
+
 # ------------------------------------------------------------------ dispatch
 def _distinct_idx(rng, n, E, k, skew=0.0):
     score = rng.random((n, E)) + skew * np.linspace(1, 0, E)[None, :]
@@ -385,7 +477,8 @@ def _forward_and_oracle(cfg, tokens=None, check_all_logits=True):
                   logit_bias=lb, alpha=cfg.alpha, renormalize=cfg.renormalize,
                   shared=DeviceExperts(layer.w, shared=True) if cfg.n_shared else None,
                   n_shared=cfg.n_shared, logits=Lg, tokens=tokens,
-                  bias_selection_only=cfg.bias_selection_only)
+                  bias_selection_only=cfg.bias_selection_only,
+                  capacity_rule=cfg.capacity_rule, reroute_rounds=cfg.reroute_rounds)
     # integer results: bit-exact
     assert np.array_equal(st["topk_idx"].cpu().numpy(), r.topk_idx)
     assert np.array_equal(st["sel_count"].cpu().numpy(), r.stats.sel_count)
@@ -397,6 +490,8 @@ def _forward_and_oracle(cfg, tokens=None, check_all_logits=True):
     np.testing.assert_allclose(st["prob_mean"].cpu().numpy(), r.stats.prob_mean, rtol=2e-5, atol=1e-8)
     assert abs(float(st["aux"].cpu()[0]) - r.stats.aux) <= 1e-5 * r.stats.aux
     _check_monitor(st["monitor"].cpu().numpy(), r.monitor)
+    rr = r.extra.get("reroute")
+    assert int(st["n_rerouted"].cpu()[0]) == (rr.n_rerouted if rr is not None else 0)
     yg = widen_t(y)[r.tokens]
     err = normwise_err(yg, r.y)
     return err, r, y
