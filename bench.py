@@ -141,6 +141,10 @@ def describe(cfg) -> str:
         s += f" logit_bias={cfg.logit_bias}"
     if cfg.bias_selection_only:
         s += " (bias for selection only)"
+    if cfg.capacity_rule != "fixed":
+        s += f" capacity_rule={cfg.capacity_rule}"
+    if cfg.reroute_rounds:
+        s += f" overflow re-routed in up to {cfg.reroute_rounds} rounds"
     return s
 
 
@@ -215,6 +219,7 @@ def cpu_baseline(cfg, inp, logits, budget_s: float):
         O.forward(x, cfg.dtype, wr, cfg.top_k, lambda e: widen_expert(raw[e]), cfg.n_experts,
                   cfg.act, logit_bias=lb, alpha=cfg.alpha, renormalize=cfg.renormalize,
                   bias_selection_only=cfg.bias_selection_only,
+                  capacity_rule=cfg.capacity_rule, reroute_rounds=cfg.reroute_rounds,
                   shared=(lambda s: widen_expert(sraw[s])) if cfg.n_shared else None,
                   n_shared=cfg.n_shared, tokens=np.arange(n_s))
         return time.perf_counter() - t0
@@ -251,6 +256,13 @@ def main():
     ap.add_argument("--bias-selection-only", action="store_true",
                     help="the logit bias steers selection only (weights from the unbiased "
                          "softmax)")
+    ap.add_argument("--reroute-rounds", type=int, default=0,
+                    help="re-route overflow to the next preferred experts with room")
+    ap.add_argument("--capacity-rule", choices=["fixed", "linear", "log"], default="fixed",
+                    help="capacity from the factor, or the batch-dependent rules")
+    ap.add_argument("--fuse", type=int, default=None,
+                    help="fusion bitmask (1 gather x rows in GEMM1, 2 routing weights in "
+                         "GEMM2's epilogue); default: the workload's own")
     ap.add_argument("--no-cold", action="store_true",
                     help="skip the cold-cache pass (a 1 GiB scratch write before each step "
                          "evicts L2 and the 256 MB Infinity Cache; stage times only)")
@@ -297,6 +309,10 @@ def main():
     cfg = CONFIGS[args.config]
     if args.bias_selection_only:
         cfg = cfg.scaled(bias_selection_only=True)
+    if args.fuse is not None:
+        cfg = cfg.scaled(fuse=args.fuse)
+    if args.reroute_rounds or args.capacity_rule != "fixed":
+        cfg = cfg.scaled(reroute_rounds=args.reroute_rounds, capacity_rule=args.capacity_rule)
     dev = torch.device("cuda:0")
     inp = synth.DeviceInputs(cfg, dev)
     layer = MoELayer.from_inputs(inp)
@@ -384,7 +400,9 @@ def main():
         "config": {"workload": describe(cfg), "n_tokens": n, "d_model": cfg.d_model,
                    "d_ff": cfg.d_ff, "n_experts": cfg.n_experts, "top_k": cfg.top_k,
                    "n_shared": cfg.n_shared, "capacity_factor": cfg.alpha,
-                   "kept_rows": kept, "experts_touched": touched},
+                   "kept_rows": kept, "experts_touched": touched,
+                   "capacity": layer.capacity(n),
+                   "n_rerouted": int(stats["n_rerouted"].item()), "fuse": cfg.fuse},
         "roofline": kernels[dominant],
         "grouped_gemm_tflops": round(gemm_tflops, 2),
         "grouped_gemm_frac_of_peak": round(gemm_tflops / peak, 4),

@@ -64,6 +64,10 @@ typedef enum {
   MOE_CAPACITY_LOG = 2     /* [MoE-2pct] §3.1 tip: alpha growing with log2(N/256) */
 } moe_capacity_rule_t;
 
+/* Fusions of moe_forward (moe_config.fuse, a bitmask). */
+#define MOE_FUSE_GATHER 1 /* GEMM1 reads the routed rows of x in place (no permuted copy) */
+#define MOE_FUSE_WEIGHT 2 /* GEMM2 scales each row by its routing weight; the combine sums */
+
 /*
  * moe_capacity -- host function, no device work.
  * Expert capacity C = floor(floor(k*N/E) * alpha) ([MoE-2pct] §3.1 gives
@@ -215,6 +219,9 @@ moe_status moe_reroute(void* stream, const float* logits, const float* logit_bia
  *   slot_row       [N][k] int32: permuted row of (t, j), or -1 if it was dropped
  *   kept_count     [E] int32 or NULL, n_dropped [1] int32 or NULL
  *   x_perm         [N*k][d] (x_dtype) or NULL: x_perm[r] = x[row_token[r]]
+ *   topk_w [N][k] float32 and row_weight [N*k] float32, or both NULL:
+ *                  row_weight[r] = topk_w[t][j] of the assignment kept in row r (for
+ *                  moe_expert_ffn's row_scale; row_weight needs topk_w)
  * capacity < 0 means no limit; capacity == 0 drops every assignment (use
  * moe_capacity to derive it from a capacity factor).
  * x may be NULL when x_perm is NULL.  d % 8 == 0 for bf16, d % 4 == 0 for float32.
@@ -225,7 +232,8 @@ moe_status moe_dispatch(void* stream, const int32_t* topk_idx, int64_t n_tokens,
                         int32_t n_experts, int64_t capacity, const void* x, moe_dtype x_dtype,
                         int64_t d_model, int32_t* expert_offsets, int32_t* row_token,
                         int32_t* slot_row, int32_t* kept_count, int32_t* n_dropped,
-                        void* x_perm, void* ws, size_t ws_bytes);
+                        void* x_perm, const float* topk_w, float* row_weight, void* ws,
+                        size_t ws_bytes);
 
 /*
  * moe_expert_ffn -- the expert networks over variable-length row segments (one grouped
@@ -236,7 +244,12 @@ moe_status moe_dispatch(void* stream, const int32_t* topk_idx, int64_t n_tokens,
  *   SwiGLU ([MoE-2pct] §3.2):  h = SiLU(a W1^T) * (a W3^T), y = h W2^T (+ b2)
  * Arguments
  *   dtype        MOE_BF16 (bf16 data, float32 accumulation, bf16 h and y) or MOE_F32.
- *   a            [rows][d]; rows = seg_offsets[S] (read on the device).
+ *   a            [rows][d]; rows = seg_offsets[S] (read on the device).  With a_rows,
+ *                the first layer reads row r as a[a_rows[r]] instead (the routed rows
+ *                gathered in place: pass x and moe_dispatch's row_token, no x_perm);
+ *                a then has a_n_rows rows (1 .. 4 GiB of data) and every a_rows[r]
+ *                for r < seg_offsets[S] must be below a_n_rows.  a_rows NULL: a_n_rows
+ *                is ignored.
  *   seg_offsets  [S+1] int32 DEVICE array, non-decreasing, seg_offsets[0] == 0,
  *                seg_offsets[S] <= max_rows.  1 <= S <= MOE_MAX_EXPERTS.
  *   max_rows     upper bound on seg_offsets[S] (sizes the launch; no row beyond it is
@@ -244,12 +257,17 @@ moe_status moe_dispatch(void* stream, const int32_t* topk_idx, int64_t n_tokens,
  *   d, d_ff      bf16: both multiples of 64.  float32: both multiples of 4.
  *   w1 [S][d_ff][d]; w3 [S][d_ff][d] (SwiGLU only, else NULL); b1 [S][d_ff] or NULL;
  *   w2 [S][d][d_ff]; b2 [S][d] or NULL.  All in `dtype`.
+ *   row_scale    [rows] float32 or NULL: the second layer's output row r is multiplied
+ *                by row_scale[r] (after its bias), e.g. moe_dispatch's row_weight, so
+ *                that moe_combine can sum without weights.
  *   h  [max_rows][d_ff] and y [max_rows][d] in `dtype` (outputs).
  */
 moe_status moe_expert_ffn(void* stream, moe_dtype dtype, moe_act act, const void* a,
+                          const int32_t* a_rows, int64_t a_n_rows,
                           const int32_t* seg_offsets, int32_t n_segments, int64_t max_rows,
                           int64_t d_model, int64_t d_ff, const void* w1, const void* w3,
-                          const void* b1, const void* w2, const void* b2, void* h, void* y);
+                          const void* b1, const void* w2, const void* b2,
+                          const float* row_scale, void* h, void* y);
 
 /*
  * moe_combine -- routing-weighted sum of the expert rows back into token order
@@ -259,7 +277,8 @@ moe_status moe_expert_ffn(void* stream, moe_dtype dtype, moe_act act, const void
  * accumulated in float32 in exactly that order (shared first, then j ascending); a
  * token with every slot dropped and no shared output gets 0.
  *   y_rows [*][d], shared_y [N][d] or NULL, out [N][d], all in `dtype`.
- *   slot_row [N][k] int32, topk_w [N][k] float32.
+ *   slot_row [N][k] int32, topk_w [N][k] float32, or NULL when the rows already carry
+ *   their weights (moe_expert_ffn's row_scale): then every weight is 1.
  */
 moe_status moe_combine(void* stream, moe_dtype dtype, const void* y_rows,
                        const int32_t* slot_row, const float* topk_w, int64_t n_tokens,
@@ -281,6 +300,10 @@ typedef struct {
   int32_t capacity_rule;  /* moe_capacity_rule_t */
   int32_t reroute_rounds; /* > 0: re-route overflow (moe_reroute) in up to this many
                              rounds before the dispatch; 0: drop it */
+  int32_t fuse;           /* MOE_FUSE_* bitmask.  MOE_FUSE_GATHER is taken when x holds
+                             at most 4 GiB; results equal the unfused ones bit for bit.
+                             MOE_FUSE_WEIGHT rounds w * expert output to dtype before
+                             the sum (unfused: the sum weights the rounded output). */
 } moe_config;
 
 typedef struct {

@@ -20,6 +20,7 @@ MOE_F32, MOE_BF16 = 0, 1
 MOE_ACT_GELU, MOE_ACT_SWIGLU = 0, 1
 MOE_MAX_EXPERTS = 512
 MOE_CAPACITY_FIXED, MOE_CAPACITY_LINEAR, MOE_CAPACITY_LOG = range(3)
+MOE_FUSE_GATHER, MOE_FUSE_WEIGHT = 1, 2
 CAPACITY_RULES = {"fixed": MOE_CAPACITY_FIXED, "linear": MOE_CAPACITY_LINEAR,
                   "log": MOE_CAPACITY_LOG}
 
@@ -37,7 +38,7 @@ class MoEConfigC(C.Structure):
                 ("renormalize", C.c_int32), ("bias_selection_only", C.c_int32),
                 ("act", C.c_int), ("dtype", C.c_int),
                 ("capacity_factor", C.c_double), ("capacity_rule", C.c_int32),
-                ("reroute_rounds", C.c_int32)]
+                ("reroute_rounds", C.c_int32), ("fuse", C.c_int32)]
 
 
 class MoEWeightsC(C.Structure):
@@ -70,9 +71,9 @@ _SIGS = {
                               _VP, _VP, _SZ]),
     "moe_dispatch_workspace_size": (_SZ, [_I64, _I32, _I32]),
     "moe_dispatch": (C.c_int, [_VP, _VP, _I64, _I32, _I32, _I64, _VP, C.c_int, _I64, _VP, _VP,
-                               _VP, _VP, _VP, _VP, _VP, _SZ]),
-    "moe_expert_ffn": (C.c_int, [_VP, C.c_int, C.c_int, _VP, _VP, _I32, _I64, _I64, _I64, _VP,
-                                 _VP, _VP, _VP, _VP, _VP, _VP]),
+                               _VP, _VP, _VP, _VP, _VP, _VP, _VP, _SZ]),
+    "moe_expert_ffn": (C.c_int, [_VP, C.c_int, C.c_int, _VP, _VP, _I64, _VP, _I32, _I64, _I64,
+                                 _I64, _VP, _VP, _VP, _VP, _VP, _VP, _VP, _VP]),
     "moe_combine": (C.c_int, [_VP, C.c_int, _VP, _VP, _VP, _I64, _I32, _I64, _VP, _VP]),
     "moe_forward_workspace_size": (_SZ, [C.POINTER(MoEConfigC)]),
     "moe_forward": (C.c_int, [_VP, C.POINTER(MoEConfigC), C.POINTER(MoEWeightsC), _VP, _VP,
@@ -196,24 +197,26 @@ def moe_dispatch_workspace_size(n_tokens: int, k: int, n_experts: int) -> int:
 
 
 def moe_dispatch(topk_idx, n_experts: int, capacity: int, x, expert_offsets, row_token,
-                 slot_row, kept_count, n_dropped, x_perm, ws, stream=None):
+                 slot_row, kept_count, n_dropped, x_perm, ws, stream=None, topk_w=None,
+                 row_weight=None):
     n, k = topk_idx.shape
     d = x.shape[1] if x is not None else 0
     xdt = _dtype(x) if x is not None else MOE_F32
     st = lib().moe_dispatch(_stream(stream), _ptr(topk_idx), n, k, n_experts, capacity,
                             _ptr(x), xdt, d, _ptr(expert_offsets), _ptr(row_token),
                             _ptr(slot_row), _ptr(kept_count), _ptr(n_dropped), _ptr(x_perm),
-                            _ptr(ws), _ws_bytes(ws))
+                            _ptr(topk_w), _ptr(row_weight), _ptr(ws), _ws_bytes(ws))
     _check("moe_dispatch", st)
 
 
 def moe_expert_ffn(act: int, a, seg_offsets, n_segments: int, max_rows: int, w1, w3, b1, w2,
-                   b2, h, y, stream=None):
+                   b2, h, y, stream=None, a_rows=None, row_scale=None):
     d = a.shape[1]
     d_ff = w1.shape[-2]
-    st = lib().moe_expert_ffn(_stream(stream), _dtype(a), act, _ptr(a), _ptr(seg_offsets),
-                              n_segments, max_rows, d, d_ff, _ptr(w1), _ptr(w3), _ptr(b1),
-                              _ptr(w2), _ptr(b2), _ptr(h), _ptr(y))
+    st = lib().moe_expert_ffn(_stream(stream), _dtype(a), act, _ptr(a), _ptr(a_rows),
+                              a.shape[0], _ptr(seg_offsets), n_segments, max_rows, d, d_ff,
+                              _ptr(w1), _ptr(w3), _ptr(b1), _ptr(w2), _ptr(b2),
+                              _ptr(row_scale), _ptr(h), _ptr(y))
     _check("moe_expert_ffn", st)
 
 
@@ -227,11 +230,11 @@ def moe_combine(y_rows, slot_row, topk_w, shared_y, out, stream=None):
 
 def make_config(n_tokens, d_model, d_ff, n_experts, top_k, act, dtype, capacity_factor=0.0,
                 n_shared=0, renormalize=True, bias_selection_only=False,
-                capacity_rule=MOE_CAPACITY_FIXED, reroute_rounds=0) -> MoEConfigC:
+                capacity_rule=MOE_CAPACITY_FIXED, reroute_rounds=0, fuse=0) -> MoEConfigC:
     return MoEConfigC(n_tokens, d_model, d_ff, n_experts, top_k, n_shared,
                       1 if renormalize else 0, 1 if bias_selection_only else 0, act, dtype,
                       float(capacity_factor) if capacity_factor else 0.0, capacity_rule,
-                      reroute_rounds)
+                      reroute_rounds, fuse)
 
 
 def moe_forward_workspace_size(cfg: MoEConfigC) -> int:

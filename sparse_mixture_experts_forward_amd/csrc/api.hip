@@ -201,14 +201,15 @@ moe_status run_route(hipStream_t st, const void* x, moe_dtype xt, int64_t n, int
 moe_status run_dispatch(hipStream_t st, const int32_t* idx, int64_t n, int32_t k, int32_t e,
                         int64_t cap, const void* x, int64_t row_bytes, int32_t* offsets,
                         int32_t* row_token, int32_t* slot_row, int32_t* kept, int32_t* dropped,
-                        void* x_perm, void* ws) {
+                        void* x_perm, const float* topk_w, float* row_weight, void* ws) {
   Carve c(ws);
   const moe::DispatchGrid g = moe::dispatch_grid(n, k);
   int32_t* hist = c.take<int32_t>(g.n_blocks * e);
   int32_t* base = c.take<int32_t>(g.n_blocks * e);
   int32_t* kept_tmp = c.take<int32_t>(e);
   return hip_check(moe::launch_dispatch(st, idx, n, k, e, cap, x, row_bytes, offsets, row_token,
-                                        slot_row, kept, dropped, x_perm, hist, base, kept_tmp),
+                                        slot_row, kept, dropped, x_perm, hist, base, kept_tmp,
+                                        topk_w, row_weight),
                    "dispatch kernels launch");
 }
 
@@ -225,15 +226,18 @@ moe_status check_ffn_shape(moe_dtype dt, moe_act act, int64_t d, int64_t d_ff) {
 }
 
 // The two grouped products of one FFN layer of experts.
+// a_rows (or null): GEMM1 reads A row r from a[a_rows[r]]; row_scale (or null): GEMM2
+// multiplies output row r by row_scale[r].
 moe_status run_ffn(hipStream_t st, moe_dtype dt, moe_act act, const void* a, int64_t lda,
                    const int32_t* seg_off, int32_t n_seg, int32_t single_rows, int64_t max_rows,
                    int64_t d, int64_t d_ff, const void* w1, const void* w3, const void* b1,
                    int64_t w_seg_stride, const void* w2, const void* b2, int64_t w2_kchunk,
                    int64_t w2_kbatch_stride, void* h, void* y,
-                   const std::function<moe_status()>& between = nullptr) {
+                   const std::function<moe_status()>& between = nullptr,
+                   const int32_t* a_rows = nullptr, const float* row_scale = nullptr) {
   const bool bf = dt == MOE_BF16;
   moe::GemmArgs g1{};
-  g1.a = a; g1.lda = lda;
+  g1.a = a; g1.lda = lda; g1.a_rows = a_rows;
   g1.b0 = w1; g1.b1 = (act == MOE_ACT_SWIGLU) ? w3 : nullptr;
   g1.ldb = d; g1.b_seg_stride = w_seg_stride;
   g1.kchunk = d; g1.kbatch_stride = 0;
@@ -246,7 +250,7 @@ moe_status run_ffn(hipStream_t st, moe_dtype dt, moe_act act, const void* a, int
                     "expert GEMM1 launch"));
   if (between) MOE_TRY(between());
   moe::GemmArgs g2{};
-  g2.a = h; g2.lda = d_ff;
+  g2.a = h; g2.lda = d_ff; g2.row_scale = row_scale;
   g2.b0 = w2; g2.b1 = nullptr;
   g2.ldb = w2_kchunk; g2.b_seg_stride = w_seg_stride;
   g2.kchunk = w2_kchunk; g2.kbatch_stride = w2_kbatch_stride;
@@ -318,9 +322,17 @@ int64_t max_rows_of(int64_t n, int32_t e, int32_t k, int64_t cap) {
   return lim < all ? lim : all;
 }
 
+// The fusions moe_forward takes for a configuration: the gather needs every byte offset
+// into x below 2^32 (32-bit load offsets in the GEMM).
+bool fuse_gather(const moe_config& c) {
+  return (c.fuse & MOE_FUSE_GATHER) &&
+         c.n_tokens * c.d_model * static_cast<int64_t>(elem_size(c.dtype)) <= UINT32_MAX;
+}
+bool fuse_weight(const moe_config& c) { return (c.fuse & MOE_FUSE_WEIGHT) != 0; }
+
 struct ForwardLayout {
   int32_t *idx, *sel, *offsets, *row_token, *slot_row, *kept, *dropped;
-  float *w, *pm, *aux, *logits;
+  float *w, *pm, *aux, *logits, *row_w;
   void *route_ws, *dispatch_ws, *x_perm, *h, *y_rows, *h_sh, *y_sh;
   moe::RerouteWs rr;
   size_t used;
@@ -350,7 +362,8 @@ ForwardLayout forward_layout(const moe_config& c, void* ws) {
     L.logits = cv.take<float>(n * e);
     L.rr = reroute_layout(cv, n, c.top_k, e);
   }
-  L.x_perm = cv.take<char>(R * c.d_model * es);
+  if (!fuse_gather(c)) L.x_perm = cv.take<char>(R * c.d_model * es);
+  if (fuse_weight(c)) L.row_w = cv.take<float>(R);
   L.h = cv.take<char>(R * c.d_ff * es);
   L.y_rows = cv.take<char>(R * c.d_model * es);
   if (c.n_shared > 0) {
@@ -372,6 +385,7 @@ moe_status check_config(const moe_config* c) {
   if (c->capacity_rule < MOE_CAPACITY_FIXED || c->capacity_rule > MOE_CAPACITY_LOG)
     return fail(MOE_ERR_INVALID_ARG, "unknown capacity rule");
   if (c->reroute_rounds < 0) return fail(MOE_ERR_INVALID_ARG, "reroute_rounds < 0");
+  if (c->fuse & ~(MOE_FUSE_GATHER | MOE_FUSE_WEIGHT)) return fail(MOE_ERR_INVALID_ARG, "unknown fuse flags");
   MOE_TRY(check_ffn_shape(c->dtype, c->act, c->d_model, c->d_ff));
   if (c->n_tokens * static_cast<int64_t>(c->top_k) > INT32_MAX / 2)
     return fail(MOE_ERR_UNSUPPORTED, "n_tokens * top_k too large");
@@ -497,7 +511,8 @@ moe_status moe_dispatch(void* stream, const int32_t* topk_idx, int64_t n_tokens,
                         int32_t n_experts, int64_t capacity, const void* x, moe_dtype x_dtype,
                         int64_t d_model, int32_t* expert_offsets, int32_t* row_token,
                         int32_t* slot_row, int32_t* kept_count, int32_t* n_dropped,
-                        void* x_perm, void* ws, size_t ws_bytes) {
+                        void* x_perm, const float* topk_w, float* row_weight, void* ws,
+                        size_t ws_bytes) {
   if (n_tokens < 0) return fail(MOE_ERR_INVALID_ARG, "n_tokens < 0");
   if (n_experts < 1) return fail(MOE_ERR_INVALID_ARG, "n_experts < 1");
   if (n_experts > MOE_MAX_EXPERTS) return fail(MOE_ERR_UNSUPPORTED, "n_experts > %d", MOE_MAX_EXPERTS);
@@ -507,6 +522,7 @@ moe_status moe_dispatch(void* stream, const int32_t* topk_idx, int64_t n_tokens,
   if (n_tokens * static_cast<int64_t>(k) > INT32_MAX / 2) return fail(MOE_ERR_UNSUPPORTED, "n_tokens too large");
   if (n_tokens > 0 && (!topk_idx || !row_token || !slot_row))
     return fail(MOE_ERR_INVALID_ARG, "topk_idx, row_token and slot_row are required");
+  if (row_weight && !topk_w) return fail(MOE_ERR_INVALID_ARG, "row_weight needs topk_w");
   int64_t row_bytes = 0;
   if (x_perm) {
     if (!dtype_ok(x_dtype)) return fail(MOE_ERR_INVALID_ARG, "unknown x dtype");
@@ -525,14 +541,18 @@ moe_status moe_dispatch(void* stream, const int32_t* topk_idx, int64_t n_tokens,
   }
   return run_dispatch(static_cast<hipStream_t>(stream), topk_idx, n_tokens, k, n_experts,
                       capacity, x, row_bytes, expert_offsets, row_token, slot_row, kept_count,
-                      n_dropped, x_perm, ws);
+                      n_dropped, x_perm, topk_w, row_weight, ws);
 }
 
 moe_status moe_expert_ffn(void* stream, moe_dtype dtype, moe_act act, const void* a,
+                          const int32_t* a_rows, int64_t a_n_rows,
                           const int32_t* seg_offsets, int32_t n_segments, int64_t max_rows,
                           int64_t d_model, int64_t d_ff, const void* w1, const void* w3,
-                          const void* b1, const void* w2, const void* b2, void* h, void* y) {
+                          const void* b1, const void* w2, const void* b2,
+                          const float* row_scale, void* h, void* y) {
   MOE_TRY(check_ffn_shape(dtype, act, d_model, d_ff));
+  if (a_rows && (a_n_rows < 1 || a_n_rows * d_model * static_cast<int64_t>(elem_size(dtype)) > UINT32_MAX))
+    return fail(MOE_ERR_UNSUPPORTED, "with a_rows, a must have 1 .. 4 GiB / row bytes rows");
   if (n_segments < 1) return fail(MOE_ERR_INVALID_ARG, "n_segments < 1");
   if (n_segments > MOE_MAX_EXPERTS) return fail(MOE_ERR_UNSUPPORTED, "n_segments > %d", MOE_MAX_EXPERTS);
   if (max_rows < 0) return fail(MOE_ERR_INVALID_ARG, "max_rows < 0");
@@ -549,7 +569,7 @@ moe_status moe_expert_ffn(void* stream, moe_dtype dtype, moe_act act, const void
   MOE_TRY(check_aligned(y, 16, "y"));
   return run_ffn(static_cast<hipStream_t>(stream), dtype, act, a, d_model, seg_offsets,
                  n_segments, 0, max_rows, d_model, d_ff, w1, w3, b1, d_ff * d_model, w2, b2,
-                 d_ff, 0, h, y, nullptr);
+                 d_ff, 0, h, y, nullptr, a_rows, row_scale);
 }
 
 moe_status moe_combine(void* stream, moe_dtype dtype, const void* y_rows,
@@ -562,8 +582,8 @@ moe_status moe_combine(void* stream, moe_dtype dtype, const void* y_rows,
   if (d_model <= 0 || d_model % vec != 0)
     return fail(MOE_ERR_UNSUPPORTED, "d_model must be a positive multiple of %lld", static_cast<long long>(vec));
   if (n_tokens == 0) return MOE_OK;
-  if (!y_rows || !slot_row || !topk_w || !out)
-    return fail(MOE_ERR_INVALID_ARG, "y_rows, slot_row, topk_w and out are required");
+  if (!y_rows || !slot_row || !out)
+    return fail(MOE_ERR_INVALID_ARG, "y_rows, slot_row and out are required");
   MOE_TRY(check_aligned(y_rows, 16, "y_rows"));
   MOE_TRY(check_aligned(out, 16, "out"));
   if (shared_y) MOE_TRY(check_aligned(shared_y, 16, "shared_y"));
@@ -637,9 +657,11 @@ moe_status moe_forward(void* stream, const moe_config* cfg, const moe_weights* w
                                           reroute ? clamp_rounds(c.reroute_rounds, e, k) : 0,
                                           idx, tw, o.n_rerouted, L.rr),
                       "re-routing launch"));
+  const bool gather = fuse_gather(c), wscale = fuse_weight(c);
   MOE_TRY(run_dispatch(st, idx, n, k, e, cap, x, c.d_model * static_cast<int64_t>(es), offsets,
-                       L.row_token, slot_row, o.kept_count, dropped, L.x_perm,
-                       L.dispatch_ws));
+                       L.row_token, slot_row, o.kept_count, dropped,
+                       gather ? nullptr : L.x_perm, wscale ? tw : nullptr,
+                       wscale ? L.row_w : nullptr, L.dispatch_ws));
   if (o.monitor)
     MOE_TRY(hip_check(moe::launch_drop_rate(st, dropped, n * k, o.monitor + 4), "drop rate launch"));
   MOE_TRY(mark(2));
@@ -661,16 +683,19 @@ moe_status moe_forward(void* stream, const moe_config* cfg, const moe_weights* w
     MOE_TRY(hip_check(hipEventRecord(side->join, side->s), "join event record"));
   }
   const int64_t R = max_rows_of(n, e, k, cap);
-  // a6-a7: routed experts over the expert-major segments
-  MOE_TRY(run_ffn(st, c.dtype, c.act, L.x_perm, c.d_model, offsets, e, 0, R, c.d_model, c.d_ff,
-                  w->w1, w->w3, w->b1, c.d_ff * c.d_model, w->w2, w->b2, c.d_ff, 0, L.h,
-                  L.y_rows, [&]() { return mark(3); }));
+  // a6-a7: routed experts over the expert-major segments; fused, GEMM1 gathers the rows
+  // of x itself and GEMM2 scales each row by its routing weight
+  MOE_TRY(run_ffn(st, c.dtype, c.act, gather ? x : L.x_perm, c.d_model, offsets, e, 0, R,
+                  c.d_model, c.d_ff, w->w1, w->w3, w->b1, c.d_ff * c.d_model, w->w2, w->b2,
+                  c.d_ff, 0, L.h, L.y_rows, [&]() { return mark(3); },
+                  gather ? L.row_token : nullptr, wscale ? L.row_w : nullptr));
   MOE_TRY(mark(4));
   // join: the combine needs the shared experts' output
   if (side) MOE_TRY(hip_check(hipStreamWaitEvent(st, side->join, 0), "join wait"));
   MOE_TRY(mark(5));
   // a9: weighted combine (shared first, then slots in order)
-  MOE_TRY(hip_check(moe::launch_combine(st, c.dtype == MOE_BF16, L.y_rows, slot_row, tw, n, k,
+  MOE_TRY(hip_check(moe::launch_combine(st, c.dtype == MOE_BF16, L.y_rows, slot_row,
+                                        wscale ? nullptr : tw, n, k,
                                         c.d_model, c.n_shared > 0 ? L.y_sh : nullptr, y),
                     "combine launch"));
   return mark(6);

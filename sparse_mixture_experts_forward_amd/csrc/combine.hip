@@ -40,7 +40,7 @@ __global__ __launch_bounds__(kThreads) void combine_bf16_kernel(
     for (int j = 0; j < k; ++j) {
       const int32_t r = slot_row[t * k + j];
       if (r < 0) continue;
-      const float w = topk_w[t * k + j];
+      const float w = topk_w ? topk_w[t * k + j] : 1.f;  // NULL: rows already weighted
       const uint4 v = *reinterpret_cast<const uint4*>(y_rows + static_cast<int64_t>(r) * d + c);
       const uint32_t w4[4] = {v.x, v.y, v.z, v.w};
 #pragma unroll
@@ -73,7 +73,7 @@ __global__ __launch_bounds__(kThreads) void combine_f32_kernel(
     for (int j = 0; j < k; ++j) {
       const int32_t r = slot_row[t * k + j];
       if (r < 0) continue;
-      const float w = topk_w[t * k + j];
+      const float w = topk_w ? topk_w[t * k + j] : 1.f;
       const float4 v = *reinterpret_cast<const float4*>(y_rows + static_cast<int64_t>(r) * d + c);
       acc.x = fmaf(w, v.x, acc.x);
       acc.y = fmaf(w, v.y, acc.y);

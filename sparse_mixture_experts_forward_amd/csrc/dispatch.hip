@@ -149,7 +149,8 @@ __global__ __launch_bounds__(kThreads) void dispatch_scatter_kernel(
     const int32_t* __restrict__ topk_idx, int64_t n, int k, int E, int64_t tpb,
     int64_t n_blocks, int64_t capacity, const int32_t* __restrict__ blk_base,
     const int32_t* __restrict__ expert_offsets, int32_t* __restrict__ row_token,
-    int32_t* __restrict__ slot_row, const uint8_t* __restrict__ x, int64_t row_bytes,
+    int32_t* __restrict__ slot_row, const float* __restrict__ topk_w,
+    float* __restrict__ row_weight, const uint8_t* __restrict__ x, int64_t row_bytes,
     uint8_t* __restrict__ x_perm) {
   __shared__ int32_t cnt[kMaxExperts];
   __shared__ int32_t srow[kMaxChunkItems];
@@ -168,6 +169,7 @@ __global__ __launch_bounds__(kThreads) void dispatch_scatter_kernel(
         if (capacity < 0 || rank < capacity) {
           r = expert_offsets[e] + static_cast<int32_t>(rank);
           row_token[r] = static_cast<int32_t>(q / k);
+          if (row_weight) row_weight[r] = topk_w[q];
         }
       }
       slot_row[q] = r;
@@ -399,7 +401,8 @@ hipError_t launch_dispatch(hipStream_t st, const int32_t* topk_idx, int64_t n, i
                            int64_t capacity, const void* x, int64_t row_bytes,
                            int32_t* expert_offsets, int32_t* row_token, int32_t* slot_row,
                            int32_t* kept_count, int32_t* n_dropped, void* x_perm,
-                           int32_t* blk_hist, int32_t* blk_base, int32_t* kept_tmp) {
+                           int32_t* blk_hist, int32_t* blk_base, int32_t* kept_tmp,
+                           const float* topk_w, float* row_weight) {
   const DispatchGrid g = dispatch_grid(n, k);
   if (g.n_blocks > 0) {
     hipLaunchKernelGGL(dispatch_hist_kernel, dim3(static_cast<unsigned>(g.n_blocks)),
@@ -419,7 +422,8 @@ hipError_t launch_dispatch(hipStream_t st, const int32_t* topk_idx, int64_t n, i
   hipLaunchKernelGGL(dispatch_scatter_kernel, dim3(static_cast<unsigned>(g.n_blocks)),
                      dim3(kThreads), 0, st, topk_idx, n, k, e, g.tokens_per_block,
                      g.n_blocks, capacity, blk_base, expert_offsets, row_token, slot_row,
-                     static_cast<const uint8_t*>(x), row_bytes, static_cast<uint8_t*>(x_perm));
+                     topk_w, row_weight, static_cast<const uint8_t*>(x), row_bytes,
+                     static_cast<uint8_t*>(x_perm));
   return hipGetLastError();
 }
 

@@ -475,6 +475,12 @@ __device__ __forceinline__ void tile_body(const GemmArgs& g, const Tile& tile, c
     }
   } else {
     const uint16_t* bias = static_cast<const uint16_t*>(g.bias);
+    float sc[TA > 0 ? TA : 1];  // per-row output scale (the routing weight of the row)
+#pragma unroll
+    for (int tm = 0; tm < TA; ++tm) {
+      const int m = (2 * tm + wm) * S::M + frow;
+      sc[tm] = (g.row_scale && m < tile.m_valid) ? g.row_scale[tile.row0 + m] : 1.f;
+    }
 #pragma unroll
     for (int tn = 0; tn < TN; ++tn) {
 #pragma unroll
@@ -495,6 +501,7 @@ __device__ __forceinline__ void tile_body(const GemmArgs& g, const Tile& tile, c
             for (int r = 0; r < 4; ++r) {
               v[r] = acc[tn][tm][4 * q + r] + bv[r];
               if (EPI == EPI_GELU) v[r] = gelu_erf(v[r]);
+              v[r] *= sc[tm];  // exact when 1
             }
             *reinterpret_cast<uint2*>(C + (tile.row0 + m) * g.ldc + col) =
                 pack_bf16x4(v[0], v[1], v[2], v[3]);
@@ -541,13 +548,17 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_bf16_kernel(GemmArgs g) {
   io.kchunk = g.kchunk;
   io.kbatch_stride = g.kbatch_stride;
   const int dl_row = lane >> 3;  // row inside an 8-row load group
-  io.a_base = static_cast<const uint16_t*>(g.a) + tile.row0 * g.lda;
+  // A rows: the tile's rows of a, or with a_rows the rows of a they name (the gather of
+  // the routed tokens; the caller keeps every byte offset below 2^32)
+  const int32_t* __restrict__ a_rows = g.a_rows;
+  io.a_base = static_cast<const uint16_t*>(g.a) + (a_rows ? 0 : tile.row0 * g.lda);
 #pragma unroll
   for (int j = 0; j < IO::A_GRP; ++j) {
     const int i = 8 * (wave + 4 * j) + dl_row;  // LDS row of the tile
     const int r = min(i, tile.m_valid - 1);     // rows past the segment repeat its last row
+    const uint32_t src = a_rows ? static_cast<uint32_t>(a_rows[tile.row0 + r]) : r;
     const int chunk = ((lane & 7) ^ lds_swizzle(i)) * 8;
-    io.a_off[j] = static_cast<uint32_t>((r * static_cast<int32_t>(g.lda) + chunk) * 2);
+    io.a_off[j] = (src * static_cast<uint32_t>(g.lda) + chunk) * 2u;
   }
   io.b_base0 = static_cast<const uint16_t*>(g.b0) + tile.seg * g.b_seg_stride;
   io.b_base1 = (EPI == EPI_SWIGLU) ? static_cast<const uint16_t*>(g.b1) + tile.seg * g.b_seg_stride
@@ -626,7 +637,8 @@ __global__ __launch_bounds__(kThreads) void gemm_f32_kernel(GemmArgs g) {
   const int ty = tid / 16, tx = tid % 16;
   const int lr = tid / 4, lk = (tid % 4) * 4;
   const float* A = static_cast<const float*>(g.a);
-  const float* arow = A + (tile.row0 + min(lr, tile.m_valid - 1)) * g.lda;
+  const int64_t a_r = tile.row0 + min(lr, tile.m_valid - 1);
+  const float* arow = A + (g.a_rows ? static_cast<int64_t>(g.a_rows[a_r]) : a_r) * g.lda;
   const int n_ld = min(tile.nt * kFBN + lr, g.n_out - 1);
   const float* brow0 = static_cast<const float*>(g.b0) + tile.seg * g.b_seg_stride + static_cast<int64_t>(n_ld) * g.ldb;
   const float* brow1 = (EPI == EPI_SWIGLU)
@@ -690,6 +702,7 @@ __global__ __launch_bounds__(kThreads) void gemm_f32_kernel(GemmArgs g) {
       } else {
         v = acc[i][j] + (bias ? bias[tile.seg * g.bias_seg_stride + col] : 0.f);
         if (EPI == EPI_GELU) v = gelu_erf(v);
+        if (g.row_scale) v *= g.row_scale[tile.row0 + m];
       }
       C[(tile.row0 + m) * g.ldc + col] = v;
     }

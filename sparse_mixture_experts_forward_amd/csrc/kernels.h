@@ -83,7 +83,8 @@ hipError_t launch_dispatch(hipStream_t st, const int32_t* topk_idx, int64_t n, i
                            int64_t capacity, const void* x, int64_t row_bytes,
                            int32_t* expert_offsets, int32_t* row_token, int32_t* slot_row,
                            int32_t* kept_count, int32_t* n_dropped, void* x_perm,
-                           int32_t* blk_hist, int32_t* blk_base, int32_t* kept_tmp);
+                           int32_t* blk_hist, int32_t* blk_base, int32_t* kept_tmp,
+                           const float* topk_w, float* row_weight);
 
 // Workspace of the overflow re-routing (all device arrays): blk_hist / blk_base
 // [E][n_blocks] (dispatch_grid), kept / room [E], state [N*k], thr_z / thr_e [N],
@@ -110,6 +111,8 @@ enum Epilogue { EPI_NONE = 0, EPI_GELU = 1, EPI_SWIGLU = 2 };
 struct GemmArgs {
   const void* a;
   int64_t lda;
+  const int32_t* a_rows;  // or null: A row r is a[a_rows[r]] (gather), else a[r]
+  const float* row_scale; // or null: output row r is multiplied by row_scale[r]
   const void* b0;        // [S][n_out][ldb] (W1 or W2)
   const void* b1;        // W3 for SwiGLU, else null
   int64_t ldb;           // row stride of B (elements)

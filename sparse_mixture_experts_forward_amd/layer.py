@@ -50,7 +50,7 @@ class MoELayer:
         return B.make_config(n_tokens, c.d_model, c.d_ff, c.n_experts, c.top_k, _act(c.act),
                              B.MOE_BF16 if c.dtype == "bf16" else B.MOE_F32,
                              c.alpha or 0.0, c.n_shared, c.renormalize, c.bias_selection_only,
-                             B.CAPACITY_RULES[c.capacity_rule], c.reroute_rounds)
+                             B.CAPACITY_RULES[c.capacity_rule], c.reroute_rounds, c.fuse)
 
     def capacity(self, n_tokens: int) -> int:
         c = self.cfg
@@ -127,7 +127,7 @@ class MoELayer:
                           self.w["logit_bias"], stream=stream)
 
     def dispatch(self, x: torch.Tensor, topk_idx: torch.Tensor, capacity: Optional[int] = None,
-                 with_copy: bool = True, stream=None) -> dict:
+                 with_copy: bool = True, stream=None, topk_w: Optional[torch.Tensor] = None) -> dict:
         c = self.cfg
         n, k = topk_idx.shape
         cap = self.capacity(n) if capacity is None else capacity
@@ -138,15 +138,19 @@ class MoELayer:
                    kept_count=torch.empty(c.n_experts, dtype=torch.int32, device=dev),
                    n_dropped=torch.empty(1, dtype=torch.int32, device=dev),
                    x_perm=(torch.zeros((max(n * k, 1), x.shape[1]), dtype=x.dtype, device=dev)
-                           if with_copy else None))
+                           if with_copy else None),
+                   row_weight=(torch.full((max(n * k, 1),), -3.0, dtype=torch.float32, device=dev)
+                               if topk_w is not None else None))
         ws = workspace(B.moe_dispatch_workspace_size(n, k, c.n_experts), dev)
         B.moe_dispatch(topk_idx, c.n_experts, cap, x if with_copy else None,
                        out["expert_offsets"], out["row_token"], out["slot_row"],
-                       out["kept_count"], out["n_dropped"], out["x_perm"], ws, stream=stream)
+                       out["kept_count"], out["n_dropped"], out["x_perm"], ws, stream=stream,
+                       topk_w=topk_w, row_weight=out["row_weight"])
         return out
 
     def expert_ffn(self, a: torch.Tensor, seg_offsets: torch.Tensor, max_rows: int,
-                   shared: bool = False, stream=None):
+                   shared: bool = False, stream=None, a_rows: Optional[torch.Tensor] = None,
+                   row_scale: Optional[torch.Tensor] = None):
         c = self.cfg
         p = "shared_" if shared else ""
         w1, w2 = self.w[p + "w1"], self.w[p + "w2"]
@@ -157,7 +161,7 @@ class MoELayer:
         h = torch.empty((rows, c.d_ff), dtype=a.dtype, device=a.device)
         y = torch.empty((rows, c.d_model), dtype=a.dtype, device=a.device)
         B.moe_expert_ffn(_act(c.act), a, seg_offsets, w1.shape[0], max_rows, w1, w3, b1, w2,
-                         b2, h, y, stream=stream)
+                         b2, h, y, stream=stream, a_rows=a_rows, row_scale=row_scale)
         return h, y
 
     def combine(self, y_rows, slot_row, topk_w, shared_y=None, stream=None):

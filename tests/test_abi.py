@@ -79,19 +79,27 @@ def test_dispatch_and_combine_validation():
     L = B.lib()
     fake = 4096
     assert L.moe_dispatch(None, fake, 4, 3, 2, -1, None, 0, 0, fake, fake, fake, None, None,
-                          None, None, 0) == B.MOE_ERR_INVALID_ARG  # k > E
+                          None, None, None, None, 0) == B.MOE_ERR_INVALID_ARG  # k > E
     assert L.moe_dispatch(None, fake, 4, 2, 8, -1, fake, B.MOE_BF16, 12, fake, fake, fake,
-                          None, None, fake, fake, 1 << 20) == B.MOE_ERR_UNSUPPORTED  # 24-byte rows
+                          None, None, fake, None, None, fake, 1 << 20) == B.MOE_ERR_UNSUPPORTED  # 24-byte rows
     assert L.moe_dispatch(None, fake, 4, 2, 8, -1, None, 0, 0, None, fake, fake, None, None,
-                          None, fake, 1 << 20) == B.MOE_ERR_INVALID_ARG  # no offsets
+                          None, None, None, fake, 1 << 20) == B.MOE_ERR_INVALID_ARG  # no offsets
+    assert L.moe_dispatch(None, fake, 4, 2, 8, -1, None, 0, 0, fake, fake, fake, None, None,
+                          None, None, fake, fake, 1 << 20) == B.MOE_ERR_INVALID_ARG  # row_weight, no topk_w
     assert L.moe_combine(None, B.MOE_BF16, fake, fake, fake, 4, 2, 12, None, fake) == B.MOE_ERR_UNSUPPORTED
     assert L.moe_combine(None, 7, fake, fake, fake, 4, 2, 16, None, fake) == B.MOE_ERR_INVALID_ARG
-    assert L.moe_expert_ffn(None, B.MOE_BF16, B.MOE_ACT_GELU, fake, fake, 2, 10, 100, 256,
-                            fake, None, None, fake, None, fake, fake) == B.MOE_ERR_UNSUPPORTED
-    assert L.moe_expert_ffn(None, B.MOE_BF16, B.MOE_ACT_SWIGLU, fake, fake, 2, 10, 128, 256,
-                            fake, None, None, fake, None, fake, fake) == B.MOE_ERR_INVALID_ARG
-    assert L.moe_expert_ffn(None, B.MOE_F32, B.MOE_ACT_GELU, fake, fake, 0, 10, 128, 256,
-                            fake, None, None, fake, None, fake, fake) == B.MOE_ERR_INVALID_ARG
+    assert L.moe_combine(None, B.MOE_BF16, None, fake, None, 4, 2, 16, None, fake) == B.MOE_ERR_INVALID_ARG
+
+    def ffn(dt, act, a_rows=None, a_n=0, nseg=2, d=128, dff=256, w3=None):
+        return L.moe_expert_ffn(None, dt, act, fake, a_rows, a_n, fake, nseg, 10, d, dff,
+                                fake, w3, None, fake, None, None, fake, fake)
+
+    assert ffn(B.MOE_BF16, B.MOE_ACT_GELU, d=100) == B.MOE_ERR_UNSUPPORTED
+    assert ffn(B.MOE_BF16, B.MOE_ACT_SWIGLU) == B.MOE_ERR_INVALID_ARG  # no w3
+    assert ffn(B.MOE_F32, B.MOE_ACT_GELU, nseg=0) == B.MOE_ERR_INVALID_ARG
+    # gathered rows: a must hold 1 .. 4 GiB
+    assert ffn(B.MOE_BF16, B.MOE_ACT_GELU, a_rows=fake, a_n=0) == B.MOE_ERR_UNSUPPORTED
+    assert ffn(B.MOE_BF16, B.MOE_ACT_GELU, a_rows=fake, a_n=(1 << 32) // 256 + 1) == B.MOE_ERR_UNSUPPORTED
 
 
 def test_forward_validation_and_workspace():
@@ -162,3 +170,14 @@ def test_reroute_validation():
     assert B.moe_forward_workspace_size(rr) >= B.moe_forward_workspace_size(base) + 64 * 64 * 4
     bad = B.make_config(64, 4096, 11008, 64, 2, B.MOE_ACT_SWIGLU, B.MOE_BF16, capacity_rule=9)
     assert B.moe_forward_workspace_size(bad) == 0
+
+
+def test_fused_forward_workspace():
+    kw = dict(n_tokens=4096, d_model=4096, d_ff=14336, n_experts=8, top_k=2, act=B.MOE_ACT_SWIGLU,
+              dtype=B.MOE_BF16)
+    plain = B.moe_forward_workspace_size(B.make_config(**kw))
+    gather = B.moe_forward_workspace_size(B.make_config(**kw, fuse=B.MOE_FUSE_GATHER))
+    both = B.moe_forward_workspace_size(B.make_config(**kw, fuse=B.MOE_FUSE_GATHER | B.MOE_FUSE_WEIGHT))
+    assert plain - gather >= 8192 * 4096 * 2  # no permuted copy of x
+    assert both - gather >= 8192 * 4  # one weight per row
+    assert B.moe_forward_workspace_size(B.make_config(**kw, fuse=4)) == 0

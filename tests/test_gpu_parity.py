@@ -208,6 +208,34 @@ def test_forward_parity_selection_only_bias():
     assert err <= TOL[cfg.dtype]
 
 
+# ------------------------------------------------------------------ fusions
+@pytest.mark.parametrize("name", list(CONFIGS))
+def test_forward_gather_fusion_is_bit_identical(name):
+    """GEMM1 reading the routed rows of x in place gives the same bits as the permuted
+    copy (the same values reach the same MFMAs in the same order)."""
+    cfg = CONFIGS[name].with_tokens(REDUCED[name]).scaled(d_ff=min(CONFIGS[name].d_ff, 2048))
+    print_case("fusion-gather", name, cfg.n_tokens)
+    inp = synth.DeviceInputs(cfg, DEV)
+    outs = []
+    for fuse in (0, B.MOE_FUSE_GATHER):  # and the same pair with the weight fusion below
+        layer = MoELayer.from_inputs(inp)
+        layer.cfg = cfg.scaled(fuse=fuse)
+        outs.append(layer.forward(inp.x).clone())
+    torch.cuda.synchronize()
+    assert np.array_equal(to_host_bits(outs[0]), to_host_bits(outs[1]))
+
+
+@pytest.mark.parametrize("name", ["switch", "mixtral", "deepseek", "decode", "tiny"])
+@pytest.mark.parametrize("fuse", [0, B.MOE_FUSE_WEIGHT])
+def test_forward_parity_fusion_variants(name, fuse):
+    # the workloads fuse both by default; the unfused path and the weight fusion alone
+    cfg = CONFIGS[name].with_tokens(REDUCED[name]).scaled(fuse=fuse,
+                                                          d_ff=min(CONFIGS[name].d_ff, 4096))
+    print_case("forward-fusion", name, fuse, cfg.n_tokens)
+    err, r, _ = _forward_and_oracle(cfg)
+    assert err <= TOL[cfg.dtype]
+
+
 # ------------------------------------------------------------------ overflow re-routing
 def _reroute_case(L, b, E, k, cap, rounds, renorm=True, sel_only=False):
     """GPU route (on given logits) then GPU re-route; the oracle re-routes the same
@@ -306,18 +334,19 @@ def _distinct_idx(rng, n, E, k, skew=0.0):
     return np.argsort(-score, axis=1)[:, :k].astype(np.int32)
 
 
-def _dispatch(idx_np, E, cap, x):
+def _dispatch(idx_np, E, cap, x, topk_w=None):
     n, k = idx_np.shape
     layer_like = MoELayer.__new__(MoELayer)
     layer_like.cfg = CONFIGS["tiny"].scaled(n_experts=E, top_k=k)
     layer_like.device = torch.device(DEV)
     out = MoELayer.dispatch(layer_like, x, torch.from_numpy(idx_np).to(DEV), capacity=cap,
-                            with_copy=x is not None)
+                            with_copy=x is not None,
+                            topk_w=None if topk_w is None else torch.from_numpy(topk_w).to(DEV))
     torch.cuda.synchronize()
     return out
 
 
-def _check_dispatch(idx, E, cap, out, x_bits=None):
+def _check_dispatch(idx, E, cap, out, x_bits=None, topk_w=None):
     plan = O.plan_dispatch(idx, E, None if cap < 0 else cap)
     total = int(plan.expert_offsets[-1])
     assert np.array_equal(out["expert_offsets"].cpu().numpy(), plan.expert_offsets)
@@ -328,6 +357,9 @@ def _check_dispatch(idx, E, cap, out, x_bits=None):
     if x_bits is not None:
         xp = to_host_bits(out["x_perm"])[:total]
         assert np.array_equal(xp, x_bits[plan.row_token])
+    if topk_w is not None:
+        rw = out["row_weight"].cpu().numpy()[:total]
+        assert np.array_equal(rw.view(np.uint32), topk_w[plan.row_token, plan.row_slot].view(np.uint32))
     return plan
 
 
@@ -343,8 +375,9 @@ def test_dispatch_parity(n, E, k, cap, skew, dtype):
     d = 64 if dtype == "bf16" else 12
     xf = rng.standard_normal((n, d)).astype(np.float32)
     xb = synth.f32_to_bf16_bits(xf) if dtype == "bf16" else xf
-    out = _dispatch(idx, E, cap, _up(xb, dtype))
-    _check_dispatch(idx, E, cap, out, xb)
+    tw = rng.random((n, k)).astype(np.float32)
+    out = _dispatch(idx, E, cap, _up(xb, dtype), tw)
+    _check_dispatch(idx, E, cap, out, xb, tw)
 
 
 def test_dispatch_without_copy_and_empty():
@@ -360,25 +393,33 @@ def test_dispatch_without_copy_and_empty():
 
 
 # ------------------------------------------------------------------ expert FFN
-def _ffn_case(dtype, act, bias, d, d_ff, sizes, seed=0):
+def _ffn_case(dtype, act, bias, d, d_ff, sizes, seed=0, gather=False, scale=False):
+    """Expert FFN over segments.  gather: the rows of a are read through a row map into
+    a larger matrix (repeats included); scale: every output row is multiplied by its own
+    weight.  The oracle applies both to its inputs and outputs directly."""
     rng = np.random.default_rng(seed)
     S = len(sizes)
     rows = int(sum(sizes))
     off = np.concatenate([[0], np.cumsum(sizes)]).astype(np.int32)
     cvt = (lambda a: synth.f32_to_bf16_bits(a)) if dtype == "bf16" else (lambda a: a)
-    a = cvt(rng.standard_normal((max(rows, 1), d)).astype(np.float32))
+    n_a = max(rows, 1) + (37 if gather else 0)
+    a_src = cvt(rng.standard_normal((n_a, d)).astype(np.float32))
+    a_rows = rng.integers(0, n_a, size=max(rows, 1)).astype(np.int32) if gather else None
+    a = a_src[a_rows] if gather else a_src
+    rs = rng.uniform(0.05, 1.0, size=max(rows, 1)).astype(np.float32) if scale else None
     w1 = cvt((rng.standard_normal((S, d_ff, d)) / np.sqrt(d)).astype(np.float32))
     w3 = cvt((rng.standard_normal((S, d_ff, d)) / np.sqrt(d)).astype(np.float32)) if act == "swiglu" else None
     w2 = cvt((rng.standard_normal((S, d, d_ff)) / np.sqrt(d_ff)).astype(np.float32))
     b1 = cvt((0.1 * rng.standard_normal((S, d_ff))).astype(np.float32)) if bias else None
     b2 = cvt((0.1 * rng.standard_normal((S, d))).astype(np.float32)) if bias else None
     up = lambda v: None if v is None else _up(v, dtype)
-    t = dict(a=up(a), w1=up(w1), w3=up(w3), w2=up(w2), b1=up(b1), b2=up(b2))
+    t = dict(a=up(a_src), w1=up(w1), w3=up(w3), w2=up(w2), b1=up(b1), b2=up(b2))
     h = torch.zeros((max(rows, 1), d_ff), dtype=t["a"].dtype, device=DEV)
     y = torch.zeros((max(rows, 1), d), dtype=t["a"].dtype, device=DEV)
     B.moe_expert_ffn(B.MOE_ACT_SWIGLU if act == "swiglu" else B.MOE_ACT_GELU, t["a"],
                      torch.from_numpy(off).to(DEV), S, rows, t["w1"], t["w3"], t["b1"], t["w2"],
-                     t["b2"], h, y)
+                     t["b2"], h, y, a_rows=None if a_rows is None else torch.from_numpy(a_rows).to(DEV),
+                     row_scale=None if rs is None else torch.from_numpy(rs).to(DEV))
     torch.cuda.synchronize()
     a64 = O.widen(a, dtype)
     hg, yg = widen_t(h), widen_t(y)
@@ -392,9 +433,10 @@ def _ffn_case(dtype, act, bias, d, d_ff, sizes, seed=0):
                             b1=None if b1 is None else O.widen(b1[s], dtype),
                             b2=None if b2 is None else O.widen(b2[s], dtype))
         ho = O.expert_hidden(a64[r0:r1], w, act)
+        sc = 1.0 if rs is None else rs[r0:r1, None].astype(np.float64)
         err_h = max(err_h, normwise_err(hg[r0:r1], ho))
-        err_y = max(err_y, normwise_err(yg[r0:r1], O.expert_output(hg[r0:r1], w)))
-        err_e2e = max(err_e2e, normwise_err(yg[r0:r1], O.expert_output(ho, w)))
+        err_y = max(err_y, normwise_err(yg[r0:r1], sc * O.expert_output(hg[r0:r1], w)))
+        err_e2e = max(err_e2e, normwise_err(yg[r0:r1], sc * O.expert_output(ho, w)))
     return err_h, err_y, err_e2e
 
 
@@ -424,6 +466,17 @@ def test_expert_ffn_parity(case):
     assert err_h <= tol, f"h error {err_h}"
     assert err_y <= tol, f"y error given h {err_y}"
     assert err_e2e <= tol, f"y error end to end {err_e2e}"
+
+
+@pytest.mark.parametrize("case", [FFN_CASES[0], FFN_CASES[1], FFN_CASES[2], FFN_CASES[7],
+                                  FFN_CASES[8], FFN_CASES[9]],
+                         ids=lambda c: f"{c[0]}-{c[1]}-{len(c[5])}seg")
+def test_expert_ffn_gather_and_row_scale(case):
+    print_case("expert_ffn-gather-scale", case)
+    for gather, scale in ((True, False), (False, True), (True, True)):
+        err_h, err_y, err_e2e = _ffn_case(*case, seed=5, gather=gather, scale=scale)
+        tol = TOL[case[0]]
+        assert max(err_h, err_y, err_e2e) <= tol, (gather, scale, err_h, err_y, err_e2e)
 
 
 # ------------------------------------------------------------------ combine
