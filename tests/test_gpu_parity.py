@@ -216,13 +216,14 @@ def test_forward_gather_fusion_is_bit_identical(name):
     cfg = CONFIGS[name].with_tokens(REDUCED[name]).scaled(d_ff=min(CONFIGS[name].d_ff, 2048))
     print_case("fusion-gather", name, cfg.n_tokens)
     inp = synth.DeviceInputs(cfg, DEV)
-    outs = []
-    for fuse in (0, B.MOE_FUSE_GATHER):  # and the same pair with the weight fusion below
-        layer = MoELayer.from_inputs(inp)
-        layer.cfg = cfg.scaled(fuse=fuse)
-        outs.append(layer.forward(inp.x).clone())
-    torch.cuda.synchronize()
-    assert np.array_equal(to_host_bits(outs[0]), to_host_bits(outs[1]))
+    for wfuse in (0, B.MOE_FUSE_WEIGHT):
+        outs = []
+        for fuse in (wfuse, wfuse | B.MOE_FUSE_GATHER):
+            layer = MoELayer.from_inputs(inp)
+            layer.cfg = cfg.scaled(fuse=fuse)
+            outs.append(layer.forward(inp.x).clone())
+        torch.cuda.synchronize()
+        assert np.array_equal(to_host_bits(outs[0]), to_host_bits(outs[1])), wfuse
 
 
 @pytest.mark.parametrize("name", ["switch", "mixtral", "deepseek", "decode", "tiny"])
