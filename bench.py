@@ -162,8 +162,13 @@ def kernel_work(cfg, kept: int, touched: int):
     w["shared"] = dict(flops=2.0 * n * d * f * sh * (m1 + 1),
                        bytes=(sh * (m1 + 1) * f * d * es + n * d * es * 2 + n * sh * f * es * 2)
                        if sh else 0)
-    w["dispatch"] = dict(flops=0.0, bytes=n * d * es + kept * d * es + n * k * 4 * 2 + kept * 4)
-    w["combine"] = dict(flops=0.0, bytes=kept * d * es + n * k * 8 + n * d * es * (2 if sh else 1))
+    gather, wscale = bool(cfg.fuse & 1), bool(cfg.fuse & 2)
+    # dispatch: ids in, slot map out, row map (and row weights) out; the row copy of x
+    # only without the gather fusion
+    w["dispatch"] = dict(flops=0.0, bytes=n * k * 4 * 2 + kept * 4 + (kept * 8 if wscale else 0)
+                         + (0 if gather else n * d * es + kept * d * es))
+    w["combine"] = dict(flops=0.0, bytes=kept * d * es + n * k * (4 if wscale else 8)
+                        + n * d * es * (2 if sh else 1))
     w["route"] = dict(flops=2.0 * n * d * cfg.n_experts,
                       bytes=n * d * es + d * cfg.n_experts * 4 + n * (cfg.n_experts * 4 + k * 8))
     return w

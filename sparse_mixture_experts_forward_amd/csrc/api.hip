@@ -201,7 +201,8 @@ moe_status run_route(hipStream_t st, const void* x, moe_dtype xt, int64_t n, int
 moe_status run_dispatch(hipStream_t st, const int32_t* idx, int64_t n, int32_t k, int32_t e,
                         int64_t cap, const void* x, int64_t row_bytes, int32_t* offsets,
                         int32_t* row_token, int32_t* slot_row, int32_t* kept, int32_t* dropped,
-                        void* x_perm, const float* topk_w, float* row_weight, void* ws) {
+                        void* x_perm, const float* topk_w, float* row_weight, void* ws,
+                        float* drop_rate = nullptr, int32_t* zero_out = nullptr) {
   Carve c(ws);
   const moe::DispatchGrid g = moe::dispatch_grid(n, k);
   int32_t* hist = c.take<int32_t>(g.n_blocks * e);
@@ -209,7 +210,7 @@ moe_status run_dispatch(hipStream_t st, const int32_t* idx, int64_t n, int32_t k
   int32_t* kept_tmp = c.take<int32_t>(e);
   return hip_check(moe::launch_dispatch(st, idx, n, k, e, cap, x, row_bytes, offsets, row_token,
                                         slot_row, kept, dropped, x_perm, hist, base, kept_tmp,
-                                        topk_w, row_weight),
+                                        topk_w, row_weight, drop_rate, zero_out),
                    "dispatch kernels launch");
 }
 
@@ -651,19 +652,18 @@ moe_status moe_forward(void* stream, const moe_config* cfg, const moe_weights* w
                     o.prob_mean, o.aux, o.monitor, L.route_ws));
   MOE_TRY(mark(1));
   // a4-a5: capacity (slots over it re-routed first if asked) and permutation
-  if (reroute || o.n_rerouted)
+  if (reroute)
     MOE_TRY(hip_check(moe::launch_reroute(st, logits, w->logit_bias, n, k, e, c.renormalize ? 1 : 0,
-                                          c.bias_selection_only ? 1 : 0, reroute ? cap : -1,
-                                          reroute ? clamp_rounds(c.reroute_rounds, e, k) : 0,
+                                          c.bias_selection_only ? 1 : 0, cap,
+                                          clamp_rounds(c.reroute_rounds, e, k),
                                           idx, tw, o.n_rerouted, L.rr),
                       "re-routing launch"));
   const bool gather = fuse_gather(c), wscale = fuse_weight(c);
   MOE_TRY(run_dispatch(st, idx, n, k, e, cap, x, c.d_model * static_cast<int64_t>(es), offsets,
                        L.row_token, slot_row, o.kept_count, dropped,
                        gather ? nullptr : L.x_perm, wscale ? tw : nullptr,
-                       wscale ? L.row_w : nullptr, L.dispatch_ws));
-  if (o.monitor)
-    MOE_TRY(hip_check(moe::launch_drop_rate(st, dropped, n * k, o.monitor + 4), "drop rate launch"));
+                       wscale ? L.row_w : nullptr, L.dispatch_ws,
+                       o.monitor ? o.monitor + 4 : nullptr, reroute ? nullptr : o.n_rerouted));
   MOE_TRY(mark(2));
   // a8 (forked): shared experts, all tokens, on the side stream, concurrent with the
   // routed experts (forked after the latency-bound router and dispatch, whose few

@@ -121,11 +121,13 @@ __global__ __launch_bounds__(kThreads) void dispatch_scan_kernel(
   }
 }
 
-// One workgroup: exclusive scan of the kept counts over experts -> expert_offsets.
+// One workgroup: exclusive scan of the kept counts over experts -> expert_offsets, the
+// dropped count and (optional) the drop rate n_dropped / (N k) and a zeroed counter.
 __global__ __launch_bounds__(kThreads) void dispatch_offsets_kernel(
     const int32_t* __restrict__ kept, int E, int64_t n_assign,
     int32_t* __restrict__ expert_offsets, int32_t* __restrict__ kept_count,
-    int32_t* __restrict__ n_dropped) {
+    int32_t* __restrict__ n_dropped, float* __restrict__ drop_rate,
+    int32_t* __restrict__ zero_out) {
   __shared__ int wsum[kThreads / kWave];
   int running = 0;
   for (int e0 = 0; e0 < E; e0 += kThreads) {
@@ -141,7 +143,11 @@ __global__ __launch_bounds__(kThreads) void dispatch_offsets_kernel(
   }
   if (threadIdx.x == 0) {
     expert_offsets[E] = running;
-    if (n_dropped) n_dropped[0] = static_cast<int32_t>(n_assign - running);
+    const int64_t dropped = n_assign - running;
+    if (n_dropped) n_dropped[0] = static_cast<int32_t>(dropped);
+    if (drop_rate)
+      drop_rate[0] = n_assign > 0 ? static_cast<float>(static_cast<double>(dropped) / n_assign) : 0.f;
+    if (zero_out) zero_out[0] = 0;
   }
 }
 
@@ -402,7 +408,8 @@ hipError_t launch_dispatch(hipStream_t st, const int32_t* topk_idx, int64_t n, i
                            int32_t* expert_offsets, int32_t* row_token, int32_t* slot_row,
                            int32_t* kept_count, int32_t* n_dropped, void* x_perm,
                            int32_t* blk_hist, int32_t* blk_base, int32_t* kept_tmp,
-                           const float* topk_w, float* row_weight) {
+                           const float* topk_w, float* row_weight, float* drop_rate,
+                           int32_t* zero_out) {
   const DispatchGrid g = dispatch_grid(n, k);
   if (g.n_blocks > 0) {
     hipLaunchKernelGGL(dispatch_hist_kernel, dim3(static_cast<unsigned>(g.n_blocks)),
@@ -416,7 +423,7 @@ hipError_t launch_dispatch(hipStream_t st, const int32_t* topk_idx, int64_t n, i
   hipError_t err = hipGetLastError();
   if (err != hipSuccess) return err;
   hipLaunchKernelGGL(dispatch_offsets_kernel, dim3(1), dim3(kThreads), 0, st, kept_tmp, e, n * k,
-                     expert_offsets, kept_count, n_dropped);
+                     expert_offsets, kept_count, n_dropped, drop_rate, zero_out);
   err = hipGetLastError();
   if (err != hipSuccess || g.n_blocks == 0) return err;
   hipLaunchKernelGGL(dispatch_scatter_kernel, dim3(static_cast<unsigned>(g.n_blocks)),

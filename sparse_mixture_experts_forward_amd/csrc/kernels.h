@@ -69,8 +69,7 @@ hipError_t launch_route_finalize(hipStream_t st, const float* part_prob,
                                  const int32_t* part_cnt, const float* part_mon, int64_t rows,
                                  int64_t n, int e, int k, int32_t* sel_count, float* prob_mean,
                                  float* aux, float* monitor, double* term, int64_t* cnt);
-// out[0] = n_dropped / (N k)
-hipError_t launch_drop_rate(hipStream_t st, const int32_t* n_dropped, int64_t nk, float* out);
+
 
 // ---------------------------------------------------------------- dispatch
 struct DispatchGrid {
@@ -84,7 +83,8 @@ hipError_t launch_dispatch(hipStream_t st, const int32_t* topk_idx, int64_t n, i
                            int32_t* expert_offsets, int32_t* row_token, int32_t* slot_row,
                            int32_t* kept_count, int32_t* n_dropped, void* x_perm,
                            int32_t* blk_hist, int32_t* blk_base, int32_t* kept_tmp,
-                           const float* topk_w, float* row_weight);
+                           const float* topk_w, float* row_weight, float* drop_rate = nullptr,
+                           int32_t* zero_out = nullptr);
 
 // Workspace of the overflow re-routing (all device arrays): blk_hist / blk_base
 // [E][n_blocks] (dispatch_grid), kept / room [E], state [N*k], thr_z / thr_e [N],

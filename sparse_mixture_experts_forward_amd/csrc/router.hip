@@ -549,11 +549,6 @@ __global__ __launch_bounds__(kThreads) void route_aux_kernel(
   }
 }
 
-// drop rate = n_dropped / (N k), written after the dispatch.
-__global__ void route_drop_rate_kernel(const int32_t* __restrict__ n_dropped, int64_t nk,
-                                       float* __restrict__ out) {
-  if (threadIdx.x == 0) out[0] = nk > 0 ? static_cast<float>(static_cast<double>(n_dropped[0]) / nk) : 0.f;
-}
 
 template <typename XT, int ET>
 hipError_t launch_route_t(hipStream_t st, const void* x, int64_t n, int64_t d,
@@ -695,11 +690,6 @@ hipError_t launch_route_finalize(hipStream_t st, const float* part_prob,
   if (aux || monitor)
     hipLaunchKernelGGL(route_aux_kernel, dim3(1), dim3(kThreads), 0, st, term, cnt, part_mon, rows,
                        n, e, aux, monitor);
-  return hipGetLastError();
-}
-
-hipError_t launch_drop_rate(hipStream_t st, const int32_t* n_dropped, int64_t nk, float* out) {
-  hipLaunchKernelGGL(route_drop_rate_kernel, dim3(1), dim3(kWave), 0, st, n_dropped, nk, out);
   return hipGetLastError();
 }
 
