@@ -235,9 +235,11 @@ moe_status run_ffn(hipStream_t st, moe_dtype dt, moe_act act, const void* a, int
                    int64_t w_seg_stride, const void* w2, const void* b2, int64_t w2_kchunk,
                    int64_t w2_kbatch_stride, void* h, void* y,
                    const std::function<moe_status()>& between = nullptr,
-                   const int32_t* a_rows = nullptr, const float* row_scale = nullptr) {
+                   const int32_t* a_rows = nullptr, const float* row_scale = nullptr,
+                   int split_g = 0, float* split_buf = nullptr, int32_t* split_desc = nullptr) {
   const bool bf = dt == MOE_BF16;
   moe::GemmArgs g1{};
+  g1.split_g = split_g; g1.split_buf = split_buf; g1.split_desc = split_desc;
   g1.a = a; g1.lda = lda; g1.a_rows = a_rows;
   g1.b0 = w1; g1.b1 = (act == MOE_ACT_SWIGLU) ? w3 : nullptr;
   g1.ldb = d; g1.b_seg_stride = w_seg_stride;
@@ -251,6 +253,7 @@ moe_status run_ffn(hipStream_t st, moe_dtype dt, moe_act act, const void* a, int
                     "expert GEMM1 launch"));
   if (between) MOE_TRY(between());
   moe::GemmArgs g2{};
+  g2.split_g = split_g; g2.split_buf = split_buf; g2.split_desc = split_desc;
   g2.a = h; g2.lda = d_ff; g2.row_scale = row_scale;
   g2.b0 = w2; g2.b1 = nullptr;
   g2.ldb = w2_kchunk; g2.b_seg_stride = w_seg_stride;
@@ -323,6 +326,15 @@ int64_t max_rows_of(int64_t n, int32_t e, int32_t k, int64_t cap) {
   return lim < all ? lim : all;
 }
 
+// Compute units of the current device: the workgroups of one round of the 256-row GEMM
+// tiles (one per CU), which the routed expert GEMMs use to split a partial last round.
+int cu_count() {
+  int dev = 0, cu = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return 0;
+  if (hipDeviceGetAttribute(&cu, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) return 0;
+  return cu;
+}
+
 // The fusions moe_forward takes for a configuration: the gather needs every byte offset
 // into x below 2^32 (32-bit load offsets in the GEMM).
 bool fuse_gather(const moe_config& c) {
@@ -333,7 +345,9 @@ bool fuse_weight(const moe_config& c) { return (c.fuse & MOE_FUSE_WEIGHT) != 0; 
 
 struct ForwardLayout {
   int32_t *idx, *sel, *offsets, *row_token, *slot_row, *kept, *dropped;
-  float *w, *pm, *aux, *logits, *row_w;
+  float *w, *pm, *aux, *logits, *row_w, *split_buf;
+  int32_t* split_desc;
+  int split_g;
   void *route_ws, *dispatch_ws, *x_perm, *h, *y_rows, *h_sh, *y_sh;
   moe::RerouteWs rr;
   size_t used;
@@ -365,6 +379,11 @@ ForwardLayout forward_layout(const moe_config& c, void* ws) {
   }
   if (!fuse_gather(c)) L.x_perm = cv.take<char>(R * c.d_model * es);
   if (fuse_weight(c)) L.row_w = cv.take<float>(R);
+  if (c.dtype == MOE_BF16) {
+    L.split_g = cu_count();
+    L.split_buf = cv.take<float>(moe::gemm_split_floats(L.split_g));
+    L.split_desc = cv.take<int32_t>(moe::gemm_split_desc_ints(L.split_g));
+  }
   L.h = cv.take<char>(R * c.d_ff * es);
   L.y_rows = cv.take<char>(R * c.d_model * es);
   if (c.n_shared > 0) {
@@ -688,7 +707,8 @@ moe_status moe_forward(void* stream, const moe_config* cfg, const moe_weights* w
   MOE_TRY(run_ffn(st, c.dtype, c.act, gather ? x : L.x_perm, c.d_model, offsets, e, 0, R,
                   c.d_model, c.d_ff, w->w1, w->w3, w->b1, c.d_ff * c.d_model, w->w2, w->b2,
                   c.d_ff, 0, L.h, L.y_rows, [&]() { return mark(3); },
-                  gather ? L.row_token : nullptr, wscale ? L.row_w : nullptr));
+                  gather ? L.row_token : nullptr, wscale ? L.row_w : nullptr, L.split_g,
+                  L.split_buf, L.split_desc));
   MOE_TRY(mark(4));
   // join: the combine needs the shared experts' output
   if (side) MOE_TRY(hip_check(hipStreamWaitEvent(st, side->join, 0), "join wait"));

@@ -52,6 +52,11 @@ struct Tile {
   int64_t row0;
   int m_valid;
   int nt;
+  // reduction range of this work item, in stages of the K loop, and for a tile of the
+  // last partial round that is split along K: its part, the number of parts and its
+  // index among the split tiles (nparts == 1: a whole tile)
+  int k_stage0, k_stages;
+  int part, nparts, split_q;
 };
 
 // Block-wide: find this workgroup's tile.  Returns false (uniformly) if it has none.
@@ -74,10 +79,16 @@ __device__ __forceinline__ void seg_bounds(const int32_t* __restrict__ seg_off, 
   hi = max(min(max(seg_off[s + 1], 0), max_rows), lo);
 }
 
+// Work items: the tiles in order, except that when there are at most four full rounds
+// of split_g resident workgroups and the last round would be at most half full, each
+// of its r tiles is split along K into S = min(split_g / r, 4, KT / 8) parts, so that
+// the round is filled (split_g = 0: never).  Parts of one tile are r work items apart.
+// (With more rounds the tail is a small share of the time, and the parts' extra
+// prologues, partial stores and the finishing launch cost more than they save.)
 template <int BM>
 __device__ bool schedule_tile(const int32_t* __restrict__ seg_off, int n_seg,
-                              int single_rows, int max_rows, int n_ntiles, SchedSmem& sm,
-                              Tile& tile) {
+                              int single_rows, int max_rows, int n_ntiles, int KT, int split_g,
+                              int32_t* split_desc, SchedSmem& sm, Tile& tile) {
   int* s_start = sm.start;
   int* s_wsum = sm.wsum;
   const int tid = threadIdx.x;
@@ -111,6 +122,11 @@ __device__ bool schedule_tile(const int32_t* __restrict__ seg_off, int n_seg,
   if (tid == 0) s_start[n_seg] = total;
   __syncthreads();
 
+  tile.k_stage0 = 0;
+  tile.k_stages = KT;
+  tile.part = 0;
+  tile.nparts = 1;
+  tile.split_q = 0;
 #if MOE_GEMM_XCD_REMAP
   const int xcd = blockIdx.x % kXcds;
   const int i = blockIdx.x / kXcds;
@@ -118,8 +134,27 @@ __device__ bool schedule_tile(const int32_t* __restrict__ seg_off, int n_seg,
   const int L = xcd * per + i;
   if (i >= per || L >= total) return false;
 #else
-  const int L = blockIdx.x;
-  if (L >= total) return false;
+  int L = blockIdx.x;
+  const int full = split_g > 0 ? total / split_g * split_g : total;
+  const int r = total - full;
+  const int ns = (r > 0 && 2 * r <= split_g && full <= 4 * split_g)
+                     ? min(min(split_g / r, 4), KT / 8) : 1;
+  // the number of split tiles, for the launch that finishes them
+  if (split_desc && blockIdx.x == 0 && tid == 0) split_desc[0] = ns > 1 ? r : 0;
+  if (ns > 1) {
+    if (L >= full + r * ns) return false;
+    if (L >= full) {
+      const int q = L - full;
+      tile.split_q = q % r;
+      tile.part = q / r;
+      tile.nparts = ns;
+      tile.k_stage0 = tile.part * KT / ns;
+      tile.k_stages = (tile.part + 1) * KT / ns - tile.k_stage0;
+      L = full + tile.split_q;
+    }
+  } else if (L >= total) {
+    return false;
+  }
 #endif
 #pragma unroll
   for (int u = 0; u < 2; ++u) {
@@ -213,6 +248,7 @@ struct TileIO {
   // LDS ring depth of the weight operand: the 256-row tiles spend the whole 160 KB of
   // LDS on 2 activation and 3 weight stages, so weights are loaded three stages ahead
   static constexpr int NBB = BM >= 256 ? 3 : 2;
+  static constexpr bool kKSplit = KSPLIT;
   const uint16_t* a_base;
   const uint16_t* b_base0;
   const uint16_t* b_base1;
@@ -427,30 +463,61 @@ __device__ __forceinline__ void k_loop(const IO& io, uint16_t* As0, uint16_t* As
 #undef MOE_STAGE
 }
 
-// The rest of a tile for a wave with TA active row blocks: the K loop, then the epilogue.
-// Each TA has its own accumulators, so no accumulator state is shared between the
-// variants.  Register 4q + r of tile (tn, tm) is the output element (activation row
+// Float32 partial accumulators of split tiles: slot (split_q * nparts + part) holds a
+// workgroup's accumulators in register order (float4 chunk c of thread t at [c][t], so
+// each access instruction covers 4 KB contiguously).
+template <class IO>
+struct SplitSlot {
+  static constexpr int kChunks = IO::TN * IO::TM * IO::S::ACC / 4;  // float4 per thread
+  static constexpr int64_t kFloats = static_cast<int64_t>(kChunks) * 4 * kThreads;
+  __device__ static f32x4_t* at(float* buf, int slot) {
+    return reinterpret_cast<f32x4_t*>(buf + static_cast<int64_t>(slot) * kFloats);
+  }
+  __device__ static int chunk(int tn, int tm, int v) {
+    return (tn * IO::TM + tm) * (IO::S::ACC / 4) + v;
+  }
+};
+
+// A part of a split tile: store the partial accumulators, and (part 0) the tile, for
+// gemm_split_finish_kernel, which sums the parts in part order after this launch.
+template <class IO, int TA>
+__device__ __forceinline__ void split_store(const GemmArgs& g, const Tile& tile,
+                                            const typename IO::S::acc_t (&acc)[IO::TN][IO::TM]) {
+  using SS = SplitSlot<IO>;
+  const int tid = threadIdx.x;
+  f32x4_t* mine = SS::at(g.split_buf, tile.split_q * tile.nparts + tile.part);
+#pragma unroll
+  for (int tn = 0; tn < IO::TN; ++tn)
+#pragma unroll
+    for (int tm = 0; tm < TA; ++tm)
+#pragma unroll
+      for (int v = 0; v < IO::S::ACC / 4; ++v) {
+        f32x4_t q;
+#pragma unroll
+        for (int r = 0; r < 4; ++r) q[r] = acc[tn][tm][4 * v + r];
+        mine[SS::chunk(tn, tm, v) * kThreads + tid] = q;
+      }
+  if (tile.part == 0 && tid == 0) {
+    int32_t* d = g.split_desc + 1 + 5 * tile.split_q;
+    d[0] = tile.seg;
+    d[1] = static_cast<int32_t>(tile.row0);
+    d[2] = tile.m_valid;
+    d[3] = tile.nt;
+    d[4] = tile.nparts;
+  }
+}
+
+// Epilogue of a tile for a wave with TA active row blocks: activation and bf16 stores.
+// Register 4q + r of tile (tn, tm) is the output element (activation row
 // (2 tm + wm)*M + row(lane), weight row tn*M + ni(q, lane) + r); the four r are
 // consecutive output columns (one 8-byte store of bf16).
 template <class IO, int EPI, int TA>
-__device__ __forceinline__ void tile_body(const GemmArgs& g, const Tile& tile, const IO& io,
-                                          uint16_t* As0, uint16_t* As1, uint16_t* Bs0,
-                                          uint16_t* Bs1, uint16_t* Bs2, int KT) {
+__device__ __forceinline__ void tile_epilogue(const GemmArgs& g, const Tile& tile, int lane,
+                                              int wm, int wn,
+                                              typename IO::S::acc_t (&acc)[IO::TN][IO::TM]) {
   using S = typename IO::S;
   constexpr int TN = IO::TN;
-  typename S::acc_t acc[TN][IO::TM];
-#pragma unroll
-  for (int a = 0; a < TN; ++a)
-#pragma unroll
-    for (int b = 0; b < TA; ++b)
-#pragma unroll
-      for (int r = 0; r < S::ACC; ++r) acc[a][b][r] = 0.f;
-  k_loop<IO, TA>(io, As0, As1, Bs0, Bs1, Bs2, KT, acc);
-  // no load may still be writing this workgroup's LDS when it exits
-  __builtin_amdgcn_s_waitcnt(0);
-  if constexpr (TA == 0) return;
-
-  const int lane = io.lane, wm = io.wm, wn = io.wn, frow = S::row(lane);
+  const int frow = S::row(lane);
   uint16_t* __restrict__ C = static_cast<uint16_t*>(g.c);
   constexpr int NQ = S::ACC / 4;
   if constexpr (EPI == EPI_SWIGLU) {
@@ -512,6 +579,36 @@ __device__ __forceinline__ void tile_body(const GemmArgs& g, const Tile& tile, c
   }
 }
 
+// The rest of a tile for a wave with TA active row blocks: the K loop, then the epilogue
+// (or, for a part of a split tile, the store of its partial sums).  Each TA has its own
+// accumulators, so no accumulator state is shared between the variants.
+template <class IO, int EPI, int TA>
+__device__ __forceinline__ void tile_body(const GemmArgs& g, const Tile& tile, const IO& io,
+                                          uint16_t* As0, uint16_t* As1, uint16_t* Bs0,
+                                          uint16_t* Bs1, uint16_t* Bs2, int KT) {
+  using S = typename IO::S;
+  constexpr int TN = IO::TN;
+  typename S::acc_t acc[TN][IO::TM];
+#pragma unroll
+  for (int a = 0; a < TN; ++a)
+#pragma unroll
+    for (int b = 0; b < TA; ++b)
+#pragma unroll
+      for (int r = 0; r < S::ACC; ++r) acc[a][b][r] = 0.f;
+  k_loop<IO, TA>(io, As0, As1, Bs0, Bs1, Bs2, KT, acc);
+  // no load may still be writing this workgroup's LDS when it exits
+  __builtin_amdgcn_s_waitcnt(0);
+  if constexpr (!IO::kKSplit) {  // the K-batched products never split
+    if (tile.nparts > 1) {
+      split_store<IO, TA>(g, tile, acc);
+      return;
+    }
+  }
+  if constexpr (TA == 0) return;
+
+  tile_epilogue<IO, EPI, TA>(g, tile, io.lane, io.wm, io.wn, acc);
+}
+
 // ------------------------------------------------------------------ bf16 MFMA kernel
 template <int BM, int EPI, bool KSPLIT>
 __global__ __launch_bounds__(kThreads, 1) void gemm_bf16_kernel(GemmArgs g) {
@@ -533,9 +630,14 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_bf16_kernel(GemmArgs g) {
 
   const int n_ntiles = (EPI == EPI_SWIGLU) ? (g.n_out + 127) / 128 : (g.n_out + 255) / 256;
   Tile tile;
-  if (!schedule_tile<BM>(g.seg_off, g.n_seg, g.single_rows, g.max_rows, n_ntiles, sched, tile))
+  if (!schedule_tile<BM>(g.seg_off, g.n_seg, g.single_rows, g.max_rows, n_ntiles, g.k / kBK,
+                         KSPLIT ? 0 : g.split_g, KSPLIT ? nullptr : g.split_desc, sched, tile))
     return;
   __syncthreads();  // the scheduler scratch is dead from here on
+  // the work item is uniform over the workgroup: keep its fields in scalar registers
+  tile.k_stage0 = __builtin_amdgcn_readfirstlane(tile.k_stage0);
+  tile.k_stages = __builtin_amdgcn_readfirstlane(tile.k_stages);
+  tile.nparts = __builtin_amdgcn_readfirstlane(tile.nparts);
 
   const int tid = threadIdx.x;
   const int lane = tid & (kWave - 1);
@@ -551,7 +653,9 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_bf16_kernel(GemmArgs g) {
   // A rows: the tile's rows of a, or with a_rows the rows of a they name (the gather of
   // the routed tokens; the caller keeps every byte offset below 2^32)
   const int32_t* __restrict__ a_rows = g.a_rows;
-  io.a_base = static_cast<const uint16_t*>(g.a) + (a_rows ? 0 : tile.row0 * g.lda);
+  // (a split tile's part starts k_stage0 stages into the reduction)
+  const int64_t k_ofs = static_cast<int64_t>(tile.k_stage0) * kBK;
+  io.a_base = static_cast<const uint16_t*>(g.a) + (a_rows ? 0 : tile.row0 * g.lda) + k_ofs;
 #pragma unroll
   for (int j = 0; j < IO::A_GRP; ++j) {
     const int i = 8 * (wave + 4 * j) + dl_row;  // LDS row of the tile
@@ -560,9 +664,10 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_bf16_kernel(GemmArgs g) {
     const int chunk = ((lane & 7) ^ lds_swizzle(i)) * 8;
     io.a_off[j] = (src * static_cast<uint32_t>(g.lda) + chunk) * 2u;
   }
-  io.b_base0 = static_cast<const uint16_t*>(g.b0) + tile.seg * g.b_seg_stride;
-  io.b_base1 = (EPI == EPI_SWIGLU) ? static_cast<const uint16_t*>(g.b1) + tile.seg * g.b_seg_stride
-                                   : io.b_base0;
+  io.b_base0 = static_cast<const uint16_t*>(g.b0) + tile.seg * g.b_seg_stride + k_ofs;
+  io.b_base1 = (EPI == EPI_SWIGLU)
+                   ? static_cast<const uint16_t*>(g.b1) + tile.seg * g.b_seg_stride + k_ofs
+                   : io.b_base0;
 #pragma unroll
   for (int j = 0; j < IO::B_GRP; ++j) {
     const int i = 8 * (wave + 4 * j) + dl_row;  // LDS row of the tile
@@ -579,7 +684,7 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_bf16_kernel(GemmArgs g) {
   io.a_row = (io.wm * S::M + frow) * kBK;  // row block wm; the wave's next blocks are 2 apart
   const int wm = io.wm;
 
-  const int KT = g.k / kBK;
+  const int KT = tile.k_stages;
   constexpr int LA = IO::A_GRP, LB = IO::B_GRP;  // direct-to-LDS loads per wave per stage
   // prologue: with a 3-deep weight ring, issue A0 B0 B1 A1 B2 (at every later boundary
   // exactly the weight loads of the boundary before may still be in flight); else
@@ -619,6 +724,57 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_bf16_kernel(GemmArgs g) {
   }
 }
 
+// Finishes the split tiles of the preceding gemm_bf16_kernel launch: workgroup q sums
+// the parts of split tile q in part order and runs the tile's epilogue.
+template <int BM, int EPI>
+__global__ __launch_bounds__(kThreads, 1) void gemm_split_finish_kernel(GemmArgs g) {
+  using IO = TileIO<BM, EPI == EPI_SWIGLU, false>;
+  using S = typename IO::S;
+  using SS = SplitSlot<IO>;
+  constexpr int TM = IO::TM;
+  const int q = blockIdx.x;
+  if (q >= g.split_desc[0]) return;
+  const int32_t* d = g.split_desc + 1 + 5 * q;
+  Tile tile;
+  tile.seg = d[0];
+  tile.row0 = d[1];
+  tile.m_valid = d[2];
+  tile.nt = d[3];
+  tile.nparts = d[4];
+  tile.part = 0;
+  tile.split_q = q;
+  tile.k_stage0 = 0;
+  tile.k_stages = 0;
+  const int tid = threadIdx.x, lane = tid & (kWave - 1);
+  const int wave = __builtin_amdgcn_readfirstlane(tid / kWave);
+  const int wm = wave >> 1, wn = wave & 1;
+  const int nb = (tile.m_valid + S::M - 1) / S::M;
+  const int ta = __builtin_amdgcn_readfirstlane(min(max((nb - wm + 1) / 2, 0), TM));
+  typename S::acc_t acc[IO::TN][TM];
+  auto sum_parts = [&](auto ta_c) {
+    constexpr int TA = decltype(ta_c)::value;
+    for (int p = 0; p < tile.nparts; ++p) {
+      const f32x4_t* sp = SS::at(g.split_buf, q * tile.nparts + p);
+#pragma unroll
+      for (int tn = 0; tn < IO::TN; ++tn)
+#pragma unroll
+        for (int tm = 0; tm < TA; ++tm)
+#pragma unroll
+          for (int v = 0; v < S::ACC / 4; ++v) {
+            const f32x4_t x = sp[SS::chunk(tn, tm, v) * kThreads + tid];
+#pragma unroll
+            for (int r = 0; r < 4; ++r)
+              acc[tn][tm][4 * v + r] = p == 0 ? x[r] : acc[tn][tm][4 * v + r] + x[r];
+          }
+    }
+    tile_epilogue<IO, EPI, TA>(g, tile, lane, wm, wn, acc);
+  };
+  if (ta == 1) sum_parts(std::integral_constant<int, 1>{});
+  else if (ta == 2) sum_parts(std::integral_constant<int, 2>{});
+  else if (ta == 3) sum_parts(std::integral_constant<int, 3>{});
+  else if (ta >= 4) sum_parts(std::integral_constant<int, 4>{});
+}
+
 // ------------------------------------------------------------------ float32 SIMT kernel
 constexpr int kFBM = 64, kFBN = 64, kFBK = 16, kFPad = 4;
 
@@ -630,7 +786,8 @@ __global__ __launch_bounds__(kThreads) void gemm_f32_kernel(GemmArgs g) {
   __shared__ SchedSmem sched;
   const int n_ntiles = (g.n_out + kFBN - 1) / kFBN;
   Tile tile;
-  if (!schedule_tile<kFBM>(g.seg_off, g.n_seg, g.single_rows, g.max_rows, n_ntiles, sched, tile))
+  if (!schedule_tile<kFBM>(g.seg_off, g.n_seg, g.single_rows, g.max_rows, n_ntiles, 0, 0,
+                           nullptr, sched, tile))
     return;
 
   const int tid = threadIdx.x;
@@ -716,11 +873,24 @@ int64_t grid_for(int64_t max_rows, int n_seg_eff, int bm, int n_ntiles) {
 }
 
 template <int BM, int EPI>
-hipError_t launch_bf16_bm(hipStream_t st, const GemmArgs& g, int64_t max_rows, bool ksplit) {
+hipError_t launch_bf16_bm(hipStream_t st, GemmArgs g, int64_t max_rows, bool ksplit) {
   const int n_ntiles = (EPI == EPI_SWIGLU) ? (g.n_out + 127) / 128 : (g.n_out + 255) / 256;
   const int n_seg_eff = g.seg_off ? g.n_seg : 1;
-  const int64_t grid = grid_for(max_rows, n_seg_eff, BM, n_ntiles);
+  int64_t grid = grid_for(max_rows, n_seg_eff, BM, n_ntiles);
   if (grid <= 0) return hipSuccess;
+  // splitting can only happen with at most four full rounds (see schedule_tile); where
+  // the bound on the tiles already rules that out, neither split nor finish
+  if (grid > 5 * static_cast<int64_t>(g.split_g)) g.split_g = 0;
+  grid += g.split_g;  // a split last round has at most split_g work items more
+  if (g.split_g > 0 && !ksplit) {
+    hipLaunchKernelGGL((gemm_bf16_kernel<BM, EPI, false>), dim3(static_cast<unsigned>(grid)),
+                       dim3(kThreads), 0, st, g);
+    const hipError_t err = hipGetLastError();
+    if (err != hipSuccess) return err;
+    hipLaunchKernelGGL((gemm_split_finish_kernel<BM, EPI>), dim3(static_cast<unsigned>(g.split_g / 2)),
+                       dim3(kThreads), 0, st, g);
+    return hipGetLastError();
+  }
   if (ksplit)
     hipLaunchKernelGGL((gemm_bf16_kernel<BM, EPI, true>), dim3(static_cast<unsigned>(grid)),
                        dim3(kThreads), 0, st, g);
@@ -737,9 +907,16 @@ hipError_t launch_bf16_epi(hipStream_t st, const GemmArgs& g, int64_t max_rows) 
   const int64_t avg = max_rows / (n_seg_eff > 0 ? n_seg_eff : 1);
   // 256-row tiles skip the MFMAs of row blocks past a segment's end, so they serve any
   // segment of a few dozen rows or more; below that the weights dominate and 32-row
-  // tiles (two workgroups per CU) keep more weight loads in flight
-  if (avg >= 48) return launch_bf16_bm<256, EPI>(st, g, max_rows, ksplit);
-  return launch_bf16_bm<32, EPI>(st, g, max_rows, ksplit);
+  // tiles (two workgroups per CU) keep more weight loads in flight.  Only 256-row tiles
+  // without K batches split their last round.
+  if (avg >= 48) {
+    GemmArgs g2 = g;
+    if (ksplit || !g.split_buf || !g.split_desc) g2.split_g = 0;
+    return launch_bf16_bm<256, EPI>(st, g2, max_rows, ksplit);
+  }
+  GemmArgs g2 = g;
+  g2.split_g = 0;
+  return launch_bf16_bm<32, EPI>(st, g2, max_rows, ksplit);
 }
 
 template <int EPI>

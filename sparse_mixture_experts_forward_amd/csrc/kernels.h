@@ -129,7 +129,18 @@ struct GemmArgs {
   int32_t max_rows;  // rows of A and C; segment bounds are clamped to [0, max_rows]
   int32_t n_out;  // output columns (h columns for SwiGLU)
   int32_t k;      // reduction length
+  // Split of the last partial round along K (bf16, 256-row tiles, no K batches):
+  // split_g resident workgroups per round (0: no split), split_buf float32 partials
+  // (gemm_split_floats(split_g)), split_desc the split tiles' count and descriptors
+  // (gemm_split_desc_ints(split_g)); a second launch finishes the split tiles.
+  int32_t split_g;
+  float* split_buf;
+  int32_t* split_desc;
 };
+
+// Sizes of the split buffers for g resident workgroups.
+inline int64_t gemm_split_floats(int g) { return static_cast<int64_t>(g) * 256 * 256; }
+inline int64_t gemm_split_desc_ints(int g) { return 1 + 5 * static_cast<int64_t>(g / 2); }
 
 hipError_t launch_gemm(hipStream_t st, bool bf16, Epilogue epi, const GemmArgs& g,
                        int64_t max_rows);
