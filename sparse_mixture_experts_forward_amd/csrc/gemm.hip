@@ -13,18 +13,23 @@
 //     (v_mfma_f32_16x16x32_bf16 when BM = 32, i.e. 16 rows per wave);
 //   * weights are the MFMA A operand, activations the B operand, so a lane ends with 4
 //     consecutive output columns of one row (8-byte stores of bf16);
-//   * K advances 32 at a time through a ring of 4 LDS stages filled by direct-to-LDS
-//     loads (global_load_lds_dwordx4) issued 3 stages ahead; each stage ends with a
-//     barrier that waits only for the loads of the next stage, so the other two stay
-//     in flight across it;
-//   * LDS rows are 64 bytes; the 16-byte chunk c of row r is stored at chunk
-//     c ^ lds_swizzle(r), which keeps the fragment reads free of bank conflicts;
+//   * K advances 64 at a time (128-byte LDS rows, whole cache lines per load); stages
+//     are filled by direct-to-LDS loads (global_load_lds_dwordx4).  With 256-row tiles
+//     LDS holds 2 activation and 3 weight stages (all 160 KB), weights loaded three
+//     stages ahead; 32-row tiles use 2 + 2.  One barrier per stage, before its last
+//     k-step's MFMAs, waits only for the next stage's loads;
+//   * the 16-byte chunk c of LDS row r is stored at chunk c ^ lds_swizzle(r), which keeps
+//     the fragment reads free of bank conflicts;
 //   * SwiGLU: each wave's 128 weight rows are 64 rows of W1 followed by the same 64 rows
 //     of W3, so g and u of an output element sit in the same lane;
+//   * a_rows (optional) gathers the activation rows through a row map, row_scale
+//     (optional) multiplies each output row in the epilogue;
 //   * scheduling happens on the device: every workgroup scans the segment offsets
 //     written by the dispatch step, so no host round trip is needed.  Tiles are ordered
-//     segment by segment, 8 column tiles x all row tiles of a segment at a time.  With
-//     MOE_GEMM_XCD_REMAP the workgroup -> tile map gives each XCD (workgroup id mod 8) a
+//     segment by segment, 8 column tiles x all row tiles of a segment at a time, so the
+//     row tiles that share a weight panel land on one XCD (workgroup id mod 8).  With
+//     few rounds, a partial last round is split along K (gemm_split_finish_kernel sums
+//     the parts).  With MOE_GEMM_XCD_REMAP the workgroup -> tile map gives each XCD a
 //     contiguous range of that order instead of every eighth tile.
 // float32 kernel: a plain LDS-tiled SIMT product (64 x 64 tiles) with the same
 // scheduling and epilogues; it serves the small float32 workload.
