@@ -515,19 +515,22 @@ __device__ __forceinline__ void split_store(const GemmArgs& g, const Tile& tile,
 // Epilogue of a tile for a wave with TA active row blocks: activation and bf16 stores.
 // Register 4q + r of tile (tn, tm) is the output element (activation row
 // (2 tm + wm)*M + row(lane), weight row tn*M + ni(q, lane) + r); the four r are
-// consecutive output columns (one 8-byte store of bf16).
-template <class IO, int EPI, int TA>
+// consecutive output columns (one 8-byte store of bf16).  HALF = 0 or 1 restricts the
+// epilogue to that half of the wave's output columns (-1: all of them).
+template <class IO, int EPI, int TA, int HALF = -1>
 __device__ __forceinline__ void tile_epilogue(const GemmArgs& g, const Tile& tile, int lane,
                                               int wm, int wn,
                                               typename IO::S::acc_t (&acc)[IO::TN][IO::TM]) {
   using S = typename IO::S;
   constexpr int TN = IO::TN;
+  constexpr int NS = EPI == EPI_SWIGLU ? TN / 2 : TN;  // tiles that own output columns
+  constexpr int T0 = HALF < 0 ? 0 : HALF * NS / 2, T1 = HALF < 0 ? NS : (HALF + 1) * NS / 2;
   const int frow = S::row(lane);
   uint16_t* __restrict__ C = static_cast<uint16_t*>(g.c);
   constexpr int NQ = S::ACC / 4;
   if constexpr (EPI == EPI_SWIGLU) {
 #pragma unroll
-    for (int tn = 0; tn < TN / 2; ++tn) {
+    for (int tn = T0; tn < T1; ++tn) {
 #pragma unroll
       for (int q = 0; q < NQ; ++q) {
         const int col = tile.nt * 128 + wn * 64 + tn * S::M + S::ni(q, lane);
@@ -554,7 +557,7 @@ __device__ __forceinline__ void tile_epilogue(const GemmArgs& g, const Tile& til
       sc[tm] = (g.row_scale && m < tile.m_valid) ? g.row_scale[tile.row0 + m] : 1.f;
     }
 #pragma unroll
-    for (int tn = 0; tn < TN; ++tn) {
+    for (int tn = T0; tn < T1; ++tn) {
 #pragma unroll
       for (int q = 0; q < NQ; ++q) {
         const int col = tile.nt * 256 + wn * 128 + tn * S::M + S::ni(q, lane);
@@ -729,15 +732,18 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_bf16_kernel(GemmArgs g) {
   }
 }
 
-// Finishes the split tiles of the preceding gemm_bf16_kernel launch: workgroup q sums
-// the parts of split tile q in part order and runs the tile's epilogue.
+// Finishes the split tiles of the preceding gemm_bf16_kernel launch: one single-wave
+// workgroup per (split tile q, wave w of the tile, half h of that wave's output
+// columns) sums its accumulators over the parts in part order and runs its share of
+// the tile's epilogue.  Eight workgroups per tile, and all loads of a part issued
+// together, keep many loads of the partials in flight.
 template <int BM, int EPI>
-__global__ __launch_bounds__(kThreads, 1) void gemm_split_finish_kernel(GemmArgs g) {
+__global__ __launch_bounds__(kWave) void gemm_split_finish_kernel(GemmArgs g) {
   using IO = TileIO<BM, EPI == EPI_SWIGLU, false>;
   using S = typename IO::S;
   using SS = SplitSlot<IO>;
-  constexpr int TM = IO::TM;
-  const int q = blockIdx.x;
+  constexpr int TM = IO::TM, TN = IO::TN, NV = S::ACC / 4;
+  const int q = blockIdx.x / 8, wave = (blockIdx.x / 2) % 4, half = blockIdx.x % 2;
   if (q >= g.split_desc[0]) return;
   const int32_t* d = g.split_desc + 1 + 5 * q;
   Tile tile;
@@ -745,39 +751,54 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_split_finish_kernel(GemmArgs
   tile.row0 = d[1];
   tile.m_valid = d[2];
   tile.nt = d[3];
-  tile.nparts = d[4];
+  tile.nparts = __builtin_amdgcn_readfirstlane(d[4]);
   tile.part = 0;
   tile.split_q = q;
   tile.k_stage0 = 0;
   tile.k_stages = 0;
-  const int tid = threadIdx.x, lane = tid & (kWave - 1);
-  const int wave = __builtin_amdgcn_readfirstlane(tid / kWave);
+  const int lane = threadIdx.x;
+  const int tid = wave * kWave + lane;  // the thread of the tile's workgroup this lane stands for
   const int wm = wave >> 1, wn = wave & 1;
   const int nb = (tile.m_valid + S::M - 1) / S::M;
   const int ta = __builtin_amdgcn_readfirstlane(min(max((nb - wm + 1) / 2, 0), TM));
-  typename S::acc_t acc[IO::TN][TM];
-  auto sum_parts = [&](auto ta_c) {
-    constexpr int TA = decltype(ta_c)::value;
+  typename S::acc_t acc[TN][TM];
+  auto run = [&](auto ta_c, auto half_c) {
+    constexpr int TA = decltype(ta_c)::value, H = decltype(half_c)::value;
+    // the two accumulator tiles behind this half's output columns
+    constexpr int NS = EPI == EPI_SWIGLU ? TN / 2 : TN;
+    constexpr int T0 = H * NS / 2;
+    constexpr int TNA = T0, TNB = EPI == EPI_SWIGLU ? T0 + TN / 2 : T0 + 1;
     for (int p = 0; p < tile.nparts; ++p) {
       const f32x4_t* sp = SS::at(g.split_buf, q * tile.nparts + p);
+      f32x4_t x[2][TA > 0 ? TA : 1][NV];
 #pragma unroll
-      for (int tn = 0; tn < IO::TN; ++tn)
+      for (int tm = 0; tm < TA; ++tm)
 #pragma unroll
-        for (int tm = 0; tm < TA; ++tm)
+        for (int v = 0; v < NV; ++v) {
+          x[0][tm][v] = sp[SS::chunk(TNA, tm, v) * kThreads + tid];
+          x[1][tm][v] = sp[SS::chunk(TNB, tm, v) * kThreads + tid];
+        }
 #pragma unroll
-          for (int v = 0; v < S::ACC / 4; ++v) {
-            const f32x4_t x = sp[SS::chunk(tn, tm, v) * kThreads + tid];
+      for (int tm = 0; tm < TA; ++tm)
 #pragma unroll
-            for (int r = 0; r < 4; ++r)
-              acc[tn][tm][4 * v + r] = p == 0 ? x[r] : acc[tn][tm][4 * v + r] + x[r];
+        for (int v = 0; v < NV; ++v)
+#pragma unroll
+          for (int r = 0; r < 4; ++r) {
+            const float a = acc[TNA][tm][4 * v + r], b = acc[TNB][tm][4 * v + r];
+            acc[TNA][tm][4 * v + r] = p == 0 ? x[0][tm][v][r] : a + x[0][tm][v][r];
+            acc[TNB][tm][4 * v + r] = p == 0 ? x[1][tm][v][r] : b + x[1][tm][v][r];
           }
     }
-    tile_epilogue<IO, EPI, TA>(g, tile, lane, wm, wn, acc);
+    tile_epilogue<IO, EPI, TA, H>(g, tile, lane, wm, wn, acc);
   };
-  if (ta == 1) sum_parts(std::integral_constant<int, 1>{});
-  else if (ta == 2) sum_parts(std::integral_constant<int, 2>{});
-  else if (ta == 3) sum_parts(std::integral_constant<int, 3>{});
-  else if (ta >= 4) sum_parts(std::integral_constant<int, 4>{});
+  auto by_ta = [&](auto half_c) {
+    if (ta == 1) run(std::integral_constant<int, 1>{}, half_c);
+    else if (ta == 2) run(std::integral_constant<int, 2>{}, half_c);
+    else if (ta == 3) run(std::integral_constant<int, 3>{}, half_c);
+    else if (ta >= 4) run(std::integral_constant<int, 4>{}, half_c);
+  };
+  if (half == 0) by_ta(std::integral_constant<int, 0>{});
+  else by_ta(std::integral_constant<int, 1>{});
 }
 
 // ------------------------------------------------------------------ float32 SIMT kernel
@@ -892,8 +913,8 @@ hipError_t launch_bf16_bm(hipStream_t st, GemmArgs g, int64_t max_rows, bool ksp
                        dim3(kThreads), 0, st, g);
     const hipError_t err = hipGetLastError();
     if (err != hipSuccess) return err;
-    hipLaunchKernelGGL((gemm_split_finish_kernel<BM, EPI>), dim3(static_cast<unsigned>(g.split_g / 2)),
-                       dim3(kThreads), 0, st, g);
+    hipLaunchKernelGGL((gemm_split_finish_kernel<BM, EPI>),
+                       dim3(static_cast<unsigned>(g.split_g / 2 * 8)), dim3(kWave), 0, st, g);
     return hipGetLastError();
   }
   if (ksplit)
