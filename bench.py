@@ -413,6 +413,10 @@ def main():
         "grouped_gemm_frac_of_peak": round(gemm_tflops / peak, 4),
         "dispatch_gbps": round(disp_gbps, 1),
         "dispatch_frac_of_hbm": round(disp_gbps / PEAK_HBM_GBPS, 4),
+        "dispatch_note": ("index maps only (capacity ranks, slot and row maps): the kept rows "
+                          "of x are gathered inside gemm1, so no row is copied"
+                          if cfg.fuse & 1 else
+                          "index maps and the permuted copy of the kept rows of x"),
         "combine_gbps": round(comb_gbps, 1),
         "stages_ms": {s: round(v, 5) for s, v in stage_ms.items()},
         "stages_ms_median": {s: round(median(v), 5) for s, v in stage_all.items()},
