@@ -4,7 +4,7 @@
 // A gather, not a scatter: each output vector (8 bf16 or 4 float32 = 16 bytes) is
 // produced by one thread that reads the shared row and the token's k expert rows and
 // accumulates in float32 in a fixed order (shared, then slot 0..k-1).  No atomics, so
-// the result is bitwise reproducible.
+// the result is bitwise reproducible.  One workgroup per token row.
 
 #include "common.h"
 #include "kernels.h"
@@ -14,74 +14,138 @@ namespace {
 
 constexpr int kThreads = 256;
 
-__global__ __launch_bounds__(kThreads) void combine_bf16_kernel(
-    const uint16_t* __restrict__ y_rows, const int32_t* __restrict__ slot_row,
-    const float* __restrict__ topk_w, int64_t n, int k, int64_t d,
-    const uint16_t* __restrict__ shared_y, uint16_t* __restrict__ out) {
-  const int64_t vpr = d / 8;
-  const int64_t total = n * vpr;
-  for (int64_t i = static_cast<int64_t>(blockIdx.x) * kThreads + threadIdx.x; i < total;
-       i += static_cast<int64_t>(gridDim.x) * kThreads) {
-    const int64_t t = i / vpr;
-    const int64_t c = (i - t * vpr) * 8;
-    float acc[8];
-    if (shared_y) {
-      const uint4 v = *reinterpret_cast<const uint4*>(shared_y + t * d + c);
-      const uint32_t w4[4] = {v.x, v.y, v.z, v.w};
+// 16-byte vectors of a row: 8 bf16 or 4 float32.
+template <bool BF16>
+struct Vec;
+
+template <>
+struct Vec<true> {
+  static constexpr int N = 8;
+  __device__ static void load(const void* p, float (&v)[8]) {
+    const uint4 u = *reinterpret_cast<const uint4*>(p);
+    const uint32_t w4[4] = {u.x, u.y, u.z, u.w};
 #pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        acc[2 * q] = bf16_to_f32(static_cast<uint16_t>(w4[q] & 0xffffu));
-        acc[2 * q + 1] = bf16_to_f32(static_cast<uint16_t>(w4[q] >> 16));
-      }
+    for (int q = 0; q < 4; ++q) {
+      v[2 * q] = bf16_to_f32(static_cast<uint16_t>(w4[q] & 0xffffu));
+      v[2 * q + 1] = bf16_to_f32(static_cast<uint16_t>(w4[q] >> 16));
+    }
+  }
+  __device__ static void store(void* p, const float (&v)[8]) {
+    uint4 o;
+    o.x = f32_to_bf16(v[0]) | (static_cast<uint32_t>(f32_to_bf16(v[1])) << 16);
+    o.y = f32_to_bf16(v[2]) | (static_cast<uint32_t>(f32_to_bf16(v[3])) << 16);
+    o.z = f32_to_bf16(v[4]) | (static_cast<uint32_t>(f32_to_bf16(v[5])) << 16);
+    o.w = f32_to_bf16(v[6]) | (static_cast<uint32_t>(f32_to_bf16(v[7])) << 16);
+    *reinterpret_cast<uint4*>(p) = o;
+  }
+};
+
+template <>
+struct Vec<false> {
+  static constexpr int N = 4;
+  __device__ static void load(const void* p, float (&v)[4]) {
+    const float4 u = *reinterpret_cast<const float4*>(p);
+    v[0] = u.x;
+    v[1] = u.y;
+    v[2] = u.z;
+    v[3] = u.w;
+  }
+  __device__ static void store(void* p, const float (&v)[4]) {
+    *reinterpret_cast<float4*>(p) = make_float4(v[0], v[1], v[2], v[3]);
+  }
+};
+
+// One workgroup per token row (rows of d/VN 16-byte vectors; thread i takes vectors
+// i, i + 256, ..., of the row's blockIdx.y-th range of 256 * VPT vectors): the token's
+// k slots and weights are the same for the whole workgroup, and each wave reads and
+// writes 1 KB contiguous pieces of the rows.  Every load of the token (k <= KMAX slot
+// rows x VPT vectors) is issued before the float32 accumulation, which then runs in the
+// fixed order shared, slot 0, ..., slot k-1.
+template <bool BF16, int VPT, int KMAX>
+__global__ __launch_bounds__(kThreads) void combine_kernel(
+    const uint8_t* __restrict__ y_rows, const int32_t* __restrict__ slot_row,
+    const float* __restrict__ topk_w, int k, int64_t d,
+    const uint8_t* __restrict__ shared_y, uint8_t* __restrict__ out) {
+  using V = Vec<BF16>;
+  constexpr int VN = V::N;
+  constexpr int64_t kVecBytes = 16;
+  const int64_t t = blockIdx.x;
+  const int64_t nvec = d / VN;
+  const int64_t row_bytes = d * (BF16 ? 2 : 4);
+  const int64_t c0 = static_cast<int64_t>(blockIdx.y) * kThreads * VPT + threadIdx.x;
+  int32_t row[KMAX];
+  float w[KMAX];
+#pragma unroll
+  for (int j = 0; j < KMAX; ++j) {
+    row[j] = j < k ? slot_row[t * k + j] : -1;
+    w[j] = (j < k && topk_w) ? topk_w[t * k + j] : 1.f;  // NULL: rows already weighted
+  }
+  uint4 raw[KMAX][VPT];
+  uint4 sh[VPT];
+#pragma unroll
+  for (int v = 0; v < VPT; ++v) {
+    const int64_t c = c0 + static_cast<int64_t>(kThreads) * v;
+    if (c < nvec) {
+      if (shared_y) sh[v] = *reinterpret_cast<const uint4*>(shared_y + t * row_bytes + c * kVecBytes);
+#pragma unroll
+      for (int j = 0; j < KMAX; ++j)
+        if (row[j] >= 0)
+          raw[j][v] = *reinterpret_cast<const uint4*>(
+              y_rows + static_cast<int64_t>(row[j]) * row_bytes + c * kVecBytes);
+    }
+  }
+#pragma unroll
+  for (int v = 0; v < VPT; ++v) {
+    const int64_t c = c0 + static_cast<int64_t>(kThreads) * v;
+    if (c >= nvec) continue;
+    float acc[VN];
+    if (shared_y) {
+      V::load(&sh[v], acc);
     } else {
 #pragma unroll
-      for (int q = 0; q < 8; ++q) acc[q] = 0.f;
+      for (int q = 0; q < VN; ++q) acc[q] = 0.f;
     }
-    for (int j = 0; j < k; ++j) {
-      const int32_t r = slot_row[t * k + j];
-      if (r < 0) continue;
-      const float w = topk_w ? topk_w[t * k + j] : 1.f;  // NULL: rows already weighted
-      const uint4 v = *reinterpret_cast<const uint4*>(y_rows + static_cast<int64_t>(r) * d + c);
-      const uint32_t w4[4] = {v.x, v.y, v.z, v.w};
 #pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        acc[2 * q] = fmaf(w, bf16_to_f32(static_cast<uint16_t>(w4[q] & 0xffffu)), acc[2 * q]);
-        acc[2 * q + 1] = fmaf(w, bf16_to_f32(static_cast<uint16_t>(w4[q] >> 16)), acc[2 * q + 1]);
-      }
+    for (int j = 0; j < KMAX; ++j) {
+      if (row[j] < 0) continue;
+      float y[VN];
+      V::load(&raw[j][v], y);
+#pragma unroll
+      for (int q = 0; q < VN; ++q) acc[q] = fmaf(w[j], y[q], acc[q]);
     }
-    uint4 o;
-    o.x = f32_to_bf16(acc[0]) | (static_cast<uint32_t>(f32_to_bf16(acc[1])) << 16);
-    o.y = f32_to_bf16(acc[2]) | (static_cast<uint32_t>(f32_to_bf16(acc[3])) << 16);
-    o.z = f32_to_bf16(acc[4]) | (static_cast<uint32_t>(f32_to_bf16(acc[5])) << 16);
-    o.w = f32_to_bf16(acc[6]) | (static_cast<uint32_t>(f32_to_bf16(acc[7])) << 16);
-    *reinterpret_cast<uint4*>(out + t * d + c) = o;
+    V::store(out + t * row_bytes + c * kVecBytes, acc);
   }
 }
 
-__global__ __launch_bounds__(kThreads) void combine_f32_kernel(
-    const float* __restrict__ y_rows, const int32_t* __restrict__ slot_row,
-    const float* __restrict__ topk_w, int64_t n, int k, int64_t d,
-    const float* __restrict__ shared_y, float* __restrict__ out) {
-  const int64_t vpr = d / 4;
-  const int64_t total = n * vpr;
-  for (int64_t i = static_cast<int64_t>(blockIdx.x) * kThreads + threadIdx.x; i < total;
-       i += static_cast<int64_t>(gridDim.x) * kThreads) {
-    const int64_t t = i / vpr;
-    const int64_t c = (i - t * vpr) * 4;
-    float4 acc = shared_y ? *reinterpret_cast<const float4*>(shared_y + t * d + c)
-                          : make_float4(0.f, 0.f, 0.f, 0.f);
-    for (int j = 0; j < k; ++j) {
-      const int32_t r = slot_row[t * k + j];
-      if (r < 0) continue;
-      const float w = topk_w ? topk_w[t * k + j] : 1.f;
-      const float4 v = *reinterpret_cast<const float4*>(y_rows + static_cast<int64_t>(r) * d + c);
-      acc.x = fmaf(w, v.x, acc.x);
-      acc.y = fmaf(w, v.y, acc.y);
-      acc.z = fmaf(w, v.z, acc.z);
-      acc.w = fmaf(w, v.w, acc.w);
-    }
-    *reinterpret_cast<float4*>(out + t * d + c) = acc;
+template <bool BF16, int KMAX>
+hipError_t launch_combine_k(hipStream_t st, const uint8_t* yr, const int32_t* slot_row,
+                            const float* topk_w, int64_t n, int k, int64_t d, const uint8_t* sy,
+                            uint8_t* o) {
+  const int64_t nvec = d / Vec<BF16>::N;
+  const int64_t vpt = (nvec + kThreads - 1) / kThreads;
+  // rows wider than 1024 vectors: ranges of 1024 along blockIdx.y
+  const dim3 grid(static_cast<unsigned>(n), static_cast<unsigned>(vpt > 4 ? (vpt + 3) / 4 : 1));
+  const dim3 blk(kThreads);
+  switch (vpt > 4 ? 4 : vpt) {
+    case 1: hipLaunchKernelGGL((combine_kernel<BF16, 1, KMAX>), grid, blk, 0, st, yr, slot_row, topk_w, k, d, sy, o); break;
+    case 2: hipLaunchKernelGGL((combine_kernel<BF16, 2, KMAX>), grid, blk, 0, st, yr, slot_row, topk_w, k, d, sy, o); break;
+    case 3: hipLaunchKernelGGL((combine_kernel<BF16, 3, KMAX>), grid, blk, 0, st, yr, slot_row, topk_w, k, d, sy, o); break;
+    case 4: hipLaunchKernelGGL((combine_kernel<BF16, 4, KMAX>), grid, blk, 0, st, yr, slot_row, topk_w, k, d, sy, o); break;
+    default: return hipErrorInvalidValue;
   }
+  return hipGetLastError();
+}
+
+template <bool BF16>
+hipError_t launch_combine_t(hipStream_t st, const void* y_rows, const int32_t* slot_row,
+                            const float* topk_w, int64_t n, int k, int64_t d,
+                            const void* shared_y, void* out) {
+  const auto* yr = static_cast<const uint8_t*>(y_rows);
+  const auto* sy = static_cast<const uint8_t*>(shared_y);
+  auto* o = static_cast<uint8_t*>(out);
+  if (k <= 2) return launch_combine_k<BF16, 2>(st, yr, slot_row, topk_w, n, k, d, sy, o);
+  if (k <= 8) return launch_combine_k<BF16, 8>(st, yr, slot_row, topk_w, n, k, d, sy, o);
+  return launch_combine_k<BF16, 16>(st, yr, slot_row, topk_w, n, k, d, sy, o);
 }
 
 }  // namespace
@@ -90,19 +154,8 @@ hipError_t launch_combine(hipStream_t st, bool bf16, const void* y_rows,
                           const int32_t* slot_row, const float* topk_w, int64_t n, int k,
                           int64_t d, const void* shared_y, void* out) {
   if (n <= 0) return hipSuccess;
-  const int64_t vec = bf16 ? 8 : 4;
-  const int64_t total = n * (d / vec);
-  int64_t blocks = (total + kThreads - 1) / kThreads;
-  if (blocks > 4096) blocks = 4096;
-  if (bf16)
-    hipLaunchKernelGGL(combine_bf16_kernel, dim3(static_cast<unsigned>(blocks)), dim3(kThreads),
-                       0, st, static_cast<const uint16_t*>(y_rows), slot_row, topk_w, n, k, d,
-                       static_cast<const uint16_t*>(shared_y), static_cast<uint16_t*>(out));
-  else
-    hipLaunchKernelGGL(combine_f32_kernel, dim3(static_cast<unsigned>(blocks)), dim3(kThreads),
-                       0, st, static_cast<const float*>(y_rows), slot_row, topk_w, n, k, d,
-                       static_cast<const float*>(shared_y), static_cast<float*>(out));
-  return hipGetLastError();
+  return bf16 ? launch_combine_t<true>(st, y_rows, slot_row, topk_w, n, k, d, shared_y, out)
+              : launch_combine_t<false>(st, y_rows, slot_row, topk_w, n, k, d, shared_y, out);
 }
 
 }  // namespace moe

@@ -481,20 +481,25 @@ def test_expert_ffn_gather_and_row_scale(case):
 
 
 # ------------------------------------------------------------------ combine
-@pytest.mark.parametrize("dtype,shared,k", [("bf16", False, 2), ("bf16", True, 6), ("f32", False, 1),
-                                            ("f32", True, 3)])
-def test_combine_parity(dtype, shared, k):
-    print_case("combine", dtype, shared, k)
-    rng = np.random.default_rng(k)
-    n, d, rows = 333, 256, 500
+# row widths: one partial range of 256 vectors, several vectors per thread, and rows
+# wider than 1024 vectors (a second range along the grid's y); weights given or not
+@pytest.mark.parametrize("dtype,shared,k,d,weights", [
+    ("bf16", False, 2, 256, True), ("bf16", True, 6, 256, True), ("f32", False, 1, 256, True),
+    ("f32", True, 3, 256, True), ("bf16", False, 2, 4096, False), ("bf16", True, 6, 5120, True),
+    ("bf16", False, 3, 8200, True), ("f32", True, 5, 4100, False), ("bf16", False, 1, 24, True)])
+def test_combine_parity(dtype, shared, k, d, weights):
+    print_case("combine", dtype, shared, k, d, weights)
+    rng = np.random.default_rng(k + d)
+    n, rows = 333, 500
     cvt = (lambda a: synth.f32_to_bf16_bits(a)) if dtype == "bf16" else (lambda a: a)
     yr = cvt(rng.standard_normal((rows, d)).astype(np.float32))
     sy = cvt(rng.standard_normal((n, d)).astype(np.float32)) if shared else None
     slot = rng.integers(-1, rows, size=(n, k)).astype(np.int32)
     slot[:5] = -1  # fully dropped tokens
-    w = rng.random((n, k)).astype(np.float32)
+    w = rng.random((n, k)).astype(np.float32) if weights else np.ones((n, k), np.float32)
     out = torch.empty((n, d), dtype=torch.bfloat16 if dtype == "bf16" else torch.float32, device=DEV)
-    B.moe_combine(_up(yr, dtype), torch.from_numpy(slot).to(DEV), torch.from_numpy(w).to(DEV),
+    B.moe_combine(_up(yr, dtype), torch.from_numpy(slot).to(DEV),
+                  torch.from_numpy(w).to(DEV) if weights else None,
                   None if sy is None else _up(sy, dtype), out)
     torch.cuda.synchronize()
     yr64 = O.widen(yr, dtype)
