@@ -362,6 +362,10 @@ typedef struct {
  * first such call and kept until the process ends) and joins it back before the
  * combine, using events; calls from several host threads are serialised while they
  * enqueue.
+ * Graph capture: the call allocates nothing, waits for nothing on the host and clears
+ * no memory with memset, so it can be captured into a HIP graph on `stream` and
+ * replayed (the internal stream joins the capture through the fork event).  Make one
+ * call with shared experts outside the capture first: it creates that stream.
  */
 size_t moe_forward_workspace_size(const moe_config* cfg);
 moe_status moe_forward(void* stream, const moe_config* cfg, const moe_weights* w,

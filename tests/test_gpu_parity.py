@@ -623,3 +623,40 @@ def test_forward_edge_cases():
     assert (st["sel_count"].cpu() == 0).all() and float(st["aux"].cpu()[0]) == 0.0
     assert (st["monitor"].cpu() == 0).all()
     assert (st["expert_offsets"].cpu() == 0).all()
+
+
+# ------------------------------------------------------------------ graph capture
+@pytest.mark.parametrize("name", ["deepseek", "switch"])
+def test_forward_replays_from_a_captured_graph(name):
+    """moe_forward allocates nothing, syncs nothing and clears nothing with memset, so a
+    captured forward (shared experts on the internal second stream included) replays
+    correctly: every replay, with eager work between replays, matches the eager result
+    bit for bit."""
+    cfg = CONFIGS[name].with_tokens(REDUCED[name]).scaled(d_ff=min(CONFIGS[name].d_ff, 1024),
+                                                          reroute_rounds=2)
+    print_case("graph", name, cfg.n_tokens)
+    inp = synth.DeviceInputs(cfg, DEV)
+    layer = MoELayer.from_inputs(inp)
+    x = inp.x.clone()
+    y = torch.empty_like(x)
+    st = layer.new_stats(cfg.n_tokens)
+    layer.forward(x, y, st)  # eager first: creates the internal stream and the workspace
+    torch.cuda.synchronize()
+    ref = y.clone()
+    g = torch.cuda.CUDAGraph()
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        with torch.cuda.graph(g, stream=s):
+            layer.forward(x, y, st, stream=s)
+    torch.cuda.current_stream().wait_stream(s)
+    for rep in range(3):
+        y.zero_()
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(y.view(torch.int16), ref.view(torch.int16)), f"replay {rep}"
+        # eager work on the same buffers between replays
+        layer.forward(x, y, st)
+        torch.cuda.synchronize()
+        assert torch.equal(y.view(torch.int16), ref.view(torch.int16))
