@@ -28,9 +28,10 @@ hipError_t launch_route(hipStream_t st, const float* x, int64_t n, int64_t d,
 
 // bf16 router: exact three-part bf16 split of W_router, the sliced logits product and
 // the gate over the slices' partial logits.
-// Gate: tokens per wave grow with N so that about a thousand waves run (1..16).
+// Gate: one token per wave up to 8192 tokens (several waves per SIMD hide the latency
+// of each token's short dependent chain), then tokens per wave grow with N (up to 16).
 inline int gate_tokens_per_wave(int64_t n_tokens) {
-  const int64_t t = (n_tokens + 1023) / 1024;
+  const int64_t t = (n_tokens + 8191) / 8192;
   return static_cast<int>(t < 1 ? 1 : (t > 16 ? 16 : t));
 }
 inline int64_t gate_blocks(int64_t n_tokens) {

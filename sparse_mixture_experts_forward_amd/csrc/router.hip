@@ -269,37 +269,52 @@ constexpr int kLRow = 40;  // LDS row stride in bf16: 80-byte rows make the 16-b
 
 // W_router [d][E] float32 -> wp[3][E_pad][d] bf16 (k contiguous), the exact three-part
 // split w = hi + mid + lo (each part the bf16 rounding of what the previous parts left);
-// rows e >= E are zero.  Thread (e, 8 consecutive k).
+// rows e >= E are zero.  A workgroup transposes a 64 (k) x 16 (e) tile through LDS:
+// the reads are 64-byte pieces of W_router rows, and each thread then splits 8
+// consecutive k of one expert and writes them as 16 bytes per plane (8 threads cover
+// 128 contiguous bytes of a plane row).
+constexpr int kSplitK = 64, kSplitE = 16;
 __global__ __launch_bounds__(kThreads) void route_split_kernel(const float* __restrict__ wr,
                                                                int64_t d, int E, int E_pad,
                                                                uint16_t* __restrict__ wp) {
-  const int64_t i = static_cast<int64_t>(blockIdx.x) * kThreads + threadIdx.x;
-  const int64_t nk8 = d / 8;
-  if (i >= static_cast<int64_t>(E_pad) * nk8) return;
-  const int e = static_cast<int>(i % E_pad);  // consecutive lanes: consecutive experts
-  const int64_t k0 = (i / E_pad) * 8;
-  uint32_t hi[4], mid[4], lo[4];
-#pragma unroll
-  for (int q = 0; q < 4; ++q) {
-    uint16_t h2[2], m2[2], l2[2];
-#pragma unroll
-    for (int r = 0; r < 2; ++r) {
-      const float w = e < E ? wr[(k0 + 2 * q + r) * E + e] : 0.f;
-      h2[r] = f32_to_bf16(w);
-      const float r1 = w - bf16_to_f32(h2[r]);  // exact
-      m2[r] = f32_to_bf16(r1);
-      const float r2 = r1 - bf16_to_f32(m2[r]);  // exact
-      l2[r] = f32_to_bf16(r2);
-    }
-    hi[q] = h2[0] | (static_cast<uint32_t>(h2[1]) << 16);
-    mid[q] = m2[0] | (static_cast<uint32_t>(m2[1]) << 16);
-    lo[q] = l2[0] | (static_cast<uint32_t>(l2[1]) << 16);
+  __shared__ float tile[kSplitK][kSplitE + 1];
+  const int64_t k_base = static_cast<int64_t>(blockIdx.x) * kSplitK;
+  const int e_base = blockIdx.y * kSplitE;
+  for (int i = threadIdx.x; i < kSplitK * kSplitE; i += kThreads) {
+    const int kk = i / kSplitE, ee = i % kSplitE;
+    const int64_t k = k_base + kk;
+    const int e = e_base + ee;
+    tile[kk][ee] = (k < d && e < E) ? wr[k * E + e] : 0.f;
   }
+  __syncthreads();
   const int64_t plane = static_cast<int64_t>(E_pad) * d;
-  uint16_t* dst = wp + static_cast<int64_t>(e) * d + k0;
-  *reinterpret_cast<u32x4_t*>(dst) = u32x4_t{hi[0], hi[1], hi[2], hi[3]};
-  *reinterpret_cast<u32x4_t*>(dst + plane) = u32x4_t{mid[0], mid[1], mid[2], mid[3]};
-  *reinterpret_cast<u32x4_t*>(dst + 2 * plane) = u32x4_t{lo[0], lo[1], lo[2], lo[3]};
+  for (int o = threadIdx.x; o < kSplitE * (kSplitK / 8); o += kThreads) {
+    const int ee = o / (kSplitK / 8), c = o % (kSplitK / 8);
+    const int e = e_base + ee;
+    const int64_t k0 = k_base + 8 * c;
+    if (e >= E_pad || k0 >= d) continue;  // d % 8 == 0: a chunk is whole or absent
+    uint32_t hi[4], mid[4], lo[4];
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      uint16_t h2[2], m2[2], l2[2];
+#pragma unroll
+      for (int r = 0; r < 2; ++r) {
+        const float w = tile[8 * c + 2 * q + r][ee];
+        h2[r] = f32_to_bf16(w);
+        const float r1 = w - bf16_to_f32(h2[r]);  // exact
+        m2[r] = f32_to_bf16(r1);
+        const float r2 = r1 - bf16_to_f32(m2[r]);  // exact
+        l2[r] = f32_to_bf16(r2);
+      }
+      hi[q] = h2[0] | (static_cast<uint32_t>(h2[1]) << 16);
+      mid[q] = m2[0] | (static_cast<uint32_t>(m2[1]) << 16);
+      lo[q] = l2[0] | (static_cast<uint32_t>(l2[1]) << 16);
+    }
+    uint16_t* dst = wp + static_cast<int64_t>(e) * d + k0;
+    *reinterpret_cast<u32x4_t*>(dst) = u32x4_t{hi[0], hi[1], hi[2], hi[3]};
+    *reinterpret_cast<u32x4_t*>(dst + plane) = u32x4_t{mid[0], mid[1], mid[2], mid[3]};
+    *reinterpret_cast<u32x4_t*>(dst + 2 * plane) = u32x4_t{lo[0], lo[1], lo[2], lo[3]};
+  }
 }
 
 // Partial logits part[z][t][e] = sum over k in slice z of x[t][k] * w[k][e], for the
@@ -635,10 +650,11 @@ RoutePlan route_plan(int64_t n, int64_t d, int e) {
 
 hipError_t launch_route_split(hipStream_t st, const float* w_router, const RoutePlan& pl,
                               uint16_t* wp) {
-  const int64_t threads = static_cast<int64_t>(pl.e_pad) * (pl.d / 8);
-  if (threads <= 0) return hipSuccess;
-  hipLaunchKernelGGL(route_split_kernel, dim3(static_cast<unsigned>((threads + kThreads - 1) / kThreads)),
-                     dim3(kThreads), 0, st, w_router, pl.d, pl.e, pl.e_pad, wp);
+  if (pl.d <= 0 || pl.e_pad <= 0) return hipSuccess;
+  const dim3 grid(static_cast<unsigned>((pl.d + kSplitK - 1) / kSplitK),
+                  static_cast<unsigned>(pl.e_pad / kSplitE));
+  hipLaunchKernelGGL(route_split_kernel, grid, dim3(kThreads), 0, st, w_router, pl.d, pl.e,
+                     pl.e_pad, wp);
   return hipGetLastError();
 }
 
