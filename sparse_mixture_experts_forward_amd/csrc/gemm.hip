@@ -68,6 +68,7 @@ struct Tile {
 struct SchedSmem {
   int start[kMaxExperts + 1];
   int wsum[kThreads / kWave];
+  int wmulti[kThreads / kWave];
   int seg;
 };
 
@@ -100,6 +101,7 @@ __device__ bool schedule_tile(const int32_t* __restrict__ seg_off, int n_seg,
   const int lane = tid & (kWave - 1), wave = tid / kWave;
 
   int cnt[2];
+  int multi = 0;  // some segment needs more than one row tile
 #pragma unroll
   for (int u = 0; u < 2; ++u) {
     const int s = 2 * tid + u;
@@ -109,17 +111,23 @@ __device__ bool schedule_tile(const int32_t* __restrict__ seg_off, int n_seg,
       seg_bounds(seg_off, s, single_rows, max_rows, lo, hi);
       m = hi - lo;
     }
+    multi |= m > BM;
     cnt[u] = ((m + BM - 1) / BM) * n_ntiles;
   }
   const int local = cnt[0] + cnt[1];
   const int incl = wave_incl_scan(local);
-  if (lane == kWave - 1) s_wsum[wave] = incl;
+  multi = __any(multi);
+  if (lane == kWave - 1) {
+    s_wsum[wave] = incl;
+    sm.wmulti[wave] = multi;
+  }
   __syncthreads();
   int woff = 0, total = 0;
 #pragma unroll
   for (int w = 0; w < kThreads / kWave; ++w) {
     if (w < wave) woff += s_wsum[w];
     total += s_wsum[w];
+    multi |= sm.wmulti[w];
   }
   const int excl = woff + incl - local;
   if (2 * tid < n_seg) s_start[2 * tid] = excl;
@@ -161,6 +169,19 @@ __device__ bool schedule_tile(const int32_t* __restrict__ seg_off, int n_seg,
     return false;
   }
 #endif
+  if (!multi) {
+    // Every segment is one row tile of n_ntiles work items, so nothing reuses a weight
+    // panel; what tiles share is a segment's activation rows.  Take the segments 8 at a
+    // time and deal them out one per XCD: work item L of a group of 8 goes to segment
+    // L mod 8 (the XCD of workgroup L), column tile L / 8, so each segment's column
+    // tiles run on one XCD and read its rows through one L2.
+    const int per = n_ntiles;
+    const int b = L / (kXcds * per);
+    const int w = min(kXcds, total / per - kXcds * b);  // segments in this group
+    const int within = L - b * kXcds * per;
+    const int nt = within / w;
+    L = (kXcds * b + (within - nt * w)) * per + nt;  // the same tile in segment order
+  }
 #pragma unroll
   for (int u = 0; u < 2; ++u) {
     const int s = 2 * tid + u;
