@@ -40,11 +40,15 @@ STAGE_KERNEL = {"gemm1_swiglu": "gemm_bf16_kernel<256, 2, false>",
 CALIB_KERNEL = "MulFunctor"  # the plain float32 copy (x * 1) that scales byte counters
 
 
+# The sources of the expert GEMM kernels, whose counter-derived traffic the bench reports.
+GEMM_SOURCES = ("common.h", "gemm.hip", "kernels.h")
+
+
 def sources_hash() -> str:
-    """Hash of the HIP sources: stored with counter-derived traffic, which is reported
-    only while the kernels are unchanged."""
+    """Hash of the expert GEMM's sources: stored with counter-derived traffic, which is
+    reported only while those kernels are unchanged."""
     h = hashlib.sha256()
-    for f in sorted(glob.glob(os.path.join(CSRC, "*"))):
+    for f in sorted(os.path.join(CSRC, n) for n in GEMM_SOURCES):
         with open(f, "rb") as fh:
             h.update(os.path.basename(f).encode() + fh.read())
     return h.hexdigest()[:16]
