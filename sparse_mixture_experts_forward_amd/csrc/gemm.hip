@@ -14,9 +14,9 @@
 //   * weights are the MFMA A operand, activations the B operand, so a lane ends with 4
 //     consecutive output columns of one row (8-byte stores of bf16);
 //   * K advances 64 at a time (128-byte LDS rows, whole cache lines per load); stages
-//     are filled by direct-to-LDS loads (global_load_lds_dwordx4).  With 256-row tiles
-//     LDS holds 2 activation and 3 weight stages (all 160 KB), weights loaded three
-//     stages ahead; 32-row tiles use 2 + 2.  One barrier per stage, before its last
+//     are filled by direct-to-LDS buffer loads (buffer_load_dwordx4 ... lds).  With
+//     256-row tiles LDS holds 2 activation and 3 weight stages (all 160 KB), weights
+//     loaded three stages ahead; 32-row tiles use 2 + 2.  One barrier per stage, before its last
 //     k-step's MFMAs, waits only for the next stage's loads;
 //   * the 16-byte chunk c of LDS row r is stored at chunk c ^ lds_swizzle(r), which keeps
 //     the fragment reads free of bank conflicts;
@@ -221,6 +221,16 @@ __device__ __forceinline__ uint2 pack_bf16x4(float a, float b, float c, float d)
 }
 
 typedef __attribute__((address_space(3))) void lds_void_t;
+
+// A pointer that is the same in every lane, moved to scalar registers (so that the
+// buffer resources built from it stay scalar).
+template <class T>
+__device__ __forceinline__ T* uniform_ptr(T* p) {
+  const uint64_t v = reinterpret_cast<uint64_t>(p);
+  const uint32_t lo = __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(v));
+  const uint32_t hi = __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(v >> 32));
+  return reinterpret_cast<T*>((static_cast<uint64_t>(hi) << 32) | lo);
+}
 typedef __attribute__((address_space(1))) void global_void_t;
 
 // The two bf16 matrix-core shapes.  Weights are the A operand (rows i of D), activations
@@ -287,14 +297,25 @@ struct TileIO {
   // Loads of one stage: wave w fills the 8-row groups w, w+4, ... of the tile; one
   // instruction moves 8 rows x 128 bytes (whole cache lines).  Lane l writes LDS row
   // 8*group + l/8, physical chunk l%8, and so loads logical chunk (l%8) ^ f(row).
-  // Addresses are a wave-uniform base that carries k plus a loop-invariant unsigned
-  // 32-bit lane offset (the scalar-base form of the load).
+  // Each is a buffer load into LDS (buffer_load_dwordx4 ... lds): a buffer resource in
+  // scalar registers whose base carries k, plus the loop-invariant unsigned 32-bit lane
+  // offset.  (The FLAT form, global_load_lds, makes the compiler treat the LDS counter
+  // as out of order, so it then waits for every fragment read before each k-step's
+  // first MFMA; with buffer loads it waits for just the fragments the MFMA uses.)
+  // Resource word 3 = 0x00020000: 32-bit data format, no format conversion; the record
+  // count 0xFFFFFFFF leaves every 32-bit offset in range, as with a plain pointer.
+  // The resource builtins exist only for the device target, hence the guard (the
+  // host pass compiles these bodies away).
   __device__ __forceinline__ void dma_a(uint16_t* as, int k0) const {
+#if defined(__HIP_DEVICE_COMPILE__)
     const char* ak = reinterpret_cast<const char*>(a_base + k0);
+    const __amdgpu_buffer_rsrc_t r = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<char*>(ak), static_cast<short>(0), -1, 0x00020000);
 #pragma unroll
     for (int j = 0; j < A_GRP; ++j)
-      __builtin_amdgcn_global_load_lds((global_void_t*)(ak + a_off[j]),
-                                       (lds_void_t*)(as + (wave + 4 * j) * 8 * kBK), 16, 0, 0);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void_t*)(as + (wave + 4 * j) * 8 * kBK),
+                                               16, a_off[j], 0, 0, 0);
+#endif
   }
   __device__ __forceinline__ void dma_b(uint16_t* bs, int k0) const {
     int64_t bk = k0;
@@ -304,13 +325,17 @@ struct TileIO {
     }
     const char* bk0 = reinterpret_cast<const char*>(b_base0 + bk);
     const char* bk1 = reinterpret_cast<const char*>(b_base1 + bk);
+#if defined(__HIP_DEVICE_COMPILE__)
 #pragma unroll
     for (int j = 0; j < B_GRP; ++j) {
       // SwiGLU: LDS rows with bit 6 set (groups j = 2, 3 mod 4) hold W3 rows
       const char* bb = (DUAL && ((j >> 1) & 1)) ? bk1 : bk0;
-      __builtin_amdgcn_global_load_lds((global_void_t*)(bb + b_off[j]),
-                                       (lds_void_t*)(bs + (wave + 4 * j) * 8 * kBK), 16, 0, 0);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(
+          __builtin_amdgcn_make_buffer_rsrc(const_cast<char*>(bb), static_cast<short>(0), -1,
+                                            0x00020000),
+          (lds_void_t*)(bs + (wave + 4 * j) * 8 * kBK), 16, b_off[j], 0, 0, 0);
     }
+#endif
   }
 };
 
@@ -330,13 +355,16 @@ __device__ __forceinline__ void read_frags(const IO& io, const uint16_t* __restr
                                            Frags<IO>& f) {
   using S = typename IO::S;
   if constexpr (TA > 0) {
-#pragma unroll
-    for (int tn = 0; tn < IO::TN; ++tn)
-      f.w[tn] = *reinterpret_cast<const bf16x8_t*>(&bc[io.b_row + tn * S::M * kBK + io.co[ks]]);
+    // in the order the next k-step consumes them: w0, then the activation fragments,
+    // then the other weight fragments
+    f.w[0] = *reinterpret_cast<const bf16x8_t*>(&bc[io.b_row + io.co[ks]]);
 #pragma unroll
     for (int tm = 0; tm < TA; ++tm)
       f.a[tm] =
           *reinterpret_cast<const bf16x8_t*>(&ac[io.a_row + tm * 2 * S::M * kBK + io.co[ks]]);
+#pragma unroll
+    for (int tn = 1; tn < IO::TN; ++tn)
+      f.w[tn] = *reinterpret_cast<const bf16x8_t*>(&bc[io.b_row + tn * S::M * kBK + io.co[ks]]);
   }
 }
 
@@ -684,7 +712,8 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_bf16_kernel(GemmArgs g) {
   const int32_t* __restrict__ a_rows = g.a_rows;
   // (a split tile's part starts k_stage0 stages into the reduction)
   const int64_t k_ofs = static_cast<int64_t>(tile.k_stage0) * kBK;
-  io.a_base = static_cast<const uint16_t*>(g.a) + (a_rows ? 0 : tile.row0 * g.lda) + k_ofs;
+  io.a_base =
+      uniform_ptr(static_cast<const uint16_t*>(g.a) + (a_rows ? 0 : tile.row0 * g.lda) + k_ofs);
 #pragma unroll
   for (int j = 0; j < IO::A_GRP; ++j) {
     const int i = 8 * (wave + 4 * j) + dl_row;  // LDS row of the tile
@@ -693,10 +722,11 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_bf16_kernel(GemmArgs g) {
     const int chunk = ((lane & 7) ^ lds_swizzle(i)) * 8;
     io.a_off[j] = (src * static_cast<uint32_t>(g.lda) + chunk) * 2u;
   }
-  io.b_base0 = static_cast<const uint16_t*>(g.b0) + tile.seg * g.b_seg_stride + k_ofs;
-  io.b_base1 = (EPI == EPI_SWIGLU)
-                   ? static_cast<const uint16_t*>(g.b1) + tile.seg * g.b_seg_stride + k_ofs
-                   : io.b_base0;
+  io.b_base0 =
+      uniform_ptr(static_cast<const uint16_t*>(g.b0) + tile.seg * g.b_seg_stride + k_ofs);
+  io.b_base1 = (EPI == EPI_SWIGLU) ? uniform_ptr(static_cast<const uint16_t*>(g.b1) +
+                                                 tile.seg * g.b_seg_stride + k_ofs)
+                                   : io.b_base0;
 #pragma unroll
   for (int j = 0; j < IO::B_GRP; ++j) {
     const int i = 8 * (wave + 4 * j) + dl_row;  // LDS row of the tile
