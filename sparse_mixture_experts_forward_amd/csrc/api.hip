@@ -202,7 +202,8 @@ moe_status run_dispatch(hipStream_t st, const int32_t* idx, int64_t n, int32_t k
                         int64_t cap, const void* x, int64_t row_bytes, int32_t* offsets,
                         int32_t* row_token, int32_t* slot_row, int32_t* kept, int32_t* dropped,
                         void* x_perm, const float* topk_w, float* row_weight, void* ws,
-                        float* drop_rate = nullptr, int32_t* zero_out = nullptr) {
+                        float* drop_rate = nullptr, int32_t* zero_out = nullptr,
+                        int32_t* small_tiles = nullptr) {
   Carve c(ws);
   const moe::DispatchGrid g = moe::dispatch_grid(n, k);
   int32_t* hist = c.take<int32_t>(g.n_blocks * e);
@@ -210,7 +211,8 @@ moe_status run_dispatch(hipStream_t st, const int32_t* idx, int64_t n, int32_t k
   int32_t* kept_tmp = c.take<int32_t>(e);
   return hip_check(moe::launch_dispatch(st, idx, n, k, e, cap, x, row_bytes, offsets, row_token,
                                         slot_row, kept, dropped, x_perm, hist, base, kept_tmp,
-                                        topk_w, row_weight, drop_rate, zero_out),
+                                        topk_w, row_weight, drop_rate, zero_out,
+                                        small_tiles),
                    "dispatch kernels launch");
 }
 
@@ -236,7 +238,8 @@ moe_status run_ffn(hipStream_t st, moe_dtype dt, moe_act act, const void* a, int
                    int64_t w2_kbatch_stride, void* h, void* y,
                    const std::function<moe_status()>& between = nullptr,
                    const int32_t* a_rows = nullptr, const float* row_scale = nullptr,
-                   int split_g = 0, float* split_buf = nullptr, int32_t* split_desc = nullptr) {
+                   int split_g = 0, float* split_buf = nullptr, int32_t* split_desc = nullptr,
+                   const int32_t* small_tiles = nullptr) {
   const bool bf = dt == MOE_BF16;
   moe::GemmArgs g1{};
   g1.split_g = split_g; g1.split_buf = split_buf; g1.split_desc = split_desc;
@@ -248,6 +251,7 @@ moe_status run_ffn(hipStream_t st, moe_dtype dt, moe_act act, const void* a, int
   g1.c = h; g1.ldc = d_ff;
   g1.seg_off = seg_off; g1.n_seg = n_seg; g1.single_rows = single_rows;
   g1.n_out = static_cast<int32_t>(d_ff); g1.k = static_cast<int32_t>(d);
+  g1.small_tiles = small_tiles;
   MOE_TRY(hip_check(moe::launch_gemm(st, bf, act == MOE_ACT_SWIGLU ? moe::EPI_SWIGLU : moe::EPI_GELU,
                                      g1, max_rows),
                     "expert GEMM1 launch"));
@@ -262,6 +266,7 @@ moe_status run_ffn(hipStream_t st, moe_dtype dt, moe_act act, const void* a, int
   g2.c = y; g2.ldc = d;
   g2.seg_off = seg_off; g2.n_seg = n_seg; g2.single_rows = single_rows;
   g2.n_out = static_cast<int32_t>(d); g2.k = static_cast<int32_t>(d_ff);
+  g2.small_tiles = small_tiles;
   return hip_check(moe::launch_gemm(st, bf, moe::EPI_NONE, g2, max_rows), "expert GEMM2 launch");
 }
 
@@ -346,7 +351,7 @@ bool fuse_weight(const moe_config& c) { return (c.fuse & MOE_FUSE_WEIGHT) != 0; 
 struct ForwardLayout {
   int32_t *idx, *sel, *offsets, *row_token, *slot_row, *kept, *dropped;
   float *w, *pm, *aux, *logits, *row_w, *split_buf;
-  int32_t* split_desc;
+  int32_t *split_desc, *small_tiles;
   int split_g;
   void *route_ws, *dispatch_ws, *x_perm, *h, *y_rows, *h_sh, *y_sh;
   moe::RerouteWs rr;
@@ -371,6 +376,7 @@ ForwardLayout forward_layout(const moe_config& c, void* ws) {
   L.slot_row = cv.take<int32_t>(nk);
   L.kept = cv.take<int32_t>(e);
   L.dropped = cv.take<int32_t>(1);
+  L.small_tiles = cv.take<int32_t>(1);
   L.route_ws = cv.take<char>(route_ws(n, c.d_model, e));
   L.dispatch_ws = cv.take<char>(dispatch_ws(n, c.top_k, e));
   if (c.reroute_rounds > 0 && cap >= 0) {
@@ -682,7 +688,8 @@ moe_status moe_forward(void* stream, const moe_config* cfg, const moe_weights* w
                        L.row_token, slot_row, o.kept_count, dropped,
                        gather ? nullptr : L.x_perm, wscale ? tw : nullptr,
                        wscale ? L.row_w : nullptr, L.dispatch_ws,
-                       o.monitor ? o.monitor + 4 : nullptr, reroute ? nullptr : o.n_rerouted));
+                       o.monitor ? o.monitor + 4 : nullptr, reroute ? nullptr : o.n_rerouted,
+                       cap >= 0 ? L.small_tiles : nullptr));
   MOE_TRY(mark(2));
   // a8 (forked): shared experts, all tokens, on the side stream, concurrent with the
   // routed experts (forked after the latency-bound router and dispatch, whose few
@@ -708,7 +715,10 @@ moe_status moe_forward(void* stream, const moe_config* cfg, const moe_weights* w
                   c.d_model, c.d_ff, w->w1, w->w3, w->b1, c.d_ff * c.d_model, w->w2, w->b2,
                   c.d_ff, 0, L.h, L.y_rows, [&]() { return mark(3); },
                   gather ? L.row_token : nullptr, wscale ? L.row_w : nullptr, L.split_g,
-                  L.split_buf, L.split_desc));
+                  L.split_buf, L.split_desc,
+                  // with a capacity the kept rows are known only on the device, which
+                  // then picks the tile height
+                  cap >= 0 ? L.small_tiles : nullptr));
   MOE_TRY(mark(4));
   // join: the combine needs the shared experts' output
   if (side) MOE_TRY(hip_check(hipStreamWaitEvent(st, side->join, 0), "join wait"));

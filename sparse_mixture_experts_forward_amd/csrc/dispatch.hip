@@ -127,21 +127,27 @@ __global__ __launch_bounds__(kThreads) void dispatch_offsets_kernel(
     const int32_t* __restrict__ kept, int E, int64_t n_assign,
     int32_t* __restrict__ expert_offsets, int32_t* __restrict__ kept_count,
     int32_t* __restrict__ n_dropped, float* __restrict__ drop_rate,
-    int32_t* __restrict__ zero_out) {
+    int32_t* __restrict__ zero_out, int32_t* __restrict__ small_tiles) {
   __shared__ int wsum[kThreads / kWave];
-  int running = 0;
+  int running = 0, nonempty = 0;
   for (int e0 = 0; e0 < E; e0 += kThreads) {
     const int e = e0 + threadIdx.x;
     const int v = (e < E) ? kept[e] : 0;
-    int chunk_total;
+    int chunk_total, chunk_nonempty;
     const int incl = block_incl_scan(v, wsum, chunk_total);
     if (e < E) {
       expert_offsets[e] = running + incl - v;
       if (kept_count) kept_count[e] = v;
     }
     running += chunk_total;
+    if (small_tiles) {
+      block_incl_scan(v > 0 ? 1 : 0, wsum, chunk_nonempty);
+      nonempty += chunk_nonempty;
+    }
   }
   if (threadIdx.x == 0) {
+    if (small_tiles)
+      small_tiles[0] = static_cast<int64_t>(running) < static_cast<int64_t>(kBigSegRows) * nonempty;
     expert_offsets[E] = running;
     const int64_t dropped = n_assign - running;
     if (n_dropped) n_dropped[0] = static_cast<int32_t>(dropped);
@@ -409,7 +415,7 @@ hipError_t launch_dispatch(hipStream_t st, const int32_t* topk_idx, int64_t n, i
                            int32_t* kept_count, int32_t* n_dropped, void* x_perm,
                            int32_t* blk_hist, int32_t* blk_base, int32_t* kept_tmp,
                            const float* topk_w, float* row_weight, float* drop_rate,
-                           int32_t* zero_out) {
+                           int32_t* zero_out, int32_t* small_tiles) {
   const DispatchGrid g = dispatch_grid(n, k);
   if (g.n_blocks > 0) {
     hipLaunchKernelGGL(dispatch_hist_kernel, dim3(static_cast<unsigned>(g.n_blocks)),
@@ -423,7 +429,7 @@ hipError_t launch_dispatch(hipStream_t st, const int32_t* topk_idx, int64_t n, i
   hipError_t err = hipGetLastError();
   if (err != hipSuccess) return err;
   hipLaunchKernelGGL(dispatch_offsets_kernel, dim3(1), dim3(kThreads), 0, st, kept_tmp, e, n * k,
-                     expert_offsets, kept_count, n_dropped, drop_rate, zero_out);
+                     expert_offsets, kept_count, n_dropped, drop_rate, zero_out, small_tiles);
   err = hipGetLastError();
   if (err != hipSuccess || g.n_blocks == 0) return err;
   hipLaunchKernelGGL(dispatch_scatter_kernel, dim3(static_cast<unsigned>(g.n_blocks)),

@@ -34,6 +34,8 @@
 // float32 kernel: a plain LDS-tiled SIMT product (64 x 64 tiles) with the same
 // scheduling and epilogues; it serves the small float32 workload.
 
+#include <algorithm>
+
 #include "common.h"
 #include "kernels.h"
 
@@ -685,6 +687,8 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_bf16_kernel(GemmArgs g) {
   static_assert(sizeof(SchedSmem) <= sizeof(Bs2), "scheduler scratch must fit");
   SchedSmem& sched = *reinterpret_cast<SchedSmem*>(Bs2);
 
+  // a launch of the tile height the dispatch did not select does nothing
+  if (g.small_tiles && *g.small_tiles != (BM < 256 ? 1 : 0)) return;
   const int n_ntiles = (EPI == EPI_SWIGLU) ? (g.n_out + 127) / 128 : (g.n_out + 255) / 256;
   Tile tile;
   if (!schedule_tile<BM>(g.seg_off, g.n_seg, g.single_rows, g.max_rows, n_ntiles, g.k / kBK,
@@ -795,6 +799,8 @@ __global__ __launch_bounds__(kWave) void gemm_split_finish_kernel(GemmArgs g) {
   using SS = SplitSlot<IO>;
   constexpr int TM = IO::TM, TN = IO::TN, NV = S::ACC / 4;
   const int q = blockIdx.x / 8, wave = (blockIdx.x / 2) % 4, half = blockIdx.x % 2;
+  // (the product launch it finishes did nothing: its split descriptors are stale)
+  if (g.small_tiles && *g.small_tiles != (BM < 256 ? 1 : 0)) return;
   if (q >= g.split_desc[0]) return;
   const int32_t* d = g.split_desc + 1 + 5 * q;
   Tile tile;
@@ -984,16 +990,26 @@ hipError_t launch_bf16_epi(hipStream_t st, const GemmArgs& g, int64_t max_rows) 
   const int64_t avg = max_rows / (n_seg_eff > 0 ? n_seg_eff : 1);
   // 256-row tiles skip the MFMAs of row blocks past a segment's end, so they serve any
   // segment of a few dozen rows or more; below that the weights dominate and 32-row
-  // tiles (two workgroups per CU) keep more weight loads in flight.  Only 256-row tiles
-  // without K batches split their last round.
-  if (avg >= 48) {
-    GemmArgs g2 = g;
-    if (ksplit || !g.split_buf || !g.split_desc) g2.split_g = 0;
-    return launch_bf16_bm<256, EPI>(st, g2, max_rows, ksplit);
+  // tiles (two workgroups per CU) keep more weight loads in flight.  The host knows a
+  // bound on the rows (max_rows); where that bound would pick 256-row tiles but the
+  // dispatch may have kept far fewer rows (g.small_tiles set), both heights are
+  // launched and the dispatch's choice runs.  Only 256-row tiles without K batches
+  // split their last round.
+  GemmArgs small = g;
+  small.split_g = 0;
+  if (avg < kBigSegRows) {
+    small.small_tiles = nullptr;
+    return launch_bf16_bm<32, EPI>(st, small, max_rows, ksplit);
   }
-  GemmArgs g2 = g;
-  g2.split_g = 0;
-  return launch_bf16_bm<32, EPI>(st, g2, max_rows, ksplit);
+  GemmArgs big = g;
+  if (ksplit || !g.split_buf || !g.split_desc) big.split_g = 0;
+  const hipError_t err = launch_bf16_bm<256, EPI>(st, big, max_rows, ksplit);
+  if (err != hipSuccess || !g.small_tiles) return err;
+  // selected, the kept rows average under kBigSegRows per non-empty segment, so the
+  // 32-row tiles number at most 2.5 per segment and column tile
+  return launch_bf16_bm<32, EPI>(
+      st, small, std::min<int64_t>(max_rows, static_cast<int64_t>(kBigSegRows) * n_seg_eff),
+      ksplit);
 }
 
 template <int EPI>

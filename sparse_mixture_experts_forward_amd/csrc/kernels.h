@@ -79,13 +79,19 @@ struct DispatchGrid {
 };
 DispatchGrid dispatch_grid(int64_t n_tokens, int32_t k);
 
+// Segments of at least kBigSegRows rows take 256-row GEMM tiles; below that 32-row
+// tiles (two workgroups per CU) keep more weight loads in flight.
+constexpr int kBigSegRows = 48;
+
+// small_tiles (or null): set to 1 when the kept rows average fewer than kBigSegRows per
+// expert that kept any, else 0 (read by the expert GEMM launches, see GemmArgs).
 hipError_t launch_dispatch(hipStream_t st, const int32_t* topk_idx, int64_t n, int k, int e,
                            int64_t capacity, const void* x, int64_t row_bytes,
                            int32_t* expert_offsets, int32_t* row_token, int32_t* slot_row,
                            int32_t* kept_count, int32_t* n_dropped, void* x_perm,
                            int32_t* blk_hist, int32_t* blk_base, int32_t* kept_tmp,
                            const float* topk_w, float* row_weight, float* drop_rate = nullptr,
-                           int32_t* zero_out = nullptr);
+                           int32_t* zero_out = nullptr, int32_t* small_tiles = nullptr);
 
 // Workspace of the overflow re-routing (all device arrays): blk_hist / blk_base
 // [E][n_blocks] (dispatch_grid), kept / room [E], state [N*k], thr_z / thr_e [N],
@@ -137,6 +143,11 @@ struct GemmArgs {
   int32_t split_g;
   float* split_buf;
   int32_t* split_desc;
+  // Tile height decided on the device (or null: by the host's row bound alone): where
+  // the host cannot tell (segments may hold from none to many rows, as with a capacity
+  // limit), both tile heights are launched and each launch's workgroups exit at once
+  // unless *small_tiles (written by the dispatch) selects it.
+  const int32_t* small_tiles;
 };
 
 // Sizes of the split buffers for g resident workgroups.
