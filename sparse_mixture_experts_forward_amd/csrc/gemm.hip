@@ -53,6 +53,7 @@ constexpr int kBRows = 256;   // bf16: weight rows per workgroup
 #endif
 constexpr int kGroupN = MOE_GEMM_GROUP_N;  // column tiles per scheduling group
 constexpr int kXcds = 8;
+constexpr int kMaxSplitParts = 4;  // K parts of a split tile
 
 struct Tile {
   int seg;
@@ -153,7 +154,7 @@ __device__ bool schedule_tile(const int32_t* __restrict__ seg_off, int n_seg,
   const int full = split_g > 0 ? total / split_g * split_g : total;
   const int r = total - full;
   const int ns = (r > 0 && 2 * r <= split_g && full <= 4 * split_g)
-                     ? min(min(split_g / r, 4), KT / 8) : 1;
+                     ? min(min(split_g / r, kMaxSplitParts), KT / 8) : 1;
   // the number of split tiles, for the launch that finishes them
   if (split_desc && blockIdx.x == 0 && tid == 0) split_desc[0] = ns > 1 ? r : 0;
   if (ns > 1) {
@@ -567,8 +568,9 @@ __device__ __forceinline__ void split_store(const GemmArgs& g, const Tile& tile,
 // Register 4q + r of tile (tn, tm) is the output element (activation row
 // (2 tm + wm)*M + row(lane), weight row tn*M + ni(q, lane) + r); the four r are
 // consecutive output columns (one 8-byte store of bf16).  HALF = 0 or 1 restricts the
-// epilogue to that half of the wave's output columns (-1: all of them).
-template <class IO, int EPI, int TA, int HALF = -1>
+// epilogue to that half of the wave's output columns (-1: all of them), TMO >= 0 to the
+// row block tm = TMO (-1: the TA blocks).
+template <class IO, int EPI, int TA, int HALF = -1, int TMO = -1>
 __device__ __forceinline__ void tile_epilogue(const GemmArgs& g, const Tile& tile, int lane,
                                               int wm, int wn,
                                               typename IO::S::acc_t (&acc)[IO::TN][IO::TM]) {
@@ -576,6 +578,7 @@ __device__ __forceinline__ void tile_epilogue(const GemmArgs& g, const Tile& til
   constexpr int TN = IO::TN;
   constexpr int NS = EPI == EPI_SWIGLU ? TN / 2 : TN;  // tiles that own output columns
   constexpr int T0 = HALF < 0 ? 0 : HALF * NS / 2, T1 = HALF < 0 ? NS : (HALF + 1) * NS / 2;
+  constexpr int TM0 = TMO < 0 ? 0 : TMO, TM1 = TMO < 0 ? TA : TMO + 1;
   const int frow = S::row(lane);
   uint16_t* __restrict__ C = static_cast<uint16_t*>(g.c);
   constexpr int NQ = S::ACC / 4;
@@ -586,7 +589,7 @@ __device__ __forceinline__ void tile_epilogue(const GemmArgs& g, const Tile& til
       for (int q = 0; q < NQ; ++q) {
         const int col = tile.nt * 128 + wn * 64 + tn * S::M + S::ni(q, lane);
 #pragma unroll
-        for (int tm = 0; tm < TA; ++tm) {
+        for (int tm = TM0; tm < TM1; ++tm) {
           const int m = (2 * tm + wm) * S::M + frow;
           if (m < tile.m_valid && col < g.n_out) {
             float v[4];
@@ -603,7 +606,7 @@ __device__ __forceinline__ void tile_epilogue(const GemmArgs& g, const Tile& til
     const uint16_t* bias = static_cast<const uint16_t*>(g.bias);
     float sc[TA > 0 ? TA : 1];  // per-row output scale (the routing weight of the row)
 #pragma unroll
-    for (int tm = 0; tm < TA; ++tm) {
+    for (int tm = TM0; tm < TM1; ++tm) {
       const int m = (2 * tm + wm) * S::M + frow;
       sc[tm] = (g.row_scale && m < tile.m_valid) ? g.row_scale[tile.row0 + m] : 1.f;
     }
@@ -619,7 +622,7 @@ __device__ __forceinline__ void tile_epilogue(const GemmArgs& g, const Tile& til
             bv[r] = bf16_to_f32(bias[tile.seg * g.bias_seg_stride + col + r]);
         }
 #pragma unroll
-        for (int tm = 0; tm < TA; ++tm) {
+        for (int tm = TM0; tm < TM1; ++tm) {
           const int m = (2 * tm + wm) * S::M + frow;
           if (m < tile.m_valid && col < g.n_out) {
             float v[4];
@@ -789,16 +792,18 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_bf16_kernel(GemmArgs g) {
 
 // Finishes the split tiles of the preceding gemm_bf16_kernel launch: one single-wave
 // workgroup per (split tile q, wave w of the tile, half h of that wave's output
-// columns) sums its accumulators over the parts in part order and runs its share of
-// the tile's epilogue.  Eight workgroups per tile, and all loads of a part issued
-// together, keep many loads of the partials in flight.
+// columns, row block tm of that wave) sums its accumulators over the parts in part
+// order and runs its share of the tile's epilogue.  32 workgroups per tile, each with
+// the loads of every part issued before the first sum, keep the partials' reads in
+// flight together.
 template <int BM, int EPI>
 __global__ __launch_bounds__(kWave) void gemm_split_finish_kernel(GemmArgs g) {
   using IO = TileIO<BM, EPI == EPI_SWIGLU, false>;
   using S = typename IO::S;
   using SS = SplitSlot<IO>;
   constexpr int TM = IO::TM, TN = IO::TN, NV = S::ACC / 4;
-  const int q = blockIdx.x / 8, wave = (blockIdx.x / 2) % 4, half = blockIdx.x % 2;
+  const int q = blockIdx.x / (8 * TM), wave = (blockIdx.x / (2 * TM)) % 4;
+  const int half = (blockIdx.x / TM) % 2, tm_w = blockIdx.x % TM;
   // (the product launch it finishes did nothing: its split descriptors are stale)
   if (g.small_tiles && *g.small_tiles != (BM < 256 ? 1 : 0)) return;
   if (q >= g.split_desc[0]) return;
@@ -818,44 +823,55 @@ __global__ __launch_bounds__(kWave) void gemm_split_finish_kernel(GemmArgs g) {
   const int wm = wave >> 1, wn = wave & 1;
   const int nb = (tile.m_valid + S::M - 1) / S::M;
   const int ta = __builtin_amdgcn_readfirstlane(min(max((nb - wm + 1) / 2, 0), TM));
+  if (tm_w >= ta) return;  // this row block holds no rows of the tile
   typename S::acc_t acc[TN][TM];
-  auto run = [&](auto ta_c, auto half_c) {
-    constexpr int TA = decltype(ta_c)::value, H = decltype(half_c)::value;
+  auto run = [&](auto tm_c, auto half_c) {
+    constexpr int TMI = decltype(tm_c)::value, H = decltype(half_c)::value;
     // the two accumulator tiles behind this half's output columns
     constexpr int NS = EPI == EPI_SWIGLU ? TN / 2 : TN;
     constexpr int T0 = H * NS / 2;
     constexpr int TNA = T0, TNB = EPI == EPI_SWIGLU ? T0 + TN / 2 : T0 + 1;
-    for (int p = 0; p < tile.nparts; ++p) {
-      const f32x4_t* sp = SS::at(g.split_buf, q * tile.nparts + p);
-      f32x4_t x[2][TA > 0 ? TA : 1][NV];
+    f32x4_t x[kMaxSplitParts][2][NV];
 #pragma unroll
-      for (int tm = 0; tm < TA; ++tm)
+    for (int p = 0; p < kMaxSplitParts; ++p) {
+      if (p < tile.nparts) {
+        const f32x4_t* sp = SS::at(g.split_buf, q * tile.nparts + p);
 #pragma unroll
         for (int v = 0; v < NV; ++v) {
-          x[0][tm][v] = sp[SS::chunk(TNA, tm, v) * kThreads + tid];
-          x[1][tm][v] = sp[SS::chunk(TNB, tm, v) * kThreads + tid];
+          x[p][0][v] = sp[SS::chunk(TNA, TMI, v) * kThreads + tid];
+          x[p][1][v] = sp[SS::chunk(TNB, TMI, v) * kThreads + tid];
         }
+      }
+    }
 #pragma unroll
-      for (int tm = 0; tm < TA; ++tm)
+    for (int v = 0; v < NV; ++v)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        acc[TNA][TMI][4 * v + r] = x[0][0][v][r];
+        acc[TNB][TMI][4 * v + r] = x[0][1][v][r];
+      }
+#pragma unroll
+    for (int p = 1; p < kMaxSplitParts; ++p) {
+      if (p < tile.nparts) {
 #pragma unroll
         for (int v = 0; v < NV; ++v)
 #pragma unroll
           for (int r = 0; r < 4; ++r) {
-            const float a = acc[TNA][tm][4 * v + r], b = acc[TNB][tm][4 * v + r];
-            acc[TNA][tm][4 * v + r] = p == 0 ? x[0][tm][v][r] : a + x[0][tm][v][r];
-            acc[TNB][tm][4 * v + r] = p == 0 ? x[1][tm][v][r] : b + x[1][tm][v][r];
+            acc[TNA][TMI][4 * v + r] += x[p][0][v][r];
+            acc[TNB][TMI][4 * v + r] += x[p][1][v][r];
           }
+      }
     }
-    tile_epilogue<IO, EPI, TA, H>(g, tile, lane, wm, wn, acc);
+    tile_epilogue<IO, EPI, TM, H, TMI>(g, tile, lane, wm, wn, acc);
   };
-  auto by_ta = [&](auto half_c) {
-    if (ta == 1) run(std::integral_constant<int, 1>{}, half_c);
-    else if (ta == 2) run(std::integral_constant<int, 2>{}, half_c);
-    else if (ta == 3) run(std::integral_constant<int, 3>{}, half_c);
-    else if (ta >= 4) run(std::integral_constant<int, 4>{}, half_c);
+  auto by_tm = [&](auto half_c) {
+    if (tm_w == 0) run(std::integral_constant<int, 0>{}, half_c);
+    if constexpr (TM > 1) if (tm_w == 1) run(std::integral_constant<int, 1>{}, half_c);
+    if constexpr (TM > 2) if (tm_w == 2) run(std::integral_constant<int, 2>{}, half_c);
+    if constexpr (TM > 3) if (tm_w == 3) run(std::integral_constant<int, 3>{}, half_c);
   };
-  if (half == 0) by_ta(std::integral_constant<int, 0>{});
-  else by_ta(std::integral_constant<int, 1>{});
+  if (half == 0) by_tm(std::integral_constant<int, 0>{});
+  else by_tm(std::integral_constant<int, 1>{});
 }
 
 // ------------------------------------------------------------------ float32 SIMT kernel
@@ -970,8 +986,10 @@ hipError_t launch_bf16_bm(hipStream_t st, GemmArgs g, int64_t max_rows, bool ksp
                        dim3(kThreads), 0, st, g);
     const hipError_t err = hipGetLastError();
     if (err != hipSuccess) return err;
+    constexpr int kFinishPerTile = 8 * TileIO<BM, EPI == EPI_SWIGLU, false>::TM;
     hipLaunchKernelGGL((gemm_split_finish_kernel<BM, EPI>),
-                       dim3(static_cast<unsigned>(g.split_g / 2 * 8)), dim3(kWave), 0, st, g);
+                       dim3(static_cast<unsigned>(g.split_g / 2 * kFinishPerTile)), dim3(kWave),
+                       0, st, g);
     return hipGetLastError();
   }
   if (ksplit)
