@@ -263,9 +263,7 @@ __global__ __launch_bounds__(kThreads) void route_kernel(
 
 // ------------------------------------------------------------ bf16 logits product
 constexpr int kLT = 64;    // tokens per logits workgroup
-constexpr int kLKC = 32;   // k per LDS chunk
-constexpr int kLRow = 40;  // LDS row stride in bf16: 80-byte rows make the 16-byte
-                           // fragment reads of 16 consecutive rows conflict free
+constexpr int kLKC = 32;   // k per LDS chunk (the least; a slice is a multiple of it)
 
 // W_router [d][E] float32 -> wp[3][E_pad][d] bf16 (k contiguous), the exact three-part
 // split w = hi + mid + lo (each part the bf16 rounding of what the previous parts left);
@@ -319,40 +317,50 @@ __global__ __launch_bounds__(kThreads) void route_split_kernel(const float* __re
 
 // Partial logits part[z][t][e] = sum over k in slice z of x[t][k] * w[k][e], for the
 // 64 tokens of workgroup x, the EPT*16 experts of group y and the k slice z (kper wide).
-// Wave w owns tokens 16w..16w+15 and all the group's experts: per 32-deep chunk one
-// activation fragment and 3*EPT weight fragments, 3*EPT MFMAs.  Chunks are staged
-// through LDS, double buffered, with the next chunk's global loads in flight during
-// the current chunk's MFMAs.
-template <int EPT>
+// Wave w owns tokens 16w..16w+15 and all the group's experts: per KC-deep chunk KC/32
+// activation fragments and 3*EPT*KC/32 weight fragments, as many MFMAs.  Chunks are
+// staged through LDS, double buffered, with the next chunk's global loads in flight
+// during the current chunk's MFMAs.  With few experts a chunk is little work, so the
+// loop runs at one global-load round trip per chunk: those groups take deeper chunks.
+// LDS rows are KC + 8 bf16 long, which keeps the 16-byte fragment reads of 16
+// consecutive rows on distinct banks.
+template <int EPT, int KC>
 __global__ __launch_bounds__(kThreads) void route_logits_kernel(
     const uint16_t* __restrict__ x, int64_t n, int64_t d, const uint16_t* __restrict__ wp,
     int E_pad, int64_t kper, float* __restrict__ part, int E) {
+  constexpr int R = KC + 8;                      // LDS row stride (bf16)
+  constexpr int PPR = KC / 8;                    // 16-byte pieces per row and chunk
+  constexpr int XPT = kLT * PPR / kThreads;      // activation pieces per thread
   constexpr int WROWS = 3 * EPT * 16;            // weight rows per chunk (3 parts)
-  constexpr int WPIECES = WROWS * 4;             // 16-byte pieces per chunk
+  constexpr int WPIECES = WROWS * PPR;           // 16-byte pieces per chunk
   constexpr int WPT = (WPIECES + kThreads - 1) / kThreads;
-  __shared__ __attribute__((aligned(16))) uint16_t xs[2][kLT * kLRow];
-  __shared__ __attribute__((aligned(16))) uint16_t ws[2][WROWS * kLRow];
+  static_assert(XPT * kThreads == kLT * PPR, "whole activation pieces per thread");
+  __shared__ __attribute__((aligned(16))) uint16_t xs[2][kLT * R];
+  __shared__ __attribute__((aligned(16))) uint16_t ws[2][WROWS * R];
   const int tid = threadIdx.x, lane = tid & (kWave - 1), wave = tid / kWave;
   const int64_t t0 = static_cast<int64_t>(blockIdx.x) * kLT;
   const int e0 = blockIdx.y * EPT * 16;
   const int64_t kb = static_cast<int64_t>(blockIdx.z) * kper;
   const int64_t ke = min(d, kb + kper);
-  const int nch = static_cast<int>((ke - kb + kLKC - 1) / kLKC);
+  const int nch = static_cast<int>((ke - kb + KC - 1) / KC);
   const int64_t plane = static_cast<int64_t>(E_pad) * d;
 
-  // this thread's load pieces: x row tid/4, chunk piece tid%4; weights piece tid + 256 j
-  const int xr = tid >> 2, xp = tid & 3;
-  const bool x_ok = t0 + xr < n;
-  const uint16_t* xsrc = x + (x_ok ? t0 + xr : 0) * d + xp * 8;
-  u32x4_t xv, wv[WPT];
+  // activation piece i = tid + 256 j: row i / PPR, piece i % PPR; weights likewise
+  u32x4_t xv[XPT], wv[WPT];
   auto load = [&](int c) {
-    const int64_t k = kb + static_cast<int64_t>(c) * kLKC;
+    const int64_t k = kb + static_cast<int64_t>(c) * KC;
     const u32x4_t zero = {0u, 0u, 0u, 0u};
-    xv = (x_ok && k + xp * 8 < ke) ? *reinterpret_cast<const u32x4_t*>(xsrc + k) : zero;
+#pragma unroll
+    for (int j = 0; j < XPT; ++j) {
+      const int i = tid + kThreads * j;
+      const int row = i / PPR, pc = i % PPR;
+      const bool ok = t0 + row < n && k + pc * 8 < ke;
+      xv[j] = ok ? *reinterpret_cast<const u32x4_t*>(x + (t0 + row) * d + k + pc * 8) : zero;
+    }
 #pragma unroll
     for (int j = 0; j < WPT; ++j) {
       const int i = tid + kThreads * j;
-      const int row = i >> 2, pc = i & 3;
+      const int row = i / PPR, pc = i % PPR;
       const int p = row / (EPT * 16), er = row - p * (EPT * 16);
       wv[j] = (i < WPIECES && k + pc * 8 < ke)
                   ? *reinterpret_cast<const u32x4_t*>(wp + p * plane +
@@ -361,11 +369,15 @@ __global__ __launch_bounds__(kThreads) void route_logits_kernel(
     }
   };
   auto store = [&](int buf) {
-    *reinterpret_cast<u32x4_t*>(&xs[buf][xr * kLRow + xp * 8]) = xv;
+#pragma unroll
+    for (int j = 0; j < XPT; ++j) {
+      const int i = tid + kThreads * j;
+      *reinterpret_cast<u32x4_t*>(&xs[buf][(i / PPR) * R + (i % PPR) * 8]) = xv[j];
+    }
 #pragma unroll
     for (int j = 0; j < WPT; ++j) {
       const int i = tid + kThreads * j;
-      if (i < WPIECES) *reinterpret_cast<u32x4_t*>(&ws[buf][(i >> 2) * kLRow + (i & 3) * 8]) = wv[j];
+      if (i < WPIECES) *reinterpret_cast<u32x4_t*>(&ws[buf][(i / PPR) * R + (i % PPR) * 8]) = wv[j];
     }
   };
 
@@ -381,14 +393,18 @@ __global__ __launch_bounds__(kThreads) void route_logits_kernel(
   for (int c = 0; c < nch; ++c) {
     const int buf = c & 1;
     if (c + 1 < nch) load(c + 1);
-    const bf16x8_t a = *reinterpret_cast<const bf16x8_t*>(&xs[buf][(16 * wave + fr) * kLRow + fk]);
 #pragma unroll
-    for (int et = 0; et < EPT; ++et) {
+    for (int kk = 0; kk < KC; kk += 32) {
+      const bf16x8_t a =
+          *reinterpret_cast<const bf16x8_t*>(&xs[buf][(16 * wave + fr) * R + kk + fk]);
 #pragma unroll
-      for (int p = 0; p < 3; ++p) {
-        const bf16x8_t b = *reinterpret_cast<const bf16x8_t*>(
-            &ws[buf][(p * EPT * 16 + et * 16 + fr) * kLRow + fk]);
-        acc[et] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, acc[et], 0, 0, 0);
+      for (int et = 0; et < EPT; ++et) {
+#pragma unroll
+        for (int p = 0; p < 3; ++p) {
+          const bf16x8_t b = *reinterpret_cast<const bf16x8_t*>(
+              &ws[buf][(p * EPT * 16 + et * 16 + fr) * R + kk + fk]);
+          acc[et] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, acc[et], 0, 0, 0);
+        }
       }
     }
     if (c + 1 < nch) store(buf ^ 1);
@@ -597,8 +613,10 @@ hipError_t launch_logits_t(hipStream_t st, const uint16_t* x, const RoutePlan& p
                            const uint16_t* wp, float* part) {
   const dim3 grid(static_cast<unsigned>(pl.token_tiles), static_cast<unsigned>(pl.egroups),
                   static_cast<unsigned>(pl.ks));
-  hipLaunchKernelGGL((route_logits_kernel<EPT>), grid, dim3(kThreads), 0, st, x, pl.n, pl.d,
-                     wp, pl.e_pad, pl.kper, part, pl.e);
+  // deeper chunks where a chunk is little work (LDS stays under 90 KB)
+  constexpr int KC = EPT <= 2 ? 128 : EPT <= 4 ? 64 : kLKC;
+  hipLaunchKernelGGL((route_logits_kernel<EPT, KC>), grid, dim3(kThreads), 0, st, x, pl.n,
+                     pl.d, wp, pl.e_pad, pl.kper, part, pl.e);
   return hipGetLastError();
 }
 
