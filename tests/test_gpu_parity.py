@@ -583,6 +583,18 @@ def test_forward_parity_full_size_sampled(name):
     torch.cuda.empty_cache()
 
 
+@pytest.mark.parametrize("n,d,d_ff,E", [(256, 1024, 2048, 8), (512, 1280, 2048, 16)])
+def test_forward_parity_split_last_round(n, d, d_ff, E):
+    """Few tiles on a 256-CU GPU: the expert products split their partial last round
+    along K (here GEMM1 into 2 parts, GEMM2 into 4 or 3), and the finishing launch sums
+    the parts; the layer must still match the oracle."""
+    cfg = CONFIGS["mixtral"].scaled(n_tokens=n, d_model=d, d_ff=d_ff, n_experts=E)
+    print_case("forward-split", cfg.name, cfg.n_tokens)
+    err, r, _ = _forward_and_oracle(cfg)
+    print(f"  d={d} d_ff={d_ff} E={E}: normwise error {err:.3e}", flush=True)
+    assert err <= TOL[cfg.dtype]
+
+
 def test_forward_is_deterministic():
     cfg = CONFIGS["mixtral"].with_tokens(300).scaled(d_ff=1024)
     print_case("determinism", cfg.name, cfg.n_tokens)
