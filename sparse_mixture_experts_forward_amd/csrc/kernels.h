@@ -43,7 +43,7 @@ struct RoutePlan {
   int64_t n, d;
   int e, e_pad;          // experts, padded to whole expert groups
   int ept, egroups;      // 16-expert tiles per workgroup, expert groups
-  int64_t token_tiles;   // 64-token tiles
+  int64_t token_tiles;   // token tiles (64 or 128 tokens, by the expert group width)
   int64_t kper;          // d_model slice per workgroup (multiple of 32)
   int ks;                // number of slices
 };

@@ -264,6 +264,8 @@ __global__ __launch_bounds__(kThreads) void route_kernel(
 // ------------------------------------------------------------ bf16 logits product
 constexpr int kLT = 64;    // tokens per logits workgroup
 constexpr int kLKC = 32;   // k per LDS chunk (the least; a slice is a multiple of it)
+// 16-token blocks per wave of the logits product for EPT 16-expert tiles per workgroup
+constexpr int route_token_blocks(int ept) { return ept >= 6 ? 2 : 1; }
 
 // W_router [d][E] float32 -> wp[3][E_pad][d] bf16 (k contiguous), the exact three-part
 // split w = hi + mid + lo (each part the bf16 rounding of what the previous parts left);
@@ -316,29 +318,32 @@ __global__ __launch_bounds__(kThreads) void route_split_kernel(const float* __re
 }
 
 // Partial logits part[z][t][e] = sum over k in slice z of x[t][k] * w[k][e], for the
-// 64 tokens of workgroup x, the EPT*16 experts of group y and the k slice z (kper wide).
-// Wave w owns tokens 16w..16w+15 and all the group's experts: per KC-deep chunk KC/32
-// activation fragments and 3*EPT*KC/32 weight fragments, as many MFMAs.  Chunks are
+// 64*TT tokens of workgroup x, the EPT*16 experts of group y and the k slice z (kper
+// wide).  Wave w owns TT blocks of 16 tokens (block j: tokens 16(4j+w)..+15) and all
+// the group's experts: per KC-deep chunk TT*KC/32 activation fragments and
+// 3*EPT*KC/32 weight fragments, TT times as many MFMAs.  With many experts the
+// weights dominate what a workgroup reads, and TT = 2 halves their re-reads.  Chunks are
 // staged through LDS, double buffered, with the next chunk's global loads in flight
 // during the current chunk's MFMAs.  With few experts a chunk is little work, so the
 // loop runs at one global-load round trip per chunk: those groups take deeper chunks.
 // LDS rows are KC + 8 bf16 long, which keeps the 16-byte fragment reads of 16
 // consecutive rows on distinct banks.
-template <int EPT, int KC>
+template <int EPT, int KC, int TT>
 __global__ __launch_bounds__(kThreads) void route_logits_kernel(
     const uint16_t* __restrict__ x, int64_t n, int64_t d, const uint16_t* __restrict__ wp,
     int E_pad, int64_t kper, float* __restrict__ part, int E) {
   constexpr int R = KC + 8;                      // LDS row stride (bf16)
   constexpr int PPR = KC / 8;                    // 16-byte pieces per row and chunk
-  constexpr int XPT = kLT * PPR / kThreads;      // activation pieces per thread
+  constexpr int LT = kLT * TT;                   // tokens per workgroup
+  constexpr int XPT = LT * PPR / kThreads;       // activation pieces per thread
   constexpr int WROWS = 3 * EPT * 16;            // weight rows per chunk (3 parts)
   constexpr int WPIECES = WROWS * PPR;           // 16-byte pieces per chunk
   constexpr int WPT = (WPIECES + kThreads - 1) / kThreads;
-  static_assert(XPT * kThreads == kLT * PPR, "whole activation pieces per thread");
-  __shared__ __attribute__((aligned(16))) uint16_t xs[2][kLT * R];
+  static_assert(XPT * kThreads == LT * PPR, "whole activation pieces per thread");
+  __shared__ __attribute__((aligned(16))) uint16_t xs[2][LT * R];
   __shared__ __attribute__((aligned(16))) uint16_t ws[2][WROWS * R];
   const int tid = threadIdx.x, lane = tid & (kWave - 1), wave = tid / kWave;
-  const int64_t t0 = static_cast<int64_t>(blockIdx.x) * kLT;
+  const int64_t t0 = static_cast<int64_t>(blockIdx.x) * LT;
   const int e0 = blockIdx.y * EPT * 16;
   const int64_t kb = static_cast<int64_t>(blockIdx.z) * kper;
   const int64_t ke = min(d, kb + kper);
@@ -381,9 +386,11 @@ __global__ __launch_bounds__(kThreads) void route_logits_kernel(
     }
   };
 
-  f32x4_t acc[EPT];
+  f32x4_t acc[TT][EPT];
 #pragma unroll
-  for (int et = 0; et < EPT; ++et) acc[et] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+  for (int tt = 0; tt < TT; ++tt)
+#pragma unroll
+    for (int et = 0; et < EPT; ++et) acc[tt][et] = f32x4_t{0.f, 0.f, 0.f, 0.f};
   const int fr = lane & 15, fk = (lane >> 4) * 8;  // fragment row and k offset of a lane
   if (nch > 0) {
     load(0);
@@ -395,32 +402,39 @@ __global__ __launch_bounds__(kThreads) void route_logits_kernel(
     if (c + 1 < nch) load(c + 1);
 #pragma unroll
     for (int kk = 0; kk < KC; kk += 32) {
-      const bf16x8_t a =
-          *reinterpret_cast<const bf16x8_t*>(&xs[buf][(16 * wave + fr) * R + kk + fk]);
+      bf16x8_t a[TT];
+#pragma unroll
+      for (int tt = 0; tt < TT; ++tt)
+        a[tt] = *reinterpret_cast<const bf16x8_t*>(
+            &xs[buf][(16 * (4 * tt + wave) + fr) * R + kk + fk]);
 #pragma unroll
       for (int et = 0; et < EPT; ++et) {
 #pragma unroll
         for (int p = 0; p < 3; ++p) {
           const bf16x8_t b = *reinterpret_cast<const bf16x8_t*>(
               &ws[buf][(p * EPT * 16 + et * 16 + fr) * R + kk + fk]);
-          acc[et] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, acc[et], 0, 0, 0);
+#pragma unroll
+          for (int tt = 0; tt < TT; ++tt)
+            acc[tt][et] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[tt], b, acc[tt][et], 0, 0, 0);
         }
       }
     }
     if (c + 1 < nch) store(buf ^ 1);
     __syncthreads();
   }
-  // lane holds tokens 16 w + 4 (lane/16) + r, expert e0 + 16 et + lane%16
+  // lane holds tokens 16 (4 tt + w) + 4 (lane/16) + r, expert e0 + 16 et + lane%16
 #pragma unroll
-  for (int et = 0; et < EPT; ++et) {
-    const int e = e0 + et * 16 + fr;
-    if (e >= E) continue;
+  for (int tt = 0; tt < TT; ++tt)
 #pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      const int64_t t = t0 + 16 * wave + 4 * (lane >> 4) + r;
-      if (t < n) part[(static_cast<int64_t>(blockIdx.z) * n + t) * E + e] = acc[et][r];
+    for (int et = 0; et < EPT; ++et) {
+      const int e = e0 + et * 16 + fr;
+      if (e >= E) continue;
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int64_t t = t0 + 16 * (4 * tt + wave) + 4 * (lane >> 4) + r;
+        if (t < n) part[(static_cast<int64_t>(blockIdx.z) * n + t) * E + e] = acc[tt][et][r];
+      }
     }
-  }
 }
 
 // ------------------------------------------------------------ gate
@@ -613,9 +627,11 @@ hipError_t launch_logits_t(hipStream_t st, const uint16_t* x, const RoutePlan& p
                            const uint16_t* wp, float* part) {
   const dim3 grid(static_cast<unsigned>(pl.token_tiles), static_cast<unsigned>(pl.egroups),
                   static_cast<unsigned>(pl.ks));
-  // deeper chunks where a chunk is little work (LDS stays under 90 KB)
+  // deeper chunks where a chunk is little work, more tokens where the weights are most
+  // of it (LDS stays under 100 KB)
   constexpr int KC = EPT <= 2 ? 128 : EPT <= 4 ? 64 : kLKC;
-  hipLaunchKernelGGL((route_logits_kernel<EPT, KC>), grid, dim3(kThreads), 0, st, x, pl.n,
+  constexpr int TT = route_token_blocks(EPT);
+  hipLaunchKernelGGL((route_logits_kernel<EPT, KC, TT>), grid, dim3(kThreads), 0, st, x, pl.n,
                      pl.d, wp, pl.e_pad, pl.kper, part, pl.e);
   return hipGetLastError();
 }
@@ -654,7 +670,8 @@ RoutePlan route_plan(int64_t n, int64_t d, int e) {
     if (v >= tiles) { pl.ept = v; break; }
   pl.egroups = (tiles + pl.ept - 1) / pl.ept;
   pl.e_pad = pl.egroups * pl.ept * 16;
-  pl.token_tiles = (n + kLT - 1) / kLT;
+  const int64_t lt = static_cast<int64_t>(kLT) * route_token_blocks(pl.ept);
+  pl.token_tiles = (n + lt - 1) / lt;
   // split d so that about 256 workgroups run (at most 16 slices: the gate adds them)
   const int64_t chunks = (d + kLKC - 1) / kLKC;
   const int64_t base = pl.token_tiles * pl.egroups;
