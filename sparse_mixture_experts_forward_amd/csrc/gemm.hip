@@ -29,8 +29,10 @@
 //     segment by segment, 8 column tiles x all row tiles of a segment at a time, so the
 //     row tiles that share a weight panel land on one XCD (workgroup id mod 8).  With
 //     few rounds, a partial last round is split along K (gemm_split_finish_kernel sums
-//     the parts).  With MOE_GEMM_XCD_REMAP the workgroup -> tile map gives each XCD a
-//     contiguous range of that order instead of every eighth tile.
+//     the parts).  When every segment fits one row tile, segments are dealt out one per
+//     XCD instead, so that a segment's column tiles share its rows through one L2;
+//   * where the host cannot bound the rows per segment well (a capacity limit), the
+//     dispatch flags the tile height and both launches are made, one of them empty.
 // float32 kernel: a plain LDS-tiled SIMT product (64 x 64 tiles) with the same
 // scheduling and epilogues; it serves the small float32 workload.
 
@@ -45,13 +47,7 @@ namespace {
 constexpr int kThreads = 256;
 constexpr int kBK = 64;       // bf16: reduction depth per LDS stage (128-byte rows)
 constexpr int kBRows = 256;   // bf16: weight rows per workgroup
-#ifndef MOE_GEMM_GROUP_N
-#define MOE_GEMM_GROUP_N 8
-#endif
-#ifndef MOE_GEMM_XCD_REMAP
-#define MOE_GEMM_XCD_REMAP 0
-#endif
-constexpr int kGroupN = MOE_GEMM_GROUP_N;  // column tiles per scheduling group
+constexpr int kGroupN = 8;  // column tiles per scheduling group
 constexpr int kXcds = 8;
 constexpr int kMaxSplitParts = 4;  // K parts of a split tile
 
@@ -143,13 +139,6 @@ __device__ bool schedule_tile(const int32_t* __restrict__ seg_off, int n_seg,
   tile.part = 0;
   tile.nparts = 1;
   tile.split_q = 0;
-#if MOE_GEMM_XCD_REMAP
-  const int xcd = blockIdx.x % kXcds;
-  const int i = blockIdx.x / kXcds;
-  const int per = (total + kXcds - 1) / kXcds;
-  const int L = xcd * per + i;
-  if (i >= per || L >= total) return false;
-#else
   int L = blockIdx.x;
   const int full = split_g > 0 ? total / split_g * split_g : total;
   const int r = total - full;
@@ -171,7 +160,6 @@ __device__ bool schedule_tile(const int32_t* __restrict__ seg_off, int n_seg,
   } else if (L >= total) {
     return false;
   }
-#endif
   if (!multi) {
     // Every segment is one row tile of n_ntiles work items, so nothing reuses a weight
     // panel; what tiles share is a segment's activation rows.  Take the segments 8 at a
