@@ -8,6 +8,7 @@
  *   [DeepSeek-V2]  www.wzjinhao.cn/news/59210, summary of the DeepSeek-V2 report
  *   [MoE-2pct]     www.mhpn.cn/news/707057, "拆解大模型里被悄悄激活的那2%"
  *   [MoE-overview] www.mooersco.com/news/2648626, MoE overview
+ *   [GPT4-2pct]    www.l189.com/news/1751418, on GPT-4 using 2% of its parameters per token
  *
  * Conventions shared by every entry point
  *   - Pointers are DEVICE pointers unless a comment says otherwise.  The caller owns
