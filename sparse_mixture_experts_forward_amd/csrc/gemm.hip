@@ -270,6 +270,7 @@ struct TileIO {
   static constexpr int TN = 128 / S::M;        // MFMA tiles per wave along weight rows
   static constexpr int A_GRPS = BM / 8;        // 8-row load groups of A per stage
   static constexpr int A_GRP = A_GRPS / 4;     // per wave
+  static constexpr int GPB = S::M / 16;        // per wave and row block (two waves share one)
   static constexpr int B_GRP = kBRows / 32;    // 8-row load groups of B per wave per stage
   static_assert(A_GRPS % 4 == 0, "BM must be a multiple of 32");
   // LDS ring depth of the weight operand: the 256-row tiles spend the whole 160 KB of
@@ -285,8 +286,9 @@ struct TileIO {
   int co[S::KSTEPS];      // swizzled element offset of this lane's chunk per k-step
   int64_t kchunk, kbatch_stride;
 
-  // Loads of one stage: wave w fills the 8-row groups w, w+4, ... of the tile; one
-  // instruction moves 8 rows x 128 bytes (whole cache lines).  Lane l writes LDS row
+  // Loads of one stage: wave w fills the weight 8-row groups w, w+4, ... of the tile and
+  // the activation groups of its own row blocks (a_group; none past the tile's rows);
+  // one instruction moves 8 rows x 128 bytes (whole cache lines).  Lane l writes LDS row
   // 8*group + l/8, physical chunk l%8, and so loads logical chunk (l%8) ^ f(row).
   // Each is a buffer load into LDS (buffer_load_dwordx4 ... lds): a buffer resource in
   // scalar registers whose base carries k, plus the loop-invariant unsigned 32-bit lane
@@ -297,15 +299,25 @@ struct TileIO {
   // count 0xFFFFFFFF leaves every 32-bit offset in range, as with a plain pointer.
   // The resource builtins exist only for the device target, hence the guard (the
   // host pass compiles these bodies away).
+  // LDS 8-row group of this wave's activation load j: the wave's row blocks are wm,
+  // wm + 2, ... (those its MFMAs use), and of each block's groups the two waves of a
+  // wave row load one half each (wn).  A wave with TA active blocks issues TA * GPB loads.
+  __device__ __forceinline__ int a_group(int j) const {
+    return (wm + 2 * (j / GPB)) * (S::M / 8) + wn * GPB + j % GPB;
+  }
+  template <int NA>
   __device__ __forceinline__ void dma_a(uint16_t* as, int k0) const {
+    static_assert(NA <= A_GRP, "activation loads per wave");
 #if defined(__HIP_DEVICE_COMPILE__)
-    const char* ak = reinterpret_cast<const char*>(a_base + k0);
-    const __amdgpu_buffer_rsrc_t r = __builtin_amdgcn_make_buffer_rsrc(
-        const_cast<char*>(ak), static_cast<short>(0), -1, 0x00020000);
+    if constexpr (NA > 0) {
+      const char* ak = reinterpret_cast<const char*>(a_base + k0);
+      const __amdgpu_buffer_rsrc_t r = __builtin_amdgcn_make_buffer_rsrc(
+          const_cast<char*>(ak), static_cast<short>(0), -1, 0x00020000);
 #pragma unroll
-    for (int j = 0; j < A_GRP; ++j)
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void_t*)(as + (wave + 4 * j) * 8 * kBK),
-                                               16, a_off[j], 0, 0, 0);
+      for (int j = 0; j < NA; ++j)
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void_t*)(as + a_group(j) * 8 * kBK),
+                                                 16, a_off[j], 0, 0, 0);
+    }
 #endif
   }
   __device__ __forceinline__ void dma_b(uint16_t* bs, int k0) const {
@@ -450,12 +462,12 @@ __device__ __forceinline__ void pipe_stage(const IO& io, uint16_t* ac, uint16_t*
                                            typename IO::S::acc_t (&acc)[IO::TN][IO::TM]) {
   constexpr int KS = IO::S::KSTEPS;
   constexpr int R = TA > 0 ? IO::TN + TA : 0, P = IO::TN * TA;
-  constexpr int LA = IO::A_GRP, LB = IO::B_GRP;
+  constexpr int LA = TA * IO::GPB, LB = IO::B_GRP;
   static_assert(KS % 2 == 0, "an even number of k-steps per stage");
   inner_steps<IO, TA, 0, KS - 1>(io, ac, bc, f, acc);
   barrier_keep_loads<IO::NBB == 3 ? LB : 0>();
   // the last k-step's MFMAs, split in two halves around the activation / weight loads
-  io.dma_a(ac, ka);
+  io.template dma_a<LA>(ac, ka);
   read_frags<IO, TA>(io, an, bn, 0, f[0]);
   mma_frags_half<IO, TA, 0>(f[1], acc);
   sched_mix<LA, R, P / 2, 0, (R > LA ? R : LA)>();
@@ -645,6 +657,21 @@ __device__ __forceinline__ void tile_body(const GemmArgs& g, const Tile& tile, c
     for (int b = 0; b < TA; ++b)
 #pragma unroll
       for (int r = 0; r < S::ACC; ++r) acc[a][b][r] = 0.f;
+  // prologue: issue A0 A1 B0 B1 (B2), then wait for all but the last weight stage or
+  // two, so at every later boundary exactly the weight loads of the boundary before may
+  // still be in flight (weight loads are always issued last).  Stages past the last one
+  // repeat it.
+  constexpr int LA = TA * IO::GPB, LB = IO::B_GRP;
+  io.template dma_a<LA>(As0, 0);
+  io.template dma_a<LA>(As1, min(1, KT - 1) * kBK);
+  io.dma_b(Bs0, 0);
+  io.dma_b(Bs1, min(1, KT - 1) * kBK);
+  if constexpr (IO::NBB == 3) {
+    io.dma_b(Bs2, min(2, KT - 1) * kBK);
+    barrier_keep_loads<LB + LB>();
+  } else {
+    barrier_keep_loads<LB>();
+  }
   k_loop<IO, TA>(io, As0, As1, Bs0, Bs1, Bs2, KT, acc);
   // no load may still be writing this workgroup's LDS when it exits
   __builtin_amdgcn_s_waitcnt(0);
@@ -711,7 +738,7 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_bf16_kernel(GemmArgs g) {
       uniform_ptr(static_cast<const uint16_t*>(g.a) + (a_rows ? 0 : tile.row0 * g.lda) + k_ofs);
 #pragma unroll
   for (int j = 0; j < IO::A_GRP; ++j) {
-    const int i = 8 * (wave + 4 * j) + dl_row;  // LDS row of the tile
+    const int i = 8 * io.a_group(j) + dl_row;  // LDS row of the tile
     const int r = min(i, tile.m_valid - 1);     // rows past the segment repeat its last row
     const uint32_t src = a_rows ? static_cast<uint32_t>(a_rows[tile.row0 + r]) : r;
     const int chunk = ((lane & 7) ^ lds_swizzle(i)) * 8;
@@ -739,22 +766,6 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_bf16_kernel(GemmArgs g) {
   const int wm = io.wm;
 
   const int KT = tile.k_stages;
-  constexpr int LA = IO::A_GRP, LB = IO::B_GRP;  // direct-to-LDS loads per wave per stage
-  // prologue: with a 3-deep weight ring, issue A0 B0 B1 A1 B2 (at every later boundary
-  // exactly the weight loads of the boundary before may still be in flight); else
-  // A0 B0 A1 B1.  Stages past the last one repeat it.
-  io.dma_a(As0, 0);
-  io.dma_b(Bs0, 0);
-  if constexpr (IO::NBB == 3) {
-    io.dma_b(Bs1, min(1, KT - 1) * kBK);
-    io.dma_a(As1, min(1, KT - 1) * kBK);
-    io.dma_b(Bs2, min(2, KT - 1) * kBK);
-    barrier_keep_loads<LB + LA + LB>();
-  } else {
-    io.dma_a(As1, min(1, KT - 1) * kBK);
-    io.dma_b(Bs1, min(1, KT - 1) * kBK);
-    barrier_keep_loads<LA + LB>();
-  }
   // row blocks of this wave that hold rows of the tile (every wave runs the same stages
   // and barriers; only the MFMA work differs)
   const int nb = (tile.m_valid + S::M - 1) / S::M;
