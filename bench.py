@@ -294,7 +294,7 @@ def main():
         return
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
-        print("bench.py runs on one GPU only: this build has no multi-GPU path "
+        print("bench.py runs on one GPU only: the library has no multi-GPU path "
               "(the layer is measured on a single MI355X); use --gpus 1", file=sys.stderr)
         sys.exit(2)
 
