@@ -242,15 +242,22 @@ def cpu_baseline(cfg, inp, logits, budget_s: float):
     if t < 0.6 * budget_s and n_s < n:
         n_s = int(min(n, max(n_s, n_s * 0.8 * budget_s / t)))
         t = run(n_s)
+    # the whole workload in less than the budget: time further whole passes (at most
+    # four in all) and report their mean
+    passes = 1
+    while n_s == n and passes < 4 and t * (passes + 1) / passes <= budget_s:
+        t += run(n_s)
+        passes += 1
     try:
         from threadpoolctl import threadpool_info
 
         cores = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
     except Exception:  # pragma: no cover
         cores = len(os.sched_getaffinity(0))
-    return dict(value=round(n_s / t, 2), unit="tokens/s", cores=int(cores), kind="oracle",
-                sample=f"first {n_s} of {n} tokens (router product, gate and capacity over all "
-                       f"{n}); float64 numpy; {t:.1f} s",
+    what = (f"all {n} tokens, {passes} passes" if passes > 1 else
+            f"first {n_s} of {n} tokens (router product, gate and capacity over all {n})")
+    return dict(value=round(n_s * passes / t, 2), unit="tokens/s", cores=int(cores),
+                kind="oracle", sample=f"{what}; float64 numpy; {t:.1f} s",
                 seconds=round(t, 2))
 
 
