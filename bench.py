@@ -261,6 +261,57 @@ def cpu_baseline(cfg, inp, logits, budget_s: float):
                 seconds=round(t, 2))
 
 
+def dispatch_copy(layer, x, topk_idx, kept: int, reps: int = 20) -> dict:
+    """The permuted copy of x that the gather fusion removes, measured through the C
+    ABI: moe_dispatch with and without the copy (preallocated buffers, HIP events
+    around each call on the launch stream); the difference of the medians is the
+    copy's cost, its algorithmic bytes x read once plus the kept rows written."""
+    import torch
+
+    from sparse_mixture_experts_forward_amd import _binding as B
+    from sparse_mixture_experts_forward_amd.layer import workspace
+
+    cfg = layer.cfg
+    n, k = topk_idx.shape
+    dev = x.device
+    i32 = torch.int32
+    offsets = torch.empty(cfg.n_experts + 1, dtype=i32, device=dev)
+    row_token = torch.empty(max(n * k, 1), dtype=i32, device=dev)
+    slot_row = torch.empty((n, k), dtype=i32, device=dev)
+    kept_count = torch.empty(cfg.n_experts, dtype=i32, device=dev)
+    dropped = torch.empty(1, dtype=i32, device=dev)
+    x_perm = torch.empty((max(n * k, 1), x.shape[1]), dtype=x.dtype, device=dev)
+    ws = workspace(B.moe_dispatch_workspace_size(n, k, cfg.n_experts), dev)
+    cap = layer.capacity(n)
+
+    def timed(with_copy):
+        times = []
+        for _ in range(reps + 3):
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            B.moe_dispatch(topk_idx, cfg.n_experts, cap, x if with_copy else None, offsets,
+                           row_token, slot_row, kept_count, dropped,
+                           x_perm if with_copy else None, ws)
+            e1.record()
+            torch.cuda.synchronize()
+            times.append(e0.elapsed_time(e1))
+        times = sorted(times[3:])
+        return times[len(times) // 2]
+
+    with_ms, without_ms = timed(True), timed(False)
+    es = x.element_size()
+    nbytes = n * x.shape[1] * es + kept * x.shape[1] * es
+    copy_ms = max(with_ms - without_ms, 1e-6)
+    gbps = nbytes / (copy_ms * 1e-3) / 1e9
+    return {"dispatch_with_copy_ms": round(with_ms, 5), "dispatch_index_maps_ms": round(without_ms, 5),
+            "copy_ms": round(copy_ms, 5), "copy_bytes": nbytes, "copy_gbps": round(gbps, 1),
+            "copy_frac_of_hbm": round(gbps / PEAK_HBM_GBPS, 4),
+            "stage_gbps_with_copy": round((nbytes + n * k * 8) / (with_ms * 1e-3) / 1e9, 1),
+            "note": "standalone moe_dispatch with the permuted copy of x (what the default "
+                    "gather fusion skips); copy = with minus without, medians of "
+                    f"{reps} calls"}
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -434,6 +485,8 @@ def main():
         "step_gpu_ms_events": round(step_gpu_ms, 4),
         "kernels": kernels,
     }
+    if cfg.fuse & 1 and n > 0:
+        out["dispatch_copy"] = dispatch_copy(layer, inp.x, stats["topk_idx"], kept)
     if cold is not None:
         cm = cold["stages_ms_median"]
         cold["dispatch_gbps"] = round(work["dispatch"]["bytes"] / (cm["dispatch"] * 1e-3) / 1e9, 1)
