@@ -319,6 +319,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--config", default="mixtral")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
+    ap.add_argument("--no-dispatch-copy", action="store_true",
+                    help="skip the standalone timing of the permuted copy of x")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--bias-selection-only", action="store_true",
                     help="the logit bias steers selection only (weights from the unbiased "
@@ -485,7 +487,7 @@ def main():
         "step_gpu_ms_events": round(step_gpu_ms, 4),
         "kernels": kernels,
     }
-    if cfg.fuse & 1 and n > 0:
+    if cfg.fuse & 1 and n > 0 and not args.no_dispatch_copy:
         out["dispatch_copy"] = dispatch_copy(layer, inp.x, stats["topk_idx"], kept)
     if cold is not None:
         cm = cold["stages_ms_median"]
