@@ -595,6 +595,18 @@ def test_forward_parity_split_last_round(n, d, d_ff, E):
     assert err <= TOL[cfg.dtype]
 
 
+@pytest.mark.parametrize("alpha", [None, 1.0])
+def test_forward_parity_most_experts(alpha):
+    """The largest expert count the library takes (512 segments in the GEMM scheduler,
+    the dispatch histograms and the gate), with and without a capacity limit."""
+    cfg = CONFIGS["deepseek"].scaled(n_tokens=384, d_model=128, d_ff=128, n_experts=512,
+                                     top_k=8, n_shared=0, alpha=alpha)
+    print_case("forward-most-experts", cfg.name, cfg.n_tokens)
+    err, r, _ = _forward_and_oracle(cfg)
+    print(f"  alpha={alpha}: normwise error {err:.3e}, dropped {r.plan.n_dropped}", flush=True)
+    assert err <= TOL[cfg.dtype]
+
+
 def test_forward_is_deterministic():
     cfg = CONFIGS["mixtral"].with_tokens(300).scaled(d_ff=1024)
     print_case("determinism", cfg.name, cfg.n_tokens)
