@@ -607,6 +607,22 @@ def test_forward_parity_most_experts(alpha):
     assert err <= TOL[cfg.dtype]
 
 
+def test_forward_parity_many_tokens_sampled():
+    """A batch of 65536 tokens (16 tokens per gate wave, many dispatch chunks), capacity
+    limited; routing, counts and the permutation over every token, outputs sampled."""
+    cfg = CONFIGS["switch"].scaled(n_tokens=65536, d_model=128, d_ff=256, n_experts=64,
+                                   top_k=2)
+    print_case("forward-many-tokens", cfg.name, cfg.n_tokens)
+    n = cfg.n_tokens
+    rng = np.random.default_rng(2)
+    tokens = np.unique(np.concatenate([np.arange(8), np.arange(n - 8, n),
+                                       rng.choice(n, size=48, replace=False)]))
+    err, r, _ = _forward_and_oracle(cfg, tokens=tokens)
+    print(f"  normwise error {err:.3e} on {len(tokens)} tokens, dropped {r.plan.n_dropped}",
+          flush=True)
+    assert err <= TOL[cfg.dtype]
+
+
 def test_forward_is_deterministic():
     cfg = CONFIGS["mixtral"].with_tokens(300).scaled(d_ff=1024)
     print_case("determinism", cfg.name, cfg.n_tokens)
