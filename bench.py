@@ -36,7 +36,12 @@ CSRC = os.path.join(ROOT, "sparse_mixture_experts_forward_amd", "csrc")
 # kernel symbol of each stage's launch, as rocprofv3 names it (bf16 workloads)
 STAGE_KERNEL = {"gemm1_swiglu": "gemm_bf16_kernel<256, 2, false>",
                 "gemm1_gelu": "gemm_bf16_kernel<256, 1, false>",
-                "gemm2": "gemm_bf16_kernel<256, 0, false>"}
+                "gemm2": "gemm_bf16_kernel<256, 0, false>",
+                # with packed weights and long segments
+                "packed_gemm1_swiglu": "gemm_packed_kernel<2>",
+                "packed_gemm1_gelu": "gemm_packed_kernel<1>",
+                "packed_gemm2": "gemm_packed_kernel<0>"}
+PACKED_ROWS = 256  # segments averaging this many rows take the packed-weight kernel
 CALIB_KERNEL = "MulFunctor"  # the plain float32 copy (x * 1) that scales byte counters
 
 
@@ -54,10 +59,23 @@ def sources_hash() -> str:
     return h.hexdigest()[:16]
 
 
-def stage_symbol(cfg, stage: str):
+def packed_path(cfg, capacity: int, packed: bool) -> bool:
+    """Whether the routed expert products run the packed-weight kernel: packed weights
+    given, bf16, and the library's bound on the kept rows averaging >= PACKED_ROWS per
+    expert."""
+    if not packed or cfg.dtype != "bf16":
+        return False
+    rows = cfg.n_tokens * cfg.top_k
+    if capacity >= 0:
+        rows = min(rows, capacity * cfg.n_experts)
+    return rows // cfg.n_experts >= PACKED_ROWS
+
+
+def stage_symbol(cfg, stage: str, packed: bool = False):
+    pre = "packed_" if packed else ""
     if stage == "gemm1":
-        return STAGE_KERNEL["gemm1_swiglu" if cfg.act == "swiglu" else "gemm1_gelu"]
-    return STAGE_KERNEL.get(stage)
+        return STAGE_KERNEL[pre + ("gemm1_swiglu" if cfg.act == "swiglu" else "gemm1_gelu")]
+    return STAGE_KERNEL.get(pre + stage if stage == "gemm2" else stage)
 
 
 def _pmc_rows(path: str):
@@ -102,9 +120,12 @@ def digest_pmc(cfg_name: str, dirs, calib_mib: int) -> dict:
         out[counter.lower() + "_calib_kib"] = calib[0]
         out[counter.lower() + "_scale"] = round(scale, 4)
     for stage in STAGES:
-        sym = stage_symbol(cfg, stage)
-        if sym is None:
+        syms = [x for x in (stage_symbol(cfg, stage, True), stage_symbol(cfg, stage)) if x]
+        if not syms:
             continue
+        # the packed-weight kernel where the profiled run used it, else the staged one
+        sym = next((x for x in syms
+                    if any(x in name for name in per["FETCH_SIZE"][0])), syms[-1])
         rec = {}
         for counter in ("FETCH_SIZE", "WRITE_SIZE"):
             vals, scale = per[counter]
@@ -118,9 +139,9 @@ def digest_pmc(cfg_name: str, dirs, calib_mib: int) -> dict:
     return out
 
 
-def stored_traffic(cfg_name: str, stage: str):
+def stored_traffic(cfg_name: str, stage: str, symbol: str):
     """HBM bytes per launch of a stage kernel from the committed counter digest, or None
-    if there is none or the kernels changed since it was taken."""
+    if there is none, it was taken of another kernel, or the kernels changed since."""
     path = os.path.join(PROFILES, f"traffic_{cfg_name}.json")
     if not os.path.exists(path):
         return None
@@ -130,6 +151,8 @@ def stored_traffic(cfg_name: str, stage: str):
         return None
     k = d.get("kernels", {}).get(stage)
     if not k or "fetch_size_bytes" not in k or "write_size_bytes" not in k:
+        return None
+    if k.get("symbol") != symbol:
         return None
     return k["fetch_size_bytes"] + k["write_size_bytes"]
 
@@ -322,6 +345,9 @@ def main():
     ap.add_argument("--no-dispatch-copy", action="store_true",
                     help="skip the standalone timing of the permuted copy of x")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-pack", action="store_true",
+                    help="do not pack the routed experts' weights (bf16): the expert "
+                         "products then stage both operands through LDS")
     ap.add_argument("--bias-selection-only", action="store_true",
                     help="the logit bias steers selection only (weights from the unbiased "
                          "softmax)")
@@ -386,6 +412,17 @@ def main():
     inp = synth.DeviceInputs(cfg, dev)
     layer = MoELayer.from_inputs(inp)
     n = cfg.n_tokens
+    # one-time relayout of the routed experts' weights (moe_pack_weights), outside the
+    # timed region like any other weight preparation
+    packed = cfg.dtype == "bf16" and not args.no_pack
+    pack_ms = None
+    if packed:
+        torch.cuda.synchronize()
+        tp = time.perf_counter()
+        layer.pack_weights()
+        torch.cuda.synchronize()
+        pack_ms = (time.perf_counter() - tp) * 1e3
+    use_packed = packed_path(cfg, layer.capacity(n), packed)
     stats = layer.new_stats(n)
     y = torch.empty_like(inp.x)
 
@@ -443,8 +480,8 @@ def main():
     kernels = {s: roofline(s, work[s], stage_ms[s], cfg.dtype) for s in STAGES
                if stage_ms[s] > 0 and (work[s]["flops"] > 0 or work[s]["bytes"] > 0)}
     for s, r in kernels.items():
-        r["symbol"] = stage_symbol(cfg, s)
-        r["traffic"] = stored_traffic(cfg.name, s)
+        r["symbol"] = stage_symbol(cfg, s, use_packed)
+        r["traffic"] = stored_traffic(cfg.name, s, r["symbol"])
     dominant = max(kernels, key=lambda s: stage_ms[s])
     gemm_ms = stage_ms["gemm1"] + stage_ms["gemm2"] + stage_ms["shared"]
     gemm_flops = work["gemm1"]["flops"] + work["gemm2"]["flops"] + work["shared"]["flops"]
@@ -471,7 +508,9 @@ def main():
                    "n_shared": cfg.n_shared, "capacity_factor": cfg.alpha,
                    "kept_rows": kept, "experts_touched": touched,
                    "capacity": layer.capacity(n),
-                   "n_rerouted": int(stats["n_rerouted"].item()), "fuse": cfg.fuse},
+                   "n_rerouted": int(stats["n_rerouted"].item()), "fuse": cfg.fuse,
+                   "packed_weights": packed, "packed_kernel": use_packed,
+                   "pack_ms_once": None if pack_ms is None else round(pack_ms, 2)},
         "roofline": kernels[dominant],
         "grouped_gemm_tflops": round(gemm_tflops, 2),
         "grouped_gemm_frac_of_peak": round(gemm_tflops / peak, 4),

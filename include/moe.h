@@ -318,7 +318,34 @@ typedef struct {
   const void* shared_w1;   /* [n_shared][d_ff][d] */
   const void* shared_w3;   /* [n_shared][d_ff][d], SwiGLU only */
   const void* shared_w2;   /* [n_shared][d][d_ff] */
+  /* Optional (bf16 only): the routed experts' w1/w3/w2 as written by moe_pack_weights
+   * from these same w1/w3/w2.  When given, the expert products over long segments read
+   * it instead (same results); w1/w3/w2 stay required for the others. */
+  const void* packed;
 } moe_weights;
+
+/*
+ * moe_pack_weights -- a one-time copy of the routed experts' weights in the order the
+ * matrix cores consume them, for moe_weights.packed.  The operation is a pure
+ * relayout (no arithmetic): the expert FFNs of [Why-MoE] §2.1 / [MoE-2pct] §3.2 compute
+ * the same h and y from it.
+ *   act, n_experts (1 .. MOE_MAX_EXPERTS), d_model, d_ff: as in moe_expert_ffn, bf16
+ *   only (d_model, d_ff multiples of 64).
+ *   w1, w3 (SwiGLU only, else NULL), w2: device, bf16, layouts of moe_weights.
+ *   packed: device, at least moe_packed_weights_size(...) bytes, 16-byte aligned,
+ *   owned by the caller; fully written (padding rows are zero).  Layout: for each
+ *   product (first layer of every expert, then second layer of every expert) the
+ *   weight rows (SwiGLU: 64 rows of W1 then the same 64 of W3, repeated) padded with
+ *   zero rows to a multiple of 512, cut into fragments of 32 rows x 16 reduction
+ *   elements (1 KB each, row-block major, reduction inner); inside a fragment the
+ *   16-byte piece of lane l holds row l % 32, elements 8 (l / 32) .. + 7.
+ * Returns MOE_ERR_INVALID_ARG / MOE_ERR_UNSUPPORTED for bad arguments (nothing is
+ * launched) or MOE_ERR_HIP if the launch fails.  Asynchronous on `stream`.
+ */
+size_t moe_packed_weights_size(moe_act act, int32_t n_experts, int64_t d_model, int64_t d_ff);
+moe_status moe_pack_weights(void* stream, moe_act act, int32_t n_experts, int64_t d_model,
+                            int64_t d_ff, const void* w1, const void* w3, const void* w2,
+                            void* packed);
 
 /* Number of optional stage markers of moe_forward (see moe_stats.stage_events). */
 #define MOE_N_STAGE_EVENTS 7

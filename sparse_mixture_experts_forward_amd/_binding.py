@@ -43,7 +43,8 @@ class MoEConfigC(C.Structure):
 
 class MoEWeightsC(C.Structure):
     _fields_ = [(n, C.c_void_p) for n in ("w_router", "logit_bias", "w1", "w3", "b1", "w2",
-                                          "b2", "shared_w1", "shared_w3", "shared_w2")]
+                                          "b2", "shared_w1", "shared_w3", "shared_w2",
+                                          "packed")]
 
 
 MOE_N_STAGE_EVENTS = 7
@@ -78,6 +79,8 @@ _SIGS = {
     "moe_forward_workspace_size": (_SZ, [C.POINTER(MoEConfigC)]),
     "moe_forward": (C.c_int, [_VP, C.POINTER(MoEConfigC), C.POINTER(MoEWeightsC), _VP, _VP,
                               C.POINTER(MoEStatsC), _VP, _SZ]),
+    "moe_packed_weights_size": (_SZ, [C.c_int, _I32, _I64, _I64]),
+    "moe_pack_weights": (C.c_int, [_VP, C.c_int, _I32, _I64, _I64, _VP, _VP, _VP, _VP]),
     "moe_status_string": (C.c_char_p, [C.c_int]),
     "moe_last_error": (C.c_char_p, []),
 }
@@ -235,6 +238,17 @@ def make_config(n_tokens, d_model, d_ff, n_experts, top_k, act, dtype, capacity_
                       1 if renormalize else 0, 1 if bias_selection_only else 0, act, dtype,
                       float(capacity_factor) if capacity_factor else 0.0, capacity_rule,
                       reroute_rounds, fuse)
+
+
+def moe_packed_weights_size(act: int, n_experts: int, d_model: int, d_ff: int) -> int:
+    return int(lib().moe_packed_weights_size(act, n_experts, d_model, d_ff))
+
+
+def moe_pack_weights(act: int, n_experts: int, d_model: int, d_ff: int, w1, w3, w2, packed,
+                     stream=None):
+    st = lib().moe_pack_weights(_stream(stream), act, n_experts, d_model, d_ff, _ptr(w1),
+                                _ptr(w3), _ptr(w2), _ptr(packed))
+    _check("moe_pack_weights", st)
 
 
 def moe_forward_workspace_size(cfg: MoEConfigC) -> int:

@@ -239,8 +239,9 @@ moe_status run_ffn(hipStream_t st, moe_dtype dt, moe_act act, const void* a, int
                    const std::function<moe_status()>& between = nullptr,
                    const int32_t* a_rows = nullptr, const float* row_scale = nullptr,
                    int split_g = 0, float* split_buf = nullptr, int32_t* split_desc = nullptr,
-                   const int32_t* small_tiles = nullptr) {
+                   const int32_t* small_tiles = nullptr, const void* packed = nullptr) {
   const bool bf = dt == MOE_BF16;
+  const bool sw = act == MOE_ACT_SWIGLU;
   moe::GemmArgs g1{};
   g1.split_g = split_g; g1.split_buf = split_buf; g1.split_desc = split_desc;
   g1.a = a; g1.lda = lda; g1.a_rows = a_rows;
@@ -252,6 +253,11 @@ moe_status run_ffn(hipStream_t st, moe_dtype dt, moe_act act, const void* a, int
   g1.seg_off = seg_off; g1.n_seg = n_seg; g1.single_rows = single_rows;
   g1.n_out = static_cast<int32_t>(d_ff); g1.k = static_cast<int32_t>(d);
   g1.small_tiles = small_tiles;
+  if (packed && bf) {
+    g1.bp = packed;
+    g1.bp_rows = static_cast<int32_t>(moe::packed_rows((sw ? 2 : 1) * d_ff));
+    g1.bp_seg_stride = g1.bp_rows * d * 2;
+  }
   MOE_TRY(hip_check(moe::launch_gemm(st, bf, act == MOE_ACT_SWIGLU ? moe::EPI_SWIGLU : moe::EPI_GELU,
                                      g1, max_rows),
                     "expert GEMM1 launch"));
@@ -267,6 +273,11 @@ moe_status run_ffn(hipStream_t st, moe_dtype dt, moe_act act, const void* a, int
   g2.seg_off = seg_off; g2.n_seg = n_seg; g2.single_rows = single_rows;
   g2.n_out = static_cast<int32_t>(d); g2.k = static_cast<int32_t>(d_ff);
   g2.small_tiles = small_tiles;
+  if (packed && bf) {
+    g2.bp = static_cast<const char*>(packed) + n_seg * moe::packed_w1_bytes(sw, d, d_ff);
+    g2.bp_rows = static_cast<int32_t>(moe::packed_rows(d));
+    g2.bp_seg_stride = g2.bp_rows * d_ff * 2;
+  }
   return hip_check(moe::launch_gemm(st, bf, moe::EPI_NONE, g2, max_rows), "expert GEMM2 launch");
 }
 
@@ -618,6 +629,32 @@ moe_status moe_combine(void* stream, moe_dtype dtype, const void* y_rows,
                    "combine launch");
 }
 
+size_t moe_packed_weights_size(moe_act act, int32_t n_experts, int64_t d_model, int64_t d_ff) {
+  if (check_ffn_shape(MOE_BF16, act, d_model, d_ff) != MOE_OK) return 0;
+  if (n_experts < 1 || n_experts > MOE_MAX_EXPERTS) return 0;
+  return static_cast<size_t>(n_experts) *
+         static_cast<size_t>(moe::packed_w1_bytes(act == MOE_ACT_SWIGLU, d_model, d_ff) +
+                             moe::packed_w2_bytes(d_model, d_ff));
+}
+
+moe_status moe_pack_weights(void* stream, moe_act act, int32_t n_experts, int64_t d_model,
+                            int64_t d_ff, const void* w1, const void* w3, const void* w2,
+                            void* packed) {
+  MOE_TRY(check_ffn_shape(MOE_BF16, act, d_model, d_ff));
+  if (n_experts < 1) return fail(MOE_ERR_INVALID_ARG, "n_experts < 1");
+  if (n_experts > MOE_MAX_EXPERTS) return fail(MOE_ERR_UNSUPPORTED, "n_experts > %d", MOE_MAX_EXPERTS);
+  const bool sw = act == MOE_ACT_SWIGLU;
+  if (!w1 || !w2 || !packed || (sw && !w3))
+    return fail(MOE_ERR_INVALID_ARG, "w1, w2, packed (and w3 for SwiGLU) are required");
+  MOE_TRY(check_aligned(w1, 16, "w1"));
+  MOE_TRY(check_aligned(w2, 16, "w2"));
+  if (sw) MOE_TRY(check_aligned(w3, 16, "w3"));
+  MOE_TRY(check_aligned(packed, 16, "packed"));
+  return hip_check(moe::launch_pack_weights(static_cast<hipStream_t>(stream), sw, n_experts,
+                                            d_model, d_ff, w1, sw ? w3 : nullptr, w2, packed),
+                   "weight packing launch");
+}
+
 size_t moe_forward_workspace_size(const moe_config* cfg) {
   if (check_config(cfg) != MOE_OK) return 0;
   return forward_layout(*cfg, nullptr).used;
@@ -644,7 +681,10 @@ moe_status moe_forward(void* stream, const moe_config* cfg, const moe_weights* w
     MOE_TRY(check_aligned(x, 16, "x"));
     MOE_TRY(check_aligned(y, 16, "y"));
   }
-  const void* wptrs[] = {w->w1, w->w2, w->w3, w->shared_w1, w->shared_w2, w->shared_w3};
+  if (w->packed && c.dtype != MOE_BF16)
+    return fail(MOE_ERR_UNSUPPORTED, "packed weights are bf16 only");
+  const void* wptrs[] = {w->w1, w->w2, w->w3, w->shared_w1, w->shared_w2, w->shared_w3,
+                         w->packed};
   for (const void* p : wptrs)
     if (p) MOE_TRY(check_aligned(p, 16, "expert weights"));
 
@@ -718,7 +758,7 @@ moe_status moe_forward(void* stream, const moe_config* cfg, const moe_weights* w
                   L.split_buf, L.split_desc,
                   // with a capacity the kept rows are known only on the device, which
                   // then picks the tile height
-                  cap >= 0 ? L.small_tiles : nullptr));
+                  cap >= 0 ? L.small_tiles : nullptr, w->packed));
   MOE_TRY(mark(4));
   // join: the combine needs the shared experts' output
   if (side) MOE_TRY(hip_check(hipStreamWaitEvent(st, side->join, 0), "join wait"));

@@ -873,6 +873,425 @@ __global__ __launch_bounds__(kWave) void gemm_split_finish_kernel(GemmArgs g) {
   else by_tm(std::integral_constant<int, 1>{});
 }
 
+// ------------------------------------------------------------------ packed-weight kernel
+// For long segments the weights are read from a packed copy (launch_pack_weights) laid
+// out in the order the matrix cores take them: a fragment of 32 weight rows x 16 k is
+// 1 KB, lane l holding row l % 32, k 8 (l / 32) .. + 8 as one 16-byte piece, so a wave
+// moves a fragment from memory into registers with one fully coalesced load.  Only the
+// activations pass through LDS:
+//   * tile 128 activation rows x 512 weight rows; each of the 4 waves multiplies all
+//     128 rows by a 128-row weight panel of its own (64 W1 + the same 64 W3 rows for
+//     SwiGLU), so no weight fragment is needed by two waves.  Per 64-deep stage the LDS
+//     then carries 16 KB of writes and 64 KB of fragment reads, against 64 KB and 128 KB
+//     when both operands are staged (those reads are the largest in-core cost of the
+//     staged kernel);
+//   * weights: a register ring of 8 k-steps of fragments, each loaded 7 k-steps ahead;
+//   * activations: 4 LDS stages of 128 rows x 64 k, filled by direct-to-LDS buffer
+//     loads 4 stages ahead, one barrier per stage (before its last k-step's MFMAs);
+//   * row blocks past a tile's last row skip their MFMAs (TA = active blocks);
+//   * same scheduling, epilogues and gather as the staged kernel.
+constexpr int kPBM = 128;      // activation rows per tile
+constexpr int kPBN = 512;      // weight rows per tile
+constexpr int kPStages = 4;    // activation LDS stages
+constexpr int kPRing = 8;      // weight register ring, in k-steps of 16
+constexpr int kPLead = kPRing - 1;
+constexpr int kPLoadsA = 4;    // activation loads (8 rows x 128 bytes) per wave per stage
+// Stage boundary of stage s: this wave's activation loads of stage s + 1 must have
+// landed.  Loads complete in order, and issued after those are at least the activation
+// loads of two later stages and the weight loads of ten k-steps (fewest at the first
+// boundary: A1 is followed by A2, A3, the 7 lead k-steps and k-steps 0..2), so waiting
+// until at most that many loads are outstanding suffices everywhere.
+constexpr int kPBoundaryWait = (kPStages - 2) * kPLoadsA + 4 * (kPLead + 3);
+static_assert(kPBoundaryWait < 64, "vmcnt range");
+
+struct PackedIO {
+  const char* a_base;  // uniform: the tile's activation rows (or a, with a gather)
+  uint32_t a_off[kPLoadsA];
+  const char* w_base;  // uniform: this wave's weight panel
+  uint32_t w_off[4];   // row block tn of the panel + this lane's 16 bytes
+  int a_row;
+  int co[4];           // swizzled element offset of this lane's chunk per k-step
+  int KT, KS;          // stages and k-steps of the reduction
+  int wave;
+
+  // activation stage `stage` (clamped to the last) into buf: this wave fills the 32 rows
+  // of row block `wave`, 8 rows x 128 bytes per instruction
+  __device__ __forceinline__ void dma_a(uint16_t* buf, int stage) const {
+#if defined(__HIP_DEVICE_COMPILE__)
+    const int st = min(stage, KT - 1);
+    const __amdgpu_buffer_rsrc_t r = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<char*>(a_base + st * kBK * 2), static_cast<short>(0), -1, 0x00020000);
+#pragma unroll
+    for (int j = 0; j < kPLoadsA; ++j)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(
+          r, (lds_void_t*)(buf + (wave * kPLoadsA + j) * 8 * kBK), 16, a_off[j], 0, 0, 0);
+#endif
+  }
+  // weight fragments of k-step ks (clamped to the last) of the panel's 4 row blocks
+  __device__ __forceinline__ void load_w(bf16x8_t (&w)[4], int ks) const {
+#if defined(__HIP_DEVICE_COMPILE__)
+    const int t = min(ks, KS - 1);
+    const __amdgpu_buffer_rsrc_t r = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<char*>(w_base), static_cast<short>(0), -1, 0x00020000);
+#pragma unroll
+    for (int tn = 0; tn < 4; ++tn)
+      w[tn] = __builtin_bit_cast(bf16x8_t,
+                                 __builtin_amdgcn_raw_buffer_load_b128(r, w_off[tn], t * 1024, 0));
+#endif
+  }
+  template <int TA>
+  __device__ __forceinline__ void read_a(const uint16_t* buf, int kstep, bf16x8_t (&a)[4]) const {
+#pragma unroll
+    for (int tm = 0; tm < TA; ++tm)
+      a[tm] = *reinterpret_cast<const bf16x8_t*>(&buf[a_row + tm * 32 * kBK + co[kstep]]);
+  }
+};
+
+// K-step t, at position T of the 16-k-step period of both rings (activation stage
+// T / 4 % 4, weight slot T % 8).  The fragments of this k-step are in af[T & 1] and
+// wr[T % 8]; the next k-step's activation fragments are read into af[(T + 1) & 1] and
+// the weights of k-step t + 7 loaded into the slot this k-step's predecessor freed.
+template <int T, int TA>
+__device__ __forceinline__ void pk_step(const PackedIO& io, uint16_t* const (&A)[kPStages], int t,
+                                        bf16x8_t (&wr)[kPRing][4], bf16x8_t (&af)[2][4],
+                                        f32x16_t (&acc)[4][4]) {
+  constexpr int J = T % 4, SB = T / 4;
+  if constexpr (J == 3) {
+    // every wave has read its fragments of this stage: its buffer takes stage s + 4
+    barrier_keep_loads<kPBoundaryWait>();
+    io.dma_a(A[SB], t / 4 + kPStages);
+  }
+  io.load_w(wr[(T + kPLead) % kPRing], t + kPLead);
+  io.template read_a<TA>(A[J == 3 ? (SB + 1) % kPStages : SB], (J + 1) % 4, af[(T + 1) & 1]);
+#pragma unroll
+  for (int tn = 0; tn < 4; ++tn)
+#pragma unroll
+    for (int tm = 0; tm < TA; ++tm)
+      acc[tn][tm] = Mfma<32>::mma(wr[T % kPRing][tn], af[T & 1][tm], acc[tn][tm]);
+  sched_mix<4 + (J == 3 ? kPLoadsA : 0), TA, 4 * TA, 0, 8>();
+}
+
+template <int T, int TA>
+__device__ __forceinline__ void pk_period(const PackedIO& io, uint16_t* const (&A)[kPStages],
+                                          int t0, bf16x8_t (&wr)[kPRing][4],
+                                          bf16x8_t (&af)[2][4], f32x16_t (&acc)[4][4]) {
+  if constexpr (T < 16) {
+    pk_step<T, TA>(io, A, t0 + T, wr, af, acc);
+    pk_period<T + 1, TA>(io, A, t0, wr, af, acc);
+  }
+}
+
+// The last rem (< 16, a multiple of 4) k-steps.
+template <int T, int TA>
+__device__ __forceinline__ void pk_tail(const PackedIO& io, uint16_t* const (&A)[kPStages], int t0,
+                                        int rem, bf16x8_t (&wr)[kPRing][4], bf16x8_t (&af)[2][4],
+                                        f32x16_t (&acc)[4][4]) {
+  if constexpr (T < 16) {
+    if (T < rem) {
+      pk_step<T, TA>(io, A, t0 + T, wr, af, acc);
+      pk_tail<T + 1, TA>(io, A, t0, rem, wr, af, acc);
+    }
+  }
+}
+
+// Epilogue: register 4q + r of acc[tn][tm] is activation row tm*32 + lane%32 of the
+// tile and packed weight row tn*32 + 8q + 4(lane/32) + r of the wave's panel p; the
+// four r are consecutive output columns (one 8-byte store).
+// TN0 .. TN1-1 restrict the epilogue to those weight tiles (SwiGLU: of the W1 tiles
+// 0, 1, each with its W3 tile tn + 2); default all.
+template <int EPI, int TA, int TN0 = 0, int TN1 = (EPI == EPI_SWIGLU ? 2 : 4)>
+__device__ __forceinline__ void packed_epilogue(const GemmArgs& g, const Tile& tile, int lane,
+                                                int p, f32x16_t (&acc)[4][4]) {
+  uint16_t* __restrict__ C = static_cast<uint16_t*>(g.c);
+  const int frow = lane & 31;
+  if constexpr (EPI == EPI_SWIGLU) {
+#pragma unroll
+    for (int tn = TN0; tn < TN1; ++tn)
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const int col = p * 64 + tn * 32 + Mfma<32>::ni(q, lane);
+        if (col >= g.n_out) continue;
+#pragma unroll
+        for (int tm = 0; tm < TA; ++tm) {
+          const int m = tm * 32 + frow;
+          if (m < tile.m_valid) {
+            float v[4];
+#pragma unroll
+            for (int r = 0; r < 4; ++r)
+              v[r] = silu(acc[tn][tm][4 * q + r]) * acc[tn + 2][tm][4 * q + r];
+            *reinterpret_cast<uint2*>(C + (tile.row0 + m) * g.ldc + col) =
+                pack_bf16x4(v[0], v[1], v[2], v[3]);
+          }
+        }
+      }
+  } else {
+    const uint16_t* bias = static_cast<const uint16_t*>(g.bias);
+    float sc[TA];
+#pragma unroll
+    for (int tm = 0; tm < TA; ++tm) {
+      const int m = tm * 32 + frow;
+      sc[tm] = (g.row_scale && m < tile.m_valid) ? g.row_scale[tile.row0 + m] : 1.f;
+    }
+#pragma unroll
+    for (int tn = TN0; tn < TN1; ++tn)
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const int col = p * 128 + tn * 32 + Mfma<32>::ni(q, lane);
+        if (col >= g.n_out) continue;
+        float bv[4] = {0.f, 0.f, 0.f, 0.f};
+        if (bias != nullptr) {
+#pragma unroll
+          for (int r = 0; r < 4; ++r) bv[r] = bf16_to_f32(bias[tile.seg * g.bias_seg_stride + col + r]);
+        }
+#pragma unroll
+        for (int tm = 0; tm < TA; ++tm) {
+          const int m = tm * 32 + frow;
+          if (m < tile.m_valid) {
+            float v[4];
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+              v[r] = acc[tn][tm][4 * q + r] + bv[r];
+              if (EPI == EPI_GELU) v[r] = gelu_erf(v[r]);
+              v[r] *= sc[tm];  // exact when 1
+            }
+            *reinterpret_cast<uint2*>(C + (tile.row0 + m) * g.ldc + col) =
+                pack_bf16x4(v[0], v[1], v[2], v[3]);
+          }
+        }
+      }
+  }
+}
+
+// Partial accumulators of a split packed tile (a slot of gemm_split_floats' 65536
+// floats per part): float4 chunk c of thread t at [c][t], c = (tn*4 + tm)*4 + v.
+__device__ __forceinline__ int pk_chunk(int tn, int tm, int v) { return (tn * 4 + tm) * 4 + v; }
+__device__ __forceinline__ f32x4_t* pk_slot(float* buf, int slot) {
+  return reinterpret_cast<f32x4_t*>(buf + static_cast<int64_t>(slot) * kPBM * kPBN);
+}
+
+template <int TA>
+__device__ __forceinline__ void packed_split_store(const GemmArgs& g, const Tile& tile,
+                                                   f32x16_t (&acc)[4][4]) {
+  const int tid = threadIdx.x;
+  f32x4_t* mine = pk_slot(g.split_buf, tile.split_q * tile.nparts + tile.part);
+#pragma unroll
+  for (int tn = 0; tn < 4; ++tn)
+#pragma unroll
+    for (int tm = 0; tm < TA; ++tm)
+#pragma unroll
+      for (int v = 0; v < 4; ++v) {
+        f32x4_t q;
+#pragma unroll
+        for (int r = 0; r < 4; ++r) q[r] = acc[tn][tm][4 * v + r];
+        mine[pk_chunk(tn, tm, v) * kThreads + tid] = q;
+      }
+  if (tile.part == 0 && tid == 0) {
+    int32_t* d = g.split_desc + 1 + 5 * tile.split_q;
+    d[0] = tile.seg;
+    d[1] = static_cast<int32_t>(tile.row0);
+    d[2] = tile.m_valid;
+    d[3] = tile.nt;
+    d[4] = tile.nparts;
+  }
+}
+
+// K loop and epilogue (or, for a part of a split tile, the store of its partial sums) of
+// a tile whose rows fill TA row blocks of 32.
+template <int EPI, int TA>
+__device__ __forceinline__ void packed_body(const GemmArgs& g, const Tile& tile, const PackedIO& io,
+                                            uint16_t* const (&A)[kPStages], int lane, int p) {
+  f32x16_t acc[4][4];
+#pragma unroll
+  for (int tn = 0; tn < 4; ++tn)
+#pragma unroll
+    for (int tm = 0; tm < TA; ++tm)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) acc[tn][tm][r] = 0.f;
+  bf16x8_t wr[kPRing][4];
+  bf16x8_t af[2][4];
+  // prologue: activation stages 0..3, then weight k-steps 0..6 in order (kept in order,
+  // so that the loop's waits for each slot are the same on entry as on every turn)
+#pragma unroll
+  for (int st = 0; st < kPStages; ++st) io.dma_a(A[st], st);
+#pragma unroll
+  for (int t = 0; t < kPLead; ++t) {
+    io.load_w(wr[t], t);
+    __builtin_amdgcn_sched_barrier(0);
+  }
+  barrier_keep_loads<(kPStages - 1) * kPLoadsA + 4 * kPLead>();
+  io.template read_a<TA>(A[0], 0, af[0]);
+  int t0 = 0;
+  for (; t0 + 16 <= io.KS; t0 += 16) pk_period<0, TA>(io, A, t0, wr, af, acc);
+  pk_tail<0, TA>(io, A, t0, io.KS - t0, wr, af, acc);
+  // no load may still be writing this workgroup's LDS when it exits
+  __builtin_amdgcn_s_waitcnt(0);
+  if (tile.nparts > 1) {
+    packed_split_store<TA>(g, tile, acc);
+    return;
+  }
+  packed_epilogue<EPI, TA>(g, tile, lane, p, acc);
+}
+
+template <int EPI>
+__global__ __launch_bounds__(kThreads, 1) void gemm_packed_kernel(GemmArgs g) {
+  __shared__ __attribute__((aligned(16))) uint16_t A0[kPBM * kBK], A1[kPBM * kBK];
+  __shared__ __attribute__((aligned(16))) uint16_t A2[kPBM * kBK], A3[kPBM * kBK];
+  __shared__ SchedSmem sched;
+  uint16_t* const A[kPStages] = {A0, A1, A2, A3};
+  // the launch stands for the 256-row tiles: it does nothing where the dispatch chose
+  // the 32-row ones
+  if (g.small_tiles && *g.small_tiles != 0) return;
+  Tile tile;
+  if (!schedule_tile<kPBM>(g.seg_off, g.n_seg, g.single_rows, g.max_rows, g.bp_rows / kPBN,
+                           g.k / kBK, g.split_g, g.split_desc, sched, tile))
+    return;
+  // the work item is uniform over the workgroup: keep its fields in scalar registers
+  tile.k_stage0 = __builtin_amdgcn_readfirstlane(tile.k_stage0);
+  tile.k_stages = __builtin_amdgcn_readfirstlane(tile.k_stages);
+  tile.nparts = __builtin_amdgcn_readfirstlane(tile.nparts);
+  const int tid = threadIdx.x;
+  const int lane = tid & (kWave - 1);
+  const int wave = __builtin_amdgcn_readfirstlane(tid / kWave);
+  PackedIO io;
+  io.wave = wave;
+  io.KT = tile.k_stages;  // a part of a split tile covers stages k_stage0 .. + k_stages
+  io.KS = 4 * tile.k_stages;
+  const int32_t* __restrict__ a_rows = g.a_rows;
+  io.a_base = uniform_ptr(reinterpret_cast<const char*>(
+      static_cast<const uint16_t*>(g.a) + (a_rows ? 0 : tile.row0 * g.lda) +
+      static_cast<int64_t>(tile.k_stage0) * kBK));
+#pragma unroll
+  for (int j = 0; j < kPLoadsA; ++j) {
+    const int i = 8 * (wave * kPLoadsA + j) + (lane >> 3);  // LDS row of the tile
+    const int r = min(i, tile.m_valid - 1);  // rows past the segment repeat its last row
+    const uint32_t src = a_rows ? static_cast<uint32_t>(a_rows[tile.row0 + r]) : r;
+    const int chunk = ((lane & 7) ^ lds_swizzle(i)) * 8;
+    io.a_off[j] = (src * static_cast<uint32_t>(g.lda) + chunk) * 2u;
+  }
+  const int p = tile.nt * 4 + wave;  // this wave's 128-row weight panel
+  io.w_base = uniform_ptr(static_cast<const char*>(g.bp) + tile.seg * g.bp_seg_stride +
+                          static_cast<int64_t>(p) * 128 * g.k * 2 +
+                          static_cast<int64_t>(tile.k_stage0) * 4 * 1024);
+#pragma unroll
+  for (int tn = 0; tn < 4; ++tn)
+    io.w_off[tn] = static_cast<uint32_t>(tn) * static_cast<uint32_t>(g.k) * 64u +
+                   static_cast<uint32_t>(lane) * 16u;
+  const int frow = lane & 31;
+#pragma unroll
+  for (int ks = 0; ks < 4; ++ks) io.co[ks] = (Mfma<32>::chunk(lane, ks) ^ lds_swizzle(frow)) * 8;
+  io.a_row = frow * kBK;
+  const int ta = __builtin_amdgcn_readfirstlane(min((tile.m_valid + 31) / 32, 4));
+  if (ta >= 4)
+    packed_body<EPI, 4>(g, tile, io, A, lane, p);
+  else if (ta == 3)
+    packed_body<EPI, 3>(g, tile, io, A, lane, p);
+  else if (ta == 2)
+    packed_body<EPI, 2>(g, tile, io, A, lane, p);
+  else
+    packed_body<EPI, 1>(g, tile, io, A, lane, p);
+}
+
+// Finishes the split tiles of the preceding gemm_packed_kernel launch: one single-wave
+// workgroup per (split tile, wave of the tile, half h of that wave's output tiles) sums
+// its accumulators over the parts in part order and runs its share of the epilogue
+// (SwiGLU: W1 tile h with W3 tile h + 2; otherwise tiles 2h, 2h + 1).
+template <int EPI, int TA, int H>
+__device__ __forceinline__ void packed_finish(const GemmArgs& g, const Tile& tile, int q, int tid,
+                                              int lane, int p) {
+  constexpr int TNA = EPI == EPI_SWIGLU ? H : 2 * H;
+  constexpr int TNB = EPI == EPI_SWIGLU ? H + 2 : 2 * H + 1;
+  f32x16_t acc[4][4];
+  for (int part = 0; part < tile.nparts; ++part) {
+    const f32x4_t* sp = pk_slot(g.split_buf, q * tile.nparts + part);
+#pragma unroll
+    for (int tm = 0; tm < TA; ++tm)
+#pragma unroll
+      for (int v = 0; v < 4; ++v) {
+        const f32x4_t xa = sp[pk_chunk(TNA, tm, v) * kThreads + tid];
+        const f32x4_t xb = sp[pk_chunk(TNB, tm, v) * kThreads + tid];
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          acc[TNA][tm][4 * v + r] = part == 0 ? xa[r] : acc[TNA][tm][4 * v + r] + xa[r];
+          acc[TNB][tm][4 * v + r] = part == 0 ? xb[r] : acc[TNB][tm][4 * v + r] + xb[r];
+        }
+      }
+  }
+  if constexpr (EPI == EPI_SWIGLU)
+    packed_epilogue<EPI, TA, H, H + 1>(g, tile, lane, p, acc);
+  else
+    packed_epilogue<EPI, TA, 2 * H, 2 * H + 2>(g, tile, lane, p, acc);
+}
+
+template <int EPI>
+__global__ __launch_bounds__(kWave) void gemm_packed_finish_kernel(GemmArgs g) {
+  const int q = blockIdx.x / 8, wave = (blockIdx.x / 2) % 4, h = blockIdx.x % 2;
+  // (the product launch it finishes did nothing: its split descriptors are stale)
+  if (g.small_tiles && *g.small_tiles != 0) return;
+  if (q >= g.split_desc[0]) return;
+  const int32_t* d = g.split_desc + 1 + 5 * q;
+  Tile tile;
+  tile.seg = d[0];
+  tile.row0 = d[1];
+  tile.m_valid = d[2];
+  tile.nt = d[3];
+  tile.nparts = __builtin_amdgcn_readfirstlane(d[4]);
+  tile.part = 0;
+  tile.split_q = q;
+  tile.k_stage0 = 0;
+  tile.k_stages = 0;
+  const int lane = threadIdx.x;
+  const int tid = wave * kWave + lane;  // the thread of the tile's workgroup this lane stands for
+  const int p = tile.nt * 4 + wave;
+  const int ta = __builtin_amdgcn_readfirstlane(min((tile.m_valid + 31) / 32, 4));
+  auto run = [&](auto h_c) {
+    constexpr int H = decltype(h_c)::value;
+    if (ta >= 4) packed_finish<EPI, 4, H>(g, tile, q, tid, lane, p);
+    else if (ta == 3) packed_finish<EPI, 3, H>(g, tile, q, tid, lane, p);
+    else if (ta == 2) packed_finish<EPI, 2, H>(g, tile, q, tid, lane, p);
+    else packed_finish<EPI, 1, H>(g, tile, q, tid, lane, p);
+  };
+  if (h == 0) run(std::integral_constant<int, 0>{});
+  else run(std::integral_constant<int, 1>{});
+}
+
+// Writes the packed copy of E experts' weights: one thread per 16-byte piece of the
+// output (first-layer products of all experts, then second-layer ones), zeros for the
+// padding rows.  Piece i of an expert's product with reduction K is lane i % 64 of
+// fragment i / 64 = (row block rb, k-step kb), rb = fragment / (K/16).
+__global__ __launch_bounds__(256) void pack_weights_kernel(
+    const uint16_t* __restrict__ w1, const uint16_t* __restrict__ w3,
+    const uint16_t* __restrict__ w2, u32x4_t* __restrict__ packed, int e, int64_t d,
+    int64_t d_ff, int swiglu, int64_t rows1, int64_t rows2) {
+  const int64_t per1 = rows1 * d / 8, per2 = rows2 * d_ff / 8;
+  const int64_t i = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x;
+  if (i >= e * (per1 + per2)) return;
+  const bool first = i < e * per1;
+  const int64_t K = first ? d : d_ff;
+  const int64_t per = first ? per1 : per2;
+  const int64_t j = first ? i : i - e * per1;
+  const int64_t ex = j / per, rem = j - ex * per;
+  const int64_t frag = rem / 64;
+  const int lane = static_cast<int>(rem % 64);
+  const int64_t rb = frag / (K / 16), kb = frag % (K / 16);
+  const int64_t n = rb * 32 + (lane & 31);
+  const int64_t k = kb * 16 + 8 * (lane >> 5);
+  const uint16_t* src = nullptr;
+  if (first) {
+    if (swiglu) {
+      const int64_t pnl = n / 128, w = n % 128, row = pnl * 64 + (w & 63);
+      if (row < d_ff) src = (w < 64 ? w1 : w3) + (ex * d_ff + row) * d + k;
+    } else if (n < d_ff) {
+      src = w1 + (ex * d_ff + n) * d + k;
+    }
+  } else if (n < d) {
+    src = w2 + (ex * d + n) * d_ff + k;
+  }
+  u32x4_t v = {0u, 0u, 0u, 0u};
+  if (src) v = *reinterpret_cast<const u32x4_t*>(src);
+  packed[i] = v;
+}
+
+
 // ------------------------------------------------------------------ float32 SIMT kernel
 constexpr int kFBM = 64, kFBN = 64, kFBK = 16, kFPad = 4;
 
@@ -970,6 +1389,24 @@ int64_t grid_for(int64_t max_rows, int n_seg_eff, int bm, int n_ntiles) {
   return ((t + kXcds - 1) / kXcds) * kXcds;
 }
 
+template <int EPI>
+hipError_t launch_packed(hipStream_t st, GemmArgs g, int64_t max_rows) {
+  const int n_seg_eff = g.seg_off ? g.n_seg : 1;
+  int64_t grid = grid_for(max_rows, n_seg_eff, kPBM, g.bp_rows / kPBN);
+  if (grid <= 0) return hipSuccess;
+  // a partial last round is split along K as in the staged kernel (same rule, same
+  // buffers: a 128 x 512 tile holds as many floats as a 256 x 256 one)
+  if (!g.split_buf || !g.split_desc || grid > 5 * static_cast<int64_t>(g.split_g)) g.split_g = 0;
+  grid += g.split_g;
+  hipLaunchKernelGGL((gemm_packed_kernel<EPI>), dim3(static_cast<unsigned>(grid)), dim3(kThreads),
+                     0, st, g);
+  hipError_t err = hipGetLastError();
+  if (err != hipSuccess || g.split_g == 0) return err;
+  hipLaunchKernelGGL((gemm_packed_finish_kernel<EPI>), dim3(static_cast<unsigned>(g.split_g / 2 * 8)),
+                     dim3(kWave), 0, st, g);
+  return hipGetLastError();
+}
+
 template <int BM, int EPI>
 hipError_t launch_bf16_bm(hipStream_t st, GemmArgs g, int64_t max_rows, bool ksplit) {
   const int n_ntiles = (EPI == EPI_SWIGLU) ? (g.n_out + 127) / 128 : (g.n_out + 255) / 256;
@@ -1020,7 +1457,11 @@ hipError_t launch_bf16_epi(hipStream_t st, const GemmArgs& g, int64_t max_rows) 
   }
   GemmArgs big = g;
   if (ksplit || !g.split_buf || !g.split_desc) big.split_g = 0;
-  const hipError_t err = launch_bf16_bm<256, EPI>(st, big, max_rows, ksplit);
+  // long segments with packed weights: the packed-weight kernel in place of the
+  // 256-row tiles
+  const bool packed = g.bp != nullptr && !ksplit && avg >= kPackedRows;
+  const hipError_t err = packed ? launch_packed<EPI>(st, g, max_rows)
+                                : launch_bf16_bm<256, EPI>(st, big, max_rows, ksplit);
   if (err != hipSuccess || !g.small_tiles) return err;
   // selected, the kept rows average under kBigSegRows per non-empty segment, so the
   // 32-row tiles number at most 2.5 per segment and column tile
@@ -1045,6 +1486,18 @@ hipError_t launch_f32_epi(hipStream_t st, const GemmArgs& g, int64_t max_rows) {
 }
 
 }  // namespace
+
+hipError_t launch_pack_weights(hipStream_t st, bool swiglu, int e, int64_t d, int64_t d_ff,
+                               const void* w1, const void* w3, const void* w2, void* packed) {
+  const int64_t rows1 = packed_rows((swiglu ? 2 : 1) * d_ff), rows2 = packed_rows(d);
+  const int64_t pieces = e * (rows1 * d + rows2 * d_ff) / 8;
+  if (pieces <= 0) return hipSuccess;
+  hipLaunchKernelGGL(pack_weights_kernel, dim3(static_cast<unsigned>((pieces + 255) / 256)),
+                     dim3(256), 0, st, static_cast<const uint16_t*>(w1),
+                     static_cast<const uint16_t*>(w3), static_cast<const uint16_t*>(w2),
+                     static_cast<u32x4_t*>(packed), e, d, d_ff, swiglu ? 1 : 0, rows1, rows2);
+  return hipGetLastError();
+}
 
 hipError_t launch_gemm(hipStream_t st, bool bf16, Epilogue epi, const GemmArgs& g_in,
                        int64_t max_rows) {

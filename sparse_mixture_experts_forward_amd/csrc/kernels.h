@@ -148,7 +148,30 @@ struct GemmArgs {
   // limit), both tile heights are launched and each launch's workgroups exit at once
   // unless *small_tiles (written by the dispatch) selects it.
   const int32_t* small_tiles;
+  // Packed weights (or null) of the launch's product, written by launch_pack_weights:
+  // where set and the segments are long (kPackedRows), the packed-weight kernel runs
+  // instead of the 256-row tiles.  bp_rows packed rows per segment (a multiple of 512),
+  // bp_seg_stride bytes between segments.
+  const void* bp;
+  int64_t bp_seg_stride;
+  int32_t bp_rows;
 };
+
+// Segments averaging at least this many rows (by the host's bound) take the
+// packed-weight kernel when packed weights are given.
+constexpr int kPackedRows = 256;
+
+// Packed layout of one expert's weights (bf16): rows of the product padded to a
+// multiple of 512, in fragments of 32 rows x 16 k (1 KB, row-block major, k inner).
+// First layer: SwiGLU interleaves 64 rows of W1 and the same 64 rows of W3 per 128
+// packed rows; GELU takes W1 as is.  Second layer: W2.
+inline int64_t packed_rows(int64_t rows) { return (rows + 511) / 512 * 512; }
+inline int64_t packed_w1_bytes(bool swiglu, int64_t d, int64_t d_ff) {
+  return packed_rows((swiglu ? 2 : 1) * d_ff) * d * 2;
+}
+inline int64_t packed_w2_bytes(int64_t d, int64_t d_ff) { return packed_rows(d) * d_ff * 2; }
+hipError_t launch_pack_weights(hipStream_t st, bool swiglu, int e, int64_t d, int64_t d_ff,
+                               const void* w1, const void* w3, const void* w2, void* packed);
 
 // Sizes of the split buffers for g resident workgroups.
 inline int64_t gemm_split_floats(int g) { return static_cast<int64_t>(g) * 256 * 256; }

@@ -45,6 +45,23 @@ class MoELayer:
                  shared_w2=inp.sw2)
         return cls(inp.cfg, w)
 
+    def pack_weights(self, stream=None) -> torch.Tensor:
+        """Writes the packed copy of the routed experts' weights (bf16 only) that the
+        expert products over long segments then read; returns it (also kept in the
+        layer's weights as "packed").  Call again after changing w1/w3/w2."""
+        c = self.cfg
+        if c.dtype != "bf16":
+            raise ValueError("packed weights are bf16 only")
+        act = _act(c.act)
+        nbytes = B.moe_packed_weights_size(act, c.n_experts, c.d_model, c.d_ff)
+        if nbytes <= 0:
+            raise ValueError("unsupported shape for packed weights")
+        packed = torch.empty(nbytes // 2, dtype=torch.bfloat16, device=self.device)
+        B.moe_pack_weights(act, c.n_experts, c.d_model, c.d_ff, self.w["w1"], self.w.get("w3"),
+                           self.w["w2"], packed, stream=stream)
+        self.w["packed"] = packed
+        return packed
+
     def config_c(self, n_tokens: int) -> B.MoEConfigC:
         c = self.cfg
         return B.make_config(n_tokens, c.d_model, c.d_ff, c.n_experts, c.top_k, _act(c.act),

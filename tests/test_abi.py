@@ -181,3 +181,30 @@ def test_fused_forward_workspace():
     assert plain - gather >= 8192 * 4096 * 2  # no permuted copy of x
     assert both - gather >= 8192 * 4  # one weight per row
     assert B.moe_forward_workspace_size(B.make_config(**kw, fuse=4)) == 0
+
+
+def test_packed_weights_size_and_validation():
+    L = B.lib()
+    sw, ge = B.MOE_ACT_SWIGLU, B.MOE_ACT_GELU
+    # rows of each product padded to a multiple of 512, two bytes per element
+    assert B.moe_packed_weights_size(sw, 8, 4096, 14336) == 8 * (28672 * 4096 + 4096 * 14336) * 2
+    assert B.moe_packed_weights_size(ge, 3, 768, 1344) == 3 * (1536 * 768 + 1024 * 1344) * 2
+    assert B.moe_packed_weights_size(sw, 2, 64, 64) == 2 * (512 * 64 + 512 * 64) * 2
+    assert B.moe_packed_weights_size(sw, 8, 100, 14336) == 0
+    assert B.moe_packed_weights_size(sw, 0, 4096, 14336) == 0
+    assert B.moe_packed_weights_size(sw, B.MOE_MAX_EXPERTS + 1, 64, 64) == 0
+    fake = 4096  # never dereferenced: validation fails first
+    pack = lambda *a: L.moe_pack_weights(None, *a)
+    assert pack(sw, 8, 4096, 14336, fake, None, fake, fake) == B.MOE_ERR_INVALID_ARG  # no w3
+    assert pack(ge, 8, 4096, 14336, fake, None, fake, None) == B.MOE_ERR_INVALID_ARG  # no output
+    assert pack(ge, 0, 4096, 14336, fake, None, fake, fake) == B.MOE_ERR_INVALID_ARG
+    assert pack(ge, 8, 4000, 14336, fake, None, fake, fake) == B.MOE_ERR_UNSUPPORTED
+    assert pack(ge, 8, 4096, 14336, fake + 2, None, fake, fake) == B.MOE_ERR_INVALID_ARG  # alignment
+    assert "w1" in L.moe_last_error().decode()
+    # packed weights with float32 layers are refused before anything runs
+    cfg = B.make_config(64, 64, 64, 4, 2, B.MOE_ACT_GELU, B.MOE_F32)
+    w = B.MoEWeightsC(w_router=fake, w1=fake, w2=fake, packed=fake)
+    ws = B.moe_forward_workspace_size(cfg)
+    st = L.moe_forward(None, C.byref(cfg), C.byref(w), fake, fake * 2, None, fake, ws)
+    assert st == B.MOE_ERR_UNSUPPORTED
+    assert "packed" in L.moe_last_error().decode()

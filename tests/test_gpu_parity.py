@@ -515,11 +515,14 @@ def test_combine_parity(dtype, shared, k, d, weights):
 
 
 # ------------------------------------------------------------------ whole layer
-def _forward_and_oracle(cfg, tokens=None, check_all_logits=True):
-    """Forward on the GPU; the oracle conditioned on its logits; integer results
-    compared bit for bit, weights and statistics within float32 tolerance."""
+def _forward_and_oracle(cfg, tokens=None, check_all_logits=True, packed=False):
+    """Forward on the GPU (packed: with the packed copy of the routed experts'
+    weights); the oracle conditioned on its logits; integer results compared bit for
+    bit, weights and statistics within float32 tolerance."""
     inp = synth.DeviceInputs(cfg, DEV)
     layer = MoELayer.from_inputs(inp)
+    if packed:
+        layer.pack_weights()
     n = cfg.n_tokens
     st = layer.new_stats(n)
     y = layer.forward(inp.x, stats=st)
@@ -700,3 +703,98 @@ def test_forward_replays_from_a_captured_graph(name):
         layer.forward(x, y, st)
         torch.cuda.synchronize()
         assert torch.equal(y.view(torch.int16), ref.view(torch.int16))
+
+
+# ------------------------------------------------------------------ packed weights
+def _pack_reference(w1, w3, w2):
+    """moe_pack_weights' layout written out with numpy on bf16 bit patterns: per product,
+    rows padded with zeros to a multiple of 512, fragments of 32 rows x 16 elements
+    (row-block major), lane l of a fragment = row l % 32, elements 8 (l / 32) .. + 7;
+    SwiGLU's first product takes 64 rows of W1 then the same 64 of W3."""
+    def frags(W):
+        E, rows, K = W.shape
+        pad = (rows + 511) // 512 * 512
+        P = np.zeros((E, pad, K), np.uint16)
+        P[:, :rows] = W
+        P = P.reshape(E, pad // 32, 32, K // 16, 2, 8).transpose(0, 1, 3, 4, 2, 5)
+        return P.reshape(-1)
+    E, d_ff, d = w1.shape
+    first = w1
+    if w3 is not None:
+        first = np.concatenate([w1.reshape(E, d_ff // 64, 64, d), w3.reshape(E, d_ff // 64, 64, d)],
+                               axis=2).reshape(E, 2 * d_ff, d)
+    return np.concatenate([frags(first), frags(w2)])
+
+
+@pytest.mark.parametrize("act,E,d,d_ff", [("swiglu", 3, 128, 192), ("gelu", 2, 320, 704),
+                                          ("swiglu", 1, 576, 64), ("gelu", 5, 64, 1088)])
+def test_pack_weights_layout(act, E, d, d_ff):
+    """Every byte of the packed copy (padding included) against the layout in numpy."""
+    print_case("pack-layout", act, E, d, d_ff)
+    gen = torch.Generator().manual_seed(E * 1000 + d)
+    mk = lambda *sh: torch.randn(*sh, generator=gen).to(torch.bfloat16).to(DEV)
+    w1, w2 = mk(E, d_ff, d), mk(E, d, d_ff)
+    w3 = mk(E, d_ff, d) if act == "swiglu" else None
+    a = B.MOE_ACT_SWIGLU if act == "swiglu" else B.MOE_ACT_GELU
+    nbytes = B.moe_packed_weights_size(a, E, d, d_ff)
+    packed = torch.full((nbytes // 2,), -7.0, dtype=torch.bfloat16, device=DEV)
+    B.moe_pack_weights(a, E, d, d_ff, w1, w3, w2, packed)
+    torch.cuda.synchronize()
+    ref = _pack_reference(to_host_bits(w1), None if w3 is None else to_host_bits(w3),
+                          to_host_bits(w2))
+    assert ref.size * 2 == nbytes
+    assert np.array_equal(to_host_bits(packed), ref)
+
+
+PACKED_CASES = [
+    # 512 rows per expert (SwiGLU, gather + weight fusion)
+    ("mixtral", dict(n_tokens=2048, d_ff=2048)),
+    # K remainders (d 320: 20 k-steps, d_ff 1344: 84), padded rows, capacity gating
+    ("mixtral", dict(n_tokens=1536, d_model=320, d_ff=1344, n_experts=4, alpha=1.0)),
+    # GELU, k = 1, capacity, expert biases, unfused (permuted copy, combine weights)
+    ("switch", dict(n_tokens=2048, d_model=768, d_ff=1344, n_experts=4, expert_bias=True,
+                    fuse=0)),
+    ("switch", dict(n_tokens=1200, d_model=256, d_ff=576, n_experts=3, alpha=None)),
+]
+
+
+@pytest.mark.parametrize("case", PACKED_CASES, ids=[f"{c[0]}-{i}" for i, c in enumerate(PACKED_CASES)])
+def test_forward_parity_packed(case):
+    """The packed-weight expert kernel (segments of >= 256 rows) against the oracle."""
+    name, kw = case
+    cfg = CONFIGS[name].scaled(**kw)
+    print_case("forward-packed", name, kw)
+    err, r, _ = _forward_and_oracle(cfg, packed=True)
+    print(f"  {name}: normwise error {err:.3e}, dropped {r.plan.n_dropped}", flush=True)
+    assert err <= TOL[cfg.dtype]
+
+
+def test_forward_packed_gather_fusion_is_bit_identical():
+    """With packed weights too, gathering the routed rows in place gives the bits of the
+    permuted copy."""
+    cfg = CONFIGS["mixtral"].scaled(n_tokens=1024, d_ff=1024, fuse=0)
+    print_case("packed-gather", cfg.name, cfg.n_tokens)
+    inp = synth.DeviceInputs(cfg, DEV)
+    outs = []
+    for fuse in (0, B.MOE_FUSE_GATHER):
+        layer = MoELayer.from_inputs(inp)
+        layer.cfg = cfg.scaled(fuse=fuse)
+        layer.pack_weights()
+        outs.append(layer.forward(inp.x).clone())
+    torch.cuda.synchronize()
+    assert np.array_equal(to_host_bits(outs[0]), to_host_bits(outs[1]))
+
+
+def test_forward_parity_full_size_sampled_packed():
+    """The Mixtral-shaped layer at full size in the configuration the benchmark times
+    (packed weights, both fusions), outputs sampled."""
+    cfg = CONFIGS["mixtral"]
+    print_case("forward-full-packed", cfg.name, cfg.n_tokens)
+    n = cfg.n_tokens
+    rng = np.random.default_rng(3)
+    tokens = np.unique(np.concatenate([np.arange(6), np.arange(n - 6, n),
+                                       rng.choice(n, size=12, replace=False)]))
+    err, r, _ = _forward_and_oracle(cfg, tokens=tokens, packed=True)
+    print(f"  normwise error {err:.3e} on {len(tokens)} tokens", flush=True)
+    assert err <= TOL[cfg.dtype]
+    torch.cuda.empty_cache()
