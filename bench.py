@@ -345,6 +345,8 @@ def main():
     ap.add_argument("--no-dispatch-copy", action="store_true",
                     help="skip the standalone timing of the permuted copy of x")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--tokens", type=int, default=0,
+                    help="override the workload's batch (tokens); 0 keeps it")
     ap.add_argument("--no-pack", action="store_true",
                     help="do not pack the routed experts' weights (bf16): the expert "
                          "products then stage both operands through LDS")
@@ -402,6 +404,8 @@ def main():
 
     B.lib()  # fails loudly if the HIP library is not built
     cfg = CONFIGS[args.config]
+    if args.tokens > 0:
+        cfg = cfg.with_tokens(args.tokens)
     if args.bias_selection_only:
         cfg = cfg.scaled(bias_selection_only=True)
     if args.fuse is not None:
@@ -413,16 +417,16 @@ def main():
     layer = MoELayer.from_inputs(inp)
     n = cfg.n_tokens
     # one-time relayout of the routed experts' weights (moe_pack_weights), outside the
-    # timed region like any other weight preparation
-    packed = cfg.dtype == "bf16" and not args.no_pack
+    # timed region like any other weight preparation; only where the packed-weight
+    # kernel will run
+    use_packed = packed_path(cfg, layer.capacity(n), not args.no_pack)
     pack_ms = None
-    if packed:
+    if use_packed:
         torch.cuda.synchronize()
         tp = time.perf_counter()
         layer.pack_weights()
         torch.cuda.synchronize()
         pack_ms = (time.perf_counter() - tp) * 1e3
-    use_packed = packed_path(cfg, layer.capacity(n), packed)
     stats = layer.new_stats(n)
     y = torch.empty_like(inp.x)
 
@@ -509,7 +513,7 @@ def main():
                    "kept_rows": kept, "experts_touched": touched,
                    "capacity": layer.capacity(n),
                    "n_rerouted": int(stats["n_rerouted"].item()), "fuse": cfg.fuse,
-                   "packed_weights": packed, "packed_kernel": use_packed,
+                   "packed_weights": use_packed,
                    "pack_ms_once": None if pack_ms is None else round(pack_ms, 2)},
         "roofline": kernels[dominant],
         "grouped_gemm_tflops": round(gemm_tflops, 2),

@@ -998,8 +998,9 @@ __device__ __forceinline__ void pk_tail(const PackedIO& io, uint16_t* const (&A)
 // tile and packed weight row tn*32 + 8q + 4(lane/32) + r of the wave's panel p; the
 // four r are consecutive output columns (one 8-byte store).
 // TN0 .. TN1-1 restrict the epilogue to those weight tiles (SwiGLU: of the W1 tiles
-// 0, 1, each with its W3 tile tn + 2); default all.
-template <int EPI, int TA, int TN0 = 0, int TN1 = (EPI == EPI_SWIGLU ? 2 : 4)>
+// 0, 1, each with its W3 tile tn + 2), TM0 .. TM1-1 to those row blocks; default all.
+template <int EPI, int TA, int TN0 = 0, int TN1 = (EPI == EPI_SWIGLU ? 2 : 4), int TM0 = 0,
+          int TM1 = TA>
 __device__ __forceinline__ void packed_epilogue(const GemmArgs& g, const Tile& tile, int lane,
                                                 int p, f32x16_t (&acc)[4][4]) {
   uint16_t* __restrict__ C = static_cast<uint16_t*>(g.c);
@@ -1012,7 +1013,7 @@ __device__ __forceinline__ void packed_epilogue(const GemmArgs& g, const Tile& t
         const int col = p * 64 + tn * 32 + Mfma<32>::ni(q, lane);
         if (col >= g.n_out) continue;
 #pragma unroll
-        for (int tm = 0; tm < TA; ++tm) {
+        for (int tm = TM0; tm < TM1; ++tm) {
           const int m = tm * 32 + frow;
           if (m < tile.m_valid) {
             float v[4];
@@ -1028,7 +1029,7 @@ __device__ __forceinline__ void packed_epilogue(const GemmArgs& g, const Tile& t
     const uint16_t* bias = static_cast<const uint16_t*>(g.bias);
     float sc[TA];
 #pragma unroll
-    for (int tm = 0; tm < TA; ++tm) {
+    for (int tm = TM0; tm < TM1; ++tm) {
       const int m = tm * 32 + frow;
       sc[tm] = (g.row_scale && m < tile.m_valid) ? g.row_scale[tile.row0 + m] : 1.f;
     }
@@ -1044,7 +1045,7 @@ __device__ __forceinline__ void packed_epilogue(const GemmArgs& g, const Tile& t
           for (int r = 0; r < 4; ++r) bv[r] = bf16_to_f32(bias[tile.seg * g.bias_seg_stride + col + r]);
         }
 #pragma unroll
-        for (int tm = 0; tm < TA; ++tm) {
+        for (int tm = TM0; tm < TM1; ++tm) {
           const int m = tm * 32 + frow;
           if (m < tile.m_valid) {
             float v[4];
@@ -1192,39 +1193,59 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_packed_kernel(GemmArgs g) {
 }
 
 // Finishes the split tiles of the preceding gemm_packed_kernel launch: one single-wave
-// workgroup per (split tile, wave of the tile, half h of that wave's output tiles) sums
-// its accumulators over the parts in part order and runs its share of the epilogue
-// (SwiGLU: W1 tile h with W3 tile h + 2; otherwise tiles 2h, 2h + 1).
-template <int EPI, int TA, int H>
+// workgroup per (split tile, wave of the tile, half h of that wave's output tiles, row
+// block tm) loads its accumulators of every part, sums them in part order and runs its
+// share of the epilogue (SwiGLU: W1 tile h with W3 tile h + 2; otherwise tiles 2h,
+// 2h + 1).  32 workgroups per tile, each with all its loads issued before the first
+// sum, keep the partials' reads in flight together.
+template <int EPI, int H, int TM>
 __device__ __forceinline__ void packed_finish(const GemmArgs& g, const Tile& tile, int q, int tid,
                                               int lane, int p) {
   constexpr int TNA = EPI == EPI_SWIGLU ? H : 2 * H;
   constexpr int TNB = EPI == EPI_SWIGLU ? H + 2 : 2 * H + 1;
-  f32x16_t acc[4][4];
-  for (int part = 0; part < tile.nparts; ++part) {
-    const f32x4_t* sp = pk_slot(g.split_buf, q * tile.nparts + part);
+  f32x4_t x[kMaxSplitParts][2][4];
 #pragma unroll
-    for (int tm = 0; tm < TA; ++tm)
+  for (int part = 0; part < kMaxSplitParts; ++part) {
+    if (part < tile.nparts) {
+      const f32x4_t* sp = pk_slot(g.split_buf, q * tile.nparts + part);
 #pragma unroll
       for (int v = 0; v < 4; ++v) {
-        const f32x4_t xa = sp[pk_chunk(TNA, tm, v) * kThreads + tid];
-        const f32x4_t xb = sp[pk_chunk(TNB, tm, v) * kThreads + tid];
+        x[part][0][v] = sp[pk_chunk(TNA, TM, v) * kThreads + tid];
+        x[part][1][v] = sp[pk_chunk(TNB, TM, v) * kThreads + tid];
+      }
+    }
+  }
+  f32x16_t acc[4][4];
+#pragma unroll
+  for (int v = 0; v < 4; ++v)
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      acc[TNA][TM][4 * v + r] = x[0][0][v][r];
+      acc[TNB][TM][4 * v + r] = x[0][1][v][r];
+    }
+#pragma unroll
+  for (int part = 1; part < kMaxSplitParts; ++part) {
+    if (part < tile.nparts) {
+#pragma unroll
+      for (int v = 0; v < 4; ++v)
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
-          acc[TNA][tm][4 * v + r] = part == 0 ? xa[r] : acc[TNA][tm][4 * v + r] + xa[r];
-          acc[TNB][tm][4 * v + r] = part == 0 ? xb[r] : acc[TNB][tm][4 * v + r] + xb[r];
+          acc[TNA][TM][4 * v + r] += x[part][0][v][r];
+          acc[TNB][TM][4 * v + r] += x[part][1][v][r];
         }
-      }
+    }
   }
+  // (TA = 4 only sizes the epilogue's row-scale array; the row block is TM)
   if constexpr (EPI == EPI_SWIGLU)
-    packed_epilogue<EPI, TA, H, H + 1>(g, tile, lane, p, acc);
+    packed_epilogue<EPI, 4, H, H + 1, TM, TM + 1>(g, tile, lane, p, acc);
   else
-    packed_epilogue<EPI, TA, 2 * H, 2 * H + 2>(g, tile, lane, p, acc);
+    packed_epilogue<EPI, 4, 2 * H, 2 * H + 2, TM, TM + 1>(g, tile, lane, p, acc);
 }
 
 template <int EPI>
 __global__ __launch_bounds__(kWave) void gemm_packed_finish_kernel(GemmArgs g) {
-  const int q = blockIdx.x / 8, wave = (blockIdx.x / 2) % 4, h = blockIdx.x % 2;
+  const int q = blockIdx.x / 32, wave = (blockIdx.x / 8) % 4, h = (blockIdx.x / 4) % 2;
+  const int tm = blockIdx.x % 4;
   // (the product launch it finishes did nothing: its split descriptors are stale)
   if (g.small_tiles && *g.small_tiles != 0) return;
   if (q >= g.split_desc[0]) return;
@@ -1239,16 +1260,16 @@ __global__ __launch_bounds__(kWave) void gemm_packed_finish_kernel(GemmArgs g) {
   tile.split_q = q;
   tile.k_stage0 = 0;
   tile.k_stages = 0;
+  if (tm * 32 >= tile.m_valid) return;  // this row block holds no rows of the tile
   const int lane = threadIdx.x;
   const int tid = wave * kWave + lane;  // the thread of the tile's workgroup this lane stands for
   const int p = tile.nt * 4 + wave;
-  const int ta = __builtin_amdgcn_readfirstlane(min((tile.m_valid + 31) / 32, 4));
   auto run = [&](auto h_c) {
     constexpr int H = decltype(h_c)::value;
-    if (ta >= 4) packed_finish<EPI, 4, H>(g, tile, q, tid, lane, p);
-    else if (ta == 3) packed_finish<EPI, 3, H>(g, tile, q, tid, lane, p);
-    else if (ta == 2) packed_finish<EPI, 2, H>(g, tile, q, tid, lane, p);
-    else packed_finish<EPI, 1, H>(g, tile, q, tid, lane, p);
+    if (tm == 0) packed_finish<EPI, H, 0>(g, tile, q, tid, lane, p);
+    else if (tm == 1) packed_finish<EPI, H, 1>(g, tile, q, tid, lane, p);
+    else if (tm == 2) packed_finish<EPI, H, 2>(g, tile, q, tid, lane, p);
+    else packed_finish<EPI, H, 3>(g, tile, q, tid, lane, p);
   };
   if (h == 0) run(std::integral_constant<int, 0>{});
   else run(std::integral_constant<int, 1>{});
@@ -1402,7 +1423,7 @@ hipError_t launch_packed(hipStream_t st, GemmArgs g, int64_t max_rows) {
                      0, st, g);
   hipError_t err = hipGetLastError();
   if (err != hipSuccess || g.split_g == 0) return err;
-  hipLaunchKernelGGL((gemm_packed_finish_kernel<EPI>), dim3(static_cast<unsigned>(g.split_g / 2 * 8)),
+  hipLaunchKernelGGL((gemm_packed_finish_kernel<EPI>), dim3(static_cast<unsigned>(g.split_g / 2 * 32)),
                      dim3(kWave), 0, st, g);
   return hipGetLastError();
 }
