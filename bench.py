@@ -71,11 +71,26 @@ def packed_path(cfg, capacity: int, packed: bool) -> bool:
     return rows // cfg.n_experts >= PACKED_ROWS
 
 
-def stage_symbol(cfg, stage: str, packed: bool = False):
+def stage_symbol(cfg, stage: str, packed: bool = False, capacity: int = -1):
+    """The kernel of a GEMM stage's launch: the packed-weight kernel, else the staged
+    kernel with 256-row tiles, or 32-row tiles where the library's bound on the kept rows
+    averages under 48 per expert (float32: the SIMT kernel).  (Above that bound, with a
+    capacity limit, the dispatch picks between the two heights on the device; the name
+    given is the 256-row one.)"""
     pre = "packed_" if packed else ""
     if stage == "gemm1":
-        return STAGE_KERNEL[pre + ("gemm1_swiglu" if cfg.act == "swiglu" else "gemm1_gelu")]
-    return STAGE_KERNEL.get(pre + stage if stage == "gemm2" else stage)
+        sym = STAGE_KERNEL[pre + ("gemm1_swiglu" if cfg.act == "swiglu" else "gemm1_gelu")]
+    else:
+        sym = STAGE_KERNEL.get(pre + stage if stage == "gemm2" else stage)
+    if sym and cfg.dtype != "bf16":
+        return sym.replace("gemm_bf16_kernel<256, ", "gemm_f32_kernel<")
+    if sym and not packed:
+        rows = cfg.n_tokens * cfg.top_k
+        if capacity >= 0:
+            rows = min(rows, capacity * cfg.n_experts)
+        if rows // cfg.n_experts < 48:
+            sym = sym.replace("<256,", "<32,")
+    return sym
 
 
 def _pmc_rows(path: str):
@@ -484,7 +499,7 @@ def main():
     kernels = {s: roofline(s, work[s], stage_ms[s], cfg.dtype) for s in STAGES
                if stage_ms[s] > 0 and (work[s]["flops"] > 0 or work[s]["bytes"] > 0)}
     for s, r in kernels.items():
-        r["symbol"] = stage_symbol(cfg, s, use_packed)
+        r["symbol"] = stage_symbol(cfg, s, use_packed, layer.capacity(n))
         r["traffic"] = stored_traffic(cfg.name, s, r["symbol"])
     dominant = max(kernels, key=lambda s: stage_ms[s])
     gemm_ms = stage_ms["gemm1"] + stage_ms["gemm2"] + stage_ms["shared"]
