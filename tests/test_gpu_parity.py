@@ -626,12 +626,18 @@ def test_forward_parity_many_tokens_sampled():
     assert err <= TOL[cfg.dtype]
 
 
-def test_forward_is_deterministic():
-    cfg = CONFIGS["mixtral"].with_tokens(300).scaled(d_ff=1024)
-    print_case("determinism", cfg.name, cfg.n_tokens)
+@pytest.mark.parametrize("packed", [False, True])
+def test_forward_is_deterministic(packed):
+    # packed: 600 rows per expert of 4, the packed kernel with a split last round
+    cfg = (CONFIGS["mixtral"].scaled(n_tokens=1200, d_ff=1024, n_experts=4) if packed
+           else CONFIGS["mixtral"].with_tokens(300).scaled(d_ff=1024))
+    print_case("determinism", cfg.name, cfg.n_tokens, packed)
     inp = synth.DeviceInputs(cfg, DEV)
     layer = MoELayer.from_inputs(inp)
-    s1, s2 = layer.new_stats(300), layer.new_stats(300)
+    if packed:
+        layer.pack_weights()
+    n = cfg.n_tokens
+    s1, s2 = layer.new_stats(n), layer.new_stats(n)
     y1 = layer.forward(inp.x, stats=s1).clone()
     y2 = layer.forward(inp.x, stats=s2)
     torch.cuda.synchronize()
@@ -669,17 +675,24 @@ def test_forward_edge_cases():
 
 
 # ------------------------------------------------------------------ graph capture
-@pytest.mark.parametrize("name", ["deepseek", "switch"])
+@pytest.mark.parametrize("name", ["deepseek", "switch", "mixtral-packed"])
 def test_forward_replays_from_a_captured_graph(name):
     """moe_forward allocates nothing, syncs nothing and clears nothing with memset, so a
     captured forward (shared experts on the internal second stream included) replays
     correctly: every replay, with eager work between replays, matches the eager result
-    bit for bit."""
-    cfg = CONFIGS[name].with_tokens(REDUCED[name]).scaled(d_ff=min(CONFIGS[name].d_ff, 1024),
-                                                          reroute_rounds=2)
+    bit for bit.  mixtral-packed: packed weights, 600 rows per expert under a capacity
+    limit (the packed kernel, its split-tile finish and the gated 32-row launch)."""
+    if name == "mixtral-packed":
+        cfg = CONFIGS["mixtral"].scaled(n_tokens=1200, d_ff=1024, n_experts=4, alpha=1.0,
+                                        reroute_rounds=2)
+    else:
+        cfg = CONFIGS[name].with_tokens(REDUCED[name]).scaled(
+            d_ff=min(CONFIGS[name].d_ff, 1024), reroute_rounds=2)
     print_case("graph", name, cfg.n_tokens)
     inp = synth.DeviceInputs(cfg, DEV)
     layer = MoELayer.from_inputs(inp)
+    if name == "mixtral-packed":
+        layer.pack_weights()
     x = inp.x.clone()
     y = torch.empty_like(x)
     st = layer.new_stats(cfg.n_tokens)
