@@ -271,6 +271,22 @@ moe_status moe_expert_ffn(void* stream, moe_dtype dtype, moe_act act, const void
                           const float* row_scale, void* h, void* y);
 
 /*
+ * moe_expert_ffn_packed -- moe_expert_ffn (bf16 only) that also takes `packed`, the copy
+ * of w1/w3/w2 written by moe_pack_weights(act, n_segments, d_model, d_ff, ...) (device,
+ * 16-byte aligned, required when max_rows > 0).  Where max_rows averages at least 256
+ * rows per segment the expert products read the packed copy (the same h and y as
+ * moe_expert_ffn); otherwise w1/w3/w2 as in moe_expert_ffn.  Arguments, layouts and
+ * errors are those of moe_expert_ffn.
+ */
+moe_status moe_expert_ffn_packed(void* stream, moe_act act, const void* a,
+                                 const int32_t* a_rows, int64_t a_n_rows,
+                                 const int32_t* seg_offsets, int32_t n_segments,
+                                 int64_t max_rows, int64_t d_model, int64_t d_ff,
+                                 const void* w1, const void* w3, const void* b1, const void* w2,
+                                 const void* b2, const void* packed, const float* row_scale,
+                                 void* h, void* y);
+
+/*
  * moe_combine -- routing-weighted sum of the expert rows back into token order
  * ([Why-MoE] §2.1: y = sum_i g_i(x) Expert_i(x); [DeepSeek-V2] §2.3: shared experts
  * add their unweighted output).

@@ -581,12 +581,15 @@ moe_status moe_dispatch(void* stream, const int32_t* topk_idx, int64_t n_tokens,
                       n_dropped, x_perm, topk_w, row_weight, ws);
 }
 
-moe_status moe_expert_ffn(void* stream, moe_dtype dtype, moe_act act, const void* a,
-                          const int32_t* a_rows, int64_t a_n_rows,
-                          const int32_t* seg_offsets, int32_t n_segments, int64_t max_rows,
-                          int64_t d_model, int64_t d_ff, const void* w1, const void* w3,
-                          const void* b1, const void* w2, const void* b2,
-                          const float* row_scale, void* h, void* y) {
+}  // extern "C"
+
+namespace {
+
+// Argument checks shared by moe_expert_ffn and moe_expert_ffn_packed.
+moe_status check_ffn_args(moe_dtype dtype, moe_act act, const void* a, const int32_t* a_rows,
+                          int64_t a_n_rows, const int32_t* seg_offsets, int32_t n_segments,
+                          int64_t max_rows, int64_t d_model, int64_t d_ff, const void* w1,
+                          const void* w3, const void* w2, const void* h, const void* y) {
   MOE_TRY(check_ffn_shape(dtype, act, d_model, d_ff));
   if (a_rows && (a_n_rows < 1 || a_n_rows * d_model * static_cast<int64_t>(elem_size(dtype)) > UINT32_MAX))
     return fail(MOE_ERR_UNSUPPORTED, "with a_rows, a must have 1 .. 4 GiB / row bytes rows");
@@ -604,9 +607,43 @@ moe_status moe_expert_ffn(void* stream, moe_dtype dtype, moe_act act, const void
   if (w3) MOE_TRY(check_aligned(w3, 16, "w3"));
   MOE_TRY(check_aligned(h, 16, "h"));
   MOE_TRY(check_aligned(y, 16, "y"));
+  return MOE_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+moe_status moe_expert_ffn(void* stream, moe_dtype dtype, moe_act act, const void* a,
+                          const int32_t* a_rows, int64_t a_n_rows,
+                          const int32_t* seg_offsets, int32_t n_segments, int64_t max_rows,
+                          int64_t d_model, int64_t d_ff, const void* w1, const void* w3,
+                          const void* b1, const void* w2, const void* b2,
+                          const float* row_scale, void* h, void* y) {
+  MOE_TRY(check_ffn_args(dtype, act, a, a_rows, a_n_rows, seg_offsets, n_segments, max_rows,
+                         d_model, d_ff, w1, w3, w2, h, y));
+  if (max_rows == 0) return MOE_OK;
   return run_ffn(static_cast<hipStream_t>(stream), dtype, act, a, d_model, seg_offsets,
                  n_segments, 0, max_rows, d_model, d_ff, w1, w3, b1, d_ff * d_model, w2, b2,
                  d_ff, 0, h, y, nullptr, a_rows, row_scale);
+}
+
+moe_status moe_expert_ffn_packed(void* stream, moe_act act, const void* a,
+                                 const int32_t* a_rows, int64_t a_n_rows,
+                                 const int32_t* seg_offsets, int32_t n_segments,
+                                 int64_t max_rows, int64_t d_model, int64_t d_ff,
+                                 const void* w1, const void* w3, const void* b1, const void* w2,
+                                 const void* b2, const void* packed, const float* row_scale,
+                                 void* h, void* y) {
+  MOE_TRY(check_ffn_args(MOE_BF16, act, a, a_rows, a_n_rows, seg_offsets, n_segments, max_rows,
+                         d_model, d_ff, w1, w3, w2, h, y));
+  if (max_rows == 0) return MOE_OK;
+  if (!packed) return fail(MOE_ERR_INVALID_ARG, "packed is required");
+  MOE_TRY(check_aligned(packed, 16, "packed"));
+  return run_ffn(static_cast<hipStream_t>(stream), MOE_BF16, act, a, d_model, seg_offsets,
+                 n_segments, 0, max_rows, d_model, d_ff, w1, w3, b1, d_ff * d_model, w2, b2,
+                 d_ff, 0, h, y, nullptr, a_rows, row_scale, 0, nullptr, nullptr, nullptr,
+                 packed);
 }
 
 moe_status moe_combine(void* stream, moe_dtype dtype, const void* y_rows,

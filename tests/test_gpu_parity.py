@@ -394,7 +394,8 @@ def test_dispatch_without_copy_and_empty():
 
 
 # ------------------------------------------------------------------ expert FFN
-def _ffn_case(dtype, act, bias, d, d_ff, sizes, seed=0, gather=False, scale=False):
+def _ffn_case(dtype, act, bias, d, d_ff, sizes, seed=0, gather=False, scale=False,
+              packed=False):
     """Expert FFN over segments.  gather: the rows of a are read through a row map into
     a larger matrix (repeats included); scale: every output row is multiplied by its own
     weight.  The oracle applies both to its inputs and outputs directly."""
@@ -417,10 +418,16 @@ def _ffn_case(dtype, act, bias, d, d_ff, sizes, seed=0, gather=False, scale=Fals
     t = dict(a=up(a_src), w1=up(w1), w3=up(w3), w2=up(w2), b1=up(b1), b2=up(b2))
     h = torch.zeros((max(rows, 1), d_ff), dtype=t["a"].dtype, device=DEV)
     y = torch.zeros((max(rows, 1), d), dtype=t["a"].dtype, device=DEV)
-    B.moe_expert_ffn(B.MOE_ACT_SWIGLU if act == "swiglu" else B.MOE_ACT_GELU, t["a"],
+    actc = B.MOE_ACT_SWIGLU if act == "swiglu" else B.MOE_ACT_GELU
+    pk = None
+    if packed:
+        pk = torch.empty(B.moe_packed_weights_size(actc, S, d, d_ff) // 2, dtype=torch.bfloat16,
+                         device=DEV)
+        B.moe_pack_weights(actc, S, d, d_ff, t["w1"], t["w3"], t["w2"], pk)
+    B.moe_expert_ffn(actc, t["a"],
                      torch.from_numpy(off).to(DEV), S, rows, t["w1"], t["w3"], t["b1"], t["w2"],
                      t["b2"], h, y, a_rows=None if a_rows is None else torch.from_numpy(a_rows).to(DEV),
-                     row_scale=None if rs is None else torch.from_numpy(rs).to(DEV))
+                     row_scale=None if rs is None else torch.from_numpy(rs).to(DEV), packed=pk)
     torch.cuda.synchronize()
     a64 = O.widen(a, dtype)
     hg, yg = widen_t(h), widen_t(y)
@@ -456,6 +463,31 @@ FFN_CASES = [
     ("f32", "gelu", True, 128, 512, [30, 0, 100, 126]),
     ("f32", "swiglu", False, 132, 260, [65, 1, 0, 200]),
 ]
+
+
+PACKED_FFN_CASES = [
+    # segments averaging >= 256 rows (the packed-weight kernel): empty and one-row
+    # segments, exactly one and two 128-row tiles, tails of 1..4 row blocks, K tails
+    # (d 192: 12 k-steps, d_ff 320: 20), padding weight rows (2*320 and 192 < 512)
+    ("bf16", "swiglu", False, 192, 320, [0, 1, 129, 300, 513, 0, 1100, 128, 256, 140]),
+    ("bf16", "gelu", True, 320, 704, [640, 0, 257, 96, 600, 33]),
+    ("bf16", "swiglu", False, 576, 1344, [1000, 1048, 30]),
+]
+
+
+@pytest.mark.parametrize("case", PACKED_FFN_CASES,
+                         ids=[f"{c[1]}-{c[3]}x{c[4]}-{len(c[5])}seg" for c in PACKED_FFN_CASES])
+@pytest.mark.parametrize("fused", [False, True])
+def test_expert_ffn_packed_parity(case, fused):
+    """moe_expert_ffn_packed: the packed-weight kernel over hand-picked segments, plain
+    and with the row gather and output row scales."""
+    print_case("expert_ffn_packed", case, fused)
+    sizes = case[5]
+    assert sum(sizes) >= 256 * len(sizes)  # the library's rule for the packed kernel
+    err_h, err_y, err_e2e = _ffn_case(*case, gather=fused, scale=fused, packed=True)
+    assert err_h <= TOL["bf16"], f"h error {err_h}"
+    assert err_y <= TOL["bf16"], f"y error given h {err_y}"
+    assert err_e2e <= TOL["bf16"], f"y error end to end {err_e2e}"
 
 
 @pytest.mark.parametrize("case", FFN_CASES, ids=[f"{c[0]}-{c[1]}-{c[3]}x{c[4]}-{len(c[5])}seg" for c in FFN_CASES])
