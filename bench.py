@@ -34,13 +34,6 @@ STAGES = ["route", "dispatch", "gemm1", "gemm2", "shared", "combine"]
 PROFILES = os.path.join(ROOT, "profiles")
 CSRC = os.path.join(ROOT, "sparse_mixture_experts_forward_amd", "csrc")
 # kernel symbol of each stage's launch, as rocprofv3 names it (bf16 workloads)
-STAGE_KERNEL = {"gemm1_swiglu": "gemm_bf16_kernel<256, 2, false>",
-                "gemm1_gelu": "gemm_bf16_kernel<256, 1, false>",
-                "gemm2": "gemm_bf16_kernel<256, 0, false>",
-                # with packed weights and long segments
-                "packed_gemm1_swiglu": "gemm_packed_kernel<2>",
-                "packed_gemm1_gelu": "gemm_packed_kernel<1>",
-                "packed_gemm2": "gemm_packed_kernel<0>"}
 PACKED_ROWS = 256  # segments averaging this many rows take the packed-weight kernel
 CALIB_KERNEL = "MulFunctor"  # the plain float32 copy (x * 1) that scales byte counters
 
@@ -59,38 +52,42 @@ def sources_hash() -> str:
     return h.hexdigest()[:16]
 
 
-def packed_path(cfg, capacity: int, packed: bool) -> bool:
-    """Whether the routed expert products run the packed-weight kernel: packed weights
-    given, bf16, and the library's bound on the kept rows averaging >= PACKED_ROWS per
-    expert."""
-    if not packed or cfg.dtype != "bf16":
-        return False
+SMALL_ROWS = 48  # below this the library takes 32-row tiles
+
+
+def _avg_rows(cfg, capacity: int) -> int:
+    """The library's bound on the kept rows per expert (what picks its GEMM kernels)."""
     rows = cfg.n_tokens * cfg.top_k
     if capacity >= 0:
         rows = min(rows, capacity * cfg.n_experts)
-    return rows // cfg.n_experts >= PACKED_ROWS
+    return rows // cfg.n_experts
+
+
+def packed_path(cfg, capacity: int, packed: bool) -> bool:
+    """Whether packed weights reach a routed expert product: bf16, and segments either
+    long (>= PACKED_ROWS: the packed-weight kernel) or short (< SMALL_ROWS: its 32-row
+    variant), both by the library's bound on the kept rows."""
+    if not packed or cfg.dtype != "bf16":
+        return False
+    avg = _avg_rows(cfg, capacity)
+    return avg >= PACKED_ROWS or avg < SMALL_ROWS
 
 
 def stage_symbol(cfg, stage: str, packed: bool = False, capacity: int = -1):
-    """The kernel of a GEMM stage's launch: the packed-weight kernel, else the staged
-    kernel with 256-row tiles, or 32-row tiles where the library's bound on the kept rows
-    averages under 48 per expert (float32: the SIMT kernel).  (Above that bound, with a
-    capacity limit, the dispatch picks between the two heights on the device; the name
-    given is the 256-row one.)"""
-    pre = "packed_" if packed else ""
-    if stage == "gemm1":
-        sym = STAGE_KERNEL[pre + ("gemm1_swiglu" if cfg.act == "swiglu" else "gemm1_gelu")]
-    else:
-        sym = STAGE_KERNEL.get(pre + stage if stage == "gemm2" else stage)
-    if sym and cfg.dtype != "bf16":
-        return sym.replace("gemm_bf16_kernel<256, ", "gemm_f32_kernel<")
-    if sym and not packed:
-        rows = cfg.n_tokens * cfg.top_k
-        if capacity >= 0:
-            rows = min(rows, capacity * cfg.n_experts)
-        if rows // cfg.n_experts < 48:
-            sym = sym.replace("<256,", "<32,")
-    return sym
+    """The kernel of a GEMM stage's launch.  (With a capacity limit and a row bound of
+    SMALL_ROWS or more per expert, the dispatch picks the tile height on the device; the
+    name given is then that of the taller tiles.)"""
+    epi = {"gemm1": 2 if cfg.act == "swiglu" else 1, "gemm2": 0}.get(stage)
+    if epi is None:
+        return None
+    if cfg.dtype != "bf16":
+        return f"gemm_f32_kernel<{epi}, false>"
+    avg = _avg_rows(cfg, capacity)
+    if avg < SMALL_ROWS:
+        return f"gemm_packed_small_kernel<{epi}>" if packed else f"gemm_bf16_kernel<32, {epi}, false>"
+    if packed and avg >= PACKED_ROWS:
+        return f"gemm_packed_kernel<{epi}>"
+    return f"gemm_bf16_kernel<256, {epi}, false>"
 
 
 def _pmc_rows(path: str):

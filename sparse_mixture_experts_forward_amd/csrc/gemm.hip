@@ -1313,6 +1313,118 @@ __global__ __launch_bounds__(256) void pack_weights_kernel(
 }
 
 
+// ------------------------------------------------------------------ packed-weight kernel, short segments
+// Segments the host knows to be short (fewer than kBigSegRows rows per expert by its
+// bound: decode-like batches): the products stream the weights, so each of the 4 waves of a workgroup streams its own 128-row panel of the
+// packed copy straight into a register ring (each k-step's 4 fragments loaded 7 k-steps
+// ahead) against the tile's 32 activation rows, which every wave also loads itself (16
+// bytes per lane per k-step, the rows gathered as elsewhere; 4 KB per stage, L1
+// resident after the first wave).  No LDS and no barriers: two workgroups per CU keep 8
+// independent weight streams in flight.  Tile 32 rows x 512 weight rows; rows past the
+// segment repeat its last row.
+constexpr int kSRing = 8;
+constexpr int kSLead = kSRing - 1;
+
+struct PackedSmallIO {
+  const char* a_base;  // uniform
+  uint32_t a_off;      // this lane's row and 16-byte piece
+  const char* w_base;  // uniform: this wave's weight panel
+  uint32_t w_off[4];
+  int KS;
+
+  __device__ __forceinline__ void load(bf16x8_t (&w)[4], bf16x8_t& a, int ks) const {
+#if defined(__HIP_DEVICE_COMPILE__)
+    const int t = min(ks, KS - 1);
+    const __amdgpu_buffer_rsrc_t rw = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<char*>(w_base), static_cast<short>(0), -1, 0x00020000);
+#pragma unroll
+    for (int tn = 0; tn < 4; ++tn)
+      w[tn] = __builtin_bit_cast(bf16x8_t,
+                                 __builtin_amdgcn_raw_buffer_load_b128(rw, w_off[tn], t * 1024, 0));
+    const __amdgpu_buffer_rsrc_t ra = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<char*>(a_base), static_cast<short>(0), -1, 0x00020000);
+    a = __builtin_bit_cast(bf16x8_t, __builtin_amdgcn_raw_buffer_load_b128(ra, a_off, t * 32, 0));
+#endif
+  }
+};
+
+template <int T>
+__device__ __forceinline__ void ps_step(const PackedSmallIO& io, int t, bf16x8_t (&wr)[kSRing][4],
+                                        bf16x8_t (&ar)[kSRing], f32x16_t (&acc)[4][4]) {
+  io.load(wr[(T + kSLead) % kSRing], ar[(T + kSLead) % kSRing], t + kSLead);
+#pragma unroll
+  for (int tn = 0; tn < 4; ++tn)
+    acc[tn][0] = Mfma<32>::mma(wr[T % kSRing][tn], ar[T % kSRing], acc[tn][0]);
+}
+
+template <int T>
+__device__ __forceinline__ void ps_period(const PackedSmallIO& io, int t0, bf16x8_t (&wr)[kSRing][4],
+                                          bf16x8_t (&ar)[kSRing], f32x16_t (&acc)[4][4]) {
+  if constexpr (T < kSRing) {
+    ps_step<T>(io, t0 + T, wr, ar, acc);
+    ps_period<T + 1>(io, t0, wr, ar, acc);
+  }
+}
+
+template <int T>
+__device__ __forceinline__ void ps_tail(const PackedSmallIO& io, int t0, int rem,
+                                        bf16x8_t (&wr)[kSRing][4], bf16x8_t (&ar)[kSRing],
+                                        f32x16_t (&acc)[4][4]) {
+  if constexpr (T < kSRing) {
+    if (T < rem) {
+      ps_step<T>(io, t0 + T, wr, ar, acc);
+      ps_tail<T + 1>(io, t0, rem, wr, ar, acc);
+    }
+  }
+}
+
+template <int EPI>
+__global__ __launch_bounds__(kThreads, 2) void gemm_packed_small_kernel(GemmArgs g) {
+  __shared__ SchedSmem sched;
+  // the launch stands for the 32-row tiles: with a device-chosen height it runs only
+  // where the dispatch chose them
+  if (g.small_tiles && *g.small_tiles != 1) return;
+  Tile tile;
+  if (!schedule_tile<32>(g.seg_off, g.n_seg, g.single_rows, g.max_rows, g.bp_rows / kPBN,
+                         g.k / kBK, 0, nullptr, sched, tile))
+    return;
+  const int tid = threadIdx.x;
+  const int lane = tid & (kWave - 1);
+  const int wave = __builtin_amdgcn_readfirstlane(tid / kWave);
+  PackedSmallIO io;
+  io.KS = g.k / 16;
+  const int32_t* __restrict__ a_rows = g.a_rows;
+  io.a_base = uniform_ptr(reinterpret_cast<const char*>(
+      static_cast<const uint16_t*>(g.a) + (a_rows ? 0 : tile.row0 * g.lda)));
+  const int r = min(lane & 31, tile.m_valid - 1);
+  const uint32_t src = a_rows ? static_cast<uint32_t>(a_rows[tile.row0 + r]) : r;
+  io.a_off = (src * static_cast<uint32_t>(g.lda) + 8u * static_cast<uint32_t>(lane >> 5)) * 2u;
+  const int p = tile.nt * 4 + wave;
+  io.w_base = uniform_ptr(static_cast<const char*>(g.bp) + tile.seg * g.bp_seg_stride +
+                          static_cast<int64_t>(p) * 128 * g.k * 2);
+#pragma unroll
+  for (int tn = 0; tn < 4; ++tn)
+    io.w_off[tn] = static_cast<uint32_t>(tn) * static_cast<uint32_t>(g.k) * 64u +
+                   static_cast<uint32_t>(lane) * 16u;
+  f32x16_t acc[4][4];
+#pragma unroll
+  for (int tn = 0; tn < 4; ++tn)
+#pragma unroll
+    for (int r2 = 0; r2 < 16; ++r2) acc[tn][0][r2] = 0.f;
+  bf16x8_t wr[kSRing][4];
+  bf16x8_t ar[kSRing];
+#pragma unroll
+  for (int t = 0; t < kSLead; ++t) {
+    io.load(wr[t], ar[t], t);
+    __builtin_amdgcn_sched_barrier(0);
+  }
+  int t0 = 0;
+  for (; t0 + kSRing <= io.KS; t0 += kSRing) ps_period<0>(io, t0, wr, ar, acc);
+  ps_tail<0>(io, t0, io.KS - t0, wr, ar, acc);
+  __builtin_amdgcn_s_waitcnt(0);
+  packed_epilogue<EPI, 1>(g, tile, lane, p, acc);
+}
+
 // ------------------------------------------------------------------ float32 SIMT kernel
 constexpr int kFBM = 64, kFBN = 64, kFBK = 16, kFPad = 4;
 
@@ -1428,6 +1540,16 @@ hipError_t launch_packed(hipStream_t st, GemmArgs g, int64_t max_rows) {
   return hipGetLastError();
 }
 
+template <int EPI>
+hipError_t launch_packed_small(hipStream_t st, const GemmArgs& g, int64_t max_rows) {
+  const int n_seg_eff = g.seg_off ? g.n_seg : 1;
+  const int64_t grid = grid_for(max_rows, n_seg_eff, 32, g.bp_rows / kPBN);
+  if (grid <= 0) return hipSuccess;
+  hipLaunchKernelGGL((gemm_packed_small_kernel<EPI>), dim3(static_cast<unsigned>(grid)),
+                     dim3(kThreads), 0, st, g);
+  return hipGetLastError();
+}
+
 template <int BM, int EPI>
 hipError_t launch_bf16_bm(hipStream_t st, GemmArgs g, int64_t max_rows, bool ksplit) {
   const int n_ntiles = (EPI == EPI_SWIGLU) ? (g.n_out + 127) / 128 : (g.n_out + 255) / 256;
@@ -1472,9 +1594,15 @@ hipError_t launch_bf16_epi(hipStream_t st, const GemmArgs& g, int64_t max_rows) 
   // split their last round.
   GemmArgs small = g;
   small.split_g = 0;
+  // with packed weights, segments the host already knows to be short take the 32-row
+  // packed-weight kernel.  (The 32-row launch made beside the 256-row tiles under a
+  // capacity limit stays staged: its products can be narrow, e.g. a Switch-style second
+  // layer of 1024 columns, where its 256-column tiles give twice the workgroups.)
+  const bool packed_small = g.bp != nullptr && !ksplit;
   if (avg < kBigSegRows) {
     small.small_tiles = nullptr;
-    return launch_bf16_bm<32, EPI>(st, small, max_rows, ksplit);
+    return packed_small ? launch_packed_small<EPI>(st, small, max_rows)
+                        : launch_bf16_bm<32, EPI>(st, small, max_rows, ksplit);
   }
   GemmArgs big = g;
   if (ksplit || !g.split_buf || !g.split_desc) big.split_g = 0;
@@ -1486,9 +1614,9 @@ hipError_t launch_bf16_epi(hipStream_t st, const GemmArgs& g, int64_t max_rows) 
   if (err != hipSuccess || !g.small_tiles) return err;
   // selected, the kept rows average under kBigSegRows per non-empty segment, so the
   // 32-row tiles number at most 2.5 per segment and column tile
-  return launch_bf16_bm<32, EPI>(
-      st, small, std::min<int64_t>(max_rows, static_cast<int64_t>(kBigSegRows) * n_seg_eff),
-      ksplit);
+  const int64_t small_rows =
+      std::min<int64_t>(max_rows, static_cast<int64_t>(kBigSegRows) * n_seg_eff);
+  return launch_bf16_bm<32, EPI>(st, small, small_rows, ksplit);
 }
 
 template <int EPI>

@@ -472,6 +472,9 @@ PACKED_FFN_CASES = [
     ("bf16", "swiglu", False, 192, 320, [0, 1, 129, 300, 513, 0, 1100, 128, 256, 140]),
     ("bf16", "gelu", True, 320, 704, [640, 0, 257, 96, 600, 33]),
     ("bf16", "swiglu", False, 576, 1344, [1000, 1048, 30]),
+    # segments averaging < 48 rows (the 32-row packed-weight kernel)
+    ("bf16", "swiglu", False, 192, 320, [3, 1, 2, 7, 30, 5, 0, 9]),
+    ("bf16", "gelu", True, 320, 704, [40, 0, 1, 33, 60, 47]),
 ]
 
 
@@ -483,7 +486,8 @@ def test_expert_ffn_packed_parity(case, fused):
     and with the row gather and output row scales."""
     print_case("expert_ffn_packed", case, fused)
     sizes = case[5]
-    assert sum(sizes) >= 256 * len(sizes)  # the library's rule for the packed kernel
+    # the library's rules for the two packed-weight kernels
+    assert sum(sizes) >= 256 * len(sizes) or sum(sizes) < 48 * len(sizes)
     err_h, err_y, err_e2e = _ffn_case(*case, gather=fused, scale=fused, packed=True)
     assert err_h <= TOL["bf16"], f"h error {err_h}"
     assert err_y <= TOL["bf16"], f"y error given h {err_y}"
@@ -800,12 +804,18 @@ PACKED_CASES = [
     ("switch", dict(n_tokens=2048, d_model=768, d_ff=1344, n_experts=4, expert_bias=True,
                     fuse=0)),
     ("switch", dict(n_tokens=1200, d_model=256, d_ff=576, n_experts=3, alpha=None)),
+    # 2 rows per expert: the 32-row packed-weight kernel
+    ("decode", dict(d_ff=2048)),
+    # capacity 80 over a skewed routing: the dispatch picks the (staged) 32-row tiles on
+    # the device, the packed-weight launch exits
+    ("switch", dict(n_tokens=4096, d_ff=1024)),
 ]
 
 
 @pytest.mark.parametrize("case", PACKED_CASES, ids=[f"{c[0]}-{i}" for i, c in enumerate(PACKED_CASES)])
 def test_forward_parity_packed(case):
-    """The packed-weight expert kernel (segments of >= 256 rows) against the oracle."""
+    """The packed-weight expert kernels (segments of >= 256 rows, and of a few rows)
+    against the oracle."""
     name, kw = case
     cfg = CONFIGS[name].scaled(**kw)
     print_case("forward-packed", name, kw)
