@@ -274,8 +274,8 @@ moe_status moe_expert_ffn(void* stream, moe_dtype dtype, moe_act act, const void
  * moe_expert_ffn_packed -- moe_expert_ffn (bf16 only) that also takes `packed`, the copy
  * of w1/w3/w2 written by moe_pack_weights(act, n_segments, d_model, d_ff, ...) (device,
  * 16-byte aligned, required when max_rows > 0).  Where max_rows averages at least 256
- * rows per segment the expert products read the packed copy (the same h and y as
- * moe_expert_ffn); otherwise w1/w3/w2 as in moe_expert_ffn.  Arguments, layouts and
+ * rows per segment, or fewer than 48, the expert products read the packed copy (the
+ * same h and y as moe_expert_ffn); otherwise w1/w3/w2 as in moe_expert_ffn.  Arguments, layouts and
  * errors are those of moe_expert_ffn.
  */
 moe_status moe_expert_ffn_packed(void* stream, moe_act act, const void* a,
@@ -335,8 +335,9 @@ typedef struct {
   const void* shared_w3;   /* [n_shared][d_ff][d], SwiGLU only */
   const void* shared_w2;   /* [n_shared][d][d_ff] */
   /* Optional (bf16 only): the routed experts' w1/w3/w2 as written by moe_pack_weights
-   * from these same w1/w3/w2.  When given, the expert products over long segments read
-   * it instead (same results); w1/w3/w2 stay required for the others. */
+   * from these same w1/w3/w2.  When given, the expert products over long segments
+   * (>= 256 rows per expert by the library's bound on the kept rows) and over short ones
+   * (< 48) read it instead (same results); w1/w3/w2 stay required for the others. */
   const void* packed;
 } moe_weights;
 

@@ -150,7 +150,8 @@ struct GemmArgs {
   const int32_t* small_tiles;
   // Packed weights (or null) of the launch's product, written by launch_pack_weights:
   // where set and the segments are long (kPackedRows), the packed-weight kernel runs
-  // instead of the 256-row tiles.  bp_rows packed rows per segment (a multiple of 512),
+  // instead of the 256-row tiles; where they are short (kBigSegRows), its 32-row variant
+  // instead of the 32-row tiles.  bp_rows packed rows per segment (a multiple of 512),
   // bp_seg_stride bytes between segments.
   const void* bp;
   int64_t bp_seg_stride;
