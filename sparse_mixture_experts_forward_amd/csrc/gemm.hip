@@ -33,6 +33,10 @@
 //     XCD instead, so that a segment's column tiles share its rows through one L2;
 //   * where the host cannot bound the rows per segment well (a capacity limit), the
 //     dispatch flags the tile height and both launches are made, one of them empty.
+// packed-weight kernels (bf16, with the copy written by launch_pack_weights, whose
+// 1 KB fragments are exactly a 32x32x16 MFMA lane's operand): for long segments
+// 128 x 512 tiles whose waves stream their own weight panels into registers while only
+// the activations pass through LDS; for short ones a 32-row variant without LDS.
 // float32 kernel: a plain LDS-tiled SIMT product (64 x 64 tiles) with the same
 // scheduling and epilogues; it serves the small float32 workload.
 
