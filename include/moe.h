@@ -275,16 +275,24 @@ moe_status moe_expert_ffn(void* stream, moe_dtype dtype, moe_act act, const void
  * of w1/w3/w2 written by moe_pack_weights(act, n_segments, d_model, d_ff, ...) (device,
  * 16-byte aligned, required when max_rows > 0).  Where max_rows averages at least 256
  * rows per segment, or fewer than 48, the expert products read the packed copy (the
- * same h and y as moe_expert_ffn); otherwise w1/w3/w2 as in moe_expert_ffn.  Arguments, layouts and
- * errors are those of moe_expert_ffn.
+ * same h and y as moe_expert_ffn, up to the order of the float32 sums noted below);
+ * otherwise w1/w3/w2 as in moe_expert_ffn.
+ *   ws, ws_bytes: optional device workspace (NULL: none), at least
+ *   moe_expert_ffn_packed_workspace_size() bytes for the current device, 256-byte
+ *   aligned.  With it, a product whose tiles leave the last round on the GPU mostly idle
+ *   splits those tiles along the reduction into float32 partials that a second launch
+ *   sums in part order (deterministic; rounding may differ from the unsplit sum).
+ * Other arguments, layouts and errors are those of moe_expert_ffn; a workspace that is
+ * too small gives MOE_ERR_WORKSPACE.
  */
+size_t moe_expert_ffn_packed_workspace_size(void);
 moe_status moe_expert_ffn_packed(void* stream, moe_act act, const void* a,
                                  const int32_t* a_rows, int64_t a_n_rows,
                                  const int32_t* seg_offsets, int32_t n_segments,
                                  int64_t max_rows, int64_t d_model, int64_t d_ff,
                                  const void* w1, const void* w3, const void* b1, const void* w2,
                                  const void* b2, const void* packed, const float* row_scale,
-                                 void* h, void* y);
+                                 void* h, void* y, void* ws, size_t ws_bytes);
 
 /*
  * moe_combine -- routing-weighted sum of the expert rows back into token order

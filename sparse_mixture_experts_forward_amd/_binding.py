@@ -75,8 +75,10 @@ _SIGS = {
                                _VP, _VP, _VP, _VP, _VP, _VP, _VP, _SZ]),
     "moe_expert_ffn": (C.c_int, [_VP, C.c_int, C.c_int, _VP, _VP, _I64, _VP, _I32, _I64, _I64,
                                  _I64, _VP, _VP, _VP, _VP, _VP, _VP, _VP, _VP]),
+    "moe_expert_ffn_packed_workspace_size": (_SZ, []),
     "moe_expert_ffn_packed": (C.c_int, [_VP, C.c_int, _VP, _VP, _I64, _VP, _I32, _I64, _I64,
-                                        _I64, _VP, _VP, _VP, _VP, _VP, _VP, _VP, _VP, _VP]),
+                                        _I64, _VP, _VP, _VP, _VP, _VP, _VP, _VP, _VP, _VP,
+                                        _VP, _SZ]),
     "moe_combine": (C.c_int, [_VP, C.c_int, _VP, _VP, _VP, _I64, _I32, _I64, _VP, _VP]),
     "moe_forward_workspace_size": (_SZ, [C.POINTER(MoEConfigC)]),
     "moe_forward": (C.c_int, [_VP, C.POINTER(MoEConfigC), C.POINTER(MoEWeightsC), _VP, _VP,
@@ -214,16 +216,22 @@ def moe_dispatch(topk_idx, n_experts: int, capacity: int, x, expert_offsets, row
     _check("moe_dispatch", st)
 
 
+def moe_expert_ffn_packed_workspace_size() -> int:
+    return int(lib().moe_expert_ffn_packed_workspace_size())
+
+
 def moe_expert_ffn(act: int, a, seg_offsets, n_segments: int, max_rows: int, w1, w3, b1, w2,
-                   b2, h, y, stream=None, a_rows=None, row_scale=None, packed=None):
-    """packed (bf16): the moe_pack_weights copy of w1/w3/w2 -> moe_expert_ffn_packed."""
+                   b2, h, y, stream=None, a_rows=None, row_scale=None, packed=None, ws=None):
+    """packed (bf16): the moe_pack_weights copy of w1/w3/w2 -> moe_expert_ffn_packed, with
+    the optional split workspace ws."""
     d = a.shape[1]
     d_ff = w1.shape[-2]
     if packed is not None:
         st = lib().moe_expert_ffn_packed(_stream(stream), act, _ptr(a), _ptr(a_rows), a.shape[0],
                                          _ptr(seg_offsets), n_segments, max_rows, d, d_ff,
                                          _ptr(w1), _ptr(w3), _ptr(b1), _ptr(w2), _ptr(b2),
-                                         _ptr(packed), _ptr(row_scale), _ptr(h), _ptr(y))
+                                         _ptr(packed), _ptr(row_scale), _ptr(h), _ptr(y),
+                                         _ptr(ws), _ws_bytes(ws))
         _check("moe_expert_ffn_packed", st)
         return
     st = lib().moe_expert_ffn(_stream(stream), _dtype(a), act, _ptr(a), _ptr(a_rows),

@@ -628,22 +628,45 @@ moe_status moe_expert_ffn(void* stream, moe_dtype dtype, moe_act act, const void
                  d_ff, 0, h, y, nullptr, a_rows, row_scale);
 }
 
+size_t moe_expert_ffn_packed_workspace_size(void) {
+  const int g = cu_count();
+  if (g <= 0) return 0;
+  return align_up(static_cast<size_t>(moe::gemm_split_floats(g)) * sizeof(float)) +
+         align_up(static_cast<size_t>(moe::gemm_split_desc_ints(g)) * sizeof(int32_t));
+}
+
 moe_status moe_expert_ffn_packed(void* stream, moe_act act, const void* a,
                                  const int32_t* a_rows, int64_t a_n_rows,
                                  const int32_t* seg_offsets, int32_t n_segments,
                                  int64_t max_rows, int64_t d_model, int64_t d_ff,
                                  const void* w1, const void* w3, const void* b1, const void* w2,
                                  const void* b2, const void* packed, const float* row_scale,
-                                 void* h, void* y) {
+                                 void* h, void* y, void* ws, size_t ws_bytes) {
   MOE_TRY(check_ffn_args(MOE_BF16, act, a, a_rows, a_n_rows, seg_offsets, n_segments, max_rows,
                          d_model, d_ff, w1, w3, w2, h, y));
   if (max_rows == 0) return MOE_OK;
   if (!packed) return fail(MOE_ERR_INVALID_ARG, "packed is required");
   MOE_TRY(check_aligned(packed, 16, "packed"));
+  // with a workspace, a partial last round of the expert products splits along K
+  int split_g = 0;
+  float* split_buf = nullptr;
+  int32_t* split_desc = nullptr;
+  if (ws) {
+    const size_t need = moe_expert_ffn_packed_workspace_size();
+    if (need == 0) return fail(MOE_ERR_HIP, "no current device");
+    if (ws_bytes < need)
+      return fail(MOE_ERR_WORKSPACE, "moe_expert_ffn_packed needs %zu workspace bytes", need);
+    MOE_TRY(check_aligned(ws, kAlign, "ws"));
+    split_g = cu_count();
+    split_buf = static_cast<float*>(ws);
+    split_desc = reinterpret_cast<int32_t*>(
+        static_cast<char*>(ws) +
+        align_up(static_cast<size_t>(moe::gemm_split_floats(split_g)) * sizeof(float)));
+  }
   return run_ffn(static_cast<hipStream_t>(stream), MOE_BF16, act, a, d_model, seg_offsets,
                  n_segments, 0, max_rows, d_model, d_ff, w1, w3, b1, d_ff * d_model, w2, b2,
-                 d_ff, 0, h, y, nullptr, a_rows, row_scale, 0, nullptr, nullptr, nullptr,
-                 packed);
+                 d_ff, 0, h, y, nullptr, a_rows, row_scale, split_g, split_buf, split_desc,
+                 nullptr, packed);
 }
 
 moe_status moe_combine(void* stream, moe_dtype dtype, const void* y_rows,

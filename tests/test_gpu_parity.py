@@ -395,7 +395,7 @@ def test_dispatch_without_copy_and_empty():
 
 # ------------------------------------------------------------------ expert FFN
 def _ffn_case(dtype, act, bias, d, d_ff, sizes, seed=0, gather=False, scale=False,
-              packed=False):
+              packed=False, split_ws=False):
     """Expert FFN over segments.  gather: the rows of a are read through a row map into
     a larger matrix (repeats included); scale: every output row is multiplied by its own
     weight.  The oracle applies both to its inputs and outputs directly."""
@@ -427,7 +427,8 @@ def _ffn_case(dtype, act, bias, d, d_ff, sizes, seed=0, gather=False, scale=Fals
     B.moe_expert_ffn(actc, t["a"],
                      torch.from_numpy(off).to(DEV), S, rows, t["w1"], t["w3"], t["b1"], t["w2"],
                      t["b2"], h, y, a_rows=None if a_rows is None else torch.from_numpy(a_rows).to(DEV),
-                     row_scale=None if rs is None else torch.from_numpy(rs).to(DEV), packed=pk)
+                     row_scale=None if rs is None else torch.from_numpy(rs).to(DEV), packed=pk,
+                     ws=workspace(B.moe_expert_ffn_packed_workspace_size(), DEV) if split_ws else None)
     torch.cuda.synchronize()
     a64 = O.widen(a, dtype)
     hg, yg = widen_t(h), widen_t(y)
@@ -482,13 +483,15 @@ PACKED_FFN_CASES = [
                          ids=[f"{c[1]}-{c[3]}x{c[4]}-{len(c[5])}seg" for c in PACKED_FFN_CASES])
 @pytest.mark.parametrize("fused", [False, True])
 def test_expert_ffn_packed_parity(case, fused):
-    """moe_expert_ffn_packed: the packed-weight kernel over hand-picked segments, plain
-    and with the row gather and output row scales."""
+    """moe_expert_ffn_packed: the packed-weight kernels over hand-picked segments, plain
+    and with the row gather and output row scales plus the split workspace (these few
+    tiles leave a partial last round, which then splits along K)."""
     print_case("expert_ffn_packed", case, fused)
     sizes = case[5]
     # the library's rules for the two packed-weight kernels
     assert sum(sizes) >= 256 * len(sizes) or sum(sizes) < 48 * len(sizes)
-    err_h, err_y, err_e2e = _ffn_case(*case, gather=fused, scale=fused, packed=True)
+    err_h, err_y, err_e2e = _ffn_case(*case, gather=fused, scale=fused, packed=True,
+                                      split_ws=fused)
     assert err_h <= TOL["bf16"], f"h error {err_h}"
     assert err_y <= TOL["bf16"], f"y error given h {err_y}"
     assert err_e2e <= TOL["bf16"], f"y error end to end {err_e2e}"
