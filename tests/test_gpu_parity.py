@@ -812,6 +812,12 @@ PACKED_CASES = [
     # capacity 80 over a skewed routing: the dispatch picks the (staged) 32-row tiles on
     # the device, the packed-weight launch exits
     ("switch", dict(n_tokens=4096, d_ff=1024)),
+    # 128 experts at exactly the 256-row threshold (16384 tokens, top-2)
+    ("deepseek", dict(n_tokens=16384, d_model=64, d_ff=128, n_experts=128, top_k=2,
+                      n_shared=0)),
+    # the most experts the library takes, a decode-like batch: 512 segments of ~1 row
+    ("deepseek", dict(n_tokens=64, d_model=256, d_ff=192, n_experts=512, top_k=8,
+                      n_shared=1)),
 ]
 
 
