@@ -64,13 +64,9 @@ def _avg_rows(cfg, capacity: int) -> int:
 
 
 def packed_path(cfg, capacity: int, packed: bool) -> bool:
-    """Whether packed weights reach a routed expert product: bf16, and segments either
-    long (>= PACKED_ROWS: the packed-weight kernel) or short (< SMALL_ROWS: its 32-row
-    variant), both by the library's bound on the kept rows."""
-    if not packed or cfg.dtype != "bf16":
-        return False
-    avg = _avg_rows(cfg, capacity)
-    return avg >= PACKED_ROWS or avg < SMALL_ROWS
+    """Whether the routed expert products read packed weights: every bf16 workload (the
+    library then runs a packed-weight kernel for every segment length)."""
+    return bool(packed) and cfg.dtype == "bf16"
 
 
 def stage_symbol(cfg, stage: str, packed: bool = False, capacity: int = -1):
@@ -85,8 +81,9 @@ def stage_symbol(cfg, stage: str, packed: bool = False, capacity: int = -1):
     avg = _avg_rows(cfg, capacity)
     if avg < SMALL_ROWS:
         return f"gemm_packed_small_kernel<{epi}>" if packed else f"gemm_bf16_kernel<32, {epi}, false>"
-    if packed and avg >= PACKED_ROWS:
-        return f"gemm_packed_kernel<{epi}>"
+    if packed:
+        return (f"gemm_packed_kernel<{epi}>" if avg >= PACKED_ROWS
+                else f"gemm_packed_mid_kernel<{epi}>")
     return f"gemm_bf16_kernel<256, {epi}, false>"
 
 
@@ -347,6 +344,156 @@ def dispatch_copy(layer, x, topk_idx, kept: int, reps: int = 20) -> dict:
                     f"{reps} calls"}
 
 
+def _median(v):
+    v = sorted(v)
+    return v[len(v) // 2] if len(v) % 2 else 0.5 * (v[len(v) // 2 - 1] + v[len(v) // 2])
+
+
+def measure(cfg, dev, steps: int, warmup: int, pack: bool, cold: bool = True) -> dict:
+    """Times `steps` moe_forward calls of one workload (after `warmup` untimed ones) on
+    inputs resident in HBM: wall clock over the steps, per-stage HIP events recorded by
+    the library on the launch stream, the roofline position of every stage kernel.
+    With packed weights (where the library's bound picks a packed-weight kernel, i.e.
+    every bf16 workload) the routed experts' weights are packed once before the warmup
+    and the layer keeps only the packed copy."""
+    import torch
+
+    from sparse_mixture_experts_forward_amd import MoELayer, synth
+    from sparse_mixture_experts_forward_amd import _binding as B
+
+    inp = synth.DeviceInputs(cfg, dev)
+    layer = MoELayer.from_inputs(inp)
+    n = cfg.n_tokens
+    cap = layer.capacity(n)
+    use_packed = packed_path(cfg, cap, pack)
+    pack_ms = None
+    if use_packed:
+        torch.cuda.synchronize()
+        tp = time.perf_counter()
+        layer.pack_weights(drop_unpacked=True)
+        torch.cuda.synchronize()
+        pack_ms = (time.perf_counter() - tp) * 1e3
+    stats = layer.new_stats(n)
+    y = torch.empty_like(inp.x)
+
+    for _ in range(warmup):
+        layer.forward(inp.x, y, stats)
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(B.MOE_N_STAGE_EVENTS)]
+          for _ in range(steps)]
+    for row in ev:  # create the events
+        for e in row:
+            e.record()
+    torch.cuda.synchronize()
+    handles = [[e.cuda_event for e in row] for row in ev]
+
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(steps):
+        layer.forward(inp.x, y, stats, stage_events=handles[i])
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t0
+
+    step_gpu_ms = sum(ev[i][0].elapsed_time(ev[i][-1]) for i in range(steps)) / steps
+    if cfg.n_shared > 0:
+        # the shared experts overlap the routed ones in the timed steps; for per-stage
+        # times a second pass runs them after the routed experts, on the same stream
+        for i in range(steps):
+            layer.forward(inp.x, y, stats, stage_events=handles[i], concurrent_shared=False)
+        torch.cuda.synchronize()
+    stage_ms = {s: 0.0 for s in STAGES}
+    stage_all = {s: [] for s in STAGES}
+    for row in ev:
+        for j, s in enumerate(STAGES):
+            t = row[j].elapsed_time(row[j + 1])
+            stage_ms[s] += t / steps
+            stage_all[s].append(t)
+
+    cold_out = None
+    if cold:
+        # each step preceded by a 1 GiB scratch write (outside the stage events)
+        scratch = torch.empty(1 << 28, dtype=torch.float32, device=dev)
+        cold_all = {s: [] for s in STAGES}
+        cold_step = []
+        for row in ev:
+            scratch.fill_(1.0)
+            layer.forward(inp.x, y, stats, stage_events=[e.cuda_event for e in row])
+        torch.cuda.synchronize()
+        for row in ev:
+            for j, s in enumerate(STAGES):
+                cold_all[s].append(row[j].elapsed_time(row[j + 1]))
+            cold_step.append(row[0].elapsed_time(row[-1]))
+        del scratch
+        cold_out = {"step_ms_median": round(_median(cold_step), 4),
+                    "stages_ms_median": {s: round(_median(v), 5) for s, v in cold_all.items()}}
+
+    kept = int(stats["kept_count"].sum().item())
+    touched = int((stats["kept_count"] > 0).sum().item())
+    work = kernel_work(cfg, kept, touched)
+    kernels = {s: roofline(s, work[s], stage_ms[s], cfg.dtype) for s in STAGES
+               if stage_ms[s] > 0 and (work[s]["flops"] > 0 or work[s]["bytes"] > 0)}
+    for s, r in kernels.items():
+        r["symbol"] = stage_symbol(cfg, s, use_packed, cap)
+        r["traffic"] = stored_traffic(cfg.name, s, r["symbol"])
+    dominant = max(kernels, key=lambda s: stage_ms[s])
+    gemm_ms = stage_ms["gemm1"] + stage_ms["gemm2"] + stage_ms["shared"]
+    gemm_flops = work["gemm1"]["flops"] + work["gemm2"]["flops"] + work["shared"]["flops"]
+    gemm_tflops = gemm_flops / (gemm_ms * 1e-3) / 1e12 if gemm_ms > 0 else 0.0
+    peak = PEAK_BF16_TFLOPS if cfg.dtype == "bf16" else PEAK_F32_TFLOPS
+    disp_gbps = work["dispatch"]["bytes"] / (stage_ms["dispatch"] * 1e-3) / 1e9
+    comb_gbps = (work["combine"]["bytes"] / (stage_ms["combine"] * 1e-3) / 1e9
+                 if stage_ms["combine"] > 0 else None)
+    ms_step = elapsed / steps * 1e3
+    # weights of the experts that kept a row, once per step: what a weight-bound step
+    # must stream from HBM at least
+    es = 2 if cfg.dtype == "bf16" else 4
+    m1 = 3 if cfg.act == "swiglu" else 2
+    touched_bytes = touched * m1 * cfg.d_model * cfg.d_ff * es
+    routed_ms = stage_ms["gemm1"] + stage_ms["gemm2"]
+    out = {
+        "tokens_per_s": round(n * steps / elapsed, 1),
+        "ms_per_step": round(ms_step, 4),
+        "config": {"workload": describe(cfg), "n_tokens": n, "d_model": cfg.d_model,
+                   "d_ff": cfg.d_ff, "n_experts": cfg.n_experts, "top_k": cfg.top_k,
+                   "n_shared": cfg.n_shared, "capacity_factor": cfg.alpha,
+                   "kept_rows": kept, "experts_touched": touched, "capacity": cap,
+                   "n_rerouted": int(stats["n_rerouted"].item()), "fuse": cfg.fuse,
+                   "packed_weights": use_packed,
+                   "pack_ms_once": None if pack_ms is None else round(pack_ms, 2),
+                   "resident_weight_bytes": layer.resident_weight_bytes()},
+        "roofline": kernels[dominant],
+        "grouped_gemm_tflops": round(gemm_tflops, 2),
+        "grouped_gemm_frac_of_peak": round(gemm_tflops / peak, 4),
+        "touched_weight_bytes": touched_bytes,
+        "touched_weight_gbps_step": round(touched_bytes / (ms_step * 1e-3) / 1e9, 1),
+        "touched_weight_gbps_routed_gemms": (round(touched_bytes / (routed_ms * 1e-3) / 1e9, 1)
+                                             if routed_ms > 0 else None),
+        "touched_weight_frac_of_hbm_step": round(touched_bytes / (ms_step * 1e-3) / 1e9
+                                                 / PEAK_HBM_GBPS, 4),
+        "dispatch_gbps": round(disp_gbps, 1),
+        "dispatch_frac_of_hbm": round(disp_gbps / PEAK_HBM_GBPS, 4),
+        "dispatch_note": ("index maps only (capacity ranks, slot and row maps): the kept rows "
+                          "of x are gathered inside gemm1, so no row is copied"
+                          if cfg.fuse & 1 else
+                          "index maps and the permuted copy of the kept rows of x"),
+        "combine_gbps": None if comb_gbps is None else round(comb_gbps, 1),
+        "stages_ms": {s: round(v, 5) for s, v in stage_ms.items()},
+        "stages_note": ("stage times from a pass with the shared experts after the routed "
+                        "ones on one stream; the timed steps overlap them"
+                        if cfg.n_shared > 0 else "stage times of the timed steps"),
+        "stages_ms_median": {s: round(_median(v), 5) for s, v in stage_all.items()},
+        "step_gpu_ms_events": round(step_gpu_ms, 4),
+        "kernels": kernels,
+        "_layer": layer, "_inputs": inp, "_stats": stats,
+    }
+    if cold_out is not None:
+        cm = cold_out["stages_ms_median"]
+        cold_out["dispatch_gbps"] = round(work["dispatch"]["bytes"] / (cm["dispatch"] * 1e-3) / 1e9, 1)
+        if cm["combine"] > 0:
+            cold_out["combine_gbps"] = round(work["combine"]["bytes"] / (cm["combine"] * 1e-3) / 1e9, 1)
+        out["cold"] = cold_out
+    return out
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -375,6 +522,9 @@ def main():
     ap.add_argument("--no-cold", action="store_true",
                     help="skip the cold-cache pass (a 1 GiB scratch write before each step "
                          "evicts L2 and the 256 MB Infinity Cache; stage times only)")
+    ap.add_argument("--workloads", default="switch,deepseek,decode,tiny",
+                    help="comma-separated further workloads measured after the headline one "
+                         "(each with its own timed steps, no CPU baseline); empty: none")
     ap.add_argument("--calibrate-copy-mib", type=int, default=0,
                     help="run only one plain device copy (float32 x * 1) of this many MiB: "
                          "the reference kernel that scales hardware byte counters")
@@ -411,7 +561,7 @@ def main():
         print(json.dumps({"calibration_copy_bytes": args.calibrate_copy_mib << 20}))
         return
 
-    from sparse_mixture_experts_forward_amd import CONFIGS, MoELayer, synth
+    from sparse_mixture_experts_forward_amd import CONFIGS
     from sparse_mixture_experts_forward_amd import _binding as B
 
     B.lib()  # fails loudly if the HIP library is not built
@@ -425,132 +575,43 @@ def main():
     if args.reroute_rounds or args.capacity_rule != "fixed":
         cfg = cfg.scaled(reroute_rounds=args.reroute_rounds, capacity_rule=args.capacity_rule)
     dev = torch.device("cuda:0")
-    inp = synth.DeviceInputs(cfg, dev)
-    layer = MoELayer.from_inputs(inp)
+    m = measure(cfg, dev, args.steps, args.warmup, not args.no_pack, cold=not args.no_cold)
+    layer, inp, stats = m.pop("_layer"), m.pop("_inputs"), m.pop("_stats")
     n = cfg.n_tokens
-    # one-time relayout of the routed experts' weights (moe_pack_weights), outside the
-    # timed region like any other weight preparation; only where the packed-weight
-    # kernel will run
-    use_packed = packed_path(cfg, layer.capacity(n), not args.no_pack)
-    pack_ms = None
-    if use_packed:
-        torch.cuda.synchronize()
-        tp = time.perf_counter()
-        layer.pack_weights()
-        torch.cuda.synchronize()
-        pack_ms = (time.perf_counter() - tp) * 1e3
-    stats = layer.new_stats(n)
-    y = torch.empty_like(inp.x)
-
-    for _ in range(args.warmup):
-        layer.forward(inp.x, y, stats)
-    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(B.MOE_N_STAGE_EVENTS)]
-          for _ in range(args.steps)]
-    for row in ev:  # create the events
-        for e in row:
-            e.record()
-    torch.cuda.synchronize()
-    handles = [[e.cuda_event for e in row] for row in ev]
-
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    for i in range(args.steps):
-        layer.forward(inp.x, y, stats, stage_events=handles[i])
-    torch.cuda.synchronize()
-    elapsed = time.perf_counter() - t0
-
-    stage_ms = {s: 0.0 for s in STAGES}
-    stage_all = {s: [] for s in STAGES}
-    for row in ev:
-        for j, s in enumerate(STAGES):
-            t = row[j].elapsed_time(row[j + 1])
-            stage_ms[s] += t / args.steps
-            stage_all[s].append(t)
-    step_gpu_ms = sum(ev[i][0].elapsed_time(ev[i][-1]) for i in range(args.steps)) / args.steps
-
-    def median(v):
-        v = sorted(v)
-        return v[len(v) // 2] if len(v) % 2 else 0.5 * (v[len(v) // 2 - 1] + v[len(v) // 2])
-
-    cold = None
-    if not args.no_cold:
-        # each step preceded by a 1 GiB scratch write (outside the stage events)
-        scratch = torch.empty(1 << 28, dtype=torch.float32, device=dev)
-        cold_all = {s: [] for s in STAGES}
-        cold_step = []
-        for row in ev:
-            scratch.fill_(1.0)
-            layer.forward(inp.x, y, stats, stage_events=[e.cuda_event for e in row])
-        torch.cuda.synchronize()
-        for row in ev:
-            for j, s in enumerate(STAGES):
-                cold_all[s].append(row[j].elapsed_time(row[j + 1]))
-            cold_step.append(row[0].elapsed_time(row[-1]))
-        del scratch
-        cold = {"step_ms_median": round(median(cold_step), 4),
-                "stages_ms_median": {s: round(median(v), 5) for s, v in cold_all.items()}}
-
-    kept = int(stats["kept_count"].sum().item())
-    touched = int((stats["kept_count"] > 0).sum().item())
-    work = kernel_work(cfg, kept, touched)
-    kernels = {s: roofline(s, work[s], stage_ms[s], cfg.dtype) for s in STAGES
-               if stage_ms[s] > 0 and (work[s]["flops"] > 0 or work[s]["bytes"] > 0)}
-    for s, r in kernels.items():
-        r["symbol"] = stage_symbol(cfg, s, use_packed, layer.capacity(n))
-        r["traffic"] = stored_traffic(cfg.name, s, r["symbol"])
-    dominant = max(kernels, key=lambda s: stage_ms[s])
-    gemm_ms = stage_ms["gemm1"] + stage_ms["gemm2"] + stage_ms["shared"]
-    gemm_flops = work["gemm1"]["flops"] + work["gemm2"]["flops"] + work["shared"]["flops"]
-    gemm_tflops = gemm_flops / (gemm_ms * 1e-3) / 1e12 if gemm_ms > 0 else 0.0
-    peak = PEAK_BF16_TFLOPS if cfg.dtype == "bf16" else PEAK_F32_TFLOPS
-    disp_gbps = work["dispatch"]["bytes"] / (stage_ms["dispatch"] * 1e-3) / 1e9
-    comb_gbps = work["combine"]["bytes"] / (stage_ms["combine"] * 1e-3) / 1e9
-
+    kept = m["config"]["kept_rows"]
     out = {
         "metric": METRIC,
-        "value": round(n * args.steps / elapsed, 1),
+        "value": m["tokens_per_s"],
         "unit": "tokens/s",
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
-        "ms_per_step": round(elapsed / args.steps * 1e3, 4),
+        "ms_per_step": m["ms_per_step"],
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
         "dtype": cfg.dtype,
         "data": "synthetic (seeded counter-based generator; x ~ N(0,1), weights ~ N(0,1/fan_in))",
-        "config": {"workload": describe(cfg), "n_tokens": n, "d_model": cfg.d_model,
-                   "d_ff": cfg.d_ff, "n_experts": cfg.n_experts, "top_k": cfg.top_k,
-                   "n_shared": cfg.n_shared, "capacity_factor": cfg.alpha,
-                   "kept_rows": kept, "experts_touched": touched,
-                   "capacity": layer.capacity(n),
-                   "n_rerouted": int(stats["n_rerouted"].item()), "fuse": cfg.fuse,
-                   "packed_weights": use_packed,
-                   "pack_ms_once": None if pack_ms is None else round(pack_ms, 2)},
-        "roofline": kernels[dominant],
-        "grouped_gemm_tflops": round(gemm_tflops, 2),
-        "grouped_gemm_frac_of_peak": round(gemm_tflops / peak, 4),
-        "dispatch_gbps": round(disp_gbps, 1),
-        "dispatch_frac_of_hbm": round(disp_gbps / PEAK_HBM_GBPS, 4),
-        "dispatch_note": ("index maps only (capacity ranks, slot and row maps): the kept rows "
-                          "of x are gathered inside gemm1, so no row is copied"
-                          if cfg.fuse & 1 else
-                          "index maps and the permuted copy of the kept rows of x"),
-        "combine_gbps": round(comb_gbps, 1),
-        "stages_ms": {s: round(v, 5) for s, v in stage_ms.items()},
-        "stages_ms_median": {s: round(median(v), 5) for s, v in stage_all.items()},
-        "step_gpu_ms_events": round(step_gpu_ms, 4),
-        "kernels": kernels,
     }
+    out.update({k: v for k, v in m.items() if k not in ("tokens_per_s", "ms_per_step")})
     if cfg.fuse & 1 and n > 0 and not args.no_dispatch_copy:
         out["dispatch_copy"] = dispatch_copy(layer, inp.x, stats["topk_idx"], kept)
-    if cold is not None:
-        cm = cold["stages_ms_median"]
-        cold["dispatch_gbps"] = round(work["dispatch"]["bytes"] / (cm["dispatch"] * 1e-3) / 1e9, 1)
-        cold["combine_gbps"] = round(work["combine"]["bytes"] / (cm["combine"] * 1e-3) / 1e9, 1)
-        out["cold"] = cold
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(cfg, inp, stats["logits"], args.cpu_seconds)
+    del layer, inp, stats
+    torch.cuda.empty_cache()
+    # the other workloads, each in the configuration it ships with (no CPU baseline)
+    names = [w for w in (args.workloads.split(",") if args.workloads else []) if w]
+    if names:
+        out["workloads"] = {}
+    for name in names:
+        if name == cfg.name and args.tokens <= 0:
+            continue
+        w = measure(CONFIGS[name], dev, args.steps, args.warmup, not args.no_pack, cold=False)
+        for k in ("_layer", "_inputs", "_stats"):
+            w.pop(k)
+        out["workloads"][name] = w
+        torch.cuda.empty_cache()
     print(json.dumps(out), flush=True)
 
 

@@ -31,7 +31,10 @@
  *   - bf16 data is stored as IEEE bfloat16 (upper 16 bits of a float32).  All products
  *     accumulate in float32.  Rounding to bf16 is round-to-nearest-even.
  *   - Results are deterministic: the same inputs give the same bits on every run.
- *   - Calls on different streams may run concurrently if their buffers do not overlap.
+ *   - The library keeps no state between calls except the thread-local error detail of
+ *     moe_last_error(): no internal streams, events, locks or caches.  Calls on
+ *     different streams may run concurrently if their buffers (workspaces and the
+ *     caller's events included) do not overlap.
  */
 #ifndef MOE_MI355X_H
 #define MOE_MI355X_H
@@ -255,7 +258,9 @@ moe_status moe_dispatch(void* stream, const int32_t* topk_idx, int64_t n_tokens,
  *                seg_offsets[S] <= max_rows.  1 <= S <= MOE_MAX_EXPERTS.
  *   max_rows     upper bound on seg_offsets[S] (sizes the launch; no row beyond it is
  *                touched).
- *   d, d_ff      bf16: both multiples of 64.  float32: both multiples of 4.
+ *   d, d_ff      bf16: both multiples of 64.  float32: both multiples of 4.  One
+ *                expert's weight matrix (d * d_ff elements) below 4 GiB, else
+ *                MOE_ERR_UNSUPPORTED.
  *   w1 [S][d_ff][d]; w3 [S][d_ff][d] (SwiGLU only, else NULL); b1 [S][d_ff] or NULL;
  *   w2 [S][d][d_ff]; b2 [S][d] or NULL.  All in `dtype`.
  *   row_scale    [rows] float32 or NULL: the second layer's output row r is multiplied
@@ -271,12 +276,14 @@ moe_status moe_expert_ffn(void* stream, moe_dtype dtype, moe_act act, const void
                           const float* row_scale, void* h, void* y);
 
 /*
- * moe_expert_ffn_packed -- moe_expert_ffn (bf16 only) that also takes `packed`, the copy
- * of w1/w3/w2 written by moe_pack_weights(act, n_segments, d_model, d_ff, ...) (device,
- * 16-byte aligned, required when max_rows > 0).  Where max_rows averages at least 256
- * rows per segment, or fewer than 48, the expert products read the packed copy (the
- * same h and y as moe_expert_ffn, up to the order of the float32 sums noted below);
- * otherwise w1/w3/w2 as in moe_expert_ffn.
+ * moe_expert_ffn_packed -- moe_expert_ffn (bf16 only) on `packed`, the copy of w1/w3/w2
+ * written by moe_pack_weights(act, n_segments, d_model, d_ff, ...) (device, 16-byte
+ * aligned, required when max_rows > 0), whose size packed_bytes must equal
+ * moe_packed_weights_size(act, n_segments, d_model, d_ff): a copy packed for another
+ * expert count or shape is rejected with MOE_ERR_INVALID_ARG.  Every expert product
+ * reads the packed copy (the same h and y as moe_expert_ffn, up to the order of the
+ * float32 sums noted below), so w1, w3 and w2 may be NULL; when given they are not
+ * read.
  *   ws, ws_bytes: optional device workspace (NULL: none), at least
  *   moe_expert_ffn_packed_workspace_size() bytes for the current device, 256-byte
  *   aligned.  With it, a product whose tiles leave the last round on the GPU mostly idle
@@ -291,8 +298,9 @@ moe_status moe_expert_ffn_packed(void* stream, moe_act act, const void* a,
                                  const int32_t* seg_offsets, int32_t n_segments,
                                  int64_t max_rows, int64_t d_model, int64_t d_ff,
                                  const void* w1, const void* w3, const void* b1, const void* w2,
-                                 const void* b2, const void* packed, const float* row_scale,
-                                 void* h, void* y, void* ws, size_t ws_bytes);
+                                 const void* b2, const void* packed, size_t packed_bytes,
+                                 const float* row_scale, void* h, void* y, void* ws,
+                                 size_t ws_bytes);
 
 /*
  * moe_combine -- routing-weighted sum of the expert rows back into token order
@@ -343,11 +351,27 @@ typedef struct {
   const void* shared_w3;   /* [n_shared][d_ff][d], SwiGLU only */
   const void* shared_w2;   /* [n_shared][d][d_ff] */
   /* Optional (bf16 only): the routed experts' w1/w3/w2 as written by moe_pack_weights
-   * from these same w1/w3/w2.  When given, the expert products over long segments
-   * (>= 256 rows per expert by the library's bound on the kept rows) and over short ones
-   * (< 48) read it instead (same results); w1/w3/w2 stay required for the others. */
+   * (same act, n_experts, d_model, d_ff), and its size in bytes, which must equal
+   * moe_packed_weights_size() for this configuration.  When given, every routed expert
+   * product reads it (same results), and w1, w3 and w2 may be NULL (they are not
+   * read): the layer then needs one copy of the routed experts' weights, not two. */
   const void* packed;
+  size_t packed_bytes;
 } moe_weights;
+
+/* Optional caller-owned resources of moe_forward for running the shared experts
+ * concurrently with the routed ones.  With side_stream set, the shared experts run on
+ * it: fork_event is recorded on `stream` after the dispatch and waited for on
+ * side_stream, join_event is recorded on side_stream after the shared experts and
+ * waited for on `stream` before the combine.  Both events are required then (created
+ * by the caller, e.g. hipEventCreateWithFlags(..., hipEventDisableTiming)); concurrent
+ * calls must not share them.  side_stream NULL (or no moe_streams at all): everything
+ * runs on `stream`, in order. */
+typedef struct {
+  void* side_stream; /* hipStream_t or NULL */
+  void* fork_event;  /* hipEvent_t */
+  void* join_event;  /* hipEvent_t */
+} moe_streams;
 
 /*
  * moe_pack_weights -- a one-time copy of the routed experts' weights in the order the
@@ -394,8 +418,8 @@ typedef struct {
   /* Timing markers (hipEvent_t handles owned by the caller, or NULL): stage_events[i]
    * is recorded on the stream at boundary i -- 0 before routing, 1 after routing and
    * its statistics, 2 after dispatch, 3 after the routed first expert layer, 4 after
-   * the routed second expert layer, 5 once the shared experts are also done (they run
-   * concurrently, see moe_forward), 6 after the combine. */
+   * the routed second expert layer, 5 once the shared experts are also done (they may
+   * run concurrently, see moe_streams), 6 after the combine. */
   void* stage_events[MOE_N_STAGE_EVENTS];
 } moe_stats;
 
@@ -407,23 +431,21 @@ typedef struct {
  * ([Why-MoE] §3 MoELayer.forward, [DeepSeek-V2] §2.2-§2.3), with every intermediate in
  * `ws`.  x [N][d] and y [N][d] are in cfg->dtype; y may not alias x.
  * Supported: bf16 with d % 64 == 0 and d_ff % 64 == 0, or float32 with d % 4 == 0 and
- * d_ff % 4 == 0; 1 <= k <= min(E, 16); E <= MOE_MAX_EXPERTS.
+ * d_ff % 4 == 0; 1 <= k <= min(E, 16); E <= MOE_MAX_EXPERTS; the shared experts'
+ * first-layer weights (n_shared * d_ff * d elements) below 4 GiB.
  * ws: at least moe_forward_workspace_size(cfg) bytes, 256-byte aligned.
  * Streams: all work is ordered after earlier work on `stream`, and work enqueued on
- * `stream` afterwards sees every output.  With shared experts the library forks them
- * onto an internal stream of the current device (default priority, created on the
- * first such call and kept until the process ends) and joins it back before the
- * combine, using events; calls from several host threads are serialised while they
- * enqueue.
+ * `stream` afterwards sees every output.  streams (or NULL): the caller's side stream
+ * and events for the shared experts (see moe_streams); without them the shared
+ * experts run on `stream` after the routed ones.
  * Graph capture: the call allocates nothing, waits for nothing on the host and clears
  * no memory with memset, so it can be captured into a HIP graph on `stream` and
- * replayed (the internal stream joins the capture through the fork event).  Make one
- * call with shared experts outside the capture first: it creates that stream.
+ * replayed (a side stream joins the capture through the fork event).
  */
 size_t moe_forward_workspace_size(const moe_config* cfg);
 moe_status moe_forward(void* stream, const moe_config* cfg, const moe_weights* w,
-                       const void* x, void* y, const moe_stats* out, void* ws,
-                       size_t ws_bytes);
+                       const void* x, void* y, const moe_stats* out,
+                       const moe_streams* streams, void* ws, size_t ws_bytes);
 
 /* Static description of a status code. */
 const char* moe_status_string(moe_status s);

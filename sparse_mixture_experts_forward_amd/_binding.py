@@ -44,7 +44,12 @@ class MoEConfigC(C.Structure):
 class MoEWeightsC(C.Structure):
     _fields_ = [(n, C.c_void_p) for n in ("w_router", "logit_bias", "w1", "w3", "b1", "w2",
                                           "b2", "shared_w1", "shared_w3", "shared_w2",
-                                          "packed")]
+                                          "packed")] + [("packed_bytes", C.c_size_t)]
+
+
+class MoEStreamsC(C.Structure):
+    _fields_ = [("side_stream", C.c_void_p), ("fork_event", C.c_void_p),
+                ("join_event", C.c_void_p)]
 
 
 MOE_N_STAGE_EVENTS = 7
@@ -77,12 +82,12 @@ _SIGS = {
                                  _I64, _VP, _VP, _VP, _VP, _VP, _VP, _VP, _VP]),
     "moe_expert_ffn_packed_workspace_size": (_SZ, []),
     "moe_expert_ffn_packed": (C.c_int, [_VP, C.c_int, _VP, _VP, _I64, _VP, _I32, _I64, _I64,
-                                        _I64, _VP, _VP, _VP, _VP, _VP, _VP, _VP, _VP, _VP,
+                                        _I64, _VP, _VP, _VP, _VP, _VP, _VP, _SZ, _VP, _VP, _VP,
                                         _VP, _SZ]),
     "moe_combine": (C.c_int, [_VP, C.c_int, _VP, _VP, _VP, _I64, _I32, _I64, _VP, _VP]),
     "moe_forward_workspace_size": (_SZ, [C.POINTER(MoEConfigC)]),
     "moe_forward": (C.c_int, [_VP, C.POINTER(MoEConfigC), C.POINTER(MoEWeightsC), _VP, _VP,
-                              C.POINTER(MoEStatsC), _VP, _SZ]),
+                              C.POINTER(MoEStatsC), C.POINTER(MoEStreamsC), _VP, _SZ]),
     "moe_packed_weights_size": (_SZ, [C.c_int, _I32, _I64, _I64]),
     "moe_pack_weights": (C.c_int, [_VP, C.c_int, _I32, _I64, _I64, _VP, _VP, _VP, _VP]),
     "moe_status_string": (C.c_char_p, [C.c_int]),
@@ -221,17 +226,21 @@ def moe_expert_ffn_packed_workspace_size() -> int:
 
 
 def moe_expert_ffn(act: int, a, seg_offsets, n_segments: int, max_rows: int, w1, w3, b1, w2,
-                   b2, h, y, stream=None, a_rows=None, row_scale=None, packed=None, ws=None):
+                   b2, h, y, stream=None, a_rows=None, row_scale=None, packed=None, ws=None,
+                   d_ff: Optional[int] = None, packed_bytes: Optional[int] = None):
     """packed (bf16): the moe_pack_weights copy of w1/w3/w2 -> moe_expert_ffn_packed, with
-    the optional split workspace ws."""
+    the optional split workspace ws (w1/w3/w2 may then be None; d_ff is taken from h).
+    packed_bytes defaults to the packed tensor's size."""
     d = a.shape[1]
-    d_ff = w1.shape[-2]
+    if d_ff is None:
+        d_ff = h.shape[1] if w1 is None else w1.shape[-2]
     if packed is not None:
+        nbytes = _ws_bytes(packed) if packed_bytes is None else packed_bytes
         st = lib().moe_expert_ffn_packed(_stream(stream), act, _ptr(a), _ptr(a_rows), a.shape[0],
                                          _ptr(seg_offsets), n_segments, max_rows, d, d_ff,
                                          _ptr(w1), _ptr(w3), _ptr(b1), _ptr(w2), _ptr(b2),
-                                         _ptr(packed), _ptr(row_scale), _ptr(h), _ptr(y),
-                                         _ptr(ws), _ws_bytes(ws))
+                                         _ptr(packed), nbytes, _ptr(row_scale), _ptr(h),
+                                         _ptr(y), _ptr(ws), _ws_bytes(ws))
         _check("moe_expert_ffn_packed", st)
         return
     st = lib().moe_expert_ffn(_stream(stream), _dtype(a), act, _ptr(a), _ptr(a_rows),
@@ -274,14 +283,22 @@ def moe_forward_workspace_size(cfg: MoEConfigC) -> int:
 
 
 def moe_forward(cfg: MoEConfigC, weights: dict, x, y, ws, stats: Optional[dict] = None,
-                stream=None, stage_events=None):
+                stream=None, stage_events=None, side=None):
     """stage_events: optional sequence of MOE_N_STAGE_EVENTS raw hipEvent_t handles (int)
-    or None entries."""
-    w = MoEWeightsC(**{k: _ptr(v) for k, v in weights.items()})
+    or None entries.  side: optional (side_stream, fork_event, join_event) raw handles
+    (int) for running the shared experts concurrently (moe_streams).  weights["packed"]
+    (optional): the packed copy; its byte size is passed as packed_bytes."""
+    w = MoEWeightsC(**{k: _ptr(v) for k, v in weights.items() if k != "packed_bytes"})
+    if weights.get("packed") is not None:
+        w.packed_bytes = weights.get("packed_bytes") or _ws_bytes(weights["packed"])
     s = MoEStatsC(**{k: _ptr(v) for k, v in (stats or {}).items() if k in STAT_FIELDS})
     if stage_events is not None:
         for i, ev in enumerate(stage_events):
             s.stage_events[i] = ev
+    sides = None
+    if side is not None:
+        sides = MoEStreamsC(*side)
     st = lib().moe_forward(_stream(stream), C.byref(cfg), C.byref(w), _ptr(x), _ptr(y),
-                           C.byref(s), _ptr(ws), _ws_bytes(ws))
+                           C.byref(s), C.byref(sides) if sides is not None else None,
+                           _ptr(ws), _ws_bytes(ws))
     _check("moe_forward", st)

@@ -30,7 +30,7 @@ class MoEConfig:
     alpha: Optional[float] = None  # capacity factor, None = unlimited
     expert_bias: bool = False  # b1/b2 on the expert linears
     n_shared: int = 0
-    logit_bias: str = "none"  # "none" | "skew4" (+2.0 on experts 0..3) | "uniform0.1"
+    logit_bias: str = "none"  # "none" | "skew4" (+2.0 on experts 0..3) | "uniform0.1" | "skew0" (+4.0 on expert 0)
     renormalize: bool = True
     bias_selection_only: bool = False  # the logit bias steers selection only (V3 scheme)
     capacity_rule: str = "fixed"  # "fixed" (alpha) | "linear" | "log" (batch-dependent)

@@ -6,8 +6,6 @@
 #include <cstdarg>
 #include <cstdio>
 #include <functional>
-#include <mutex>
-#include <unordered_map>
 
 #include "../../include/moe.h"
 #include "kernels.h"
@@ -225,6 +223,10 @@ moe_status check_ffn_shape(moe_dtype dt, moe_act act, int64_t d, int64_t d_ff) {
     return fail(MOE_ERR_UNSUPPORTED, "d_model and d_ff must be multiples of %lld for this dtype",
                 static_cast<long long>(q));
   if (d > (1 << 20) || d_ff > (1 << 20)) return fail(MOE_ERR_UNSUPPORTED, "d_model or d_ff too large");
+  // the expert kernels address a weight row with a 32-bit byte offset from the expert's
+  // base: one expert's matrix must stay below 4 GiB
+  if (d * d_ff * static_cast<int64_t>(elem_size(dt)) > UINT32_MAX)
+    return fail(MOE_ERR_UNSUPPORTED, "one expert's weights (d_model * d_ff) must be below 4 GiB");
   return MOE_OK;
 }
 
@@ -279,31 +281,6 @@ moe_status run_ffn(hipStream_t st, moe_dtype dt, moe_act act, const void* a, int
     g2.bp_seg_stride = g2.bp_rows * d_ff * 2;
   }
   return hip_check(moe::launch_gemm(st, bf, moe::EPI_NONE, g2, max_rows), "expert GEMM2 launch");
-}
-
-// A second stream per device (default priority, created on first use) on which the
-// shared experts run concurrently with the router, dispatch and routed experts: they
-// depend on x only.  The fork and join events are reused, so their use is serialised
-// by `mu` for as long as a call enqueues work.
-struct SideStream {
-  hipStream_t s = nullptr;
-  hipEvent_t fork = nullptr, join = nullptr;
-};
-
-std::mutex g_side_mu;
-
-moe_status side_stream(SideStream** out) {
-  static std::unordered_map<int, SideStream> by_dev;
-  int dev = 0;
-  MOE_TRY(hip_check(hipGetDevice(&dev), "hipGetDevice"));
-  SideStream& ss = by_dev[dev];
-  if (!ss.s) {
-    MOE_TRY(hip_check(hipStreamCreateWithFlags(&ss.s, hipStreamNonBlocking), "side stream create"));
-    MOE_TRY(hip_check(hipEventCreateWithFlags(&ss.fork, hipEventDisableTiming), "event create"));
-    MOE_TRY(hip_check(hipEventCreateWithFlags(&ss.join, hipEventDisableTiming), "event create"));
-  }
-  *out = &ss;
-  return MOE_OK;
 }
 
 // Batch-dependent capacities: [MoE-2pct] §5.3 (factor 1 + 0.5 min(1, N/256) inside
@@ -428,6 +405,26 @@ moe_status check_config(const moe_config* c) {
     return fail(MOE_ERR_UNSUPPORTED, "n_tokens * top_k too large");
   if (c->n_tokens * static_cast<int64_t>(c->n_shared) * c->d_ff > INT32_MAX)
     return fail(MOE_ERR_UNSUPPORTED, "shared hidden activations too large");
+  // the shared experts run as one FFN of width n_shared * d_ff, whose first-layer
+  // weight rows are addressed with 32-bit byte offsets
+  if (static_cast<int64_t>(c->n_shared) * c->d_ff * c->d_model *
+          static_cast<int64_t>(elem_size(c->dtype)) > UINT32_MAX)
+    return fail(MOE_ERR_UNSUPPORTED, "shared experts' weights (n_shared * d_ff * d_model) must be below 4 GiB");
+  return MOE_OK;
+}
+
+// The packed copy must be the one moe_pack_weights writes for this shape: its second
+// layer starts after n_seg experts' first layers.
+moe_status check_packed(const void* packed, size_t packed_bytes, moe_act act, int32_t n_seg,
+                        int64_t d, int64_t d_ff) {
+  MOE_TRY(check_aligned(packed, 16, "packed"));
+  const size_t want = static_cast<size_t>(n_seg) *
+                      static_cast<size_t>(moe::packed_w1_bytes(act == MOE_ACT_SWIGLU, d, d_ff) +
+                                          moe::packed_w2_bytes(d, d_ff));
+  if (packed_bytes != want)
+    return fail(MOE_ERR_INVALID_ARG,
+                "packed_bytes is %zu, but the packed copy of %d experts of this shape is %zu bytes",
+                packed_bytes, n_seg, want);
   return MOE_OK;
 }
 
@@ -585,11 +582,13 @@ moe_status moe_dispatch(void* stream, const int32_t* topk_idx, int64_t n_tokens,
 
 namespace {
 
-// Argument checks shared by moe_expert_ffn and moe_expert_ffn_packed.
+// Argument checks shared by moe_expert_ffn and moe_expert_ffn_packed (packed: w1, w3
+// and w2 are not read and may be NULL).
 moe_status check_ffn_args(moe_dtype dtype, moe_act act, const void* a, const int32_t* a_rows,
                           int64_t a_n_rows, const int32_t* seg_offsets, int32_t n_segments,
                           int64_t max_rows, int64_t d_model, int64_t d_ff, const void* w1,
-                          const void* w3, const void* w2, const void* h, const void* y) {
+                          const void* w3, const void* w2, const void* h, const void* y,
+                          bool packed = false) {
   MOE_TRY(check_ffn_shape(dtype, act, d_model, d_ff));
   if (a_rows && (a_n_rows < 1 || a_n_rows * d_model * static_cast<int64_t>(elem_size(dtype)) > UINT32_MAX))
     return fail(MOE_ERR_UNSUPPORTED, "with a_rows, a must have 1 .. 4 GiB / row bytes rows");
@@ -598,13 +597,16 @@ moe_status check_ffn_args(moe_dtype dtype, moe_act act, const void* a, const int
   if (max_rows < 0) return fail(MOE_ERR_INVALID_ARG, "max_rows < 0");
   if (max_rows > INT32_MAX / 2) return fail(MOE_ERR_UNSUPPORTED, "max_rows too large");
   if (max_rows == 0) return MOE_OK;
-  if (!a || !seg_offsets || !w1 || !w2 || !h || !y)
-    return fail(MOE_ERR_INVALID_ARG, "a, seg_offsets, w1, w2, h and y are required");
-  if (act == MOE_ACT_SWIGLU && !w3) return fail(MOE_ERR_INVALID_ARG, "SwiGLU needs w3");
+  if (!a || !seg_offsets || !h || !y)
+    return fail(MOE_ERR_INVALID_ARG, "a, seg_offsets, h and y are required");
   MOE_TRY(check_aligned(a, 16, "a"));
-  MOE_TRY(check_aligned(w1, 16, "w1"));
-  MOE_TRY(check_aligned(w2, 16, "w2"));
-  if (w3) MOE_TRY(check_aligned(w3, 16, "w3"));
+  if (!packed) {
+    if (!w1 || !w2) return fail(MOE_ERR_INVALID_ARG, "w1 and w2 are required");
+    if (act == MOE_ACT_SWIGLU && !w3) return fail(MOE_ERR_INVALID_ARG, "SwiGLU needs w3");
+    MOE_TRY(check_aligned(w1, 16, "w1"));
+    MOE_TRY(check_aligned(w2, 16, "w2"));
+    if (w3) MOE_TRY(check_aligned(w3, 16, "w3"));
+  }
   MOE_TRY(check_aligned(h, 16, "h"));
   MOE_TRY(check_aligned(y, 16, "y"));
   return MOE_OK;
@@ -640,13 +642,14 @@ moe_status moe_expert_ffn_packed(void* stream, moe_act act, const void* a,
                                  const int32_t* seg_offsets, int32_t n_segments,
                                  int64_t max_rows, int64_t d_model, int64_t d_ff,
                                  const void* w1, const void* w3, const void* b1, const void* w2,
-                                 const void* b2, const void* packed, const float* row_scale,
-                                 void* h, void* y, void* ws, size_t ws_bytes) {
+                                 const void* b2, const void* packed, size_t packed_bytes,
+                                 const float* row_scale, void* h, void* y, void* ws,
+                                 size_t ws_bytes) {
   MOE_TRY(check_ffn_args(MOE_BF16, act, a, a_rows, a_n_rows, seg_offsets, n_segments, max_rows,
-                         d_model, d_ff, w1, w3, w2, h, y));
+                         d_model, d_ff, w1, w3, w2, h, y, true));
   if (max_rows == 0) return MOE_OK;
   if (!packed) return fail(MOE_ERR_INVALID_ARG, "packed is required");
-  MOE_TRY(check_aligned(packed, 16, "packed"));
+  MOE_TRY(check_packed(packed, packed_bytes, act, n_segments, d_model, d_ff));
   // with a workspace, a partial last round of the expert products splits along K
   int split_g = 0;
   float* split_buf = nullptr;
@@ -721,14 +724,29 @@ size_t moe_forward_workspace_size(const moe_config* cfg) {
 }
 
 moe_status moe_forward(void* stream, const moe_config* cfg, const moe_weights* w,
-                       const void* x, void* y, const moe_stats* out, void* ws,
-                       size_t ws_bytes) {
+                       const void* x, void* y, const moe_stats* out,
+                       const moe_streams* streams, void* ws, size_t ws_bytes) {
   MOE_TRY(check_config(cfg));
   if (!w) return fail(MOE_ERR_INVALID_ARG, "weights are NULL");
   const moe_config& c = *cfg;
   const bool swiglu = c.act == MOE_ACT_SWIGLU;
-  if (!w->w_router || !w->w1 || !w->w2 || (swiglu && !w->w3))
-    return fail(MOE_ERR_INVALID_ARG, "w_router, w1, w2 (and w3 for SwiGLU) are required");
+  if (!w->w_router) return fail(MOE_ERR_INVALID_ARG, "w_router is required");
+  if (w->packed && c.dtype != MOE_BF16)
+    return fail(MOE_ERR_UNSUPPORTED, "packed weights are bf16 only");
+  if (w->packed) {
+    MOE_TRY(check_packed(w->packed, w->packed_bytes, c.act, c.n_experts, c.d_model, c.d_ff));
+  } else if (!w->w1 || !w->w2 || (swiglu && !w->w3)) {
+    return fail(MOE_ERR_INVALID_ARG, "w1, w2 (and w3 for SwiGLU) are required without packed weights");
+  }
+  hipStream_t side = nullptr;
+  hipEvent_t fork_ev = nullptr, join_ev = nullptr;
+  if (streams && streams->side_stream && streams->side_stream != stream) {
+    if (!streams->fork_event || !streams->join_event)
+      return fail(MOE_ERR_INVALID_ARG, "a side stream needs fork_event and join_event");
+    side = static_cast<hipStream_t>(streams->side_stream);
+    fork_ev = static_cast<hipEvent_t>(streams->fork_event);
+    join_ev = static_cast<hipEvent_t>(streams->join_event);
+  }
   if (c.n_shared > 0 && (!w->shared_w1 || !w->shared_w2 || (swiglu && !w->shared_w3)))
     return fail(MOE_ERR_INVALID_ARG, "shared expert weights are required when n_shared > 0");
   if (c.n_tokens > 0 && (!x || !y)) return fail(MOE_ERR_INVALID_ARG, "x and y are required");
@@ -741,10 +759,7 @@ moe_status moe_forward(void* stream, const moe_config* cfg, const moe_weights* w
     MOE_TRY(check_aligned(x, 16, "x"));
     MOE_TRY(check_aligned(y, 16, "y"));
   }
-  if (w->packed && c.dtype != MOE_BF16)
-    return fail(MOE_ERR_UNSUPPORTED, "packed weights are bf16 only");
-  const void* wptrs[] = {w->w1, w->w2, w->w3, w->shared_w1, w->shared_w2, w->shared_w3,
-                         w->packed};
+  const void* wptrs[] = {w->w1, w->w2, w->w3, w->shared_w1, w->shared_w2, w->shared_w3};
   for (const void* p : wptrs)
     if (p) MOE_TRY(check_aligned(p, 16, "expert weights"));
 
@@ -791,22 +806,22 @@ moe_status moe_forward(void* stream, const moe_config* cfg, const moe_weights* w
                        o.monitor ? o.monitor + 4 : nullptr, reroute ? nullptr : o.n_rerouted,
                        cap >= 0 ? L.small_tiles : nullptr));
   MOE_TRY(mark(2));
-  // a8 (forked): shared experts, all tokens, on the side stream, concurrent with the
-  // routed experts (forked after the latency-bound router and dispatch, whose few
-  // workgroups would otherwise wait behind its tiles); the S experts act as one FFN of
-  // width S*d_ff (W1/W3 rows concatenate, W2 splits its reduction into S chunks of d_ff)
-  SideStream* side = nullptr;
-  std::unique_lock<std::mutex> side_lock(g_side_mu, std::defer_lock);
-  if (c.n_shared > 0 && n > 0) {
-    side_lock.lock();
-    MOE_TRY(side_stream(&side));
-    MOE_TRY(hip_check(hipEventRecord(side->fork, st), "fork event record"));
-    MOE_TRY(hip_check(hipStreamWaitEvent(side->s, side->fork, 0), "fork wait"));
-    const int64_t dffs = c.d_ff * c.n_shared;
-    MOE_TRY(run_ffn(side->s, c.dtype, c.act, x, c.d_model, nullptr, 1, static_cast<int32_t>(n), n,
-                    c.d_model, dffs, w->shared_w1, w->shared_w3, nullptr, 0, w->shared_w2,
-                    nullptr, c.d_ff, c.d_model * c.d_ff, L.h_sh, L.y_sh, nullptr));
-    MOE_TRY(hip_check(hipEventRecord(side->join, side->s), "join event record"));
+  // a8: shared experts, all tokens; the S experts act as one FFN of width S*d_ff (W1/W3
+  // rows concatenate, W2 splits its reduction into S chunks of d_ff).  On the caller's
+  // side stream they run concurrently with the routed experts (forked after the
+  // latency-bound router and dispatch, whose few workgroups would otherwise wait
+  // behind its tiles); without one, after the routed experts on `stream`.
+  const bool shared = c.n_shared > 0 && n > 0;
+  auto run_shared = [&](hipStream_t s) {
+    return run_ffn(s, c.dtype, c.act, x, c.d_model, nullptr, 1, static_cast<int32_t>(n), n,
+                   c.d_model, c.d_ff * c.n_shared, w->shared_w1, w->shared_w3, nullptr, 0,
+                   w->shared_w2, nullptr, c.d_ff, c.d_model * c.d_ff, L.h_sh, L.y_sh, nullptr);
+  };
+  if (shared && side) {
+    MOE_TRY(hip_check(hipEventRecord(fork_ev, st), "fork event record"));
+    MOE_TRY(hip_check(hipStreamWaitEvent(side, fork_ev, 0), "fork wait"));
+    MOE_TRY(run_shared(side));
+    MOE_TRY(hip_check(hipEventRecord(join_ev, side), "join event record"));
   }
   const int64_t R = max_rows_of(n, e, k, cap);
   // a6-a7: routed experts over the expert-major segments; fused, GEMM1 gathers the rows
@@ -820,8 +835,9 @@ moe_status moe_forward(void* stream, const moe_config* cfg, const moe_weights* w
                   // then picks the tile height
                   cap >= 0 ? L.small_tiles : nullptr, w->packed));
   MOE_TRY(mark(4));
-  // join: the combine needs the shared experts' output
-  if (side) MOE_TRY(hip_check(hipStreamWaitEvent(st, side->join, 0), "join wait"));
+  // the combine needs the shared experts' output
+  if (shared && side) MOE_TRY(hip_check(hipStreamWaitEvent(st, join_ev, 0), "join wait"));
+  if (shared && !side) MOE_TRY(run_shared(st));
   MOE_TRY(mark(5));
   // a9: weighted combine (shared first, then slots in order)
   MOE_TRY(hip_check(moe::launch_combine(st, c.dtype == MOE_BF16, L.y_rows, slot_row,

@@ -586,6 +586,10 @@ __device__ __forceinline__ void tile_epilogue(const GemmArgs& g, const Tile& til
   const int frow = S::row(lane);
   uint16_t* __restrict__ C = static_cast<uint16_t*>(g.c);
   constexpr int NQ = S::ACC / 4;
+  // output row of tile row m (c_rows: the token's own row), looked up at each store
+  auto orow = [&](int m) -> int64_t {
+    return g.c_rows ? static_cast<int64_t>(g.c_rows[tile.row0 + m]) : tile.row0 + m;
+  };
   if constexpr (EPI == EPI_SWIGLU) {
 #pragma unroll
     for (int tn = T0; tn < T1; ++tn) {
@@ -600,7 +604,7 @@ __device__ __forceinline__ void tile_epilogue(const GemmArgs& g, const Tile& til
 #pragma unroll
             for (int r = 0; r < 4; ++r)
               v[r] = silu(acc[tn][tm][4 * q + r]) * acc[tn + TN / 2][tm][4 * q + r];
-            *reinterpret_cast<uint2*>(C + (tile.row0 + m) * g.ldc + col) =
+            *reinterpret_cast<uint2*>(C + orow(m) * g.ldc + col) =
                 pack_bf16x4(v[0], v[1], v[2], v[3]);
           }
         }
@@ -636,7 +640,7 @@ __device__ __forceinline__ void tile_epilogue(const GemmArgs& g, const Tile& til
               if (EPI == EPI_GELU) v[r] = gelu_erf(v[r]);
               v[r] *= sc[tm];  // exact when 1
             }
-            *reinterpret_cast<uint2*>(C + (tile.row0 + m) * g.ldc + col) =
+            *reinterpret_cast<uint2*>(C + orow(m) * g.ldc + col) =
                 pack_bf16x4(v[0], v[1], v[2], v[3]);
           }
         }
@@ -998,23 +1002,30 @@ __device__ __forceinline__ void pk_tail(const PackedIO& io, uint16_t* const (&A)
   }
 }
 
-// Epilogue: register 4q + r of acc[tn][tm] is activation row tm*32 + lane%32 of the
-// tile and packed weight row tn*32 + 8q + 4(lane/32) + r of the wave's panel p; the
-// four r are consecutive output columns (one 8-byte store).
-// TN0 .. TN1-1 restrict the epilogue to those weight tiles (SwiGLU: of the W1 tiles
-// 0, 1, each with its W3 tile tn + 2), TM0 .. TM1-1 to those row blocks; default all.
-template <int EPI, int TA, int TN0 = 0, int TN1 = (EPI == EPI_SWIGLU ? 2 : 4), int TM0 = 0,
-          int TM1 = TA>
+// Epilogue of the packed-weight kernels: register 4q + r of acc[tn][tm] is activation
+// row tm*32 + lane%32 of the tile and output column col0 + tn*32 + 8q + 4(lane/32) + r
+// (SwiGLU: tn < NTW/2 are W1 tiles, each paired with the W3 tile tn + NTW/2 of the
+// same columns); the four r are consecutive output columns (one 8-byte store).
+// TN0 .. TN1-1 restrict the epilogue to those tiles (SwiGLU: W1 tiles), TM0 .. TM1-1 to
+// those row blocks; default all.  With g.c_rows the output row of tile row m is
+// c_rows[row0 + m] (rows written straight into their token's row), else row0 + m.
+template <int EPI, int NTW, int TMAX, int TA, int TN0 = 0,
+          int TN1 = (EPI == EPI_SWIGLU ? NTW / 2 : NTW), int TM0 = 0, int TM1 = TA>
 __device__ __forceinline__ void packed_epilogue(const GemmArgs& g, const Tile& tile, int lane,
-                                                int p, f32x16_t (&acc)[4][4]) {
+                                                int col0, f32x16_t (&acc)[NTW][TMAX]) {
   uint16_t* __restrict__ C = static_cast<uint16_t*>(g.c);
   const int frow = lane & 31;
+  // (the output row is looked up at each store: kept live across the epilogue, the
+  // rows would add to the register pressure of the accumulators)
+  auto orow = [&](int m) -> int64_t {
+    return g.c_rows ? static_cast<int64_t>(g.c_rows[tile.row0 + m]) : tile.row0 + m;
+  };
   if constexpr (EPI == EPI_SWIGLU) {
 #pragma unroll
     for (int tn = TN0; tn < TN1; ++tn)
 #pragma unroll
       for (int q = 0; q < 4; ++q) {
-        const int col = p * 64 + tn * 32 + Mfma<32>::ni(q, lane);
+        const int col = col0 + tn * 32 + Mfma<32>::ni(q, lane);
         if (col >= g.n_out) continue;
 #pragma unroll
         for (int tm = TM0; tm < TM1; ++tm) {
@@ -1023,8 +1034,8 @@ __device__ __forceinline__ void packed_epilogue(const GemmArgs& g, const Tile& t
             float v[4];
 #pragma unroll
             for (int r = 0; r < 4; ++r)
-              v[r] = silu(acc[tn][tm][4 * q + r]) * acc[tn + 2][tm][4 * q + r];
-            *reinterpret_cast<uint2*>(C + (tile.row0 + m) * g.ldc + col) =
+              v[r] = silu(acc[tn][tm][4 * q + r]) * acc[tn + NTW / 2][tm][4 * q + r];
+            *reinterpret_cast<uint2*>(C + orow(m) * g.ldc + col) =
                 pack_bf16x4(v[0], v[1], v[2], v[3]);
           }
         }
@@ -1041,7 +1052,7 @@ __device__ __forceinline__ void packed_epilogue(const GemmArgs& g, const Tile& t
     for (int tn = TN0; tn < TN1; ++tn)
 #pragma unroll
       for (int q = 0; q < 4; ++q) {
-        const int col = p * 128 + tn * 32 + Mfma<32>::ni(q, lane);
+        const int col = col0 + tn * 32 + Mfma<32>::ni(q, lane);
         if (col >= g.n_out) continue;
         float bv[4] = {0.f, 0.f, 0.f, 0.f};
         if (bias != nullptr) {
@@ -1059,13 +1070,19 @@ __device__ __forceinline__ void packed_epilogue(const GemmArgs& g, const Tile& t
               if (EPI == EPI_GELU) v[r] = gelu_erf(v[r]);
               v[r] *= sc[tm];  // exact when 1
             }
-            *reinterpret_cast<uint2*>(C + (tile.row0 + m) * g.ldc + col) =
+            *reinterpret_cast<uint2*>(C + orow(m) * g.ldc + col) =
                 pack_bf16x4(v[0], v[1], v[2], v[3]);
           }
         }
       }
   }
 }
+
+// Output column of the first accumulator tile of a packed kernel's wave whose weight
+// panel is p (128 packed rows).  SwiGLU panels hold 64 output columns (64 W1 rows, then
+// the same 64 of W3), others 128.
+template <int EPI>
+__device__ __forceinline__ int panel_col0(int p) { return p * (EPI == EPI_SWIGLU ? 64 : 128); }
 
 // Partial accumulators of a split packed tile (a slot of gemm_split_floats' 65536
 // floats per part): float4 chunk c of thread t at [c][t], c = (tn*4 + tm)*4 + v.
@@ -1134,7 +1151,7 @@ __device__ __forceinline__ void packed_body(const GemmArgs& g, const Tile& tile,
     packed_split_store<TA>(g, tile, acc);
     return;
   }
-  packed_epilogue<EPI, TA>(g, tile, lane, p, acc);
+  packed_epilogue<EPI, 4, 4, TA>(g, tile, lane, panel_col0<EPI>(p), acc);
 }
 
 template <int EPI>
@@ -1239,11 +1256,12 @@ __device__ __forceinline__ void packed_finish(const GemmArgs& g, const Tile& til
         }
     }
   }
-  // (TA = 4 only sizes the epilogue's row-scale array; the row block is TM)
+  // (TA = 4 only sizes the epilogue's per-row arrays; the row block is TM)
   if constexpr (EPI == EPI_SWIGLU)
-    packed_epilogue<EPI, 4, H, H + 1, TM, TM + 1>(g, tile, lane, p, acc);
+    packed_epilogue<EPI, 4, 4, 4, H, H + 1, TM, TM + 1>(g, tile, lane, panel_col0<EPI>(p), acc);
   else
-    packed_epilogue<EPI, 4, 2 * H, 2 * H + 2, TM, TM + 1>(g, tile, lane, p, acc);
+    packed_epilogue<EPI, 4, 4, 4, 2 * H, 2 * H + 2, TM, TM + 1>(g, tile, lane, panel_col0<EPI>(p),
+                                                               acc);
 }
 
 template <int EPI>
@@ -1426,7 +1444,212 @@ __global__ __launch_bounds__(kThreads, 2) void gemm_packed_small_kernel(GemmArgs
   for (; t0 + kSRing <= io.KS; t0 += kSRing) ps_period<0>(io, t0, wr, ar, acc);
   ps_tail<0>(io, t0, io.KS - t0, wr, ar, acc);
   __builtin_amdgcn_s_waitcnt(0);
-  packed_epilogue<EPI, 1>(g, tile, lane, p, acc);
+  packed_epilogue<EPI, 4, 4, 1>(g, tile, lane, panel_col0<EPI>(p), acc);
+}
+
+// ------------------------------------------------------------------ packed-weight kernel, mid-size segments
+// Segments of a few dozen to a few hundred rows (fine-grained experts, capacity-limited
+// batches): the products are bound by the weight stream, so every (segment, column
+// tile) is one work item that reads its weights once.  A tile is up to 256 activation
+// rows (a whole segment of up to 256 rows) x 256 packed weight rows; each of the 4 waves
+// streams 64 weight rows of its own (SwiGLU: 32 rows of W1 and the same 32 of W3) from
+// the packed copy into a register ring (each k-step's 2 fragments loaded 15 k-steps
+// ahead) and multiplies them with all of the tile's active row blocks, which pass
+// through LDS (4 stages of 64 k, direct-to-LDS loads 4 stages ahead).  Only the
+// active row blocks (TA of 8) are loaded and multiplied, so a tile's MFMA work and
+// activation traffic follow its rows while its weight traffic is that of one pass.
+// Activation load j of wave w fills the 8-row group 4j + w, so every wave issues TA
+// loads per stage and the in-order wait counts depend on TA only.
+constexpr int kMBM = 256;   // activation rows per tile
+constexpr int kMBN = 256;   // packed weight rows per tile (two 128-row panels)
+constexpr int kMTM = kMBM / 32;
+// Weight register ring of the mid-size kernel, in k-steps: the products are bound by the
+// weight stream, so each wave keeps 15 k-steps (30 KB) of weight loads in flight.
+constexpr int kMRing = 16;
+constexpr int kMLead = kMRing - 1;
+
+struct MidIO {
+  const char* a_base;   // uniform: the tile's activation rows (or a, with a gather)
+  uint32_t a_off[kMTM]; // load j: 8-row group 4j + wave, this lane's row and 16 bytes
+  const char* w_base;   // uniform: this wave's 128-row weight panel
+  uint32_t w_off[2];    // this wave's two 32-row blocks of the panel + this lane's 16 bytes
+  int a_row;
+  int co[4];
+  int KT, KS;
+  int wave;
+
+  template <int TA>
+  __device__ __forceinline__ void dma_a(uint16_t* buf, int stage) const {
+#if defined(__HIP_DEVICE_COMPILE__)
+    const int st = min(stage, KT - 1);
+    const __amdgpu_buffer_rsrc_t r = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<char*>(a_base + st * kBK * 2), static_cast<short>(0), -1, 0x00020000);
+#pragma unroll
+    for (int j = 0; j < TA; ++j)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(
+          r, (lds_void_t*)(buf + (4 * j + wave) * 8 * kBK), 16, a_off[j], 0, 0, 0);
+#endif
+  }
+  __device__ __forceinline__ void load_w(bf16x8_t (&w)[2], int ks) const {
+#if defined(__HIP_DEVICE_COMPILE__)
+    const int t = min(ks, KS - 1);
+    const __amdgpu_buffer_rsrc_t r = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<char*>(w_base), static_cast<short>(0), -1, 0x00020000);
+#pragma unroll
+    for (int tn = 0; tn < 2; ++tn)
+      w[tn] = __builtin_bit_cast(bf16x8_t,
+                                 __builtin_amdgcn_raw_buffer_load_b128(r, w_off[tn], t * 1024, 0));
+#endif
+  }
+  template <int TA>
+  __device__ __forceinline__ void read_a(const uint16_t* buf, int kstep, bf16x8_t (&a)[kMTM]) const {
+#pragma unroll
+    for (int tm = 0; tm < TA; ++tm)
+      a[tm] = *reinterpret_cast<const bf16x8_t*>(&buf[a_row + tm * 32 * kBK + co[kstep]]);
+  }
+};
+
+// Stage boundary wait of the mid-size kernel: the next stage's activation loads must
+// have landed; issued after them are at least two later stages' activation loads and
+// kMLead + 3 k-steps' weight loads (fewest at the first boundary: A1 is followed by A2,
+// A3, the lead k-steps of the prologue and those issued in k-steps 0..2).
+template <int TA>
+struct MidWait {
+  static constexpr int kBoundary = (kPStages - 2) * TA + 2 * (kMLead + 3);
+  static constexpr int kPrologue = (kPStages - 1) * TA + 2 * kMLead;
+  static_assert(kBoundary < 64 && kPrologue < 64, "vmcnt range");
+};
+
+template <int T, int TA>
+__device__ __forceinline__ void md_step(const MidIO& io, uint16_t* const (&A)[kPStages], int t,
+                                        bf16x8_t (&wr)[kMRing][2], bf16x8_t (&af)[2][kMTM],
+                                        f32x16_t (&acc)[2][kMTM]) {
+  constexpr int J = T % 4, SB = T / 4;
+  if constexpr (J == 3) {
+    barrier_keep_loads<MidWait<TA>::kBoundary>();
+    io.template dma_a<TA>(A[SB], t / 4 + kPStages);
+  }
+  io.load_w(wr[(T + kMLead) % kMRing], t + kMLead);
+  io.template read_a<TA>(A[J == 3 ? (SB + 1) % kPStages : SB], (J + 1) % 4, af[(T + 1) & 1]);
+#pragma unroll
+  for (int tn = 0; tn < 2; ++tn)
+#pragma unroll
+    for (int tm = 0; tm < TA; ++tm)
+      acc[tn][tm] = Mfma<32>::mma(wr[T % kMRing][tn], af[T & 1][tm], acc[tn][tm]);
+  sched_mix<2 + (J == 3 ? TA : 0), TA, 2 * TA, 0, 8>();
+}
+
+template <int T, int TA>
+__device__ __forceinline__ void md_period(const MidIO& io, uint16_t* const (&A)[kPStages], int t0,
+                                          bf16x8_t (&wr)[kMRing][2], bf16x8_t (&af)[2][kMTM],
+                                          f32x16_t (&acc)[2][kMTM]) {
+  if constexpr (T < 16) {
+    md_step<T, TA>(io, A, t0 + T, wr, af, acc);
+    md_period<T + 1, TA>(io, A, t0, wr, af, acc);
+  }
+}
+
+template <int T, int TA>
+__device__ __forceinline__ void md_tail(const MidIO& io, uint16_t* const (&A)[kPStages], int t0,
+                                        int rem, bf16x8_t (&wr)[kMRing][2],
+                                        bf16x8_t (&af)[2][kMTM], f32x16_t (&acc)[2][kMTM]) {
+  if constexpr (T < 16) {
+    if (T < rem) {
+      md_step<T, TA>(io, A, t0 + T, wr, af, acc);
+      md_tail<T + 1, TA>(io, A, t0, rem, wr, af, acc);
+    }
+  }
+}
+
+template <int EPI, int TA>
+__device__ __forceinline__ void mid_body(const GemmArgs& g, const Tile& tile, const MidIO& io,
+                                         uint16_t* const (&A)[kPStages], int lane, int col0) {
+  f32x16_t acc[2][kMTM];
+#pragma unroll
+  for (int tn = 0; tn < 2; ++tn)
+#pragma unroll
+    for (int tm = 0; tm < TA; ++tm)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) acc[tn][tm][r] = 0.f;
+  bf16x8_t wr[kMRing][2];
+  bf16x8_t af[2][kMTM];
+  // prologue: activation stages 0..3, then weight k-steps 0 .. kMLead - 1 in order
+#pragma unroll
+  for (int st = 0; st < kPStages; ++st) io.template dma_a<TA>(A[st], st);
+#pragma unroll
+  for (int t = 0; t < kMLead; ++t) {
+    io.load_w(wr[t], t);
+    __builtin_amdgcn_sched_barrier(0);
+  }
+  barrier_keep_loads<MidWait<TA>::kPrologue>();
+  io.template read_a<TA>(A[0], 0, af[0]);
+  int t0 = 0;
+  for (; t0 + 16 <= io.KS; t0 += 16) md_period<0, TA>(io, A, t0, wr, af, acc);
+  md_tail<0, TA>(io, A, t0, io.KS - t0, wr, af, acc);
+  // no load may still be writing this workgroup's LDS when it exits
+  __builtin_amdgcn_s_waitcnt(0);
+  packed_epilogue<EPI, 2, kMTM, TA>(g, tile, lane, col0, acc);
+}
+
+template <int EPI>
+__global__ __launch_bounds__(kThreads, 1) void gemm_packed_mid_kernel(GemmArgs g) {
+  __shared__ __attribute__((aligned(16))) uint16_t A0[kMBM * kBK], A1[kMBM * kBK];
+  __shared__ __attribute__((aligned(16))) uint16_t A2[kMBM * kBK], A3[kMBM * kBK];
+  __shared__ SchedSmem sched;
+  uint16_t* const A[kPStages] = {A0, A1, A2, A3};
+  // as the alternative of a 128 x 512 launch (device-chosen height) it runs only where
+  // the dispatch chose the short tiles
+  if (g.small_tiles && *g.small_tiles != 1) return;
+  Tile tile;
+  if (!schedule_tile<kMBM>(g.seg_off, g.n_seg, g.single_rows, g.max_rows, g.bp_rows / kMBN,
+                           g.k / kBK, 0, nullptr, sched, tile))
+    return;
+  const int tid = threadIdx.x;
+  const int lane = tid & (kWave - 1);
+  const int wave = __builtin_amdgcn_readfirstlane(tid / kWave);
+  MidIO io;
+  io.wave = wave;
+  io.KT = g.k / kBK;
+  io.KS = 4 * io.KT;
+  const int32_t* __restrict__ a_rows = g.a_rows;
+  io.a_base = uniform_ptr(reinterpret_cast<const char*>(
+      static_cast<const uint16_t*>(g.a) + (a_rows ? 0 : tile.row0 * g.lda)));
+#pragma unroll
+  for (int j = 0; j < kMTM; ++j) {
+    const int i = 8 * (4 * j + wave) + (lane >> 3);  // LDS row of the tile
+    const int r = min(i, tile.m_valid - 1);          // rows past the segment repeat its last row
+    const uint32_t src = a_rows ? static_cast<uint32_t>(a_rows[tile.row0 + r]) : r;
+    const int chunk = ((lane & 7) ^ lds_swizzle(i)) * 8;
+    io.a_off[j] = (src * static_cast<uint32_t>(g.lda) + chunk) * 2u;
+  }
+  // wave w: panel p = 2 nt + w / 2, half h = w % 2 of it.  SwiGLU panels are 32-row
+  // blocks W1a W1b W3a W3b: half h takes W1 block h and W3 block h (output columns
+  // 64 p + 32 h ..); other panels take blocks 2h, 2h + 1 (columns 128 p + 64 h ..).
+  const int p = tile.nt * 2 + (wave >> 1), h = wave & 1;
+  io.w_base = uniform_ptr(static_cast<const char*>(g.bp) + tile.seg * g.bp_seg_stride +
+                          static_cast<int64_t>(p) * 128 * g.k * 2);
+#pragma unroll
+  for (int tn = 0; tn < 2; ++tn) {
+    const int blk = EPI == EPI_SWIGLU ? h + 2 * tn : 2 * h + tn;
+    io.w_off[tn] = static_cast<uint32_t>(blk) * static_cast<uint32_t>(g.k) * 64u +
+                   static_cast<uint32_t>(lane) * 16u;
+  }
+  const int col0 = panel_col0<EPI>(p) + h * (EPI == EPI_SWIGLU ? 32 : 64);
+  const int frow = lane & 31;
+#pragma unroll
+  for (int ks = 0; ks < 4; ++ks) io.co[ks] = (Mfma<32>::chunk(lane, ks) ^ lds_swizzle(frow)) * 8;
+  io.a_row = frow * kBK;
+  const int ta = __builtin_amdgcn_readfirstlane(min((tile.m_valid + 31) / 32, kMTM));
+  switch (ta) {
+    case 1: mid_body<EPI, 1>(g, tile, io, A, lane, col0); break;
+    case 2: mid_body<EPI, 2>(g, tile, io, A, lane, col0); break;
+    case 3: mid_body<EPI, 3>(g, tile, io, A, lane, col0); break;
+    case 4: mid_body<EPI, 4>(g, tile, io, A, lane, col0); break;
+    case 5: mid_body<EPI, 5>(g, tile, io, A, lane, col0); break;
+    case 6: mid_body<EPI, 6>(g, tile, io, A, lane, col0); break;
+    case 7: mid_body<EPI, 7>(g, tile, io, A, lane, col0); break;
+    default: mid_body<EPI, 8>(g, tile, io, A, lane, col0); break;
+  }
 }
 
 // ------------------------------------------------------------------ float32 SIMT kernel
@@ -1503,6 +1726,7 @@ __global__ __launch_bounds__(kThreads) void gemm_f32_kernel(GemmArgs g) {
   for (int i = 0; i < 4; ++i) {
     const int m = ty + 16 * i;
     if (m >= tile.m_valid) continue;
+    const int64_t orow = g.c_rows ? g.c_rows[tile.row0 + m] : tile.row0 + m;
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
       const int col = tile.nt * kFBN + tx + 16 * j;
@@ -1515,7 +1739,7 @@ __global__ __launch_bounds__(kThreads) void gemm_f32_kernel(GemmArgs g) {
         if (EPI == EPI_GELU) v = gelu_erf(v);
         if (g.row_scale) v *= g.row_scale[tile.row0 + m];
       }
-      C[(tile.row0 + m) * g.ldc + col] = v;
+      C[orow * g.ldc + col] = v;
     }
   }
 }
@@ -1585,36 +1809,62 @@ hipError_t launch_bf16_bm(hipStream_t st, GemmArgs g, int64_t max_rows, bool ksp
 }
 
 template <int EPI>
+hipError_t launch_packed_mid(hipStream_t st, GemmArgs g, int64_t max_rows) {
+  const int n_seg_eff = g.seg_off ? g.n_seg : 1;
+  const int64_t grid = grid_for(max_rows, n_seg_eff, kMBM, g.bp_rows / kMBN);
+  if (grid <= 0) return hipSuccess;
+  g.split_g = 0;
+  hipLaunchKernelGGL((gemm_packed_mid_kernel<EPI>), dim3(static_cast<unsigned>(grid)),
+                     dim3(kThreads), 0, st, g);
+  return hipGetLastError();
+}
+
+// With packed weights every product reads the packed copy: segments the host knows to
+// be short (under kBigSegRows rows per segment by its bound) take the 32-row kernel,
+// mid-size ones (under kPackedRows) the 256 x 256 weight-streaming kernel, long ones
+// the 128 x 512 kernel.  Where the host's bound picks the long tiles but the dispatch
+// may keep far fewer rows (g.small_tiles set), the mid-size kernel is launched beside
+// them and the dispatch's choice runs.
+template <int EPI>
+hipError_t launch_packed_epi(hipStream_t st, const GemmArgs& g, int64_t max_rows, int64_t avg) {
+  GemmArgs q = g;
+  q.small_tiles = nullptr;
+  q.split_g = 0;
+  if (avg < kBigSegRows) return launch_packed_small<EPI>(st, q, max_rows);
+  if (avg < kPackedRows) return launch_packed_mid<EPI>(st, q, max_rows);
+  const hipError_t err = launch_packed<EPI>(st, g, max_rows);
+  if (err != hipSuccess || !g.small_tiles) return err;
+  const int n_seg_eff = g.seg_off ? g.n_seg : 1;
+  // selected, the kept rows average under kBigSegRows per non-empty segment
+  const int64_t small_rows =
+      std::min<int64_t>(max_rows, static_cast<int64_t>(kBigSegRows) * n_seg_eff);
+  GemmArgs gated = g;
+  gated.split_g = 0;
+  return launch_packed_mid<EPI>(st, gated, small_rows);
+}
+
+template <int EPI>
 hipError_t launch_bf16_epi(hipStream_t st, const GemmArgs& g, int64_t max_rows) {
   const bool ksplit = g.kchunk != g.k;
   const int n_seg_eff = g.seg_off ? g.n_seg : 1;
   const int64_t avg = max_rows / (n_seg_eff > 0 ? n_seg_eff : 1);
-  // 256-row tiles skip the MFMAs of row blocks past a segment's end, so they serve any
-  // segment of a few dozen rows or more; below that the weights dominate and 32-row
-  // tiles (two workgroups per CU) keep more weight loads in flight.  The host knows a
-  // bound on the rows (max_rows); where that bound would pick 256-row tiles but the
-  // dispatch may have kept far fewer rows (g.small_tiles set), both heights are
-  // launched and the dispatch's choice runs.  Only 256-row tiles without K batches
-  // split their last round.
+  if (g.bp != nullptr && !ksplit) return launch_packed_epi<EPI>(st, g, max_rows, avg);
+  // Staged weights.  256-row tiles skip the MFMAs of row blocks past a segment's end,
+  // so they serve any segment of a few dozen rows or more; below that the weights
+  // dominate and 32-row tiles (two workgroups per CU) keep more weight loads in flight.
+  // The host knows a bound on the rows (max_rows); where that bound would pick 256-row
+  // tiles but the dispatch may have kept far fewer rows (g.small_tiles set), both
+  // heights are launched and the dispatch's choice runs.  Only 256-row tiles without K
+  // batches split their last round.
   GemmArgs small = g;
   small.split_g = 0;
-  // with packed weights, segments the host already knows to be short take the 32-row
-  // packed-weight kernel.  (The 32-row launch made beside the 256-row tiles under a
-  // capacity limit stays staged: its products can be narrow, e.g. a Switch-style second
-  // layer of 1024 columns, where its 256-column tiles give twice the workgroups.)
-  const bool packed_small = g.bp != nullptr && !ksplit;
   if (avg < kBigSegRows) {
     small.small_tiles = nullptr;
-    return packed_small ? launch_packed_small<EPI>(st, small, max_rows)
-                        : launch_bf16_bm<32, EPI>(st, small, max_rows, ksplit);
+    return launch_bf16_bm<32, EPI>(st, small, max_rows, ksplit);
   }
   GemmArgs big = g;
   if (ksplit || !g.split_buf || !g.split_desc) big.split_g = 0;
-  // long segments with packed weights: the packed-weight kernel in place of the
-  // 256-row tiles
-  const bool packed = g.bp != nullptr && !ksplit && avg >= kPackedRows;
-  const hipError_t err = packed ? launch_packed<EPI>(st, g, max_rows)
-                                : launch_bf16_bm<256, EPI>(st, big, max_rows, ksplit);
+  const hipError_t err = launch_bf16_bm<256, EPI>(st, big, max_rows, ksplit);
   if (err != hipSuccess || !g.small_tiles) return err;
   // selected, the kept rows average under kBigSegRows per non-empty segment, so the
   // 32-row tiles number at most 2.5 per segment and column tile

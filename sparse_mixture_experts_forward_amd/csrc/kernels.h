@@ -130,6 +130,7 @@ struct GemmArgs {
   int64_t bias_seg_stride;
   void* c;
   int64_t ldc;
+  const int32_t* c_rows; // or null: output row r is written to c[c_rows[r]], else c[r]
   const int32_t* seg_off;
   int32_t n_seg;
   int32_t single_rows;

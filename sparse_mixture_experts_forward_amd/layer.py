@@ -33,9 +33,23 @@ class MoELayer:
     def __init__(self, cfg: MoEConfig, weights: dict):
         self.cfg = cfg
         self.w = {k: v for k, v in weights.items() if v is not None}
-        self.device = self.w["w1"].device
+        self.device = self.w["w_router"].device
         self._ws = None
         self._ws_key = None
+        self._side = None
+
+    def side_streams(self):
+        """The layer's own side stream and fork / join events (default priority), on
+        which the shared experts run concurrently with the routed ones: raw handles for
+        moe_forward's moe_streams, created on first use."""
+        if self._side is None:
+            s = torch.cuda.Stream(device=self.device)
+            evs = [torch.cuda.Event(), torch.cuda.Event()]
+            for e in evs:  # creates the events
+                e.record(s)
+            torch.cuda.synchronize(self.device)
+            self._side = (s, evs, (s.cuda_stream, evs[0].cuda_event, evs[1].cuda_event))
+        return self._side[2]
 
     @classmethod
     def from_inputs(cls, inp) -> "MoELayer":
@@ -45,10 +59,12 @@ class MoELayer:
                  shared_w2=inp.sw2)
         return cls(inp.cfg, w)
 
-    def pack_weights(self, stream=None) -> torch.Tensor:
-        """Writes the packed copy of the routed experts' weights (bf16 only) that the
-        expert products over long segments then read; returns it (also kept in the
-        layer's weights as "packed").  Call again after changing w1/w3/w2."""
+    def pack_weights(self, stream=None, drop_unpacked: bool = False) -> torch.Tensor:
+        """Writes the packed copy of the routed experts' weights (bf16 only) that every
+        routed expert product then reads; returns it (also kept in the layer's weights as
+        "packed").  drop_unpacked: the layer then forgets w1/w3/w2 (the library does not
+        need them with the packed copy), so only one copy stays resident once the caller
+        drops its own references.  Call again after changing w1/w3/w2."""
         c = self.cfg
         if c.dtype != "bf16":
             raise ValueError("packed weights are bf16 only")
@@ -60,7 +76,16 @@ class MoELayer:
         B.moe_pack_weights(act, c.n_experts, c.d_model, c.d_ff, self.w["w1"], self.w.get("w3"),
                            self.w["w2"], packed, stream=stream)
         self.w["packed"] = packed
+        if drop_unpacked:
+            for k in ("w1", "w3", "w2"):
+                self.w.pop(k, None)
         return packed
+
+    def resident_weight_bytes(self) -> int:
+        """Bytes of the weight tensors the layer holds (router, routed experts in
+        whichever copies are kept, shared experts)."""
+        return sum(v.numel() * v.element_size() for v in self.w.values()
+                   if isinstance(v, torch.Tensor))
 
     def config_c(self, n_tokens: int) -> B.MoEConfigC:
         c = self.cfg
@@ -99,12 +124,16 @@ class MoELayer:
             n_rerouted=torch.empty(1, dtype=i32, device=dev))
 
     def forward(self, x: torch.Tensor, y: Optional[torch.Tensor] = None,
-                stats: Optional[dict] = None, stream=None, stage_events=None) -> torch.Tensor:
+                stats: Optional[dict] = None, stream=None, stage_events=None,
+                concurrent_shared: bool = True) -> torch.Tensor:
+        """concurrent_shared: run the shared experts on the layer's side stream (else
+        after the routed experts on the launch stream)."""
         n = x.shape[0]
         if y is None:
             y = torch.empty_like(x)
+        side = self.side_streams() if self.cfg.n_shared > 0 and concurrent_shared else None
         B.moe_forward(self.config_c(n), self.w, x, y, self._workspace(n), stats, stream,
-                      stage_events)
+                      stage_events, side=side)
         return y
 
     __call__ = forward
@@ -170,15 +199,18 @@ class MoELayer:
                    row_scale: Optional[torch.Tensor] = None):
         c = self.cfg
         p = "shared_" if shared else ""
-        w1, w2 = self.w[p + "w1"], self.w[p + "w2"]
+        w1, w2 = self.w.get(p + "w1"), self.w.get(p + "w2")
         w3 = self.w.get(p + "w3")
         b1 = None if shared else self.w.get("b1")
         b2 = None if shared else self.w.get("b2")
         rows = max(max_rows, 1)
         h = torch.empty((rows, c.d_ff), dtype=a.dtype, device=a.device)
         y = torch.empty((rows, c.d_model), dtype=a.dtype, device=a.device)
-        B.moe_expert_ffn(_act(c.act), a, seg_offsets, w1.shape[0], max_rows, w1, w3, b1, w2,
-                         b2, h, y, stream=stream, a_rows=a_rows, row_scale=row_scale)
+        packed = None if shared else self.w.get("packed")
+        B.moe_expert_ffn(_act(c.act), a, seg_offsets,
+                         c.n_shared if shared else c.n_experts, max_rows, w1, w3, b1, w2,
+                         b2, h, y, stream=stream, a_rows=a_rows, row_scale=row_scale,
+                         packed=packed, d_ff=c.d_ff)
         return h, y
 
     def combine(self, y_rows, slot_row, topk_w, shared_y=None, stream=None):

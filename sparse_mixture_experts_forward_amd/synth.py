@@ -154,6 +154,10 @@ def logit_bias_np(cfg: MoEConfig, seed: int = 0) -> Optional[np.ndarray]:
         return b
     if cfg.logit_bias == "uniform0.1":
         return uniform_np(stream_key(seed, cfg.cfg_id, T_LOGIT_BIAS), cfg.n_experts, 0.1)
+    if cfg.logit_bias == "skew0":  # +4.0 on expert 0: nearly every token picks it
+        b = np.zeros(cfg.n_experts, dtype=np.float32)
+        b[0] = 4.0
+        return b
     raise ValueError(cfg.logit_bias)
 
 

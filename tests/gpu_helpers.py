@@ -1,6 +1,8 @@
 """Shared helpers of the GPU parity tests (not collected by pytest)."""
 from __future__ import annotations
 
+import os
+
 import numpy as np
 import torch
 
@@ -57,6 +59,38 @@ def normwise_err(y_gpu: np.ndarray, y_ref: np.ndarray):
     if not nz.any():
         return 0.0
     return float((np.abs(y_gpu[nz] - y_ref[nz]).max(axis=1) / ref_norm[nz]).max())
+
+
+def elementwise_err(y_gpu: np.ndarray, y_ref: np.ndarray, floor: float = 1e-2) -> float:
+    """max over elements of |y - ref| / max(|ref|, floor * ||ref_t||_inf): the element-wise
+    relative error, with an absolute floor scaled to each row's largest value (elements
+    far below their row's scale are measured against that floor).  Reported beside the
+    normwise error; rows whose reference is 0 are skipped (normwise_err checks them)."""
+    ref_norm = np.abs(y_ref).max(axis=1, keepdims=True)
+    nz = ref_norm[:, 0] > 0
+    if not nz.any():
+        return 0.0
+    den = np.maximum(np.abs(y_ref[nz]), floor * ref_norm[nz])
+    return float((np.abs(y_gpu[nz] - y_ref[nz]) / den).max())
+
+
+# Parity margins of the tests that ran, printed in the terminal summary (tests/conftest.py).
+MARGINS = []
+
+
+def current_test() -> str:
+    """The running test's id (file part dropped)."""
+    t = os.environ.get("PYTEST_CURRENT_TEST", "?").split("::")[-1]
+    return t.rsplit(" ", 1)[0]
+
+
+def record_margin(case: str, normwise: float, tol: float, elementwise: float = None,
+                  n_tokens: int = None):
+    MARGINS.append(dict(case=case, normwise=normwise, tol=tol, elementwise=elementwise,
+                        n_tokens=n_tokens))
+    el = "" if elementwise is None else f", element-wise {elementwise:.3e}"
+    nt = "" if n_tokens is None else f" over {n_tokens} tokens"
+    print(f"  {case}: normwise {normwise:.3e} (tolerance {tol:g}){el}{nt}", flush=True)
 
 
 def logits_tolerance(x64: np.ndarray, wr64: np.ndarray) -> np.ndarray:

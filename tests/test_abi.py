@@ -114,11 +114,79 @@ def test_forward_validation_and_workspace():
     assert B.moe_forward_workspace_size(bad) == 0
     w = B.MoEWeightsC()
     s = B.MoEStatsC()
-    st = L.moe_forward(None, C.byref(cfg), C.byref(w), 4096, 8192, C.byref(s), None, 0)
+    st = L.moe_forward(None, C.byref(cfg), C.byref(w), 4096, 8192, C.byref(s), None, None, 0)
     assert st == B.MOE_ERR_INVALID_ARG
     with pytest.raises(B.MoEError):
         B._check("moe_forward", st)
-    assert L.moe_forward(None, C.byref(bad), C.byref(w), None, None, None, None, 0) == B.MOE_ERR_UNSUPPORTED
+    assert L.moe_forward(None, C.byref(bad), C.byref(w), None, None, None, None, None, 0) == B.MOE_ERR_UNSUPPORTED
+
+
+def test_forward_packed_copy_and_side_stream_validation():
+    """The packed copy must be the one moe_pack_weights writes for the configuration
+    (its size says so); without it the nn.Linear weights are required; a side stream
+    needs both events."""
+    L = B.lib()
+    fake = 4096  # never dereferenced: validation fails first
+    cfg = B.make_config(64, 4096, 14336, 8, 2, B.MOE_ACT_SWIGLU, B.MOE_BF16)
+    ws = B.moe_forward_workspace_size(cfg)
+    size = B.moe_packed_weights_size(B.MOE_ACT_SWIGLU, 8, 4096, 14336)
+    call = lambda w, streams=None: L.moe_forward(None, C.byref(cfg), C.byref(w), fake, fake * 2,
+                                                 None, streams, fake, ws)
+    # no routed weights at all
+    assert call(B.MoEWeightsC(w_router=fake)) == B.MOE_ERR_INVALID_ARG
+    assert "w1" in L.moe_last_error().decode()
+    # a copy packed for 4 experts (or any other size) is refused
+    small = B.moe_packed_weights_size(B.MOE_ACT_SWIGLU, 4, 4096, 14336)
+    for nbytes in (0, small, size - 16, size + 16):
+        st = call(B.MoEWeightsC(w_router=fake, packed=fake, packed_bytes=nbytes))
+        assert st == B.MOE_ERR_INVALID_ARG, nbytes
+        assert "packed_bytes" in L.moe_last_error().decode()
+    # misaligned packed copy
+    assert call(B.MoEWeightsC(w_router=fake, packed=fake + 8, packed_bytes=size)) == B.MOE_ERR_INVALID_ARG
+    # a side stream without its events
+    w = B.MoEWeightsC(w_router=fake, w1=fake, w3=fake, w2=fake)
+    for sides in (B.MoEStreamsC(fake, None, fake), B.MoEStreamsC(fake, fake, None)):
+        assert call(w, C.byref(sides)) == B.MOE_ERR_INVALID_ARG
+        assert "event" in L.moe_last_error().decode()
+
+
+def test_expert_ffn_packed_size_validation():
+    L = B.lib()
+    fake = 4096
+    sw = B.MOE_ACT_SWIGLU
+    size = B.moe_packed_weights_size(sw, 3, 256, 512)
+
+    def call(nbytes, nseg=3, w1=None):
+        return L.moe_expert_ffn_packed(None, sw, fake, None, 0, fake, nseg, 100, 256, 512, w1,
+                                       None, None, None, None, fake, nbytes, None, fake, fake,
+                                       None, 0)
+
+    for nbytes in (0, size - 1024, size + 1024):
+        assert call(nbytes) == B.MOE_ERR_INVALID_ARG
+        assert "packed_bytes" in L.moe_last_error().decode()
+    # packed for 3 experts, called with 2 segments: the second layer would be misplaced
+    assert call(size, nseg=2) == B.MOE_ERR_INVALID_ARG
+
+
+def test_weight_offsets_stay_32_bit():
+    """One expert's weights (and the shared experts' first layer, taken as one matrix)
+    must stay below 4 GiB: larger shapes are refused, not wrapped."""
+    L = B.lib()
+    fake = 4096
+    # 65536 x 32768 bf16 = 4 GiB
+    st = L.moe_expert_ffn(None, B.MOE_BF16, B.MOE_ACT_GELU, fake, None, 0, fake, 2, 10, 65536,
+                          32768, fake, None, None, fake, None, None, fake, fake)
+    assert st == B.MOE_ERR_UNSUPPORTED and "4 GiB" in L.moe_last_error().decode()
+    # just below: the shape passes, and the missing w1 is what is reported
+    st = L.moe_expert_ffn(None, B.MOE_BF16, B.MOE_ACT_GELU, fake, None, 0, fake, 2, 10, 65536,
+                          32704, None, None, None, fake, None, None, fake, fake)
+    assert st == B.MOE_ERR_INVALID_ARG and "w1" in L.moe_last_error().decode()
+    assert B.moe_packed_weights_size(B.MOE_ACT_GELU, 2, 65536, 32768) == 0
+    # 8 shared experts of 16384 x 16384 bf16: 4 GiB as one first-layer matrix
+    big = B.make_config(16, 16384, 16384, 8, 2, B.MOE_ACT_SWIGLU, B.MOE_BF16, n_shared=8)
+    assert B.moe_forward_workspace_size(big) == 0
+    ok = B.make_config(16, 16384, 16384, 8, 2, B.MOE_ACT_SWIGLU, B.MOE_BF16, n_shared=4)
+    assert B.moe_forward_workspace_size(ok) > 0
 
 
 def test_update_bias_validation():
@@ -205,6 +273,6 @@ def test_packed_weights_size_and_validation():
     cfg = B.make_config(64, 64, 64, 4, 2, B.MOE_ACT_GELU, B.MOE_F32)
     w = B.MoEWeightsC(w_router=fake, w1=fake, w2=fake, packed=fake)
     ws = B.moe_forward_workspace_size(cfg)
-    st = L.moe_forward(None, C.byref(cfg), C.byref(w), fake, fake * 2, None, fake, ws)
+    st = L.moe_forward(None, C.byref(cfg), C.byref(w), fake, fake * 2, None, None, fake, ws)
     assert st == B.MOE_ERR_UNSUPPORTED
     assert "packed" in L.moe_last_error().decode()
