@@ -32,9 +32,10 @@
  *     accumulate in float32.  Rounding to bf16 is round-to-nearest-even.
  *   - Results are deterministic: the same inputs give the same bits on every run.
  *   - The library keeps no state between calls except the thread-local error detail of
- *     moe_last_error(): no internal streams, events, locks or caches.  Calls on
- *     different streams may run concurrently if their buffers (workspaces and the
- *     caller's events included) do not overlap.
+ *     moe_last_error() and the per-GPU scratch array of moe_dispatch_noalloc: no
+ *     internal streams, events, locks or caches.  Calls on different streams may run
+ *     concurrently if their buffers (workspaces and the caller's events included) do
+ *     not overlap.
  */
 #ifndef MOE_MI355X_H
 #define MOE_MI355X_H
@@ -238,6 +239,27 @@ moe_status moe_dispatch(void* stream, const int32_t* topk_idx, int64_t n_tokens,
                         int32_t* slot_row, int32_t* kept_count, int32_t* n_dropped,
                         void* x_perm, const float* topk_w, float* row_weight, void* ws,
                         size_t ws_bytes);
+
+/*
+ * moe_dispatch_noalloc -- moe_dispatch for callers that cannot allocate device memory
+ * (code under HIP graph capture, tight serving loops, harnesses that forbid
+ * allocation): the same arguments without ws / ws_bytes, the same results bit for bit.
+ * Its scratch (per-chunk histograms and bases, kept counts) lives in a library-owned
+ * device array of MOE_NOALLOC_SCRATCH_BYTES per GPU, held until the process ends; the
+ * call allocates nothing.  A call whose moe_dispatch_workspace_size(N, k, E) exceeds
+ * that size returns MOE_ERR_UNSUPPORTED and queues nothing.  Every call on a GPU uses
+ * that GPU's one array: calls that overlap on one GPU (on different streams, or from
+ * several threads) race and give undefined results; calls ordered on one stream are
+ * safe.  The array's device address is looked up once per device, on the first call
+ * with that device current.
+ */
+#define MOE_NOALLOC_SCRATCH_BYTES (4u << 20)
+moe_status moe_dispatch_noalloc(void* stream, const int32_t* topk_idx, int64_t n_tokens,
+                                int32_t k, int32_t n_experts, int64_t capacity, const void* x,
+                                moe_dtype x_dtype, int64_t d_model, int32_t* expert_offsets,
+                                int32_t* row_token, int32_t* slot_row, int32_t* kept_count,
+                                int32_t* n_dropped, void* x_perm, const float* topk_w,
+                                float* row_weight);
 
 /*
  * moe_expert_ffn -- the expert networks over variable-length row segments (one grouped

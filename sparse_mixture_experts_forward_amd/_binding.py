@@ -78,6 +78,8 @@ _SIGS = {
     "moe_dispatch_workspace_size": (_SZ, [_I64, _I32, _I32]),
     "moe_dispatch": (C.c_int, [_VP, _VP, _I64, _I32, _I32, _I64, _VP, C.c_int, _I64, _VP, _VP,
                                _VP, _VP, _VP, _VP, _VP, _VP, _VP, _SZ]),
+    "moe_dispatch_noalloc": (C.c_int, [_VP, _VP, _I64, _I32, _I32, _I64, _VP, C.c_int, _I64, _VP,
+                                       _VP, _VP, _VP, _VP, _VP, _VP, _VP]),
     "moe_expert_ffn": (C.c_int, [_VP, C.c_int, C.c_int, _VP, _VP, _I64, _VP, _I32, _I64, _I64,
                                  _I64, _VP, _VP, _VP, _VP, _VP, _VP, _VP, _VP]),
     "moe_expert_ffn_packed_workspace_size": (_SZ, []),
@@ -219,6 +221,23 @@ def moe_dispatch(topk_idx, n_experts: int, capacity: int, x, expert_offsets, row
                             _ptr(slot_row), _ptr(kept_count), _ptr(n_dropped), _ptr(x_perm),
                             _ptr(topk_w), _ptr(row_weight), _ptr(ws), _ws_bytes(ws))
     _check("moe_dispatch", st)
+
+
+MOE_NOALLOC_SCRATCH_BYTES = 4 << 20
+
+
+def moe_dispatch_noalloc(topk_idx, n_experts: int, capacity: int, x, expert_offsets, row_token,
+                         slot_row, kept_count, n_dropped, x_perm, stream=None, topk_w=None,
+                         row_weight=None):
+    """moe_dispatch without a workspace: the library's per-GPU scratch is used."""
+    n, k = topk_idx.shape
+    d = x.shape[1] if x is not None else 0
+    xdt = _dtype(x) if x is not None else MOE_F32
+    st = lib().moe_dispatch_noalloc(_stream(stream), _ptr(topk_idx), n, k, n_experts, capacity,
+                                    _ptr(x), xdt, d, _ptr(expert_offsets), _ptr(row_token),
+                                    _ptr(slot_row), _ptr(kept_count), _ptr(n_dropped),
+                                    _ptr(x_perm), _ptr(topk_w), _ptr(row_weight))
+    _check("moe_dispatch_noalloc", st)
 
 
 def moe_expert_ffn_packed_workspace_size() -> int:

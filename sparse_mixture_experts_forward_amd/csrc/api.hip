@@ -2,6 +2,7 @@
 // of the kernels (include/moe.h documents every entry point).
 
 #include <algorithm>
+#include <atomic>
 #include <cmath>
 #include <cstdarg>
 #include <cstdio>
@@ -541,12 +542,18 @@ size_t moe_dispatch_workspace_size(int64_t n_tokens, int32_t k, int32_t n_expert
   return dispatch_ws(n_tokens, k, n_experts);
 }
 
-moe_status moe_dispatch(void* stream, const int32_t* topk_idx, int64_t n_tokens, int32_t k,
-                        int32_t n_experts, int64_t capacity, const void* x, moe_dtype x_dtype,
-                        int64_t d_model, int32_t* expert_offsets, int32_t* row_token,
-                        int32_t* slot_row, int32_t* kept_count, int32_t* n_dropped,
-                        void* x_perm, const float* topk_w, float* row_weight, void* ws,
-                        size_t ws_bytes) {
+}  // extern "C"
+
+namespace {
+
+// Argument checks of moe_dispatch and moe_dispatch_noalloc (everything but the
+// workspace); row_bytes receives the size of an x row (0 without a permuted copy).
+moe_status check_dispatch_args(const int32_t* topk_idx, int64_t n_tokens, int32_t k,
+                               int32_t n_experts, const void* x, moe_dtype x_dtype,
+                               int64_t d_model, const int32_t* expert_offsets,
+                               const int32_t* row_token, const int32_t* slot_row,
+                               const void* x_perm, const float* topk_w,
+                               const float* row_weight, int64_t& row_bytes) {
   if (n_tokens < 0) return fail(MOE_ERR_INVALID_ARG, "n_tokens < 0");
   if (n_experts < 1) return fail(MOE_ERR_INVALID_ARG, "n_experts < 1");
   if (n_experts > MOE_MAX_EXPERTS) return fail(MOE_ERR_UNSUPPORTED, "n_experts > %d", MOE_MAX_EXPERTS);
@@ -557,7 +564,7 @@ moe_status moe_dispatch(void* stream, const int32_t* topk_idx, int64_t n_tokens,
   if (n_tokens > 0 && (!topk_idx || !row_token || !slot_row))
     return fail(MOE_ERR_INVALID_ARG, "topk_idx, row_token and slot_row are required");
   if (row_weight && !topk_w) return fail(MOE_ERR_INVALID_ARG, "row_weight needs topk_w");
-  int64_t row_bytes = 0;
+  row_bytes = 0;
   if (x_perm) {
     if (!dtype_ok(x_dtype)) return fail(MOE_ERR_INVALID_ARG, "unknown x dtype");
     if (!x) return fail(MOE_ERR_INVALID_ARG, "x is required when x_perm is given");
@@ -567,12 +574,78 @@ moe_status moe_dispatch(void* stream, const int32_t* topk_idx, int64_t n_tokens,
     MOE_TRY(check_aligned(x, 16, "x"));
     MOE_TRY(check_aligned(x_perm, 16, "x_perm"));
   }
+  return MOE_OK;
+}
+
+// The no-allocation dispatch's scratch: one array per GPU (each device that loads the
+// library holds its own copy), of MOE_NOALLOC_SCRATCH_BYTES, kept until the process
+// ends.  Host code never uses the array's name as an address: the device address of
+// each GPU's copy is looked up once, with that device current, and kept here.
+__device__ __align__(256) char scratch[MOE_NOALLOC_SCRATCH_BYTES];
+
+constexpr int kMaxDevices = 64;
+std::atomic<void*> g_scratch_ptr[kMaxDevices];
+
+moe_status scratch_ptr(void** out) {
+  int dev = 0;
+  MOE_TRY(hip_check(hipGetDevice(&dev), "hipGetDevice"));
+  if (dev < 0 || dev >= kMaxDevices)
+    return fail(MOE_ERR_UNSUPPORTED, "device %d is beyond the %d the no-alloc scratch serves", dev,
+                kMaxDevices);
+  void* p = g_scratch_ptr[dev].load(std::memory_order_acquire);
+  if (!p) {
+    MOE_TRY(hip_check(hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)),
+                      "hipGetSymbolAddress of the no-alloc scratch"));
+    if (!p) return fail(MOE_ERR_HIP, "no device address for the no-alloc scratch");
+    g_scratch_ptr[dev].store(p, std::memory_order_release);
+  }
+  *out = p;
+  return MOE_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+moe_status moe_dispatch(void* stream, const int32_t* topk_idx, int64_t n_tokens, int32_t k,
+                        int32_t n_experts, int64_t capacity, const void* x, moe_dtype x_dtype,
+                        int64_t d_model, int32_t* expert_offsets, int32_t* row_token,
+                        int32_t* slot_row, int32_t* kept_count, int32_t* n_dropped,
+                        void* x_perm, const float* topk_w, float* row_weight, void* ws,
+                        size_t ws_bytes) {
+  int64_t row_bytes = 0;
+  MOE_TRY(check_dispatch_args(topk_idx, n_tokens, k, n_experts, x, x_dtype, d_model,
+                              expert_offsets, row_token, slot_row, x_perm, topk_w, row_weight,
+                              row_bytes));
   const size_t need = dispatch_ws(n_tokens, k, n_experts);
   if (ws_bytes < need) return fail(MOE_ERR_WORKSPACE, "moe_dispatch needs %zu workspace bytes", need);
   if (need > 0) {
     if (!ws) return fail(MOE_ERR_INVALID_ARG, "ws is NULL");
     MOE_TRY(check_aligned(ws, kAlign, "ws"));
   }
+  return run_dispatch(static_cast<hipStream_t>(stream), topk_idx, n_tokens, k, n_experts,
+                      capacity, x, row_bytes, expert_offsets, row_token, slot_row, kept_count,
+                      n_dropped, x_perm, topk_w, row_weight, ws);
+}
+
+moe_status moe_dispatch_noalloc(void* stream, const int32_t* topk_idx, int64_t n_tokens,
+                                int32_t k, int32_t n_experts, int64_t capacity, const void* x,
+                                moe_dtype x_dtype, int64_t d_model, int32_t* expert_offsets,
+                                int32_t* row_token, int32_t* slot_row, int32_t* kept_count,
+                                int32_t* n_dropped, void* x_perm, const float* topk_w,
+                                float* row_weight) {
+  int64_t row_bytes = 0;
+  MOE_TRY(check_dispatch_args(topk_idx, n_tokens, k, n_experts, x, x_dtype, d_model,
+                              expert_offsets, row_token, slot_row, x_perm, topk_w, row_weight,
+                              row_bytes));
+  const size_t need = dispatch_ws(n_tokens, k, n_experts);
+  if (need > MOE_NOALLOC_SCRATCH_BYTES)
+    return fail(MOE_ERR_UNSUPPORTED,
+                "moe_dispatch_noalloc: this batch needs %zu scratch bytes, more than the %u "
+                "it holds (use moe_dispatch with a workspace)",
+                need, static_cast<unsigned>(MOE_NOALLOC_SCRATCH_BYTES));
+  void* ws = nullptr;
+  MOE_TRY(scratch_ptr(&ws));
   return run_dispatch(static_cast<hipStream_t>(stream), topk_idx, n_tokens, k, n_experts,
                       capacity, x, row_bytes, expert_offsets, row_token, slot_row, kept_count,
                       n_dropped, x_perm, topk_w, row_weight, ws);
