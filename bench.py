@@ -198,13 +198,16 @@ def kernel_work(cfg, kept: int, touched: int):
     w["shared"] = dict(flops=2.0 * n * d * f * sh * (m1 + 1),
                        bytes=(sh * (m1 + 1) * f * d * es + n * d * es * 2 + n * sh * f * es * 2)
                        if sh else 0)
-    gather, wscale = bool(cfg.fuse & 1), bool(cfg.fuse & 2)
+    scatter = bool(cfg.fuse & 4) and k == 1 and sh == 0
+    gather, wscale = bool(cfg.fuse & 1), bool(cfg.fuse & 2) or scatter
     # dispatch: ids in, slot map out, row map (and row weights) out; the row copy of x
-    # only without the gather fusion
+    # only without the gather fusion; with the scatter fusion the output rows of tokens
+    # whose slot was dropped are zeroed
     w["dispatch"] = dict(flops=0.0, bytes=n * k * 4 * 2 + kept * 4 + (kept * 8 if wscale else 0)
-                         + (0 if gather else n * d * es + kept * d * es))
-    w["combine"] = dict(flops=0.0, bytes=kept * d * es + n * k * (4 if wscale else 8)
-                        + n * d * es * (2 if sh else 1))
+                         + (0 if gather else n * d * es + kept * d * es)
+                         + ((n - kept) * d * es if scatter else 0))
+    w["combine"] = dict(flops=0.0, bytes=0 if scatter else
+                        kept * d * es + n * k * (4 if wscale else 8) + n * d * es * (2 if sh else 1))
     w["route"] = dict(flops=2.0 * n * d * cfg.n_experts,
                       bytes=n * d * es + d * cfg.n_experts * 4 + n * (cfg.n_experts * 4 + k * 8))
     return w
@@ -518,7 +521,8 @@ def main():
                     help="capacity from the factor, or the batch-dependent rules")
     ap.add_argument("--fuse", type=int, default=None,
                     help="fusion bitmask (1 gather x rows in GEMM1, 2 routing weights in "
-                         "GEMM2's epilogue); default: the workload's own")
+                         "GEMM2's epilogue, 4 top-1 rows written straight to the output); "
+                         "default: the workload's own")
     ap.add_argument("--no-cold", action="store_true",
                     help="skip the cold-cache pass (a 1 GiB scratch write before each step "
                          "evicts L2 and the 256 MB Infinity Cache; stage times only)")

@@ -72,6 +72,11 @@ typedef enum {
 /* Fusions of moe_forward (moe_config.fuse, a bitmask). */
 #define MOE_FUSE_GATHER 1 /* GEMM1 reads the routed rows of x in place (no permuted copy) */
 #define MOE_FUSE_WEIGHT 2 /* GEMM2 scales each row by its routing weight; the combine sums */
+#define MOE_FUSE_SCATTER 4 /* top-1 without shared experts: GEMM2 writes each kept row,
+                              scaled by its routing weight, straight into its token's
+                              output row and the dispatch zeroes the rows of tokens whose
+                              slot was dropped; no combine (ignored for k > 1 or shared
+                              experts) */
 
 /*
  * moe_capacity -- host function, no device work.
@@ -358,7 +363,10 @@ typedef struct {
   int32_t fuse;           /* MOE_FUSE_* bitmask.  MOE_FUSE_GATHER is taken when x holds
                              at most 4 GiB; results equal the unfused ones bit for bit.
                              MOE_FUSE_WEIGHT rounds w * expert output to dtype before
-                             the sum (unfused: the sum weights the rounded output). */
+                             the sum (unfused: the sum weights the rounded output);
+                             MOE_FUSE_SCATTER rounds it the same way, and with it a
+                             top-1 layer's y equals that of MOE_FUSE_WEIGHT bit for
+                             bit. */
 } moe_config;
 
 typedef struct {

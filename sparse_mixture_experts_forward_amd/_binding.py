@@ -20,7 +20,7 @@ MOE_F32, MOE_BF16 = 0, 1
 MOE_ACT_GELU, MOE_ACT_SWIGLU = 0, 1
 MOE_MAX_EXPERTS = 512
 MOE_CAPACITY_FIXED, MOE_CAPACITY_LINEAR, MOE_CAPACITY_LOG = range(3)
-MOE_FUSE_GATHER, MOE_FUSE_WEIGHT = 1, 2
+MOE_FUSE_GATHER, MOE_FUSE_WEIGHT, MOE_FUSE_SCATTER = 1, 2, 4
 CAPACITY_RULES = {"fixed": MOE_CAPACITY_FIXED, "linear": MOE_CAPACITY_LINEAR,
                   "log": MOE_CAPACITY_LOG}
 

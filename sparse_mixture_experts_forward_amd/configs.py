@@ -36,8 +36,10 @@ class MoEConfig:
     capacity_rule: str = "fixed"  # "fixed" (alpha) | "linear" | "log" (batch-dependent)
     reroute_rounds: int = 0  # > 0: overflow goes on to the next-best experts with room
     # bitmask: 1 GEMM1 gathers the routed rows of x in place (no permuted copy), 2 GEMM2's
-    # epilogue applies the routing weights (the combine only sums); both by default
-    fuse: int = 3
+    # epilogue applies the routing weights (the combine only sums), 4 top-1 layers without
+    # shared experts write GEMM2's rows straight into the output (no combine); all by
+    # default
+    fuse: int = 7
 
     def with_tokens(self, n: int) -> "MoEConfig":
         return replace(self, n_tokens=n)

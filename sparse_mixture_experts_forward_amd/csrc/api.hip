@@ -95,6 +95,7 @@ struct RouteWs {
   float* pmon;
   double* term;
   int64_t* cnt;
+  int32_t* done;
   uint16_t* wp;
   float* part;
 };
@@ -107,6 +108,7 @@ RouteWs route_layout(Carve& c, int64_t n, int64_t d, int32_t e) {
   r.pmon = c.take<float>(2 * b);
   r.term = c.take<double>(e);
   r.cnt = c.take<int64_t>(e);
+  r.done = c.take<int32_t>(1);
   if (d >= 8 && d % 8 == 0) {
     const moe::RoutePlan pl = moe::route_plan(n, d, e);
     r.wp = c.take<uint16_t>(3 * static_cast<int64_t>(pl.e_pad) * d);
@@ -156,6 +158,7 @@ size_t dispatch_ws(int64_t n, int32_t k, int32_t e) {
   c.take<int32_t>(g.n_blocks * e);
   c.take<int32_t>(g.n_blocks * e);
   c.take<int32_t>(e);
+  c.take<int32_t>(1);
   return c.used;
 }
 
@@ -168,7 +171,7 @@ moe_status run_route(hipStream_t st, const void* x, moe_dtype xt, int64_t n, int
   if (monitor) flags |= moe::kGateMonitor;
   auto finalize = [&](int64_t rows) {
     return hip_check(moe::launch_route_finalize(st, r.pp, r.pc, r.pmon, rows, n, e, k, sel, pm,
-                                                aux, monitor, r.term, r.cnt),
+                                                aux, monitor, r.term, r.cnt, r.done),
                      "router statistics launch");
   };
   int64_t rows;
@@ -176,7 +179,7 @@ moe_status run_route(hipStream_t st, const void* x, moe_dtype xt, int64_t n, int
     // the gate alone, over the caller's logits
     rows = moe::gate_blocks(n);
     MOE_TRY(hip_check(moe::launch_route_gate(st, logits_in, 1, n, e, bias, k, flags, logits_out,
-                                             idx, w, r.pp, r.pc, r.pmon),
+                                             idx, w, r.pp, r.pc, r.pmon, r.done),
                       "router gate launch"));
   } else if (xt == MOE_BF16) {
     const moe::RoutePlan pl = moe::route_plan(n, d, e);
@@ -186,12 +189,12 @@ moe_status run_route(hipStream_t st, const void* x, moe_dtype xt, int64_t n, int
     MOE_TRY(hip_check(moe::launch_route_logits(st, static_cast<const uint16_t*>(x), pl, r.wp, r.part),
                       "router logits launch"));
     MOE_TRY(hip_check(moe::launch_route_gate(st, r.part, pl.ks, n, e, bias, k, flags, logits_out,
-                                             idx, w, r.pp, r.pc, r.pmon),
+                                             idx, w, r.pp, r.pc, r.pmon, r.done),
                       "router gate launch"));
   } else {
     rows = moe::route_blocks(n);
     MOE_TRY(hip_check(moe::launch_route(st, static_cast<const float*>(x), n, d, wr, bias, e, k,
-                                        flags, logits_out, idx, w, r.pp, r.pc, r.pmon),
+                                        flags, logits_out, idx, w, r.pp, r.pc, r.pmon, r.done),
                       "router kernel launch"));
   }
   return finalize(rows);
@@ -202,16 +205,18 @@ moe_status run_dispatch(hipStream_t st, const int32_t* idx, int64_t n, int32_t k
                         int32_t* row_token, int32_t* slot_row, int32_t* kept, int32_t* dropped,
                         void* x_perm, const float* topk_w, float* row_weight, void* ws,
                         float* drop_rate = nullptr, int32_t* zero_out = nullptr,
-                        int32_t* small_tiles = nullptr) {
+                        int32_t* small_tiles = nullptr, void* zero_rows = nullptr,
+                        int64_t zero_row_bytes = 0) {
   Carve c(ws);
   const moe::DispatchGrid g = moe::dispatch_grid(n, k);
   int32_t* hist = c.take<int32_t>(g.n_blocks * e);
   int32_t* base = c.take<int32_t>(g.n_blocks * e);
   int32_t* kept_tmp = c.take<int32_t>(e);
+  int32_t* done = c.take<int32_t>(1);
   return hip_check(moe::launch_dispatch(st, idx, n, k, e, cap, x, row_bytes, offsets, row_token,
                                         slot_row, kept, dropped, x_perm, hist, base, kept_tmp,
-                                        topk_w, row_weight, drop_rate, zero_out,
-                                        small_tiles),
+                                        done, topk_w, row_weight, drop_rate, zero_out,
+                                        small_tiles, zero_rows, zero_row_bytes),
                    "dispatch kernels launch");
 }
 
@@ -242,7 +247,8 @@ moe_status run_ffn(hipStream_t st, moe_dtype dt, moe_act act, const void* a, int
                    const std::function<moe_status()>& between = nullptr,
                    const int32_t* a_rows = nullptr, const float* row_scale = nullptr,
                    int split_g = 0, float* split_buf = nullptr, int32_t* split_desc = nullptr,
-                   const int32_t* small_tiles = nullptr, const void* packed = nullptr) {
+                   const int32_t* small_tiles = nullptr, const void* packed = nullptr,
+                   const int32_t* y_rows_map = nullptr, int64_t ldy = 0) {
   const bool bf = dt == MOE_BF16;
   const bool sw = act == MOE_ACT_SWIGLU;
   moe::GemmArgs g1{};
@@ -272,7 +278,8 @@ moe_status run_ffn(hipStream_t st, moe_dtype dt, moe_act act, const void* a, int
   g2.ldb = w2_kchunk; g2.b_seg_stride = w_seg_stride;
   g2.kchunk = w2_kchunk; g2.kbatch_stride = w2_kbatch_stride;
   g2.bias = b2; g2.bias_seg_stride = d;
-  g2.c = y; g2.ldc = d;
+  g2.c = y; g2.ldc = ldy > 0 ? ldy : d;
+  g2.c_rows = y_rows_map;
   g2.seg_off = seg_off; g2.n_seg = n_seg; g2.single_rows = single_rows;
   g2.n_out = static_cast<int32_t>(d); g2.k = static_cast<int32_t>(d_ff);
   g2.small_tiles = small_tiles;
@@ -335,7 +342,14 @@ bool fuse_gather(const moe_config& c) {
   return (c.fuse & MOE_FUSE_GATHER) &&
          c.n_tokens * c.d_model * static_cast<int64_t>(elem_size(c.dtype)) <= UINT32_MAX;
 }
-bool fuse_weight(const moe_config& c) { return (c.fuse & MOE_FUSE_WEIGHT) != 0; }
+// Top-1 without shared experts, with the scatter fusion: GEMM2 writes each kept row
+// (weighted) into its token's output row; no combine, no expert-output rows.
+bool fuse_scatter(const moe_config& c) {
+  return (c.fuse & MOE_FUSE_SCATTER) && c.top_k == 1 && c.n_shared == 0;
+}
+// The weight fusion, which the scatter fusion implies (the row weights travel with the
+// rows into GEMM2's epilogue).
+bool fuse_weight(const moe_config& c) { return (c.fuse & MOE_FUSE_WEIGHT) != 0 || fuse_scatter(c); }
 
 struct ForwardLayout {
   int32_t *idx, *sel, *offsets, *row_token, *slot_row, *kept, *dropped;
@@ -380,7 +394,7 @@ ForwardLayout forward_layout(const moe_config& c, void* ws) {
     L.split_desc = cv.take<int32_t>(moe::gemm_split_desc_ints(L.split_g));
   }
   L.h = cv.take<char>(R * c.d_ff * es);
-  L.y_rows = cv.take<char>(R * c.d_model * es);
+  if (!fuse_scatter(c)) L.y_rows = cv.take<char>(R * c.d_model * es);
   if (c.n_shared > 0) {
     L.h_sh = cv.take<char>(n * c.n_shared * c.d_ff * es);
     L.y_sh = cv.take<char>(n * c.d_model * es);
@@ -400,7 +414,8 @@ moe_status check_config(const moe_config* c) {
   if (c->capacity_rule < MOE_CAPACITY_FIXED || c->capacity_rule > MOE_CAPACITY_LOG)
     return fail(MOE_ERR_INVALID_ARG, "unknown capacity rule");
   if (c->reroute_rounds < 0) return fail(MOE_ERR_INVALID_ARG, "reroute_rounds < 0");
-  if (c->fuse & ~(MOE_FUSE_GATHER | MOE_FUSE_WEIGHT)) return fail(MOE_ERR_INVALID_ARG, "unknown fuse flags");
+  if (c->fuse & ~(MOE_FUSE_GATHER | MOE_FUSE_WEIGHT | MOE_FUSE_SCATTER))
+    return fail(MOE_ERR_INVALID_ARG, "unknown fuse flags");
   MOE_TRY(check_ffn_shape(c->dtype, c->act, c->d_model, c->d_ff));
   if (c->n_tokens * static_cast<int64_t>(c->top_k) > INT32_MAX / 2)
     return fail(MOE_ERR_UNSUPPORTED, "n_tokens * top_k too large");
@@ -871,13 +886,14 @@ moe_status moe_forward(void* stream, const moe_config* cfg, const moe_weights* w
                                           clamp_rounds(c.reroute_rounds, e, k),
                                           idx, tw, o.n_rerouted, L.rr),
                       "re-routing launch"));
-  const bool gather = fuse_gather(c), wscale = fuse_weight(c);
-  MOE_TRY(run_dispatch(st, idx, n, k, e, cap, x, c.d_model * static_cast<int64_t>(es), offsets,
+  const bool gather = fuse_gather(c), wscale = fuse_weight(c), scatter = fuse_scatter(c);
+  const int64_t row_bytes = c.d_model * static_cast<int64_t>(es);
+  MOE_TRY(run_dispatch(st, idx, n, k, e, cap, x, row_bytes, offsets,
                        L.row_token, slot_row, o.kept_count, dropped,
                        gather ? nullptr : L.x_perm, wscale ? tw : nullptr,
                        wscale ? L.row_w : nullptr, L.dispatch_ws,
                        o.monitor ? o.monitor + 4 : nullptr, reroute ? nullptr : o.n_rerouted,
-                       cap >= 0 ? L.small_tiles : nullptr));
+                       cap >= 0 ? L.small_tiles : nullptr, scatter ? y : nullptr, row_bytes));
   MOE_TRY(mark(2));
   // a8: shared experts, all tokens; the S experts act as one FFN of width S*d_ff (W1/W3
   // rows concatenate, W2 splits its reduction into S chunks of d_ff).  On the caller's
@@ -899,24 +915,28 @@ moe_status moe_forward(void* stream, const moe_config* cfg, const moe_weights* w
   const int64_t R = max_rows_of(n, e, k, cap);
   // a6-a7: routed experts over the expert-major segments; fused, GEMM1 gathers the rows
   // of x itself and GEMM2 scales each row by its routing weight
+  // (scatter: GEMM2's row r goes to the output row of its token, row_token[r])
   MOE_TRY(run_ffn(st, c.dtype, c.act, gather ? x : L.x_perm, c.d_model, offsets, e, 0, R,
                   c.d_model, c.d_ff, w->w1, w->w3, w->b1, c.d_ff * c.d_model, w->w2, w->b2,
-                  c.d_ff, 0, L.h, L.y_rows, [&]() { return mark(3); },
+                  c.d_ff, 0, L.h, scatter ? y : L.y_rows, [&]() { return mark(3); },
                   gather ? L.row_token : nullptr, wscale ? L.row_w : nullptr, L.split_g,
                   L.split_buf, L.split_desc,
                   // with a capacity the kept rows are known only on the device, which
                   // then picks the tile height
-                  cap >= 0 ? L.small_tiles : nullptr, w->packed));
+                  cap >= 0 ? L.small_tiles : nullptr, w->packed,
+                  scatter ? L.row_token : nullptr));
   MOE_TRY(mark(4));
   // the combine needs the shared experts' output
   if (shared && side) MOE_TRY(hip_check(hipStreamWaitEvent(st, join_ev, 0), "join wait"));
   if (shared && !side) MOE_TRY(run_shared(st));
   MOE_TRY(mark(5));
-  // a9: weighted combine (shared first, then slots in order)
-  MOE_TRY(hip_check(moe::launch_combine(st, c.dtype == MOE_BF16, L.y_rows, slot_row,
-                                        wscale ? nullptr : tw, n, k,
-                                        c.d_model, c.n_shared > 0 ? L.y_sh : nullptr, y),
-                    "combine launch"));
+  // a9: weighted combine (shared first, then slots in order); with the scatter fusion
+  // the expert rows are already in place
+  if (!scatter)
+    MOE_TRY(hip_check(moe::launch_combine(st, c.dtype == MOE_BF16, L.y_rows, slot_row,
+                                          wscale ? nullptr : tw, n, k,
+                                          c.d_model, c.n_shared > 0 ? L.y_sh : nullptr, y),
+                      "combine launch"));
   return mark(6);
 }
 

@@ -7,13 +7,15 @@
 // Kernels over contiguous token chunks (one workgroup per chunk) and experts:
 //   1. hist:    LDS histogram of the chunk's expert ids -> blk_hist[e][b]
 //   2. scan:    one workgroup per expert; exclusive scan over chunks (the rank of the
-//               chunk's first assignment), kept = min(total, C); then one workgroup,
-//               exclusive scan over experts -> expert_offsets
+//               chunk's first assignment), kept = min(total, C); the last workgroup to
+//               finish then scans the kept counts over experts -> expert_offsets
 //   3. scatter: per chunk, the stable in-chunk rank of each assignment (ballot-based
 //               match inside a wave, running per-expert counters in LDS), the row
 //               maps, then the copy of every token row to its kept rows with 16-byte
 //               loads and stores (each x row is read once).
 // No atomics decide an order, so the permutation is the same on every run.
+
+#include <algorithm>
 
 #include "common.h"
 #include "kernels.h"
@@ -24,10 +26,14 @@ namespace {
 constexpr int kThreads = 256;
 constexpr int kMaxChunkItems = 1024;  // tokens_per_block * k upper bound
 
+// (done, or null: the scan's completion counter, zeroed here by workgroup 0 for the
+// per-expert scan workgroups that follow; the launch has at least one workgroup)
 __global__ __launch_bounds__(kThreads) void dispatch_hist_kernel(
     const int32_t* __restrict__ topk_idx, int64_t n, int k, int E, int64_t tpb,
-    int64_t n_blocks, int32_t* __restrict__ blk_hist) {
+    int64_t n_blocks, int32_t* __restrict__ blk_hist, int32_t* __restrict__ done) {
   __shared__ int32_t h[kMaxExperts];
+  if (done && blockIdx.x == 0 && threadIdx.x == 0) done[0] = 0;
+  if (static_cast<int64_t>(blockIdx.x) >= n_blocks) return;
   for (int e = threadIdx.x; e < E; e += kThreads) h[e] = 0;
   __syncthreads();
   const int64_t t0 = static_cast<int64_t>(blockIdx.x) * tpb;
@@ -95,40 +101,14 @@ __device__ __forceinline__ int block_incl_scan(int v, int* wsum, int& total) {
   return off + incl;
 }
 
-// One workgroup per expert: exclusive scan of its chunk counts -> blk_base, and the
-// kept count min(total, limit).  Without `room` the limit is `capacity` (< 0: none).
-// With `room` (re-routing) the limit is `capacity` if >= 0, else room[e], and room[e]
-// becomes limit - kept.
-__global__ __launch_bounds__(kThreads) void dispatch_scan_kernel(
-    const int32_t* __restrict__ blk_hist, int64_t n_blocks, int64_t capacity,
-    int32_t* __restrict__ blk_base, int32_t* __restrict__ kept, int32_t* __restrict__ room) {
-  __shared__ int wsum[kThreads / kWave];
-  const int e = blockIdx.x;
-  int running = 0;
-  for (int64_t b0 = 0; b0 < n_blocks; b0 += kThreads) {
-    const int64_t b = b0 + threadIdx.x;
-    const int v = (b < n_blocks) ? blk_hist[e * n_blocks + b] : 0;
-    int chunk_total;
-    const int incl = block_incl_scan(v, wsum, chunk_total);
-    if (b < n_blocks) blk_base[e * n_blocks + b] = running + incl - v;
-    running += chunk_total;
-  }
-  if (threadIdx.x == kThreads - 1) {
-    const int64_t lim = (room && capacity < 0) ? room[e] : capacity;
-    const int64_t kc = (lim >= 0 && running > lim) ? lim : running;
-    kept[e] = static_cast<int32_t>(kc);
-    if (room) room[e] = static_cast<int32_t>(lim - kc);
-  }
-}
-
-// One workgroup: exclusive scan of the kept counts over experts -> expert_offsets, the
-// dropped count and (optional) the drop rate n_dropped / (N k) and a zeroed counter.
-__global__ __launch_bounds__(kThreads) void dispatch_offsets_kernel(
+// Exclusive scan of the kept counts over experts -> expert_offsets, the dropped count
+// and (optional) the drop rate n_dropped / (N k), a zeroed counter and the tile-height
+// flag.  Run by one whole workgroup.
+__device__ __forceinline__ void offsets_body(
     const int32_t* __restrict__ kept, int E, int64_t n_assign,
     int32_t* __restrict__ expert_offsets, int32_t* __restrict__ kept_count,
     int32_t* __restrict__ n_dropped, float* __restrict__ drop_rate,
-    int32_t* __restrict__ zero_out, int32_t* __restrict__ small_tiles) {
-  __shared__ int wsum[kThreads / kWave];
+    int32_t* __restrict__ zero_out, int32_t* __restrict__ small_tiles, int* wsum) {
   int running = 0, nonempty = 0;
   for (int e0 = 0; e0 < E; e0 += kThreads) {
     const int e = e0 + threadIdx.x;
@@ -157,13 +137,58 @@ __global__ __launch_bounds__(kThreads) void dispatch_offsets_kernel(
   }
 }
 
+// One workgroup per expert: exclusive scan of its chunk counts -> blk_base, and the
+// kept count min(total, limit).  Without `room` the limit is `capacity` (< 0: none).
+// With `room` (re-routing) the limit is `capacity` if >= 0, else room[e], and room[e]
+// becomes limit - kept.
+// With `done` (the counter dispatch_hist_kernel zeroed) the workgroup that finishes
+// last also runs offsets_body over every expert's kept count, so the dispatch's
+// capacity plan takes one launch: each workgroup publishes kept[e] with an agent-scope
+// release before taking its ticket, and the last one acquires before reading them.
+__global__ __launch_bounds__(kThreads) void dispatch_scan_kernel(
+    const int32_t* __restrict__ blk_hist, int64_t n_blocks, int64_t capacity,
+    int32_t* __restrict__ blk_base, int32_t* kept, int32_t* __restrict__ room,
+    int32_t* done, int64_t n_assign, int32_t* __restrict__ expert_offsets,
+    int32_t* __restrict__ kept_count, int32_t* __restrict__ n_dropped,
+    float* __restrict__ drop_rate, int32_t* __restrict__ zero_out,
+    int32_t* __restrict__ small_tiles) {
+  __shared__ int wsum[kThreads / kWave];
+  __shared__ int last;
+  const int e = blockIdx.x;
+  int running = 0;
+  for (int64_t b0 = 0; b0 < n_blocks; b0 += kThreads) {
+    const int64_t b = b0 + threadIdx.x;
+    const int v = (b < n_blocks) ? blk_hist[e * n_blocks + b] : 0;
+    int chunk_total;
+    const int incl = block_incl_scan(v, wsum, chunk_total);
+    if (b < n_blocks) blk_base[e * n_blocks + b] = running + incl - v;
+    running += chunk_total;
+  }
+  if (threadIdx.x == kThreads - 1) {
+    const int64_t lim = (room && capacity < 0) ? room[e] : capacity;
+    const int64_t kc = (lim >= 0 && running > lim) ? lim : running;
+    kept[e] = static_cast<int32_t>(kc);
+    if (room) room[e] = static_cast<int32_t>(lim - kc);
+    if (done) {
+      const int ticket = __hip_atomic_fetch_add(done, 1, __ATOMIC_ACQ_REL, __HIP_MEMORY_SCOPE_AGENT);
+      last = ticket == static_cast<int>(gridDim.x) - 1;
+    }
+  }
+  if (!done) return;
+  __syncthreads();
+  if (!last) return;
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");  // every workgroup's kept[e] is visible
+  offsets_body(kept, static_cast<int>(gridDim.x), n_assign, expert_offsets, kept_count, n_dropped,
+               drop_rate, zero_out, small_tiles, wsum);
+}
+
 __global__ __launch_bounds__(kThreads) void dispatch_scatter_kernel(
     const int32_t* __restrict__ topk_idx, int64_t n, int k, int E, int64_t tpb,
     int64_t n_blocks, int64_t capacity, const int32_t* __restrict__ blk_base,
     const int32_t* __restrict__ expert_offsets, int32_t* __restrict__ row_token,
     int32_t* __restrict__ slot_row, const float* __restrict__ topk_w,
     float* __restrict__ row_weight, const uint8_t* __restrict__ x, int64_t row_bytes,
-    uint8_t* __restrict__ x_perm) {
+    uint8_t* __restrict__ x_perm, uint8_t* __restrict__ zero_out, int64_t zero_row_bytes) {
   __shared__ int32_t cnt[kMaxExperts];
   __shared__ int32_t srow[kMaxChunkItems];
   for (int e = threadIdx.x; e < E; e += kThreads) cnt[e] = 0;
@@ -188,8 +213,22 @@ __global__ __launch_bounds__(kThreads) void dispatch_scatter_kernel(
       srow[q - q_begin] = r;
     });
   }
-  if (x_perm == nullptr) return;
+  if (x_perm == nullptr && zero_out == nullptr) return;
   __syncthreads();
+
+  // top-1 layers whose expert rows go straight to their tokens' output rows: the rows
+  // of tokens whose only slot was dropped are zeroed here (16-byte stores)
+  if (zero_out != nullptr) {
+    const int64_t zvpr = zero_row_bytes / 16;
+    const int64_t nz = (t1 - t0) * zvpr;
+    for (int64_t i = threadIdx.x; i < nz; i += kThreads) {
+      const int64_t tt = i / zvpr;
+      if (srow[tt] < 0)
+        *reinterpret_cast<uint4*>(zero_out + (t0 + tt) * zero_row_bytes + (i - tt * zvpr) * 16) =
+            make_uint4(0u, 0u, 0u, 0u);
+    }
+  }
+  if (x_perm == nullptr) return;
 
   // copy: 16-byte vectors, each x row read once and written to each kept row
   const int64_t vpr = row_bytes / 16;
@@ -414,21 +453,20 @@ hipError_t launch_dispatch(hipStream_t st, const int32_t* topk_idx, int64_t n, i
                            int32_t* expert_offsets, int32_t* row_token, int32_t* slot_row,
                            int32_t* kept_count, int32_t* n_dropped, void* x_perm,
                            int32_t* blk_hist, int32_t* blk_base, int32_t* kept_tmp,
+                           int32_t* done,
                            const float* topk_w, float* row_weight, float* drop_rate,
-                           int32_t* zero_out, int32_t* small_tiles) {
+                           int32_t* zero_out, int32_t* small_tiles, void* zero_rows,
+                           int64_t zero_row_bytes) {
   const DispatchGrid g = dispatch_grid(n, k);
-  if (g.n_blocks > 0) {
-    hipLaunchKernelGGL(dispatch_hist_kernel, dim3(static_cast<unsigned>(g.n_blocks)),
-                       dim3(kThreads), 0, st, topk_idx, n, k, e, g.tokens_per_block,
-                       g.n_blocks, blk_hist);
-    hipError_t err = hipGetLastError();
-    if (err != hipSuccess) return err;
-  }
-  hipLaunchKernelGGL(dispatch_scan_kernel, dim3(static_cast<unsigned>(e)), dim3(kThreads), 0, st,
-                     blk_hist, g.n_blocks, capacity, blk_base, kept_tmp, nullptr);
+  // histogram (at least one workgroup: it also zeroes the scan's counter), then the
+  // per-expert scans, the last of which lays out the expert offsets
+  hipLaunchKernelGGL(dispatch_hist_kernel, dim3(static_cast<unsigned>(std::max<int64_t>(g.n_blocks, 1))),
+                     dim3(kThreads), 0, st, topk_idx, n, k, e, g.tokens_per_block,
+                     g.n_blocks, blk_hist, done);
   hipError_t err = hipGetLastError();
   if (err != hipSuccess) return err;
-  hipLaunchKernelGGL(dispatch_offsets_kernel, dim3(1), dim3(kThreads), 0, st, kept_tmp, e, n * k,
+  hipLaunchKernelGGL(dispatch_scan_kernel, dim3(static_cast<unsigned>(e)), dim3(kThreads), 0, st,
+                     blk_hist, g.n_blocks, capacity, blk_base, kept_tmp, nullptr, done, n * k,
                      expert_offsets, kept_count, n_dropped, drop_rate, zero_out, small_tiles);
   err = hipGetLastError();
   if (err != hipSuccess || g.n_blocks == 0) return err;
@@ -436,7 +474,8 @@ hipError_t launch_dispatch(hipStream_t st, const int32_t* topk_idx, int64_t n, i
                      dim3(kThreads), 0, st, topk_idx, n, k, e, g.tokens_per_block,
                      g.n_blocks, capacity, blk_base, expert_offsets, row_token, slot_row,
                      topk_w, row_weight, static_cast<const uint8_t*>(x), row_bytes,
-                     static_cast<uint8_t*>(x_perm));
+                     static_cast<uint8_t*>(x_perm), k == 1 ? static_cast<uint8_t*>(zero_rows) : nullptr,
+                     zero_row_bytes);
   return hipGetLastError();
 }
 
@@ -453,11 +492,12 @@ hipError_t launch_reroute(hipStream_t st, const float* logits, const float* bias
   const int64_t tpb = g.tokens_per_block;
   // round 0: the plain capacity rule
   hipLaunchKernelGGL(dispatch_hist_kernel, grid, blk, 0, st, topk_idx, n, k, e, tpb, g.n_blocks,
-                     w.blk_hist);
+                     w.blk_hist, nullptr);
   hipError_t err = hipGetLastError();
   if (err != hipSuccess) return err;
   hipLaunchKernelGGL(dispatch_scan_kernel, dim3(static_cast<unsigned>(e)), blk, 0, st, w.blk_hist,
-                     g.n_blocks, capacity, w.blk_base, w.kept, w.room);
+                     g.n_blocks, capacity, w.blk_base, w.kept, w.room, nullptr, 0, nullptr,
+                     nullptr, nullptr, nullptr, nullptr, nullptr);
   if ((err = hipGetLastError()) != hipSuccess) return err;
   hipLaunchKernelGGL(reroute_accept_kernel, grid, blk, 0, st, topk_idx, n, k, e, tpb, g.n_blocks,
                      w.blk_base, w.kept, 1, logits, bias, topk_idx, w.state, w.thr_z, w.thr_e,
@@ -478,7 +518,8 @@ hipError_t launch_reroute(hipStream_t st, const float* logits, const float* bias
     }
     if ((err = hipGetLastError()) != hipSuccess) return err;
     hipLaunchKernelGGL(dispatch_scan_kernel, dim3(static_cast<unsigned>(e)), blk, 0, st,
-                       w.blk_hist, g.n_blocks, int64_t{-1}, w.blk_base, w.kept, w.room);
+                       w.blk_hist, g.n_blocks, int64_t{-1}, w.blk_base, w.kept, w.room, nullptr,
+                       0, nullptr, nullptr, nullptr, nullptr, nullptr, nullptr);
     if ((err = hipGetLastError()) != hipSuccess) return err;
     hipLaunchKernelGGL(reroute_accept_kernel, grid, blk, 0, st, w.props, n, k, e, tpb,
                        g.n_blocks, w.blk_base, w.kept, 0, logits, bias, topk_idx, w.state,

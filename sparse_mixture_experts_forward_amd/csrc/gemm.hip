@@ -1449,30 +1449,39 @@ __global__ __launch_bounds__(kThreads, 2) void gemm_packed_small_kernel(GemmArgs
 
 // ------------------------------------------------------------------ packed-weight kernel, mid-size segments
 // Segments of a few dozen to a few hundred rows (fine-grained experts, capacity-limited
-// batches): the products are bound by the weight stream, so every (segment, column
-// tile) is one work item that reads its weights once.  A tile is up to 256 activation
-// rows (a whole segment of up to 256 rows) x 256 packed weight rows; each of the 4 waves
-// streams 64 weight rows of its own (SwiGLU: 32 rows of W1 and the same 32 of W3) from
-// the packed copy into a register ring (each k-step's 2 fragments loaded 15 k-steps
-// ahead) and multiplies them with all of the tile's active row blocks, which pass
-// through LDS (4 stages of 64 k, direct-to-LDS loads 4 stages ahead).  Only the
-// active row blocks (TA of 8) are loaded and multiplied, so a tile's MFMA work and
-// activation traffic follow its rows while its weight traffic is that of one pass.
+// batches): the products are bound by the weight stream.  A tile is up to BM activation
+// rows x 256 packed weight rows; each of the 4 waves streams 64 weight rows of its own
+// (SwiGLU: 32 rows of W1 and the same 32 of W3) from the packed copy into a register
+// ring (each k-step's 2 fragments loaded RING - 1 k-steps ahead) and multiplies them
+// with all of the tile's active row blocks, which pass through LDS (4 stages of 64 k,
+// direct-to-LDS loads 4 stages ahead).  Only the active row blocks (TA of BM / 32) are
+// loaded and multiplied, so a tile's MFMA work and activation traffic follow its rows.
 // Activation load j of wave w fills the 8-row group 4j + w, so every wave issues TA
 // loads per stage and the in-order wait counts depend on TA only.
-constexpr int kMBM = 256;   // activation rows per tile
+// The shape in use is BM = 256: a whole segment of up to 256 rows per tile, so every
+// (segment, column tile) reads its weights once; one workgroup per CU with a 16-k-step
+// ring.  (BM = 128 with two workgroups per CU and an 8-k-step ring was measured too:
+// the Switch-shaped first layer 0.161 -> 0.148 ms, but its second layer 0.144 -> 0.167
+// and the DeepSeek-shaped first layer 1.06 -> 1.57 ms, where a second row tile
+// re-streams the weights.)
 constexpr int kMBN = 256;   // packed weight rows per tile (two 128-row panels)
-constexpr int kMTM = kMBM / 32;
-// Weight register ring of the mid-size kernel, in k-steps: the products are bound by the
-// weight stream, so each wave keeps 15 k-steps (30 KB) of weight loads in flight.
-constexpr int kMRing = 16;
-constexpr int kMLead = kMRing - 1;
 
+template <int BM_, int RING_>
+struct MidShape {
+  static constexpr int BM = BM_;
+  static constexpr int TMAX = BM / 32;  // activation row blocks
+  static constexpr int RING = RING_;    // weight register ring, in k-steps
+  static constexpr int LEAD = RING - 1;
+  static constexpr int OCC = BM >= 256 ? 1 : 2;  // workgroups per CU
+};
+using MidLarge = MidShape<256, 16>;
+
+template <class MS>
 struct MidIO {
-  const char* a_base;   // uniform: the tile's activation rows (or a, with a gather)
-  uint32_t a_off[kMTM]; // load j: 8-row group 4j + wave, this lane's row and 16 bytes
-  const char* w_base;   // uniform: this wave's 128-row weight panel
-  uint32_t w_off[2];    // this wave's two 32-row blocks of the panel + this lane's 16 bytes
+  const char* a_base;         // uniform: the tile's activation rows (or a, with a gather)
+  uint32_t a_off[MS::TMAX];   // load j: 8-row group 4j + wave, this lane's row and 16 bytes
+  const char* w_base;         // uniform: this wave's 128-row weight panel
+  uint32_t w_off[2];          // this wave's two 32-row blocks of the panel + this lane's 16 bytes
   int a_row;
   int co[4];
   int KT, KS;
@@ -1502,7 +1511,8 @@ struct MidIO {
 #endif
   }
   template <int TA>
-  __device__ __forceinline__ void read_a(const uint16_t* buf, int kstep, bf16x8_t (&a)[kMTM]) const {
+  __device__ __forceinline__ void read_a(const uint16_t* buf, int kstep,
+                                         bf16x8_t (&a)[MS::TMAX]) const {
 #pragma unroll
     for (int tm = 0; tm < TA; ++tm)
       a[tm] = *reinterpret_cast<const bf16x8_t*>(&buf[a_row + tm * 32 * kBK + co[kstep]]);
@@ -1511,103 +1521,107 @@ struct MidIO {
 
 // Stage boundary wait of the mid-size kernel: the next stage's activation loads must
 // have landed; issued after them are at least two later stages' activation loads and
-// kMLead + 3 k-steps' weight loads (fewest at the first boundary: A1 is followed by A2,
+// LEAD + 3 k-steps' weight loads (fewest at the first boundary: A1 is followed by A2,
 // A3, the lead k-steps of the prologue and those issued in k-steps 0..2).
-template <int TA>
+template <class MS, int TA>
 struct MidWait {
-  static constexpr int kBoundary = (kPStages - 2) * TA + 2 * (kMLead + 3);
-  static constexpr int kPrologue = (kPStages - 1) * TA + 2 * kMLead;
+  static constexpr int kBoundary = (kPStages - 2) * TA + 2 * (MS::LEAD + 3);
+  static constexpr int kPrologue = (kPStages - 1) * TA + 2 * MS::LEAD;
   static_assert(kBoundary < 64 && kPrologue < 64, "vmcnt range");
 };
 
-template <int T, int TA>
-__device__ __forceinline__ void md_step(const MidIO& io, uint16_t* const (&A)[kPStages], int t,
-                                        bf16x8_t (&wr)[kMRing][2], bf16x8_t (&af)[2][kMTM],
-                                        f32x16_t (&acc)[2][kMTM]) {
+template <class MS, int T, int TA>
+__device__ __forceinline__ void md_step(const MidIO<MS>& io, uint16_t* const (&A)[kPStages], int t,
+                                        bf16x8_t (&wr)[MS::RING][2],
+                                        bf16x8_t (&af)[2][MS::TMAX],
+                                        f32x16_t (&acc)[2][MS::TMAX]) {
   constexpr int J = T % 4, SB = T / 4;
   if constexpr (J == 3) {
-    barrier_keep_loads<MidWait<TA>::kBoundary>();
+    barrier_keep_loads<MidWait<MS, TA>::kBoundary>();
     io.template dma_a<TA>(A[SB], t / 4 + kPStages);
   }
-  io.load_w(wr[(T + kMLead) % kMRing], t + kMLead);
+  io.load_w(wr[(T + MS::LEAD) % MS::RING], t + MS::LEAD);
   io.template read_a<TA>(A[J == 3 ? (SB + 1) % kPStages : SB], (J + 1) % 4, af[(T + 1) & 1]);
 #pragma unroll
   for (int tn = 0; tn < 2; ++tn)
 #pragma unroll
     for (int tm = 0; tm < TA; ++tm)
-      acc[tn][tm] = Mfma<32>::mma(wr[T % kMRing][tn], af[T & 1][tm], acc[tn][tm]);
+      acc[tn][tm] = Mfma<32>::mma(wr[T % MS::RING][tn], af[T & 1][tm], acc[tn][tm]);
   sched_mix<2 + (J == 3 ? TA : 0), TA, 2 * TA, 0, 8>();
 }
 
-template <int T, int TA>
-__device__ __forceinline__ void md_period(const MidIO& io, uint16_t* const (&A)[kPStages], int t0,
-                                          bf16x8_t (&wr)[kMRing][2], bf16x8_t (&af)[2][kMTM],
-                                          f32x16_t (&acc)[2][kMTM]) {
+template <class MS, int T, int TA>
+__device__ __forceinline__ void md_period(const MidIO<MS>& io, uint16_t* const (&A)[kPStages],
+                                          int t0, bf16x8_t (&wr)[MS::RING][2],
+                                          bf16x8_t (&af)[2][MS::TMAX],
+                                          f32x16_t (&acc)[2][MS::TMAX]) {
   if constexpr (T < 16) {
-    md_step<T, TA>(io, A, t0 + T, wr, af, acc);
-    md_period<T + 1, TA>(io, A, t0, wr, af, acc);
+    md_step<MS, T, TA>(io, A, t0 + T, wr, af, acc);
+    md_period<MS, T + 1, TA>(io, A, t0, wr, af, acc);
   }
 }
 
-template <int T, int TA>
-__device__ __forceinline__ void md_tail(const MidIO& io, uint16_t* const (&A)[kPStages], int t0,
-                                        int rem, bf16x8_t (&wr)[kMRing][2],
-                                        bf16x8_t (&af)[2][kMTM], f32x16_t (&acc)[2][kMTM]) {
+template <class MS, int T, int TA>
+__device__ __forceinline__ void md_tail(const MidIO<MS>& io, uint16_t* const (&A)[kPStages],
+                                        int t0, int rem, bf16x8_t (&wr)[MS::RING][2],
+                                        bf16x8_t (&af)[2][MS::TMAX],
+                                        f32x16_t (&acc)[2][MS::TMAX]) {
   if constexpr (T < 16) {
     if (T < rem) {
-      md_step<T, TA>(io, A, t0 + T, wr, af, acc);
-      md_tail<T + 1, TA>(io, A, t0, rem, wr, af, acc);
+      md_step<MS, T, TA>(io, A, t0 + T, wr, af, acc);
+      md_tail<MS, T + 1, TA>(io, A, t0, rem, wr, af, acc);
     }
   }
 }
 
-template <int EPI, int TA>
-__device__ __forceinline__ void mid_body(const GemmArgs& g, const Tile& tile, const MidIO& io,
+template <class MS, int EPI, int TA>
+__device__ __forceinline__ void mid_body(const GemmArgs& g, const Tile& tile, const MidIO<MS>& io,
                                          uint16_t* const (&A)[kPStages], int lane, int col0) {
-  f32x16_t acc[2][kMTM];
+  static_assert(16 % MS::RING == 0, "the ring period divides the 16-k-step period");
+  f32x16_t acc[2][MS::TMAX];
 #pragma unroll
   for (int tn = 0; tn < 2; ++tn)
 #pragma unroll
     for (int tm = 0; tm < TA; ++tm)
 #pragma unroll
       for (int r = 0; r < 16; ++r) acc[tn][tm][r] = 0.f;
-  bf16x8_t wr[kMRing][2];
-  bf16x8_t af[2][kMTM];
-  // prologue: activation stages 0..3, then weight k-steps 0 .. kMLead - 1 in order
+  bf16x8_t wr[MS::RING][2];
+  bf16x8_t af[2][MS::TMAX];
+  // prologue: activation stages 0..3, then weight k-steps 0 .. LEAD - 1 in order
 #pragma unroll
   for (int st = 0; st < kPStages; ++st) io.template dma_a<TA>(A[st], st);
 #pragma unroll
-  for (int t = 0; t < kMLead; ++t) {
+  for (int t = 0; t < MS::LEAD; ++t) {
     io.load_w(wr[t], t);
     __builtin_amdgcn_sched_barrier(0);
   }
-  barrier_keep_loads<MidWait<TA>::kPrologue>();
+  barrier_keep_loads<MidWait<MS, TA>::kPrologue>();
   io.template read_a<TA>(A[0], 0, af[0]);
   int t0 = 0;
-  for (; t0 + 16 <= io.KS; t0 += 16) md_period<0, TA>(io, A, t0, wr, af, acc);
-  md_tail<0, TA>(io, A, t0, io.KS - t0, wr, af, acc);
+  for (; t0 + 16 <= io.KS; t0 += 16) md_period<MS, 0, TA>(io, A, t0, wr, af, acc);
+  md_tail<MS, 0, TA>(io, A, t0, io.KS - t0, wr, af, acc);
   // no load may still be writing this workgroup's LDS when it exits
   __builtin_amdgcn_s_waitcnt(0);
-  packed_epilogue<EPI, 2, kMTM, TA>(g, tile, lane, col0, acc);
+  packed_epilogue<EPI, 2, MS::TMAX, TA>(g, tile, lane, col0, acc);
 }
 
-template <int EPI>
-__global__ __launch_bounds__(kThreads, 1) void gemm_packed_mid_kernel(GemmArgs g) {
-  __shared__ __attribute__((aligned(16))) uint16_t A0[kMBM * kBK], A1[kMBM * kBK];
-  __shared__ __attribute__((aligned(16))) uint16_t A2[kMBM * kBK], A3[kMBM * kBK];
+template <class MS, int EPI>
+__global__ __launch_bounds__(kThreads, MS::OCC) void gemm_packed_mid_kernel(GemmArgs g) {
+  __shared__ __attribute__((aligned(16))) uint16_t A0[MS::BM * kBK], A1[MS::BM * kBK];
+  __shared__ __attribute__((aligned(16))) uint16_t A2[MS::BM * kBK], A3[MS::BM * kBK];
   __shared__ SchedSmem sched;
   uint16_t* const A[kPStages] = {A0, A1, A2, A3};
   // as the alternative of a 128 x 512 launch (device-chosen height) it runs only where
   // the dispatch chose the short tiles
   if (g.small_tiles && *g.small_tiles != 1) return;
   Tile tile;
-  if (!schedule_tile<kMBM>(g.seg_off, g.n_seg, g.single_rows, g.max_rows, g.bp_rows / kMBN,
-                           g.k / kBK, 0, nullptr, sched, tile))
+  if (!schedule_tile<MS::BM>(g.seg_off, g.n_seg, g.single_rows, g.max_rows, g.bp_rows / kMBN,
+                             g.k / kBK, 0, nullptr, sched, tile))
     return;
   const int tid = threadIdx.x;
   const int lane = tid & (kWave - 1);
   const int wave = __builtin_amdgcn_readfirstlane(tid / kWave);
-  MidIO io;
+  MidIO<MS> io;
   io.wave = wave;
   io.KT = g.k / kBK;
   io.KS = 4 * io.KT;
@@ -1615,7 +1629,7 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_packed_mid_kernel(GemmArgs g
   io.a_base = uniform_ptr(reinterpret_cast<const char*>(
       static_cast<const uint16_t*>(g.a) + (a_rows ? 0 : tile.row0 * g.lda)));
 #pragma unroll
-  for (int j = 0; j < kMTM; ++j) {
+  for (int j = 0; j < MS::TMAX; ++j) {
     const int i = 8 * (4 * j + wave) + (lane >> 3);  // LDS row of the tile
     const int r = min(i, tile.m_valid - 1);          // rows past the segment repeat its last row
     const uint32_t src = a_rows ? static_cast<uint32_t>(a_rows[tile.row0 + r]) : r;
@@ -1639,16 +1653,24 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_packed_mid_kernel(GemmArgs g
 #pragma unroll
   for (int ks = 0; ks < 4; ++ks) io.co[ks] = (Mfma<32>::chunk(lane, ks) ^ lds_swizzle(frow)) * 8;
   io.a_row = frow * kBK;
-  const int ta = __builtin_amdgcn_readfirstlane(min((tile.m_valid + 31) / 32, kMTM));
+  const int ta = __builtin_amdgcn_readfirstlane(min((tile.m_valid + 31) / 32, MS::TMAX));
   switch (ta) {
-    case 1: mid_body<EPI, 1>(g, tile, io, A, lane, col0); break;
-    case 2: mid_body<EPI, 2>(g, tile, io, A, lane, col0); break;
-    case 3: mid_body<EPI, 3>(g, tile, io, A, lane, col0); break;
-    case 4: mid_body<EPI, 4>(g, tile, io, A, lane, col0); break;
-    case 5: mid_body<EPI, 5>(g, tile, io, A, lane, col0); break;
-    case 6: mid_body<EPI, 6>(g, tile, io, A, lane, col0); break;
-    case 7: mid_body<EPI, 7>(g, tile, io, A, lane, col0); break;
-    default: mid_body<EPI, 8>(g, tile, io, A, lane, col0); break;
+    case 1: mid_body<MS, EPI, 1>(g, tile, io, A, lane, col0); break;
+    case 2: mid_body<MS, EPI, 2>(g, tile, io, A, lane, col0); break;
+    case 3: mid_body<MS, EPI, 3>(g, tile, io, A, lane, col0); break;
+    default:
+      if constexpr (MS::TMAX == 4) {
+        mid_body<MS, EPI, 4>(g, tile, io, A, lane, col0);
+      } else {
+        switch (ta) {
+          case 4: mid_body<MS, EPI, 4>(g, tile, io, A, lane, col0); break;
+          case 5: mid_body<MS, EPI, 5>(g, tile, io, A, lane, col0); break;
+          case 6: mid_body<MS, EPI, 6>(g, tile, io, A, lane, col0); break;
+          case 7: mid_body<MS, EPI, 7>(g, tile, io, A, lane, col0); break;
+          default: mid_body<MS, EPI, MS::TMAX>(g, tile, io, A, lane, col0); break;
+        }
+      }
+      break;
   }
 }
 
@@ -1810,11 +1832,12 @@ hipError_t launch_bf16_bm(hipStream_t st, GemmArgs g, int64_t max_rows, bool ksp
 
 template <int EPI>
 hipError_t launch_packed_mid(hipStream_t st, GemmArgs g, int64_t max_rows) {
+  using MS = MidLarge;
   const int n_seg_eff = g.seg_off ? g.n_seg : 1;
-  const int64_t grid = grid_for(max_rows, n_seg_eff, kMBM, g.bp_rows / kMBN);
+  const int64_t grid = grid_for(max_rows, n_seg_eff, MS::BM, g.bp_rows / kMBN);
   if (grid <= 0) return hipSuccess;
   g.split_g = 0;
-  hipLaunchKernelGGL((gemm_packed_mid_kernel<EPI>), dim3(static_cast<unsigned>(grid)),
+  hipLaunchKernelGGL((gemm_packed_mid_kernel<MS, EPI>), dim3(static_cast<unsigned>(grid)),
                      dim3(kThreads), 0, st, g);
   return hipGetLastError();
 }

@@ -24,7 +24,7 @@ inline int64_t route_blocks(int64_t n_tokens) {
 hipError_t launch_route(hipStream_t st, const float* x, int64_t n, int64_t d,
                         const float* w_router, const float* logit_bias, int e, int k,
                         int renorm, float* logits_out, int32_t* topk_idx, float* topk_w,
-                        float* part_prob, int32_t* part_cnt, float* part_mon);
+                        float* part_prob, int32_t* part_cnt, float* part_mon, int32_t* done);
 
 // bf16 router: exact three-part bf16 split of W_router, the sliced logits product and
 // the gate over the slices' partial logits.
@@ -56,7 +56,7 @@ hipError_t launch_route_logits(hipStream_t st, const uint16_t* x, const RoutePla
 hipError_t launch_route_gate(hipStream_t st, const float* part, int ks, int64_t n, int e,
                              const float* bias, int k, int renorm, float* logits_out,
                              int32_t* topk_idx, float* topk_w, float* part_prob,
-                             int32_t* part_cnt, float* part_mon);
+                             int32_t* part_cnt, float* part_mon, int32_t* done);
 
 // Batch-level bias update: b[e] -= gamma if sel_count[e]*E > N*k, += gamma if below.
 hipError_t launch_update_bias(hipStream_t st, const int32_t* sel_count, int e, int64_t n, int k,
@@ -65,11 +65,14 @@ hipError_t launch_update_bias(hipStream_t st, const int32_t* sel_count, int e, i
 // Statistics over `rows` partial rows: per-expert workgroups (sel_count, prob_mean and
 // the aux terms; `term` E doubles and `cnt` E counts of scratch), then aux and, if
 // `monitor` is given, z-loss, mean top-k entropy, sum of squared load shares and load
-// CV (monitor[0..3]; part_mon holds two floats per row).
+// CV (monitor[0..3]; part_mon holds two floats per row).  done [1]: a counter that the
+// gate launch before (launch_route, launch_route_gate with the same `done`) zeroes; with
+// it the statistics take one launch.
 hipError_t launch_route_finalize(hipStream_t st, const float* part_prob,
                                  const int32_t* part_cnt, const float* part_mon, int64_t rows,
                                  int64_t n, int e, int k, int32_t* sel_count, float* prob_mean,
-                                 float* aux, float* monitor, double* term, int64_t* cnt);
+                                 float* aux, float* monitor, double* term, int64_t* cnt,
+                                 int32_t* done);
 
 
 // ---------------------------------------------------------------- dispatch
@@ -85,13 +88,19 @@ constexpr int kBigSegRows = 48;
 
 // small_tiles (or null): set to 1 when the kept rows average fewer than kBigSegRows per
 // expert that kept any, else 0 (read by the expert GEMM launches, see GemmArgs).
+// blk_hist / blk_base [E][n_blocks], kept_tmp [E] and done [1]: scratch.
+// zero_rows (or null, k == 1 only): the output [N][zero_row_bytes] whose rows of tokens
+// with their slot dropped are zeroed (the kept rows are written by the second expert
+// product straight into their tokens' rows).
 hipError_t launch_dispatch(hipStream_t st, const int32_t* topk_idx, int64_t n, int k, int e,
                            int64_t capacity, const void* x, int64_t row_bytes,
                            int32_t* expert_offsets, int32_t* row_token, int32_t* slot_row,
                            int32_t* kept_count, int32_t* n_dropped, void* x_perm,
                            int32_t* blk_hist, int32_t* blk_base, int32_t* kept_tmp,
-                           const float* topk_w, float* row_weight, float* drop_rate = nullptr,
-                           int32_t* zero_out = nullptr, int32_t* small_tiles = nullptr);
+                           int32_t* done, const float* topk_w, float* row_weight,
+                           float* drop_rate = nullptr,
+                           int32_t* zero_out = nullptr, int32_t* small_tiles = nullptr,
+                           void* zero_rows = nullptr, int64_t zero_row_bytes = 0);
 
 // Workspace of the overflow re-routing (all device arrays): blk_hist / blk_base
 // [E][n_blocks] (dispatch_grid), kept / room [E], state [N*k], thr_z / thr_e [N],

@@ -144,8 +144,10 @@ __global__ __launch_bounds__(kThreads) void route_kernel(
     const float* __restrict__ bias, int E, int k, int flags,
     const float* __restrict__ logits_in, float* __restrict__ logits_out,
     int32_t* __restrict__ topk_idx, float* __restrict__ topk_w,
-    float* __restrict__ part_prob, int32_t* __restrict__ part_cnt, float* __restrict__ part_mon) {
+    float* __restrict__ part_prob, int32_t* __restrict__ part_cnt, float* __restrict__ part_mon,
+    int32_t* __restrict__ done) {
   constexpr int EP = ET * 16;             // padded expert count (LDS row stride)
+  if (done && blockIdx.x == 0 && threadIdx.x == 0) done[0] = 0;  // the statistics' counter
   const int renorm = flags & kGateRenorm, sel_only = (flags & kGateSelectionOnly) ? 1 : 0;
   const int monitor = (flags & kGateMonitor) ? 1 : 0;
   float lse2 = 0.f, ent = 0.f;
@@ -446,8 +448,9 @@ __global__ __launch_bounds__(kThreads) void route_gate_kernel(
     const float* __restrict__ part, int ks, int64_t n, int E, const float* __restrict__ bias,
     int k, int flags, int tpw, float* __restrict__ logits_out, int32_t* __restrict__ topk_idx,
     float* __restrict__ topk_w, float* __restrict__ part_prob, int32_t* __restrict__ part_cnt,
-    float* __restrict__ part_mon) {
+    float* __restrict__ part_mon, int32_t* __restrict__ done) {
   constexpr int EP = VPL * kWave;
+  if (done && blockIdx.x == 0 && threadIdx.x == 0) done[0] = 0;  // the statistics' counter
   const int renorm = flags & kGateRenorm, sel_only = (flags & kGateSelectionOnly) ? 1 : 0;
   const int monitor = (flags & kGateMonitor) ? 1 : 0;
   float lse2 = 0.f, ent = 0.f;
@@ -504,60 +507,12 @@ __global__ __launch_bounds__(kThreads) void route_gate_kernel(
 // One workgroup per expert: thread j adds rows j, j + 256, ... of the partials in order
 // (float64), then a fixed-shape tree over the 256 threads; writes sel_count, prob_mean
 // and the expert's aux term (count / (N k)) * prob_mean.
-__global__ __launch_bounds__(kThreads) void route_stats_kernel(
-    const float* __restrict__ part_prob, const int32_t* __restrict__ part_cnt, int64_t rows,
-    int64_t n, int E, int k, int32_t* __restrict__ sel_count, float* __restrict__ prob_mean,
-    double* __restrict__ term, int64_t* __restrict__ cnt) {
-  __shared__ double sp[kThreads];
-  __shared__ int64_t sc[kThreads];
-  const int e = blockIdx.x;
-  double ps = 0.0;
-  int64_t cs = 0;
-  for (int64_t b = threadIdx.x; b < rows; b += kThreads) {
-    ps += static_cast<double>(part_prob[b * E + e]);
-    cs += part_cnt[b * E + e];
-  }
-  sp[threadIdx.x] = ps;
-  sc[threadIdx.x] = cs;
-  __syncthreads();
-  for (int s = kThreads / 2; s >= 1; s >>= 1) {
-    if (threadIdx.x < s) {
-      sp[threadIdx.x] += sp[threadIdx.x + s];
-      sc[threadIdx.x] += sc[threadIdx.x + s];
-    }
-    __syncthreads();
-  }
-  if (threadIdx.x == 0) {
-    const double pm = n > 0 ? sp[0] / static_cast<double>(n) : 0.0;
-    const double fr = n > 0 ? static_cast<double>(sc[0]) / static_cast<double>(n * k) : 0.0;
-    if (sel_count) sel_count[e] = static_cast<int32_t>(sc[0]);
-    if (prob_mean) prob_mean[e] = static_cast<float>(pm);
-    term[e] = fr * pm;
-    cnt[e] = sc[0];
-  }
-}
-
-// Batch-level bias update of the bias-for-selection scheme ([Why-MoE] §2.4): an expert
-// chosen more often than the mean load N*k/E (compared as sel_count*E against N*k, in
-// integers) has gamma subtracted from its bias, one chosen less often gamma added.
-__global__ __launch_bounds__(kThreads) void route_update_bias_kernel(
-    const int32_t* __restrict__ sel_count, int E, int64_t nk, float gamma,
-    float* __restrict__ logit_bias) {
-  const int e = blockIdx.x * kThreads + threadIdx.x;
-  if (e >= E) return;
-  const int64_t load = static_cast<int64_t>(sel_count[e]) * E;
-  const float b = logit_bias[e];
-  logit_bias[e] = load > nk ? __fsub_rn(b, gamma) : (load < nk ? __fadd_rn(b, gamma) : b);
-}
-
-// aux = E * sum_e term[e], the sum over a fixed-shape tree.  With monitor (4 floats):
-// z-loss 0.001 * (sum of the rows' logsumexp^2) / N, the mean top-k entropy, the sum
-// over experts of (count / N)^2 and the count's standard deviation over its mean.
-__global__ __launch_bounds__(kThreads) void route_aux_kernel(
-    const double* __restrict__ term, const int64_t* __restrict__ cnt,
-    const float* __restrict__ part_mon, int64_t rows, int64_t n, int E,
-    float* __restrict__ aux, float* __restrict__ monitor) {
-  __shared__ double red[5][kThreads];
+// Sums of the aux terms, monitoring partials and load moments over a fixed tree, then
+// aux = E * sum of terms and the monitoring signals.  Run by one whole workgroup.
+__device__ __forceinline__ void aux_body(const double* term, const int64_t* cnt,
+                                         const float* __restrict__ part_mon, int64_t rows,
+                                         int64_t n, int E, float* __restrict__ aux,
+                                         float* __restrict__ monitor, double (&red)[5][kThreads]) {
   double v[5] = {0.0, 0.0, 0.0, 0.0, 0.0};
   for (int e = threadIdx.x; e < E; e += kThreads) v[0] += term[e];
   if (monitor) {
@@ -594,16 +549,89 @@ __global__ __launch_bounds__(kThreads) void route_aux_kernel(
   }
 }
 
+// With `done` (zeroed by the gate launch before it) the workgroup that finishes last
+// also runs aux_body, so the statistics take one launch: each workgroup publishes its
+// term and count with an agent-scope release before taking its ticket, and the last one
+// acquires before reading them all.
+__global__ __launch_bounds__(kThreads) void route_stats_kernel(
+    const float* __restrict__ part_prob, const int32_t* __restrict__ part_cnt, int64_t rows,
+    int64_t n, int E, int k, int32_t* __restrict__ sel_count, float* __restrict__ prob_mean,
+    double* term, int64_t* cnt, int32_t* done, const float* __restrict__ part_mon,
+    float* __restrict__ aux, float* __restrict__ monitor) {
+  __shared__ double sp[kThreads];
+  __shared__ int64_t sc[kThreads];
+  __shared__ int last;
+  const int e = blockIdx.x;
+  double ps = 0.0;
+  int64_t cs = 0;
+  for (int64_t b = threadIdx.x; b < rows; b += kThreads) {
+    ps += static_cast<double>(part_prob[b * E + e]);
+    cs += part_cnt[b * E + e];
+  }
+  sp[threadIdx.x] = ps;
+  sc[threadIdx.x] = cs;
+  __syncthreads();
+  for (int s = kThreads / 2; s >= 1; s >>= 1) {
+    if (threadIdx.x < s) {
+      sp[threadIdx.x] += sp[threadIdx.x + s];
+      sc[threadIdx.x] += sc[threadIdx.x + s];
+    }
+    __syncthreads();
+  }
+  if (threadIdx.x == 0) {
+    const double pm = n > 0 ? sp[0] / static_cast<double>(n) : 0.0;
+    const double fr = n > 0 ? static_cast<double>(sc[0]) / static_cast<double>(n * k) : 0.0;
+    if (sel_count) sel_count[e] = static_cast<int32_t>(sc[0]);
+    if (prob_mean) prob_mean[e] = static_cast<float>(pm);
+    term[e] = fr * pm;
+    cnt[e] = sc[0];
+    if (done) {
+      const int ticket = __hip_atomic_fetch_add(done, 1, __ATOMIC_ACQ_REL, __HIP_MEMORY_SCOPE_AGENT);
+      last = ticket == E - 1;
+    }
+  }
+  if (!done || !(aux || monitor)) return;
+  __syncthreads();
+  if (!last) return;
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");  // every workgroup's term and count
+  __shared__ double red[5][kThreads];
+  aux_body(term, cnt, part_mon, rows, n, E, aux, monitor, red);
+}
+
+// Batch-level bias update of the bias-for-selection scheme ([Why-MoE] §2.4): an expert
+// chosen more often than the mean load N*k/E (compared as sel_count*E against N*k, in
+// integers) has gamma subtracted from its bias, one chosen less often gamma added.
+__global__ __launch_bounds__(kThreads) void route_update_bias_kernel(
+    const int32_t* __restrict__ sel_count, int E, int64_t nk, float gamma,
+    float* __restrict__ logit_bias) {
+  const int e = blockIdx.x * kThreads + threadIdx.x;
+  if (e >= E) return;
+  const int64_t load = static_cast<int64_t>(sel_count[e]) * E;
+  const float b = logit_bias[e];
+  logit_bias[e] = load > nk ? __fsub_rn(b, gamma) : (load < nk ? __fadd_rn(b, gamma) : b);
+}
+
+// aux = E * sum_e term[e], the sum over a fixed-shape tree.  With monitor (4 floats):
+// z-loss 0.001 * (sum of the rows' logsumexp^2) / N, the mean top-k entropy, the sum
+// over experts of (count / N)^2 and the count's standard deviation over its mean.
+__global__ __launch_bounds__(kThreads) void route_aux_kernel(
+    const double* __restrict__ term, const int64_t* __restrict__ cnt,
+    const float* __restrict__ part_mon, int64_t rows, int64_t n, int E,
+    float* __restrict__ aux, float* __restrict__ monitor) {
+  __shared__ double red[5][kThreads];
+  aux_body(term, cnt, part_mon, rows, n, E, aux, monitor, red);
+}
+
 
 template <typename XT, int ET>
 hipError_t launch_route_t(hipStream_t st, const void* x, int64_t n, int64_t d,
                           const float* wr, const float* bias, int e, int k, int renorm,
                           const float* logits_in, float* logits_out, int32_t* idx,
-                          float* w, float* pp, int32_t* pc, float* pm) {
+                          float* w, float* pp, int32_t* pc, float* pm, int32_t* done) {
   const int64_t blocks = route_blocks(n);
   hipLaunchKernelGGL((route_kernel<XT, ET>), dim3(static_cast<unsigned>(blocks)),
                      dim3(kThreads), 0, st, static_cast<const XT*>(x), n, d, wr, bias, e, k,
-                     renorm, logits_in, logits_out, idx, w, pp, pc, pm);
+                     renorm, logits_in, logits_out, idx, w, pp, pc, pm, done);
   return hipGetLastError();
 }
 
@@ -611,15 +639,15 @@ template <typename XT>
 hipError_t launch_route_dt(hipStream_t st, const void* x, int64_t n, int64_t d,
                            const float* wr, const float* bias, int e, int k, int renorm,
                            const float* li, float* lo, int32_t* idx, float* w, float* pp,
-                           int32_t* pc, float* pm) {
+                           int32_t* pc, float* pm, int32_t* done) {
   const int n_et = (e + 15) / 16;
-  if (n_et <= 1) return launch_route_t<XT, 1>(st, x, n, d, wr, bias, e, k, renorm, li, lo, idx, w, pp, pc, pm);
-  if (n_et <= 2) return launch_route_t<XT, 2>(st, x, n, d, wr, bias, e, k, renorm, li, lo, idx, w, pp, pc, pm);
-  if (n_et <= 4) return launch_route_t<XT, 4>(st, x, n, d, wr, bias, e, k, renorm, li, lo, idx, w, pp, pc, pm);
-  if (n_et <= 8) return launch_route_t<XT, 8>(st, x, n, d, wr, bias, e, k, renorm, li, lo, idx, w, pp, pc, pm);
-  if (n_et <= 10) return launch_route_t<XT, 10>(st, x, n, d, wr, bias, e, k, renorm, li, lo, idx, w, pp, pc, pm);
-  if (n_et <= 16) return launch_route_t<XT, 16>(st, x, n, d, wr, bias, e, k, renorm, li, lo, idx, w, pp, pc, pm);
-  return launch_route_t<XT, 32>(st, x, n, d, wr, bias, e, k, renorm, li, lo, idx, w, pp, pc, pm);
+  if (n_et <= 1) return launch_route_t<XT, 1>(st, x, n, d, wr, bias, e, k, renorm, li, lo, idx, w, pp, pc, pm, done);
+  if (n_et <= 2) return launch_route_t<XT, 2>(st, x, n, d, wr, bias, e, k, renorm, li, lo, idx, w, pp, pc, pm, done);
+  if (n_et <= 4) return launch_route_t<XT, 4>(st, x, n, d, wr, bias, e, k, renorm, li, lo, idx, w, pp, pc, pm, done);
+  if (n_et <= 8) return launch_route_t<XT, 8>(st, x, n, d, wr, bias, e, k, renorm, li, lo, idx, w, pp, pc, pm, done);
+  if (n_et <= 10) return launch_route_t<XT, 10>(st, x, n, d, wr, bias, e, k, renorm, li, lo, idx, w, pp, pc, pm, done);
+  if (n_et <= 16) return launch_route_t<XT, 16>(st, x, n, d, wr, bias, e, k, renorm, li, lo, idx, w, pp, pc, pm, done);
+  return launch_route_t<XT, 32>(st, x, n, d, wr, bias, e, k, renorm, li, lo, idx, w, pp, pc, pm, done);
 }
 
 template <int EPT>
@@ -639,11 +667,11 @@ hipError_t launch_logits_t(hipStream_t st, const uint16_t* x, const RoutePlan& p
 template <int VPL>
 hipError_t launch_gate_t(hipStream_t st, const float* part, int ks, int64_t n, int e,
                          const float* bias, int k, int renorm, float* lo, int32_t* idx,
-                         float* w, float* pp, int32_t* pc, float* pm) {
+                         float* w, float* pp, int32_t* pc, float* pm, int32_t* done) {
   const int tpw = gate_tokens_per_wave(n);
   hipLaunchKernelGGL((route_gate_kernel<VPL>), dim3(static_cast<unsigned>(gate_blocks(n))),
                      dim3(kThreads), 0, st, part, ks, n, e, bias, k, renorm, tpw, lo, idx, w,
-                     pp, pc, pm);
+                     pp, pc, pm, done);
   return hipGetLastError();
 }
 
@@ -652,10 +680,10 @@ hipError_t launch_gate_t(hipStream_t st, const float* part, int ks, int64_t n, i
 hipError_t launch_route(hipStream_t st, const float* x, int64_t n, int64_t d,
                         const float* w_router, const float* logit_bias, int e, int k,
                         int renorm, float* logits_out, int32_t* topk_idx, float* topk_w,
-                        float* part_prob, int32_t* part_cnt, float* part_mon) {
+                        float* part_prob, int32_t* part_cnt, float* part_mon, int32_t* done) {
   if (n <= 0) return hipSuccess;
   return launch_route_dt<float>(st, x, n, d, w_router, logit_bias, e, k, renorm, nullptr,
-                                logits_out, topk_idx, topk_w, part_prob, part_cnt, part_mon);
+                                logits_out, topk_idx, topk_w, part_prob, part_cnt, part_mon, done);
 }
 
 RoutePlan route_plan(int64_t n, int64_t d, int e) {
@@ -711,14 +739,14 @@ hipError_t launch_route_logits(hipStream_t st, const uint16_t* x, const RoutePla
 hipError_t launch_route_gate(hipStream_t st, const float* part, int ks, int64_t n, int e,
                              const float* bias, int k, int renorm, float* logits_out,
                              int32_t* topk_idx, float* topk_w, float* part_prob,
-                             int32_t* part_cnt, float* part_mon) {
+                             int32_t* part_cnt, float* part_mon, int32_t* done) {
   if (n <= 0) return hipSuccess;
   const int vpl = (e + kWave - 1) / kWave;
-  if (vpl <= 1) return launch_gate_t<1>(st, part, ks, n, e, bias, k, renorm, logits_out, topk_idx, topk_w, part_prob, part_cnt, part_mon);
-  if (vpl <= 2) return launch_gate_t<2>(st, part, ks, n, e, bias, k, renorm, logits_out, topk_idx, topk_w, part_prob, part_cnt, part_mon);
-  if (vpl <= 3) return launch_gate_t<3>(st, part, ks, n, e, bias, k, renorm, logits_out, topk_idx, topk_w, part_prob, part_cnt, part_mon);
-  if (vpl <= 4) return launch_gate_t<4>(st, part, ks, n, e, bias, k, renorm, logits_out, topk_idx, topk_w, part_prob, part_cnt, part_mon);
-  return launch_gate_t<8>(st, part, ks, n, e, bias, k, renorm, logits_out, topk_idx, topk_w, part_prob, part_cnt, part_mon);
+  if (vpl <= 1) return launch_gate_t<1>(st, part, ks, n, e, bias, k, renorm, logits_out, topk_idx, topk_w, part_prob, part_cnt, part_mon, done);
+  if (vpl <= 2) return launch_gate_t<2>(st, part, ks, n, e, bias, k, renorm, logits_out, topk_idx, topk_w, part_prob, part_cnt, part_mon, done);
+  if (vpl <= 3) return launch_gate_t<3>(st, part, ks, n, e, bias, k, renorm, logits_out, topk_idx, topk_w, part_prob, part_cnt, part_mon, done);
+  if (vpl <= 4) return launch_gate_t<4>(st, part, ks, n, e, bias, k, renorm, logits_out, topk_idx, topk_w, part_prob, part_cnt, part_mon, done);
+  return launch_gate_t<8>(st, part, ks, n, e, bias, k, renorm, logits_out, topk_idx, topk_w, part_prob, part_cnt, part_mon, done);
 }
 
 hipError_t launch_update_bias(hipStream_t st, const int32_t* sel_count, int e, int64_t n, int k,
@@ -731,12 +759,17 @@ hipError_t launch_update_bias(hipStream_t st, const int32_t* sel_count, int e, i
 hipError_t launch_route_finalize(hipStream_t st, const float* part_prob,
                                  const int32_t* part_cnt, const float* part_mon, int64_t rows,
                                  int64_t n, int e, int k, int32_t* sel_count, float* prob_mean,
-                                 float* aux, float* monitor, double* term, int64_t* cnt) {
+                                 float* aux, float* monitor, double* term, int64_t* cnt,
+                                 int32_t* done) {
+  // with a gate launch before it (n > 0) the counter is zeroed and the last per-expert
+  // workgroup finishes aux and the monitor; otherwise a second launch does
+  const bool fold = done != nullptr && n > 0;
   hipLaunchKernelGGL(route_stats_kernel, dim3(static_cast<unsigned>(e)), dim3(kThreads), 0, st,
-                     part_prob, part_cnt, rows, n, e, k, sel_count, prob_mean, term, cnt);
+                     part_prob, part_cnt, rows, n, e, k, sel_count, prob_mean, term, cnt,
+                     fold ? done : nullptr, part_mon, aux, monitor);
   {
     const hipError_t err = hipGetLastError();
-    if (err != hipSuccess) return err;
+    if (err != hipSuccess || fold) return err;
   }
   if (aux || monitor)
     hipLaunchKernelGGL(route_aux_kernel, dim3(1), dim3(kThreads), 0, st, term, cnt, part_mon, rows,

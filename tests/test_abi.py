@@ -248,7 +248,14 @@ def test_fused_forward_workspace():
     both = B.moe_forward_workspace_size(B.make_config(**kw, fuse=B.MOE_FUSE_GATHER | B.MOE_FUSE_WEIGHT))
     assert plain - gather >= 8192 * 4096 * 2  # no permuted copy of x
     assert both - gather >= 8192 * 4  # one weight per row
-    assert B.moe_forward_workspace_size(B.make_config(**kw, fuse=4)) == 0
+    assert B.moe_forward_workspace_size(B.make_config(**kw, fuse=8)) == 0
+    # the scatter fusion applies to top-1 layers without shared experts: no expert-output
+    # rows in the workspace
+    kw1 = dict(kw, top_k=1)
+    w1 = B.moe_forward_workspace_size(B.make_config(**kw1, fuse=3))
+    w7 = B.moe_forward_workspace_size(B.make_config(**kw1, fuse=7))
+    assert w1 - w7 >= 4096 * 4096 * 2
+    assert B.moe_forward_workspace_size(B.make_config(**kw, fuse=7)) == both  # k = 2: ignored
 
 
 def test_packed_weights_size_and_validation():

@@ -227,8 +227,37 @@ def test_forward_gather_fusion_is_bit_identical(name):
         assert np.array_equal(to_host_bits(outs[0]), to_host_bits(outs[1])), wfuse
 
 
+@pytest.mark.parametrize("case", [
+    ("switch", {}),  # capacity: most tokens dropped, their rows zeroed by the dispatch
+    ("switch", dict(alpha=None, n_tokens=1536)),
+    ("switch", dict(n_tokens=2048, d_model=768, d_ff=1344, n_experts=4, expert_bias=True)),
+    ("tiny", dict(top_k=1)),  # float32
+    ("mixtral", dict(top_k=1, n_tokens=2048, d_ff=1024)),  # 128 x 512 packed tiles
+])
+@pytest.mark.parametrize("packed", [False, True])
+def test_forward_scatter_fusion_is_bit_identical(case, packed):
+    """Top-1: GEMM2 writing each row straight into its token's output row (dropped tokens
+    zeroed by the dispatch) gives the bits of the weight fusion followed by the combine."""
+    name, kw = case
+    cfg = CONFIGS[name].with_tokens(REDUCED[name]).scaled(**kw)
+    cfg = cfg.scaled(d_ff=min(cfg.d_ff, 2048))
+    if packed and cfg.dtype != "bf16":
+        pytest.skip("packed weights are bf16 only")
+    print_case("fusion-scatter", name, kw, packed)
+    inp = synth.DeviceInputs(cfg, DEV)
+    outs = []
+    for fuse in (3, 7):
+        layer = _layer(inp, "packed_only" if packed else "staged")
+        layer.cfg = cfg.scaled(fuse=fuse)
+        y = torch.full_like(inp.x, 7.0)  # stale values where nothing would be written
+        layer.forward(inp.x, y)
+        outs.append(y)
+    torch.cuda.synchronize()
+    assert np.array_equal(to_host_bits(outs[0]), to_host_bits(outs[1]))
+
+
 @pytest.mark.parametrize("name", ["switch", "mixtral", "deepseek", "decode", "tiny"])
-@pytest.mark.parametrize("fuse", [0, B.MOE_FUSE_WEIGHT])
+@pytest.mark.parametrize("fuse", [0, B.MOE_FUSE_WEIGHT, B.MOE_FUSE_SCATTER])
 def test_forward_parity_fusion_variants(name, fuse):
     # the workloads fuse both by default; the unfused path and the weight fusion alone
     cfg = CONFIGS[name].with_tokens(REDUCED[name]).scaled(fuse=fuse,
