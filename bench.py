@@ -38,8 +38,11 @@ PACKED_ROWS = 256  # segments averaging this many rows take the packed-weight ke
 CALIB_KERNEL = "MulFunctor"  # the plain float32 copy (x * 1) that scales byte counters
 
 
-# The sources of the expert GEMM kernels, whose counter-derived traffic the bench reports.
+# The sources of the expert GEMM kernels, whose counter-derived traffic the bench reports:
+# gemm.hip, common.h and the grouped-GEMM part of kernels.h.
 GEMM_SOURCES = ("common.h", "gemm.hip", "kernels.h")
+GEMM_HEADER_PART = ("// ---------------------------------------------------------------- grouped GEMM",
+                    "// ---------------------------------------------------------------- combine")
 
 
 def sources_hash() -> str:
@@ -48,7 +51,11 @@ def sources_hash() -> str:
     h = hashlib.sha256()
     for f in sorted(os.path.join(CSRC, n) for n in GEMM_SOURCES):
         with open(f, "rb") as fh:
-            h.update(os.path.basename(f).encode() + fh.read())
+            text = fh.read()
+        if os.path.basename(f) == "kernels.h":
+            a, b = (p.encode() for p in GEMM_HEADER_PART)
+            text = text[text.index(a):text.index(b)]
+        h.update(os.path.basename(f).encode() + text)
     return h.hexdigest()[:16]
 
 
@@ -83,7 +90,7 @@ def stage_symbol(cfg, stage: str, packed: bool = False, capacity: int = -1):
         return f"gemm_packed_small_kernel<{epi}>" if packed else f"gemm_bf16_kernel<32, {epi}, false>"
     if packed:
         return (f"gemm_packed_kernel<{epi}>" if avg >= PACKED_ROWS
-                else f"gemm_packed_mid_kernel<{epi}>")
+                else f"gemm_packed_mid_kernel<MidShape<256, 16>, {epi}>")
     return f"gemm_bf16_kernel<256, {epi}, false>"
 
 
@@ -97,10 +104,12 @@ def _pmc_rows(path: str):
 
 
 def _counter_values(path: str, counter: str) -> dict:
+    """{kernel name: [value per dispatch]}, names without the library's namespaces."""
     vals = {}
     for r in _pmc_rows(path):
         if r["Counter_Name"] == counter:
-            vals.setdefault(r["Kernel_Name"], []).append(float(r["Counter_Value"]))
+            name = r["Kernel_Name"].replace("moe::(anonymous namespace)::", "")
+            vals.setdefault(name, []).append(float(r["Counter_Value"]))
     return vals
 
 

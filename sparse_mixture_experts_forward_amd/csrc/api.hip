@@ -95,7 +95,6 @@ struct RouteWs {
   float* pmon;
   double* term;
   int64_t* cnt;
-  int32_t* done;
   uint16_t* wp;
   float* part;
 };
@@ -108,7 +107,6 @@ RouteWs route_layout(Carve& c, int64_t n, int64_t d, int32_t e) {
   r.pmon = c.take<float>(2 * b);
   r.term = c.take<double>(e);
   r.cnt = c.take<int64_t>(e);
-  r.done = c.take<int32_t>(1);
   if (d >= 8 && d % 8 == 0) {
     const moe::RoutePlan pl = moe::route_plan(n, d, e);
     r.wp = c.take<uint16_t>(3 * static_cast<int64_t>(pl.e_pad) * d);
@@ -171,7 +169,7 @@ moe_status run_route(hipStream_t st, const void* x, moe_dtype xt, int64_t n, int
   if (monitor) flags |= moe::kGateMonitor;
   auto finalize = [&](int64_t rows) {
     return hip_check(moe::launch_route_finalize(st, r.pp, r.pc, r.pmon, rows, n, e, k, sel, pm,
-                                                aux, monitor, r.term, r.cnt, r.done),
+                                                aux, monitor, r.term, r.cnt),
                      "router statistics launch");
   };
   int64_t rows;
@@ -179,7 +177,7 @@ moe_status run_route(hipStream_t st, const void* x, moe_dtype xt, int64_t n, int
     // the gate alone, over the caller's logits
     rows = moe::gate_blocks(n);
     MOE_TRY(hip_check(moe::launch_route_gate(st, logits_in, 1, n, e, bias, k, flags, logits_out,
-                                             idx, w, r.pp, r.pc, r.pmon, r.done),
+                                             idx, w, r.pp, r.pc, r.pmon),
                       "router gate launch"));
   } else if (xt == MOE_BF16) {
     const moe::RoutePlan pl = moe::route_plan(n, d, e);
@@ -189,12 +187,12 @@ moe_status run_route(hipStream_t st, const void* x, moe_dtype xt, int64_t n, int
     MOE_TRY(hip_check(moe::launch_route_logits(st, static_cast<const uint16_t*>(x), pl, r.wp, r.part),
                       "router logits launch"));
     MOE_TRY(hip_check(moe::launch_route_gate(st, r.part, pl.ks, n, e, bias, k, flags, logits_out,
-                                             idx, w, r.pp, r.pc, r.pmon, r.done),
+                                             idx, w, r.pp, r.pc, r.pmon),
                       "router gate launch"));
   } else {
     rows = moe::route_blocks(n);
     MOE_TRY(hip_check(moe::launch_route(st, static_cast<const float*>(x), n, d, wr, bias, e, k,
-                                        flags, logits_out, idx, w, r.pp, r.pc, r.pmon, r.done),
+                                        flags, logits_out, idx, w, r.pp, r.pc, r.pmon),
                       "router kernel launch"));
   }
   return finalize(rows);

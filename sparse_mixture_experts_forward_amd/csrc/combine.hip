@@ -4,7 +4,8 @@
 // A gather, not a scatter: each output vector (8 bf16 or 4 float32 = 16 bytes) is
 // produced by one thread that reads the shared row and the token's k expert rows and
 // accumulates in float32 in a fixed order (shared, then slot 0..k-1).  No atomics, so
-// the result is bitwise reproducible.  One workgroup per token row.
+// the result is bitwise reproducible.  A workgroup takes one token, or two when tokens
+// have at most two slots.
 
 #include "common.h"
 #include "kernels.h"
@@ -55,12 +56,12 @@ struct Vec<false> {
   }
 };
 
-// One workgroup per token row (rows of d/VN 16-byte vectors; thread i takes vectors
-// i, i + 256, ..., of the row's blockIdx.y-th range of 256 * VPT vectors): the token's
-// k slots and weights are the same for the whole workgroup, and each wave reads and
-// writes 1 KB contiguous pieces of the rows.  Every load of the token (k <= KMAX slot
-// rows x VPT vectors) is issued before the float32 accumulation, which then runs in the
-// fixed order shared, slot 0, ..., slot k-1.
+// TPW tokens per workgroup (rows of d/VN 16-byte vectors; thread i takes vectors i,
+// i + 256, ..., of each token's blockIdx.y-th range of 256 * VPT vectors): every load
+// of the workgroup's tokens (TPW tokens x (shared + k <= KMAX slot rows) x VPT
+// vectors) is issued before the float32 accumulation, which then runs per token in the
+// fixed order shared, slot 0, ..., slot k-1; each wave reads and writes 1 KB contiguous
+// pieces of the rows.
 // 16-byte load; NT: nontemporal (read once, kept out of the caches' retention)
 template <bool NT>
 __device__ __forceinline__ uint4 load16(const uint8_t* p) {
@@ -72,10 +73,10 @@ __device__ __forceinline__ uint4 load16(const uint8_t* p) {
   }
 }
 
-template <bool BF16, int VPT, int KMAX>
+template <bool BF16, int VPT, int KMAX, int TPW>
 __global__ __launch_bounds__(kThreads) void combine_kernel(
     const uint8_t* __restrict__ y_rows, const int32_t* __restrict__ slot_row,
-    const float* __restrict__ topk_w, int k, int64_t d,
+    const float* __restrict__ topk_w, int64_t n, int k, int64_t d,
     const uint8_t* __restrict__ shared_y, uint8_t* __restrict__ out) {
   using V = Vec<BF16>;
   constexpr int VN = V::N;
@@ -83,50 +84,64 @@ __global__ __launch_bounds__(kThreads) void combine_kernel(
   // DeepSeek-shaped, 6 slots + shared, 64 -> 59 us; with 2 slots they cost a little)
   constexpr bool NT = KMAX >= 8;
   constexpr int64_t kVecBytes = 16;
-  const int64_t t = blockIdx.x;
   const int64_t nvec = d / VN;
   const int64_t row_bytes = d * (BF16 ? 2 : 4);
   const int64_t c0 = static_cast<int64_t>(blockIdx.y) * kThreads * VPT + threadIdx.x;
-  int32_t row[KMAX];
-  float w[KMAX];
+  int32_t row[TPW][KMAX];
+  float w[TPW][KMAX];
 #pragma unroll
-  for (int j = 0; j < KMAX; ++j) {
-    row[j] = j < k ? slot_row[t * k + j] : -1;
-    w[j] = (j < k && topk_w) ? topk_w[t * k + j] : 1.f;  // NULL: rows already weighted
-  }
-  uint4 raw[KMAX][VPT];
-  uint4 sh[VPT];
-#pragma unroll
-  for (int v = 0; v < VPT; ++v) {
-    const int64_t c = c0 + static_cast<int64_t>(kThreads) * v;
-    if (c < nvec) {
-      if (shared_y) sh[v] = load16<NT>(shared_y + t * row_bytes + c * kVecBytes);
-#pragma unroll
-      for (int j = 0; j < KMAX; ++j)
-        if (row[j] >= 0)
-          raw[j][v] = load16<NT>(y_rows + static_cast<int64_t>(row[j]) * row_bytes + c * kVecBytes);
-    }
-  }
-#pragma unroll
-  for (int v = 0; v < VPT; ++v) {
-    const int64_t c = c0 + static_cast<int64_t>(kThreads) * v;
-    if (c >= nvec) continue;
-    float acc[VN];
-    if (shared_y) {
-      V::load(&sh[v], acc);
-    } else {
-#pragma unroll
-      for (int q = 0; q < VN; ++q) acc[q] = 0.f;
-    }
+  for (int u = 0; u < TPW; ++u) {
+    const int64_t t = static_cast<int64_t>(blockIdx.x) * TPW + u;
 #pragma unroll
     for (int j = 0; j < KMAX; ++j) {
-      if (row[j] < 0) continue;
-      float y[VN];
-      V::load(&raw[j][v], y);
-#pragma unroll
-      for (int q = 0; q < VN; ++q) acc[q] = fmaf(w[j], y[q], acc[q]);
+      const bool ok = t < n && j < k;
+      row[u][j] = ok ? slot_row[t * k + j] : -1;
+      w[u][j] = (ok && topk_w) ? topk_w[t * k + j] : 1.f;  // NULL: rows already weighted
     }
-    V::store(out + t * row_bytes + c * kVecBytes, acc);
+  }
+  uint4 raw[TPW][KMAX][VPT];
+  uint4 sh[TPW][VPT];
+#pragma unroll
+  for (int u = 0; u < TPW; ++u) {
+    const int64_t t = static_cast<int64_t>(blockIdx.x) * TPW + u;
+#pragma unroll
+    for (int v = 0; v < VPT; ++v) {
+      const int64_t c = c0 + static_cast<int64_t>(kThreads) * v;
+      if (c < nvec && t < n) {
+        if (shared_y) sh[u][v] = load16<NT>(shared_y + t * row_bytes + c * kVecBytes);
+#pragma unroll
+        for (int j = 0; j < KMAX; ++j)
+          if (row[u][j] >= 0)
+            raw[u][j][v] =
+                load16<NT>(y_rows + static_cast<int64_t>(row[u][j]) * row_bytes + c * kVecBytes);
+      }
+    }
+  }
+#pragma unroll
+  for (int u = 0; u < TPW; ++u) {
+    const int64_t t = static_cast<int64_t>(blockIdx.x) * TPW + u;
+    if (t >= n) break;
+#pragma unroll
+    for (int v = 0; v < VPT; ++v) {
+      const int64_t c = c0 + static_cast<int64_t>(kThreads) * v;
+      if (c >= nvec) continue;
+      float acc[VN];
+      if (shared_y) {
+        V::load(&sh[u][v], acc);
+      } else {
+#pragma unroll
+        for (int q = 0; q < VN; ++q) acc[q] = 0.f;
+      }
+#pragma unroll
+      for (int j = 0; j < KMAX; ++j) {
+        if (row[u][j] < 0) continue;
+        float y[VN];
+        V::load(&raw[u][j][v], y);
+#pragma unroll
+        for (int q = 0; q < VN; ++q) acc[q] = fmaf(w[u][j], y[q], acc[q]);
+      }
+      V::store(out + t * row_bytes + c * kVecBytes, acc);
+    }
   }
 }
 
@@ -136,14 +151,17 @@ hipError_t launch_combine_k(hipStream_t st, const uint8_t* yr, const int32_t* sl
                             uint8_t* o) {
   const int64_t nvec = d / Vec<BF16>::N;
   const int64_t vpt = (nvec + kThreads - 1) / kThreads;
+  // few slot rows per token: several tokens per workgroup keep more loads in flight
+  constexpr int TPW = KMAX <= 2 ? 2 : 1;
   // rows wider than 1024 vectors: ranges of 1024 along blockIdx.y
-  const dim3 grid(static_cast<unsigned>(n), static_cast<unsigned>(vpt > 4 ? (vpt + 3) / 4 : 1));
+  const dim3 grid(static_cast<unsigned>((n + TPW - 1) / TPW),
+                  static_cast<unsigned>(vpt > 4 ? (vpt + 3) / 4 : 1));
   const dim3 blk(kThreads);
   switch (vpt > 4 ? 4 : vpt) {
-    case 1: hipLaunchKernelGGL((combine_kernel<BF16, 1, KMAX>), grid, blk, 0, st, yr, slot_row, topk_w, k, d, sy, o); break;
-    case 2: hipLaunchKernelGGL((combine_kernel<BF16, 2, KMAX>), grid, blk, 0, st, yr, slot_row, topk_w, k, d, sy, o); break;
-    case 3: hipLaunchKernelGGL((combine_kernel<BF16, 3, KMAX>), grid, blk, 0, st, yr, slot_row, topk_w, k, d, sy, o); break;
-    case 4: hipLaunchKernelGGL((combine_kernel<BF16, 4, KMAX>), grid, blk, 0, st, yr, slot_row, topk_w, k, d, sy, o); break;
+    case 1: hipLaunchKernelGGL((combine_kernel<BF16, 1, KMAX, TPW>), grid, blk, 0, st, yr, slot_row, topk_w, n, k, d, sy, o); break;
+    case 2: hipLaunchKernelGGL((combine_kernel<BF16, 2, KMAX, TPW>), grid, blk, 0, st, yr, slot_row, topk_w, n, k, d, sy, o); break;
+    case 3: hipLaunchKernelGGL((combine_kernel<BF16, 3, KMAX, TPW>), grid, blk, 0, st, yr, slot_row, topk_w, n, k, d, sy, o); break;
+    case 4: hipLaunchKernelGGL((combine_kernel<BF16, 4, KMAX, TPW>), grid, blk, 0, st, yr, slot_row, topk_w, n, k, d, sy, o); break;
     default: return hipErrorInvalidValue;
   }
   return hipGetLastError();

@@ -24,7 +24,7 @@ inline int64_t route_blocks(int64_t n_tokens) {
 hipError_t launch_route(hipStream_t st, const float* x, int64_t n, int64_t d,
                         const float* w_router, const float* logit_bias, int e, int k,
                         int renorm, float* logits_out, int32_t* topk_idx, float* topk_w,
-                        float* part_prob, int32_t* part_cnt, float* part_mon, int32_t* done);
+                        float* part_prob, int32_t* part_cnt, float* part_mon);
 
 // bf16 router: exact three-part bf16 split of W_router, the sliced logits product and
 // the gate over the slices' partial logits.
@@ -56,7 +56,7 @@ hipError_t launch_route_logits(hipStream_t st, const uint16_t* x, const RoutePla
 hipError_t launch_route_gate(hipStream_t st, const float* part, int ks, int64_t n, int e,
                              const float* bias, int k, int renorm, float* logits_out,
                              int32_t* topk_idx, float* topk_w, float* part_prob,
-                             int32_t* part_cnt, float* part_mon, int32_t* done);
+                             int32_t* part_cnt, float* part_mon);
 
 // Batch-level bias update: b[e] -= gamma if sel_count[e]*E > N*k, += gamma if below.
 hipError_t launch_update_bias(hipStream_t st, const int32_t* sel_count, int e, int64_t n, int k,
@@ -65,14 +65,11 @@ hipError_t launch_update_bias(hipStream_t st, const int32_t* sel_count, int e, i
 // Statistics over `rows` partial rows: per-expert workgroups (sel_count, prob_mean and
 // the aux terms; `term` E doubles and `cnt` E counts of scratch), then aux and, if
 // `monitor` is given, z-loss, mean top-k entropy, sum of squared load shares and load
-// CV (monitor[0..3]; part_mon holds two floats per row).  done [1]: a counter that the
-// gate launch before (launch_route, launch_route_gate with the same `done`) zeroes; with
-// it the statistics take one launch.
+// CV (monitor[0..3]; part_mon holds two floats per row).
 hipError_t launch_route_finalize(hipStream_t st, const float* part_prob,
                                  const int32_t* part_cnt, const float* part_mon, int64_t rows,
                                  int64_t n, int e, int k, int32_t* sel_count, float* prob_mean,
-                                 float* aux, float* monitor, double* term, int64_t* cnt,
-                                 int32_t* done);
+                                 float* aux, float* monitor, double* term, int64_t* cnt);
 
 
 // ---------------------------------------------------------------- dispatch

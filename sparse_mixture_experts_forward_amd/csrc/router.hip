@@ -144,10 +144,8 @@ __global__ __launch_bounds__(kThreads) void route_kernel(
     const float* __restrict__ bias, int E, int k, int flags,
     const float* __restrict__ logits_in, float* __restrict__ logits_out,
     int32_t* __restrict__ topk_idx, float* __restrict__ topk_w,
-    float* __restrict__ part_prob, int32_t* __restrict__ part_cnt, float* __restrict__ part_mon,
-    int32_t* __restrict__ done) {
+    float* __restrict__ part_prob, int32_t* __restrict__ part_cnt, float* __restrict__ part_mon) {
   constexpr int EP = ET * 16;             // padded expert count (LDS row stride)
-  if (done && blockIdx.x == 0 && threadIdx.x == 0) done[0] = 0;  // the statistics' counter
   const int renorm = flags & kGateRenorm, sel_only = (flags & kGateSelectionOnly) ? 1 : 0;
   const int monitor = (flags & kGateMonitor) ? 1 : 0;
   float lse2 = 0.f, ent = 0.f;
@@ -448,9 +446,8 @@ __global__ __launch_bounds__(kThreads) void route_gate_kernel(
     const float* __restrict__ part, int ks, int64_t n, int E, const float* __restrict__ bias,
     int k, int flags, int tpw, float* __restrict__ logits_out, int32_t* __restrict__ topk_idx,
     float* __restrict__ topk_w, float* __restrict__ part_prob, int32_t* __restrict__ part_cnt,
-    float* __restrict__ part_mon, int32_t* __restrict__ done) {
+    float* __restrict__ part_mon) {
   constexpr int EP = VPL * kWave;
-  if (done && blockIdx.x == 0 && threadIdx.x == 0) done[0] = 0;  // the statistics' counter
   const int renorm = flags & kGateRenorm, sel_only = (flags & kGateSelectionOnly) ? 1 : 0;
   const int monitor = (flags & kGateMonitor) ? 1 : 0;
   float lse2 = 0.f, ent = 0.f;
@@ -509,7 +506,8 @@ __global__ __launch_bounds__(kThreads) void route_gate_kernel(
 // and the expert's aux term (count / (N k)) * prob_mean.
 // Sums of the aux terms, monitoring partials and load moments over a fixed tree, then
 // aux = E * sum of terms and the monitoring signals.  Run by one whole workgroup.
-__device__ __forceinline__ void aux_body(const double* term, const int64_t* cnt,
+__device__ __forceinline__ void aux_body(const double* __restrict__ term,
+                                         const int64_t* __restrict__ cnt,
                                          const float* __restrict__ part_mon, int64_t rows,
                                          int64_t n, int E, float* __restrict__ aux,
                                          float* __restrict__ monitor, double (&red)[5][kThreads]) {
@@ -549,18 +547,12 @@ __device__ __forceinline__ void aux_body(const double* term, const int64_t* cnt,
   }
 }
 
-// With `done` (zeroed by the gate launch before it) the workgroup that finishes last
-// also runs aux_body, so the statistics take one launch: each workgroup publishes its
-// term and count with an agent-scope release before taking its ticket, and the last one
-// acquires before reading them all.
 __global__ __launch_bounds__(kThreads) void route_stats_kernel(
     const float* __restrict__ part_prob, const int32_t* __restrict__ part_cnt, int64_t rows,
     int64_t n, int E, int k, int32_t* __restrict__ sel_count, float* __restrict__ prob_mean,
-    double* term, int64_t* cnt, int32_t* done, const float* __restrict__ part_mon,
-    float* __restrict__ aux, float* __restrict__ monitor) {
+    double* __restrict__ term, int64_t* __restrict__ cnt) {
   __shared__ double sp[kThreads];
   __shared__ int64_t sc[kThreads];
-  __shared__ int last;
   const int e = blockIdx.x;
   double ps = 0.0;
   int64_t cs = 0;
@@ -585,17 +577,7 @@ __global__ __launch_bounds__(kThreads) void route_stats_kernel(
     if (prob_mean) prob_mean[e] = static_cast<float>(pm);
     term[e] = fr * pm;
     cnt[e] = sc[0];
-    if (done) {
-      const int ticket = __hip_atomic_fetch_add(done, 1, __ATOMIC_ACQ_REL, __HIP_MEMORY_SCOPE_AGENT);
-      last = ticket == E - 1;
-    }
   }
-  if (!done || !(aux || monitor)) return;
-  __syncthreads();
-  if (!last) return;
-  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");  // every workgroup's term and count
-  __shared__ double red[5][kThreads];
-  aux_body(term, cnt, part_mon, rows, n, E, aux, monitor, red);
 }
 
 // Batch-level bias update of the bias-for-selection scheme ([Why-MoE] §2.4): an expert
@@ -627,11 +609,11 @@ template <typename XT, int ET>
 hipError_t launch_route_t(hipStream_t st, const void* x, int64_t n, int64_t d,
                           const float* wr, const float* bias, int e, int k, int renorm,
                           const float* logits_in, float* logits_out, int32_t* idx,
-                          float* w, float* pp, int32_t* pc, float* pm, int32_t* done) {
+                          float* w, float* pp, int32_t* pc, float* pm) {
   const int64_t blocks = route_blocks(n);
   hipLaunchKernelGGL((route_kernel<XT, ET>), dim3(static_cast<unsigned>(blocks)),
                      dim3(kThreads), 0, st, static_cast<const XT*>(x), n, d, wr, bias, e, k,
-                     renorm, logits_in, logits_out, idx, w, pp, pc, pm, done);
+                     renorm, logits_in, logits_out, idx, w, pp, pc, pm);
   return hipGetLastError();
 }
 
@@ -639,15 +621,15 @@ template <typename XT>
 hipError_t launch_route_dt(hipStream_t st, const void* x, int64_t n, int64_t d,
                            const float* wr, const float* bias, int e, int k, int renorm,
                            const float* li, float* lo, int32_t* idx, float* w, float* pp,
-                           int32_t* pc, float* pm, int32_t* done) {
+                           int32_t* pc, float* pm) {
   const int n_et = (e + 15) / 16;
-  if (n_et <= 1) return launch_route_t<XT, 1>(st, x, n, d, wr, bias, e, k, renorm, li, lo, idx, w, pp, pc, pm, done);
-  if (n_et <= 2) return launch_route_t<XT, 2>(st, x, n, d, wr, bias, e, k, renorm, li, lo, idx, w, pp, pc, pm, done);
-  if (n_et <= 4) return launch_route_t<XT, 4>(st, x, n, d, wr, bias, e, k, renorm, li, lo, idx, w, pp, pc, pm, done);
-  if (n_et <= 8) return launch_route_t<XT, 8>(st, x, n, d, wr, bias, e, k, renorm, li, lo, idx, w, pp, pc, pm, done);
-  if (n_et <= 10) return launch_route_t<XT, 10>(st, x, n, d, wr, bias, e, k, renorm, li, lo, idx, w, pp, pc, pm, done);
-  if (n_et <= 16) return launch_route_t<XT, 16>(st, x, n, d, wr, bias, e, k, renorm, li, lo, idx, w, pp, pc, pm, done);
-  return launch_route_t<XT, 32>(st, x, n, d, wr, bias, e, k, renorm, li, lo, idx, w, pp, pc, pm, done);
+  if (n_et <= 1) return launch_route_t<XT, 1>(st, x, n, d, wr, bias, e, k, renorm, li, lo, idx, w, pp, pc, pm);
+  if (n_et <= 2) return launch_route_t<XT, 2>(st, x, n, d, wr, bias, e, k, renorm, li, lo, idx, w, pp, pc, pm);
+  if (n_et <= 4) return launch_route_t<XT, 4>(st, x, n, d, wr, bias, e, k, renorm, li, lo, idx, w, pp, pc, pm);
+  if (n_et <= 8) return launch_route_t<XT, 8>(st, x, n, d, wr, bias, e, k, renorm, li, lo, idx, w, pp, pc, pm);
+  if (n_et <= 10) return launch_route_t<XT, 10>(st, x, n, d, wr, bias, e, k, renorm, li, lo, idx, w, pp, pc, pm);
+  if (n_et <= 16) return launch_route_t<XT, 16>(st, x, n, d, wr, bias, e, k, renorm, li, lo, idx, w, pp, pc, pm);
+  return launch_route_t<XT, 32>(st, x, n, d, wr, bias, e, k, renorm, li, lo, idx, w, pp, pc, pm);
 }
 
 template <int EPT>
@@ -667,11 +649,11 @@ hipError_t launch_logits_t(hipStream_t st, const uint16_t* x, const RoutePlan& p
 template <int VPL>
 hipError_t launch_gate_t(hipStream_t st, const float* part, int ks, int64_t n, int e,
                          const float* bias, int k, int renorm, float* lo, int32_t* idx,
-                         float* w, float* pp, int32_t* pc, float* pm, int32_t* done) {
+                         float* w, float* pp, int32_t* pc, float* pm) {
   const int tpw = gate_tokens_per_wave(n);
   hipLaunchKernelGGL((route_gate_kernel<VPL>), dim3(static_cast<unsigned>(gate_blocks(n))),
                      dim3(kThreads), 0, st, part, ks, n, e, bias, k, renorm, tpw, lo, idx, w,
-                     pp, pc, pm, done);
+                     pp, pc, pm);
   return hipGetLastError();
 }
 
@@ -680,10 +662,10 @@ hipError_t launch_gate_t(hipStream_t st, const float* part, int ks, int64_t n, i
 hipError_t launch_route(hipStream_t st, const float* x, int64_t n, int64_t d,
                         const float* w_router, const float* logit_bias, int e, int k,
                         int renorm, float* logits_out, int32_t* topk_idx, float* topk_w,
-                        float* part_prob, int32_t* part_cnt, float* part_mon, int32_t* done) {
+                        float* part_prob, int32_t* part_cnt, float* part_mon) {
   if (n <= 0) return hipSuccess;
   return launch_route_dt<float>(st, x, n, d, w_router, logit_bias, e, k, renorm, nullptr,
-                                logits_out, topk_idx, topk_w, part_prob, part_cnt, part_mon, done);
+                                logits_out, topk_idx, topk_w, part_prob, part_cnt, part_mon);
 }
 
 RoutePlan route_plan(int64_t n, int64_t d, int e) {
@@ -739,14 +721,14 @@ hipError_t launch_route_logits(hipStream_t st, const uint16_t* x, const RoutePla
 hipError_t launch_route_gate(hipStream_t st, const float* part, int ks, int64_t n, int e,
                              const float* bias, int k, int renorm, float* logits_out,
                              int32_t* topk_idx, float* topk_w, float* part_prob,
-                             int32_t* part_cnt, float* part_mon, int32_t* done) {
+                             int32_t* part_cnt, float* part_mon) {
   if (n <= 0) return hipSuccess;
   const int vpl = (e + kWave - 1) / kWave;
-  if (vpl <= 1) return launch_gate_t<1>(st, part, ks, n, e, bias, k, renorm, logits_out, topk_idx, topk_w, part_prob, part_cnt, part_mon, done);
-  if (vpl <= 2) return launch_gate_t<2>(st, part, ks, n, e, bias, k, renorm, logits_out, topk_idx, topk_w, part_prob, part_cnt, part_mon, done);
-  if (vpl <= 3) return launch_gate_t<3>(st, part, ks, n, e, bias, k, renorm, logits_out, topk_idx, topk_w, part_prob, part_cnt, part_mon, done);
-  if (vpl <= 4) return launch_gate_t<4>(st, part, ks, n, e, bias, k, renorm, logits_out, topk_idx, topk_w, part_prob, part_cnt, part_mon, done);
-  return launch_gate_t<8>(st, part, ks, n, e, bias, k, renorm, logits_out, topk_idx, topk_w, part_prob, part_cnt, part_mon, done);
+  if (vpl <= 1) return launch_gate_t<1>(st, part, ks, n, e, bias, k, renorm, logits_out, topk_idx, topk_w, part_prob, part_cnt, part_mon);
+  if (vpl <= 2) return launch_gate_t<2>(st, part, ks, n, e, bias, k, renorm, logits_out, topk_idx, topk_w, part_prob, part_cnt, part_mon);
+  if (vpl <= 3) return launch_gate_t<3>(st, part, ks, n, e, bias, k, renorm, logits_out, topk_idx, topk_w, part_prob, part_cnt, part_mon);
+  if (vpl <= 4) return launch_gate_t<4>(st, part, ks, n, e, bias, k, renorm, logits_out, topk_idx, topk_w, part_prob, part_cnt, part_mon);
+  return launch_gate_t<8>(st, part, ks, n, e, bias, k, renorm, logits_out, topk_idx, topk_w, part_prob, part_cnt, part_mon);
 }
 
 hipError_t launch_update_bias(hipStream_t st, const int32_t* sel_count, int e, int64_t n, int k,
@@ -759,17 +741,12 @@ hipError_t launch_update_bias(hipStream_t st, const int32_t* sel_count, int e, i
 hipError_t launch_route_finalize(hipStream_t st, const float* part_prob,
                                  const int32_t* part_cnt, const float* part_mon, int64_t rows,
                                  int64_t n, int e, int k, int32_t* sel_count, float* prob_mean,
-                                 float* aux, float* monitor, double* term, int64_t* cnt,
-                                 int32_t* done) {
-  // with a gate launch before it (n > 0) the counter is zeroed and the last per-expert
-  // workgroup finishes aux and the monitor; otherwise a second launch does
-  const bool fold = done != nullptr && n > 0;
+                                 float* aux, float* monitor, double* term, int64_t* cnt) {
   hipLaunchKernelGGL(route_stats_kernel, dim3(static_cast<unsigned>(e)), dim3(kThreads), 0, st,
-                     part_prob, part_cnt, rows, n, e, k, sel_count, prob_mean, term, cnt,
-                     fold ? done : nullptr, part_mon, aux, monitor);
+                     part_prob, part_cnt, rows, n, e, k, sel_count, prob_mean, term, cnt);
   {
     const hipError_t err = hipGetLastError();
-    if (err != hipSuccess || fold) return err;
+    if (err != hipSuccess) return err;
   }
   if (aux || monitor)
     hipLaunchKernelGGL(route_aux_kernel, dim3(1), dim3(kThreads), 0, st, term, cnt, part_mon, rows,

@@ -17,8 +17,8 @@ def test_stage_kernels_of_the_workloads():
     want = {  # workload: (packed?, gemm1 kernel, gemm2 kernel) with packing allowed
         "mixtral": (True, "gemm_packed_kernel<2>", "gemm_packed_kernel<0>"),
         "decode": (True, "gemm_packed_small_kernel<2>", "gemm_packed_small_kernel<0>"),
-        "deepseek": (True, "gemm_packed_mid_kernel<2>", "gemm_packed_mid_kernel<0>"),
-        "switch": (True, "gemm_packed_mid_kernel<1>", "gemm_packed_mid_kernel<0>"),
+        "deepseek": (True, "gemm_packed_mid_kernel<MidShape<256, 16>, 2>", "gemm_packed_mid_kernel<MidShape<256, 16>, 0>"),
+        "switch": (True, "gemm_packed_mid_kernel<MidShape<256, 16>, 1>", "gemm_packed_mid_kernel<MidShape<256, 16>, 0>"),
         "tiny": (False, "gemm_f32_kernel<1, false>", "gemm_f32_kernel<0, false>"),
     }
     for name, (packed, k1, k2) in want.items():
@@ -36,8 +36,8 @@ def test_kernel_rules_at_the_thresholds():
     m = CONFIGS["mixtral"]
     # 256 rows per expert (N k / E): 128 x 512 kernel; 255: mid-size; 47: 32-row
     for n, k1, staged in ((1024, "gemm_packed_kernel<2>", "gemm_bf16_kernel<256, 2, false>"),
-                          (1020, "gemm_packed_mid_kernel<2>", "gemm_bf16_kernel<256, 2, false>"),
-                          (192, "gemm_packed_mid_kernel<2>", "gemm_bf16_kernel<256, 2, false>"),
+                          (1020, "gemm_packed_mid_kernel<MidShape<256, 16>, 2>", "gemm_bf16_kernel<256, 2, false>"),
+                          (192, "gemm_packed_mid_kernel<MidShape<256, 16>, 2>", "gemm_bf16_kernel<256, 2, false>"),
                           (188, "gemm_packed_small_kernel<2>", "gemm_bf16_kernel<32, 2, false>")):
         c = m.with_tokens(n)
         assert bench.packed_path(c, -1, True), n
