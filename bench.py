@@ -89,8 +89,8 @@ def stage_symbol(cfg, stage: str, packed: bool = False, capacity: int = -1):
     if avg < SMALL_ROWS:
         return f"gemm_packed_small_kernel<{epi}>" if packed else f"gemm_bf16_kernel<32, {epi}, false>"
     if packed:
-        return (f"gemm_packed_kernel<{epi}>" if avg >= PACKED_ROWS
-                else f"gemm_packed_mid_kernel<MidShape<256, 16>, {epi}>")
+        shape = "128, 8, 8, 0" if avg >= PACKED_ROWS else "256, 16, 4, 1"
+        return f"gemm_packed_kernel<PackedShape<{shape}>, {epi}>"
     return f"gemm_bf16_kernel<256, {epi}, false>"
 
 

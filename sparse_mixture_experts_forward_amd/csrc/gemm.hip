@@ -34,9 +34,14 @@
 //   * where the host cannot bound the rows per segment well (a capacity limit), the
 //     dispatch flags the tile height and both launches are made, one of them empty.
 // packed-weight kernels (bf16, with the copy written by launch_pack_weights, whose
-// 1 KB fragments are exactly a 32x32x16 MFMA lane's operand): for long segments
-// 128 x 512 tiles whose waves stream their own weight panels into registers while only
-// the activations pass through LDS; for short ones a 32-row variant without LDS.
+// 1 KB fragments are exactly a 32x32x16 MFMA lane's operand), one per segment length:
+//   * long segments (>= 256 rows per segment by the host's bound): 128 x 512 tiles of 8
+//     waves, two per SIMD, each streaming 64 weight rows of its own into a register ring
+//     against the tile's 128 activation rows, which pass through LDS; a partial last
+//     round splits along K (gemm_packed_finish_kernel sums the parts);
+//   * mid-size segments (48 .. 255): 256 x 256 tiles of 4 waves, a whole segment of up
+//     to 256 rows per tile, so every (segment, column tile) reads its weights once;
+//   * short segments (< 48): 32 x 512 tiles without LDS, two workgroups per CU.
 // float32 kernel: a plain LDS-tiled SIMT product (64 x 64 tiles) with the same
 // scheduling and epilogues; it serves the small float32 workload.
 
@@ -68,10 +73,11 @@ struct Tile {
 };
 
 // Block-wide: find this workgroup's tile.  Returns false (uniformly) if it has none.
+constexpr int kMaxWaves = 16;  // waves per workgroup the scheduler serves
 struct SchedSmem {
   int start[kMaxExperts + 1];
-  int wsum[kThreads / kWave];
-  int wmulti[kThreads / kWave];
+  int wsum[kMaxWaves];
+  int wmulti[kMaxWaves];
   int seg;
 };
 
@@ -94,10 +100,11 @@ __device__ __forceinline__ void seg_bounds(const int32_t* __restrict__ seg_off, 
 // the round is filled (split_g = 0: never).  Parts of one tile are r work items apart.
 // (With more rounds the tail is a small share of the time, and the parts' extra
 // prologues, partial stores and the finishing launch cost more than they save.)
-template <int BM>
+template <int BM, int NT = kThreads>
 __device__ bool schedule_tile(const int32_t* __restrict__ seg_off, int n_seg,
                               int single_rows, int max_rows, int n_ntiles, int KT, int split_g,
                               int32_t* split_desc, SchedSmem& sm, Tile& tile) {
+  static_assert(NT / kWave <= kMaxWaves && 2 * NT >= kMaxExperts, "scheduler workgroup size");
   int* s_start = sm.start;
   int* s_wsum = sm.wsum;
   const int tid = threadIdx.x;
@@ -127,7 +134,7 @@ __device__ bool schedule_tile(const int32_t* __restrict__ seg_off, int n_seg,
   __syncthreads();
   int woff = 0, total = 0;
 #pragma unroll
-  for (int w = 0; w < kThreads / kWave; ++w) {
+  for (int w = 0; w < NT / kWave; ++w) {
     if (w < wave) woff += s_wsum[w];
     total += s_wsum[w];
     multi |= sm.wmulti[w];
@@ -881,126 +888,15 @@ __global__ __launch_bounds__(kWave) void gemm_split_finish_kernel(GemmArgs g) {
   else by_tm(std::integral_constant<int, 1>{});
 }
 
-// ------------------------------------------------------------------ packed-weight kernel
-// For long segments the weights are read from a packed copy (launch_pack_weights) laid
-// out in the order the matrix cores take them: a fragment of 32 weight rows x 16 k is
-// 1 KB, lane l holding row l % 32, k 8 (l / 32) .. + 8 as one 16-byte piece, so a wave
-// moves a fragment from memory into registers with one fully coalesced load.  Only the
-// activations pass through LDS:
-//   * tile 128 activation rows x 512 weight rows; each of the 4 waves multiplies all
-//     128 rows by a 128-row weight panel of its own (64 W1 + the same 64 W3 rows for
-//     SwiGLU), so no weight fragment is needed by two waves.  Per 64-deep stage the LDS
-//     then carries 16 KB of writes and 64 KB of fragment reads, against 64 KB and 128 KB
-//     when both operands are staged (those reads are the largest in-core cost of the
-//     staged kernel);
-//   * weights: a register ring of 8 k-steps of fragments, each loaded 7 k-steps ahead;
-//   * activations: 4 LDS stages of 128 rows x 64 k, filled by direct-to-LDS buffer
-//     loads 4 stages ahead, one barrier per stage (before its last k-step's MFMAs);
-//   * row blocks past a tile's last row skip their MFMAs (TA = active blocks);
-//   * same scheduling, epilogues and gather as the staged kernel.
-constexpr int kPBM = 128;      // activation rows per tile
-constexpr int kPBN = 512;      // weight rows per tile
+// ------------------------------------------------------------------ packed-weight kernels
+// With packed weights (launch_pack_weights) the weights are read in the order the matrix
+// cores take them: a fragment of 32 weight rows x 16 k is 1 KB, lane l holding row
+// l % 32, k 8 (l / 32) .. + 8 as one 16-byte piece, so a wave moves a fragment from
+// memory into registers with one fully coalesced load; only the activations pass
+// through LDS (or none at all, in the 32-row kernel).  Per 64-deep stage the LDS then
+// carries the activation writes and reads only, where staging both operands made the
+// fragment reads the largest in-core cost.
 constexpr int kPStages = 4;    // activation LDS stages
-constexpr int kPRing = 8;      // weight register ring, in k-steps of 16
-constexpr int kPLead = kPRing - 1;
-constexpr int kPLoadsA = 4;    // activation loads (8 rows x 128 bytes) per wave per stage
-// Stage boundary of stage s: this wave's activation loads of stage s + 1 must have
-// landed.  Loads complete in order, and issued after those are at least the activation
-// loads of two later stages and the weight loads of ten k-steps (fewest at the first
-// boundary: A1 is followed by A2, A3, the 7 lead k-steps and k-steps 0..2), so waiting
-// until at most that many loads are outstanding suffices everywhere.
-constexpr int kPBoundaryWait = (kPStages - 2) * kPLoadsA + 4 * (kPLead + 3);
-static_assert(kPBoundaryWait < 64, "vmcnt range");
-
-struct PackedIO {
-  const char* a_base;  // uniform: the tile's activation rows (or a, with a gather)
-  uint32_t a_off[kPLoadsA];
-  const char* w_base;  // uniform: this wave's weight panel
-  uint32_t w_off[4];   // row block tn of the panel + this lane's 16 bytes
-  int a_row;
-  int co[4];           // swizzled element offset of this lane's chunk per k-step
-  int KT, KS;          // stages and k-steps of the reduction
-  int wave;
-
-  // activation stage `stage` (clamped to the last) into buf: this wave fills the 32 rows
-  // of row block `wave`, 8 rows x 128 bytes per instruction
-  __device__ __forceinline__ void dma_a(uint16_t* buf, int stage) const {
-#if defined(__HIP_DEVICE_COMPILE__)
-    const int st = min(stage, KT - 1);
-    const __amdgpu_buffer_rsrc_t r = __builtin_amdgcn_make_buffer_rsrc(
-        const_cast<char*>(a_base + st * kBK * 2), static_cast<short>(0), -1, 0x00020000);
-#pragma unroll
-    for (int j = 0; j < kPLoadsA; ++j)
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(
-          r, (lds_void_t*)(buf + (wave * kPLoadsA + j) * 8 * kBK), 16, a_off[j], 0, 0, 0);
-#endif
-  }
-  // weight fragments of k-step ks (clamped to the last) of the panel's 4 row blocks
-  __device__ __forceinline__ void load_w(bf16x8_t (&w)[4], int ks) const {
-#if defined(__HIP_DEVICE_COMPILE__)
-    const int t = min(ks, KS - 1);
-    const __amdgpu_buffer_rsrc_t r = __builtin_amdgcn_make_buffer_rsrc(
-        const_cast<char*>(w_base), static_cast<short>(0), -1, 0x00020000);
-#pragma unroll
-    for (int tn = 0; tn < 4; ++tn)
-      w[tn] = __builtin_bit_cast(bf16x8_t,
-                                 __builtin_amdgcn_raw_buffer_load_b128(r, w_off[tn], t * 1024, 0));
-#endif
-  }
-  template <int TA>
-  __device__ __forceinline__ void read_a(const uint16_t* buf, int kstep, bf16x8_t (&a)[4]) const {
-#pragma unroll
-    for (int tm = 0; tm < TA; ++tm)
-      a[tm] = *reinterpret_cast<const bf16x8_t*>(&buf[a_row + tm * 32 * kBK + co[kstep]]);
-  }
-};
-
-// K-step t, at position T of the 16-k-step period of both rings (activation stage
-// T / 4 % 4, weight slot T % 8).  The fragments of this k-step are in af[T & 1] and
-// wr[T % 8]; the next k-step's activation fragments are read into af[(T + 1) & 1] and
-// the weights of k-step t + 7 loaded into the slot this k-step's predecessor freed.
-template <int T, int TA>
-__device__ __forceinline__ void pk_step(const PackedIO& io, uint16_t* const (&A)[kPStages], int t,
-                                        bf16x8_t (&wr)[kPRing][4], bf16x8_t (&af)[2][4],
-                                        f32x16_t (&acc)[4][4]) {
-  constexpr int J = T % 4, SB = T / 4;
-  if constexpr (J == 3) {
-    // every wave has read its fragments of this stage: its buffer takes stage s + 4
-    barrier_keep_loads<kPBoundaryWait>();
-    io.dma_a(A[SB], t / 4 + kPStages);
-  }
-  io.load_w(wr[(T + kPLead) % kPRing], t + kPLead);
-  io.template read_a<TA>(A[J == 3 ? (SB + 1) % kPStages : SB], (J + 1) % 4, af[(T + 1) & 1]);
-#pragma unroll
-  for (int tn = 0; tn < 4; ++tn)
-#pragma unroll
-    for (int tm = 0; tm < TA; ++tm)
-      acc[tn][tm] = Mfma<32>::mma(wr[T % kPRing][tn], af[T & 1][tm], acc[tn][tm]);
-  sched_mix<4 + (J == 3 ? kPLoadsA : 0), TA, 4 * TA, 0, 8>();
-}
-
-template <int T, int TA>
-__device__ __forceinline__ void pk_period(const PackedIO& io, uint16_t* const (&A)[kPStages],
-                                          int t0, bf16x8_t (&wr)[kPRing][4],
-                                          bf16x8_t (&af)[2][4], f32x16_t (&acc)[4][4]) {
-  if constexpr (T < 16) {
-    pk_step<T, TA>(io, A, t0 + T, wr, af, acc);
-    pk_period<T + 1, TA>(io, A, t0, wr, af, acc);
-  }
-}
-
-// The last rem (< 16, a multiple of 4) k-steps.
-template <int T, int TA>
-__device__ __forceinline__ void pk_tail(const PackedIO& io, uint16_t* const (&A)[kPStages], int t0,
-                                        int rem, bf16x8_t (&wr)[kPRing][4], bf16x8_t (&af)[2][4],
-                                        f32x16_t (&acc)[4][4]) {
-  if constexpr (T < 16) {
-    if (T < rem) {
-      pk_step<T, TA>(io, A, t0 + T, wr, af, acc);
-      pk_tail<T + 1, TA>(io, A, t0, rem, wr, af, acc);
-    }
-  }
-}
 
 // Epilogue of the packed-weight kernels: register 4q + r of acc[tn][tm] is activation
 // row tm*32 + lane%32 of the tile and output column col0 + tn*32 + 8q + 4(lane/32) + r
@@ -1084,219 +980,6 @@ __device__ __forceinline__ void packed_epilogue(const GemmArgs& g, const Tile& t
 template <int EPI>
 __device__ __forceinline__ int panel_col0(int p) { return p * (EPI == EPI_SWIGLU ? 64 : 128); }
 
-// Partial accumulators of a split packed tile (a slot of gemm_split_floats' 65536
-// floats per part): float4 chunk c of thread t at [c][t], c = (tn*4 + tm)*4 + v.
-__device__ __forceinline__ int pk_chunk(int tn, int tm, int v) { return (tn * 4 + tm) * 4 + v; }
-__device__ __forceinline__ f32x4_t* pk_slot(float* buf, int slot) {
-  return reinterpret_cast<f32x4_t*>(buf + static_cast<int64_t>(slot) * kPBM * kPBN);
-}
-
-template <int TA>
-__device__ __forceinline__ void packed_split_store(const GemmArgs& g, const Tile& tile,
-                                                   f32x16_t (&acc)[4][4]) {
-  const int tid = threadIdx.x;
-  f32x4_t* mine = pk_slot(g.split_buf, tile.split_q * tile.nparts + tile.part);
-#pragma unroll
-  for (int tn = 0; tn < 4; ++tn)
-#pragma unroll
-    for (int tm = 0; tm < TA; ++tm)
-#pragma unroll
-      for (int v = 0; v < 4; ++v) {
-        f32x4_t q;
-#pragma unroll
-        for (int r = 0; r < 4; ++r) q[r] = acc[tn][tm][4 * v + r];
-        mine[pk_chunk(tn, tm, v) * kThreads + tid] = q;
-      }
-  if (tile.part == 0 && tid == 0) {
-    int32_t* d = g.split_desc + 1 + 5 * tile.split_q;
-    d[0] = tile.seg;
-    d[1] = static_cast<int32_t>(tile.row0);
-    d[2] = tile.m_valid;
-    d[3] = tile.nt;
-    d[4] = tile.nparts;
-  }
-}
-
-// K loop and epilogue (or, for a part of a split tile, the store of its partial sums) of
-// a tile whose rows fill TA row blocks of 32.
-template <int EPI, int TA>
-__device__ __forceinline__ void packed_body(const GemmArgs& g, const Tile& tile, const PackedIO& io,
-                                            uint16_t* const (&A)[kPStages], int lane, int p) {
-  f32x16_t acc[4][4];
-#pragma unroll
-  for (int tn = 0; tn < 4; ++tn)
-#pragma unroll
-    for (int tm = 0; tm < TA; ++tm)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) acc[tn][tm][r] = 0.f;
-  bf16x8_t wr[kPRing][4];
-  bf16x8_t af[2][4];
-  // prologue: activation stages 0..3, then weight k-steps 0..6 in order (kept in order,
-  // so that the loop's waits for each slot are the same on entry as on every turn)
-#pragma unroll
-  for (int st = 0; st < kPStages; ++st) io.dma_a(A[st], st);
-#pragma unroll
-  for (int t = 0; t < kPLead; ++t) {
-    io.load_w(wr[t], t);
-    __builtin_amdgcn_sched_barrier(0);
-  }
-  barrier_keep_loads<(kPStages - 1) * kPLoadsA + 4 * kPLead>();
-  io.template read_a<TA>(A[0], 0, af[0]);
-  int t0 = 0;
-  for (; t0 + 16 <= io.KS; t0 += 16) pk_period<0, TA>(io, A, t0, wr, af, acc);
-  pk_tail<0, TA>(io, A, t0, io.KS - t0, wr, af, acc);
-  // no load may still be writing this workgroup's LDS when it exits
-  __builtin_amdgcn_s_waitcnt(0);
-  if (tile.nparts > 1) {
-    packed_split_store<TA>(g, tile, acc);
-    return;
-  }
-  packed_epilogue<EPI, 4, 4, TA>(g, tile, lane, panel_col0<EPI>(p), acc);
-}
-
-template <int EPI>
-__global__ __launch_bounds__(kThreads, 1) void gemm_packed_kernel(GemmArgs g) {
-  __shared__ __attribute__((aligned(16))) uint16_t A0[kPBM * kBK], A1[kPBM * kBK];
-  __shared__ __attribute__((aligned(16))) uint16_t A2[kPBM * kBK], A3[kPBM * kBK];
-  __shared__ SchedSmem sched;
-  uint16_t* const A[kPStages] = {A0, A1, A2, A3};
-  // the launch stands for the 256-row tiles: it does nothing where the dispatch chose
-  // the 32-row ones
-  if (g.small_tiles && *g.small_tiles != 0) return;
-  Tile tile;
-  if (!schedule_tile<kPBM>(g.seg_off, g.n_seg, g.single_rows, g.max_rows, g.bp_rows / kPBN,
-                           g.k / kBK, g.split_g, g.split_desc, sched, tile))
-    return;
-  // the work item is uniform over the workgroup: keep its fields in scalar registers
-  tile.k_stage0 = __builtin_amdgcn_readfirstlane(tile.k_stage0);
-  tile.k_stages = __builtin_amdgcn_readfirstlane(tile.k_stages);
-  tile.nparts = __builtin_amdgcn_readfirstlane(tile.nparts);
-  const int tid = threadIdx.x;
-  const int lane = tid & (kWave - 1);
-  const int wave = __builtin_amdgcn_readfirstlane(tid / kWave);
-  PackedIO io;
-  io.wave = wave;
-  io.KT = tile.k_stages;  // a part of a split tile covers stages k_stage0 .. + k_stages
-  io.KS = 4 * tile.k_stages;
-  const int32_t* __restrict__ a_rows = g.a_rows;
-  io.a_base = uniform_ptr(reinterpret_cast<const char*>(
-      static_cast<const uint16_t*>(g.a) + (a_rows ? 0 : tile.row0 * g.lda) +
-      static_cast<int64_t>(tile.k_stage0) * kBK));
-#pragma unroll
-  for (int j = 0; j < kPLoadsA; ++j) {
-    const int i = 8 * (wave * kPLoadsA + j) + (lane >> 3);  // LDS row of the tile
-    const int r = min(i, tile.m_valid - 1);  // rows past the segment repeat its last row
-    const uint32_t src = a_rows ? static_cast<uint32_t>(a_rows[tile.row0 + r]) : r;
-    const int chunk = ((lane & 7) ^ lds_swizzle(i)) * 8;
-    io.a_off[j] = (src * static_cast<uint32_t>(g.lda) + chunk) * 2u;
-  }
-  const int p = tile.nt * 4 + wave;  // this wave's 128-row weight panel
-  io.w_base = uniform_ptr(static_cast<const char*>(g.bp) + tile.seg * g.bp_seg_stride +
-                          static_cast<int64_t>(p) * 128 * g.k * 2 +
-                          static_cast<int64_t>(tile.k_stage0) * 4 * 1024);
-#pragma unroll
-  for (int tn = 0; tn < 4; ++tn)
-    io.w_off[tn] = static_cast<uint32_t>(tn) * static_cast<uint32_t>(g.k) * 64u +
-                   static_cast<uint32_t>(lane) * 16u;
-  const int frow = lane & 31;
-#pragma unroll
-  for (int ks = 0; ks < 4; ++ks) io.co[ks] = (Mfma<32>::chunk(lane, ks) ^ lds_swizzle(frow)) * 8;
-  io.a_row = frow * kBK;
-  const int ta = __builtin_amdgcn_readfirstlane(min((tile.m_valid + 31) / 32, 4));
-  if (ta >= 4)
-    packed_body<EPI, 4>(g, tile, io, A, lane, p);
-  else if (ta == 3)
-    packed_body<EPI, 3>(g, tile, io, A, lane, p);
-  else if (ta == 2)
-    packed_body<EPI, 2>(g, tile, io, A, lane, p);
-  else
-    packed_body<EPI, 1>(g, tile, io, A, lane, p);
-}
-
-// Finishes the split tiles of the preceding gemm_packed_kernel launch: one single-wave
-// workgroup per (split tile, wave of the tile, half h of that wave's output tiles, row
-// block tm) loads its accumulators of every part, sums them in part order and runs its
-// share of the epilogue (SwiGLU: W1 tile h with W3 tile h + 2; otherwise tiles 2h,
-// 2h + 1).  32 workgroups per tile, each with all its loads issued before the first
-// sum, keep the partials' reads in flight together.
-template <int EPI, int H, int TM>
-__device__ __forceinline__ void packed_finish(const GemmArgs& g, const Tile& tile, int q, int tid,
-                                              int lane, int p) {
-  constexpr int TNA = EPI == EPI_SWIGLU ? H : 2 * H;
-  constexpr int TNB = EPI == EPI_SWIGLU ? H + 2 : 2 * H + 1;
-  f32x4_t x[kMaxSplitParts][2][4];
-#pragma unroll
-  for (int part = 0; part < kMaxSplitParts; ++part) {
-    if (part < tile.nparts) {
-      const f32x4_t* sp = pk_slot(g.split_buf, q * tile.nparts + part);
-#pragma unroll
-      for (int v = 0; v < 4; ++v) {
-        x[part][0][v] = sp[pk_chunk(TNA, TM, v) * kThreads + tid];
-        x[part][1][v] = sp[pk_chunk(TNB, TM, v) * kThreads + tid];
-      }
-    }
-  }
-  f32x16_t acc[4][4];
-#pragma unroll
-  for (int v = 0; v < 4; ++v)
-#pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      acc[TNA][TM][4 * v + r] = x[0][0][v][r];
-      acc[TNB][TM][4 * v + r] = x[0][1][v][r];
-    }
-#pragma unroll
-  for (int part = 1; part < kMaxSplitParts; ++part) {
-    if (part < tile.nparts) {
-#pragma unroll
-      for (int v = 0; v < 4; ++v)
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          acc[TNA][TM][4 * v + r] += x[part][0][v][r];
-          acc[TNB][TM][4 * v + r] += x[part][1][v][r];
-        }
-    }
-  }
-  // (TA = 4 only sizes the epilogue's per-row arrays; the row block is TM)
-  if constexpr (EPI == EPI_SWIGLU)
-    packed_epilogue<EPI, 4, 4, 4, H, H + 1, TM, TM + 1>(g, tile, lane, panel_col0<EPI>(p), acc);
-  else
-    packed_epilogue<EPI, 4, 4, 4, 2 * H, 2 * H + 2, TM, TM + 1>(g, tile, lane, panel_col0<EPI>(p),
-                                                               acc);
-}
-
-template <int EPI>
-__global__ __launch_bounds__(kWave) void gemm_packed_finish_kernel(GemmArgs g) {
-  const int q = blockIdx.x / 32, wave = (blockIdx.x / 8) % 4, h = (blockIdx.x / 4) % 2;
-  const int tm = blockIdx.x % 4;
-  // (the product launch it finishes did nothing: its split descriptors are stale)
-  if (g.small_tiles && *g.small_tiles != 0) return;
-  if (q >= g.split_desc[0]) return;
-  const int32_t* d = g.split_desc + 1 + 5 * q;
-  Tile tile;
-  tile.seg = d[0];
-  tile.row0 = d[1];
-  tile.m_valid = d[2];
-  tile.nt = d[3];
-  tile.nparts = __builtin_amdgcn_readfirstlane(d[4]);
-  tile.part = 0;
-  tile.split_q = q;
-  tile.k_stage0 = 0;
-  tile.k_stages = 0;
-  if (tm * 32 >= tile.m_valid) return;  // this row block holds no rows of the tile
-  const int lane = threadIdx.x;
-  const int tid = wave * kWave + lane;  // the thread of the tile's workgroup this lane stands for
-  const int p = tile.nt * 4 + wave;
-  auto run = [&](auto h_c) {
-    constexpr int H = decltype(h_c)::value;
-    if (tm == 0) packed_finish<EPI, H, 0>(g, tile, q, tid, lane, p);
-    else if (tm == 1) packed_finish<EPI, H, 1>(g, tile, q, tid, lane, p);
-    else if (tm == 2) packed_finish<EPI, H, 2>(g, tile, q, tid, lane, p);
-    else packed_finish<EPI, H, 3>(g, tile, q, tid, lane, p);
-  };
-  if (h == 0) run(std::integral_constant<int, 0>{});
-  else run(std::integral_constant<int, 1>{});
-}
-
 // Writes the packed copy of E experts' weights: one thread per 16-byte piece of the
 // output (first-layer products of all experts, then second-layer ones), zeros for the
 // padding rows.  Piece i of an expert's product with reduction K is lane i % 64 of
@@ -1346,6 +1029,7 @@ __global__ __launch_bounds__(256) void pack_weights_kernel(
 // segment repeat its last row.
 constexpr int kSRing = 8;
 constexpr int kSLead = kSRing - 1;
+constexpr int kSBN = 512;  // packed weight rows per tile (4 waves x 128)
 
 struct PackedSmallIO {
   const char* a_base;  // uniform
@@ -1407,7 +1091,7 @@ __global__ __launch_bounds__(kThreads, 2) void gemm_packed_small_kernel(GemmArgs
   // where the dispatch chose them
   if (g.small_tiles && *g.small_tiles != 1) return;
   Tile tile;
-  if (!schedule_tile<32>(g.seg_off, g.n_seg, g.single_rows, g.max_rows, g.bp_rows / kPBN,
+  if (!schedule_tile<32>(g.seg_off, g.n_seg, g.single_rows, g.max_rows, g.bp_rows / kSBN,
                          g.k / kBK, 0, nullptr, sched, tile))
     return;
   const int tid = threadIdx.x;
@@ -1447,39 +1131,53 @@ __global__ __launch_bounds__(kThreads, 2) void gemm_packed_small_kernel(GemmArgs
   packed_epilogue<EPI, 4, 4, 1>(g, tile, lane, panel_col0<EPI>(p), acc);
 }
 
-// ------------------------------------------------------------------ packed-weight kernel, mid-size segments
-// Segments of a few dozen to a few hundred rows (fine-grained experts, capacity-limited
-// batches): the products are bound by the weight stream.  A tile is up to BM activation
-// rows x 256 packed weight rows; each of the 4 waves streams 64 weight rows of its own
-// (SwiGLU: 32 rows of W1 and the same 32 of W3) from the packed copy into a register
-// ring (each k-step's 2 fragments loaded RING - 1 k-steps ahead) and multiplies them
-// with all of the tile's active row blocks, which pass through LDS (4 stages of 64 k,
-// direct-to-LDS loads 4 stages ahead).  Only the active row blocks (TA of BM / 32) are
-// loaded and multiplied, so a tile's MFMA work and activation traffic follow its rows.
-// Activation load j of wave w fills the 8-row group 4j + w, so every wave issues TA
-// loads per stage and the in-order wait counts depend on TA only.
-// The shape in use is BM = 256: a whole segment of up to 256 rows per tile, so every
-// (segment, column tile) reads its weights once; one workgroup per CU with a 16-k-step
-// ring.  (BM = 128 with two workgroups per CU and an 8-k-step ring was measured too:
-// the Switch-shaped first layer 0.161 -> 0.148 ms, but its second layer 0.144 -> 0.167
-// and the DeepSeek-shaped first layer 1.06 -> 1.57 ms, where a second row tile
-// re-streams the weights.)
-constexpr int kMBN = 256;   // packed weight rows per tile (two 128-row panels)
-
-template <int BM_, int RING_>
-struct MidShape {
+// ------------------------------------------------------------------ packed-weight kernel (long and mid-size segments)
+// A tile is up to BM activation rows x 64 NW packed weight rows; each of the NW waves
+// streams 64 weight rows of its own (SwiGLU: 32 rows of W1 and the same 32 of W3) from
+// the packed copy into a register ring (each k-step's 2 fragments loaded RING - 1
+// k-steps ahead) and multiplies them with all of the tile's active row blocks, which
+// pass through LDS (4 stages of 64 k, direct-to-LDS loads 4 stages ahead, one barrier
+// per stage).  Only the active row blocks (TA of BM / 32) are loaded and multiplied, so
+// a tile's MFMA work and activation traffic follow its rows.  Activation load j of wave
+// w fills the 8-row group NW j + w.  Two shapes:
+//   * PackedLong (segments of >= 256 rows): 128 x 512 tiles of 8 waves, two per SIMD,
+//     each with 128 accumulator registers and an 8-k-step ring, so the other wave's
+//     MFMAs cover a wave's waits (Mixtral-shaped first layer 1.79 -> 1.66 ms against
+//     4 waves of 128 x 128 each); a partial last round splits along K.
+//   * PackedMid (48 .. 255 rows): 256 x 256 tiles of 4 waves with a 16-k-step ring, a
+//     whole segment of up to 256 rows per tile, so every (segment, column tile) reads
+//     its weights once; these products are bound by the weight stream.  (128-row tiles
+//     with two workgroups per CU were measured too: the Switch-shaped first layer
+//     0.161 -> 0.148 ms, but its second layer 0.144 -> 0.167 and the DeepSeek-shaped
+//     first layer 1.06 -> 1.57 ms, where a second row tile re-streams the weights.)
+template <int BM_, int RING_, int NW_, int GATE_>
+struct PackedShape {
+  // under a device-chosen tile height (GemmArgs.small_tiles set) the launch runs only
+  // where the dispatch's flag equals GATE: 1 for the short-segment shape, 0 for the long
+  static constexpr int GATE = GATE_;
+  // the long-segment shape splits a partial last round along K; the other never does
+  static constexpr bool SPLIT = GATE_ == 0;
   static constexpr int BM = BM_;
   static constexpr int TMAX = BM / 32;  // activation row blocks
   static constexpr int RING = RING_;    // weight register ring, in k-steps
   static constexpr int LEAD = RING - 1;
-  static constexpr int OCC = BM >= 256 ? 1 : 2;  // workgroups per CU
+  static constexpr int NW = NW_;        // waves per workgroup, 64 packed weight rows each
+  static constexpr int NT = NW * kWave;
+  static constexpr int BN = NW * 64;
+  // activation loads (8-row groups) per wave and stage: group g goes to wave g % NW
+  static constexpr int JMAX = (4 * TMAX + NW - 1) / NW;
+  template <int TA>
+  static constexpr int na_min() { return 4 * TA / NW; }  // fewest any wave issues
+  template <int TA>
+  static constexpr int na_max() { return (4 * TA + NW - 1) / NW; }
 };
-using MidLarge = MidShape<256, 16>;
+using PackedMid = PackedShape<256, 16, 4, 1>;
+using PackedLong = PackedShape<128, 8, 8, 0>;
 
 template <class MS>
-struct MidIO {
+struct PackedIO {
   const char* a_base;         // uniform: the tile's activation rows (or a, with a gather)
-  uint32_t a_off[MS::TMAX];   // load j: 8-row group 4j + wave, this lane's row and 16 bytes
+  uint32_t a_off[MS::JMAX];   // load j: 8-row group NW j + wave, this lane's row and 16 bytes
   const char* w_base;         // uniform: this wave's 128-row weight panel
   uint32_t w_off[2];          // this wave's two 32-row blocks of the panel + this lane's 16 bytes
   int a_row;
@@ -1494,9 +1192,10 @@ struct MidIO {
     const __amdgpu_buffer_rsrc_t r = __builtin_amdgcn_make_buffer_rsrc(
         const_cast<char*>(a_base + st * kBK * 2), static_cast<short>(0), -1, 0x00020000);
 #pragma unroll
-    for (int j = 0; j < TA; ++j)
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(
-          r, (lds_void_t*)(buf + (4 * j + wave) * 8 * kBK), 16, a_off[j], 0, 0, 0);
+    for (int j = 0; j < MS::template na_max<TA>(); ++j)
+      if (j < MS::template na_min<TA>() || MS::NW * j + wave < 4 * TA)
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(
+            r, (lds_void_t*)(buf + (MS::NW * j + wave) * 8 * kBK), 16, a_off[j], 0, 0, 0);
 #endif
   }
   __device__ __forceinline__ void load_w(bf16x8_t (&w)[2], int ks) const {
@@ -1519,25 +1218,27 @@ struct MidIO {
   }
 };
 
-// Stage boundary wait of the mid-size kernel: the next stage's activation loads must
+// Stage boundary wait of the packed kernel: the next stage's activation loads must
 // have landed; issued after them are at least two later stages' activation loads and
 // LEAD + 3 k-steps' weight loads (fewest at the first boundary: A1 is followed by A2,
-// A3, the lead k-steps of the prologue and those issued in k-steps 0..2).
+// A3, the lead k-steps of the prologue and those issued in k-steps 0..2).  Where waves
+// issue different numbers of activation loads (NW = 8), the wave with the fewest sets
+// the count, which waits at least as long as every wave needs.
 template <class MS, int TA>
-struct MidWait {
-  static constexpr int kBoundary = (kPStages - 2) * TA + 2 * (MS::LEAD + 3);
-  static constexpr int kPrologue = (kPStages - 1) * TA + 2 * MS::LEAD;
+struct PackedWait {
+  static constexpr int kBoundary = (kPStages - 2) * MS::template na_min<TA>() + 2 * (MS::LEAD + 3);
+  static constexpr int kPrologue = (kPStages - 1) * MS::template na_min<TA>() + 2 * MS::LEAD;
   static_assert(kBoundary < 64 && kPrologue < 64, "vmcnt range");
 };
 
 template <class MS, int T, int TA>
-__device__ __forceinline__ void md_step(const MidIO<MS>& io, uint16_t* const (&A)[kPStages], int t,
+__device__ __forceinline__ void pk_step(const PackedIO<MS>& io, uint16_t* const (&A)[kPStages], int t,
                                         bf16x8_t (&wr)[MS::RING][2],
                                         bf16x8_t (&af)[2][MS::TMAX],
                                         f32x16_t (&acc)[2][MS::TMAX]) {
   constexpr int J = T % 4, SB = T / 4;
   if constexpr (J == 3) {
-    barrier_keep_loads<MidWait<MS, TA>::kBoundary>();
+    barrier_keep_loads<PackedWait<MS, TA>::kBoundary>();
     io.template dma_a<TA>(A[SB], t / 4 + kPStages);
   }
   io.load_w(wr[(T + MS::LEAD) % MS::RING], t + MS::LEAD);
@@ -1547,35 +1248,74 @@ __device__ __forceinline__ void md_step(const MidIO<MS>& io, uint16_t* const (&A
 #pragma unroll
     for (int tm = 0; tm < TA; ++tm)
       acc[tn][tm] = Mfma<32>::mma(wr[T % MS::RING][tn], af[T & 1][tm], acc[tn][tm]);
-  sched_mix<2 + (J == 3 ? TA : 0), TA, 2 * TA, 0, 8>();
+  sched_mix<2 + (J == 3 ? MS::template na_max<TA>() : 0), TA, 2 * TA, 0, 8>();
 }
 
 template <class MS, int T, int TA>
-__device__ __forceinline__ void md_period(const MidIO<MS>& io, uint16_t* const (&A)[kPStages],
+__device__ __forceinline__ void pk_period(const PackedIO<MS>& io, uint16_t* const (&A)[kPStages],
                                           int t0, bf16x8_t (&wr)[MS::RING][2],
                                           bf16x8_t (&af)[2][MS::TMAX],
                                           f32x16_t (&acc)[2][MS::TMAX]) {
   if constexpr (T < 16) {
-    md_step<MS, T, TA>(io, A, t0 + T, wr, af, acc);
-    md_period<MS, T + 1, TA>(io, A, t0, wr, af, acc);
+    pk_step<MS, T, TA>(io, A, t0 + T, wr, af, acc);
+    pk_period<MS, T + 1, TA>(io, A, t0, wr, af, acc);
   }
 }
 
 template <class MS, int T, int TA>
-__device__ __forceinline__ void md_tail(const MidIO<MS>& io, uint16_t* const (&A)[kPStages],
+__device__ __forceinline__ void pk_tail(const PackedIO<MS>& io, uint16_t* const (&A)[kPStages],
                                         int t0, int rem, bf16x8_t (&wr)[MS::RING][2],
                                         bf16x8_t (&af)[2][MS::TMAX],
                                         f32x16_t (&acc)[2][MS::TMAX]) {
   if constexpr (T < 16) {
     if (T < rem) {
-      md_step<MS, T, TA>(io, A, t0 + T, wr, af, acc);
-      md_tail<MS, T + 1, TA>(io, A, t0, rem, wr, af, acc);
+      pk_step<MS, T, TA>(io, A, t0 + T, wr, af, acc);
+      pk_tail<MS, T + 1, TA>(io, A, t0, rem, wr, af, acc);
     }
   }
 }
 
+// Partial accumulators of a split tile of the packed kernel: a slot of
+// gemm_split_floats' 65536 floats per part; float4 chunk c = (tn TMAX + tm) 4 + v of
+// thread t at [c][t], so each access instruction covers NT * 16 contiguous bytes.
+template <class MS>
+struct PackedSplit {
+  static_assert(2 * MS::TMAX * 4 * MS::NT * 4 == 65536, "one split slot per part");
+  __device__ static f32x4_t* slot(float* buf, int s) {
+    return reinterpret_cast<f32x4_t*>(buf + static_cast<int64_t>(s) * 65536);
+  }
+  __device__ static int chunk(int tn, int tm, int v) { return (tn * MS::TMAX + tm) * 4 + v; }
+};
+
+template <class MS, int TA>
+__device__ __forceinline__ void packed_split_store(const GemmArgs& g, const Tile& tile,
+                                                f32x16_t (&acc)[2][MS::TMAX]) {
+  using SP = PackedSplit<MS>;
+  const int tid = threadIdx.x;
+  f32x4_t* mine = SP::slot(g.split_buf, tile.split_q * tile.nparts + tile.part);
+#pragma unroll
+  for (int tn = 0; tn < 2; ++tn)
+#pragma unroll
+    for (int tm = 0; tm < TA; ++tm)
+#pragma unroll
+      for (int v = 0; v < 4; ++v) {
+        f32x4_t q;
+#pragma unroll
+        for (int r = 0; r < 4; ++r) q[r] = acc[tn][tm][4 * v + r];
+        mine[SP::chunk(tn, tm, v) * MS::NT + tid] = q;
+      }
+  if (tile.part == 0 && tid == 0) {
+    int32_t* d = g.split_desc + 1 + 5 * tile.split_q;
+    d[0] = tile.seg;
+    d[1] = static_cast<int32_t>(tile.row0);
+    d[2] = tile.m_valid;
+    d[3] = tile.nt;
+    d[4] = tile.nparts;
+  }
+}
+
 template <class MS, int EPI, int TA>
-__device__ __forceinline__ void mid_body(const GemmArgs& g, const Tile& tile, const MidIO<MS>& io,
+__device__ __forceinline__ void packed_body(const GemmArgs& g, const Tile& tile, const PackedIO<MS>& io,
                                          uint16_t* const (&A)[kPStages], int lane, int col0) {
   static_assert(16 % MS::RING == 0, "the ring period divides the 16-k-step period");
   f32x16_t acc[2][MS::TMAX];
@@ -1595,53 +1335,65 @@ __device__ __forceinline__ void mid_body(const GemmArgs& g, const Tile& tile, co
     io.load_w(wr[t], t);
     __builtin_amdgcn_sched_barrier(0);
   }
-  barrier_keep_loads<MidWait<MS, TA>::kPrologue>();
+  barrier_keep_loads<PackedWait<MS, TA>::kPrologue>();
   io.template read_a<TA>(A[0], 0, af[0]);
   int t0 = 0;
-  for (; t0 + 16 <= io.KS; t0 += 16) md_period<MS, 0, TA>(io, A, t0, wr, af, acc);
-  md_tail<MS, 0, TA>(io, A, t0, io.KS - t0, wr, af, acc);
+  for (; t0 + 16 <= io.KS; t0 += 16) pk_period<MS, 0, TA>(io, A, t0, wr, af, acc);
+  pk_tail<MS, 0, TA>(io, A, t0, io.KS - t0, wr, af, acc);
   // no load may still be writing this workgroup's LDS when it exits
   __builtin_amdgcn_s_waitcnt(0);
+  if constexpr (MS::SPLIT) {
+    if (tile.nparts > 1) {
+      packed_split_store<MS, TA>(g, tile, acc);
+      return;
+    }
+  }
   packed_epilogue<EPI, 2, MS::TMAX, TA>(g, tile, lane, col0, acc);
 }
 
 template <class MS, int EPI>
-__global__ __launch_bounds__(kThreads, MS::OCC) void gemm_packed_mid_kernel(GemmArgs g) {
+__global__ __launch_bounds__(MS::NT, 1) void gemm_packed_kernel(GemmArgs g) {
   __shared__ __attribute__((aligned(16))) uint16_t A0[MS::BM * kBK], A1[MS::BM * kBK];
   __shared__ __attribute__((aligned(16))) uint16_t A2[MS::BM * kBK], A3[MS::BM * kBK];
   __shared__ SchedSmem sched;
   uint16_t* const A[kPStages] = {A0, A1, A2, A3};
-  // as the alternative of a 128 x 512 launch (device-chosen height) it runs only where
-  // the dispatch chose the short tiles
-  if (g.small_tiles && *g.small_tiles != 1) return;
+  // with a device-chosen tile height the launch runs only where the dispatch chose it
+  if (g.small_tiles && *g.small_tiles != MS::GATE) return;
   Tile tile;
-  if (!schedule_tile<MS::BM>(g.seg_off, g.n_seg, g.single_rows, g.max_rows, g.bp_rows / kMBN,
-                             g.k / kBK, 0, nullptr, sched, tile))
+  if (!schedule_tile<MS::BM, MS::NT>(g.seg_off, g.n_seg, g.single_rows, g.max_rows,
+                                     g.bp_rows / MS::BN, g.k / kBK, MS::SPLIT ? g.split_g : 0,
+                                     MS::SPLIT ? g.split_desc : nullptr, sched, tile))
     return;
+  // the work item is uniform over the workgroup: keep its fields in scalar registers
+  tile.k_stage0 = __builtin_amdgcn_readfirstlane(tile.k_stage0);
+  tile.k_stages = __builtin_amdgcn_readfirstlane(tile.k_stages);
+  tile.nparts = __builtin_amdgcn_readfirstlane(tile.nparts);
   const int tid = threadIdx.x;
   const int lane = tid & (kWave - 1);
-  const int wave = __builtin_amdgcn_readfirstlane(tid / kWave);
-  MidIO<MS> io;
+  const int wave = __builtin_amdgcn_readfirstlane(tid / kWave);  // 0 .. NW - 1
+  PackedIO<MS> io;
   io.wave = wave;
-  io.KT = g.k / kBK;
+  io.KT = tile.k_stages;  // a part of a split tile covers stages k_stage0 .. + k_stages
   io.KS = 4 * io.KT;
   const int32_t* __restrict__ a_rows = g.a_rows;
   io.a_base = uniform_ptr(reinterpret_cast<const char*>(
-      static_cast<const uint16_t*>(g.a) + (a_rows ? 0 : tile.row0 * g.lda)));
+      static_cast<const uint16_t*>(g.a) + (a_rows ? 0 : tile.row0 * g.lda) +
+      static_cast<int64_t>(tile.k_stage0) * kBK));
 #pragma unroll
-  for (int j = 0; j < MS::TMAX; ++j) {
-    const int i = 8 * (4 * j + wave) + (lane >> 3);  // LDS row of the tile
-    const int r = min(i, tile.m_valid - 1);          // rows past the segment repeat its last row
+  for (int j = 0; j < MS::JMAX; ++j) {
+    const int i = 8 * (MS::NW * j + wave) + (lane >> 3);  // LDS row of the tile
+    const int r = min(i, tile.m_valid - 1);  // rows past the segment repeat its last row
     const uint32_t src = a_rows ? static_cast<uint32_t>(a_rows[tile.row0 + r]) : r;
     const int chunk = ((lane & 7) ^ lds_swizzle(i)) * 8;
     io.a_off[j] = (src * static_cast<uint32_t>(g.lda) + chunk) * 2u;
   }
-  // wave w: panel p = 2 nt + w / 2, half h = w % 2 of it.  SwiGLU panels are 32-row
-  // blocks W1a W1b W3a W3b: half h takes W1 block h and W3 block h (output columns
-  // 64 p + 32 h ..); other panels take blocks 2h, 2h + 1 (columns 128 p + 64 h ..).
-  const int p = tile.nt * 2 + (wave >> 1), h = wave & 1;
+  // wave w: panel p = (NW / 2) nt + w / 2, half h = w % 2 of it.  SwiGLU panels are
+  // 32-row blocks W1a W1b W3a W3b: half h takes W1 block h and W3 block h (output
+  // columns 64 p + 32 h ..); other panels take blocks 2h, 2h + 1 (columns 128 p + 64 h ..).
+  const int p = tile.nt * (MS::NW / 2) + (wave >> 1), h = wave & 1;
   io.w_base = uniform_ptr(static_cast<const char*>(g.bp) + tile.seg * g.bp_seg_stride +
-                          static_cast<int64_t>(p) * 128 * g.k * 2);
+                          static_cast<int64_t>(p) * 128 * g.k * 2 +
+                          static_cast<int64_t>(tile.k_stage0) * 4 * 1024);
 #pragma unroll
   for (int tn = 0; tn < 2; ++tn) {
     const int blk = EPI == EPI_SWIGLU ? h + 2 * tn : 2 * h + tn;
@@ -1655,23 +1407,94 @@ __global__ __launch_bounds__(kThreads, MS::OCC) void gemm_packed_mid_kernel(Gemm
   io.a_row = frow * kBK;
   const int ta = __builtin_amdgcn_readfirstlane(min((tile.m_valid + 31) / 32, MS::TMAX));
   switch (ta) {
-    case 1: mid_body<MS, EPI, 1>(g, tile, io, A, lane, col0); break;
-    case 2: mid_body<MS, EPI, 2>(g, tile, io, A, lane, col0); break;
-    case 3: mid_body<MS, EPI, 3>(g, tile, io, A, lane, col0); break;
+    case 1: packed_body<MS, EPI, 1>(g, tile, io, A, lane, col0); break;
+    case 2: packed_body<MS, EPI, 2>(g, tile, io, A, lane, col0); break;
+    case 3: packed_body<MS, EPI, 3>(g, tile, io, A, lane, col0); break;
     default:
       if constexpr (MS::TMAX == 4) {
-        mid_body<MS, EPI, 4>(g, tile, io, A, lane, col0);
+        packed_body<MS, EPI, 4>(g, tile, io, A, lane, col0);
       } else {
         switch (ta) {
-          case 4: mid_body<MS, EPI, 4>(g, tile, io, A, lane, col0); break;
-          case 5: mid_body<MS, EPI, 5>(g, tile, io, A, lane, col0); break;
-          case 6: mid_body<MS, EPI, 6>(g, tile, io, A, lane, col0); break;
-          case 7: mid_body<MS, EPI, 7>(g, tile, io, A, lane, col0); break;
-          default: mid_body<MS, EPI, MS::TMAX>(g, tile, io, A, lane, col0); break;
+          case 4: packed_body<MS, EPI, 4>(g, tile, io, A, lane, col0); break;
+          case 5: packed_body<MS, EPI, 5>(g, tile, io, A, lane, col0); break;
+          case 6: packed_body<MS, EPI, 6>(g, tile, io, A, lane, col0); break;
+          case 7: packed_body<MS, EPI, 7>(g, tile, io, A, lane, col0); break;
+          default: packed_body<MS, EPI, MS::TMAX>(g, tile, io, A, lane, col0); break;
         }
       }
       break;
   }
+}
+
+// Finishes the split tiles of the preceding gemm_packed_kernel launch: one
+// single-wave workgroup per (split tile, wave w of the tile, row block tm) loads that
+// wave's accumulators of the row block from every part, sums them in part order and
+// runs the row block's epilogue.
+template <class MS, int EPI, int TM>
+__device__ __forceinline__ void packed_finish(const GemmArgs& g, const Tile& tile, int q, int tid,
+                                           int lane, int col0) {
+  using SP = PackedSplit<MS>;
+  f32x4_t x[kMaxSplitParts][2][4];
+#pragma unroll
+  for (int part = 0; part < kMaxSplitParts; ++part) {
+    if (part < tile.nparts) {
+      const f32x4_t* sp = SP::slot(g.split_buf, q * tile.nparts + part);
+#pragma unroll
+      for (int tn = 0; tn < 2; ++tn)
+#pragma unroll
+        for (int v = 0; v < 4; ++v) x[part][tn][v] = sp[SP::chunk(tn, TM, v) * MS::NT + tid];
+    }
+  }
+  f32x16_t acc[2][MS::TMAX];
+#pragma unroll
+  for (int tn = 0; tn < 2; ++tn)
+#pragma unroll
+    for (int v = 0; v < 4; ++v)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) acc[tn][TM][4 * v + r] = x[0][tn][v][r];
+#pragma unroll
+  for (int part = 1; part < kMaxSplitParts; ++part) {
+    if (part < tile.nparts) {
+#pragma unroll
+      for (int tn = 0; tn < 2; ++tn)
+#pragma unroll
+        for (int v = 0; v < 4; ++v)
+#pragma unroll
+          for (int r = 0; r < 4; ++r) acc[tn][TM][4 * v + r] += x[part][tn][v][r];
+    }
+  }
+  // (TA = TMAX only sizes the epilogue's per-row arrays; the row block is TM)
+  packed_epilogue<EPI, 2, MS::TMAX, MS::TMAX, 0, (EPI == EPI_SWIGLU ? 1 : 2), TM, TM + 1>(
+      g, tile, lane, col0, acc);
+}
+
+template <class MS, int EPI>
+__global__ __launch_bounds__(kWave) void gemm_packed_finish_kernel(GemmArgs g) {
+  const int q = blockIdx.x / (MS::NW * MS::TMAX);
+  const int wave = (blockIdx.x / MS::TMAX) % MS::NW, tm = blockIdx.x % MS::TMAX;
+  // (the product launch it finishes did nothing: its split descriptors are stale)
+  if (g.small_tiles && *g.small_tiles != MS::GATE) return;
+  if (q >= g.split_desc[0]) return;
+  const int32_t* d = g.split_desc + 1 + 5 * q;
+  Tile tile;
+  tile.seg = d[0];
+  tile.row0 = d[1];
+  tile.m_valid = d[2];
+  tile.nt = d[3];
+  tile.nparts = __builtin_amdgcn_readfirstlane(d[4]);
+  tile.part = 0;
+  tile.split_q = q;
+  tile.k_stage0 = 0;
+  tile.k_stages = 0;
+  if (tm * 32 >= tile.m_valid) return;  // this row block holds no rows of the tile
+  const int lane = threadIdx.x;
+  const int tid = wave * kWave + lane;  // the thread of the tile's workgroup this lane stands for
+  const int p = tile.nt * (MS::NW / 2) + (wave >> 1), h = wave & 1;
+  const int col0 = panel_col0<EPI>(p) + h * (EPI == EPI_SWIGLU ? 32 : 64);
+  if (tm == 0) packed_finish<MS, EPI, 0>(g, tile, q, tid, lane, col0);
+  if constexpr (MS::TMAX > 1) if (tm == 1) packed_finish<MS, EPI, 1>(g, tile, q, tid, lane, col0);
+  if constexpr (MS::TMAX > 2) if (tm == 2) packed_finish<MS, EPI, 2>(g, tile, q, tid, lane, col0);
+  if constexpr (MS::TMAX > 3) if (tm == 3) packed_finish<MS, EPI, 3>(g, tile, q, tid, lane, col0);
 }
 
 // ------------------------------------------------------------------ float32 SIMT kernel
@@ -1773,27 +1596,9 @@ int64_t grid_for(int64_t max_rows, int n_seg_eff, int bm, int n_ntiles) {
 }
 
 template <int EPI>
-hipError_t launch_packed(hipStream_t st, GemmArgs g, int64_t max_rows) {
-  const int n_seg_eff = g.seg_off ? g.n_seg : 1;
-  int64_t grid = grid_for(max_rows, n_seg_eff, kPBM, g.bp_rows / kPBN);
-  if (grid <= 0) return hipSuccess;
-  // a partial last round is split along K as in the staged kernel (same rule, same
-  // buffers: a 128 x 512 tile holds as many floats as a 256 x 256 one)
-  if (!g.split_buf || !g.split_desc || grid > 5 * static_cast<int64_t>(g.split_g)) g.split_g = 0;
-  grid += g.split_g;
-  hipLaunchKernelGGL((gemm_packed_kernel<EPI>), dim3(static_cast<unsigned>(grid)), dim3(kThreads),
-                     0, st, g);
-  hipError_t err = hipGetLastError();
-  if (err != hipSuccess || g.split_g == 0) return err;
-  hipLaunchKernelGGL((gemm_packed_finish_kernel<EPI>), dim3(static_cast<unsigned>(g.split_g / 2 * 32)),
-                     dim3(kWave), 0, st, g);
-  return hipGetLastError();
-}
-
-template <int EPI>
 hipError_t launch_packed_small(hipStream_t st, const GemmArgs& g, int64_t max_rows) {
   const int n_seg_eff = g.seg_off ? g.n_seg : 1;
-  const int64_t grid = grid_for(max_rows, n_seg_eff, 32, g.bp_rows / kPBN);
+  const int64_t grid = grid_for(max_rows, n_seg_eff, 32, g.bp_rows / kSBN);
   if (grid <= 0) return hipSuccess;
   hipLaunchKernelGGL((gemm_packed_small_kernel<EPI>), dim3(static_cast<unsigned>(grid)),
                      dim3(kThreads), 0, st, g);
@@ -1830,23 +1635,35 @@ hipError_t launch_bf16_bm(hipStream_t st, GemmArgs g, int64_t max_rows, bool ksp
   return hipGetLastError();
 }
 
-template <int EPI>
-hipError_t launch_packed_mid(hipStream_t st, GemmArgs g, int64_t max_rows) {
-  using MS = MidLarge;
+// The packed-weight kernel: PackedMid for mid-size segments (no split), PackedLong for
+// long ones (a partial last round split along K where g.split_g is set, as in the
+// staged kernel; the finishing launch sums the parts).
+template <int EPI, class MS = PackedMid>
+hipError_t launch_packed(hipStream_t st, GemmArgs g, int64_t max_rows) {
   const int n_seg_eff = g.seg_off ? g.n_seg : 1;
-  const int64_t grid = grid_for(max_rows, n_seg_eff, MS::BM, g.bp_rows / kMBN);
+  int64_t grid = grid_for(max_rows, n_seg_eff, MS::BM, g.bp_rows / MS::BN);
   if (grid <= 0) return hipSuccess;
-  g.split_g = 0;
-  hipLaunchKernelGGL((gemm_packed_mid_kernel<MS, EPI>), dim3(static_cast<unsigned>(grid)),
-                     dim3(kThreads), 0, st, g);
-  return hipGetLastError();
+  if (!MS::SPLIT || !g.split_buf || !g.split_desc || grid > 5 * static_cast<int64_t>(g.split_g))
+    g.split_g = 0;
+  grid += g.split_g;  // a split last round has at most split_g work items more
+  hipLaunchKernelGGL((gemm_packed_kernel<MS, EPI>), dim3(static_cast<unsigned>(grid)),
+                     dim3(MS::NT), 0, st, g);
+  hipError_t err = hipGetLastError();
+  if constexpr (MS::SPLIT) {
+    if (err != hipSuccess || g.split_g == 0) return err;
+    hipLaunchKernelGGL((gemm_packed_finish_kernel<MS, EPI>),
+                       dim3(static_cast<unsigned>(g.split_g / 2 * MS::NW * MS::TMAX)),
+                       dim3(kWave), 0, st, g);
+    err = hipGetLastError();
+  }
+  return err;
 }
 
 // With packed weights every product reads the packed copy: segments the host knows to
 // be short (under kBigSegRows rows per segment by its bound) take the 32-row kernel,
 // mid-size ones (under kPackedRows) the 256 x 256 weight-streaming kernel, long ones
 // the 128 x 512 kernel.  Where the host's bound picks the long tiles but the dispatch
-// may keep far fewer rows (g.small_tiles set), the mid-size kernel is launched beside
+// may keep far fewer rows (g.small_tiles set), the mid-size shape is launched beside
 // them and the dispatch's choice runs.
 template <int EPI>
 hipError_t launch_packed_epi(hipStream_t st, const GemmArgs& g, int64_t max_rows, int64_t avg) {
@@ -1854,8 +1671,8 @@ hipError_t launch_packed_epi(hipStream_t st, const GemmArgs& g, int64_t max_rows
   q.small_tiles = nullptr;
   q.split_g = 0;
   if (avg < kBigSegRows) return launch_packed_small<EPI>(st, q, max_rows);
-  if (avg < kPackedRows) return launch_packed_mid<EPI>(st, q, max_rows);
-  const hipError_t err = launch_packed<EPI>(st, g, max_rows);
+  if (avg < kPackedRows) return launch_packed<EPI>(st, q, max_rows);
+  const hipError_t err = launch_packed<EPI, PackedLong>(st, g, max_rows);
   if (err != hipSuccess || !g.small_tiles) return err;
   const int n_seg_eff = g.seg_off ? g.n_seg : 1;
   // selected, the kept rows average under kBigSegRows per non-empty segment
@@ -1863,7 +1680,8 @@ hipError_t launch_packed_epi(hipStream_t st, const GemmArgs& g, int64_t max_rows
       std::min<int64_t>(max_rows, static_cast<int64_t>(kBigSegRows) * n_seg_eff);
   GemmArgs gated = g;
   gated.split_g = 0;
-  return launch_packed_mid<EPI>(st, gated, small_rows);
+  gated.split_desc = nullptr;
+  return launch_packed<EPI>(st, gated, small_rows);
 }
 
 template <int EPI>

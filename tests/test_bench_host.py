@@ -1,7 +1,7 @@
 """bench.py's host-side choices (no GPU): which expert kernels a workload's launches run,
 and where the benchmark packs the expert weights, following the library's rules (with
 packed weights, by the library's bound on the kept rows per expert: >= 256 the 128 x 512
-kernel, 48 .. 255 the mid-size kernel, < 48 the 32-row kernel; staged weights: >= 48 the
+shape, 48 .. 255 the 256 x 256 shape, < 48 the 32-row kernel; staged weights: >= 48 the
 256-row tiles, < 48 the 32-row tiles; float32 the SIMT kernel)."""
 import bench
 from sparse_mixture_experts_forward_amd import CONFIGS
@@ -15,10 +15,10 @@ def _cap(c):
 
 def test_stage_kernels_of_the_workloads():
     want = {  # workload: (packed?, gemm1 kernel, gemm2 kernel) with packing allowed
-        "mixtral": (True, "gemm_packed_kernel<2>", "gemm_packed_kernel<0>"),
+        "mixtral": (True, "gemm_packed_kernel<PackedShape<128, 8, 8, 0>, 2>", "gemm_packed_kernel<PackedShape<128, 8, 8, 0>, 0>"),
         "decode": (True, "gemm_packed_small_kernel<2>", "gemm_packed_small_kernel<0>"),
-        "deepseek": (True, "gemm_packed_mid_kernel<MidShape<256, 16>, 2>", "gemm_packed_mid_kernel<MidShape<256, 16>, 0>"),
-        "switch": (True, "gemm_packed_mid_kernel<MidShape<256, 16>, 1>", "gemm_packed_mid_kernel<MidShape<256, 16>, 0>"),
+        "deepseek": (True, "gemm_packed_kernel<PackedShape<256, 16, 4, 1>, 2>", "gemm_packed_kernel<PackedShape<256, 16, 4, 1>, 0>"),
+        "switch": (True, "gemm_packed_kernel<PackedShape<256, 16, 4, 1>, 1>", "gemm_packed_kernel<PackedShape<256, 16, 4, 1>, 0>"),
         "tiny": (False, "gemm_f32_kernel<1, false>", "gemm_f32_kernel<0, false>"),
     }
     for name, (packed, k1, k2) in want.items():
@@ -35,9 +35,9 @@ def test_stage_kernels_of_the_workloads():
 def test_kernel_rules_at_the_thresholds():
     m = CONFIGS["mixtral"]
     # 256 rows per expert (N k / E): 128 x 512 kernel; 255: mid-size; 47: 32-row
-    for n, k1, staged in ((1024, "gemm_packed_kernel<2>", "gemm_bf16_kernel<256, 2, false>"),
-                          (1020, "gemm_packed_mid_kernel<MidShape<256, 16>, 2>", "gemm_bf16_kernel<256, 2, false>"),
-                          (192, "gemm_packed_mid_kernel<MidShape<256, 16>, 2>", "gemm_bf16_kernel<256, 2, false>"),
+    for n, k1, staged in ((1024, "gemm_packed_kernel<PackedShape<128, 8, 8, 0>, 2>", "gemm_bf16_kernel<256, 2, false>"),
+                          (1020, "gemm_packed_kernel<PackedShape<256, 16, 4, 1>, 2>", "gemm_bf16_kernel<256, 2, false>"),
+                          (192, "gemm_packed_kernel<PackedShape<256, 16, 4, 1>, 2>", "gemm_bf16_kernel<256, 2, false>"),
                           (188, "gemm_packed_small_kernel<2>", "gemm_bf16_kernel<32, 2, false>")):
         c = m.with_tokens(n)
         assert bench.packed_path(c, -1, True), n
