@@ -440,6 +440,29 @@ def expert_ffn(a64: np.ndarray, w: ExpertWeights, act: str) -> np.ndarray:
 
 
 # ----------------------------------------------------------------------------------
+# Combine.  [Why-MoE] §2.1: a token's output is the sum over its selected experts of
+# the gate weight times that expert's output; [DeepSeek-V2] §2.3 adds the shared
+# experts' output, unweighted.  Here the expert outputs are given as rows of the
+# permuted buffer (slot_row maps slot (t, j) to its row, -1 for a dropped slot, which
+# contributes nothing).
+# ----------------------------------------------------------------------------------
+def combine(y_rows64: np.ndarray, slot_row: np.ndarray, w64: Optional[np.ndarray],
+            shared64: Optional[np.ndarray] = None) -> np.ndarray:
+    """out[t] = shared[t] + sum over kept slots j of w[t, j] * y_rows[slot_row[t, j]];
+    w None: weights of one (the rows already carry their weights)."""
+    n, k = slot_row.shape
+    out = np.zeros((n, y_rows64.shape[1]), dtype=F64)
+    if shared64 is not None:
+        out += shared64
+    for t in range(n):
+        for j in range(k):
+            r = int(slot_row[t, j])
+            if r >= 0:
+                out[t] += (1.0 if w64 is None else float(w64[t, j])) * y_rows64[r]
+    return out
+
+
+# ----------------------------------------------------------------------------------
 # Whole layer.  [Why-MoE] §2.1: y = sum over the k selected experts of g_i(x) E_i(x);
 # the MoELayer listing accumulates each expert's weighted output back into the token's
 # row.  [DeepSeek-V2] §2.3: shared experts see every token, unweighted, and their sum

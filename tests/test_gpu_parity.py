@@ -576,11 +576,8 @@ def test_combine_parity(dtype, shared, k, d, weights):
                   torch.from_numpy(w).to(DEV) if weights else None,
                   None if sy is None else _up(sy, dtype), out)
     torch.cuda.synchronize()
-    yr64 = O.widen(yr, dtype)
-    ref = np.zeros((n, d)) if sy is None else O.widen(sy, dtype).copy()
-    for j in range(k):
-        m = slot[:, j] >= 0
-        ref[m] += w[m, j, None].astype(np.float64) * yr64[slot[m, j]]
+    ref = O.combine(O.widen(yr, dtype), slot, w.astype(np.float64) if weights else None,
+                    None if sy is None else O.widen(sy, dtype))
     got = widen_t(out)
     if not shared:
         assert (got[:5] == 0).all()

@@ -336,6 +336,40 @@ def test_layer_matches_dense_bruteforce(act, cap, n_shared, renorm):
     assert np.allclose(r.y, y, rtol=1e-12, atol=1e-14)
 
 
+@pytest.mark.parametrize("cap,n_shared", [(None, 0), (2, 1), (1, 0)])
+def test_combine_of_expert_rows_is_the_dense_layer(cap, n_shared):
+    """The per-token combine over the permuted expert-output rows (each row the expert's
+    FFN of its token, computed here with loops) equals the dense brute-force layer."""
+    rng = _rng(21)
+    N, d, d_ff, E, k = 13, 4, 6, 4, 2
+    act = "swiglu"
+    x = rng.standard_normal((N, d)).astype(np.float32)
+    logits = rng.standard_normal((N, E)).astype(np.float32)
+    ws = _tiny_experts(rng, E, d, d_ff, act)
+    sh = _tiny_experts(rng, n_shared, d, d_ff, act)
+    y_ref, idx, keep = _bruteforce_layer(x, logits, None, k, ws, sh, act, cap, True)
+    alpha = None if cap is None else cap / ((k * N) // E)
+    r = O.forward(x, "f32", None, k, lambda e: ws[e], E, act, alpha=alpha,
+                  shared=lambda s: sh[s], n_shared=n_shared, logits=logits)
+    plan = r.plan
+    assert np.array_equal(plan.keep, keep)
+    rows = np.array([_loop_ffn(x[int(t)].astype(np.float64), ws[int(idx[t, j])], act)
+                     for t, j in zip(plan.row_token, plan.row_slot)]).reshape(-1, d)
+    shared = None
+    if n_shared:
+        shared = np.array([np.sum([_loop_ffn(x[t].astype(np.float64), s, act) for s in sh],
+                                  axis=0) for t in range(N)])
+    got = O.combine(rows, plan.slot_row, r.topk_w, shared)
+    assert np.allclose(got, y_ref, rtol=1e-12, atol=1e-14)
+    # unweighted rows: the weights folded into the rows beforehand give the same sum
+    wrows = rows * r.topk_w[plan.row_token, plan.row_slot][:, None]
+    assert np.allclose(O.combine(wrows, plan.slot_row, None, shared), y_ref, rtol=1e-12,
+                       atol=1e-14)
+    dropped = ~plan.keep.any(axis=1)
+    if n_shared == 0 and dropped.any():
+        assert (got[dropped] == 0).all()
+
+
 def test_fully_dropped_token_is_zero():
     rng = _rng(9)
     N, d, d_ff, E = 8, 3, 4, 2
