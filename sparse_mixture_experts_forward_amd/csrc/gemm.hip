@@ -59,6 +59,9 @@ constexpr int kBRows = 256;   // bf16: weight rows per workgroup
 constexpr int kGroupN = 8;  // column tiles per scheduling group
 constexpr int kXcds = 8;
 constexpr int kMaxSplitParts = 4;  // K parts of a split tile
+// Cache policy of a buffer load streaming data read once (the "nt" bit): measured on
+// a plain 4 GiB read, 6.3 TB/s with default loads against 7.1 TB/s with these.
+constexpr int kCpolNT = 2;
 
 struct Tile {
   int seg;
@@ -71,6 +74,21 @@ struct Tile {
   int k_stage0, k_stages;
   int part, nparts, split_q;
 };
+
+// The work item is uniform over the workgroup: keep its fields in scalar registers
+// (computed through LDS, the compiler cannot tell, and would hold them in vector
+// registers, which the packed kernels' accumulators leave none of).
+__device__ __forceinline__ void make_uniform(Tile& t) {
+  t.seg = __builtin_amdgcn_readfirstlane(t.seg);
+  t.nt = __builtin_amdgcn_readfirstlane(t.nt);
+  t.m_valid = __builtin_amdgcn_readfirstlane(t.m_valid);
+  t.row0 = static_cast<int64_t>(__builtin_amdgcn_readfirstlane(static_cast<int32_t>(t.row0)));
+  t.k_stage0 = __builtin_amdgcn_readfirstlane(t.k_stage0);
+  t.k_stages = __builtin_amdgcn_readfirstlane(t.k_stages);
+  t.part = __builtin_amdgcn_readfirstlane(t.part);
+  t.nparts = __builtin_amdgcn_readfirstlane(t.nparts);
+  t.split_q = __builtin_amdgcn_readfirstlane(t.split_q);
+}
 
 // Block-wide: find this workgroup's tile.  Returns false (uniformly) if it has none.
 constexpr int kMaxWaves = 16;  // waves per workgroup the scheduler serves
@@ -101,7 +119,7 @@ __device__ __forceinline__ void seg_bounds(const int32_t* __restrict__ seg_off, 
 // (With more rounds the tail is a small share of the time, and the parts' extra
 // prologues, partial stores and the finishing launch cost more than they save.)
 template <int BM, int NT = kThreads>
-__device__ bool schedule_tile(const int32_t* __restrict__ seg_off, int n_seg,
+__device__ __forceinline__ bool schedule_tile(const int32_t* __restrict__ seg_off, int n_seg,
                               int single_rows, int max_rows, int n_ntiles, int KT, int split_g,
                               int32_t* split_desc, SchedSmem& sm, Tile& tile) {
   static_assert(NT / kWave <= kMaxWaves && 2 * NT >= kMaxExperts, "scheduler workgroup size");
@@ -217,8 +235,8 @@ __device__ __forceinline__ int lds_swizzle(int r) { return ((r >> 1) ^ ((r & 1) 
 
 __device__ __forceinline__ uint2 pack_bf16x4(float a, float b, float c, float d) {
   uint2 r;
-  r.x = static_cast<uint32_t>(f32_to_bf16(a)) | (static_cast<uint32_t>(f32_to_bf16(b)) << 16);
-  r.y = static_cast<uint32_t>(f32_to_bf16(c)) | (static_cast<uint32_t>(f32_to_bf16(d)) << 16);
+  r.x = f32x2_to_bf16x2(a, b);
+  r.y = f32x2_to_bf16x2(c, d);
   return r;
 }
 
@@ -644,7 +662,7 @@ __device__ __forceinline__ void tile_epilogue(const GemmArgs& g, const Tile& til
 #pragma unroll
             for (int r = 0; r < 4; ++r) {
               v[r] = acc[tn][tm][4 * q + r] + bv[r];
-              if (EPI == EPI_GELU) v[r] = gelu_erf(v[r]);
+              if (EPI == EPI_GELU) v[r] = gelu_bf16(v[r]);
               v[r] *= sc[tm];  // exact when 1
             }
             *reinterpret_cast<uint2*>(C + orow(m) * g.ldc + col) =
@@ -898,24 +916,86 @@ __global__ __launch_bounds__(kWave) void gemm_split_finish_kernel(GemmArgs g) {
 // fragment reads the largest in-core cost.
 constexpr int kPStages = 4;    // activation LDS stages
 
+// Output row and row weight of each row of a packed kernel's tile, read before the
+// tile's main loop and kept in LDS (EpiRowsLds) or, where a lane only ever stores its
+// own row, in two registers (EpiRowReg).  The epilogue then issues its stores with no
+// load between them: a wait for a load also waits for every store issued before it,
+// and under a saturated memory system each such wait is a full round trip of several
+// microseconds.  With g.c_rows the output row of tile row m is c_rows[row0 + m] (rows
+// written straight into their token's row), else row0 + m; the weight is
+// g.row_scale[row0 + m], or 1.
+struct EpiRowLoad {
+  int32_t row;
+  float scale;
+  __device__ __forceinline__ void load(const GemmArgs& g, const Tile& tile, int m) {
+    row = -1;
+    scale = 1.f;
+    if (m < tile.m_valid) {
+      const int64_t r = tile.row0 + m;
+      row = g.c_rows ? g.c_rows[r] : static_cast<int32_t>(r);
+      if (g.row_scale) scale = g.row_scale[r];
+    }
+  }
+};
+
+template <int BM>
+struct EpiRowsLds {
+  static_assert(BM % kWave == 0, "one wave per 64 rows");
+  int32_t row[BM];
+  float scale[BM];
+  // Wave w < BM / 64 fills rows m = 64 w + lane: direct-to-LDS loads of c_rows[row0 + m]
+  // and row_scale[row0 + m] (lane l of the load writes the LDS word at the wave's base +
+  // 4 l; no registers held, nothing waited for here; rows past m_valid read 0 through
+  // the buffer's bound), or the identity row and weight 1.  Issued before the operands'
+  // loads, so they have landed wherever those have.
+  __device__ __forceinline__ void stage(const GemmArgs& g, const Tile& tile, int wave, int lane) {
+    if (wave >= BM / kWave) return;
+    const int m = wave * kWave + lane;
+    const int nbytes = tile.m_valid * 4;
+#if defined(__HIP_DEVICE_COMPILE__)
+    if (g.c_rows) {
+      const __amdgpu_buffer_rsrc_t r = __builtin_amdgcn_make_buffer_rsrc(
+          const_cast<int32_t*>(g.c_rows + tile.row0), static_cast<short>(0), nbytes, 0x00020000);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void_t*)(row + wave * kWave), 4,
+                                               static_cast<uint32_t>(m) * 4u, 0, 0, 0);
+    } else {
+      row[m] = static_cast<int32_t>(tile.row0) + m;
+    }
+    if (g.row_scale) {
+      const __amdgpu_buffer_rsrc_t r = __builtin_amdgcn_make_buffer_rsrc(
+          const_cast<float*>(g.row_scale + tile.row0), static_cast<short>(0), nbytes, 0x00020000);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void_t*)(scale + wave * kWave), 4,
+                                               static_cast<uint32_t>(m) * 4u, 0, 0, 0);
+    } else {
+      scale[m] = 1.f;
+    }
+#endif
+  }
+  __device__ __forceinline__ int64_t out(int m) const { return row[m]; }
+  __device__ __forceinline__ float weight(int m) const { return scale[m]; }
+};
+
+struct EpiRowReg {  // only row m of the lane (the caller's row block)
+  EpiRowLoad v;
+  __device__ __forceinline__ int64_t out(int) const { return v.row; }
+  __device__ __forceinline__ float weight(int) const { return v.scale; }
+};
+
 // Epilogue of the packed-weight kernels: register 4q + r of acc[tn][tm] is activation
 // row tm*32 + lane%32 of the tile and output column col0 + tn*32 + 8q + 4(lane/32) + r
 // (SwiGLU: tn < NTW/2 are W1 tiles, each paired with the W3 tile tn + NTW/2 of the
 // same columns); the four r are consecutive output columns (one 8-byte store).
 // TN0 .. TN1-1 restrict the epilogue to those tiles (SwiGLU: W1 tiles), TM0 .. TM1-1 to
-// those row blocks; default all.  With g.c_rows the output row of tile row m is
-// c_rows[row0 + m] (rows written straight into their token's row), else row0 + m.
+// those row blocks; default all.  rows gives each row's output row and weight (the
+// accessors above).
 template <int EPI, int NTW, int TMAX, int TA, int TN0 = 0,
-          int TN1 = (EPI == EPI_SWIGLU ? NTW / 2 : NTW), int TM0 = 0, int TM1 = TA>
+          int TN1 = (EPI == EPI_SWIGLU ? NTW / 2 : NTW), int TM0 = 0, int TM1 = TA, class Rows>
 __device__ __forceinline__ void packed_epilogue(const GemmArgs& g, const Tile& tile, int lane,
-                                                int col0, f32x16_t (&acc)[NTW][TMAX]) {
+                                                int col0, f32x16_t (&acc)[NTW][TMAX],
+                                                const Rows& rows) {
   uint16_t* __restrict__ C = static_cast<uint16_t*>(g.c);
   const int frow = lane & 31;
-  // (the output row is looked up at each store: kept live across the epilogue, the
-  // rows would add to the register pressure of the accumulators)
-  auto orow = [&](int m) -> int64_t {
-    return g.c_rows ? static_cast<int64_t>(g.c_rows[tile.row0 + m]) : tile.row0 + m;
-  };
+  auto orow = [&](int m) -> int64_t { return rows.out(m); };
   if constexpr (EPI == EPI_SWIGLU) {
 #pragma unroll
     for (int tn = TN0; tn < TN1; ++tn)
@@ -937,13 +1017,12 @@ __device__ __forceinline__ void packed_epilogue(const GemmArgs& g, const Tile& t
         }
       }
   } else {
+    // (a bias, where given, is read per column group, between stores: no workload that
+    // runs these kernels has one, and held for the whole tile it would cost registers)
     const uint16_t* bias = static_cast<const uint16_t*>(g.bias);
     float sc[TA];
 #pragma unroll
-    for (int tm = TM0; tm < TM1; ++tm) {
-      const int m = tm * 32 + frow;
-      sc[tm] = (g.row_scale && m < tile.m_valid) ? g.row_scale[tile.row0 + m] : 1.f;
-    }
+    for (int tm = TM0; tm < TM1; ++tm) sc[tm] = rows.weight(tm * 32 + frow);
 #pragma unroll
     for (int tn = TN0; tn < TN1; ++tn)
 #pragma unroll
@@ -963,7 +1042,7 @@ __device__ __forceinline__ void packed_epilogue(const GemmArgs& g, const Tile& t
 #pragma unroll
             for (int r = 0; r < 4; ++r) {
               v[r] = acc[tn][tm][4 * q + r] + bv[r];
-              if (EPI == EPI_GELU) v[r] = gelu_erf(v[r]);
+              if (EPI == EPI_GELU) v[r] = gelu_bf16(v[r]);
               v[r] *= sc[tm];  // exact when 1
             }
             *reinterpret_cast<uint2*>(C + orow(m) * g.ldc + col) =
@@ -1045,8 +1124,8 @@ struct PackedSmallIO {
         const_cast<char*>(w_base), static_cast<short>(0), -1, 0x00020000);
 #pragma unroll
     for (int tn = 0; tn < 4; ++tn)
-      w[tn] = __builtin_bit_cast(bf16x8_t,
-                                 __builtin_amdgcn_raw_buffer_load_b128(rw, w_off[tn], t * 1024, 0));
+      w[tn] = __builtin_bit_cast(
+          bf16x8_t, __builtin_amdgcn_raw_buffer_load_b128(rw, w_off[tn], t * 1024, kCpolNT));
     const __amdgpu_buffer_rsrc_t ra = __builtin_amdgcn_make_buffer_rsrc(
         const_cast<char*>(a_base), static_cast<short>(0), -1, 0x00020000);
     a = __builtin_bit_cast(bf16x8_t, __builtin_amdgcn_raw_buffer_load_b128(ra, a_off, t * 32, 0));
@@ -1094,9 +1173,12 @@ __global__ __launch_bounds__(kThreads, 2) void gemm_packed_small_kernel(GemmArgs
   if (!schedule_tile<32>(g.seg_off, g.n_seg, g.single_rows, g.max_rows, g.bp_rows / kSBN,
                          g.k / kBK, 0, nullptr, sched, tile))
     return;
+  make_uniform(tile);
   const int tid = threadIdx.x;
   const int lane = tid & (kWave - 1);
   const int wave = __builtin_amdgcn_readfirstlane(tid / kWave);
+  EpiRowReg rows;  // the lane's one output row, read before the loop
+  rows.v.load(g, tile, lane & 31);
   PackedSmallIO io;
   io.KS = g.k / 16;
   const int32_t* __restrict__ a_rows = g.a_rows;
@@ -1128,7 +1210,7 @@ __global__ __launch_bounds__(kThreads, 2) void gemm_packed_small_kernel(GemmArgs
   for (; t0 + kSRing <= io.KS; t0 += kSRing) ps_period<0>(io, t0, wr, ar, acc);
   ps_tail<0>(io, t0, io.KS - t0, wr, ar, acc);
   __builtin_amdgcn_s_waitcnt(0);
-  packed_epilogue<EPI, 4, 4, 1>(g, tile, lane, panel_col0<EPI>(p), acc);
+  packed_epilogue<EPI, 4, 4, 1>(g, tile, lane, panel_col0<EPI>(p), acc, rows);
 }
 
 // ------------------------------------------------------------------ packed-weight kernel (long and mid-size segments)
@@ -1166,6 +1248,9 @@ struct PackedShape {
   static constexpr int BN = NW * 64;
   // activation loads (8-row groups) per wave and stage: group g goes to wave g % NW
   static constexpr int JMAX = (4 * TMAX + NW - 1) / NW;
+  // weight loads: non-temporal where every weight panel is read by one tile only (the
+  // mid-size shape takes whole segments), cached where row tiles of a segment share it
+  static constexpr int W_CPOL = GATE_ ? kCpolNT : 0;
   template <int TA>
   static constexpr int na_min() { return 4 * TA / NW; }  // fewest any wave issues
   template <int TA>
@@ -1205,8 +1290,8 @@ struct PackedIO {
         const_cast<char*>(w_base), static_cast<short>(0), -1, 0x00020000);
 #pragma unroll
     for (int tn = 0; tn < 2; ++tn)
-      w[tn] = __builtin_bit_cast(bf16x8_t,
-                                 __builtin_amdgcn_raw_buffer_load_b128(r, w_off[tn], t * 1024, 0));
+      w[tn] = __builtin_bit_cast(
+          bf16x8_t, __builtin_amdgcn_raw_buffer_load_b128(r, w_off[tn], t * 1024, MS::W_CPOL));
 #endif
   }
   template <int TA>
@@ -1316,7 +1401,8 @@ __device__ __forceinline__ void packed_split_store(const GemmArgs& g, const Tile
 
 template <class MS, int EPI, int TA>
 __device__ __forceinline__ void packed_body(const GemmArgs& g, const Tile& tile, const PackedIO<MS>& io,
-                                         uint16_t* const (&A)[kPStages], int lane, int col0) {
+                                         uint16_t* const (&A)[kPStages], int lane, int col0,
+                                         const EpiRowsLds<MS::BM>& rows) {
   static_assert(16 % MS::RING == 0, "the ring period divides the 16-k-step period");
   f32x16_t acc[2][MS::TMAX];
 #pragma unroll
@@ -1348,7 +1434,8 @@ __device__ __forceinline__ void packed_body(const GemmArgs& g, const Tile& tile,
       return;
     }
   }
-  packed_epilogue<EPI, 2, MS::TMAX, TA>(g, tile, lane, col0, acc);
+  __syncthreads();  // the tile's output rows are in LDS
+  packed_epilogue<EPI, 2, MS::TMAX, TA>(g, tile, lane, col0, acc, rows);
 }
 
 template <class MS, int EPI>
@@ -1356,6 +1443,7 @@ __global__ __launch_bounds__(MS::NT, 1) void gemm_packed_kernel(GemmArgs g) {
   __shared__ __attribute__((aligned(16))) uint16_t A0[MS::BM * kBK], A1[MS::BM * kBK];
   __shared__ __attribute__((aligned(16))) uint16_t A2[MS::BM * kBK], A3[MS::BM * kBK];
   __shared__ SchedSmem sched;
+  __shared__ EpiRowsLds<MS::BM> rows;
   uint16_t* const A[kPStages] = {A0, A1, A2, A3};
   // with a device-chosen tile height the launch runs only where the dispatch chose it
   if (g.small_tiles && *g.small_tiles != MS::GATE) return;
@@ -1364,13 +1452,12 @@ __global__ __launch_bounds__(MS::NT, 1) void gemm_packed_kernel(GemmArgs g) {
                                      g.bp_rows / MS::BN, g.k / kBK, MS::SPLIT ? g.split_g : 0,
                                      MS::SPLIT ? g.split_desc : nullptr, sched, tile))
     return;
-  // the work item is uniform over the workgroup: keep its fields in scalar registers
-  tile.k_stage0 = __builtin_amdgcn_readfirstlane(tile.k_stage0);
-  tile.k_stages = __builtin_amdgcn_readfirstlane(tile.k_stages);
-  tile.nparts = __builtin_amdgcn_readfirstlane(tile.nparts);
+  make_uniform(tile);
   const int tid = threadIdx.x;
+
   const int lane = tid & (kWave - 1);
   const int wave = __builtin_amdgcn_readfirstlane(tid / kWave);  // 0 .. NW - 1
+  rows.stage(g, tile, wave, lane);
   PackedIO<MS> io;
   io.wave = wave;
   io.KT = tile.k_stages;  // a part of a split tile covers stages k_stage0 .. + k_stages
@@ -1407,19 +1494,19 @@ __global__ __launch_bounds__(MS::NT, 1) void gemm_packed_kernel(GemmArgs g) {
   io.a_row = frow * kBK;
   const int ta = __builtin_amdgcn_readfirstlane(min((tile.m_valid + 31) / 32, MS::TMAX));
   switch (ta) {
-    case 1: packed_body<MS, EPI, 1>(g, tile, io, A, lane, col0); break;
-    case 2: packed_body<MS, EPI, 2>(g, tile, io, A, lane, col0); break;
-    case 3: packed_body<MS, EPI, 3>(g, tile, io, A, lane, col0); break;
+    case 1: packed_body<MS, EPI, 1>(g, tile, io, A, lane, col0, rows); break;
+    case 2: packed_body<MS, EPI, 2>(g, tile, io, A, lane, col0, rows); break;
+    case 3: packed_body<MS, EPI, 3>(g, tile, io, A, lane, col0, rows); break;
     default:
       if constexpr (MS::TMAX == 4) {
-        packed_body<MS, EPI, 4>(g, tile, io, A, lane, col0);
+        packed_body<MS, EPI, 4>(g, tile, io, A, lane, col0, rows);
       } else {
         switch (ta) {
-          case 4: packed_body<MS, EPI, 4>(g, tile, io, A, lane, col0); break;
-          case 5: packed_body<MS, EPI, 5>(g, tile, io, A, lane, col0); break;
-          case 6: packed_body<MS, EPI, 6>(g, tile, io, A, lane, col0); break;
-          case 7: packed_body<MS, EPI, 7>(g, tile, io, A, lane, col0); break;
-          default: packed_body<MS, EPI, MS::TMAX>(g, tile, io, A, lane, col0); break;
+          case 4: packed_body<MS, EPI, 4>(g, tile, io, A, lane, col0, rows); break;
+          case 5: packed_body<MS, EPI, 5>(g, tile, io, A, lane, col0, rows); break;
+          case 6: packed_body<MS, EPI, 6>(g, tile, io, A, lane, col0, rows); break;
+          case 7: packed_body<MS, EPI, 7>(g, tile, io, A, lane, col0, rows); break;
+          default: packed_body<MS, EPI, MS::TMAX>(g, tile, io, A, lane, col0, rows); break;
         }
       }
       break;
@@ -1434,6 +1521,8 @@ template <class MS, int EPI, int TM>
 __device__ __forceinline__ void packed_finish(const GemmArgs& g, const Tile& tile, int q, int tid,
                                            int lane, int col0) {
   using SP = PackedSplit<MS>;
+  EpiRowReg rows;  // the lane's row of block TM
+  rows.v.load(g, tile, TM * 32 + (lane & 31));
   f32x4_t x[kMaxSplitParts][2][4];
 #pragma unroll
   for (int part = 0; part < kMaxSplitParts; ++part) {
@@ -1465,7 +1554,7 @@ __device__ __forceinline__ void packed_finish(const GemmArgs& g, const Tile& til
   }
   // (TA = TMAX only sizes the epilogue's per-row arrays; the row block is TM)
   packed_epilogue<EPI, 2, MS::TMAX, MS::TMAX, 0, (EPI == EPI_SWIGLU ? 1 : 2), TM, TM + 1>(
-      g, tile, lane, col0, acc);
+      g, tile, lane, col0, acc, rows);
 }
 
 template <class MS, int EPI>

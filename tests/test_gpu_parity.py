@@ -233,6 +233,10 @@ def test_forward_gather_fusion_is_bit_identical(name):
     ("switch", dict(n_tokens=2048, d_model=768, d_ff=1344, n_experts=4, expert_bias=True)),
     ("tiny", dict(top_k=1)),  # float32
     ("mixtral", dict(top_k=1, n_tokens=2048, d_ff=1024)),  # 128 x 512 packed tiles
+    # weights that are not 1 (no renormalisation over one slot): the rows' weights reach
+    # the second product's epilogue, in tiles of more than 64 rows
+    ("mixtral", dict(top_k=1, n_tokens=2048, d_ff=1024, renormalize=False)),
+    ("switch", dict(alpha=None, n_tokens=8192, renormalize=False)),  # 256-row mid-size tiles
 ])
 @pytest.mark.parametrize("packed", [False, True])
 def test_forward_scatter_fusion_is_bit_identical(case, packed):
@@ -583,6 +587,38 @@ def test_combine_parity(dtype, shared, k, d, weights):
         assert (got[:5] == 0).all()
     rel = 2.0 ** -8 if dtype == "bf16" else 1e-6
     assert np.all(np.abs(got - ref) <= rel * np.abs(ref) + 1e-6 * np.abs(ref).max())
+
+
+def test_bf16_output_rounding_is_nearest_even():
+    """The bf16 outputs round to nearest, ties to even: a two-slot unweighted combine
+    writes bf16(float32(a + b)) (one float32 addition of two bf16 rows), compared bit
+    for bit with that rounding done on the host, on random sums, exact ties in both
+    directions, sums that need no rounding, signed zeros and values near the largest
+    and smallest normal float32."""
+    rng = np.random.default_rng(11)
+    n, d = 64, 256
+    a = rng.standard_normal((n, d)).astype(np.float32)
+    b = (rng.standard_normal((n, d)) * rng.choice([1e-3, 1.0, 1e3], (n, d))).astype(np.float32)
+    a_bits, b_bits = synth.f32_to_bf16_bits(a), synth.f32_to_bf16_bits(b)
+    one, half_ulp = np.uint16(0x3F80), np.float32(2.0 ** -8)  # 1.0; half a bf16 ulp at 1
+    ties = synth.f32_to_bf16_bits(np.float32([half_ulp, -half_ulp, 3 * half_ulp, 0.0, -0.0]))
+    a_bits[0, :5] = one
+    b_bits[0, :5] = ties  # 1 + 2^-8 -> 1, 1 - 2^-8 exact, 1 + 3 2^-8 -> 1 + 2^-6 (even), 1, 1
+    a_bits[1, :4] = synth.f32_to_bf16_bits(np.float32([3.0e38, 1.2e-38, -0.0, 0.0]))
+    b_bits[1, :4] = synth.f32_to_bf16_bits(np.float32([3.0e37, 1.0e-37, -0.0, -0.0]))
+    fa, fb = O.decode_bf16(a_bits), O.decode_bf16(b_bits)
+    with np.errstate(over="ignore"):  # the kernel's sum starts from +0: (0 + a) + b
+        s32 = ((np.float32(0) + fa) + fb).astype(np.float32)
+    finite = np.isfinite(s32)
+    expect = synth.f32_to_bf16_bits(np.where(finite, s32, 0).astype(np.float32))
+    rows = np.concatenate([a_bits, b_bits])  # row t: a_t, row n + t: b_t
+    slot = np.stack([np.arange(n), n + np.arange(n)], axis=1).astype(np.int32)
+    out = torch.empty((n, d), dtype=torch.bfloat16, device=DEV)
+    B.moe_combine(_up(rows, "bf16"), torch.from_numpy(slot).to(DEV), None, None, out)
+    torch.cuda.synchronize()
+    got = out.view(torch.int16).cpu().numpy().view(np.uint16)
+    assert np.array_equal(got[finite], expect[finite])
+    assert got[0, 0] == 0x3F80 and got[0, 2] == 0x3F82  # the two ties went to even
 
 
 # ------------------------------------------------------------------ whole layer
