@@ -41,11 +41,15 @@
 //     round splits along K (gemm_packed_finish_kernel sums the parts);
 //   * mid-size segments (48 .. 255): 256 x 256 tiles of 4 waves, a whole segment of up
 //     to 256 rows per tile, so every (segment, column tile) reads its weights once;
-//   * short segments (< 48): 32 x 512 tiles without LDS, two workgroups per CU.
+//   * short segments (< 48): 32 x 512 tiles without LDS, two workgroups per CU;
+//   * each tile's output rows and row weights reach LDS before its main loop, and the
+//     long and mid-size tiles pass their outputs through the LDS stage buffers, so the
+//     epilogue stores whole 128-byte lines with no load waited for between stores.
 // float32 kernel: a plain LDS-tiled SIMT product (64 x 64 tiles) with the same
 // scheduling and epilogues; it serves the small float32 workload.
 
 #include <algorithm>
+#include <type_traits>
 
 #include "common.h"
 #include "kernels.h"
@@ -59,6 +63,15 @@ constexpr int kBRows = 256;   // bf16: weight rows per workgroup
 constexpr int kGroupN = 8;  // column tiles per scheduling group
 constexpr int kXcds = 8;
 constexpr int kMaxSplitParts = 4;  // K parts of a split tile
+// Calls f(std::integral_constant<int, i>) for i = 0 .. N - 1 (compile-time indices).
+template <int N, int I = 0, class F>
+__device__ __forceinline__ void static_for(F&& f) {
+  if constexpr (I < N) {
+    f(std::integral_constant<int, I>{});
+    static_for<N, I + 1>(f);
+  }
+}
+
 // Cache policy of a buffer load streaming data read once (the "nt" bit): measured on
 // a plain 4 GiB read, 6.3 TB/s with default loads against 7.1 TB/s with these.
 constexpr int kCpolNT = 2;
@@ -1399,6 +1412,124 @@ __device__ __forceinline__ void packed_split_store(const GemmArgs& g, const Tile
   }
 }
 
+// Output tile of a packed-kernel workgroup in LDS (bf16, rows x BN_OUT columns), written
+// by the waves from their accumulators and read back as whole rows, so that each store
+// instruction writes full 128-byte lines of output rows (the accumulator layout gives
+// 16 bytes of each of 32 rows per instruction).  It lives in the four activation stage
+// buffers, which the main loop no longer reads: PASS_ROWS rows at a time, ROWS_PER of
+// them per stage buffer (the buffers stay separate arrays, so that the compiler can tell
+// which one a direct-to-LDS load writes).  The 16-byte chunk c of row m sits at chunk
+// c ^ (m mod NCH): the 32 rows a write instruction covers fall on distinct chunks, and
+// a read of a row's chunks stays a permutation of them.
+template <class MS, int EPI>
+struct PackedCTile {
+  static constexpr int BN_OUT = EPI == EPI_SWIGLU ? MS::BN / 2 : MS::BN;  // output columns
+  static constexpr int PITCH = BN_OUT * 2;  // bytes per row
+  static constexpr int NCH = PITCH / 16;    // 16-byte chunks per row
+  static constexpr int STAGE_BYTES = MS::BM * kBK * 2;
+  static constexpr int ROWS_PER = STAGE_BYTES / PITCH < MS::BM ? STAGE_BYTES / PITCH : MS::BM;
+  static constexpr int PASS_ROWS = kPStages * ROWS_PER < MS::BM ? kPStages * ROWS_PER : MS::BM;
+  static_assert((NCH & (NCH - 1)) == 0, "power-of-two chunks per row");
+  static_assert(PASS_ROWS % 32 == 0 && MS::BM % PASS_ROWS == 0, "whole row blocks per pass");
+  __device__ static int swz(int lm, int c) { return (c ^ (lm & (NCH - 1))) << 4; }
+  // chunk c of pass-local row lm = 32 TR + frow (row block TR of the pass); the stage
+  // buffer is known at compile time, or one of two when a stage holds 16 rows
+  template <int TR>
+  __device__ static uint8_t* waddr(uint16_t* const (&A)[kPStages], int frow, int c) {
+    const int lm = TR * 32 + frow;
+    if constexpr (ROWS_PER % 32 == 0) {
+      constexpr int st = TR * 32 / ROWS_PER;
+      return reinterpret_cast<uint8_t*>(A[st]) + (lm - st * ROWS_PER) * PITCH + swz(lm, c);
+    } else {
+      static_assert(ROWS_PER == 16, "a stage holds 16 rows or a multiple of 32");
+      uint8_t* const b = reinterpret_cast<uint8_t*>(frow < 16 ? A[2 * TR] : A[2 * TR + 1]);
+      return b + (frow & 15) * PITCH + swz(lm, c);
+    }
+  }
+  // chunk c of row r of stage buffer ST (pass-local row ST ROWS_PER + r)
+  template <int ST>
+  __device__ static const uint8_t* raddr(uint16_t* const (&A)[kPStages], int r, int c) {
+    return reinterpret_cast<const uint8_t*>(A[ST]) + r * PITCH + swz(ST * ROWS_PER + r, c);
+  }
+};
+
+// Epilogue through the LDS output tile (the stage buffers A, free once every wave has
+// passed the barrier after its last operand read).  The values are those of
+// packed_epilogue (activation, bias, row weight, rounding to bf16); rows and columns past
+// the tile's bounds are not stored.
+template <class MS, int EPI, int TA>
+__device__ __forceinline__ void packed_epilogue_lds(const GemmArgs& g, const Tile& tile, int lane,
+                                                    int col0, f32x16_t (&acc)[2][MS::TMAX],
+                                                    const EpiRowsLds<MS::BM>& rows,
+                                                    uint16_t* const (&A)[kPStages]) {
+  using CT = PackedCTile<MS, EPI>;
+  constexpr int TM_PASS = CT::PASS_ROWS / 32;  // row blocks per pass
+  constexpr int NPASS = (TA + TM_PASS - 1) / TM_PASS;
+  const int frow = lane & 31;
+  const int wc0 = col0 - tile.nt * CT::BN_OUT;  // the wave's first column in the tile
+  const int col_base = tile.nt * CT::BN_OUT;
+  constexpr int TN = EPI == EPI_SWIGLU ? 1 : 2;
+  const uint16_t* bias = static_cast<const uint16_t*>(g.bias);
+  uint16_t* __restrict__ C = static_cast<uint16_t*>(g.c);
+#pragma unroll
+  for (int pass = 0; pass < NPASS; ++pass) {
+    const int tm0 = pass * TM_PASS;
+    if (pass > 0) __syncthreads();  // the previous pass's rows are read
+#pragma unroll
+    for (int tn = 0; tn < TN; ++tn)
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const int wc = wc0 + tn * 32 + Mfma<32>::ni(q, lane);  // 4 consecutive columns
+        float bv[4] = {0.f, 0.f, 0.f, 0.f};
+        if (EPI != EPI_SWIGLU && bias != nullptr) {
+          const int col = min(col_base + wc, g.n_out - 4);  // (past n_out: not stored)
+#pragma unroll
+          for (int r = 0; r < 4; ++r)
+            bv[r] = bf16_to_f32(bias[tile.seg * g.bias_seg_stride + col + r]);
+        }
+        static_for<TM_PASS>([&](auto tr) {
+          constexpr int TR = decltype(tr)::value;
+          const int tm = tm0 + TR;
+          if (tm >= TA) return;
+          const int m = tm * 32 + frow;
+          const float sc = rows.weight(m);
+          float v[4];
+#pragma unroll
+          for (int r = 0; r < 4; ++r) {
+            if constexpr (EPI == EPI_SWIGLU) {
+              v[r] = silu(acc[0][tm][4 * q + r]) * acc[1][tm][4 * q + r];
+            } else {
+              v[r] = acc[tn][tm][4 * q + r] + bv[r];
+              if (EPI == EPI_GELU) v[r] = gelu_bf16(v[r]);
+              v[r] *= sc;  // exact when 1
+            }
+          }
+          *reinterpret_cast<uint2*>(CT::template waddr<TR>(A, frow, wc >> 3) + ((wc & 4) << 1)) =
+              pack_bf16x4(v[0], v[1], v[2], v[3]);
+        });
+      }
+    __syncthreads();
+    const int rows_here = min(TA - tm0, TM_PASS) * 32;
+    constexpr int kIters = CT::ROWS_PER * CT::NCH / MS::NT;  // per stage buffer
+    static_assert(kIters * MS::NT == CT::ROWS_PER * CT::NCH, "whole read rounds");
+    static_for<kPStages>([&](auto st) {
+      constexpr int ST = decltype(st)::value;
+      if (ST * CT::ROWS_PER >= CT::PASS_ROWS) return;
+#pragma unroll
+      for (int it = 0; it < kIters; ++it) {
+        const int i = it * MS::NT + static_cast<int>(threadIdx.x);
+        const int r = i / CT::NCH, c = i % CT::NCH;
+        const int lm = ST * CT::ROWS_PER + r;
+        const int m = tm0 * 32 + lm;
+        if (lm < rows_here && m < tile.m_valid && col_base + c * 8 < g.n_out) {
+          const uint4 v = *reinterpret_cast<const uint4*>(CT::template raddr<ST>(A, r, c));
+          *reinterpret_cast<uint4*>(C + rows.out(m) * g.ldc + col_base + c * 8) = v;
+        }
+      }
+    });
+  }
+}
+
 template <class MS, int EPI, int TA>
 __device__ __forceinline__ void packed_body(const GemmArgs& g, const Tile& tile, const PackedIO<MS>& io,
                                          uint16_t* const (&A)[kPStages], int lane, int col0,
@@ -1434,12 +1565,13 @@ __device__ __forceinline__ void packed_body(const GemmArgs& g, const Tile& tile,
       return;
     }
   }
-  __syncthreads();  // the tile's output rows are in LDS
-  packed_epilogue<EPI, 2, MS::TMAX, TA>(g, tile, lane, col0, acc, rows);
+  __syncthreads();  // the operand stages are free, the tile's output rows in LDS
+  packed_epilogue_lds<MS, EPI, TA>(g, tile, lane, col0, acc, rows, A);
 }
 
 template <class MS, int EPI>
 __global__ __launch_bounds__(MS::NT, 1) void gemm_packed_kernel(GemmArgs g) {
+  // the activation stages during the main loop, the output tile in the epilogue
   __shared__ __attribute__((aligned(16))) uint16_t A0[MS::BM * kBK], A1[MS::BM * kBK];
   __shared__ __attribute__((aligned(16))) uint16_t A2[MS::BM * kBK], A3[MS::BM * kBK];
   __shared__ SchedSmem sched;
