@@ -387,6 +387,13 @@ typedef struct {
    * read): the layer then needs one copy of the routed experts' weights, not two. */
   const void* packed;
   size_t packed_bytes;
+  /* Optional (bf16 only, n_shared > 0): the shared experts' shared_w1/w3/w2 as written
+   * by moe_pack_shared_weights (same act, n_shared, d_model, d_ff), and its size in
+   * bytes, which must equal moe_packed_shared_weights_size() for this configuration.
+   * When given, the shared experts read it (same results) and shared_w1, shared_w3 and
+   * shared_w2 may be NULL. */
+  const void* shared_packed;
+  size_t shared_packed_bytes;
 } moe_weights;
 
 /* Optional caller-owned resources of moe_forward for running the shared experts
@@ -425,6 +432,29 @@ size_t moe_packed_weights_size(moe_act act, int32_t n_experts, int64_t d_model, 
 moe_status moe_pack_weights(void* stream, moe_act act, int32_t n_experts, int64_t d_model,
                             int64_t d_ff, const void* w1, const void* w3, const void* w2,
                             void* packed);
+
+/*
+ * moe_pack_shared_weights -- the same relayout for the n_shared shared experts
+ * ([DeepSeek-V2] §2.3: they see every token and their outputs add up), which moe_forward
+ * runs as one FFN of width n_shared * d_ff: the packed copy is that of one expert whose
+ * W1 (and W3) are the n_shared experts' stacked along d_ff ([n_shared * d_ff][d], the
+ * memory order of shared_w1) and whose W2 is [d][n_shared * d_ff], row n holding
+ * W2_0[n], W2_1[n], ... (so its reduction runs over every shared expert's hidden units
+ * in turn).  Layout otherwise that of moe_pack_weights for one expert of d_ff' =
+ * n_shared * d_ff.
+ *   act, n_shared (1 .. 8), d_model, d_ff: as in moe_config, bf16 only (d_model, d_ff
+ *   multiples of 64).
+ *   w1, w3 (SwiGLU only, else NULL), w2: device, bf16, the layouts of moe_weights'
+ *   shared_w1 / shared_w3 / shared_w2.
+ *   packed: device, at least moe_packed_shared_weights_size(...) bytes, 16-byte aligned,
+ *   owned by the caller; fully written.
+ * Errors and asynchrony as moe_pack_weights.
+ */
+size_t moe_packed_shared_weights_size(moe_act act, int32_t n_shared, int64_t d_model,
+                                      int64_t d_ff);
+moe_status moe_pack_shared_weights(void* stream, moe_act act, int32_t n_shared, int64_t d_model,
+                                   int64_t d_ff, const void* w1, const void* w3, const void* w2,
+                                   void* packed);
 
 /* Number of optional stage markers of moe_forward (see moe_stats.stage_events). */
 #define MOE_N_STAGE_EVENTS 7

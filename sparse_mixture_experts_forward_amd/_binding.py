@@ -44,7 +44,9 @@ class MoEConfigC(C.Structure):
 class MoEWeightsC(C.Structure):
     _fields_ = [(n, C.c_void_p) for n in ("w_router", "logit_bias", "w1", "w3", "b1", "w2",
                                           "b2", "shared_w1", "shared_w3", "shared_w2",
-                                          "packed")] + [("packed_bytes", C.c_size_t)]
+                                          "packed")] + [("packed_bytes", C.c_size_t),
+                                                        ("shared_packed", C.c_void_p),
+                                                        ("shared_packed_bytes", C.c_size_t)]
 
 
 class MoEStreamsC(C.Structure):
@@ -92,6 +94,8 @@ _SIGS = {
                               C.POINTER(MoEStatsC), C.POINTER(MoEStreamsC), _VP, _SZ]),
     "moe_packed_weights_size": (_SZ, [C.c_int, _I32, _I64, _I64]),
     "moe_pack_weights": (C.c_int, [_VP, C.c_int, _I32, _I64, _I64, _VP, _VP, _VP, _VP]),
+    "moe_packed_shared_weights_size": (_SZ, [C.c_int, _I32, _I64, _I64]),
+    "moe_pack_shared_weights": (C.c_int, [_VP, C.c_int, _I32, _I64, _I64, _VP, _VP, _VP, _VP]),
     "moe_status_string": (C.c_char_p, [C.c_int]),
     "moe_last_error": (C.c_char_p, []),
 }
@@ -297,6 +301,17 @@ def moe_pack_weights(act: int, n_experts: int, d_model: int, d_ff: int, w1, w3, 
     _check("moe_pack_weights", st)
 
 
+def moe_packed_shared_weights_size(act: int, n_shared: int, d_model: int, d_ff: int) -> int:
+    return int(lib().moe_packed_shared_weights_size(act, n_shared, d_model, d_ff))
+
+
+def moe_pack_shared_weights(act: int, n_shared: int, d_model: int, d_ff: int, w1, w3, w2,
+                            packed, stream=None):
+    st = lib().moe_pack_shared_weights(_stream(stream), act, n_shared, d_model, d_ff, _ptr(w1),
+                                       _ptr(w3), _ptr(w2), _ptr(packed))
+    _check("moe_pack_shared_weights", st)
+
+
 def moe_forward_workspace_size(cfg: MoEConfigC) -> int:
     return int(lib().moe_forward_workspace_size(C.byref(cfg)))
 
@@ -306,10 +321,15 @@ def moe_forward(cfg: MoEConfigC, weights: dict, x, y, ws, stats: Optional[dict] 
     """stage_events: optional sequence of MOE_N_STAGE_EVENTS raw hipEvent_t handles (int)
     or None entries.  side: optional (side_stream, fork_event, join_event) raw handles
     (int) for running the shared experts concurrently (moe_streams).  weights["packed"]
-    (optional): the packed copy; its byte size is passed as packed_bytes."""
-    w = MoEWeightsC(**{k: _ptr(v) for k, v in weights.items() if k != "packed_bytes"})
+    and weights["shared_packed"] (optional): the packed copies; their byte sizes are passed
+    as packed_bytes / shared_packed_bytes."""
+    sizes = ("packed_bytes", "shared_packed_bytes")
+    w = MoEWeightsC(**{k: _ptr(v) for k, v in weights.items() if k not in sizes})
     if weights.get("packed") is not None:
         w.packed_bytes = weights.get("packed_bytes") or _ws_bytes(weights["packed"])
+    if weights.get("shared_packed") is not None:
+        w.shared_packed_bytes = (weights.get("shared_packed_bytes")
+                                 or _ws_bytes(weights["shared_packed"]))
     s = MoEStatsC(**{k: _ptr(v) for k, v in (stats or {}).items() if k in STAT_FIELDS})
     if stage_events is not None:
         for i, ev in enumerate(stage_events):

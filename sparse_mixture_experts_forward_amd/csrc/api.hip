@@ -282,6 +282,9 @@ moe_status run_ffn(hipStream_t st, moe_dtype dt, moe_act act, const void* a, int
   g2.n_out = static_cast<int32_t>(d); g2.k = static_cast<int32_t>(d_ff);
   g2.small_tiles = small_tiles;
   if (packed && bf) {
+    // the packed second layer's reduction is contiguous, whatever w2's chunks
+    g2.kchunk = g2.k;
+    g2.kbatch_stride = 0;
     g2.bp = static_cast<const char*>(packed) + n_seg * moe::packed_w1_bytes(sw, d, d_ff);
     g2.bp_rows = static_cast<int32_t>(moe::packed_rows(d));
     g2.bp_seg_stride = g2.bp_rows * d_ff * 2;
@@ -804,6 +807,36 @@ moe_status moe_pack_weights(void* stream, moe_act act, int32_t n_experts, int64_
                    "weight packing launch");
 }
 
+size_t moe_packed_shared_weights_size(moe_act act, int32_t n_shared, int64_t d_model,
+                                      int64_t d_ff) {
+  if (check_ffn_shape(MOE_BF16, act, d_model, d_ff) != MOE_OK) return 0;
+  if (n_shared < 1 || n_shared > 8) return 0;
+  const int64_t f = static_cast<int64_t>(n_shared) * d_ff;
+  if (f * d_model * 2 > UINT32_MAX) return 0;
+  return static_cast<size_t>(moe::packed_w1_bytes(act == MOE_ACT_SWIGLU, d_model, f) +
+                             moe::packed_w2_bytes(d_model, f));
+}
+
+moe_status moe_pack_shared_weights(void* stream, moe_act act, int32_t n_shared, int64_t d_model,
+                                   int64_t d_ff, const void* w1, const void* w3, const void* w2,
+                                   void* packed) {
+  MOE_TRY(check_ffn_shape(MOE_BF16, act, d_model, d_ff));
+  if (n_shared < 1 || n_shared > 8) return fail(MOE_ERR_UNSUPPORTED, "n_shared must be 1..8");
+  const int64_t f = static_cast<int64_t>(n_shared) * d_ff;
+  if (f * d_model * 2 > UINT32_MAX)
+    return fail(MOE_ERR_UNSUPPORTED, "shared experts' weights (n_shared * d_ff * d_model) must be below 4 GiB");
+  const bool sw = act == MOE_ACT_SWIGLU;
+  if (!w1 || !w2 || !packed || (sw && !w3))
+    return fail(MOE_ERR_INVALID_ARG, "w1, w2, packed (and w3 for SwiGLU) are required");
+  MOE_TRY(check_aligned(w1, 16, "w1"));
+  MOE_TRY(check_aligned(w2, 16, "w2"));
+  if (sw) MOE_TRY(check_aligned(w3, 16, "w3"));
+  MOE_TRY(check_aligned(packed, 16, "packed"));
+  return hip_check(moe::launch_pack_weights(static_cast<hipStream_t>(stream), sw, 1, d_model, f,
+                                            w1, sw ? w3 : nullptr, w2, packed, n_shared),
+                   "shared weight packing launch");
+}
+
 size_t moe_forward_workspace_size(const moe_config* cfg) {
   if (check_config(cfg) != MOE_OK) return 0;
   return forward_layout(*cfg, nullptr).used;
@@ -833,8 +866,17 @@ moe_status moe_forward(void* stream, const moe_config* cfg, const moe_weights* w
     fork_ev = static_cast<hipEvent_t>(streams->fork_event);
     join_ev = static_cast<hipEvent_t>(streams->join_event);
   }
-  if (c.n_shared > 0 && (!w->shared_w1 || !w->shared_w2 || (swiglu && !w->shared_w3)))
+  if (w->shared_packed && c.n_shared > 0) {
+    if (c.dtype != MOE_BF16) return fail(MOE_ERR_UNSUPPORTED, "packed weights are bf16 only");
+    MOE_TRY(check_aligned(w->shared_packed, 16, "shared_packed"));
+    const size_t want = moe_packed_shared_weights_size(c.act, c.n_shared, c.d_model, c.d_ff);
+    if (w->shared_packed_bytes != want)
+      return fail(MOE_ERR_INVALID_ARG,
+                  "shared_packed_bytes is %zu, but the packed copy of %d shared experts of this "
+                  "shape is %zu bytes", w->shared_packed_bytes, c.n_shared, want);
+  } else if (c.n_shared > 0 && (!w->shared_w1 || !w->shared_w2 || (swiglu && !w->shared_w3))) {
     return fail(MOE_ERR_INVALID_ARG, "shared expert weights are required when n_shared > 0");
+  }
   if (c.n_tokens > 0 && (!x || !y)) return fail(MOE_ERR_INVALID_ARG, "x and y are required");
   if (c.n_tokens > 0 && x == y) return fail(MOE_ERR_INVALID_ARG, "y may not alias x");
   const ForwardLayout need = forward_layout(c, nullptr);
@@ -846,6 +888,7 @@ moe_status moe_forward(void* stream, const moe_config* cfg, const moe_weights* w
     MOE_TRY(check_aligned(y, 16, "y"));
   }
   const void* wptrs[] = {w->w1, w->w2, w->w3, w->shared_w1, w->shared_w2, w->shared_w3};
+  // (the packed copies' alignment is checked above)
   for (const void* p : wptrs)
     if (p) MOE_TRY(check_aligned(p, 16, "expert weights"));
 
@@ -899,10 +942,13 @@ moe_status moe_forward(void* stream, const moe_config* cfg, const moe_weights* w
   // latency-bound router and dispatch, whose few workgroups would otherwise wait
   // behind its tiles); without one, after the routed experts on `stream`.
   const bool shared = c.n_shared > 0 && n > 0;
+  // (with the packed copy, W2's S chunks are one reduction of S*d_ff)
   auto run_shared = [&](hipStream_t s) {
     return run_ffn(s, c.dtype, c.act, x, c.d_model, nullptr, 1, static_cast<int32_t>(n), n,
                    c.d_model, c.d_ff * c.n_shared, w->shared_w1, w->shared_w3, nullptr, 0,
-                   w->shared_w2, nullptr, c.d_ff, c.d_model * c.d_ff, L.h_sh, L.y_sh, nullptr);
+                   w->shared_w2, nullptr, c.d_ff, c.d_model * c.d_ff, L.h_sh, L.y_sh, nullptr,
+                   nullptr, nullptr, 0, nullptr, nullptr, nullptr,
+                   c.n_shared > 0 ? w->shared_packed : nullptr);
   };
   if (shared && side) {
     MOE_TRY(hip_check(hipEventRecord(fork_ev, st), "fork event record"));

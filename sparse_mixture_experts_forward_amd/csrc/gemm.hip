@@ -1075,11 +1075,14 @@ __device__ __forceinline__ int panel_col0(int p) { return p * (EPI == EPI_SWIGLU
 // Writes the packed copy of E experts' weights: one thread per 16-byte piece of the
 // output (first-layer products of all experts, then second-layer ones), zeros for the
 // padding rows.  Piece i of an expert's product with reduction K is lane i % 64 of
-// fragment i / 64 = (row block rb, k-step kb), rb = fragment / (K/16).
+// fragment i / 64 = (row block rb, k-step kb), rb = fragment / (K/16).  The second
+// layer's reduction (d_ff) may consist of w2_chunks matrices [d][d_ff / w2_chunks] one
+// after another in memory (shared experts as one FFN): element (n, k) is then that of
+// matrix k / (d_ff / w2_chunks).
 __global__ __launch_bounds__(256) void pack_weights_kernel(
     const uint16_t* __restrict__ w1, const uint16_t* __restrict__ w3,
     const uint16_t* __restrict__ w2, u32x4_t* __restrict__ packed, int e, int64_t d,
-    int64_t d_ff, int swiglu, int64_t rows1, int64_t rows2) {
+    int64_t d_ff, int swiglu, int64_t rows1, int64_t rows2, int w2_chunks) {
   const int64_t per1 = rows1 * d / 8, per2 = rows2 * d_ff / 8;
   const int64_t i = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x;
   if (i >= e * (per1 + per2)) return;
@@ -1102,7 +1105,8 @@ __global__ __launch_bounds__(256) void pack_weights_kernel(
       src = w1 + (ex * d_ff + n) * d + k;
     }
   } else if (n < d) {
-    src = w2 + (ex * d + n) * d_ff + k;
+    const int64_t kc = d_ff / w2_chunks, c = k / kc;  // (8-element pieces never straddle)
+    src = w2 + ((ex * w2_chunks + c) * d + n) * kc + (k - c * kc);
   }
   u32x4_t v = {0u, 0u, 0u, 0u};
   if (src) v = *reinterpret_cast<const u32x4_t*>(src);
@@ -1953,14 +1957,16 @@ hipError_t launch_f32_epi(hipStream_t st, const GemmArgs& g, int64_t max_rows) {
 }  // namespace
 
 hipError_t launch_pack_weights(hipStream_t st, bool swiglu, int e, int64_t d, int64_t d_ff,
-                               const void* w1, const void* w3, const void* w2, void* packed) {
+                               const void* w1, const void* w3, const void* w2, void* packed,
+                               int w2_chunks) {
   const int64_t rows1 = packed_rows((swiglu ? 2 : 1) * d_ff), rows2 = packed_rows(d);
   const int64_t pieces = e * (rows1 * d + rows2 * d_ff) / 8;
   if (pieces <= 0) return hipSuccess;
   hipLaunchKernelGGL(pack_weights_kernel, dim3(static_cast<unsigned>((pieces + 255) / 256)),
                      dim3(256), 0, st, static_cast<const uint16_t*>(w1),
                      static_cast<const uint16_t*>(w3), static_cast<const uint16_t*>(w2),
-                     static_cast<u32x4_t*>(packed), e, d, d_ff, swiglu ? 1 : 0, rows1, rows2);
+                     static_cast<u32x4_t*>(packed), e, d, d_ff, swiglu ? 1 : 0, rows1, rows2,
+                     w2_chunks);
   return hipGetLastError();
 }
 

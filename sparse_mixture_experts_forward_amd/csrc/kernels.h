@@ -178,8 +178,11 @@ inline int64_t packed_w1_bytes(bool swiglu, int64_t d, int64_t d_ff) {
   return packed_rows((swiglu ? 2 : 1) * d_ff) * d * 2;
 }
 inline int64_t packed_w2_bytes(int64_t d, int64_t d_ff) { return packed_rows(d) * d_ff * 2; }
+// w2_chunks: the second layer's reduction is that many [d][d_ff / w2_chunks] matrices in
+// a row (the shared experts packed as one expert of width d_ff); 1 otherwise.
 hipError_t launch_pack_weights(hipStream_t st, bool swiglu, int e, int64_t d, int64_t d_ff,
-                               const void* w1, const void* w3, const void* w2, void* packed);
+                               const void* w1, const void* w3, const void* w2, void* packed,
+                               int w2_chunks = 1);
 
 // Sizes of the split buffers for g resident workgroups.
 inline int64_t gemm_split_floats(int g) { return static_cast<int64_t>(g) * 256 * 256; }

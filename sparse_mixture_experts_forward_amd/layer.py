@@ -61,10 +61,12 @@ class MoELayer:
 
     def pack_weights(self, stream=None, drop_unpacked: bool = False) -> torch.Tensor:
         """Writes the packed copy of the routed experts' weights (bf16 only) that every
-        routed expert product then reads; returns it (also kept in the layer's weights as
-        "packed").  drop_unpacked: the layer then forgets w1/w3/w2 (the library does not
-        need them with the packed copy), so only one copy stays resident once the caller
-        drops its own references.  Call again after changing w1/w3/w2."""
+        routed expert product then reads, and that of the shared experts if the layer has
+        any; returns the routed one (both are kept in the layer's weights, as "packed" and
+        "shared_packed").  drop_unpacked: the layer then forgets w1/w3/w2 and the shared
+        experts' weights (the library does not need them with the packed copies), so only
+        one copy stays resident once the caller drops its own references.  Call again
+        after changing the expert weights."""
         c = self.cfg
         if c.dtype != "bf16":
             raise ValueError("packed weights are bf16 only")
@@ -76,8 +78,17 @@ class MoELayer:
         B.moe_pack_weights(act, c.n_experts, c.d_model, c.d_ff, self.w["w1"], self.w.get("w3"),
                            self.w["w2"], packed, stream=stream)
         self.w["packed"] = packed
+        if c.n_shared > 0:
+            sbytes = B.moe_packed_shared_weights_size(act, c.n_shared, c.d_model, c.d_ff)
+            if sbytes <= 0:
+                raise ValueError("unsupported shape for packed shared weights")
+            spacked = torch.empty(sbytes // 2, dtype=torch.bfloat16, device=self.device)
+            B.moe_pack_shared_weights(act, c.n_shared, c.d_model, c.d_ff, self.w["shared_w1"],
+                                      self.w.get("shared_w3"), self.w["shared_w2"], spacked,
+                                      stream=stream)
+            self.w["shared_packed"] = spacked
         if drop_unpacked:
-            for k in ("w1", "w3", "w2"):
+            for k in ("w1", "w3", "w2", "shared_w1", "shared_w3", "shared_w2"):
                 self.w.pop(k, None)
         return packed
 

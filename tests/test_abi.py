@@ -258,6 +258,42 @@ def test_fused_forward_workspace():
     assert B.moe_forward_workspace_size(B.make_config(**kw, fuse=7)) == both  # k = 2: ignored
 
 
+def test_packed_shared_weights_size_and_validation():
+    """The shared experts' packed copy is that of one expert of width n_shared * d_ff, and
+    moe_forward accepts it (without the unpacked shared weights) only at exactly that
+    size, bf16 and 16-byte aligned."""
+    L = B.lib()
+    sw, ge = B.MOE_ACT_SWIGLU, B.MOE_ACT_GELU
+    # DeepSeek-shaped: 2 x 1536 = 3072 hidden units; first layer 6144 packed rows of 5120,
+    # second layer 5120 rows of 3072
+    size = B.moe_packed_shared_weights_size(sw, 2, 5120, 1536)
+    assert size == (6144 * 5120 + 5120 * 3072) * 2
+    assert size == B.moe_packed_weights_size(sw, 1, 5120, 2 * 1536)
+    assert B.moe_packed_shared_weights_size(ge, 3, 768, 1344) == (4096 * 768 + 1024 * 4032) * 2
+    assert B.moe_packed_shared_weights_size(sw, 0, 5120, 1536) == 0
+    assert B.moe_packed_shared_weights_size(sw, 9, 5120, 1536) == 0
+    assert B.moe_packed_shared_weights_size(sw, 2, 5000, 1536) == 0
+    fake = 4096  # never dereferenced: validation fails first
+    pack = lambda *a: L.moe_pack_shared_weights(None, *a)
+    assert pack(sw, 2, 5120, 1536, fake, None, fake, fake) == B.MOE_ERR_INVALID_ARG  # no w3
+    assert pack(sw, 9, 5120, 1536, fake, fake, fake, fake) == B.MOE_ERR_UNSUPPORTED
+    assert pack(sw, 2, 5120, 1536, fake, fake, fake, fake + 8) == B.MOE_ERR_INVALID_ARG
+    cfg = B.make_config(64, 5120, 1536, 160, 6, sw, B.MOE_BF16, n_shared=2)
+    ws = B.moe_forward_workspace_size(cfg)
+    call = lambda w: L.moe_forward(None, C.byref(cfg), C.byref(w), fake, fake * 2, None, None,
+                                   fake, ws)
+    routed = dict(w_router=fake, w1=fake, w3=fake, w2=fake)
+    # no shared weights at all
+    assert call(B.MoEWeightsC(**routed)) == B.MOE_ERR_INVALID_ARG
+    assert "shared" in L.moe_last_error().decode()
+    for nbytes in (0, size - 16, size + 16):
+        st = call(B.MoEWeightsC(**routed, shared_packed=fake, shared_packed_bytes=nbytes))
+        assert st == B.MOE_ERR_INVALID_ARG, nbytes
+        assert "shared_packed_bytes" in L.moe_last_error().decode()
+    st = call(B.MoEWeightsC(**routed, shared_packed=fake + 8, shared_packed_bytes=size))
+    assert st == B.MOE_ERR_INVALID_ARG and "shared_packed" in L.moe_last_error().decode()
+
+
 def test_packed_weights_size_and_validation():
     L = B.lib()
     sw, ge = B.MOE_ACT_SWIGLU, B.MOE_ACT_GELU
