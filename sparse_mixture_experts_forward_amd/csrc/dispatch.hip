@@ -258,19 +258,17 @@ constexpr uint8_t kPlaced = 0, kUnplaced = 1, kMoved = 2, kExhausted = 3;
 // the others are unplaced; every token's threshold becomes its last selection.
 // Later rounds (props = this round's proposals, -1 for none): a proposal ranked below
 // kept[e] (the number of proposals expert e accepts) moves its slot to e.
-__global__ __launch_bounds__(kThreads) void reroute_accept_kernel(
-    const int32_t* props, int64_t n, int k, int E, int64_t tpb, int64_t n_blocks,
+// Chunk `b` by one whole wave (cnt: E ints of LDS, zeroed); the number of moved slots is
+// added to n_moved (round 0: workgroup 0 zeroes it).
+__device__ __forceinline__ void accept_chunk(
+    const int32_t* props, int64_t n, int k, int E, int64_t tpb, int64_t n_blocks, int64_t b,
     const int32_t* __restrict__ blk_base, const int32_t* __restrict__ kept, int first,
-    const float* __restrict__ logits, const float* __restrict__ bias,
-    int32_t* topk_idx /* = props in round 0 */, uint8_t* __restrict__ state,
-    float* __restrict__ thr_z, int32_t* __restrict__ thr_e, int32_t* __restrict__ n_moved) {
-  __shared__ int32_t cnt[kMaxExperts];
-  for (int e = threadIdx.x; e < E; e += kThreads) cnt[e] = 0;
-  __syncthreads();
-  if (threadIdx.x >= kWave) return;
-  const int64_t t0 = static_cast<int64_t>(blockIdx.x) * tpb;
+    const float* __restrict__ logits, const float* __restrict__ bias, int32_t* topk_idx,
+    uint8_t* __restrict__ state, float* __restrict__ thr_z, int32_t* __restrict__ thr_e,
+    int32_t* __restrict__ n_moved, int32_t* cnt) {
+  const int64_t t0 = b * tpb;
   const int64_t t1 = min(n, t0 + tpb);
-  const int32_t* base_e = blk_base + blockIdx.x;
+  const int32_t* base_e = blk_base + b;
   int moved = 0;
   chunk_ranks(props, t0 * k, t1 * k, E, cnt, [&](int64_t q, int e, int r) {
     const bool take = e >= 0 && base_e[e * n_blocks] + r < kept[e];
@@ -288,31 +286,60 @@ __global__ __launch_bounds__(kThreads) void reroute_accept_kernel(
     }
   });
   if (first) {
-    if (blockIdx.x == 0 && threadIdx.x == 0 && n_moved) n_moved[0] = 0;
+    if (b == 0 && lane_id() == 0 && n_moved) n_moved[0] = 0;
     return;
   }
   const float tot = wave_sum(static_cast<float>(moved));  // < 2^24 per chunk: exact
-  if (threadIdx.x == 0 && tot > 0.f && n_moved) atomicAdd(n_moved, static_cast<int32_t>(tot));
+  if (lane_id() == 0 && tot > 0.f && n_moved) atomicAdd(n_moved, static_cast<int32_t>(tot));
 }
 
-// One round's proposals.  Experts with room at the round's start are open.  Each
-// token with unplaced slots takes, slot by slot, its best open candidate after its
-// threshold (a wave per token, VPL experts per lane), and the threshold moves to the
-// last one taken; slots left without a candidate are exhausted for good (the open set
-// only shrinks).  The chunk's per-expert proposal counts go to blk_hist[e][chunk].
+// The last round's acceptances (the others run at the start of the next round's
+// proposals, reroute_propose_kernel).
+__global__ __launch_bounds__(kThreads) void reroute_accept_kernel(
+    const int32_t* props, int64_t n, int k, int E, int64_t tpb, int64_t n_blocks,
+    const int32_t* __restrict__ blk_base, const int32_t* __restrict__ kept, int first,
+    const float* __restrict__ logits, const float* __restrict__ bias,
+    int32_t* topk_idx /* = props in round 0 */, uint8_t* __restrict__ state,
+    float* __restrict__ thr_z, int32_t* __restrict__ thr_e, int32_t* __restrict__ n_moved) {
+  __shared__ int32_t cnt[kMaxExperts];
+  for (int e = threadIdx.x; e < E; e += kThreads) cnt[e] = 0;
+  __syncthreads();
+  if (threadIdx.x >= kWave) return;
+  accept_chunk(props, n, k, E, tpb, n_blocks, blockIdx.x, blk_base, kept, first, logits, bias,
+               topk_idx, state, thr_z, thr_e, n_moved, cnt);
+}
+
+// One round's proposals, after the chunk's acceptances of the previous round (acc_props:
+// that round's proposals, or topk_idx with first != 0 for the plain capacity rule;
+// blk_base / kept from the scan that closed it): both only touch the chunk's own slots
+// and tokens, and the room they use is the scan's, so one launch serves both.  Experts
+// with room at the round's start are open.  Each token with unplaced slots takes, slot
+// by slot, its best open candidate after its threshold (a wave per token, VPL experts
+// per lane), and the threshold moves to the last one taken; slots left without a
+// candidate are exhausted for good (the open set only shrinks).  The chunk's per-expert
+// proposal counts go to blk_hist[e][chunk].  props may be acc_props (rewritten in place
+// once the acceptances are done).
 template <int VPL>
 __global__ __launch_bounds__(kThreads) void reroute_propose_kernel(
     const float* __restrict__ logits, const float* __restrict__ bias, int64_t n, int k, int E,
     int64_t tpb, int64_t n_blocks, const int32_t* __restrict__ room,
     uint8_t* __restrict__ state, float* __restrict__ thr_z, int32_t* __restrict__ thr_e,
-    int32_t* __restrict__ props, int32_t* __restrict__ blk_hist) {
+    int32_t* props, int32_t* __restrict__ blk_hist, const int32_t* acc_props, int first,
+    const int32_t* __restrict__ blk_base, const int32_t* __restrict__ kept,
+    int32_t* topk_idx, int32_t* __restrict__ n_moved) {
   __shared__ int32_t open_e[kMaxExperts];
   __shared__ int32_t h[kMaxExperts];
+  __shared__ int32_t cnt[kMaxExperts];
   for (int e = threadIdx.x; e < E; e += kThreads) {
     open_e[e] = room[e] > 0;
     h[e] = 0;
+    cnt[e] = 0;
   }
   __syncthreads();
+  if (threadIdx.x < kWave)
+    accept_chunk(acc_props, n, k, E, tpb, n_blocks, blockIdx.x, blk_base, kept, first, logits,
+                 bias, topk_idx, state, thr_z, thr_e, n_moved, cnt);
+  __syncthreads();  // the chunk's states, thresholds and selections are final
   const int lane = lane_id(), wave = threadIdx.x / kWave;
   const int64_t t0 = static_cast<int64_t>(blockIdx.x) * tpb;
   const int64_t t1 = min(n, t0 + tpb);
@@ -499,17 +526,18 @@ hipError_t launch_reroute(hipStream_t st, const float* logits, const float* bias
                      g.n_blocks, capacity, w.blk_base, w.kept, w.room, nullptr, 0, nullptr,
                      nullptr, nullptr, nullptr, nullptr, nullptr);
   if ((err = hipGetLastError()) != hipSuccess) return err;
-  hipLaunchKernelGGL(reroute_accept_kernel, grid, blk, 0, st, topk_idx, n, k, e, tpb, g.n_blocks,
-                     w.blk_base, w.kept, 1, logits, bias, topk_idx, w.state, w.thr_z, w.thr_e,
-                     n_moved);
-  if ((err = hipGetLastError()) != hipSuccess) return err;
+  // rounds 1 .. R: each launch accepts the previous round (round 0: the capacity rule)
+  // and proposes this one; a scan closes every round; the last round's acceptances
+  // take a launch of their own
   const int vpl = (e + kWave - 1) / kWave;
   for (int r = 0; r < rounds; ++r) {
+    const int32_t* acc = r == 0 ? topk_idx : w.props;
     switch (vpl) {
 #define MOE_PROPOSE(V)                                                                        \
   case V:                                                                                     \
     hipLaunchKernelGGL(reroute_propose_kernel<V>, grid, blk, 0, st, logits, bias, n, k, e, tpb, \
-                       g.n_blocks, w.room, w.state, w.thr_z, w.thr_e, w.props, w.blk_hist);   \
+                       g.n_blocks, w.room, w.state, w.thr_z, w.thr_e, w.props, w.blk_hist,    \
+                       acc, r == 0 ? 1 : 0, w.blk_base, w.kept, topk_idx, n_moved);           \
     break;
       MOE_PROPOSE(1) MOE_PROPOSE(2) MOE_PROPOSE(3) MOE_PROPOSE(4)
       MOE_PROPOSE(5) MOE_PROPOSE(6) MOE_PROPOSE(7) MOE_PROPOSE(8)
@@ -521,11 +549,11 @@ hipError_t launch_reroute(hipStream_t st, const float* logits, const float* bias
                        w.blk_hist, g.n_blocks, int64_t{-1}, w.blk_base, w.kept, w.room, nullptr,
                        0, nullptr, nullptr, nullptr, nullptr, nullptr, nullptr);
     if ((err = hipGetLastError()) != hipSuccess) return err;
-    hipLaunchKernelGGL(reroute_accept_kernel, grid, blk, 0, st, w.props, n, k, e, tpb,
-                       g.n_blocks, w.blk_base, w.kept, 0, logits, bias, topk_idx, w.state,
-                       w.thr_z, w.thr_e, n_moved);
-    if ((err = hipGetLastError()) != hipSuccess) return err;
   }
+  hipLaunchKernelGGL(reroute_accept_kernel, grid, blk, 0, st, w.props, n, k, e, tpb, g.n_blocks,
+                     w.blk_base, w.kept, 0, logits, bias, topk_idx, w.state, w.thr_z, w.thr_e,
+                     n_moved);
+  if ((err = hipGetLastError()) != hipSuccess) return err;
   const int64_t wblocks = std::min<int64_t>((n + 3) / 4, 2048);
   switch (vpl) {
 #define MOE_WEIGHTS(V)                                                                       \
