@@ -394,6 +394,12 @@ typedef struct {
    * shared_w2 may be NULL. */
   const void* shared_packed;
   size_t shared_packed_bytes;
+  /* Optional (bf16 x only): w_router's three bf16 planes as written by moe_pack_router
+   * (same d_model, n_experts), and their size in bytes, which must equal
+   * moe_router_packed_size().  When given, the router reads them instead of splitting
+   * w_router on every call (same logits); w_router is still required (not read). */
+  const void* router_packed;
+  size_t router_packed_bytes;
 } moe_weights;
 
 /* Optional caller-owned resources of moe_forward for running the shared experts
@@ -452,6 +458,24 @@ moe_status moe_pack_weights(void* stream, moe_act act, int32_t n_experts, int64_
  */
 size_t moe_packed_shared_weights_size(moe_act act, int32_t n_shared, int64_t d_model,
                                       int64_t d_ff);
+/*
+ * moe_pack_router -- the router's weight preparation for bf16 activations, done once:
+ * W_router (float32 [d][E]) split exactly into three bf16 planes, w = hi + mid + lo with
+ * each part the bf16 rounding of what the previous parts left (8 + 8 + 8 significant
+ * bits cover float32's 24), so that the logits x W_router of [Why-MoE] §2.2 come from
+ * the bf16 matrix cores at float32 accuracy.  moe_route and moe_forward without
+ * router_packed do the same split on every call.
+ *   w_router: device, [d_model][n_experts] float32.  d_model a positive multiple of 8,
+ *   1 <= n_experts <= MOE_MAX_EXPERTS.
+ *   packed: device, moe_router_packed_size(d_model, n_experts) bytes, 16-byte aligned,
+ *   owned by the caller; fully written.  Layout: planes hi, mid, lo, each [E_pad][d_model]
+ *   bf16 (reduction contiguous), E_pad the expert count padded to the router's expert
+ *   groups (rows past n_experts are zero).
+ * Errors and asynchrony as moe_pack_weights.
+ */
+size_t moe_router_packed_size(int64_t d_model, int32_t n_experts);
+moe_status moe_pack_router(void* stream, const float* w_router, int64_t d_model,
+                           int32_t n_experts, void* packed);
 moe_status moe_pack_shared_weights(void* stream, moe_act act, int32_t n_shared, int64_t d_model,
                                    int64_t d_ff, const void* w1, const void* w3, const void* w2,
                                    void* packed);

@@ -46,7 +46,9 @@ class MoEWeightsC(C.Structure):
                                           "b2", "shared_w1", "shared_w3", "shared_w2",
                                           "packed")] + [("packed_bytes", C.c_size_t),
                                                         ("shared_packed", C.c_void_p),
-                                                        ("shared_packed_bytes", C.c_size_t)]
+                                                        ("shared_packed_bytes", C.c_size_t),
+                                                        ("router_packed", C.c_void_p),
+                                                        ("router_packed_bytes", C.c_size_t)]
 
 
 class MoEStreamsC(C.Structure):
@@ -95,6 +97,8 @@ _SIGS = {
     "moe_packed_weights_size": (_SZ, [C.c_int, _I32, _I64, _I64]),
     "moe_pack_weights": (C.c_int, [_VP, C.c_int, _I32, _I64, _I64, _VP, _VP, _VP, _VP]),
     "moe_packed_shared_weights_size": (_SZ, [C.c_int, _I32, _I64, _I64]),
+    "moe_router_packed_size": (_SZ, [_I64, _I32]),
+    "moe_pack_router": (C.c_int, [_VP, _VP, _I64, _I32, _VP]),
     "moe_pack_shared_weights": (C.c_int, [_VP, C.c_int, _I32, _I64, _I64, _VP, _VP, _VP, _VP]),
     "moe_status_string": (C.c_char_p, [C.c_int]),
     "moe_last_error": (C.c_char_p, []),
@@ -312,6 +316,15 @@ def moe_pack_shared_weights(act: int, n_shared: int, d_model: int, d_ff: int, w1
     _check("moe_pack_shared_weights", st)
 
 
+def moe_router_packed_size(d_model: int, n_experts: int) -> int:
+    return int(lib().moe_router_packed_size(d_model, n_experts))
+
+
+def moe_pack_router(w_router, d_model: int, n_experts: int, packed, stream=None):
+    st = lib().moe_pack_router(_stream(stream), _ptr(w_router), d_model, n_experts, _ptr(packed))
+    _check("moe_pack_router", st)
+
+
 def moe_forward_workspace_size(cfg: MoEConfigC) -> int:
     return int(lib().moe_forward_workspace_size(C.byref(cfg)))
 
@@ -321,15 +334,18 @@ def moe_forward(cfg: MoEConfigC, weights: dict, x, y, ws, stats: Optional[dict] 
     """stage_events: optional sequence of MOE_N_STAGE_EVENTS raw hipEvent_t handles (int)
     or None entries.  side: optional (side_stream, fork_event, join_event) raw handles
     (int) for running the shared experts concurrently (moe_streams).  weights["packed"]
-    and weights["shared_packed"] (optional): the packed copies; their byte sizes are passed
-    as packed_bytes / shared_packed_bytes."""
-    sizes = ("packed_bytes", "shared_packed_bytes")
+    weights["shared_packed"] and weights["router_packed"] (optional): the packed copies;
+    their byte sizes are passed as packed_bytes / shared_packed_bytes / router_packed_bytes."""
+    sizes = ("packed_bytes", "shared_packed_bytes", "router_packed_bytes")
     w = MoEWeightsC(**{k: _ptr(v) for k, v in weights.items() if k not in sizes})
     if weights.get("packed") is not None:
         w.packed_bytes = weights.get("packed_bytes") or _ws_bytes(weights["packed"])
     if weights.get("shared_packed") is not None:
         w.shared_packed_bytes = (weights.get("shared_packed_bytes")
                                  or _ws_bytes(weights["shared_packed"]))
+    if weights.get("router_packed") is not None:
+        w.router_packed_bytes = (weights.get("router_packed_bytes")
+                                 or _ws_bytes(weights["router_packed"]))
     s = MoEStatsC(**{k: _ptr(v) for k, v in (stats or {}).items() if k in STAT_FIELDS})
     if stage_events is not None:
         for i, ev in enumerate(stage_events):

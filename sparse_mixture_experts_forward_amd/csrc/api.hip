@@ -160,10 +160,13 @@ size_t dispatch_ws(int64_t n, int32_t k, int32_t e) {
   return c.used;
 }
 
+// wp_given (or null): the three bf16 planes of W_router as moe_pack_router writes them;
+// then the router does not split W_router itself.
 moe_status run_route(hipStream_t st, const void* x, moe_dtype xt, int64_t n, int64_t d,
                      const float* wr, const float* bias, int32_t e, int32_t k, int32_t flags,
                      const float* logits_in, float* logits_out, int32_t* idx, float* w,
-                     int32_t* sel, float* pm, float* aux, float* monitor, void* ws) {
+                     int32_t* sel, float* pm, float* aux, float* monitor, void* ws,
+                     const uint16_t* wp_given = nullptr) {
   Carve c(ws);
   const RouteWs r = route_layout(c, n, d, e);
   if (monitor) flags |= moe::kGateMonitor;
@@ -183,8 +186,10 @@ moe_status run_route(hipStream_t st, const void* x, moe_dtype xt, int64_t n, int
     const moe::RoutePlan pl = moe::route_plan(n, d, e);
     rows = moe::gate_blocks(n);
     if (n == 0) return finalize(0);
-    MOE_TRY(hip_check(moe::launch_route_split(st, wr, pl, r.wp), "router weight split launch"));
-    MOE_TRY(hip_check(moe::launch_route_logits(st, static_cast<const uint16_t*>(x), pl, r.wp, r.part),
+    if (!wp_given)
+      MOE_TRY(hip_check(moe::launch_route_split(st, wr, pl, r.wp), "router weight split launch"));
+    MOE_TRY(hip_check(moe::launch_route_logits(st, static_cast<const uint16_t*>(x), pl,
+                                               wp_given ? wp_given : r.wp, r.part),
                       "router logits launch"));
     MOE_TRY(hip_check(moe::launch_route_gate(st, r.part, pl.ks, n, e, bias, k, flags, logits_out,
                                              idx, w, r.pp, r.pc, r.pmon),
@@ -837,6 +842,26 @@ moe_status moe_pack_shared_weights(void* stream, moe_act act, int32_t n_shared, 
                    "shared weight packing launch");
 }
 
+size_t moe_router_packed_size(int64_t d_model, int32_t n_experts) {
+  if (d_model < 8 || d_model % 8 != 0 || n_experts < 1 || n_experts > MOE_MAX_EXPERTS) return 0;
+  return 3 * static_cast<size_t>(moe::route_plan(1, d_model, n_experts).e_pad) *
+         static_cast<size_t>(d_model) * 2;
+}
+
+moe_status moe_pack_router(void* stream, const float* w_router, int64_t d_model,
+                           int32_t n_experts, void* packed) {
+  if (n_experts < 1) return fail(MOE_ERR_INVALID_ARG, "n_experts < 1");
+  if (n_experts > MOE_MAX_EXPERTS) return fail(MOE_ERR_UNSUPPORTED, "n_experts > %d", MOE_MAX_EXPERTS);
+  if (d_model < 8 || d_model % 8 != 0)
+    return fail(MOE_ERR_UNSUPPORTED, "d_model must be a positive multiple of 8");
+  if (!w_router || !packed) return fail(MOE_ERR_INVALID_ARG, "w_router and packed are required");
+  MOE_TRY(check_aligned(packed, 16, "packed"));
+  return hip_check(moe::launch_route_split(static_cast<hipStream_t>(stream), w_router,
+                                           moe::route_plan(1, d_model, n_experts),
+                                           static_cast<uint16_t*>(packed)),
+                   "router packing launch");
+}
+
 size_t moe_forward_workspace_size(const moe_config* cfg) {
   if (check_config(cfg) != MOE_OK) return 0;
   return forward_layout(*cfg, nullptr).used;
@@ -865,6 +890,15 @@ moe_status moe_forward(void* stream, const moe_config* cfg, const moe_weights* w
     side = static_cast<hipStream_t>(streams->side_stream);
     fork_ev = static_cast<hipEvent_t>(streams->fork_event);
     join_ev = static_cast<hipEvent_t>(streams->join_event);
+  }
+  if (w->router_packed) {
+    if (c.dtype != MOE_BF16) return fail(MOE_ERR_UNSUPPORTED, "the packed router is for bf16 x only");
+    MOE_TRY(check_aligned(w->router_packed, 16, "router_packed"));
+    const size_t want = moe_router_packed_size(c.d_model, c.n_experts);
+    if (w->router_packed_bytes != want)
+      return fail(MOE_ERR_INVALID_ARG,
+                  "router_packed_bytes is %zu, but the packed router of this shape is %zu bytes",
+                  w->router_packed_bytes, want);
   }
   if (w->shared_packed && c.n_shared > 0) {
     if (c.dtype != MOE_BF16) return fail(MOE_ERR_UNSUPPORTED, "packed weights are bf16 only");
@@ -918,7 +952,8 @@ moe_status moe_forward(void* stream, const moe_config* cfg, const moe_weights* w
   MOE_TRY(run_route(st, x, c.dtype, n, c.d_model, w->w_router, w->logit_bias, e, k,
                     gate_flags(c.renormalize, c.bias_selection_only), nullptr, logits, idx,
                     tw, o.sel_count,
-                    o.prob_mean, o.aux, o.monitor, L.route_ws));
+                    o.prob_mean, o.aux, o.monitor, L.route_ws,
+                    static_cast<const uint16_t*>(w->router_packed)));
   MOE_TRY(mark(1));
   // a4-a5: capacity (slots over it re-routed first if asked) and permutation
   if (reroute)

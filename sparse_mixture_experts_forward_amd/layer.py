@@ -61,9 +61,9 @@ class MoELayer:
 
     def pack_weights(self, stream=None, drop_unpacked: bool = False) -> torch.Tensor:
         """Writes the packed copy of the routed experts' weights (bf16 only) that every
-        routed expert product then reads, and that of the shared experts if the layer has
-        any; returns the routed one (both are kept in the layer's weights, as "packed" and
-        "shared_packed").  drop_unpacked: the layer then forgets w1/w3/w2 and the shared
+        routed expert product then reads, that of the shared experts if the layer has any,
+        and the router's bf16 planes; returns the routed one (all are kept in the layer's
+        weights, as "packed", "shared_packed" and "router_packed").  drop_unpacked: the layer then forgets w1/w3/w2 and the shared
         experts' weights (the library does not need them with the packed copies), so only
         one copy stays resident once the caller drops its own references.  Call again
         after changing the expert weights."""
@@ -87,6 +87,11 @@ class MoELayer:
                                       self.w.get("shared_w3"), self.w["shared_w2"], spacked,
                                       stream=stream)
             self.w["shared_packed"] = spacked
+        rbytes = B.moe_router_packed_size(c.d_model, c.n_experts)
+        if rbytes > 0:
+            rpacked = torch.empty(rbytes // 2, dtype=torch.bfloat16, device=self.device)
+            B.moe_pack_router(self.w["w_router"], c.d_model, c.n_experts, rpacked, stream=stream)
+            self.w["router_packed"] = rpacked
         if drop_unpacked:
             for k in ("w1", "w3", "w2", "shared_w1", "shared_w3", "shared_w2"):
                 self.w.pop(k, None)

@@ -294,6 +294,39 @@ def test_packed_shared_weights_size_and_validation():
     assert st == B.MOE_ERR_INVALID_ARG and "shared_packed" in L.moe_last_error().decode()
 
 
+def test_packed_router_size_and_validation():
+    """Three bf16 planes of the expert count padded to the router's expert groups; the
+    forward takes them only for bf16 activations, at exactly that size."""
+    L = B.lib()
+    # 8 experts: one group of one 16-expert tile; 160: 10 tiles; 64: 4 tiles
+    assert B.moe_router_packed_size(4096, 8) == 3 * 16 * 4096 * 2
+    assert B.moe_router_packed_size(5120, 160) == 3 * 160 * 5120 * 2
+    assert B.moe_router_packed_size(1024, 64) == 3 * 64 * 1024 * 2
+    assert B.moe_router_packed_size(1024, 17) == 3 * 32 * 1024 * 2
+    assert B.moe_router_packed_size(100, 8) == 0
+    assert B.moe_router_packed_size(1024, 0) == 0
+    assert B.moe_router_packed_size(1024, B.MOE_MAX_EXPERTS + 1) == 0
+    fake = 4096
+    assert L.moe_pack_router(None, fake, 1024, 64, None) == B.MOE_ERR_INVALID_ARG
+    assert L.moe_pack_router(None, fake, 1020, 64, fake) == B.MOE_ERR_UNSUPPORTED
+    assert L.moe_pack_router(None, fake, 1024, 64, fake + 8) == B.MOE_ERR_INVALID_ARG
+    size = B.moe_router_packed_size(4096, 8)
+    cfg = B.make_config(64, 4096, 14336, 8, 2, B.MOE_ACT_SWIGLU, B.MOE_BF16)
+    ws = B.moe_forward_workspace_size(cfg)
+    call = lambda w, c=cfg, wsz=ws: L.moe_forward(None, C.byref(c), C.byref(w), fake, fake * 2,
+                                                  None, None, fake, wsz)
+    routed = dict(w_router=fake, w1=fake, w3=fake, w2=fake)
+    for nbytes in (0, size - 16, size + 16):
+        st = call(B.MoEWeightsC(**routed, router_packed=fake, router_packed_bytes=nbytes))
+        assert st == B.MOE_ERR_INVALID_ARG, nbytes
+        assert "router_packed_bytes" in L.moe_last_error().decode()
+    f32 = B.make_config(64, 128, 512, 8, 2, B.MOE_ACT_GELU, B.MOE_F32)
+    st = call(B.MoEWeightsC(w_router=fake, w1=fake, w2=fake, router_packed=fake,
+                            router_packed_bytes=B.moe_router_packed_size(128, 8)),
+              f32, B.moe_forward_workspace_size(f32))
+    assert st == B.MOE_ERR_UNSUPPORTED and "router" in L.moe_last_error().decode()
+
+
 def test_packed_weights_size_and_validation():
     L = B.lib()
     sw, ge = B.MOE_ACT_SWIGLU, B.MOE_ACT_GELU

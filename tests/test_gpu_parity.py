@@ -839,6 +839,31 @@ def test_forward_concurrent_streams_match_sequential():
             assert torch.equal(outs[i].view(torch.int16), ref[i].view(torch.int16)), (rep, i)
 
 
+@pytest.mark.parametrize("name", ["switch", "deepseek"])
+def test_forward_packed_router_is_bit_identical(name):
+    """The router's planes written once by moe_pack_router give the bits (output, logits,
+    selections, statistics) of the split done inside every call."""
+    cfg = CONFIGS[name].with_tokens(REDUCED[name])
+    print_case("packed-router", name, cfg.n_tokens)
+    inp = synth.DeviceInputs(cfg, DEV)
+    outs = []
+    for packed in (False, True):
+        layer = MoELayer.from_inputs(inp)
+        if packed:
+            rb = B.moe_router_packed_size(cfg.d_model, cfg.n_experts)
+            rp = torch.empty(rb // 2, dtype=torch.bfloat16, device=DEV)
+            B.moe_pack_router(inp.w_router, cfg.d_model, cfg.n_experts, rp)
+            layer.w["router_packed"] = rp
+        st = layer.new_stats(cfg.n_tokens)
+        y = layer.forward(inp.x, stats=st)
+        torch.cuda.synchronize()
+        outs.append((y, st))
+    (y0, s0), (y1, s1) = outs
+    assert torch.equal(y0.view(torch.int16), y1.view(torch.int16))
+    for key in ("logits", "topk_idx", "topk_w", "sel_count", "prob_mean", "aux", "monitor"):
+        assert torch.equal(s0[key], s1[key]), key
+
+
 # ------------------------------------------------------------------ graph capture
 @pytest.mark.parametrize("name", ["deepseek", "switch", "mixtral-packed"])
 def test_forward_replays_from_a_captured_graph(name):
