@@ -1723,8 +1723,14 @@ __global__ __launch_bounds__(kWave) void gemm_packed_finish_kernel(GemmArgs g) {
 }
 
 // ------------------------------------------------------------------ float32 SIMT kernel
-constexpr int kFBM = 64, kFBN = 64, kFBK = 16, kFPad = 4;
+constexpr int kFBM = 64, kFBN = 64, kFBK = 64, kFPad = 4;
+constexpr int kFLd = kFBK / 16;  // float4 loads per thread and operand per chunk
 
+// 64 x 64 output tile per workgroup of 256 threads (4 x 4 outputs each), K in chunks of
+// 64 staged through LDS; the next chunk's global loads are issued before the current
+// chunk's FMAs, so a chunk costs one load round trip at most (the products of the small
+// float32 layer are latency-bound: one 16-deep chunk per round trip took 52 us for a
+// 512-deep product).  Every output accumulates its k terms in ascending order.
 template <int EPI, bool KSPLIT>
 __global__ __launch_bounds__(kThreads) void gemm_f32_kernel(GemmArgs g) {
   __shared__ float As[kFBK][kFBM + kFPad];
@@ -1739,7 +1745,7 @@ __global__ __launch_bounds__(kThreads) void gemm_f32_kernel(GemmArgs g) {
 
   const int tid = threadIdx.x;
   const int ty = tid / 16, tx = tid % 16;
-  const int lr = tid / 4, lk = (tid % 4) * 4;
+  const int lr = tid / 4, lk = (tid % 4) * 4;  // row, and first k of the thread's float4s
   const float* A = static_cast<const float*>(g.a);
   const int64_t a_r = tile.row0 + min(lr, tile.m_valid - 1);
   const float* arow = A + (g.a_rows ? static_cast<int64_t>(g.a_rows[a_r]) : a_r) * g.lda;
@@ -1749,27 +1755,40 @@ __global__ __launch_bounds__(kThreads) void gemm_f32_kernel(GemmArgs g) {
                            ? static_cast<const float*>(g.b1) + tile.seg * g.b_seg_stride + static_cast<int64_t>(n_ld) * g.ldb
                            : nullptr;
 
-  float acc[4][4] = {}, acc3[4][4] = {};
-  for (int k0 = 0; k0 < g.k; k0 += kFBK) {
-    const int kk = k0 + lk;
-    float4 av = make_float4(0.f, 0.f, 0.f, 0.f), bv = av, b3v = av;
-    if (kk < g.k) {
-      int64_t bk = kk;
-      if (KSPLIT) {
-        const int64_t kb = kk / g.kchunk;
-        bk = kb * g.kbatch_stride + (kk - kb * g.kchunk);
+  // float4 u of a chunk at k0: k = k0 + lk + 16 u (zero past K)
+  float4 av[kFLd], bv[kFLd], b3v[kFLd];
+  auto load = [&](int k0) {
+#pragma unroll
+    for (int u = 0; u < kFLd; ++u) {
+      const int kk = k0 + lk + 16 * u;
+      av[u] = bv[u] = b3v[u] = make_float4(0.f, 0.f, 0.f, 0.f);
+      if (kk < g.k) {
+        int64_t bk = kk;
+        if (KSPLIT) {
+          const int64_t kb = kk / g.kchunk;
+          bk = kb * g.kbatch_stride + (kk - kb * g.kchunk);
+        }
+        av[u] = *reinterpret_cast<const float4*>(arow + kk);
+        bv[u] = *reinterpret_cast<const float4*>(brow0 + bk);
+        if (EPI == EPI_SWIGLU) b3v[u] = *reinterpret_cast<const float4*>(brow1 + bk);
       }
-      av = *reinterpret_cast<const float4*>(arow + kk);
-      bv = *reinterpret_cast<const float4*>(brow0 + bk);
-      if (EPI == EPI_SWIGLU) b3v = *reinterpret_cast<const float4*>(brow1 + bk);
     }
-    As[lk + 0][lr] = av.x; As[lk + 1][lr] = av.y; As[lk + 2][lr] = av.z; As[lk + 3][lr] = av.w;
-    Bs[lk + 0][lr] = bv.x; Bs[lk + 1][lr] = bv.y; Bs[lk + 2][lr] = bv.z; Bs[lk + 3][lr] = bv.w;
-    if (EPI == EPI_SWIGLU) {
-      B3s[lk + 0][lr] = b3v.x; B3s[lk + 1][lr] = b3v.y; B3s[lk + 2][lr] = b3v.z; B3s[lk + 3][lr] = b3v.w;
+  };
+  float acc[4][4] = {}, acc3[4][4] = {};
+  load(0);
+  for (int k0 = 0; k0 < g.k; k0 += kFBK) {
+#pragma unroll
+    for (int u = 0; u < kFLd; ++u) {
+      const int q = lk + 16 * u;
+      As[q + 0][lr] = av[u].x; As[q + 1][lr] = av[u].y; As[q + 2][lr] = av[u].z; As[q + 3][lr] = av[u].w;
+      Bs[q + 0][lr] = bv[u].x; Bs[q + 1][lr] = bv[u].y; Bs[q + 2][lr] = bv[u].z; Bs[q + 3][lr] = bv[u].w;
+      if (EPI == EPI_SWIGLU) {
+        B3s[q + 0][lr] = b3v[u].x; B3s[q + 1][lr] = b3v[u].y; B3s[q + 2][lr] = b3v[u].z; B3s[q + 3][lr] = b3v[u].w;
+      }
     }
     __syncthreads();
-#pragma unroll
+    if (k0 + kFBK < g.k) load(k0 + kFBK);  // in flight during this chunk's FMAs
+#pragma unroll 16
     for (int q = 0; q < kFBK; ++q) {
       float a[4], b[4], b3[4];
 #pragma unroll
