@@ -1320,18 +1320,57 @@ struct PackedIO {
   }
 };
 
-// Stage boundary wait of the packed kernel: the next stage's activation loads must
-// have landed; issued after them are at least two later stages' activation loads and
-// LEAD + 3 k-steps' weight loads (fewest at the first boundary: A1 is followed by A2,
-// A3, the lead k-steps of the prologue and those issued in k-steps 0..2).  Where waves
-// issue different numbers of activation loads (NW = 8), the wave with the fewest sets
-// the count, which waits at least as long as every wave needs.
+// Stage boundary wait of the packed kernel (vector memory operations complete in
+// order): the next stage's activation loads must have landed, so the count allowed in
+// flight is what was issued after them.  At boundary s (k-step 4s + 3) that is two
+// later stages' activation loads and the weight loads of
+//   * stages 1..3 (loaded in the prologue): the LEAD prologue k-steps and k-steps
+//     0 .. 4s + 2, at least LEAD + 3 k-steps;
+//   * stages >= 4 (loaded at boundary s - 3): k-steps 4s - 9 .. 4s + 2, 12 k-steps.
+// Hence min(LEAD + 3, 12) k-steps of two loads.  Where waves issue different numbers of
+// activation loads (NW = 8), the wave with the fewest sets the count, which waits at
+// least as long as every wave needs.
 template <class MS, int TA>
 struct PackedWait {
-  static constexpr int kBoundary = (kPStages - 2) * MS::template na_min<TA>() + 2 * (MS::LEAD + 3);
+  static constexpr int kWKSteps = MS::LEAD + 3 < 4 * (kPStages - 1) ? MS::LEAD + 3 : 4 * (kPStages - 1);
+  static constexpr int kBoundary = (kPStages - 2) * MS::template na_min<TA>() + 2 * kWKSteps;
   static constexpr int kPrologue = (kPStages - 1) * MS::template na_min<TA>() + 2 * MS::LEAD;
   static_assert(kBoundary < 64 && kPrologue < 64, "vmcnt range");
 };
+
+// Compile-time check of those counts: replays one wave's issue order (the prologue's
+// activation stages 0..3 and LEAD weight k-steps, then per k-step t the boundary wait
+// and next-but-three stage's activation loads when t % 4 == 3, and two weight loads)
+// for a wave with the fewest and one with the most activation loads, and requires
+// every wait's count to be at most the number of operations issued after the awaited
+// stage's activation loads (with in-order completion, the wait then returns only once
+// they have landed).  12 stages reach the steady state.
+template <class MS, int TA>
+constexpr bool packed_waits_safe() {
+  constexpr int KT = 12;
+  const int nas[2] = {MS::template na_min<TA>(), MS::template na_max<TA>()};
+  for (int v = 0; v < 2; ++v) {
+    const int na = nas[v];
+    int issued = 0;
+    int a_done[KT + kPStages] = {};  // operations issued up to the stage's last load
+    for (int st = 0; st < kPStages; ++st) {
+      issued += na;
+      a_done[st] = issued;
+    }
+    issued += 2 * MS::LEAD;
+    if (issued - a_done[0] < PackedWait<MS, TA>::kPrologue) return false;
+    for (int t = 0; t < 4 * KT; ++t) {
+      if (t % 4 == 3) {
+        const int s = t / 4;
+        if (issued - a_done[s + 1] < PackedWait<MS, TA>::kBoundary) return false;
+        issued += na;
+        a_done[s + kPStages] = issued;
+      }
+      issued += 2;
+    }
+  }
+  return true;
+}
 
 template <class MS, int T, int TA>
 __device__ __forceinline__ void pk_step(const PackedIO<MS>& io, uint16_t* const (&A)[kPStages], int t,
@@ -1538,6 +1577,7 @@ template <class MS, int EPI, int TA>
 __device__ __forceinline__ void packed_body(const GemmArgs& g, const Tile& tile, const PackedIO<MS>& io,
                                          uint16_t* const (&A)[kPStages], int lane, int col0,
                                          const EpiRowsLds<MS::BM>& rows) {
+  static_assert(packed_waits_safe<MS, TA>(), "a stage boundary wait would not cover its loads");
   static_assert(16 % MS::RING == 0, "the ring period divides the 16-k-step period");
   f32x16_t acc[2][MS::TMAX];
 #pragma unroll
