@@ -160,17 +160,46 @@ size_t dispatch_ws(int64_t n, int32_t k, int32_t e) {
   return c.used;
 }
 
+// Tokens per router workgroup (one row of the statistics partials) of moe_forward's
+// router for activations of type xt.
+int64_t router_rtok(moe_dtype xt, int64_t n) {
+  return xt == MOE_BF16 ? 4 * static_cast<int64_t>(moe::gate_tokens_per_wave(n)) : moe::kRouteTokens;
+}
+
+// The planned dispatch's workspace (moe_forward without re-routing): chunk bases
+// [E][n_blocks], kept [E], the ticket counter.
+struct PlannedWs {
+  int32_t *base, *kept, *done;
+};
+PlannedWs planned_layout(Carve& c, int64_t n, int32_t k, int32_t e, int64_t rtok) {
+  const moe::PlannedGrid g = moe::planned_dispatch_grid(n, k, rtok);
+  PlannedWs w{};
+  w.base = c.take<int32_t>(g.n_blocks * e);
+  w.kept = c.take<int32_t>(e);
+  w.done = c.take<int32_t>(1);
+  return w;
+}
+
+size_t forward_dispatch_ws(int64_t n, int32_t k, int32_t e, moe_dtype xt) {
+  Carve c(nullptr);
+  planned_layout(c, n, k, e, router_rtok(xt, n));
+  return std::max(c.used, dispatch_ws(n, k, e));
+}
+
 // wp_given (or null): the three bf16 planes of W_router as moe_pack_router writes them;
 // then the router does not split W_router itself.
 moe_status run_route(hipStream_t st, const void* x, moe_dtype xt, int64_t n, int64_t d,
                      const float* wr, const float* bias, int32_t e, int32_t k, int32_t flags,
                      const float* logits_in, float* logits_out, int32_t* idx, float* w,
                      int32_t* sel, float* pm, float* aux, float* monitor, void* ws,
-                     const uint16_t* wp_given = nullptr) {
+                     const uint16_t* wp_given = nullptr, int32_t* plan_ctr = nullptr) {
   Carve c(ws);
   const RouteWs r = route_layout(c, n, d, e);
   if (monitor) flags |= moe::kGateMonitor;
+  // plan_ctr (moe_forward, n > 0, x given): the statistics are left to the planned
+  // dispatch, whose ticket counter the router kernel clears
   auto finalize = [&](int64_t rows) {
+    if (plan_ctr && n > 0) return MOE_OK;
     return hip_check(moe::launch_route_finalize(st, r.pp, r.pc, r.pmon, rows, n, e, k, sel, pm,
                                                 aux, monitor, r.term, r.cnt),
                      "router statistics launch");
@@ -180,7 +209,7 @@ moe_status run_route(hipStream_t st, const void* x, moe_dtype xt, int64_t n, int
     // the gate alone, over the caller's logits
     rows = moe::gate_blocks(n);
     MOE_TRY(hip_check(moe::launch_route_gate(st, logits_in, 1, n, e, bias, k, flags, logits_out,
-                                             idx, w, r.pp, r.pc, r.pmon),
+                                             idx, w, r.pp, r.pc, r.pmon, plan_ctr),
                       "router gate launch"));
   } else if (xt == MOE_BF16) {
     const moe::RoutePlan pl = moe::route_plan(n, d, e);
@@ -192,12 +221,12 @@ moe_status run_route(hipStream_t st, const void* x, moe_dtype xt, int64_t n, int
                                                wp_given ? wp_given : r.wp, r.part),
                       "router logits launch"));
     MOE_TRY(hip_check(moe::launch_route_gate(st, r.part, pl.ks, n, e, bias, k, flags, logits_out,
-                                             idx, w, r.pp, r.pc, r.pmon),
+                                             idx, w, r.pp, r.pc, r.pmon, plan_ctr),
                       "router gate launch"));
   } else {
     rows = moe::route_blocks(n);
     MOE_TRY(hip_check(moe::launch_route(st, static_cast<const float*>(x), n, d, wr, bias, e, k,
-                                        flags, logits_out, idx, w, r.pp, r.pc, r.pmon),
+                                        flags, logits_out, idx, w, r.pp, r.pc, r.pmon, plan_ctr),
                       "router kernel launch"));
   }
   return finalize(rows);
@@ -387,7 +416,7 @@ ForwardLayout forward_layout(const moe_config& c, void* ws) {
   L.dropped = cv.take<int32_t>(1);
   L.small_tiles = cv.take<int32_t>(1);
   L.route_ws = cv.take<char>(route_ws(n, c.d_model, e));
-  L.dispatch_ws = cv.take<char>(dispatch_ws(n, c.top_k, e));
+  L.dispatch_ws = cv.take<char>(forward_dispatch_ws(n, c.top_k, e, c.dtype));
   if (c.reroute_rounds > 0 && cap >= 0) {
     L.logits = cv.take<float>(n * e);
     L.rr = reroute_layout(cv, n, c.top_k, e);
@@ -947,13 +976,21 @@ moe_status moe_forward(void* stream, const moe_config* cfg, const moe_weights* w
     return hip_check(hipEventRecord(static_cast<hipEvent_t>(o.stage_events[i]), st),
                      "stage event record");
   };
+  // Without re-routing the dispatch's capacity plan reads the router's per-workgroup
+  // partials and also finishes the statistics (no histogram or statistics launches).
+  const bool planned = !reroute && n > 0;
+  const int64_t rtok = router_rtok(c.dtype, n);
+  Carve rcv(L.route_ws), pcv(L.dispatch_ws);
+  const RouteWs rws = route_layout(rcv, n, c.d_model, e);
+  const PlannedWs pws = planned_layout(pcv, n, k, e, rtok);
   MOE_TRY(mark(0));
   // a1-a3: router product, gate, statistics
   MOE_TRY(run_route(st, x, c.dtype, n, c.d_model, w->w_router, w->logit_bias, e, k,
                     gate_flags(c.renormalize, c.bias_selection_only), nullptr, logits, idx,
                     tw, o.sel_count,
                     o.prob_mean, o.aux, o.monitor, L.route_ws,
-                    static_cast<const uint16_t*>(w->router_packed)));
+                    static_cast<const uint16_t*>(w->router_packed),
+                    planned ? pws.done : nullptr));
   MOE_TRY(mark(1));
   // a4-a5: capacity (slots over it re-routed first if asked) and permutation
   if (reroute)
@@ -964,12 +1001,24 @@ moe_status moe_forward(void* stream, const moe_config* cfg, const moe_weights* w
                       "re-routing launch"));
   const bool gather = fuse_gather(c), wscale = fuse_weight(c), scatter = fuse_scatter(c);
   const int64_t row_bytes = c.d_model * static_cast<int64_t>(es);
-  MOE_TRY(run_dispatch(st, idx, n, k, e, cap, x, row_bytes, offsets,
-                       L.row_token, slot_row, o.kept_count, dropped,
-                       gather ? nullptr : L.x_perm, wscale ? tw : nullptr,
-                       wscale ? L.row_w : nullptr, L.dispatch_ws,
-                       o.monitor ? o.monitor + 4 : nullptr, reroute ? nullptr : o.n_rerouted,
-                       cap >= 0 ? L.small_tiles : nullptr, scatter ? y : nullptr, row_bytes));
+  if (planned) {
+    MOE_TRY(hip_check(
+        moe::launch_dispatch_planned(
+            st, rws.pc, rws.pp, rws.pmon, (n + rtok - 1) / rtok, rtok, idx, n, k, e, cap, x,
+            row_bytes, offsets, L.row_token, slot_row, o.kept_count, dropped,
+            gather ? nullptr : L.x_perm, pws.base, pws.kept, pws.done, wscale ? tw : nullptr,
+            wscale ? L.row_w : nullptr, o.monitor ? o.monitor + 4 : nullptr, o.n_rerouted,
+            cap >= 0 ? L.small_tiles : nullptr, scatter ? y : nullptr, row_bytes, o.sel_count,
+            o.prob_mean, o.aux, o.monitor, rws.term, rws.cnt),
+        "planned dispatch launch"));
+  } else {
+    MOE_TRY(run_dispatch(st, idx, n, k, e, cap, x, row_bytes, offsets,
+                         L.row_token, slot_row, o.kept_count, dropped,
+                         gather ? nullptr : L.x_perm, wscale ? tw : nullptr,
+                         wscale ? L.row_w : nullptr, L.dispatch_ws,
+                         o.monitor ? o.monitor + 4 : nullptr, reroute ? nullptr : o.n_rerouted,
+                         cap >= 0 ? L.small_tiles : nullptr, scatter ? y : nullptr, row_bytes));
+  }
   MOE_TRY(mark(2));
   // a8: shared experts, all tokens; the S experts act as one FFN of width S*d_ff (W1/W3
   // rows concatenate, W2 splits its reduction into S chunks of d_ff).  On the caller's

@@ -19,6 +19,7 @@
 
 #include "common.h"
 #include "kernels.h"
+#include "stats.h"
 
 namespace moe {
 namespace {
@@ -180,6 +181,72 @@ __global__ __launch_bounds__(kThreads) void dispatch_scan_kernel(
   __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");  // every workgroup's kept[e] is visible
   offsets_body(kept, static_cast<int>(gridDim.x), n_assign, expert_offsets, kept_count, n_dropped,
                drop_rate, zero_out, small_tiles, wsum);
+}
+
+// The capacity plan of the forward pass from the router's per-workgroup partials, with
+// the balance statistics: one workgroup per expert scans the counts of dispatch chunk b
+// (router rows b*per .. b*per + per - 1, the chunk's tokens in order) -> blk_base, and
+// sums the expert's probability partials in float64 (thread j: chunks j, j + 256, ...,
+// rows in order, then a fixed tree) -> prob_mean, sel_count and the aux term; kept =
+// min(total, capacity).  Thread 0 writes the expert's results and then takes a ticket
+// (agent-scope release); the workgroup that takes the last one acquires, lays out the
+// expert offsets and computes aux and the monitoring signals, so the whole plan and the
+// statistics are one launch.
+__global__ __launch_bounds__(kThreads) void dispatch_plan_kernel(
+    const int32_t* __restrict__ part_cnt, const float* __restrict__ part_prob,
+    const float* __restrict__ part_mon, int64_t rows, int64_t per, int64_t n_blocks,
+    int64_t n, int k, int64_t capacity, int32_t* __restrict__ blk_base, int32_t* kept,
+    int32_t* done, int32_t* __restrict__ expert_offsets, int32_t* __restrict__ kept_count,
+    int32_t* __restrict__ n_dropped, float* __restrict__ drop_rate,
+    int32_t* __restrict__ zero_out, int32_t* __restrict__ small_tiles,
+    int32_t* __restrict__ sel_count, float* __restrict__ prob_mean, double* term,
+    int64_t* cnt, float* __restrict__ aux, float* __restrict__ monitor) {
+  static_assert(kThreads == kStatsThreads, "one workgroup size");
+  __shared__ int wsum[kThreads / kWave];
+  __shared__ double red[5][kThreads];
+  __shared__ int last;
+  const int E = static_cast<int>(gridDim.x);
+  const int e = blockIdx.x;
+  int running = 0;
+  double ps = 0.0;
+  for (int64_t b0 = 0; b0 < n_blocks; b0 += kThreads) {
+    const int64_t b = b0 + threadIdx.x;
+    int v = 0;
+    if (b < n_blocks) {
+      const int64_t r1 = min(rows, (b + 1) * per);
+      for (int64_t r = b * per; r < r1; ++r) {
+        v += part_cnt[r * E + e];
+        ps += static_cast<double>(part_prob[r * E + e]);
+      }
+    }
+    int chunk_total;
+    const int incl = block_incl_scan(v, wsum, chunk_total);
+    if (b < n_blocks) blk_base[e * n_blocks + b] = running + incl - v;
+    running += chunk_total;
+  }
+  red[0][threadIdx.x] = ps;
+  __syncthreads();
+  for (int s = kThreads / 2; s >= 1; s >>= 1) {
+    if (threadIdx.x < s) red[0][threadIdx.x] += red[0][threadIdx.x + s];
+    __syncthreads();
+  }
+  if (threadIdx.x == 0) {
+    const double pm = n > 0 ? red[0][0] / static_cast<double>(n) : 0.0;
+    const double fr = n > 0 ? static_cast<double>(running) / static_cast<double>(n * k) : 0.0;
+    if (sel_count) sel_count[e] = running;
+    if (prob_mean) prob_mean[e] = static_cast<float>(pm);
+    term[e] = fr * pm;
+    cnt[e] = running;
+    kept[e] = (capacity >= 0 && running > capacity) ? static_cast<int32_t>(capacity) : running;
+    const int ticket = __hip_atomic_fetch_add(done, 1, __ATOMIC_ACQ_REL, __HIP_MEMORY_SCOPE_AGENT);
+    last = ticket == E - 1;
+  }
+  __syncthreads();
+  if (!last) return;
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");  // every workgroup's results are visible
+  offsets_body(kept, E, n * k, expert_offsets, kept_count, n_dropped, drop_rate, zero_out,
+               small_tiles, wsum);
+  if (aux || monitor) aux_body(term, cnt, part_mon, rows, n, E, aux, monitor, red);
 }
 
 __global__ __launch_bounds__(kThreads) void dispatch_scatter_kernel(
@@ -497,6 +564,49 @@ hipError_t launch_dispatch(hipStream_t st, const int32_t* topk_idx, int64_t n, i
                      expert_offsets, kept_count, n_dropped, drop_rate, zero_out, small_tiles);
   err = hipGetLastError();
   if (err != hipSuccess || g.n_blocks == 0) return err;
+  hipLaunchKernelGGL(dispatch_scatter_kernel, dim3(static_cast<unsigned>(g.n_blocks)),
+                     dim3(kThreads), 0, st, topk_idx, n, k, e, g.tokens_per_block,
+                     g.n_blocks, capacity, blk_base, expert_offsets, row_token, slot_row,
+                     topk_w, row_weight, static_cast<const uint8_t*>(x), row_bytes,
+                     static_cast<uint8_t*>(x_perm), k == 1 ? static_cast<uint8_t*>(zero_rows) : nullptr,
+                     zero_row_bytes);
+  return hipGetLastError();
+}
+
+PlannedGrid planned_dispatch_grid(int64_t n_tokens, int32_t k, int64_t rtok) {
+  // chunks of whole router rows, about as long as dispatch_grid's and within
+  // kMaxChunkItems assignments (rtok * k <= kMaxChunkItems for every router)
+  const DispatchGrid g = dispatch_grid(n_tokens, k);
+  const int64_t r = rtok > 0 ? rtok : 1;
+  int64_t per = (g.tokens_per_block + r - 1) / r;
+  const int64_t max_per = kMaxChunkItems / ((k > 0 ? k : 1) * r);
+  if (per > max_per) per = max_per;
+  if (per < 1) per = 1;
+  PlannedGrid p;
+  p.rows_per_block = per;
+  p.tokens_per_block = per * r;
+  p.n_blocks = n_tokens > 0 ? (n_tokens + p.tokens_per_block - 1) / p.tokens_per_block : 0;
+  return p;
+}
+
+hipError_t launch_dispatch_planned(
+    hipStream_t st, const int32_t* part_cnt, const float* part_prob, const float* part_mon,
+    int64_t rows, int64_t rtok, const int32_t* topk_idx, int64_t n, int k, int e,
+    int64_t capacity, const void* x, int64_t row_bytes, int32_t* expert_offsets,
+    int32_t* row_token, int32_t* slot_row, int32_t* kept_count, int32_t* n_dropped,
+    void* x_perm, int32_t* blk_base, int32_t* kept_tmp, int32_t* done, const float* topk_w,
+    float* row_weight, float* drop_rate, int32_t* zero_out, int32_t* small_tiles,
+    void* zero_rows, int64_t zero_row_bytes, int32_t* sel_count, float* prob_mean, float* aux,
+    float* monitor, double* term, int64_t* cnt) {
+  const PlannedGrid g = planned_dispatch_grid(n, k, rtok);
+  if (g.n_blocks == 0) return hipErrorInvalidValue;  // the caller plans only tokens
+  hipLaunchKernelGGL(dispatch_plan_kernel, dim3(static_cast<unsigned>(e)), dim3(kThreads), 0, st,
+                     part_cnt, part_prob, part_mon, rows, g.rows_per_block, g.n_blocks, n, k,
+                     capacity, blk_base, kept_tmp, done, expert_offsets, kept_count, n_dropped,
+                     drop_rate, zero_out, small_tiles, sel_count, prob_mean, term, cnt, aux,
+                     monitor);
+  hipError_t err = hipGetLastError();
+  if (err != hipSuccess) return err;
   hipLaunchKernelGGL(dispatch_scatter_kernel, dim3(static_cast<unsigned>(g.n_blocks)),
                      dim3(kThreads), 0, st, topk_idx, n, k, e, g.tokens_per_block,
                      g.n_blocks, capacity, blk_base, expert_offsets, row_token, slot_row,

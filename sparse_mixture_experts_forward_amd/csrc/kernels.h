@@ -24,7 +24,8 @@ inline int64_t route_blocks(int64_t n_tokens) {
 hipError_t launch_route(hipStream_t st, const float* x, int64_t n, int64_t d,
                         const float* w_router, const float* logit_bias, int e, int k,
                         int renorm, float* logits_out, int32_t* topk_idx, float* topk_w,
-                        float* part_prob, int32_t* part_cnt, float* part_mon);
+                        float* part_prob, int32_t* part_cnt, float* part_mon,
+                        int32_t* zero_ctr = nullptr);
 
 // bf16 router: exact three-part bf16 split of W_router, the sliced logits product and
 // the gate over the slices' partial logits.
@@ -56,7 +57,7 @@ hipError_t launch_route_logits(hipStream_t st, const uint16_t* x, const RoutePla
 hipError_t launch_route_gate(hipStream_t st, const float* part, int ks, int64_t n, int e,
                              const float* bias, int k, int renorm, float* logits_out,
                              int32_t* topk_idx, float* topk_w, float* part_prob,
-                             int32_t* part_cnt, float* part_mon);
+                             int32_t* part_cnt, float* part_mon, int32_t* zero_ctr = nullptr);
 
 // Batch-level bias update: b[e] -= gamma if sel_count[e]*E > N*k, += gamma if below.
 hipError_t launch_update_bias(hipStream_t st, const int32_t* sel_count, int e, int64_t n, int k,
@@ -98,6 +99,30 @@ hipError_t launch_dispatch(hipStream_t st, const int32_t* topk_idx, int64_t n, i
                            float* drop_rate = nullptr,
                            int32_t* zero_out = nullptr, int32_t* small_tiles = nullptr,
                            void* zero_rows = nullptr, int64_t zero_row_bytes = 0);
+
+// The forward pass's dispatch when the router's per-workgroup partials are at hand
+// (rows router workgroups of rtok consecutive tokens each: part_cnt / part_prob [rows][E],
+// part_mon [rows][2] with `monitor`): no histogram launch and no statistics launches.
+// Dispatch chunks are runs of whole router rows (planned_dispatch_grid).  One launch
+// scans the chunk counts per expert, sums the statistics (sel_count, prob_mean, aux,
+// monitor[0..3] as launch_route_finalize; each may be null) and lays out the capacity
+// plan; the scatter follows.  `done` must be zero when the launch starts: the router
+// kernel given it as zero_ctr clears it.  term [E] doubles, cnt [E]: scratch.
+struct PlannedGrid {
+  int64_t rows_per_block;    // router rows per dispatch chunk
+  int64_t tokens_per_block;  // rows_per_block * rtok
+  int64_t n_blocks;
+};
+PlannedGrid planned_dispatch_grid(int64_t n_tokens, int32_t k, int64_t rtok);
+hipError_t launch_dispatch_planned(
+    hipStream_t st, const int32_t* part_cnt, const float* part_prob, const float* part_mon,
+    int64_t rows, int64_t rtok, const int32_t* topk_idx, int64_t n, int k, int e,
+    int64_t capacity, const void* x, int64_t row_bytes, int32_t* expert_offsets,
+    int32_t* row_token, int32_t* slot_row, int32_t* kept_count, int32_t* n_dropped,
+    void* x_perm, int32_t* blk_base, int32_t* kept_tmp, int32_t* done, const float* topk_w,
+    float* row_weight, float* drop_rate, int32_t* zero_out, int32_t* small_tiles,
+    void* zero_rows, int64_t zero_row_bytes, int32_t* sel_count, float* prob_mean, float* aux,
+    float* monitor, double* term, int64_t* cnt);
 
 // Workspace of the overflow re-routing (all device arrays): blk_hist / blk_base
 // [E][n_blocks] (dispatch_grid), kept / room [E], state [N*k], thr_z / thr_e [N],

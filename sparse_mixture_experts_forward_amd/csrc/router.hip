@@ -21,6 +21,7 @@
 
 #include "common.h"
 #include "kernels.h"
+#include "stats.h"
 
 namespace moe {
 namespace {
@@ -144,7 +145,8 @@ __global__ __launch_bounds__(kThreads) void route_kernel(
     const float* __restrict__ bias, int E, int k, int flags,
     const float* __restrict__ logits_in, float* __restrict__ logits_out,
     int32_t* __restrict__ topk_idx, float* __restrict__ topk_w,
-    float* __restrict__ part_prob, int32_t* __restrict__ part_cnt, float* __restrict__ part_mon) {
+    float* __restrict__ part_prob, int32_t* __restrict__ part_cnt, float* __restrict__ part_mon,
+    int32_t* __restrict__ zero_ctr) {
   constexpr int EP = ET * 16;             // padded expert count (LDS row stride)
   const int renorm = flags & kGateRenorm, sel_only = (flags & kGateSelectionOnly) ? 1 : 0;
   const int monitor = (flags & kGateMonitor) ? 1 : 0;
@@ -157,6 +159,8 @@ __global__ __launch_bounds__(kThreads) void route_kernel(
 
   const int lane = lane_id();
   const int wave = threadIdx.x / kWave;
+  // (the forward pass's capacity-plan counter, cleared for the launch after this one)
+  if (zero_ctr && blockIdx.x == 0 && threadIdx.x == 0) zero_ctr[0] = 0;
   const int64_t t0 = static_cast<int64_t>(blockIdx.x) * kRouteTokens;
   const int ntok = static_cast<int>(min<int64_t>(kRouteTokens, n - t0));
   const int n_et = (E + 15) / 16;
@@ -438,6 +442,7 @@ __global__ __launch_bounds__(kThreads) void route_logits_kernel(
 }
 
 // ------------------------------------------------------------ gate
+constexpr int kGateBatch = 8;  // partial-logit slices whose loads are in flight together
 // Gate of 4 * tpw tokens per workgroup (tpw per wave, one token at a time): logits are
 // the sum of the ks partial slices in slice order (or logits_in when ks == 1 and part
 // == logits_in).  Per-workgroup statistics partials are added in wave order.
@@ -446,8 +451,10 @@ __global__ __launch_bounds__(kThreads) void route_gate_kernel(
     const float* __restrict__ part, int ks, int64_t n, int E, const float* __restrict__ bias,
     int k, int flags, int tpw, float* __restrict__ logits_out, int32_t* __restrict__ topk_idx,
     float* __restrict__ topk_w, float* __restrict__ part_prob, int32_t* __restrict__ part_cnt,
-    float* __restrict__ part_mon) {
+    float* __restrict__ part_mon, int32_t* __restrict__ zero_ctr) {
   constexpr int EP = VPL * kWave;
+  // (the forward pass's capacity-plan counter, cleared for the launch after this one)
+  if (zero_ctr && blockIdx.x == 0 && threadIdx.x == 0) zero_ctr[0] = 0;
   const int renorm = flags & kGateRenorm, sel_only = (flags & kGateSelectionOnly) ? 1 : 0;
   const int monitor = (flags & kGateMonitor) ? 1 : 0;
   float lse2 = 0.f, ent = 0.f;
@@ -470,7 +477,16 @@ __global__ __launch_bounds__(kThreads) void route_gate_kernel(
       const int e = lane + kWave * i;
       float v = 0.f;
       if (e < E) {
-        for (int z = 0; z < ks; ++z) v += part[(static_cast<int64_t>(z) * n + t) * E + e];
+        // the slices' loads are issued kGateBatch at a time, then added in slice order
+        for (int z0 = 0; z0 < ks; z0 += kGateBatch) {
+          float pz[kGateBatch];
+#pragma unroll
+          for (int j = 0; j < kGateBatch; ++j)
+            pz[j] = z0 + j < ks ? part[(static_cast<int64_t>(z0 + j) * n + t) * E + e] : 0.f;
+#pragma unroll
+          for (int j = 0; j < kGateBatch; ++j)
+            if (z0 + j < ks) v += pz[j];
+        }
         if (logits_out) logits_out[t * E + e] = v;
       }
       l[i] = v;
@@ -504,49 +520,6 @@ __global__ __launch_bounds__(kThreads) void route_gate_kernel(
 // One workgroup per expert: thread j adds rows j, j + 256, ... of the partials in order
 // (float64), then a fixed-shape tree over the 256 threads; writes sel_count, prob_mean
 // and the expert's aux term (count / (N k)) * prob_mean.
-// Sums of the aux terms, monitoring partials and load moments over a fixed tree, then
-// aux = E * sum of terms and the monitoring signals.  Run by one whole workgroup.
-__device__ __forceinline__ void aux_body(const double* __restrict__ term,
-                                         const int64_t* __restrict__ cnt,
-                                         const float* __restrict__ part_mon, int64_t rows,
-                                         int64_t n, int E, float* __restrict__ aux,
-                                         float* __restrict__ monitor, double (&red)[5][kThreads]) {
-  double v[5] = {0.0, 0.0, 0.0, 0.0, 0.0};
-  for (int e = threadIdx.x; e < E; e += kThreads) v[0] += term[e];
-  if (monitor) {
-    for (int64_t b = threadIdx.x; b < rows; b += kThreads) {
-      v[1] += static_cast<double>(part_mon[2 * b]);
-      v[2] += static_cast<double>(part_mon[2 * b + 1]);
-    }
-    for (int e = threadIdx.x; e < E; e += kThreads) {
-      const double c = static_cast<double>(cnt[e]);
-      v[3] += c;
-      v[4] += c * c;
-    }
-  }
-#pragma unroll
-  for (int q = 0; q < 5; ++q) red[q][threadIdx.x] = v[q];
-  __syncthreads();
-  for (int s = kThreads / 2; s >= 1; s >>= 1) {
-    if (threadIdx.x < s) {
-#pragma unroll
-      for (int q = 0; q < 5; ++q) red[q][threadIdx.x] += red[q][threadIdx.x + s];
-    }
-    __syncthreads();
-  }
-  if (threadIdx.x != 0) return;
-  if (aux) aux[0] = static_cast<float>(static_cast<double>(E) * red[0][0]);
-  if (monitor) {
-    const double nn = static_cast<double>(n);
-    const double mean = red[3][0] / E;
-    const double var = red[4][0] / E - mean * mean;
-    monitor[0] = n > 0 ? static_cast<float>(0.001 * red[1][0] / nn) : 0.f;
-    monitor[1] = n > 0 ? static_cast<float>(red[2][0] / nn) : 0.f;
-    monitor[2] = n > 0 ? static_cast<float>(red[4][0] / (nn * nn)) : 0.f;
-    monitor[3] = mean > 0.0 ? static_cast<float>(sqrt(var > 0.0 ? var : 0.0) / mean) : 0.f;
-  }
-}
-
 __global__ __launch_bounds__(kThreads) void route_stats_kernel(
     const float* __restrict__ part_prob, const int32_t* __restrict__ part_cnt, int64_t rows,
     int64_t n, int E, int k, int32_t* __restrict__ sel_count, float* __restrict__ prob_mean,
@@ -609,11 +582,11 @@ template <typename XT, int ET>
 hipError_t launch_route_t(hipStream_t st, const void* x, int64_t n, int64_t d,
                           const float* wr, const float* bias, int e, int k, int renorm,
                           const float* logits_in, float* logits_out, int32_t* idx,
-                          float* w, float* pp, int32_t* pc, float* pm) {
+                          float* w, float* pp, int32_t* pc, float* pm, int32_t* zc) {
   const int64_t blocks = route_blocks(n);
   hipLaunchKernelGGL((route_kernel<XT, ET>), dim3(static_cast<unsigned>(blocks)),
                      dim3(kThreads), 0, st, static_cast<const XT*>(x), n, d, wr, bias, e, k,
-                     renorm, logits_in, logits_out, idx, w, pp, pc, pm);
+                     renorm, logits_in, logits_out, idx, w, pp, pc, pm, zc);
   return hipGetLastError();
 }
 
@@ -621,15 +594,15 @@ template <typename XT>
 hipError_t launch_route_dt(hipStream_t st, const void* x, int64_t n, int64_t d,
                            const float* wr, const float* bias, int e, int k, int renorm,
                            const float* li, float* lo, int32_t* idx, float* w, float* pp,
-                           int32_t* pc, float* pm) {
+                           int32_t* pc, float* pm, int32_t* zc) {
   const int n_et = (e + 15) / 16;
-  if (n_et <= 1) return launch_route_t<XT, 1>(st, x, n, d, wr, bias, e, k, renorm, li, lo, idx, w, pp, pc, pm);
-  if (n_et <= 2) return launch_route_t<XT, 2>(st, x, n, d, wr, bias, e, k, renorm, li, lo, idx, w, pp, pc, pm);
-  if (n_et <= 4) return launch_route_t<XT, 4>(st, x, n, d, wr, bias, e, k, renorm, li, lo, idx, w, pp, pc, pm);
-  if (n_et <= 8) return launch_route_t<XT, 8>(st, x, n, d, wr, bias, e, k, renorm, li, lo, idx, w, pp, pc, pm);
-  if (n_et <= 10) return launch_route_t<XT, 10>(st, x, n, d, wr, bias, e, k, renorm, li, lo, idx, w, pp, pc, pm);
-  if (n_et <= 16) return launch_route_t<XT, 16>(st, x, n, d, wr, bias, e, k, renorm, li, lo, idx, w, pp, pc, pm);
-  return launch_route_t<XT, 32>(st, x, n, d, wr, bias, e, k, renorm, li, lo, idx, w, pp, pc, pm);
+  if (n_et <= 1) return launch_route_t<XT, 1>(st, x, n, d, wr, bias, e, k, renorm, li, lo, idx, w, pp, pc, pm, zc);
+  if (n_et <= 2) return launch_route_t<XT, 2>(st, x, n, d, wr, bias, e, k, renorm, li, lo, idx, w, pp, pc, pm, zc);
+  if (n_et <= 4) return launch_route_t<XT, 4>(st, x, n, d, wr, bias, e, k, renorm, li, lo, idx, w, pp, pc, pm, zc);
+  if (n_et <= 8) return launch_route_t<XT, 8>(st, x, n, d, wr, bias, e, k, renorm, li, lo, idx, w, pp, pc, pm, zc);
+  if (n_et <= 10) return launch_route_t<XT, 10>(st, x, n, d, wr, bias, e, k, renorm, li, lo, idx, w, pp, pc, pm, zc);
+  if (n_et <= 16) return launch_route_t<XT, 16>(st, x, n, d, wr, bias, e, k, renorm, li, lo, idx, w, pp, pc, pm, zc);
+  return launch_route_t<XT, 32>(st, x, n, d, wr, bias, e, k, renorm, li, lo, idx, w, pp, pc, pm, zc);
 }
 
 template <int EPT>
@@ -649,11 +622,11 @@ hipError_t launch_logits_t(hipStream_t st, const uint16_t* x, const RoutePlan& p
 template <int VPL>
 hipError_t launch_gate_t(hipStream_t st, const float* part, int ks, int64_t n, int e,
                          const float* bias, int k, int renorm, float* lo, int32_t* idx,
-                         float* w, float* pp, int32_t* pc, float* pm) {
+                         float* w, float* pp, int32_t* pc, float* pm, int32_t* zc) {
   const int tpw = gate_tokens_per_wave(n);
   hipLaunchKernelGGL((route_gate_kernel<VPL>), dim3(static_cast<unsigned>(gate_blocks(n))),
                      dim3(kThreads), 0, st, part, ks, n, e, bias, k, renorm, tpw, lo, idx, w,
-                     pp, pc, pm);
+                     pp, pc, pm, zc);
   return hipGetLastError();
 }
 
@@ -662,10 +635,11 @@ hipError_t launch_gate_t(hipStream_t st, const float* part, int ks, int64_t n, i
 hipError_t launch_route(hipStream_t st, const float* x, int64_t n, int64_t d,
                         const float* w_router, const float* logit_bias, int e, int k,
                         int renorm, float* logits_out, int32_t* topk_idx, float* topk_w,
-                        float* part_prob, int32_t* part_cnt, float* part_mon) {
+                        float* part_prob, int32_t* part_cnt, float* part_mon, int32_t* zero_ctr) {
   if (n <= 0) return hipSuccess;
   return launch_route_dt<float>(st, x, n, d, w_router, logit_bias, e, k, renorm, nullptr,
-                                logits_out, topk_idx, topk_w, part_prob, part_cnt, part_mon);
+                                logits_out, topk_idx, topk_w, part_prob, part_cnt, part_mon,
+                                zero_ctr);
 }
 
 RoutePlan route_plan(int64_t n, int64_t d, int e) {
@@ -721,14 +695,14 @@ hipError_t launch_route_logits(hipStream_t st, const uint16_t* x, const RoutePla
 hipError_t launch_route_gate(hipStream_t st, const float* part, int ks, int64_t n, int e,
                              const float* bias, int k, int renorm, float* logits_out,
                              int32_t* topk_idx, float* topk_w, float* part_prob,
-                             int32_t* part_cnt, float* part_mon) {
+                             int32_t* part_cnt, float* part_mon, int32_t* zero_ctr) {
   if (n <= 0) return hipSuccess;
   const int vpl = (e + kWave - 1) / kWave;
-  if (vpl <= 1) return launch_gate_t<1>(st, part, ks, n, e, bias, k, renorm, logits_out, topk_idx, topk_w, part_prob, part_cnt, part_mon);
-  if (vpl <= 2) return launch_gate_t<2>(st, part, ks, n, e, bias, k, renorm, logits_out, topk_idx, topk_w, part_prob, part_cnt, part_mon);
-  if (vpl <= 3) return launch_gate_t<3>(st, part, ks, n, e, bias, k, renorm, logits_out, topk_idx, topk_w, part_prob, part_cnt, part_mon);
-  if (vpl <= 4) return launch_gate_t<4>(st, part, ks, n, e, bias, k, renorm, logits_out, topk_idx, topk_w, part_prob, part_cnt, part_mon);
-  return launch_gate_t<8>(st, part, ks, n, e, bias, k, renorm, logits_out, topk_idx, topk_w, part_prob, part_cnt, part_mon);
+  if (vpl <= 1) return launch_gate_t<1>(st, part, ks, n, e, bias, k, renorm, logits_out, topk_idx, topk_w, part_prob, part_cnt, part_mon, zero_ctr);
+  if (vpl <= 2) return launch_gate_t<2>(st, part, ks, n, e, bias, k, renorm, logits_out, topk_idx, topk_w, part_prob, part_cnt, part_mon, zero_ctr);
+  if (vpl <= 3) return launch_gate_t<3>(st, part, ks, n, e, bias, k, renorm, logits_out, topk_idx, topk_w, part_prob, part_cnt, part_mon, zero_ctr);
+  if (vpl <= 4) return launch_gate_t<4>(st, part, ks, n, e, bias, k, renorm, logits_out, topk_idx, topk_w, part_prob, part_cnt, part_mon, zero_ctr);
+  return launch_gate_t<8>(st, part, ks, n, e, bias, k, renorm, logits_out, topk_idx, topk_w, part_prob, part_cnt, part_mon, zero_ctr);
 }
 
 hipError_t launch_update_bias(hipStream_t st, const int32_t* sel_count, int e, int64_t n, int k,
