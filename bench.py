@@ -76,6 +76,21 @@ def packed_path(cfg, capacity: int, packed: bool) -> bool:
     return bool(packed) and cfg.dtype == "bf16"
 
 
+def _grid_for(max_rows: int, n_seg: int, bm: int, n_ntiles: int) -> int:
+    t = (-(-max_rows // bm) + n_seg) * n_ntiles
+    return -(-t // 8) * 8
+
+
+def _f32_tile(cfg, stage: str, capacity: int) -> int:
+    """The float32 product's tile side: 64 where 64 x 64 tiles give 512 workgroups or
+    more by the library's row bound, else 32."""
+    rows = cfg.n_tokens * cfg.top_k
+    if capacity >= 0:
+        rows = min(rows, capacity * cfg.n_experts)
+    n_out = cfg.d_ff if stage == "gemm1" else cfg.d_model
+    return 64 if _grid_for(rows, cfg.n_experts, 64, -(-n_out // 64)) >= 512 else 32
+
+
 def stage_symbol(cfg, stage: str, packed: bool = False, capacity: int = -1):
     """The kernel of a GEMM stage's launch.  (With a capacity limit and a row bound of
     SMALL_ROWS or more per expert, the dispatch picks the tile height on the device; the
@@ -84,7 +99,7 @@ def stage_symbol(cfg, stage: str, packed: bool = False, capacity: int = -1):
     if epi is None:
         return None
     if cfg.dtype != "bf16":
-        return f"gemm_f32_kernel<{epi}, false>"
+        return f"gemm_f32_kernel<{epi}, false, {_f32_tile(cfg, stage, capacity)}>"
     avg = _avg_rows(cfg, capacity)
     if avg < SMALL_ROWS:
         return f"gemm_packed_small_kernel<{epi}>" if packed else f"gemm_bf16_kernel<32, {epi}, false>"

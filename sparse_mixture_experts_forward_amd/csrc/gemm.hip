@@ -1763,16 +1763,21 @@ __global__ __launch_bounds__(kWave) void gemm_packed_finish_kernel(GemmArgs g) {
 }
 
 // ------------------------------------------------------------------ float32 SIMT kernel
-constexpr int kFBM = 64, kFBN = 64, kFBK = 64, kFPad = 4;
-constexpr int kFLd = kFBK / 16;  // float4 loads per thread and operand per chunk
+constexpr int kFBK = 64, kFPad = 4;
 
-// 64 x 64 output tile per workgroup of 256 threads (4 x 4 outputs each), K in chunks of
-// 64 staged through LDS; the next chunk's global loads are issued before the current
+// FB x FB output tile per workgroup of 256 threads (FB / 16 x FB / 16 outputs each: 64 x
+// 64, or 32 x 32 where 64 x 64 tiles would leave most CUs idle), K in chunks of 64 staged
+// through LDS; the next chunk's global loads are issued before the current
 // chunk's FMAs, so a chunk costs one load round trip at most (the products of the small
 // float32 layer are latency-bound: one 16-deep chunk per round trip took 52 us for a
 // 512-deep product).  Every output accumulates its k terms in ascending order.
-template <int EPI, bool KSPLIT>
+template <int EPI, bool KSPLIT, int FB>
 __global__ __launch_bounds__(kThreads) void gemm_f32_kernel(GemmArgs g) {
+  constexpr int kFBM = FB, kFBN = FB;
+  constexpr int TPR = kThreads / FB;        // threads per staged row
+  constexpr int kFLd = kFBK / (4 * TPR);    // float4 loads per thread and operand per chunk
+  constexpr int TO = FB / 16;               // outputs per thread along each side
+  static_assert(kFLd >= 1 && TO >= 1, "tile size");
   __shared__ float As[kFBK][kFBM + kFPad];
   __shared__ float Bs[kFBK][kFBN + kFPad];
   __shared__ float B3s[(EPI == EPI_SWIGLU) ? kFBK : 1][kFBN + kFPad];
@@ -1785,7 +1790,7 @@ __global__ __launch_bounds__(kThreads) void gemm_f32_kernel(GemmArgs g) {
 
   const int tid = threadIdx.x;
   const int ty = tid / 16, tx = tid % 16;
-  const int lr = tid / 4, lk = (tid % 4) * 4;  // row, and first k of the thread's float4s
+  const int lr = tid / TPR, lk = (tid % TPR) * 4;  // row, and first k of the thread's float4s
   const float* A = static_cast<const float*>(g.a);
   const int64_t a_r = tile.row0 + min(lr, tile.m_valid - 1);
   const float* arow = A + (g.a_rows ? static_cast<int64_t>(g.a_rows[a_r]) : a_r) * g.lda;
@@ -1795,12 +1800,12 @@ __global__ __launch_bounds__(kThreads) void gemm_f32_kernel(GemmArgs g) {
                            ? static_cast<const float*>(g.b1) + tile.seg * g.b_seg_stride + static_cast<int64_t>(n_ld) * g.ldb
                            : nullptr;
 
-  // float4 u of a chunk at k0: k = k0 + lk + 16 u (zero past K)
+  // float4 u of a chunk at k0: k = k0 + lk + 4 TPR u (zero past K)
   float4 av[kFLd], bv[kFLd], b3v[kFLd];
   auto load = [&](int k0) {
 #pragma unroll
     for (int u = 0; u < kFLd; ++u) {
-      const int kk = k0 + lk + 16 * u;
+      const int kk = k0 + lk + 4 * TPR * u;
       av[u] = bv[u] = b3v[u] = make_float4(0.f, 0.f, 0.f, 0.f);
       if (kk < g.k) {
         int64_t bk = kk;
@@ -1814,12 +1819,12 @@ __global__ __launch_bounds__(kThreads) void gemm_f32_kernel(GemmArgs g) {
       }
     }
   };
-  float acc[4][4] = {}, acc3[4][4] = {};
+  float acc[TO][TO] = {}, acc3[TO][TO] = {};
   load(0);
   for (int k0 = 0; k0 < g.k; k0 += kFBK) {
 #pragma unroll
     for (int u = 0; u < kFLd; ++u) {
-      const int q = lk + 16 * u;
+      const int q = lk + 4 * TPR * u;
       As[q + 0][lr] = av[u].x; As[q + 1][lr] = av[u].y; As[q + 2][lr] = av[u].z; As[q + 3][lr] = av[u].w;
       Bs[q + 0][lr] = bv[u].x; Bs[q + 1][lr] = bv[u].y; Bs[q + 2][lr] = bv[u].z; Bs[q + 3][lr] = bv[u].w;
       if (EPI == EPI_SWIGLU) {
@@ -1830,18 +1835,18 @@ __global__ __launch_bounds__(kThreads) void gemm_f32_kernel(GemmArgs g) {
     if (k0 + kFBK < g.k) load(k0 + kFBK);  // in flight during this chunk's FMAs
 #pragma unroll 16
     for (int q = 0; q < kFBK; ++q) {
-      float a[4], b[4], b3[4];
+      float a[TO], b[TO], b3[TO];
 #pragma unroll
-      for (int i = 0; i < 4; ++i) a[i] = As[q][ty + 16 * i];
+      for (int i = 0; i < TO; ++i) a[i] = As[q][ty + 16 * i];
 #pragma unroll
-      for (int j = 0; j < 4; ++j) {
+      for (int j = 0; j < TO; ++j) {
         b[j] = Bs[q][tx + 16 * j];
         if (EPI == EPI_SWIGLU) b3[j] = B3s[q][tx + 16 * j];
       }
 #pragma unroll
-      for (int i = 0; i < 4; ++i)
+      for (int i = 0; i < TO; ++i)
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
+        for (int j = 0; j < TO; ++j) {
           acc[i][j] = fmaf(a[i], b[j], acc[i][j]);
           if (EPI == EPI_SWIGLU) acc3[i][j] = fmaf(a[i], b3[j], acc3[i][j]);
         }
@@ -1852,12 +1857,12 @@ __global__ __launch_bounds__(kThreads) void gemm_f32_kernel(GemmArgs g) {
   float* C = static_cast<float*>(g.c);
   const float* bias = static_cast<const float*>(g.bias);
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
+  for (int i = 0; i < TO; ++i) {
     const int m = ty + 16 * i;
     if (m >= tile.m_valid) continue;
     const int64_t orow = g.c_rows ? g.c_rows[tile.row0 + m] : tile.row0 + m;
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
+    for (int j = 0; j < TO; ++j) {
       const int col = tile.nt * kFBN + tx + 16 * j;
       if (col >= g.n_out) continue;
       float v;
@@ -1998,19 +2003,26 @@ hipError_t launch_bf16_epi(hipStream_t st, const GemmArgs& g, int64_t max_rows) 
   return launch_bf16_bm<32, EPI>(st, small, small_rows, ksplit);
 }
 
-template <int EPI>
-hipError_t launch_f32_epi(hipStream_t st, const GemmArgs& g, int64_t max_rows) {
-  const int n_ntiles = (g.n_out + kFBN - 1) / kFBN;
-  const int n_seg_eff = g.seg_off ? g.n_seg : 1;
-  const int64_t grid = grid_for(max_rows, n_seg_eff, kFBM, n_ntiles);
-  if (grid <= 0) return hipSuccess;
+template <int EPI, int FB>
+hipError_t launch_f32_fb(hipStream_t st, const GemmArgs& g, int64_t grid) {
   if (g.kchunk != g.k)
-    hipLaunchKernelGGL((gemm_f32_kernel<EPI, true>), dim3(static_cast<unsigned>(grid)),
+    hipLaunchKernelGGL((gemm_f32_kernel<EPI, true, FB>), dim3(static_cast<unsigned>(grid)),
                        dim3(kThreads), 0, st, g);
   else
-    hipLaunchKernelGGL((gemm_f32_kernel<EPI, false>), dim3(static_cast<unsigned>(grid)),
+    hipLaunchKernelGGL((gemm_f32_kernel<EPI, false, FB>), dim3(static_cast<unsigned>(grid)),
                        dim3(kThreads), 0, st, g);
   return hipGetLastError();
+}
+
+template <int EPI>
+hipError_t launch_f32_epi(hipStream_t st, const GemmArgs& g, int64_t max_rows) {
+  const int n_seg_eff = g.seg_off ? g.n_seg : 1;
+  // 64 x 64 tiles where they fill the GPU twice over, else 32 x 32 (four times as many
+  // workgroups: the small float32 layer's second product has 16 tiles of 64 x 64)
+  const int64_t grid64 = grid_for(max_rows, n_seg_eff, 64, (g.n_out + 63) / 64);
+  if (grid64 <= 0) return hipSuccess;
+  if (grid64 >= 512) return launch_f32_fb<EPI, 64>(st, g, grid64);
+  return launch_f32_fb<EPI, 32>(st, g, grid_for(max_rows, n_seg_eff, 32, (g.n_out + 31) / 32));
 }
 
 }  // namespace

@@ -2,7 +2,8 @@
 and where the benchmark packs the expert weights, following the library's rules (with
 packed weights, by the library's bound on the kept rows per expert: >= 256 the 128 x 512
 shape, 48 .. 255 the 256 x 256 shape, < 48 the 32-row kernel; staged weights: >= 48 the
-256-row tiles, < 48 the 32-row tiles; float32 the SIMT kernel)."""
+256-row tiles, < 48 the 32-row tiles; float32 the SIMT kernel, on 32 x 32 tiles where
+64 x 64 tiles would number under 512)."""
 import bench
 from sparse_mixture_experts_forward_amd import CONFIGS
 from sparse_mixture_experts_forward_amd import _binding as B
@@ -19,7 +20,7 @@ def test_stage_kernels_of_the_workloads():
         "decode": (True, "gemm_packed_small_kernel<2>", "gemm_packed_small_kernel<0>"),
         "deepseek": (True, "gemm_packed_kernel<PackedShape<256, 16, 4, 1>, 2>", "gemm_packed_kernel<PackedShape<256, 16, 4, 1>, 0>"),
         "switch": (True, "gemm_packed_kernel<PackedShape<256, 16, 4, 1>, 1>", "gemm_packed_kernel<PackedShape<256, 16, 4, 1>, 0>"),
-        "tiny": (False, "gemm_f32_kernel<1, false>", "gemm_f32_kernel<0, false>"),
+        "tiny": (False, "gemm_f32_kernel<1, false, 32>", "gemm_f32_kernel<0, false, 32>"),
     }
     for name, (packed, k1, k2) in want.items():
         c = CONFIGS[name]
@@ -45,3 +46,11 @@ def test_kernel_rules_at_the_thresholds():
         assert bench.stage_symbol(c, "gemm1", False, -1) == staged, n
     # a capacity bounds the rows: 4096 tokens, capacity 20 -> 20 rows per expert
     assert bench.stage_symbol(m, "gemm2", True, 20) == "gemm_packed_small_kernel<0>"
+
+
+def test_float32_tile_choice():
+    t = CONFIGS["tiny"]
+    # 512 rows over 8 experts: 64 x 64 tiles number (8 + 8) x 8 = 128 (gemm1), x 2 (gemm2)
+    assert bench._f32_tile(t, "gemm1", -1) == 32 and bench._f32_tile(t, "gemm2", -1) == 32
+    big = t.with_tokens(8192)  # (256 + 8) x 8 = 2112 tiles of 64 x 64 for gemm1
+    assert bench._f32_tile(big, "gemm1", -1) == 64
