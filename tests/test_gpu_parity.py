@@ -811,6 +811,44 @@ def test_forward_edge_cases():
     assert (st["expert_offsets"].cpu() == 0).all()
 
 
+PLAN_CASES = [
+    ("switch", dict()),  # capacity 160, top-1: 2048 gate workgroups of 4 tokens
+    ("deepseek", dict(n_tokens=1000, d_ff=128)),  # logit bias, top-6, shared experts
+    ("tiny", dict()),  # float32 router: 16-token rows
+    ("switch", dict(n_tokens=65536, d_model=128, d_ff=256, alpha=1.0)),  # > 256 chunks
+    ("decode", dict()),  # capacity 2
+]
+
+
+@pytest.mark.parametrize("name,kw", PLAN_CASES, ids=[f"{n}-{i}" for i, (n, _) in enumerate(PLAN_CASES)])
+def test_forward_plan_matches_route_and_dispatch(name, kw):
+    """moe_forward takes its capacity plan and the balance statistics from the router's
+    per-workgroup partials in one launch; moe_route followed by moe_dispatch builds them
+    from the top-k indices with launches of their own.  The plan must be the same bits,
+    the statistics the same up to the order of their float64 sums."""
+    cfg = CONFIGS[name].scaled(**kw)
+    print_case("plan", name, cfg.n_tokens)
+    inp = synth.DeviceInputs(cfg, DEV)
+    layer = MoELayer.from_inputs(inp)
+    st = layer.new_stats(cfg.n_tokens)
+    layer.forward(inp.x, stats=st)
+    torch.cuda.synchronize()
+    got = {key: t.cpu().numpy() for key, t in st.items()}
+    r = _route(inp.x, inp.w_router, inp.logit_bias, cfg.n_experts, cfg.top_k,
+               renorm=cfg.renormalize, sel_only=cfg.bias_selection_only)
+    cap = B.moe_capacity_rule(cfg.n_tokens, cfg.n_experts, cfg.top_k,
+                              B.CAPACITY_RULES[cfg.capacity_rule], cfg.alpha or 0.0)
+    out = _dispatch(r["idx"], cfg.n_experts, cap, None)
+    assert np.array_equal(got["logits"].view(np.uint32), r["logits"].view(np.uint32))
+    assert np.array_equal(got["topk_idx"], r["idx"])
+    assert np.array_equal(got["sel_count"], r["sel"])
+    np.testing.assert_allclose(got["prob_mean"], r["pm"], rtol=1e-6, atol=0)
+    np.testing.assert_allclose(got["aux"], r["aux"], rtol=1e-6, atol=0)
+    np.testing.assert_allclose(got["monitor"][:4], r["mon"], rtol=1e-5, atol=1e-7)
+    for key in ("expert_offsets", "slot_row", "kept_count", "n_dropped"):
+        assert np.array_equal(got[key], out[key].cpu().numpy()), key
+
+
 # ------------------------------------------------------------------ streams
 def test_forward_concurrent_streams_match_sequential():
     """The library keeps no state between calls: two layers with shared experts (each
