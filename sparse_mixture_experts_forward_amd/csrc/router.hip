@@ -67,7 +67,7 @@ __device__ __forceinline__ void gate_token(const float (&l)[VPL], int lane, int 
       z[i] = -INFINITY;
     }
   }
-  const float m = wave_max(qmax);
+  const float m = wave_max_dpp(qmax);
   float lsum = 0.f;
 #pragma unroll
   for (int i = 0; i < VPL; ++i) {
@@ -75,7 +75,7 @@ __device__ __forceinline__ void gate_token(const float (&l)[VPL], int lane, int 
     ex[i] = (e < E) ? expf((sel_only ? l[i] : z[i]) - m) : 0.f;
     lsum += ex[i];
   }
-  const float s = wave_sum(lsum);
+  const float s = wave_sum_dpp(lsum);
 #pragma unroll
   for (int i = 0; i < VPL; ++i) pacc[i] += ex[i] / s;
 
@@ -91,12 +91,7 @@ __device__ __forceinline__ void gate_token(const float (&l)[VPL], int lane, int 
       const int e = lane + kWave * i;
       if (z[i] > bv || (z[i] == bv && e < be)) { bv = z[i]; be = e; }
     }
-#pragma unroll
-    for (int msk = 32; msk >= 1; msk >>= 1) {
-      const float ov = __shfl_xor(bv, msk, kWave);
-      const int oe = __shfl_xor(be, msk, kWave);
-      if (ov > bv || (ov == bv && oe < be)) { bv = ov; be = oe; }
-    }
+    wave_argmax_dpp(bv, be);
     const int owner = be & (kWave - 1);
     const int slot = be / kWave;
     float oex = 0.f;
@@ -108,7 +103,7 @@ __device__ __forceinline__ void gate_token(const float (&l)[VPL], int lane, int 
         cacc[i] += 1;
       }
     }
-    const float wex = __shfl(oex, owner, kWave);
+    const float wex = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(oex), owner));
     sel_ex_sum += wex;
     if (lane == j) { my_ex = wex; my_idx = be; }
   }
@@ -125,16 +120,16 @@ __device__ __forceinline__ void gate_token(const float (&l)[VPL], int lane, int 
 #pragma unroll
       for (int i = 0; i < VPL; ++i)
         if (lane + kWave * i < E) lm = fmaxf(lm, l[i]);
-      lm = wave_max(lm);
+      lm = wave_max_dpp(lm);
       float ls = 0.f;
 #pragma unroll
       for (int i = 0; i < VPL; ++i)
         if (lane + kWave * i < E) ls += expf(l[i] - lm);
-      lse = lm + logf(wave_sum(ls));
+      lse = lm + logf(wave_sum_dpp(ls));
     }
     lse2 += lse * lse;
     const float q = (lane < k) ? my_ex / sel_ex_sum : 0.f;
-    ent += wave_sum(q > 0.f ? -q * log2f(q) : 0.f);
+    ent += wave_sum_dpp(q > 0.f ? -q * log2f(q) : 0.f);
   }
 }
 
