@@ -47,55 +47,6 @@ __device__ __forceinline__ float wave_sum(float v) {
   return v;
 }
 
-// Wave-wide max, sum and (value, index) argmax without LDS round trips inside a row of
-// 16 lanes: DPP quad swaps (lane ^ 1, lane ^ 2), the half-row mirror (lanes i and 7 - i
-// of each 8), the row mirror (i and 15 - i), a swizzle exchanging lane i and i ^ 16, then
-// the two 32-lane halves read from lanes 0 and 32.  Every step combines two values built
-// from disjoint lane sets, so for a commutative operation each lane holds the same bits
-// after each step and the result is wave-uniform.
-template <int CTRL>
-__device__ __forceinline__ int dpp_i(int v) {
-  return __builtin_amdgcn_update_dpp(0, v, CTRL, 0xF, 0xF, false);
-}
-constexpr int kDppXor1 = 0xB1, kDppXor2 = 0x4E, kDppHalfMirror = 0x141, kDppMirror = 0x140;
-__device__ __forceinline__ int swz_xor16(int v) { return __builtin_amdgcn_ds_swizzle(v, 0x401F); }
-
-template <class F>
-__device__ __forceinline__ float wave_reduce_dpp(float v, F op) {
-  v = op(v, __int_as_float(dpp_i<kDppXor1>(__float_as_int(v))));
-  v = op(v, __int_as_float(dpp_i<kDppXor2>(__float_as_int(v))));
-  v = op(v, __int_as_float(dpp_i<kDppHalfMirror>(__float_as_int(v))));
-  v = op(v, __int_as_float(dpp_i<kDppMirror>(__float_as_int(v))));
-  v = op(v, __int_as_float(swz_xor16(__float_as_int(v))));
-  return op(__int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 0)),
-            __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 32)));
-}
-__device__ __forceinline__ float wave_max_dpp(float v) {
-  return wave_reduce_dpp(v, [](float a, float b) { return fmaxf(a, b); });
-}
-__device__ __forceinline__ float wave_sum_dpp(float v) {
-  return wave_reduce_dpp(v, [](float a, float b) { return a + b; });
-}
-// The largest v over the wave, ties to the lowest e (a total order on distinct e);
-// returns it in v and e of every lane.
-__device__ __forceinline__ void wave_argmax_dpp(float& v, int& e) {
-  auto take = [&](float ov, int oe) {
-    if (ov > v || (ov == v && oe < e)) { v = ov; e = oe; }
-  };
-  take(__int_as_float(dpp_i<kDppXor1>(__float_as_int(v))), dpp_i<kDppXor1>(e));
-  take(__int_as_float(dpp_i<kDppXor2>(__float_as_int(v))), dpp_i<kDppXor2>(e));
-  take(__int_as_float(dpp_i<kDppHalfMirror>(__float_as_int(v))), dpp_i<kDppHalfMirror>(e));
-  take(__int_as_float(dpp_i<kDppMirror>(__float_as_int(v))), dpp_i<kDppMirror>(e));
-  take(__int_as_float(swz_xor16(__float_as_int(v))), swz_xor16(e));
-  const float v0 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 0));
-  const int e0 = __builtin_amdgcn_readlane(e, 0);
-  const float v1 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 32));
-  const int e1 = __builtin_amdgcn_readlane(e, 32);
-  const bool hi = v1 > v0 || (v1 == v0 && e1 < e0);
-  v = hi ? v1 : v0;
-  e = hi ? e1 : e0;
-}
-
 // Inclusive prefix sum over the 64 lanes of a wave.
 __device__ __forceinline__ int wave_incl_scan(int v) {
   const int lane = lane_id();

@@ -215,8 +215,8 @@ __global__ __launch_bounds__(kThreads) void dispatch_plan_kernel(
     if (b < n_blocks) {
       const int64_t r1 = min(rows, (b + 1) * per);
       for (int64_t r = b * per; r < r1; ++r) {
-        v += part_cnt[r * E + e];
-        ps += static_cast<double>(part_prob[r * E + e]);
+        v += part_cnt[e * rows + r];
+        ps += static_cast<double>(part_prob[e * rows + r]);
       }
     }
     int chunk_total;

@@ -63,7 +63,8 @@ hipError_t launch_route_gate(hipStream_t st, const float* part, int ks, int64_t 
 hipError_t launch_update_bias(hipStream_t st, const int32_t* sel_count, int e, int64_t n, int k,
                               float gamma, float* logit_bias);
 
-// Statistics over `rows` partial rows: per-expert workgroups (sel_count, prob_mean and
+// Statistics over `rows` partial rows (part_prob / part_cnt [E][rows], one column per
+// router workgroup): per-expert workgroups (sel_count, prob_mean and
 // the aux terms; `term` E doubles and `cnt` E counts of scratch), then aux and, if
 // `monitor` is given, z-loss, mean top-k entropy, sum of squared load shares and load
 // CV (monitor[0..3]; part_mon holds two floats per row).
@@ -101,7 +102,7 @@ hipError_t launch_dispatch(hipStream_t st, const int32_t* topk_idx, int64_t n, i
                            void* zero_rows = nullptr, int64_t zero_row_bytes = 0);
 
 // The forward pass's dispatch when the router's per-workgroup partials are at hand
-// (rows router workgroups of rtok consecutive tokens each: part_cnt / part_prob [rows][E],
+// (rows router workgroups of rtok consecutive tokens each: part_cnt / part_prob [E][rows],
 // part_mon [rows][2] with `monitor`): no histogram launch and no statistics launches.
 // Dispatch chunks are runs of whole router rows (planned_dispatch_grid).  One launch
 // scans the chunk counts per expert, sums the statistics (sel_count, prob_mean, aux,
