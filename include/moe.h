@@ -500,8 +500,10 @@ typedef struct {
   float* monitor;
   int32_t* n_rerouted;     /* [1]: slots moved by re-routing (0 without it) */
   /* Timing markers (hipEvent_t handles owned by the caller, or NULL): stage_events[i]
-   * is recorded on the stream at boundary i -- 0 before routing, 1 after routing and
-   * its statistics, 2 after dispatch, 3 after the routed first expert layer, 4 after
+   * is recorded on the stream at boundary i -- 0 before routing, 1 after routing (and
+   * its statistics with re-routing; without it the statistics are finished by the
+   * capacity-plan launch, before 2), 2 after dispatch, 3 after the routed first expert
+   * layer, 4 after
    * the routed second expert layer, 5 once the shared experts are also done (they may
    * run concurrently, see moe_streams), 6 after the combine. */
   void* stage_events[MOE_N_STAGE_EVENTS];
