@@ -763,6 +763,19 @@ def test_forward_parity_many_tokens():
         assert err <= TOL[cfg.dtype], v
 
 
+@pytest.mark.parametrize("n", [8192, 4096, 1000])
+def test_forward_parity_float32_tile_sizes(n):
+    """The float32 expert products take 64 x 64 tiles where those number 512 or more and
+    32 x 32 tiles below: at 8192 tokens both products run the 64 x 64 kernel, at 4096 the
+    first (d_ff 512) the 64 x 64 one and the second (d 128) the 32 x 32 one, at 1000 both
+    32 x 32, with ragged segments and tails.  Every output token against the oracle."""
+    cfg = CONFIGS["tiny"].with_tokens(n)
+    print_case("forward-f32-tiles", cfg.name, n)
+    out, r = _forward_variants(cfg, ("staged",))
+    assert len(r.tokens) == n
+    assert out["staged"][0] <= TOL["f32"]
+
+
 @pytest.mark.parametrize("packed", [False, True])
 def test_forward_is_deterministic(packed):
     # packed: 600 rows per expert of 4, the packed kernel with a split last round
