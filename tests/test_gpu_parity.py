@@ -763,6 +763,18 @@ def test_forward_parity_many_tokens():
         assert err <= TOL[cfg.dtype], v
 
 
+@pytest.mark.parametrize("rule", ["linear", "log"])
+def test_forward_parity_adaptive_capacity_without_reroute(rule):
+    """The batch-dependent capacities with plain dropping (no re-routing): the plan
+    comes from the router's partials in one launch; every token against the oracle."""
+    cfg = CONFIGS["switch"].scaled(n_tokens=2048, d_ff=1024, capacity_rule=rule)
+    print_case("forward-capacity-rule", rule, cfg.n_tokens)
+    out, r = _forward_variants(cfg, ("staged", "packed_only"))
+    assert r.plan.n_dropped > 0
+    for v, (err, _, _) in out.items():
+        assert err <= TOL[cfg.dtype], v
+
+
 @pytest.mark.parametrize("n", [8192, 4096, 1000])
 def test_forward_parity_float32_tile_sizes(n):
     """The float32 expert products take 64 x 64 tiles where those number 512 or more and
@@ -830,6 +842,8 @@ PLAN_CASES = [
     ("tiny", dict()),  # float32 router: 16-token rows
     ("switch", dict(n_tokens=65536, d_model=128, d_ff=256, alpha=1.0)),  # > 256 chunks
     ("decode", dict()),  # capacity 2
+    ("decode", dict(capacity_rule="linear")),  # batch-dependent capacity, no re-routing
+    ("switch", dict(n_tokens=2048, capacity_rule="log")),
 ]
 
 
